@@ -1,0 +1,255 @@
+/*
+ * paged_decode.h - C ABI of the MI355X (gfx950) paged split-KV decode library.
+ *
+ * Two attention operations over a paged KV cache addressed through a
+ * per-request block table, a static split-count helper and the split merge:
+ *
+ *   paged_decode_gqa   one query token per request, grouped-query heads,
+ *                      optional per-head sinks and a sliding window;
+ *   paged_verify_mla   qlen causal "verify" tokens per request over one shared
+ *                      latent cache, V read as K[..., :Lv], bf16 or FP8 cache;
+ *   num_kv_splits_cap  static split cap from static sizes (graph-capture safe);
+ *   merge_splits       merges fp32 split partials into O and a natural-log LSE.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers are DEVICE pointers unless marked [host].  The caller allocates
+ *   and owns every buffer (inputs, outputs, workspace); the library keeps no
+ *   per-call state and never allocates, frees or synchronises.
+ * - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *   null stream).  The launch shape depends only on the integer arguments,
+ *   never on device data, so a call can be captured in a HIP graph.
+ * - Strides are in ELEMENTS of the tensor they describe; the innermost
+ *   dimension is always contiguous (stride 1).
+ * - Every argument check happens on the host before any HIP call; a failed
+ *   check returns a negative pd_status and enqueues nothing.  Device data
+ *   (lengths, block-table entries) is never read on the host.  On the device,
+ *   a length below 0 counts as 0, a length beyond the block-table row's
+ *   capacity (max_blocks * page_size) is clamped to it, and an attended
+ *   block-table entry outside [0, num_pages) is never dereferenced: the
+ *   affected (request, head) outputs are written as NaN instead.
+ * - bf16 values are IEEE binary32 truncated to their upper 16 bits (round to
+ *   nearest even on output); FP8 is OCP E4M3FN.
+ *
+ * Numerics (module docstring of "vllm.models.flint.ops.decode_attention"):
+ * scores are bf16 x bf16 products accumulated in fp32; softmax runs in fp32 as
+ * exp2(s * c - m * c) with c = sm_scale * log2(e) and a running max m of the
+ * unscaled scores; probabilities are rounded to bf16 for the P.V product
+ * (fp32 accumulation); split partials stay fp32.
+ */
+#ifndef PAGED_DECODE_H_
+#define PAGED_DECODE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define PD_API __attribute__((visibility("default")))
+#else
+#define PD_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes.  0 is success; every error is negative. */
+typedef enum {
+  PD_OK = 0,
+  PD_ERR_INVALID = -1,     /* null pointer, negative size or inconsistent sizes */
+  PD_ERR_ALIGN = -2,       /* pointer not 16-byte aligned / stride not 16-byte multiple */
+  PD_ERR_UNSUPPORTED = -3, /* a size this build has no kernel for */
+  PD_ERR_WORKSPACE = -4,   /* workspace missing or smaller than pd_workspace_bytes() */
+  PD_ERR_HIP = -5          /* a HIP runtime call failed (launch, device query) */
+} pd_status;
+
+/* Cache element type of the MLA latent cache. */
+typedef enum { PD_KV_BF16 = 0, PD_KV_FP8_E4M3FN = 1 } pd_kv_dtype;
+
+/* [host] Static text for a pd_status value (never NULL). */
+PD_API const char* pd_status_string(int status);
+
+/*
+ * num_kv_splits_cap - static upper bound on KV splits per request.
+ *
+ * Restates "vllm.v1.attention.ops.triton_decode_attention",
+ * verify_num_kv_splits: a program is one (request, row block) pair, with
+ * ceil(qlen * num_heads / block_h) row blocks per request; the ideal split
+ * count is ceil(max_seq_len / min_work_per_split); with
+ * slots = floor(occupancy * num_cus) resident programs, if one split of every
+ * request fits in one dispatch round the cap fills that round
+ * (slots / programs), otherwise it is the n <= min(ideal, max_splits) that
+ * minimises ceil(n * programs / slots) / n, preferring the smallest n within
+ * 5% of the best; the result is clamped to [1, min(ideal, 2 * num_cus)].
+ *
+ * Skew extension (balance_chunk > 0): that rule assumes every request has
+ * max_seq_len keys.  With skewed lengths one long request would leave a few
+ * programs running long after the rest, so the cap is raised to at least
+ * min(max_splits, ideal, ceil(max_seq_len / balance_chunk)), which bounds the
+ * keys any one split of the longest request can hold.  balance_chunk <= 0
+ * gives the unmodified rule.
+ *
+ * For GQA decode pass qlen = 1, num_heads = num_kv_heads, block_h = 1 (one
+ * program per (request, kv head)).  num_cus <= 0 queries the current device.
+ * Pure host function; it reads no device data.  Returns the cap (>= 1), or a
+ * negative pd_status for negative sizes, block_h < 1, occupancy <= 0,
+ * max_splits < 1, or a failed device query.
+ */
+PD_API int32_t num_kv_splits_cap(int32_t max_seq_len, int32_t batch, int32_t qlen,
+                          int32_t num_heads, int32_t block_h, int32_t num_cus,
+                          float occupancy, int32_t min_work_per_split,
+                          int32_t max_splits, int32_t balance_chunk);
+
+/*
+ * [host] Bytes of fp32 workspace a call with `num_splits` > 1 needs:
+ * rows * num_heads * num_splits * (head_dim_v + 1) * 4, laid out
+ * [rows][num_heads][num_splits][head_dim_v + 1] ("vllm.v1.attention.ops.
+ * triton_decode_attention", decode_attention_fwd_verify, parameter
+ * attn_logits).  Slot [..., s, 0:Dv] holds split s's normalised output
+ * O_s = sum_j e^{x_j} V_j / sum_j e^{x_j}; slot [..., s, Dv] holds its
+ * natural-log lse_s (-inf when the split saw no key, O_s then unspecified).
+ * Returns 0 when num_splits <= 1 (no workspace is used).
+ */
+PD_API size_t pd_workspace_bytes(int32_t rows, int32_t num_heads, int32_t num_splits,
+                          int32_t head_dim_v);
+
+/*
+ * paged_decode_gqa - paged GQA decode, one query token per request.
+ *
+ * Defined by "vllm.models.flint.ops.decode_attention", flint_decode_attention
+ * and its kernel: query head h of request b attends the keys at positions
+ * [lo, L) of its kv head h / (Hq / Hkv), with L = seq_lens[b] (the KV length
+ * including the current token) and lo = max(L - window, 0) for window > 0
+ * (the last `window` positions), else lo = 0.  Position j is slot j % P of
+ * physical page block_table[b][j / P] ("Atención paginada", decode path:
+ * the block table maps a request's logical blocks to cache blocks; -1 marks
+ * unallocated blocks, which are never read).
+ *
+ *   O[b,h]   = sum_j e^{x_j} V_j / (sum_j e^{x_j} + e^{sinks[h]}),
+ *   x_j      = sm_scale * q[b,h] . K_j,
+ *   LSE[b,h] = ln sum_j e^{x_j}           (sink excluded; -inf with no key),
+ *   O = 0 for a request with no attended key (e.g. seq_lens[b] == 0).
+ *
+ * q            [B, Hq, D] bf16, strides (q_stride_b, q_stride_h, 1).
+ * kv           HND cache [num_pages, Hkv, P, 2D] bf16: K in [..., 0:D], V in
+ *              [..., D:2D], token stride 2D, strides (kv_stride_page,
+ *              kv_stride_head, 2D, 1); 8 KB per page per kv head at D=128, P=16.
+ * block_table  [B, max_blocks] int32, row stride bt_stride_b.
+ * seq_lens     [B] int32.
+ * sinks        [Hq] fp32 sink logits, or NULL for none.
+ * window       <= 0 for full attention.
+ * num_kv_splits static split cap S >= 1 (see num_kv_splits_cap); each request
+ *              uses only as many splits as its own length needs.  S == 1
+ *              writes O / LSE directly; S > 1 writes fp32 partials to
+ *              `workspace` (>= pd_workspace_bytes(B, Hq, S, D) bytes) and
+ *              merges them with the same kernel as merge_splits.
+ * out          [B, Hq, D] bf16, strides (o_stride_b, o_stride_h, 1).
+ * lse          [B, Hq] fp32 with row stride lse_stride_b, or NULL.
+ *
+ * Supported: D = 128; P in {16, 32}; Hq = G * Hkv with 1 <= G <= 16.
+ * q, kv, out, workspace 16-byte aligned; q/kv/out strides multiples of 8.
+ * A workspace must not be shared by calls in flight on different streams.
+ */
+PD_API int paged_decode_gqa(const void* q, int64_t q_stride_b, int64_t q_stride_h,
+                     const void* kv, int64_t kv_stride_page, int64_t kv_stride_head,
+                     int32_t num_pages,
+                     const int32_t* block_table, int64_t bt_stride_b, int32_t max_blocks,
+                     const int32_t* seq_lens, const float* sinks, int32_t window,
+                     float sm_scale, int32_t batch, int32_t num_q_heads,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                     int32_t num_kv_splits, float* workspace, size_t workspace_bytes,
+                     void* out, int64_t o_stride_b, int64_t o_stride_h,
+                     float* lse, int64_t lse_stride_b, void* stream);
+
+/*
+ * paged_decode_gqa_partials - the split partials of paged_decode_gqa only.
+ *
+ * Same arguments and key ranges as paged_decode_gqa (no sinks, no outputs):
+ * writes every (request, query head, split) slot of `workspace`, laid out as
+ * in pd_workspace_bytes(B, Hq, max(S, 2), D) but with S slots per head, for
+ * S = num_kv_splits >= 1, and launches no merge.  A split slot a request does
+ * not use gets lse = -inf.  merge_splits over that workspace (with the sinks)
+ * gives exactly paged_decode_gqa's result.  This is the per-shard half of
+ * split-KV ("vllm.models.flint.ops.decode_attention", module docstring:
+ * per-split fp32 partials merged afterwards): a caller that holds a
+ * request's keys in several places (another stream, another device) merges
+ * the partials once they are gathered.  Workspace bytes >=
+ * B * Hq * S * (D + 1) * 4.
+ */
+PD_API int paged_decode_gqa_partials(const void* q, int64_t q_stride_b, int64_t q_stride_h,
+                              const void* kv, int64_t kv_stride_page, int64_t kv_stride_head,
+                              int32_t num_pages, const int32_t* block_table,
+                              int64_t bt_stride_b, int32_t max_blocks, const int32_t* seq_lens,
+                              int32_t window, float sm_scale, int32_t batch,
+                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t page_size, int32_t num_kv_splits, float* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/*
+ * paged_verify_mla - causal MLA verify over a per-request block table.
+ *
+ * Defined by "vllm.v1.attention.ops.triton_decode_attention",
+ * decode_attention_fwd_verify: the qlen verify rows of request b are rows
+ * b*qlen + t (t = 0..qlen-1) of q; row t attends key positions [0, hi) with
+ *   hi = max(min(L - qlen + 1 + t, L_real), 0),  L = seq_lens[b],
+ *   L_real = real_seq_lens[b] (or L when real_seq_lens is NULL);
+ * K_j is latent row j (all Lk dims) and V_j = K_j[0:Lv]; the block table has
+ * one row per request shared by its qlen rows.  O and LSE as for GQA without
+ * sinks; rows with hi = 0 get O = 0 and LSE = -inf.
+ *
+ * q            [B*qlen, H, Lk] bf16, strides (q_stride_row, q_stride_h, 1).
+ * kv           latent cache [num_pages, P, 1, Lk] (a [num_pages*P, 1, Lk]
+ *              view is the same memory), element type kv_dtype, strides
+ *              (kv_stride_page, kv_stride_tok, -, 1).
+ * k_scale      device fp32 scalar dequantising an FP8 cache (value = code *
+ *              k_scale, for K and V alike), or NULL for 1; ignored for bf16.
+ * block_table  [B, max_blocks] int32; seq_lens, real_seq_lens [B] int32
+ *              (real_seq_lens may be NULL).
+ * num_kv_splits, workspace: as for GQA with rows = B*qlen, Dv = Lv.
+ * out          [B*qlen, H, Lv] bf16, strides (o_stride_row, o_stride_h, 1).
+ * lse          [B*qlen, H] fp32 with row stride lse_stride_row, or NULL.
+ *
+ * Supported: Lk = 576, Lv = 512 (512 + 64 rope dims); P = 16;
+ * qlen * H a multiple of 32; pointers 16-byte aligned; strides multiples of
+ * 16 bytes.
+ */
+PD_API int paged_verify_mla(const void* q, int64_t q_stride_row, int64_t q_stride_h,
+                     const void* kv, int32_t kv_dtype, int64_t kv_stride_page,
+                     int64_t kv_stride_tok, int32_t num_pages, const float* k_scale,
+                     const int32_t* block_table, int64_t bt_stride_b, int32_t max_blocks,
+                     const int32_t* seq_lens, const int32_t* real_seq_lens,
+                     int32_t qlen, float sm_scale, int32_t batch, int32_t num_heads,
+                     int32_t head_dim_k, int32_t head_dim_v, int32_t page_size,
+                     int32_t num_kv_splits, float* workspace, size_t workspace_bytes,
+                     void* out, int64_t o_stride_row, int64_t o_stride_h,
+                     float* lse, int64_t lse_stride_row, void* stream);
+
+/*
+ * merge_splits - merge fp32 split partials into O (bf16) and LSE (fp32).
+ *
+ * For each (row, head) with partials (O_s, lse_s) in the workspace layout of
+ * pd_workspace_bytes():
+ *   M = max_s lse_s,  w_s = e^{lse_s - M} (0 when lse_s = -inf),
+ *   O = sum_s w_s O_s / (sum_s w_s + e^{sinks[h] - M}),  LSE = M + ln sum_s w_s,
+ * and O = 0, LSE = -inf when every lse_s is -inf.  This is the split combine
+ * of "vllm.models.flint.ops.decode_attention" (combine_splits: max over
+ * splits, per-split weights, weighted l and O, sink in the final
+ * denominator) restated for normalised partials and natural logs.  A split
+ * whose lse_s is -inf is skipped, so its O_s may hold anything (even NaN).
+ *
+ * workspace  fp32 [rows, num_heads, num_splits, head_dim_v + 1], contiguous.
+ * sinks      [num_heads] fp32 or NULL.
+ * out        [rows, num_heads, head_dim_v] bf16, strides (o_stride_row,
+ *            o_stride_h, 1); lse [rows, num_heads] fp32 or NULL.
+ * Supported: head_dim_v in {128, 256, 512, 1024}; num_splits >= 1.
+ */
+PD_API int merge_splits(const float* workspace, int32_t rows, int32_t num_heads,
+                 int32_t num_splits, int32_t head_dim_v, const float* sinks,
+                 void* out, int64_t o_stride_row, int64_t o_stride_h,
+                 float* lse, int64_t lse_stride_row, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_DECODE_H_ */

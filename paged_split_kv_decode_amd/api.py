@@ -1,0 +1,266 @@
+"""Thin torch binding of the C ABI: argument marshalling only.
+
+torch supplies device memory and the current stream; every step of the
+computation runs in the HIP kernels of ``libpaged_decode.so``.  Outputs and
+the split workspace are allocated here with torch when the caller does not
+pass them (pass them to keep a call allocation-free, e.g. under graph
+capture).
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _native
+from ._native import PD_KV_BF16, PD_KV_FP8_E4M3FN, check, lib
+
+# Split-cap policy of this build (arguments of num_kv_splits_cap).
+GQA_OCCUPANCY = 1.0          # resident decode workgroups per CU (128 KB LDS each)
+GQA_MIN_WORK = 256           # keys per split before a request uses fewer splits
+GQA_MAX_SPLITS = 64
+GQA_BALANCE_CHUNK = 1024     # skew bound: no split of the longest request above this
+MLA_BLOCK_H = 128            # verify rows (qlen * heads) per workgroup
+MLA_OCCUPANCY = 1.0
+MLA_MIN_WORK = 128
+MLA_MAX_SPLITS = 16
+MLA_BALANCE_CHUNK = 2048
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, name, dtype, dim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device (HIP) tensor")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name} must be {dim}-D, got shape {tuple(t.shape)}")
+
+
+def num_kv_splits_cap(max_seq_len: int, batch: int, qlen: int, num_heads: int, block_h: int,
+                      num_cus: int = 0, occupancy: float = 1.0, min_work_per_split: int = 64,
+                      max_splits: int = 8, balance_chunk: int = 0) -> int:
+    """Static split cap (see include/paged_decode.h); a pure host function."""
+    r = lib.num_kv_splits_cap(int(max_seq_len), int(batch), int(qlen), int(num_heads),
+                              int(block_h), int(num_cus), float(occupancy),
+                              int(min_work_per_split), int(max_splits), int(balance_chunk))
+    if r < 0:
+        check("num_kv_splits_cap", r)
+    return int(r)
+
+
+def gqa_split_cap(batch: int, num_kv_heads: int, max_seq_len: int, window: int = 0,
+                  num_cus: int = 0) -> int:
+    """Split cap for paged_decode_gqa: one program per (request, kv head)."""
+    eff = min(max_seq_len, window) if window and window > 0 else max_seq_len
+    return num_kv_splits_cap(eff, batch, 1, num_kv_heads, 1, num_cus, GQA_OCCUPANCY,
+                             GQA_MIN_WORK, GQA_MAX_SPLITS, GQA_BALANCE_CHUNK)
+
+
+def mla_split_cap(batch: int, qlen: int, num_heads: int, max_seq_len: int,
+                  num_cus: int = 0) -> int:
+    """Split cap for paged_verify_mla: one program per (request, row block)."""
+    return num_kv_splits_cap(max_seq_len, batch, qlen, num_heads, MLA_BLOCK_H, num_cus,
+                             MLA_OCCUPANCY, MLA_MIN_WORK, MLA_MAX_SPLITS, MLA_BALANCE_CHUNK)
+
+
+def workspace_bytes(rows: int, num_heads: int, num_splits: int, head_dim_v: int) -> int:
+    return int(lib.pd_workspace_bytes(int(rows), int(num_heads), int(num_splits),
+                                      int(head_dim_v)))
+
+
+def alloc_workspace(rows, num_heads, num_splits, head_dim_v, device):
+    n = workspace_bytes(rows, num_heads, num_splits, head_dim_v)
+    if n == 0:
+        return None
+    return torch.empty(n // 4, dtype=torch.float32, device=device)
+
+
+def paged_decode_gqa(q, kv, block_table, seq_lens, sm_scale, sinks=None, window=0,
+                     num_kv_splits=1, workspace=None, out=None, lse=None, stream=None,
+                     return_lse=True):
+    """Paged GQA decode (include/paged_decode.h: paged_decode_gqa).
+
+    q [B, Hq, D] bf16; kv [num_pages, Hkv, P, 2D] bf16 (K | V); block_table
+    [B, max_blocks] int32; seq_lens [B] int32; sinks [Hq] fp32 or None.
+    Returns (out [B, Hq, D] bf16, lse [B, Hq] fp32 or None).
+    """
+    _need(q, "q", torch.bfloat16, 3)
+    _need(kv, "kv", torch.bfloat16, 4)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    B, Hq, D = q.shape
+    num_pages, Hkv, P, two_d = kv.shape
+    if two_d != 2 * D or kv.stride(3) != 1 or kv.stride(2) != 2 * D or q.stride(2) != 1:
+        raise ValueError("kv must be [pages, Hkv, P, 2D] with contiguous token rows")
+    if block_table.shape[0] != B or seq_lens.shape[0] != B or block_table.stride(1) != 1:
+        raise ValueError("block_table / seq_lens must have one row per request")
+    if sinks is not None:
+        _need(sinks, "sinks", torch.float32, 1)
+        if sinks.shape[0] != Hq or sinks.stride(0) != 1:
+            raise ValueError("sinks must be a contiguous [Hq] tensor")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", torch.bfloat16, 3)
+    if out.stride(2) != 1:
+        raise ValueError("out must have a contiguous last dim")
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 2)
+        if lse.stride(1) != 1:
+            raise ValueError("lse must have a contiguous last dim")
+    S = int(num_kv_splits)
+    if S > 1 and workspace is None:
+        workspace = alloc_workspace(B, Hq, S, D, q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.paged_decode_gqa(
+        _ptr(q), q.stride(0), q.stride(1),
+        _ptr(kv), kv.stride(0), kv.stride(1), num_pages,
+        _ptr(block_table), block_table.stride(0), block_table.shape[1],
+        _ptr(seq_lens), _ptr(sinks), int(window or 0), float(sm_scale),
+        B, Hq, Hkv, D, P, S, _ptr(workspace), ws_bytes,
+        _ptr(out), out.stride(0), out.stride(1),
+        _ptr(lse), 0 if lse is None else lse.stride(0), _stream(stream))
+    check("paged_decode_gqa", st)
+    return out, lse
+
+
+def paged_decode_gqa_partials(q, kv, block_table, seq_lens, sm_scale, window=0,
+                              num_kv_splits=1, workspace=None, stream=None):
+    """Split partials of paged_decode_gqa without the merge
+    (include/paged_decode.h: paged_decode_gqa_partials).  Returns the fp32
+    workspace viewed as [B, Hq, S, D + 1]."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(kv, "kv", torch.bfloat16, 4)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    B, Hq, D = q.shape
+    num_pages, Hkv, P, two_d = kv.shape
+    if two_d != 2 * D or kv.stride(3) != 1 or kv.stride(2) != 2 * D or q.stride(2) != 1:
+        raise ValueError("kv must be [pages, Hkv, P, 2D] with contiguous token rows")
+    if block_table.stride(1) != 1:
+        raise ValueError("block_table rows must be contiguous")
+    S = int(num_kv_splits)
+    n = B * Hq * S * (D + 1)
+    if workspace is None:
+        workspace = torch.empty(n, dtype=torch.float32, device=q.device)
+    _need(workspace, "workspace", torch.float32)
+    st = lib.paged_decode_gqa_partials(
+        _ptr(q), q.stride(0), q.stride(1),
+        _ptr(kv), kv.stride(0), kv.stride(1), num_pages,
+        _ptr(block_table), block_table.stride(0), block_table.shape[1],
+        _ptr(seq_lens), int(window or 0), float(sm_scale),
+        B, Hq, Hkv, D, P, S, _ptr(workspace), workspace.numel() * 4, _stream(stream))
+    check("paged_decode_gqa_partials", st)
+    return workspace[:n].view(B, Hq, S, D + 1)
+
+
+def paged_verify_mla(q, kv, block_table, seq_lens, real_seq_lens, qlen, sm_scale,
+                     head_dim_v=512, page_size=None, k_scale=None, num_kv_splits=1,
+                     workspace=None, out=None, lse=None, stream=None):
+    """Causal MLA verify (include/paged_decode.h: paged_verify_mla).
+
+    q [B*qlen, H, Lk] bf16; kv [num_pages, P, 1, Lk] (or [num_pages*P, 1, Lk])
+    as bf16, or as uint8 FP8 E4M3FN codes with ``k_scale`` a 1-element fp32
+    device tensor.  Returns (out [B*qlen, H, Lv] bf16, lse [B*qlen, H] fp32).
+    """
+    _need(q, "q", torch.bfloat16, 3)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    rows, H, Lk = q.shape
+    if kv.dtype == torch.bfloat16:
+        kv_dtype = PD_KV_BF16
+    elif kv.dtype in (torch.uint8, torch.float8_e4m3fn):
+        kv_dtype = PD_KV_FP8_E4M3FN
+    else:
+        raise TypeError(f"kv must be bf16 or FP8 E4M3FN codes, got {kv.dtype}")
+    if not kv.is_cuda:
+        raise ValueError("kv must be a device tensor")
+    if kv.dim() == 4:
+        num_pages, P = kv.shape[0], kv.shape[1]
+        if kv.shape[2] != 1:
+            raise ValueError("the verify path expects a single latent KV head")
+        s_page, s_tok = kv.stride(0), kv.stride(1)
+    elif kv.dim() == 3:
+        if page_size is None:
+            raise ValueError("page_size is required for a 3-D cache view")
+        P = int(page_size)
+        if kv.shape[0] % P or kv.shape[1] != 1:
+            raise ValueError("3-D cache must be [num_pages * P, 1, Lk]")
+        num_pages = kv.shape[0] // P
+        s_tok = kv.stride(0)
+        s_page = s_tok * P
+    else:
+        raise ValueError("kv must be 3-D or 4-D")
+    if kv.shape[-1] != Lk or kv.stride(-1) != 1 or q.stride(2) != 1:
+        raise ValueError("cache / q last dims must match Lk and be contiguous")
+    if rows % qlen:
+        raise ValueError("q rows must be a multiple of qlen")
+    B = rows // qlen
+    if real_seq_lens is not None:
+        _need(real_seq_lens, "real_seq_lens", torch.int32, 1)
+    if k_scale is not None:
+        _need(k_scale, "k_scale", torch.float32)
+    Lv = int(head_dim_v)
+    if out is None:
+        out = torch.empty((rows, H, Lv), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((rows, H), dtype=torch.float32, device=q.device)
+    S = int(num_kv_splits)
+    if S > 1 and workspace is None:
+        workspace = alloc_workspace(rows, H, S, Lv, q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.paged_verify_mla(
+        _ptr(q), q.stride(0), q.stride(1),
+        _ptr(kv), kv_dtype, s_page, s_tok, num_pages, _ptr(k_scale),
+        _ptr(block_table), block_table.stride(0), block_table.shape[1],
+        _ptr(seq_lens), _ptr(real_seq_lens), int(qlen), float(sm_scale),
+        B, H, Lk, Lv, P, S, _ptr(workspace), ws_bytes,
+        _ptr(out), out.stride(0), out.stride(1),
+        _ptr(lse), lse.stride(0), _stream(stream))
+    check("paged_verify_mla", st)
+    return out, lse
+
+
+def merge_splits(workspace, rows, num_heads, num_splits, head_dim_v, sinks=None, out=None,
+                 lse=None, stream=None):
+    """Merge fp32 split partials [rows, H, S, Dv + 1] into bf16 O and fp32 LSE."""
+    _need(workspace, "workspace", torch.float32)
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    need = int(rows) * int(num_heads) * int(num_splits) * (int(head_dim_v) + 1)
+    if workspace.numel() < need:
+        raise ValueError("workspace smaller than rows * H * S * (Dv + 1)")
+    dev = workspace.device
+    if out is None:
+        out = torch.empty((rows, num_heads, head_dim_v), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((rows, num_heads), dtype=torch.float32, device=dev)
+    if sinks is not None:
+        _need(sinks, "sinks", torch.float32, 1)
+    st = lib.merge_splits(_ptr(workspace), int(rows), int(num_heads), int(num_splits),
+                          int(head_dim_v), _ptr(sinks), _ptr(out), out.stride(0),
+                          out.stride(1), _ptr(lse), lse.stride(0), _stream(stream))
+    check("merge_splits", st)
+    return out, lse
+
+
+__all__ = [
+    "PD_KV_BF16", "PD_KV_FP8_E4M3FN", "alloc_workspace", "gqa_split_cap", "merge_splits",
+    "paged_decode_gqa_partials",
+    "mla_split_cap", "num_kv_splits_cap", "paged_decode_gqa", "paged_verify_mla",
+    "workspace_bytes", "_native",
+]

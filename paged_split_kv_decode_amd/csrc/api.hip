@@ -1,0 +1,321 @@
+// C ABI of the library: argument checks (host only, before any HIP call),
+// the static split cap, workspace sizing and dispatch to the kernels.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/paged_decode.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+extern "C" {
+
+const char* pd_status_string(int status) {
+  switch (status) {
+    case PD_OK: return "ok";
+    case PD_ERR_INVALID: return "invalid argument";
+    case PD_ERR_ALIGN: return "pointer or stride not 16-byte aligned";
+    case PD_ERR_UNSUPPORTED: return "unsupported size";
+    case PD_ERR_WORKSPACE: return "workspace missing or too small";
+    case PD_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int32_t num_kv_splits_cap(int32_t max_seq_len, int32_t batch, int32_t qlen, int32_t num_heads,
+                          int32_t block_h, int32_t num_cus, float occupancy,
+                          int32_t min_work_per_split, int32_t max_splits,
+                          int32_t balance_chunk) {
+  if (max_seq_len < 0 || batch < 0 || qlen < 1 || num_heads < 1 || block_h < 1 ||
+      !(occupancy > 0.f) || max_splits < 1)
+    return PD_ERR_INVALID;
+  if (num_cus <= 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return PD_ERR_HIP;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return PD_ERR_HIP;
+    num_cus = n;
+  }
+  const int64_t row_blocks = cdiv64((int64_t)qlen * num_heads, block_h);
+  const int64_t per_split = (int64_t)(batch > 1 ? batch : 1) * row_blocks;
+  const int64_t ideal =
+      cdiv64(max_seq_len > 1 ? max_seq_len : 1, min_work_per_split > 1 ? min_work_per_split : 1);
+  int64_t slots = (int64_t)((double)occupancy * (double)num_cus);
+  if (slots < 1) slots = 1;
+  int64_t n;
+  if (per_split <= slots) {
+    n = slots / per_split;
+  } else {
+    const int64_t top = ideal < max_splits ? ideal : max_splits;
+    const int64_t hi = top > 1 ? top : 1;
+    double best = 1e300;
+    for (int64_t k = 1; k <= hi; ++k) {
+      const double cost = (double)cdiv64(k * per_split, slots) / (double)k;
+      if (cost < best) best = cost;
+    }
+    n = hi;
+    for (int64_t k = 1; k <= hi; ++k) {
+      const double cost = (double)cdiv64(k * per_split, slots) / (double)k;
+      if (cost <= best * 1.05) {
+        n = k;
+        break;
+      }
+    }
+  }
+  int64_t cap = n;
+  if (ideal < cap) cap = ideal;
+  if (2 * (int64_t)num_cus < cap) cap = 2 * (int64_t)num_cus;
+  if (cap < 1) cap = 1;
+  if (balance_chunk > 0) {
+    int64_t bal = cdiv64(max_seq_len > 1 ? max_seq_len : 1, balance_chunk);
+    if (bal > max_splits) bal = max_splits;
+    if (bal > ideal) bal = ideal;
+    if (bal > cap) cap = bal;
+  }
+  return (int32_t)cap;
+}
+
+size_t pd_workspace_bytes(int32_t rows, int32_t num_heads, int32_t num_splits, int32_t head_dim_v) {
+  if (rows <= 0 || num_heads <= 0 || num_splits <= 1 || head_dim_v <= 0) return 0;
+  return (size_t)rows * (size_t)num_heads * (size_t)num_splits * (size_t)(head_dim_v + 1) *
+         sizeof(float);
+}
+
+namespace {
+
+static int gqa_common(const void* q, int64_t q_stride_b, int64_t q_stride_h, const void* kv,
+               int64_t kv_stride_page, int64_t kv_stride_head, int32_t num_pages,
+               const int32_t* block_table, int64_t bt_stride_b, int32_t max_blocks,
+               const int32_t* seq_lens, const float* sinks, int32_t window, float sm_scale,
+               int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+               int32_t page_size, int32_t num_kv_splits, float* workspace,
+               size_t workspace_bytes, void* out, int64_t o_stride_b, int64_t o_stride_h,
+               float* lse, int64_t lse_stride_b, void* stream, bool partials_only) {
+  if (batch < 0 || num_q_heads < 1 || num_kv_heads < 1 || num_kv_splits < 1 ||
+      num_pages < 0 || max_blocks < 0 || !std::isfinite(sm_scale))
+    return PD_ERR_INVALID;
+  if (num_q_heads % num_kv_heads != 0) return PD_ERR_INVALID;
+  const int32_t G = num_q_heads / num_kv_heads;
+  if (head_dim != 128 || (page_size != 16 && page_size != 32) || G > 16)
+    return PD_ERR_UNSUPPORTED;
+  if (batch == 0) return PD_OK;
+  if (q == nullptr || kv == nullptr || block_table == nullptr || seq_lens == nullptr ||
+      (!partials_only && out == nullptr))
+    return PD_ERR_INVALID;
+  if (q_stride_b < 0 || q_stride_h < 0 || kv_stride_page < 0 || kv_stride_head < 0 ||
+      bt_stride_b < 0 || o_stride_b < 0 || o_stride_h < 0 || lse_stride_b < 0)
+    return PD_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(kv) || q_stride_b % 8 || q_stride_h % 8 ||
+      kv_stride_page % 8 || kv_stride_head % 8)
+    return PD_ERR_ALIGN;
+  if (!partials_only && (!aligned16(out) || o_stride_b % 8 || o_stride_h % 8)) return PD_ERR_ALIGN;
+  if (num_kv_splits > 1 || partials_only) {
+    const int32_t ws_splits = num_kv_splits > 1 ? num_kv_splits : 2;
+    size_t need = pd_workspace_bytes(batch, num_q_heads, ws_splits, head_dim);
+    if (num_kv_splits == 1) need /= 2;
+    if (workspace == nullptr || workspace_bytes < need) return PD_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return PD_ERR_ALIGN;
+  }
+  if (num_kv_heads > 65535 || batch > 65535 || num_kv_splits > 65535) return PD_ERR_UNSUPPORTED;
+
+  pd::GqaArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.q_sb = q_stride_b;
+  a.q_sh = q_stride_h;
+  a.kv = static_cast<const uint16_t*>(kv);
+  a.kv_sp = kv_stride_page;
+  a.kv_sh = kv_stride_head;
+  a.num_pages = num_pages;
+  a.bt = block_table;
+  a.bt_sb = bt_stride_b;
+  a.max_blocks = max_blocks;
+  a.seq_lens = seq_lens;
+  a.sinks = sinks;
+  a.window = window;
+  a.scale_log2 = sm_scale * kLog2eHost;
+  a.B = batch;
+  a.Hq = num_q_heads;
+  a.Hkv = num_kv_heads;
+  a.G = G;
+  a.P = page_size;
+  a.S = num_kv_splits;
+  a.partials = partials_only ? 1 : 0;
+  a.ws = workspace;
+  a.out = static_cast<uint16_t*>(out);
+  a.o_sb = o_stride_b;
+  a.o_sh = o_stride_h;
+  a.lse = lse;
+  a.lse_sb = lse_stride_b;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (pd::launch_gqa_decode(a, s) != hipSuccess) return PD_ERR_HIP;
+  if (num_kv_splits > 1 && !partials_only) {
+    pd::MergeArgs m{};
+    m.ws = workspace;
+    m.rows = batch;
+    m.H = num_q_heads;
+    m.S = num_kv_splits;
+    m.Dv = head_dim;
+    m.sinks = sinks;
+    m.out = static_cast<uint16_t*>(out);
+    m.o_srow = o_stride_b;
+    m.o_sh = o_stride_h;
+    m.lse = lse;
+    m.lse_srow = lse_stride_b;
+    if (pd::launch_merge(m, s) != hipSuccess) return PD_ERR_HIP;
+  }
+  return PD_OK;
+}
+
+}  // namespace
+
+int paged_decode_gqa(const void* q, int64_t q_stride_b, int64_t q_stride_h, const void* kv,
+                     int64_t kv_stride_page, int64_t kv_stride_head, int32_t num_pages,
+                     const int32_t* block_table, int64_t bt_stride_b, int32_t max_blocks,
+                     const int32_t* seq_lens, const float* sinks, int32_t window, float sm_scale,
+                     int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                     int32_t page_size, int32_t num_kv_splits, float* workspace,
+                     size_t workspace_bytes, void* out, int64_t o_stride_b, int64_t o_stride_h,
+                     float* lse, int64_t lse_stride_b, void* stream) {
+  return gqa_common(q, q_stride_b, q_stride_h, kv, kv_stride_page, kv_stride_head, num_pages,
+                    block_table, bt_stride_b, max_blocks, seq_lens, sinks, window, sm_scale,
+                    batch, num_q_heads, num_kv_heads, head_dim, page_size, num_kv_splits,
+                    workspace, workspace_bytes, out, o_stride_b, o_stride_h, lse, lse_stride_b,
+                    stream, false);
+}
+
+int paged_decode_gqa_partials(const void* q, int64_t q_stride_b, int64_t q_stride_h,
+                              const void* kv, int64_t kv_stride_page, int64_t kv_stride_head,
+                              int32_t num_pages, const int32_t* block_table,
+                              int64_t bt_stride_b, int32_t max_blocks, const int32_t* seq_lens,
+                              int32_t window, float sm_scale, int32_t batch,
+                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t page_size, int32_t num_kv_splits, float* workspace,
+                              size_t workspace_bytes, void* stream) {
+  return gqa_common(q, q_stride_b, q_stride_h, kv, kv_stride_page, kv_stride_head, num_pages,
+                    block_table, bt_stride_b, max_blocks, seq_lens, nullptr, window, sm_scale,
+                    batch, num_q_heads, num_kv_heads, head_dim, page_size, num_kv_splits,
+                    workspace, workspace_bytes, nullptr, 0, 0, nullptr, 0, stream, true);
+}
+
+int paged_verify_mla(const void* q, int64_t q_stride_row, int64_t q_stride_h, const void* kv,
+                     int32_t kv_dtype, int64_t kv_stride_page, int64_t kv_stride_tok,
+                     int32_t num_pages, const float* k_scale, const int32_t* block_table,
+                     int64_t bt_stride_b, int32_t max_blocks, const int32_t* seq_lens,
+                     const int32_t* real_seq_lens, int32_t qlen, float sm_scale, int32_t batch,
+                     int32_t num_heads, int32_t head_dim_k, int32_t head_dim_v,
+                     int32_t page_size, int32_t num_kv_splits, float* workspace,
+                     size_t workspace_bytes, void* out, int64_t o_stride_row,
+                     int64_t o_stride_h, float* lse, int64_t lse_stride_row, void* stream) {
+  if (batch < 0 || qlen < 1 || num_heads < 1 || num_kv_splits < 1 || num_pages < 0 ||
+      max_blocks < 0 || !std::isfinite(sm_scale))
+    return PD_ERR_INVALID;
+  if (kv_dtype != PD_KV_BF16 && kv_dtype != PD_KV_FP8_E4M3FN) return PD_ERR_INVALID;
+  if (head_dim_k != 576 || head_dim_v != 512 || page_size != 16 ||
+      ((int64_t)qlen * num_heads) % 32 != 0)
+    return PD_ERR_UNSUPPORTED;
+  if (batch == 0) return PD_OK;
+  if (q == nullptr || kv == nullptr || block_table == nullptr || seq_lens == nullptr ||
+      out == nullptr)
+    return PD_ERR_INVALID;
+  if (q_stride_row < 0 || q_stride_h < 0 || kv_stride_page < 0 || kv_stride_tok < 0 ||
+      bt_stride_b < 0 || o_stride_row < 0 || o_stride_h < 0 || lse_stride_row < 0)
+    return PD_ERR_INVALID;
+  const int64_t kv_align = kv_dtype == PD_KV_BF16 ? 8 : 16;
+  if (!aligned16(q) || !aligned16(kv) || !aligned16(out) || q_stride_row % 8 ||
+      q_stride_h % 8 || kv_stride_page % kv_align || kv_stride_tok % kv_align ||
+      o_stride_row % 8 || o_stride_h % 8)
+    return PD_ERR_ALIGN;
+  const int64_t rows = (int64_t)batch * qlen;
+  if (rows > 0x7fffffff) return PD_ERR_UNSUPPORTED;
+  if (num_kv_splits > 1) {
+    if (workspace == nullptr ||
+        workspace_bytes < pd_workspace_bytes((int32_t)rows, num_heads, num_kv_splits, head_dim_v))
+      return PD_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return PD_ERR_ALIGN;
+  }
+  pd::MlaArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.q_srow = q_stride_row;
+  a.q_sh = q_stride_h;
+  a.kv = kv;
+  a.kv_fp8 = kv_dtype == PD_KV_FP8_E4M3FN;
+  a.kv_sp = kv_stride_page;
+  a.kv_st = kv_stride_tok;
+  a.num_pages = num_pages;
+  a.k_scale = k_scale;
+  a.bt = block_table;
+  a.bt_sb = bt_stride_b;
+  a.max_blocks = max_blocks;
+  a.seq_lens = seq_lens;
+  a.real_lens = real_seq_lens;
+  a.qlen = qlen;
+  a.scale_log2 = sm_scale * kLog2eHost;
+  a.B = batch;
+  a.H = num_heads;
+  a.P = page_size;
+  a.S = num_kv_splits;
+  a.ws = workspace;
+  a.out = static_cast<uint16_t*>(out);
+  a.o_srow = o_stride_row;
+  a.o_sh = o_stride_h;
+  a.lse = lse;
+  a.lse_srow = lse_stride_row;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (pd::launch_mla_verify(a, s) != hipSuccess) return PD_ERR_HIP;
+  if (num_kv_splits > 1) {
+    pd::MergeArgs m{};
+    m.ws = workspace;
+    m.rows = (int32_t)rows;
+    m.H = num_heads;
+    m.S = num_kv_splits;
+    m.Dv = head_dim_v;
+    m.sinks = nullptr;
+    m.out = static_cast<uint16_t*>(out);
+    m.o_srow = o_stride_row;
+    m.o_sh = o_stride_h;
+    m.lse = lse;
+    m.lse_srow = lse_stride_row;
+    if (pd::launch_merge(m, s) != hipSuccess) return PD_ERR_HIP;
+  }
+  return PD_OK;
+}
+
+int merge_splits(const float* workspace, int32_t rows, int32_t num_heads, int32_t num_splits,
+                 int32_t head_dim_v, const float* sinks, void* out, int64_t o_stride_row,
+                 int64_t o_stride_h, float* lse, int64_t lse_stride_row, void* stream) {
+  if (rows < 0 || num_heads < 1 || num_splits < 1 || head_dim_v < 1) return PD_ERR_INVALID;
+  if (head_dim_v != 128 && head_dim_v != 256 && head_dim_v != 512 && head_dim_v != 1024)
+    return PD_ERR_UNSUPPORTED;
+  if (rows == 0) return PD_OK;
+  if (workspace == nullptr || out == nullptr) return PD_ERR_INVALID;
+  if (o_stride_row < 0 || o_stride_h < 0 || lse_stride_row < 0) return PD_ERR_INVALID;
+  if (!aligned16(out) || o_stride_row % 8 || o_stride_h % 8 ||
+      (reinterpret_cast<uintptr_t>(workspace) & 3u))
+    return PD_ERR_ALIGN;
+  pd::MergeArgs m{};
+  m.ws = workspace;
+  m.rows = rows;
+  m.H = num_heads;
+  m.S = num_splits;
+  m.Dv = head_dim_v;
+  m.sinks = sinks;
+  m.out = static_cast<uint16_t*>(out);
+  m.o_srow = o_stride_row;
+  m.o_sh = o_stride_h;
+  m.lse = lse;
+  m.lse_srow = lse_stride_row;
+  if (pd::launch_merge(m, static_cast<hipStream_t>(stream)) != hipSuccess) return PD_ERR_HIP;
+  return PD_OK;
+}
+
+}  // extern "C"

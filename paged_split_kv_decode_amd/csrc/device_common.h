@@ -1,0 +1,104 @@
+// Device helpers shared by the gfx950 kernels of this library.
+//
+// Everything here is CDNA4-specific: wave64 lane shuffles, the MFMA operand
+// vector types, direct global->LDS loads and the LDS transpose read.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pd {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+
+#define PD_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+// 2^x on the hardware transcendental unit (v_exp_f32); exp2(-inf) = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// log2(x) on the hardware unit (v_log_f32).
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+
+// Lane exchange across the whole wave64 (ds_bpermute based).
+__device__ __forceinline__ float shfl_xor(float v, int mask) {
+  int src = (lane_id() ^ mask) << 2;
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(v)));
+}
+
+__device__ __forceinline__ float readlane(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// fp32 -> bf16 bits with round-to-nearest-even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  __bf16 a = (__bf16)lo;
+  __bf16 b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+#define PD_CONST __attribute__((address_space(4)))
+
+// Read-only int32 data the kernel never writes (block tables, lengths),
+// viewed through the constant address space: a wave-uniform load from it
+// becomes a scalar s_load (counted by lgkmcnt, not vmcnt), which keeps the
+// vmcnt bookkeeping of the LDS-DMA page ring exact.
+__device__ __forceinline__ const PD_CONST int32_t* as_const(const int32_t* p) {
+  return (const PD_CONST int32_t*)p;
+}
+
+// 16 bytes per lane from global memory straight into LDS
+// (global_load_lds_dwordx4): the wave writes 64 consecutive 16-byte chunks
+// starting at LDS byte address `lds_addr` (wave-uniform, goes to M0); lane
+// i's chunk comes from `base + voff_i` (base wave-uniform).
+//
+// Issued as inline asm on purpose: the compiler's own wait insertion treats
+// every later LDS read as dependent on every outstanding LDS-DMA and would
+// drain the whole ring (vmcnt(0)) before each transpose read.  Callers own
+// the ordering instead: `wait_vmcnt<N>()` before reading a slot (vector
+// memory ops complete in order) and `wait_lgkmcnt0()` before refilling a
+// slot that was just read.  The `s_nop` covers the M0-write -> LDS-DMA hazard.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void global_to_lds_16(const void* base, uint32_t voff, uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2"
+      :
+      : "s"(lds_addr), "v"(voff), "s"(base)
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ uint32_t lds_addr(PD_LDS const void* p) {
+  return (uint32_t)(uintptr_t)p;
+}
+
+// s_waitcnt with only the vector-memory counter constrained.  gfx9 encoding:
+// vmcnt[3:0] in bits 3:0 and vmcnt[5:4] in bits 15:14; expcnt (6:4) and
+// lgkmcnt (11:8) left at their maxima.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt out of range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));
+}
+
+}  // namespace pd

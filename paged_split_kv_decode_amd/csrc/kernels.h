@@ -1,0 +1,79 @@
+// Internal launch interface between the C-ABI layer (api.hip) and the
+// kernels.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pd {
+
+// Token tile every kernel walks the keys in (one MFMA contraction depth).
+constexpr int kTileTokens = 32;
+// Fewest 32-token tiles a GQA split takes before the request uses fewer
+// splits (256 keys = 128 KB of K|V per kv head).
+constexpr int kGqaMinSplitTiles = 8;
+// Same for the MLA verify path (in 32-token tiles).
+constexpr int kMlaMinSplitTiles = 4;
+
+struct GqaArgs {
+  const uint16_t* q;
+  int64_t q_sb, q_sh;
+  const uint16_t* kv;
+  int64_t kv_sp, kv_sh;
+  int32_t num_pages;
+  const int32_t* bt;
+  int64_t bt_sb;
+  int32_t max_blocks;
+  const int32_t* seq_lens;
+  const float* sinks;
+  int32_t window;
+  float scale_log2;  // sm_scale * log2(e)
+  int32_t B, Hq, Hkv, G, P;
+  int32_t S;         // split cap
+  int32_t partials;  // 1: always write workspace partials (never O / LSE)
+  float* ws;         // [B, Hq, S, D + 1] when S > 1 or partials
+  uint16_t* out;
+  int64_t o_sb, o_sh;
+  float* lse;
+  int64_t lse_sb;
+};
+
+struct MergeArgs {
+  const float* ws;   // [rows, H, S, Dv + 1]
+  int32_t rows, H, S, Dv;
+  const float* sinks;
+  uint16_t* out;
+  int64_t o_srow, o_sh;
+  float* lse;
+  int64_t lse_srow;
+};
+
+struct MlaArgs {
+  const uint16_t* q;
+  int64_t q_srow, q_sh;
+  const void* kv;
+  int32_t kv_fp8;
+  int64_t kv_sp, kv_st;
+  int32_t num_pages;
+  const float* k_scale;
+  const int32_t* bt;
+  int64_t bt_sb;
+  int32_t max_blocks;
+  const int32_t* seq_lens;
+  const int32_t* real_lens;
+  int32_t qlen;
+  float scale_log2;
+  int32_t B, H, P;
+  int32_t S;
+  float* ws;
+  uint16_t* out;
+  int64_t o_srow, o_sh;
+  float* lse;
+  int64_t lse_srow;
+};
+
+hipError_t launch_gqa_decode(const GqaArgs& a, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
+hipError_t launch_mla_verify(const MlaArgs& a, hipStream_t stream);
+
+}  // namespace pd

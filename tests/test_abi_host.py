@@ -1,0 +1,166 @@
+"""Host-side tests of the C ABI (no GPU needed).
+
+The library must load, export every function include/paged_decode.h
+declares, compute the static split cap exactly as the oracle's restatement of
+the pages' rule, and reject bad arguments with the documented status before
+any HIP call (fake device addresses are never dereferenced on the host).
+"""
+
+import ctypes
+import os
+import random
+import re
+
+import pytest
+
+import oracle
+from paged_split_kv_decode_amd import _native
+from paged_split_kv_decode_amd._native import (PD_ERR_ALIGN, PD_ERR_INVALID, PD_ERR_UNSUPPORTED,
+                                               PD_ERR_WORKSPACE, PD_OK, lib)
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "paged_decode.h")
+FAKE = 0x100000          # 16-byte aligned stand-in address, never dereferenced
+NULL = None
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^PD_API\s+[\w\s\*]+?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_abi():
+    names = _declared_functions()
+    for want in ("paged_decode_gqa", "paged_verify_mla", "num_kv_splits_cap", "merge_splits"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    raw = ctypes.CDLL(_native.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(raw, name), f"{name} declared in paged_decode.h but not exported"
+    assert set(_native.EXPORTS) <= set(_declared_functions())
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4, -5):
+        assert lib.pd_status_string(s)
+    assert lib.pd_status_string(7) == b"unknown status"
+
+
+def _cap(*a):
+    return lib.num_kv_splits_cap(*a)
+
+
+@pytest.mark.parametrize("args,want", [
+    ((70, 3, 1, 1, 1, 256, 1.0, 64, 8), 2),
+    ((100000, 300, 1, 1, 1, 256, 1.0, 64, 8), 4),
+    ((4096, 1, 1, 32, 32, 256, 1.0, 64, 8), 64),
+    ((64, 1, 1, 32, 32, 256, 1.0, 64, 8), 1),
+    ((16384, 4, 4, 128, 64, 256, 1.0, 64, 16), 8),
+    ((16384, 32, 4, 128, 64, 256, 1.0, 64, 16), 1),
+])
+def test_split_cap_hand_values(args, want):
+    assert _cap(*args, 0) == want
+
+
+def test_split_cap_matches_oracle_rule_randomised():
+    rng = random.Random(0)
+    for _ in range(3000):
+        msl = rng.choice([0, 1, 7, 64, 100, 1000, 4096, 16384, 131072, rng.randint(0, 200000)])
+        batch = rng.choice([0, 1, 2, 3, 17, 64, 256, rng.randint(0, 5000)])
+        qlen = rng.randint(1, 8)
+        heads = rng.choice([1, 8, 16, 32, 64, 128])
+        block_h = rng.choice([1, 16, 32, 64, 128])
+        sm = rng.choice([1, 80, 256, 304])
+        occ = rng.choice([1.0, 2.0, 4.0])
+        mw = rng.choice([1, 16, 64, 256])
+        ms = rng.choice([1, 2, 8, 16, 64])
+        want = oracle.verify_num_kv_splits(msl, batch, qlen, heads, sm, block_h, occ, mw, ms)
+        assert _cap(msl, batch, qlen, heads, block_h, sm, occ, mw, ms, 0) == want
+
+
+def test_split_cap_balance_extension():
+    # P1 rule alone returns 1 when programs exceed slots with equal rounds
+    assert _cap(131072, 256, 1, 8, 1, 256, 1.0, 256, 64, 0) == 1
+    # the skew bound raises it to ceil(max_len / chunk), capped by max_splits
+    assert _cap(131072, 256, 1, 8, 1, 256, 1.0, 256, 64, 1024) == 64
+    assert _cap(8192, 64, 1, 8, 1, 256, 1.0, 256, 64, 1024) == 8
+    # and never above ideal = ceil(max_len / min_work)
+    assert _cap(128, 64, 1, 8, 1, 256, 1.0, 256, 64, 16) == 1
+
+
+def test_split_cap_rejects_bad_arguments():
+    assert _cap(-1, 1, 1, 1, 1, 256, 1.0, 64, 8, 0) == PD_ERR_INVALID
+    assert _cap(10, 1, 0, 1, 1, 256, 1.0, 64, 8, 0) == PD_ERR_INVALID
+    assert _cap(10, 1, 1, 1, 0, 256, 1.0, 64, 8, 0) == PD_ERR_INVALID
+    assert _cap(10, 1, 1, 1, 1, 256, 0.0, 64, 8, 0) == PD_ERR_INVALID
+    assert _cap(10, 1, 1, 1, 1, 256, 1.0, 64, 0, 0) == PD_ERR_INVALID
+
+
+def test_workspace_bytes():
+    assert lib.pd_workspace_bytes(64, 64, 8, 128) == 64 * 64 * 8 * 129 * 4
+    assert lib.pd_workspace_bytes(128, 128, 16, 512) == 128 * 128 * 16 * 513 * 4
+    assert lib.pd_workspace_bytes(64, 64, 1, 128) == 0
+    assert lib.pd_workspace_bytes(0, 64, 4, 128) == 0
+
+
+def _gqa(**kw):
+    a = dict(q=FAKE, qsb=64 * 128, qsh=128, kv=FAKE, kvsp=8 * 16 * 256, kvsh=16 * 256, npages=10,
+             bt=FAKE, btsb=4, maxb=4, sl=FAKE, sinks=NULL, window=0, scale=0.088, B=2, Hq=64,
+             Hkv=8, D=128, P=16, S=1, ws=NULL, wsb=0, out=FAKE, osb=64 * 128, osh=128,
+             lse=NULL, lsesb=64, stream=NULL)
+    a.update(kw)
+    return lib.paged_decode_gqa(*a.values())
+
+
+def test_gqa_argument_checks_happen_before_any_hip_call():
+    assert _gqa(B=0, q=NULL, kv=NULL, bt=NULL, sl=NULL, out=NULL) == PD_OK
+    assert _gqa(q=NULL) == PD_ERR_INVALID
+    assert _gqa(sl=NULL) == PD_ERR_INVALID
+    assert _gqa(Hq=60) == PD_ERR_INVALID                      # Hq % Hkv
+    assert _gqa(B=-1) == PD_ERR_INVALID
+    assert _gqa(scale=float("nan")) == PD_ERR_INVALID
+    assert _gqa(D=64) == PD_ERR_UNSUPPORTED
+    assert _gqa(P=8) == PD_ERR_UNSUPPORTED
+    assert _gqa(Hq=136, Hkv=8) == PD_ERR_UNSUPPORTED          # G = 17
+    assert _gqa(q=FAKE + 8) == PD_ERR_ALIGN
+    assert _gqa(kvsp=8 * 16 * 256 + 4) == PD_ERR_ALIGN
+    assert _gqa(osh=132) == PD_ERR_ALIGN
+    assert _gqa(S=4) == PD_ERR_WORKSPACE                       # no workspace
+    need = lib.pd_workspace_bytes(2, 64, 4, 128)
+    assert _gqa(S=4, ws=FAKE, wsb=need - 4) == PD_ERR_WORKSPACE
+    assert _gqa(S=4, ws=FAKE + 4, wsb=need) == PD_ERR_ALIGN
+
+
+def _mla(**kw):
+    a = dict(q=FAKE, qsr=128 * 576, qsh=576, kv=FAKE, dt=0, sp=16 * 576, st=576, npages=10,
+             ks=NULL, bt=FAKE, btsb=4, maxb=4, sl=FAKE, real=NULL, qlen=4, scale=0.07, B=2,
+             H=128, Lk=576, Lv=512, P=16, S=1, ws=NULL, wsb=0, out=FAKE, osr=128 * 512,
+             osh=512, lse=FAKE, lser=128, stream=NULL)
+    a.update(kw)
+    return lib.paged_verify_mla(*a.values())
+
+
+def test_mla_argument_checks_happen_before_any_hip_call():
+    assert _mla(B=0, q=NULL, kv=NULL, bt=NULL, sl=NULL, out=NULL) == PD_OK
+    assert _mla(kv=NULL) == PD_ERR_INVALID
+    assert _mla(qlen=0) == PD_ERR_INVALID
+    assert _mla(dt=7) == PD_ERR_INVALID
+    assert _mla(Lk=512) == PD_ERR_UNSUPPORTED
+    assert _mla(Lv=256) == PD_ERR_UNSUPPORTED
+    assert _mla(P=32) == PD_ERR_UNSUPPORTED
+    assert _mla(H=7, qlen=1) == PD_ERR_UNSUPPORTED             # rows per block
+    assert _mla(out=FAKE + 2) == PD_ERR_ALIGN
+    assert _mla(dt=1, st=576 + 8) == PD_ERR_ALIGN              # fp8 rows need 16 B
+    assert _mla(S=2) == PD_ERR_WORKSPACE
+
+
+def test_merge_argument_checks():
+    f = lib.merge_splits
+    assert f(FAKE, 0, 8, 2, 128, NULL, FAKE, 1024, 128, NULL, 8, NULL) == PD_OK
+    assert f(NULL, 4, 8, 2, 128, NULL, FAKE, 1024, 128, NULL, 8, NULL) == PD_ERR_INVALID
+    assert f(FAKE, 4, 8, 2, 96, NULL, FAKE, 1024, 128, NULL, 8, NULL) == PD_ERR_UNSUPPORTED
+    assert f(FAKE, 4, 8, 0, 128, NULL, FAKE, 1024, 128, NULL, 8, NULL) == PD_ERR_INVALID
+    assert f(FAKE, 4, 8, 2, 128, NULL, FAKE + 2, 1024, 128, NULL, 8, NULL) == PD_ERR_ALIGN
