@@ -37,9 +37,18 @@ def sources() -> list[str]:
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
+# Per-source code-generation flags.  The MLA kernel keeps its 256 x 32 fp32
+# accumulator per wave in AGPRs so the VGPR file holds the query fragment
+# and the LDS operands.
+PER_SOURCE_FLAGS = {
+    "mla_verify.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=0"],
+}
+
+
 def _compile(src: str, extra: list[str]) -> str:
     obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *HIPCC_FLAGS, *extra, "-c", src, "-o", obj]
+    per = PER_SOURCE_FLAGS.get(os.path.basename(src), [])
+    cmd = [_hipcc(), *HIPCC_FLAGS, *per, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

@@ -31,6 +31,9 @@
 // * The waves' (m, l, O) are combined through LDS; a single split writes
 //   bf16 O and LSE, several splits write fp32 (O/l, lse) partials for the
 //   merge kernel.
+#include <cstdlib>
+#include <cstring>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -38,12 +41,9 @@ namespace pd {
 namespace {
 
 constexpr int kD = 128;
-constexpr int kNW = 4;                                  // waves per workgroup
-constexpr int kNS = 2;                                  // ring stages per wave
 constexpr int kRowBytes = 2 * kD * 2;                   // K|V row of one token
 constexpr int kTileBytes = kTileTokens * kRowBytes;     // 16 KB
 constexpr int kLoadsPerTile = kTileBytes / (64 * 16);   // 16 wave loads
-constexpr int kLdsBytes = kNW * kNS * kTileBytes;       // 128 KB
 constexpr int kCombHeadStride = kD + 4;                 // floats, padded
 constexpr int kCombWaveFloats = 16 * kCombHeadStride + 48;
 
@@ -57,8 +57,11 @@ __device__ __forceinline__ uint32_t keep_mask(bool lo_ok, bool hi_ok) {
   return (lo_ok ? 0x0000FFFFu : 0u) | (hi_ok ? 0xFFFF0000u : 0u);
 }
 
-template <int P>
-__global__ __launch_bounds__(kNW * 64, 1) void gqa_decode_kernel(GqaArgs a) {
+// kNW waves per workgroup, kNS ring stages (tiles) per wave.
+template <int P, int kNW, int kNS>
+__global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
+  constexpr int kLdsBytes = kNW * kNS * kTileBytes;
+  static_assert(kLdsBytes >= kNW * kCombWaveFloats * 4, "combine buffer must fit the ring");
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
   PD_LDS char* lds = (PD_LDS char*)smem;
 
@@ -78,7 +81,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void gqa_decode_kernel(GqaArgs a) {
   const float c = a.scale_log2;
 
   // ---- key range of this request and the split plan --------------------
-  int L = a.seq_lens[b];
+  int L = as_const(a.seq_lens)[b];
   L = min(max(L, 0), a.max_blocks * P);
   const int hi = L;
   const int lo = a.window > 0 ? max(hi - a.window, 0) : 0;
@@ -86,8 +89,9 @@ __global__ __launch_bounds__(kNW * 64, 1) void gqa_decode_kernel(GqaArgs a) {
   const int n_tiles = hi > lo ? ((hi + 31) >> 5) - t_first : 0;
   int chunk = 1, active = 0;
   if (n_tiles > 0) {
-    chunk = max((n_tiles + S - 1) / S, kGqaMinSplitTiles);
-    active = (n_tiles + chunk - 1) / chunk;
+    // (integer division runs on the VALU: pin the results to SGPRs)
+    chunk = __builtin_amdgcn_readfirstlane(max((n_tiles + S - 1) / S, kGqaMinSplitTiles));
+    active = __builtin_amdgcn_readfirstlane((n_tiles + chunk - 1) / chunk);
   }
 
   if (split >= active) {
@@ -108,7 +112,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void gqa_decode_kernel(GqaArgs a) {
   const int tb = t_first + split * chunk;
   const int te = min(tb + chunk, t_first + n_tiles);
   const int nst = te - tb;
-  const int n_w = nst > wave ? (nst - wave + kNW - 1) / kNW : 0;
+  const int n_w = __builtin_amdgcn_readfirstlane(nst > wave ? (nst - wave + kNW - 1) / kNW : 0);
   const int pg_lo = lo / P;
   const int pg_hi = (hi + P - 1) / P;
 
@@ -331,14 +335,41 @@ __global__ __launch_bounds__(kNW * 64, 1) void gqa_decode_kernel(GqaArgs a) {
 
 }  // namespace
 
-hipError_t launch_gqa_decode(const GqaArgs& a, hipStream_t stream) {
-  dim3 grid(a.S, a.Hkv, a.B), block(kNW * 64);
+template <int NW, int NS>
+static hipError_t launch_variant(const GqaArgs& a, hipStream_t stream) {
+  dim3 grid(a.S, a.Hkv, a.B), block(NW * 64);
   switch (a.P) {
-    case 16: hipLaunchKernelGGL(gqa_decode_kernel<16>, grid, block, 0, stream, a); break;
-    case 32: hipLaunchKernelGGL(gqa_decode_kernel<32>, grid, block, 0, stream, a); break;
+    case 16: hipLaunchKernelGGL((gqa_decode_kernel<16, NW, NS>), grid, block, 0, stream, a); break;
+    case 32: hipLaunchKernelGGL((gqa_decode_kernel<32, NW, NS>), grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+// Tuning override for sweeps (never needed for correctness): PD_GQA_TUNE =
+// "<waves>x<stages>" picks another compiled (waves, ring stages) variant.
+static int tune_variant() {
+  static int v = [] {
+    const char* e = getenv("PD_GQA_TUNE");
+    if (e == nullptr) return 0;
+    if (!strcmp(e, "4x2")) return 0;
+    if (!strcmp(e, "2x2")) return 1;
+    if (!strcmp(e, "2x4")) return 2;
+    if (!strcmp(e, "2x3")) return 3;
+    if (!strcmp(e, "1x4")) return 4;
+    return 0;
+  }();
+  return v;
+}
+
+hipError_t launch_gqa_decode(const GqaArgs& a, hipStream_t stream) {
+  switch (tune_variant()) {
+    case 1: return launch_variant<2, 2>(a, stream);
+    case 2: return launch_variant<2, 4>(a, stream);
+    case 3: return launch_variant<2, 3>(a, stream);
+    case 4: return launch_variant<1, 4>(a, stream);
+    default: return launch_variant<4, 2>(a, stream);
+  }
 }
 
 }  // namespace pd

@@ -1,5 +1,436 @@
+// Causal MLA verify for gfx950: qlen query tokens per request, all heads,
+// over one shared latent cache with V = K[..., :Lv].
+//
+// Operation: "vllm.v1.attention.ops.triton_decode_attention",
+// decode_attention_fwd_verify (row limit max(min(L - qlen + 1 + t, L_real), 0),
+// V read from K, natural-log LSE, [rows, H, S, Lv + 1] fp32 partials, scalar
+// k_scale for an FP8 cache); the split rule (a request's own length cut into
+// max(ceil(L / S), min) chunks) is the one its verify_num_kv_splits describes.
+//
+// Design on CDNA4
+// ---------------
+// * The qlen * H (token, head) pairs of a request are the "rows".  A
+//   workgroup of 4 waves (one per SIMD, 512 registers each) owns 128
+//   consecutive rows of one request and one split of its keys; each wave
+//   owns 32 rows: its query fragment (32 x 576 bf16, 144 VGPRs) and its
+//   output accumulator (512 x 32 fp32, all 256 AGPRs) stay in registers for
+//   the whole split.  The 4 row blocks of one (request, split) are placed on
+//   the same XCD (workgroup-id remap) so they re-read the latent tiles from
+//   that XCD's L2.
+// * Latent tiles of 32 tokens (2 pages, 36 KB bf16 / 18 KB fp8) stream from
+//   HBM into a 3-stage LDS ring shared by the 4 waves, with
+//   global_load_lds_dwordx4 (1 KB per wave instruction); one barrier per tile.
+//   The FP8 cache is dequantised exactly (v_cvt_scalef32_pk_bf16_fp8, scale
+//   1) into a bf16 staging tile; k_scale is folded into the softmax scale and
+//   the output.
+// * S^T[token, row] = K . Q^T with v_mfma_f32_32x32x16_bf16 (two independent
+//   accumulation chains), K fragments read from LDS in batches ahead of
+//   their MFMAs.
+// * O^T[d, row] += V^T . P^T: P leaves the score MFMA already in B-operand
+//   order; V^T is read from the same LDS tile (first 512 dims) with
+//   ds_read_b64_tr_b16, a few blocks ahead of their MFMAs.
+// * Online softmax in the exp2 domain (x = score * sm_scale * log2 e) with a
+//   fixed per-row reference: a row's reference max is its first non-empty
+//   tile's max and is never rescaled, so no vector instruction ever touches
+//   the accumulator (which is what keeps it in AGPRs).  The exact row max is
+//   tracked alongside; if a later score exceeds the reference by more than
+//   2^64 (overflow risk) the workgroup runs the split a second time with the
+//   exact max as reference.  Real attention scores never trigger it.
+// * Each wave owns its rows, so there is no cross-wave combine: a single
+//   split writes bf16 O and LSE, several splits write fp32 partials.
 #include "device_common.h"
 #include "kernels.h"
+
 namespace pd {
-hipError_t launch_mla_verify(const MlaArgs&, hipStream_t) { return hipErrorNotSupported; }
+namespace {
+
+constexpr int kLk = 576;
+constexpr int kLv = 512;
+constexpr int kWaves = 4;                                          // one per SIMD
+constexpr int kRowsPerWave = 32;
+constexpr int kRowsPerBlock = kWaves * kRowsPerWave;              // 128
+constexpr int kRowBytes = kLk * 2;                                 // bf16 latent row
+constexpr int kTileBytes = kTileTokens * kRowBytes;                // 36 KB
+constexpr int kPageRegion = 16 * kRowBytes;                        // 18 KB (bf16)
+constexpr int kRowBytes8 = kLk;                                    // fp8 latent row
+constexpr int kTileBytes8 = kTileTokens * kRowBytes8;              // 18 KB
+constexpr int kPageRegion8 = 16 * kRowBytes8;                      // 9 KB (fp8)
+constexpr int kKSteps = kLk / 16;                                  // 36
+constexpr int kKBatch = 6;                                         // K fragments per batch
+constexpr int kVBlocks = kLv / 32;                                 // 16
+constexpr int kVBatch = 4;                                         // V^T blocks per batch
+// p = 2^(x - m_ref) stays below 2^64 while the row max has not grown more
+// than this above the reference (fp32 / bf16 hold 2^127; with up to 2^20
+// keys and |V| < 2^40 the accumulator cannot overflow).
+constexpr float kRefHeadroomLog2 = 64.f;
+
+// LDS tile layout.  A 32-token tile is two 16-row page regions.  Inside a
+// region the 16-byte chunk c (of the latent row) of row r16 is stored at
+// 16-byte slot 16 * c + (r16 ^ 4 * (c & 1)): chunk-column-major, so
+//  * one global_load_lds instruction (64 slots) fills 4 whole chunk columns
+//    of one page, and each lane's global offset is a lane constant plus
+//    64 bytes per instruction;
+//  * a K-operand read (16 rows, one chunk) touches 16 consecutive slots, and
+//    a transpose read of V (4 rows x chunks c, c + 1) touches two groups of 4
+//    slots whose bank groups differ by the row XOR: both bank-conflict free.
+__device__ __forceinline__ int tile_slot(int c, int r16) { return 16 * c + (r16 ^ (4 * (c & 1))); }
+
+__device__ __forceinline__ uint32_t keep_mask(bool lo_ok, bool hi_ok) {
+  return (lo_ok ? 0x0000FFFFu : 0u) | (hi_ok ? 0xFFFF0000u : 0u);
 }
+
+template <int NS, bool FP8>
+__global__ __launch_bounds__(kWaves * 64, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mla_verify_kernel(MlaArgs a) {
+  constexpr int kRingTile = FP8 ? kTileBytes8 : kTileBytes;
+  constexpr int kLoadsPerTile = kRingTile / 1024;                  // 36 or 18
+  constexpr int kLoadsPerPage = kLoadsPerTile / 2;
+  // bf16: 4 waves x 9 loads; fp8: waves 0 and 1 load one page (9 loads) each,
+  // so every issuing wave has the same count for its vmcnt bookkeeping.
+  constexpr int kIssueWaves = FP8 ? 2 : 4;
+  constexpr int kStageOff = NS * kRingTile;                         // fp8 -> bf16 tile
+  constexpr int kLoadsPerWave = kLoadsPerTile / kIssueWaves;
+  static_assert(kLoadsPerWave * kIssueWaves == kLoadsPerTile, "even load split");
+  constexpr int kFlagOff = kStageOff + (FP8 ? kTileBytes : 0);     // 2 pass flags
+  constexpr int kLdsBytes = kFlagOff + 16;
+  __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
+  PD_LDS char* lds = (PD_LDS char*)smem;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int g2 = lane >> 5;
+  const int S = a.S;
+  const bool direct = S == 1;
+
+  // ---- which (request, split, row block): XCD-aware remap ---------------
+  // Hardware hands consecutive workgroup ids to the 8 XCDs round-robin;
+  // remapping gives every XCD a contiguous range of logical ids, so the row
+  // blocks of one (request, split) share an XCD and its L2.
+  const int n_wg = gridDim.x;
+  int id = blockIdx.x;
+  const int per_xcd = n_wg / 8;
+  if (id < per_xcd * 8) id = (id % 8) * per_xcd + id / 8;
+  const int rows_req = a.qlen * a.H;
+  const int n_rb = (rows_req + kRowsPerBlock - 1) / kRowsPerBlock;
+  // (integer division runs on the VALU: pin the results to SGPRs)
+  const int rb = __builtin_amdgcn_readfirstlane(id % n_rb);
+  const int split = __builtin_amdgcn_readfirstlane((id / n_rb) % S);
+  const int b = __builtin_amdgcn_readfirstlane(id / n_rb / S);
+
+  // ---- rows of this lane and their causal limits ------------------------
+  int L = as_const(a.seq_lens)[b];
+  L = min(max(L, 0), a.max_blocks * a.P);
+  const int Lr = a.real_lens != nullptr ? as_const(a.real_lens)[b] : L;
+  const int my_row = rb * kRowsPerBlock + wave * kRowsPerWave + l32;
+  const bool row_ok = my_row < rows_req;
+  const int t_row = row_ok ? my_row / a.H : 0;
+  const int h_row = row_ok ? my_row % a.H : 0;
+  const int hi_row = row_ok ? max(min(L - a.qlen + 1 + t_row, Lr), 0) : 0;
+  const int last_row = min(rb * kRowsPerBlock + kRowsPerBlock, rows_req) - 1;
+  const int hi_blk = __builtin_amdgcn_readfirstlane(max(min(L - a.qlen + 1 + last_row / a.H, Lr), 0));
+  const int n_tiles = (hi_blk + kTileTokens - 1) / kTileTokens;
+  int chunk = 1, active = 0;
+  if (n_tiles > 0) {
+    chunk = __builtin_amdgcn_readfirstlane(max((n_tiles + S - 1) / S, kMlaMinSplitTiles));
+    active = __builtin_amdgcn_readfirstlane((n_tiles + chunk - 1) / chunk);
+  }
+  const int64_t q_row = (int64_t)b * a.qlen + t_row;
+
+  if (split >= active) {
+    if (row_ok) {
+      if (direct) {
+        uint16_t* orow = a.out + q_row * a.o_srow + (int64_t)h_row * a.o_sh;
+        for (int d = g2 * 8; d < kLv; d += 16) *(u32x4*)(orow + d) = u32x4{0, 0, 0, 0};
+        if (a.lse != nullptr && g2 == 0) a.lse[q_row * a.lse_srow + h_row] = neg_inf();
+      } else if (g2 == 0) {
+        a.ws[((q_row * a.H + h_row) * S + split) * (kLv + 1) + kLv] = neg_inf();
+      }
+    }
+    return;
+  }
+
+  const int tb = split * chunk;
+  const int te = min(tb + chunk, n_tiles);
+  const int n = te - tb;
+  const int pg_hi = __builtin_amdgcn_readfirstlane((hi_blk + a.P - 1) / a.P);
+
+  float kscale = 1.f;
+  if constexpr (FP8) {
+    if (a.k_scale != nullptr) kscale = a.k_scale[0];
+  }
+  const float c = a.scale_log2 * kscale;   // log2-domain scale of raw scores
+
+  // ---- Q fragment: B operand of S^T = K Q^T (32 rows x 576 dims) --------
+  bf16x8 qf[kKSteps];
+  {
+    const uint16_t* qp = a.q + q_row * a.q_srow + (int64_t)h_row * a.q_sh + 8 * g2;
+#pragma unroll
+    for (int kk = 0; kk < kKSteps; ++kk) {
+      u32x4 v = *(const u32x4*)(qp + 16 * kk);
+      if (!row_ok) v = u32x4{0, 0, 0, 0};
+      qf[kk] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  const char* kv = (const char*)a.kv;
+  const int elem = FP8 ? 1 : 2;
+  const int64_t sp_bytes = a.kv_sp * elem;
+  const int64_t st_bytes = a.kv_st * elem;
+  const PD_CONST int32_t* bt_row = as_const(a.bt) + (int64_t)b * a.bt_sb;
+  bool bad = false;
+
+  // Issue this wave's share of the HBM->LDS loads of tile T into slot:
+  // issuing wave w loads page w / (waves per page), instructions
+  // (w % waves per page) * kLoadsPerWave + j of that page.
+  constexpr int kWavesPerPage = kIssueWaves / 2;
+  const int my_page = wave / kWavesPerPage;
+  const int i0 = (wave % kWavesPerPage) * kLoadsPerWave;   // first instruction of this wave
+  const uint32_t lane_off = (uint32_t)((FP8 ? (lane & 15) : ((lane & 15) ^ (4 * ((lane >> 4) & 1)))) *
+                                       st_bytes) + 16u * (uint32_t)(lane >> 4);
+  auto issue = [&](int T, int slot) {
+    // both pages of the tile are checked by every wave (indices < pg_hi), so
+    // the invalid-entry flag is workgroup-uniform
+    int pid[2];
+    bool pok[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int pidx = 2 * T + j;
+      pok[j] = pidx < pg_hi;
+      pid[j] = pok[j] ? bt_row[pidx] : 0;
+      if (pok[j] && (pid[j] < 0 || pid[j] >= a.num_pages)) {
+        bad = true;
+        pok[j] = false;
+      }
+    }
+    const bool ok = (my_page & 1) ? pok[1] : pok[0];
+    const int my_pid = (my_page & 1) ? pid[1] : pid[0];
+    if (wave >= kIssueWaves || !ok) return;
+    // instruction i of a page covers 16-byte slots [64 i, 64 i + 64): chunk
+    // columns 4 i .. 4 i + 3, i.e. 64 more bytes into every row
+    const char* base = kv + (int64_t)my_pid * sp_bytes + 64 * i0;
+    PD_LDS char* dst = lds + slot * kRingTile + my_page * (FP8 ? kPageRegion8 : kPageRegion) + i0 * 1024;
+#pragma unroll
+    for (int j = 0; j < kLoadsPerWave; ++j)
+      global_to_lds_16(base + 64 * j, lane_off, lds_addr(dst + j * 1024));
+  };
+
+  float m_seen = neg_inf();   // exact running max of this lane's row
+  float m_ref = neg_inf();    // fixed reference of the current pass
+  float l_run = 0.f;
+  f32x16 o[kVBlocks];
+  PD_LDS int* pass_flag = (PD_LDS int*)(lds + kFlagOff);
+  if (tid < 2) pass_flag[tid] = 0;   // ordered before use by the first tile barrier
+
+  // lane-constant parts of the transpose-read addresses
+  const int q16 = lane >> 4;
+  const int L16 = lane & 15;
+  const int vrow = 4 * (q16 >> 1) + (L16 >> 2);          // + 16 s (+ 8): rows 0..15 of a page
+  const int vcol0 = 16 * (q16 & 1) + 4 * (L16 & 3);      // + 32 blk
+  // byte offset of this lane's first transpose read (step 0, block 0, read a)
+  const int vcc0 = vcol0 >> 3;                           // chunk column
+  const uint32_t vlane_off = (uint32_t)(tile_slot(vcc0, vrow) * 16 + (vcol0 & 7) * 2);
+
+  for (int pass = 0; pass < 2; ++pass) {
+  // pass 1 only runs if pass 0 saw a score too far above its reference
+  m_ref = pass == 0 ? neg_inf() : m_seen;
+  l_run = 0.f;
+  bool overflow = false;
+#pragma unroll
+  for (int i = 0; i < kVBlocks; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[i][e] = 0.f;
+#pragma unroll
+  for (int k = 0; k < NS - 1; ++k)
+    if (k < n) issue(tb + k, k);
+
+  for (int k = 0; k < n; ++k) {
+    const int kn = k + NS - 1;
+    if (kn - 1 >= n - 1)
+      wait_vmcnt<0>();
+    else
+      wait_vmcnt<kLoadsPerWave * (NS - 2)>();
+    __syncthreads();  // tile k is in LDS; every wave is done with tile k-1
+    PD_LDS char* tl;
+    if constexpr (FP8) {
+      // exact fp8 -> bf16 into the staging tile: item = (page, fp8 chunk
+      // column c8, row r16) -> bf16 chunk columns 2 c8 and 2 c8 + 1
+      PD_LDS char* src = lds + (k % NS) * kRingTile;
+      tl = lds + kStageOff;
+      for (int i = tid; i < 2 * 36 * 16; i += kWaves * 64) {
+        const int r16 = i & 15;
+        const int c8 = (i >> 4) % 36;
+        const int pg = i / (36 * 16);
+        const u32x4 w = *(PD_LDS u32x4*)(src + pg * kPageRegion8 + (16 * c8 + r16) * 16);
+        PD_LDS char* dpg = tl + pg * kPageRegion;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          u32x4 cv;
+          cv[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * h], 1.f, false));
+          cv[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * h], 1.f, true));
+          cv[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * h + 1], 1.f, false));
+          cv[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * h + 1], 1.f, true));
+          *(PD_LDS u32x4*)(dpg + tile_slot(2 * c8 + h, r16) * 16) = cv;
+        }
+      }
+      __syncthreads();
+    } else {
+      tl = lds + (k % NS) * kRingTile;
+    }
+    if (kn < n) issue(tb + kn, kn % NS);
+
+    const int tok0 = (tb + k) * kTileTokens;
+
+    // ---- scores S^T[token, row] over all 576 dims -------------------------
+    // K fragments in batches of kKBatch read ahead of their MFMAs; two
+    // independent accumulation chains
+    f32x16 sacc, sacc2;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sacc[e] = sacc2[e] = 0.f;
+    {
+      PD_LDS char* kpage = tl + (l32 >> 4) * kPageRegion;
+      const int r16 = l32 & 15;
+#pragma unroll
+      for (int b0 = 0; b0 < kKSteps; b0 += kKBatch) {
+        bf16x8 kf[kKBatch];
+#pragma unroll
+        for (int i = 0; i < kKBatch; ++i)
+          kf[i] = *(PD_LDS bf16x8*)(kpage + tile_slot(g2 + 2 * (b0 + i), r16) * 16);
+#pragma unroll
+        for (int i = 0; i < kKBatch; ++i) {
+          if (i & 1)
+            sacc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[b0 + i], sacc2, 0, 0, 0);
+          else
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[b0 + i], sacc, 0, 0, 0);
+        }
+      }
+    }
+    float x[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) x[e] = (sacc[e] + sacc2[e]) * c;
+    // causal limit of this lane's row: token tok0 + 8j + 4 g2 + i < hi_row
+    if (tok0 + kTileTokens > hi_row) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int tok = tok0 + 8 * (e >> 2) + 4 * g2 + (e & 3);
+        if (tok >= hi_row) x[e] = neg_inf();
+      }
+    }
+
+    // ---- online softmax against the fixed row reference ----
+    float mt = x[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mt = fmaxf(mt, x[e]);
+    mt = fmaxf(mt, shfl_xor(mt, 32));
+    m_seen = fmaxf(m_seen, mt);
+    // first non-empty tile of the row: take its max as the reference (the
+    // accumulator and l are still exactly 0, so nothing needs rescaling)
+    if (m_ref == neg_inf()) m_ref = mt;
+    overflow |= mt - m_ref > kRefHeadroomLog2;           // false while -inf
+    const float mref = m_ref == neg_inf() ? 0.f : m_ref;
+    float p[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      p[e] = fast_exp2(x[e] - mref);
+      l_run += p[e];
+    }
+    bf16x8 pb[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const u32x4 w = {pack_bf16x2(p[8 * st + 0], p[8 * st + 1]), pack_bf16x2(p[8 * st + 2], p[8 * st + 3]),
+                       pack_bf16x2(p[8 * st + 4], p[8 * st + 5]), pack_bf16x2(p[8 * st + 6], p[8 * st + 7])};
+      pb[st] = __builtin_bit_cast(bf16x8, w);
+    }
+
+    // ---- O^T += V^T P^T over all 512 output dims ----
+    const bool vedge = tok0 + kTileTokens > hi_blk;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      u32x4 vkeep = {~0u, ~0u, ~0u, ~0u};
+      if (vedge) {
+        const int ta = tok0 + 16 * st + 4 * g2;    // first of the 4 tokens of read a
+        const int tbk = ta + 8;
+        vkeep = u32x4{keep_mask(ta + 0 < hi_blk, ta + 1 < hi_blk), keep_mask(ta + 2 < hi_blk, ta + 3 < hi_blk),
+                      keep_mask(tbk + 0 < hi_blk, tbk + 1 < hi_blk), keep_mask(tbk + 2 < hi_blk, tbk + 3 < hi_blk)};
+      }
+#pragma unroll
+      for (int b0 = 0; b0 < kVBlocks; b0 += kVBatch) {
+        u32x4 vop[kVBatch];
+#pragma unroll
+        for (int i = 0; i < kVBatch; ++i) {
+          // read a: rows vrow.., read b: rows vrow + 8.. (slot + 8); block
+          // blk is 4 chunk columns (1 KB) further; step st is the next page
+          PD_LDS char* pa = tl + vlane_off + st * kPageRegion + (b0 + i) * 1024;
+          bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((PD_LDS bf16x4*)pa);
+          bf16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((PD_LDS bf16x4*)(pa + 128));
+          const u32x2 ua = __builtin_bit_cast(u32x2, va);
+          const u32x2 ub = __builtin_bit_cast(u32x2, vb);
+          vop[i] = u32x4{ua[0], ua[1], ub[0], ub[1]} & vkeep;
+        }
+#pragma unroll
+        for (int i = 0; i < kVBatch; ++i)
+          o[b0 + i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vop[i]), pb[st],
+                                                              o[b0 + i], 0, 0, 0);
+      }
+    }
+  }
+  // every wave is past its last LDS read of this pass; agree on a rerun
+  if (__ballot(overflow) != 0ull && lane == 0) pass_flag[pass] = 1;
+  __syncthreads();
+  if (pass_flag[pass] == 0) break;
+  }
+
+  // ---- epilogue: each wave writes its own 32 rows -------------------------
+  l_run += shfl_xor(l_run, 32);
+  if (!row_ok) return;
+  const bool empty = !(l_run > 0.f);
+  const float qnan = __builtin_nanf("");
+  const float lse_nat = empty ? neg_inf() : (m_ref + fast_log2(l_run)) * kLn2;
+  if (direct) {
+    const float inv = empty ? 0.f : kscale / l_run;
+    uint16_t* orow = a.out + q_row * a.o_srow + (int64_t)h_row * a.o_sh;
+#pragma unroll
+    for (int blk = 0; blk < kVBlocks; ++blk)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = 32 * blk + 8 * j + 4 * g2;
+        float x0 = o[blk][4 * j + 0] * inv, x1 = o[blk][4 * j + 1] * inv;
+        float x2 = o[blk][4 * j + 2] * inv, x3 = o[blk][4 * j + 3] * inv;
+        if (bad) x0 = x1 = x2 = x3 = qnan;
+        *(u32x2*)(orow + d) = u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+      }
+    if (a.lse != nullptr && g2 == 0) a.lse[q_row * a.lse_srow + h_row] = bad ? qnan : lse_nat;
+  } else {
+    const float inv = empty ? 0.f : kscale / l_run;
+    float* slot = a.ws + ((q_row * a.H + h_row) * S + split) * (kLv + 1);
+    float* oslot = slot;
+#pragma unroll
+    for (int blk = 0; blk < kVBlocks; ++blk)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = 32 * blk + 8 * j + 4 * g2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) oslot[d + i] = bad ? qnan : o[blk][4 * j + i] * inv;
+      }
+    if (g2 == 0) slot[kLv] = bad ? qnan : lse_nat;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_mla_verify(const MlaArgs& a, hipStream_t stream) {
+  const int rows_req = a.qlen * a.H;
+  const int n_rb = (rows_req + kRowsPerBlock - 1) / kRowsPerBlock;
+  const int64_t n_wg = (int64_t)a.B * a.S * n_rb;
+  if (n_wg == 0) return hipSuccess;
+  if (n_wg > 0x7fffffff) return hipErrorInvalidValue;
+  dim3 grid((unsigned)n_wg), block(kWaves * 64);
+  if (a.kv_fp8)
+    hipLaunchKernelGGL((mla_verify_kernel<3, true>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((mla_verify_kernel<3, false>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace pd
