@@ -39,6 +39,9 @@ def _parse():
     p.add_argument("--config", default="gqa_sinks")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--splits", type=int, default=0, help="override the split cap")
+    p.add_argument("--calib-copy-mib", type=int, default=0,
+                   help="after timing, run one plain device copy of this many MiB (a "
+                        "known-size reference for hardware byte counters)")
     return p.parse_args()
 
 
@@ -105,6 +108,32 @@ def _mla_case(fp8, torch, pd, splits):
     return dict(w=w, vals=vals, S=S, step=step, kernel=None, rest=None,
                 kv_bytes=w.kv_bytes(1 if fp8 else 2), flops=w.flops(), desc=desc,
                 kind="mla_fp8" if fp8 else "mla", kernel_name="mla_verify_kernel")
+
+
+def _profiled_traffic(kernel, config):
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (profiles/<kernel>__<config>.md: calibrated FETCH_SIZE + WRITE_SIZE), or
+    None when there is none or the kernel's sources changed since."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"{kernel}__{config}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.split(":", 1)[0] in (
+                "traffic_bytes_per_launch", "kernel_source_sha256_16", "kernel_sources"):
+            k, v = line.split(":", 1)
+            fields[k] = v.strip()
+    try:
+        h = hashlib.sha256()
+        for f in fields["kernel_sources"].split():
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+        if h.hexdigest()[:16] != fields["kernel_source_sha256_16"]:
+            return None
+        return int(float(fields["traffic_bytes_per_launch"]))
+    except (KeyError, OSError, ValueError):
+        return None
 
 
 def _cpu_baseline(case, budget_s=20.0):
@@ -222,9 +251,19 @@ def main():
         roof = {"bound": "mfma", "achieved": round(case["flops"] / (k_ms * 1e-3) / 1e12, 2),
                 "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
+    roof["traffic"] = _profiled_traffic(case["kernel_name"], name)
     roof["kernel"] = case["kernel_name"]
     roof["kernel_us"] = round(k_ms * 1e3, 2)
+
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"# calibration copy: {n} bytes read, {n} bytes written", file=sys.stderr)
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:
