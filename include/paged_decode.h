@@ -28,6 +28,9 @@
  *   capacity (max_blocks * page_size) is clamped to it, and an attended
  *   block-table entry outside [0, num_pages) is never dereferenced: the
  *   affected (request, head) outputs are written as NaN instead.
+ * - sm_scale must be finite and > 0 (the GQA kernel keeps its running
+ *   maximum in unscaled scores, which orders them only for a positive
+ *   scale); any other value returns PD_ERR_INVALID.
  * - bf16 values are IEEE binary32 truncated to their upper 16 bits (round to
  *   nearest even on output); FP8 is OCP E4M3FN.
  *

@@ -102,7 +102,7 @@ static int gqa_common(const void* q, int64_t q_stride_b, int64_t q_stride_h, con
                size_t workspace_bytes, void* out, int64_t o_stride_b, int64_t o_stride_h,
                float* lse, int64_t lse_stride_b, void* stream, bool partials_only) {
   if (batch < 0 || num_q_heads < 1 || num_kv_heads < 1 || num_kv_splits < 1 ||
-      num_pages < 0 || max_blocks < 0 || !std::isfinite(sm_scale))
+      num_pages < 0 || max_blocks < 0 || !std::isfinite(sm_scale) || !(sm_scale > 0.f))
     return PD_ERR_INVALID;
   if (num_q_heads % num_kv_heads != 0) return PD_ERR_INVALID;
   const int32_t G = num_q_heads / num_kv_heads;
@@ -217,7 +217,7 @@ int paged_verify_mla(const void* q, int64_t q_stride_row, int64_t q_stride_h, co
                      size_t workspace_bytes, void* out, int64_t o_stride_row,
                      int64_t o_stride_h, float* lse, int64_t lse_stride_row, void* stream) {
   if (batch < 0 || qlen < 1 || num_heads < 1 || num_kv_splits < 1 || num_pages < 0 ||
-      max_blocks < 0 || !std::isfinite(sm_scale))
+      max_blocks < 0 || !std::isfinite(sm_scale) || !(sm_scale > 0.f))
     return PD_ERR_INVALID;
   if (kv_dtype != PD_KV_BF16 && kv_dtype != PD_KV_FP8_E4M3FN) return PD_ERR_INVALID;
   if (head_dim_k != 576 || head_dim_v != 512 || page_size != 16 ||

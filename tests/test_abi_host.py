@@ -122,6 +122,8 @@ def test_gqa_argument_checks_happen_before_any_hip_call():
     assert _gqa(Hq=60) == PD_ERR_INVALID                      # Hq % Hkv
     assert _gqa(B=-1) == PD_ERR_INVALID
     assert _gqa(scale=float("nan")) == PD_ERR_INVALID
+    assert _gqa(scale=0.0) == PD_ERR_INVALID                  # softmax scale must be > 0
+    assert _gqa(scale=-0.088) == PD_ERR_INVALID
     assert _gqa(D=64) == PD_ERR_UNSUPPORTED
     assert _gqa(P=8) == PD_ERR_UNSUPPORTED
     assert _gqa(Hq=136, Hkv=8) == PD_ERR_UNSUPPORTED          # G = 17
@@ -148,6 +150,7 @@ def test_mla_argument_checks_happen_before_any_hip_call():
     assert _mla(kv=NULL) == PD_ERR_INVALID
     assert _mla(qlen=0) == PD_ERR_INVALID
     assert _mla(dt=7) == PD_ERR_INVALID
+    assert _mla(scale=-0.07) == PD_ERR_INVALID
     assert _mla(Lk=512) == PD_ERR_UNSUPPORTED
     assert _mla(Lv=256) == PD_ERR_UNSUPPORTED
     assert _mla(P=32) == PD_ERR_UNSUPPORTED
