@@ -20,7 +20,7 @@ from ._native import PD_KV_BF16, PD_KV_FP8_E4M3FN, check, lib
 GQA_OCCUPANCY = 1.0          # resident decode workgroups per CU (128 KB LDS each)
 GQA_MIN_WORK = 256           # keys per split before a request uses fewer splits
 GQA_MAX_SPLITS = 64
-GQA_BALANCE_CHUNK = 2048     # skew bound: no split of the longest request above this
+GQA_BALANCE_CHUNK = 1024     # skew bound: pieces of the longest request may be this short
 MLA_BLOCK_H = 128            # verify rows (qlen * heads) per workgroup
 MLA_OCCUPANCY = 1.0
 MLA_MIN_WORK = 128

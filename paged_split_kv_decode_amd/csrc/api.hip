@@ -127,17 +127,25 @@ static int gqa_common(const void* q, int64_t q_stride_b, int64_t q_stride_h, con
     if (!aligned16(workspace)) return PD_ERR_ALIGN;
   }
   if (num_kv_heads > 65535 || batch > 65535 || num_kv_splits > 65535) return PD_ERR_UNSUPPORTED;
+  const int64_t kLim = INT32_MAX;
+  if (q_stride_b > kLim || q_stride_h > kLim || kv_stride_page > kLim || kv_stride_head > kLim ||
+      bt_stride_b > kLim || o_stride_b > kLim || o_stride_h > kLim || lse_stride_b > kLim)
+    return PD_ERR_UNSUPPORTED;
+  // the kernel indexes all (request, kv head, 32-token tile) triples with int32
+  if ((int64_t)max_blocks * page_size > (int64_t)INT32_MAX / 2 ||
+      (int64_t)batch * num_kv_heads * cdiv64((int64_t)max_blocks * page_size, 32) > INT32_MAX / 2)
+    return PD_ERR_UNSUPPORTED;
 
   pd::GqaArgs a{};
   a.q = static_cast<const uint16_t*>(q);
-  a.q_sb = q_stride_b;
-  a.q_sh = q_stride_h;
+  a.q_sb = (int32_t)q_stride_b;
+  a.q_sh = (int32_t)q_stride_h;
   a.kv = static_cast<const uint16_t*>(kv);
-  a.kv_sp = kv_stride_page;
-  a.kv_sh = kv_stride_head;
+  a.kv_sp = (int32_t)kv_stride_page;
+  a.kv_sh = (int32_t)kv_stride_head;
   a.num_pages = num_pages;
   a.bt = block_table;
-  a.bt_sb = bt_stride_b;
+  a.bt_sb = (int32_t)bt_stride_b;
   a.max_blocks = max_blocks;
   a.seq_lens = seq_lens;
   a.sinks = sinks;
@@ -152,10 +160,10 @@ static int gqa_common(const void* q, int64_t q_stride_b, int64_t q_stride_h, con
   a.partials = partials_only ? 1 : 0;
   a.ws = workspace;
   a.out = static_cast<uint16_t*>(out);
-  a.o_sb = o_stride_b;
-  a.o_sh = o_stride_h;
+  a.o_sb = (int32_t)o_stride_b;
+  a.o_sh = (int32_t)o_stride_h;
   a.lse = lse;
-  a.lse_sb = lse_stride_b;
+  a.lse_sb = (int32_t)lse_stride_b;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (pd::launch_gqa_decode(a, s) != hipSuccess) return PD_ERR_HIP;
   if (num_kv_splits > 1 && !partials_only) {

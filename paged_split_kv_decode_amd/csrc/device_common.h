@@ -83,6 +83,19 @@ __device__ __forceinline__ void global_to_lds_16(const void* base, uint32_t voff
       : "s"(lds_addr), "v"(voff), "s"(base)
       : "memory", "m0");
 }
+// Same, with the LDS address given as a wave-uniform base plus a constant
+// byte offset that is added inside the asm, so a run of loads into one LDS
+// buffer keeps a single base in a scalar register.
+template <uint32_t kOff>
+__device__ __forceinline__ void global_to_lds_16_at(const void* base, uint32_t voff, uint32_t lds_base) {
+  asm volatile(
+      "s_add_u32 m0, %0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2"
+      :
+      : "s"(lds_base), "v"(voff), "s"(base), "i"(kOff)
+      : "memory", "m0", "scc");
+}
 #pragma clang diagnostic pop
 
 __device__ __forceinline__ uint32_t lds_addr(PD_LDS const void* p) {

@@ -1,38 +1,43 @@
 // Paged GQA split-KV decode for gfx950 (one query token per request).
 //
 // Operation: "vllm.models.flint.ops.decode_attention", flint_decode_attention
-// and _FlintDecodeAttention.kernel (page range of a request, sliding-window
-// start, per-split page interleave, intra-workgroup combine, sink in the final
-// denominator); block-table addressing as in "Atención paginada", decode path.
+// and _FlintDecodeAttention.kernel (key range of a request, sliding-window
+// start, per-split partials, sink in the final denominator); block-table
+// addressing as in "Atención paginada", section "Ruta de decodificación".
 //
-// Design on CDNA4
-// ---------------
-// * One workgroup of 4 waves per (split, kv head, request).  The split's
-//   32-token tiles are interleaved over the waves; each wave streams its
-//   tiles through a private 2-stage LDS ring and keeps its own online-softmax
-//   state, so the hot loop needs no workgroup barrier.
-// * Page gather: a tile is 32 token rows of [K | V] (512 B each, 16 KB per
-//   tile).  Each wave moves it with 16 `global_load_lds_dwordx4`
-//   instructions (1 KB per instruction, HBM -> LDS with no VGPR staging);
-//   the physical page of every row comes from the block table with scalar
-//   loads.  16-byte chunks are XOR-swizzled per row so the MFMA operand reads
-//   below are bank-conflict free.
+// Design on CDNA4: a persistent, length-balanced stream
+// -----------------------------------------------------
+// * Work unit = (request b, kv head); its keys are cut into 32-token tiles
+//   (tile t covers positions [32t, 32t + 32), clipped to the request's key
+//   range).  All units' tiles, request-major then kv-head-major, form one
+//   flat sequence of U tiles.  The grid is one 4-wave workgroup per compute
+//   unit, and every wave takes an equal contiguous share of that sequence
+//   (tpw tiles), so the waves finish together whatever the length mix.
+// * A wave streams its share as one pipeline that runs straight across unit
+//   boundaries: it has a private 2-stage ring of 16 KB tiles in LDS and
+//   issues tile k+1 (16 `global_load_lds_dwordx4`, 1 KB each, HBM -> LDS
+//   with no VGPR staging) while it computes tile k.  The physical page of
+//   each tile row comes from the block table through scalar loads made one
+//   tile ahead of their use, so their latency is hidden.  No workgroup
+//   barrier exists anywhere: the waves share nothing but the CU.
+// * Where a wave's share cuts a unit, each piece is a split: the wave writes
+//   its fp32 partial (O / l, lse) to the piece's slot, and the merge kernel
+//   combines them.  With the split cap S >= 2 the share size is raised
+//   until no unit spans more than S waves; the wave that holds a unit's
+//   first tile marks the unit's unused slots with lse = -inf.  With S == 1
+//   shares are rounded to whole units and the wave writes O and LSE
+//   directly.
 // * Scores S^T[token, head] = K . Q^T on v_mfma_f32_16x16x32_bf16 with the
-//   query heads of the kv head in the N dimension (G <= 16, padded with zero
-//   heads).  Each lane then holds 8 scores of one head.
-// * Online softmax in fp32 with exp2 and a running max in unscaled logits;
-//   the max is reduced over the 4 lanes of a head with two lane exchanges,
-//   the row sum is kept per lane and reduced once at the end.
-// * P is rounded to bf16 and is already in the B-operand layout of the
-//   P.V product O^T[d, head] += V^T . P^T; V^T comes from the LDS tile with
-//   `ds_read_b64_tr_b16` (transposing 4x16 bf16 blocks on the fly).
+//   G query heads of the kv head in the N dimension (G <= 16, zero-padded).
+//   Online softmax in fp32 with exp2 and a running max in unscaled logits,
+//   reduced over the 4 lanes of a head with two lane exchanges.  P (bf16)
+//   is already in the B-operand layout of O^T[d, head] += V^T . P^T, and
+//   V^T is read from the LDS tile with ds_read_b64_tr_b16.
 // * Keys outside [lo, hi) get a -inf score and a zero V (select, never a
-//   multiply), so stale or NaN cache contents never reach the output.
-// * The waves' (m, l, O) are combined through LDS; a single split writes
-//   bf16 O and LSE, several splits write fp32 (O/l, lse) partials for the
-//   merge kernel.
-#include <cstdlib>
-#include <cstring>
+//   multiply), so stale or NaN cache contents never reach the output.  A
+//   block-table entry outside [0, num_pages) is never dereferenced: its
+//   rows are loaded from a harmless address and the piece's result is NaN.
+#include <utility>
 
 #include "device_common.h"
 #include "kernels.h"
@@ -41,11 +46,13 @@ namespace pd {
 namespace {
 
 constexpr int kD = 128;
+constexpr int kNW = 4;                                  // waves per workgroup
 constexpr int kRowBytes = 2 * kD * 2;                   // K|V row of one token
 constexpr int kTileBytes = kTileTokens * kRowBytes;     // 16 KB
 constexpr int kLoadsPerTile = kTileBytes / (64 * 16);   // 16 wave loads
-constexpr int kCombHeadStride = kD + 4;                 // floats, padded
-constexpr int kCombWaveFloats = 16 * kCombHeadStride + 48;
+constexpr int kRingBytes = 2 * kTileBytes;              // per wave
+// Smallest share a wave takes: below it the per-wave start-up dominates.
+constexpr int kMinWaveTiles = 4;
 
 // 16-byte chunk c of token row r is stored at chunk c ^ swz(r).  Rows
 // 0..7 get distinct low-3-bit patterns (K reads: 8 consecutive rows, same
@@ -57,319 +64,519 @@ __device__ __forceinline__ uint32_t keep_mask(bool lo_ok, bool hi_ok) {
   return (lo_ok ? 0x0000FFFFu : 0u) | (hi_ok ? 0xFFFF0000u : 0u);
 }
 
-// kNW waves per workgroup, kNS ring stages (tiles) per wave.
-template <int P, int kNW, int kNS>
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __builtin_amdgcn_ds_bpermute((lane_id() ^ m) << 2, v);
+  return v;
+}
+__device__ __forceinline__ int wave_max(int v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = max(v, __builtin_amdgcn_ds_bpermute((lane_id() ^ m) << 2, v));
+  return v;
+}
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ int wave_incl_sum(int v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __builtin_amdgcn_ds_bpermute((lane >= d ? lane - d : lane) << 2, v);
+    if (lane >= d) v += y;
+  }
+  return v;
+}
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Key range of one request: positions [lo, hi), tiles lo / 32 ... lo / 32 + nt - 1.
+struct Req {
+  int lo, hi, nt;
+};
+
+// Key range of a request of length L (clamped to the block-table row).
+template <int P>
+__device__ __forceinline__ Req range_of(const GqaArgs& a, int L) {
+  L = min(max(L, 0), a.max_blocks * P);
+  Req r;
+  r.hi = L;
+  r.lo = a.window > 0 ? max(L - a.window, 0) : 0;
+  r.nt = r.hi > r.lo ? ((r.hi + 31) >> 5) - (r.lo >> 5) : 0;
+  return r;
+}
+
+template <int P>
+__device__ __forceinline__ Req request_range(const GqaArgs& a, int b) {
+  return range_of<P>(a, as_const(a.seq_lens)[b]);
+}
+
+// A position in one wave's tile sequence (wave-uniform).  b == B: the share
+// is done.
+struct Cursor {
+  int b, kvh;   // unit
+  int p0;       // flat index of the unit's first tile
+  int i, i_end; // current tile of the unit, end of this wave's piece of it
+  Req r;
+};
+
+// The wave's share of the flat tile sequence.
+struct Share {
+  int g0, g1;   // [g0, g1): raw share (the last used wave also owns every unit past g1)
+  int tpw;
+  bool last;
+  bool split;   // S >= 2: pieces may cut units; S == 1: whole units only
+};
+
+constexpr int kQSlotBytes = 16 * kD * 2;                 // query rows of one piece (G <= 16)
+constexpr int kWaveLds = kRingBytes + 2 * kQSlotBytes;    // ring + 2 query slots = 40 KB
+constexpr int kCachedChunks = 4;                          // request lengths kept in registers (x64)
+
+template <int P>
 __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
-  constexpr int kLdsBytes = kNW * kNS * kTileBytes;
-  static_assert(kLdsBytes >= kNW * kCombWaveFloats * 4, "combine buffer must fit the ring");
-  __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
-  PD_LDS char* lds = (PD_LDS char*)smem;
+  __shared__ __attribute__((aligned(1024))) char smem[kNW * kWaveLds];
 
   const int tid = threadIdx.x;
-  // wave index as an SGPR value: everything derived from it stays scalar
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_in_wg = uniform(tid >> 6);
   const int lane = tid & 63;
   const int g4 = lane >> 4;
   const int l16 = lane & 15;
-  const int split = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int b = blockIdx.z;
   const int G = a.G;
   const int S = a.S;
-  const bool direct = S == 1 && !a.partials;   // write O / LSE, no workspace
-  const int hq0 = kvh * G;
+  const int Hkv = a.Hkv;
+  const bool direct = S == 1 && !a.partials;
   const float c = a.scale_log2;
+  const int n_waves = gridDim.x * kNW;
+  const int w = uniform(blockIdx.x * kNW + wave_in_wg);
+  PD_LDS char* ring = (PD_LDS char*)smem + wave_in_wg * kWaveLds;
+  PD_LDS char* qslots = ring + kRingBytes;
 
-  // ---- key range of this request and the split plan --------------------
-  int L = as_const(a.seq_lens)[b];
-  L = min(max(L, 0), a.max_blocks * P);
-  const int hi = L;
-  const int lo = a.window > 0 ? max(hi - a.window, 0) : 0;
-  const int t_first = lo >> 5;
-  const int n_tiles = hi > lo ? ((hi + 31) >> 5) - t_first : 0;
-  int chunk = 1, active = 0;
-  if (n_tiles > 0) {
-    // (integer division runs on the VALU: pin the results to SGPRs)
-    chunk = __builtin_amdgcn_readfirstlane(max((n_tiles + S - 1) / S, kGqaMinSplitTiles));
-    active = __builtin_amdgcn_readfirstlane((n_tiles + chunk - 1) / chunk);
-  }
-
-  if (split >= active) {
-    // Nothing to attend in this slot: zeros / -inf (direct), or an empty
-    // partial (lse = -inf) for the merge.
-    if (direct) {
-      for (int i = tid; i < G * (kD / 8); i += kNW * 64) {
-        const int h = i / (kD / 8), d8 = (i % (kD / 8)) * 8;
-        *(u32x4*)(a.out + (int64_t)b * a.o_sb + (int64_t)(hq0 + h) * a.o_sh + d8) = u32x4{0, 0, 0, 0};
-      }
-      if (a.lse != nullptr && tid < G) a.lse[(int64_t)b * a.lse_sb + hq0 + tid] = neg_inf();
-    } else if (tid < G) {
-      a.ws[((int64_t)(b * a.Hq + hq0 + tid) * S + split) * (kD + 1) + kD] = neg_inf();
-    }
-    return;
-  }
-
-  const int tb = t_first + split * chunk;
-  const int te = min(tb + chunk, t_first + n_tiles);
-  const int nst = te - tb;
-  const int n_w = __builtin_amdgcn_readfirstlane(nst > wave ? (nst - wave + kNW - 1) / kNW : 0);
-  const int pg_lo = lo / P;
-  const int pg_hi = (hi + P - 1) / P;
-
-  // ---- query fragment: B operand of S^T = K Q^T -------------------------
-  bf16x8 qf[4];
-  {
-    const bool hv = l16 < G;
-    const uint16_t* qrow = a.q + (int64_t)b * a.q_sb + (int64_t)(hq0 + (hv ? l16 : 0)) * a.q_sh;
+  // ---- the plan: total tiles, longest request, this wave's share --------
+  // Lane l of chunk c holds the length of request 64c + l (0 past the batch).
+  int Lc[kCachedChunks];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      u32x4 v = *(const u32x4*)(qrow + 8 * g4 + 32 * s);
-      if (!hv) v = u32x4{0, 0, 0, 0};
-      qf[s] = __builtin_bit_cast(bf16x8, v);
-    }
+  for (int ch = 0; ch < kCachedChunks; ++ch) {
+    const int b = 64 * ch + lane;
+    Lc[ch] = b < a.B ? as_const(a.seq_lens)[b] : 0;
   }
+  int nt_sum = 0, nt_max = 0;
+#pragma unroll
+  for (int ch = 0; ch < kCachedChunks; ++ch) {
+    const int nt = range_of<P>(a, Lc[ch]).nt;
+    nt_sum += wave_sum(nt);
+    nt_max = max(nt_max, wave_max(nt));
+  }
+  for (int base = 64 * kCachedChunks; base < a.B; base += 64) {
+    const int nt = base + lane < a.B ? request_range<P>(a, base + lane).nt : 0;
+    nt_sum += wave_sum(nt);
+    nt_max = max(nt_max, wave_max(nt));
+  }
+  nt_sum = uniform(nt_sum);
+  nt_max = uniform(nt_max);
+  const int U = nt_sum * Hkv;
+  Share sh;
+  sh.split = S >= 2;
+  int tpw = max((U + n_waves - 1) / n_waves, kMinWaveTiles);
+  // a unit of n tiles cut every tpw tiles at an arbitrary offset spans at
+  // most floor((n - 1) / tpw) + 2 shares: keep that <= S
+  if (sh.split) tpw = max(tpw, (nt_max - 1) / (S - 1) + 1);
+  sh.tpw = tpw = uniform(tpw);
+  const int w_used = uniform(max((U + tpw - 1) / tpw, 1));
+  if (w >= w_used) return;
+  sh.g0 = w * tpw;
+  sh.last = w == w_used - 1;
+  sh.g1 = sh.last ? U : sh.g0 + tpw;
 
-  const char* kv_head = (const char*)(a.kv + (int64_t)kvh * a.kv_sh);
-  PD_LDS char* ring = lds + wave * kNS * kTileBytes;
-  const PD_CONST int32_t* bt_row = as_const(a.bt) + (int64_t)b * a.bt_sb;
-  bool bad = false;
+  // ---- first unit of the share ------------------------------------------
+  // split: the unit holding tile g0, or an empty unit starting at or after
+  // g0; whole units: the first unit starting at or after g0.
+  int b_s = -1, L_s = 0, cb_s = 0;
+  {
+    int C = 0;  // tiles of the requests before this chunk (one kv head)
+    auto probe = [&](int base, int L) {
+      const bool in = base + lane < a.B;
+      const int nt = range_of<P>(a, L).nt;
+      const int incl = wave_incl_sum(nt);
+      const int cb1 = (C + incl) * Hkv;     // flat start of request b + 1
+      const int cb = cb1 - nt * Hkv;         // flat start of request b
+      const bool pred = in && (sh.split ? (cb1 > sh.g0 || cb >= sh.g0)
+                                        : (cb + (Hkv - 1) * nt >= sh.g0));
+      const uint64_t m = __ballot(pred);
+      if (m != 0) {
+        const int l0 = __builtin_ctzll(m);
+        b_s = base + l0;
+        L_s = __builtin_amdgcn_readlane(L, l0);
+        cb_s = __builtin_amdgcn_readlane(cb, l0);
+        return true;
+      }
+      C += __builtin_amdgcn_readlane(incl, 63);
+      return false;
+    };
+    bool found = false;
+#pragma unroll
+    for (int ch = 0; ch < kCachedChunks; ++ch)
+      if (!found && 64 * ch < a.B) found = probe(64 * ch, Lc[ch]);
+    for (int base = 64 * kCachedChunks; !found && base < a.B; base += 64)
+      found = probe(base, base + lane < a.B ? as_const(a.seq_lens)[base + lane] : 0);
+  }
+  if (b_s < 0) return;
+  b_s = uniform(b_s);
+  const Req r_s = range_of<P>(a, uniform(L_s));
+  int kvh_s = 0;
+  if (sh.g0 > cb_s)
+    kvh_s = sh.split ? (sh.g0 - cb_s) / r_s.nt : (sh.g0 - cb_s + r_s.nt - 1) / r_s.nt;
+  kvh_s = uniform(kvh_s);
+  const int p0_s = uniform(cb_s + kvh_s * r_s.nt);
 
-  // Issue the 16 HBM->LDS loads of tile T into ring slot `slot`.
-  auto issue = [&](int T, int slot) {
-    constexpr int PPT = P >= kTileTokens ? 1 : kTileTokens / P;   // pages per tile
-    PD_LDS char* dst = ring + slot * kTileBytes;
-    const int tok0 = T * kTileTokens;
-    int pid[PPT];
-    bool pok[PPT];
+  // Step to the next unit (no range checks).
+  auto next_unit = [&](Cursor& cu) {
+    cu.p0 += cu.r.nt;
+    if (cu.kvh + 1 < Hkv) {
+      ++cu.kvh;
+    } else {
+      cu.kvh = 0;
+      ++cu.b;
+      if (cu.b < a.B) cu.r = request_range<P>(a, cu.b);
+    }
+  };
+  // Make the cursor point at a tile, skipping empty units; b = B once the
+  // share is done.
+  auto settle = [&](Cursor& cu) {
+    for (;;) {
+      if (cu.b >= a.B || (!sh.last && cu.p0 >= sh.g1)) {
+        cu.b = a.B;
+        return;
+      }
+      if (cu.r.nt > 0) {
+        cu.i = sh.split ? max(sh.g0 - cu.p0, 0) : 0;
+        cu.i_end = sh.split ? min(cu.r.nt, sh.g1 - cu.p0) : cu.r.nt;
+        return;
+      }
+      next_unit(cu);
+    }
+  };
+  // first tile of this wave's piece of the cursor's unit?
+  auto piece_start = [&](const Cursor& cu) { return cu.i == (sh.split ? max(sh.g0 - cu.p0, 0) : 0); };
+  auto advance = [&](Cursor& cu) {
+    if (++cu.i < cu.i_end) return;
+    next_unit(cu);
+    settle(cu);
+  };
+
+  Cursor cc;  // tile being computed
+  cc.b = b_s;
+  cc.kvh = kvh_s;
+  cc.p0 = p0_s;
+  cc.r = r_s;
+  settle(cc);
+  Cursor ci = cc;  // next tile to issue
+
+  // ---- block-table entries of one tile (scalar loads) -------------------
+  constexpr int PPT = P >= kTileTokens ? 1 : kTileTokens / P;   // pages per tile
+  struct TilePages {
+    int id[PPT];
+    bool ok[PPT];   // page attended and its entry in range
+    bool bad;       // an attended page has an out-of-range entry
+  };
+  auto fetch_pages = [&](const Cursor& cu) {
+    TilePages tp;
+    tp.bad = false;
+    const PD_CONST int32_t* bt_row = as_const(a.bt) + (int64_t)cu.b * a.bt_sb;
+    const int tok0 = ((cu.r.lo >> 5) + cu.i) * kTileTokens;
+    const int pg_lo = cu.r.lo / P, pg_hi = (cu.r.hi + P - 1) / P;
 #pragma unroll
     for (int j = 0; j < PPT; ++j) {
       const int pidx = tok0 / P + j;
-      bool ok = pidx >= pg_lo && pidx < pg_hi;
-      int id = ok ? bt_row[pidx] : 0;
-      if (ok && (id < 0 || id >= a.num_pages)) {
-        bad = true;
-        ok = false;
-      }
-      pid[j] = id;
-      pok[j] = ok;
+      const bool att = pidx >= pg_lo && pidx < pg_hi;
+      const int id = att ? bt_row[pidx] : 0;
+      const bool inr = id >= 0 && id < a.num_pages;
+      tp.id[j] = id;
+      tp.ok[j] = att && inr;
+      tp.bad |= att && !inr;
     }
-    const int cs = lane & 31;
+    return tp;
+  };
+  TilePages pages_none;
 #pragma unroll
-    for (int i = 0; i < kLoadsPerTile; ++i) {
-      constexpr int kRowsPerLoad = 2;
-      const int j = P >= kTileTokens ? 0 : (kRowsPerLoad * i) / P;
-      if (!pok[j]) continue;
-      // uniform page base (SGPR pair) + 32-bit per-lane byte offset
-      const char* page_base = kv_head + (int64_t)pid[j] * a.kv_sp * 2;
-      const int r = kRowsPerLoad * i + (lane >> 5);
-      const uint32_t slot_tok = (uint32_t)((tok0 + r) & (P - 1));
-      const uint32_t ch = (uint32_t)(cs ^ swz(r));
-      global_to_lds_16(page_base, (slot_tok * (2 * kD) + ch * 8) * 2, lds_addr(dst + i * 1024));
+  for (int j = 0; j < PPT; ++j) {
+    pages_none.id[j] = 0;
+    pages_none.ok[j] = false;
+  }
+  pages_none.bad = false;
+
+  // ---- HBM -> LDS loads of one tile (and of a new piece's query rows) ----
+  // A tile is always exactly kLoadsPerTile loads (rows of a page that is not
+  // read come from a harmless 16-byte source), so the vmcnt bookkeeping of
+  // the ring is exact.  Query rows go to one of two LDS slots before the
+  // tile's loads, so they have landed when the tile has.
+  int q_issued = 0, q_used = 0;   // pieces whose query rows were loaded / read
+  auto load_q = [&](const Cursor& cu) {
+    const uint32_t dst = uniform((int)lds_addr(qslots + (q_issued & 1) * kQSlotBytes));
+    const char* qbase = (const char*)(a.q + (int64_t)cu.b * a.q_sb + (int64_t)cu.kvh * G * a.q_sh);
+    const int chunk = lane & 15;
+    for (int i = 0; i < (G + 3) / 4; ++i) {   // 4 heads (1 KB) per load
+      const int h = min(4 * i + (lane >> 4), G - 1);
+      const uint32_t voff = (uint32_t)(h * a.q_sh + chunk * 8) * 2u;
+      global_to_lds_16(qbase, voff, dst + i * 1024);
     }
+    ++q_issued;
+  };
+  auto issue = [&](const Cursor& cu, const TilePages& tp, int slot) {
+    if (piece_start(cu)) load_q(cu);
+    const uint32_t dst = uniform((int)lds_addr(ring + slot * kTileBytes));
+    const char* kv_head = (const char*)(a.kv + (int64_t)cu.kvh * a.kv_sh);
+    const int cs = lane & 31;
+    const char* pbase[PPT];
+#pragma unroll
+    for (int j = 0; j < PPT; ++j)
+      pbase[j] = tp.ok[j] ? kv_head + (int64_t)tp.id[j] * a.kv_sp * 2 : (const char*)a.q;
+    auto one = [&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      constexpr int kRowsPerLoad = 2;
+      constexpr int j = P >= kTileTokens ? 0 : (kRowsPerLoad * i) / P;
+      // tiles start on a page boundary, so a row's slot in its page is r mod P
+      const int r = kRowsPerLoad * i + (lane >> 5);
+      const uint32_t slot_tok = (uint32_t)(r & (P - 1));
+      const uint32_t ch = (uint32_t)(cs ^ swz(r));
+      const uint32_t voff = tp.ok[j] ? (slot_tok * (2 * kD) + ch * 8) * 2 : 0u;
+      global_to_lds_16_at<i * 1024>(pbase[j], voff, dst);
+    };
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      (one(std::integral_constant<int, I>{}), ...);
+    }(std::make_integer_sequence<int, kLoadsPerTile>{});
   };
 
+  // ---- per-piece state ----------------------------------------------------
+  bf16x8 qf[4];
   float m_run = neg_inf();
   float l_run = 0.f;
   f32x4 o[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bool piece_bad = false;
+  int bad_slots = 0;   // bit s: the tile in ring slot s read a bad page
 
-  // prologue
+  auto finish_piece = [&](const Cursor& cu) {
+    const float l_tot_part = l_run + shfl_xor(l_run, 16);
+    const float l_tot = l_tot_part + shfl_xor(l_tot_part, 32);
+    const int hq = cu.kvh * G + l16;
+    if (l16 < G) {
+      const bool empty = !(l_tot > 0.f);
+      const float lse_nat = empty ? neg_inf() : (m_run * c + fast_log2(l_tot)) * kLn2;
+      const float nan = __builtin_nanf("");
+      if (direct) {
+        float den = l_tot;
+        if (a.sinks != nullptr && !empty) den += fast_exp2(a.sinks[hq] * kLog2e - m_run * c);
+        const float inv = empty ? 0.f : 1.f / den;
+        uint16_t* orow = a.out + (int64_t)cu.b * a.o_sb + (int64_t)hq * a.o_sh + 4 * g4;
 #pragma unroll
-  for (int k = 0; k < kNS - 1; ++k)
-    if (k < n_w) issue(tb + wave + k * kNW, k);
-
-  for (int k = 0; k < n_w; ++k) {
-    const int kn = k + kNS - 1;
-    if (kn < n_w) {
-      wait_lgkmcnt0();  // this slot's LDS reads of the previous tile are done
-      issue(tb + wave + kn * kNW, kn % kNS);
+        for (int blk = 0; blk < 8; ++blk) {
+          f32x4 r = o[blk] * inv;
+          if (piece_bad) r = f32x4{nan, nan, nan, nan};
+          *(u32x2*)(orow + 16 * blk) = u32x2{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
+        }
+        if (a.lse != nullptr && g4 == 0)
+          a.lse[(int64_t)cu.b * a.lse_sb + hq] = piece_bad ? nan : lse_nat;
+      } else {
+        const int s = sh.split ? w - cu.p0 / sh.tpw : 0;
+        float* slot = a.ws + (((int64_t)cu.b * a.Hq + hq) * S + s) * (kD + 1);
+        const float inv = empty ? 0.f : 1.f / l_tot;
+#pragma unroll
+        for (int blk = 0; blk < 8; ++blk) {
+          f32x4 r = o[blk] * inv;
+          if (piece_bad) r = f32x4{nan, nan, nan, nan};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) slot[16 * blk + 4 * g4 + e] = r[e];
+        }
+        if (g4 == 0) slot[kD] = piece_bad ? nan : lse_nat;
+      }
     }
-    if (kn >= n_w - 1)
-      wait_vmcnt<0>();
-    else
-      wait_vmcnt<kLoadsPerTile * (kNS - 1)>();
+  };
 
-    const int T = tb + wave + k * kNW;
-    const int tok0 = T * kTileTokens;
-    PD_LDS char* tl = ring + (k % kNS) * kTileBytes;
+  if (cc.b < a.B) {
+    // ---- prologue -----------------------------------------------------------
+    // The block-table entries of the next tile to issue are fetched one
+    // iteration ahead of their use.
+    TilePages pg_next = fetch_pages(ci);
+    issue(ci, pg_next, 0);
+    bad_slots = pg_next.bad ? 1 : 0;
+    advance(ci);
+    pg_next = ci.b < a.B ? fetch_pages(ci) : pages_none;
 
-    // ---- scores ----
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-    const int sw = swz(l16);
+    for (int k = 0; cc.b < a.B; ++k) {
+      const bool first = piece_start(cc);
+      if (first) {
+        m_run = neg_inf();
+        l_run = 0.f;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int ch = (g4 + 4 * s) ^ sw;
-      bf16x8 k0 = *(PD_LDS bf16x8*)(tl + l16 * kRowBytes + ch * 16);
-      bf16x8 k1 = *(PD_LDS bf16x8*)(tl + (16 + l16) * kRowBytes + ch * 16);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[s], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[s], s1, 0, 0, 0);
-    }
+        for (int i = 0; i < 8; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        piece_bad = false;
+      }
 
-    const bool edge = tok0 < lo || tok0 + kTileTokens > hi;
-    bool v0[4], v1[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t0 = tok0 + 4 * g4 + i, t1 = t0 + 16;
-      v0[i] = !edge || (t0 >= lo && t0 < hi);
-      v1[i] = !edge || (t1 >= lo && t1 < hi);
-      if (!v0[i]) s0[i] = neg_inf();
-      if (!v1[i]) s1[i] = neg_inf();
-    }
+      const bool issuing = ci.b < a.B;
+      if (issuing) {
+        wait_lgkmcnt0();  // LDS reads of the slot (tile k-1) and of an old query slot are done
+        const int slot = (k + 1) & 1;
+        issue(ci, pg_next, slot);
+        bad_slots = (bad_slots & ~(1 << slot)) | (pg_next.bad ? 1 << slot : 0);
+        advance(ci);
+        pg_next = ci.b < a.B ? fetch_pages(ci) : pages_none;
+      }
+      if (issuing)
+        wait_vmcnt<kLoadsPerTile>();
+      else
+        wait_vmcnt<0>();
 
-    // ---- online softmax (fp32, exp2, running max in unscaled logits) ----
-    float mx = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
-                     fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
-    mx = fmaxf(mx, shfl_xor(mx, 16));
-    mx = fmaxf(mx, shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_ref = m_new == neg_inf() ? 0.f : m_new;
-    const float mc = m_ref * c;
-    const float alpha = fast_exp2(m_run * c - mc);
-    float p0[4], p1[4];
-    float psum = 0.f;
+      if (first) {
+        // the piece's query rows (loaded before its first tile): B operand
+        // of S^T = K Q^T, zero for padding heads
+        PD_LDS const char* qs = qslots + (q_used & 1) * kQSlotBytes + l16 * (kD * 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p0[i] = fast_exp2(s0[i] * c - mc);
-      p1[i] = fast_exp2(s1[i] * c - mc);
-      psum += p0[i] + p1[i];
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] *= alpha;
+        for (int s = 0; s < 4; ++s) {
+          const bf16x8 v = *(PD_LDS const bf16x8*)(qs + (8 * g4 + 32 * s) * 2);
+          qf[s] = l16 < G ? v : bf16x8{};
+        }
+        ++q_used;
+      }
 
-    // P^T as the B operand: k = 8*g4 + j <-> tokens 4*g4 + j (j < 4) and
-    // 16 + 4*g4 + (j - 4) (j >= 4), exactly this lane's scores.
-    const u32x4 pw = {pack_bf16x2(p0[0], p0[1]), pack_bf16x2(p0[2], p0[3]),
-                      pack_bf16x2(p1[0], p1[1]), pack_bf16x2(p1[2], p1[3])};
-    const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
-    const u32x4 vkeep = {keep_mask(v0[0], v0[1]), keep_mask(v0[2], v0[3]),
-                         keep_mask(v1[0], v1[1]), keep_mask(v1[2], v1[3])};
+      const int slot = k & 1;
+      piece_bad |= (bad_slots >> slot) & 1;
+      PD_LDS char* tl = ring + slot * kTileBytes;
+      const int lo = cc.r.lo, hi = cc.r.hi;
+      const int tok0 = ((lo >> 5) + cc.i) * kTileTokens;
 
-    // ---- O^T += V^T P^T ----
-    const int ra = 4 * g4 + (l16 >> 2);
-    const int rb = ra + 16;
-    const int swa = swz(ra);
+      // ---- scores ----
+      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+      const int sw = swz(l16);
 #pragma unroll
-    for (int blk = 0; blk < 8; ++blk) {
-      const int ch = 16 + 2 * blk + ((l16 & 3) >> 1);
-      const int within = (l16 & 1) * 8;
-      bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-          (PD_LDS bf16x4*)(tl + ra * kRowBytes + ((ch ^ swa) << 4) + within));
-      bf16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-          (PD_LDS bf16x4*)(tl + rb * kRowBytes + ((ch ^ swa) << 4) + within));
-      u32x2 ua = __builtin_bit_cast(u32x2, va);
-      u32x2 ub = __builtin_bit_cast(u32x2, vb);
-      u32x4 vv = {ua[0], ua[1], ub[0], ub[1]};
-      if (edge) vv &= vkeep;
-      o[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pf, o[blk], 0, 0, 0);
+      for (int s = 0; s < 4; ++s) {
+        const int ch = (g4 + 4 * s) ^ sw;
+        bf16x8 k0 = *(PD_LDS bf16x8*)(tl + l16 * kRowBytes + ch * 16);
+        bf16x8 k1 = *(PD_LDS bf16x8*)(tl + (16 + l16) * kRowBytes + ch * 16);
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[s], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[s], s1, 0, 0, 0);
+      }
+
+      const bool edge = tok0 < lo || tok0 + kTileTokens > hi;
+      bool v0[4], v1[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t0 = tok0 + 4 * g4 + i, t1 = t0 + 16;
+        v0[i] = !edge || (t0 >= lo && t0 < hi);
+        v1[i] = !edge || (t1 >= lo && t1 < hi);
+        if (!v0[i]) s0[i] = neg_inf();
+        if (!v1[i]) s1[i] = neg_inf();
+      }
+
+      // ---- online softmax (fp32, exp2, running max in unscaled logits) ----
+      float mx = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
+                       fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
+      mx = fmaxf(mx, shfl_xor(mx, 16));
+      mx = fmaxf(mx, shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      const float m_ref = m_new == neg_inf() ? 0.f : m_new;
+      const float mc = m_ref * c;
+      const float alpha = fast_exp2(m_run * c - mc);
+      float p0[4], p1[4];
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p0[i] = fast_exp2(s0[i] * c - mc);
+        p1[i] = fast_exp2(s1[i] * c - mc);
+        psum += p0[i] + p1[i];
+      }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] *= alpha;
+
+      // P^T as the B operand: k = 8*g4 + j <-> tokens 4*g4 + j (j < 4) and
+      // 16 + 4*g4 + (j - 4) (j >= 4), exactly this lane's scores.
+      const u32x4 pw = {pack_bf16x2(p0[0], p0[1]), pack_bf16x2(p0[2], p0[3]),
+                        pack_bf16x2(p1[0], p1[1]), pack_bf16x2(p1[2], p1[3])};
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
+      const u32x4 vkeep = {keep_mask(v0[0], v0[1]), keep_mask(v0[2], v0[3]),
+                           keep_mask(v1[0], v1[1]), keep_mask(v1[2], v1[3])};
+
+      // ---- O^T += V^T P^T ----
+      const int ra = 4 * g4 + (l16 >> 2);
+      const int rb = ra + 16;
+      const int swa = swz(ra);
+#pragma unroll
+      for (int blk = 0; blk < 8; ++blk) {
+        const int ch = 16 + 2 * blk + ((l16 & 3) >> 1);
+        const int within = (l16 & 1) * 8;
+        bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (PD_LDS bf16x4*)(tl + ra * kRowBytes + ((ch ^ swa) << 4) + within));
+        bf16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (PD_LDS bf16x4*)(tl + rb * kRowBytes + ((ch ^ swa) << 4) + within));
+        u32x2 ua = __builtin_bit_cast(u32x2, va);
+        u32x2 ub = __builtin_bit_cast(u32x2, vb);
+        u32x4 vv = {ua[0], ua[1], ub[0], ub[1]};
+        if (edge) vv &= vkeep;
+        o[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pf, o[blk], 0, 0, 0);
+      }
+
+      if (cc.i + 1 == cc.i_end) finish_piece(cc);
+      advance(cc);
     }
   }
 
-  // ---- per-wave row sums, then the workgroup combine through LDS --------
-  l_run += shfl_xor(l_run, 16);
-  l_run += shfl_xor(l_run, 32);
-
-  __syncthreads();  // every wave is done with its ring
-  float* comb = (float*)smem;
-  {
-    float* wb = comb + wave * kCombWaveFloats;
-#pragma unroll
-    for (int blk = 0; blk < 8; ++blk)
-      *(f32x4*)(wb + l16 * kCombHeadStride + 16 * blk + 4 * g4) = o[blk];
-    if (g4 == 0) {
-      wb[16 * kCombHeadStride + l16] = m_run;
-      wb[16 * kCombHeadStride + 16 + l16] = l_run;
+  // ---- units this wave answers for without streaming them ---------------
+  // Empty units owned by this share get O = 0 / LSE = -inf (or lse = -inf in
+  // every split slot); a unit whose first tile is in this share gets
+  // lse = -inf in the split slots no piece of it uses.
+  Cursor cw;
+  cw.b = b_s;
+  cw.kvh = kvh_s;
+  cw.p0 = p0_s;
+  cw.r = r_s;
+  while (cw.b < a.B && (sh.last || cw.p0 < sh.g1)) {
+    const int hq0 = cw.kvh * G;
+    if (cw.r.nt == 0) {
+      if (direct) {
+        for (int i = lane; i < G * (kD / 8); i += 64) {
+          const int h = i / (kD / 8), d8 = (i % (kD / 8)) * 8;
+          *(u32x4*)(a.out + (int64_t)cw.b * a.o_sb + (int64_t)(hq0 + h) * a.o_sh + d8) = u32x4{0, 0, 0, 0};
+        }
+        if (a.lse != nullptr && lane < G) a.lse[(int64_t)cw.b * a.lse_sb + hq0 + lane] = neg_inf();
+      } else {
+        for (int i = lane; i < G * S; i += 64) {
+          const int h = i / S, s = i % S;
+          a.ws[(((int64_t)cw.b * a.Hq + hq0 + h) * S + s) * (kD + 1) + kD] = neg_inf();
+        }
+      }
+    } else if (sh.split && cw.p0 >= sh.g0) {
+      const int nseg = (cw.p0 + cw.r.nt - 1) / sh.tpw - cw.p0 / sh.tpw + 1;
+      for (int i = lane; i < G * (S - nseg); i += 64) {
+        const int h = i / (S - nseg), s = nseg + i % (S - nseg);
+        a.ws[(((int64_t)cw.b * a.Hq + hq0 + h) * S + s) * (kD + 1) + kD] = neg_inf();
+      }
     }
-    if (lane == 0) wb[16 * kCombHeadStride + 32] = bad ? 1.f : 0.f;
-  }
-  __syncthreads();
-
-  bool any_bad = false;
-#pragma unroll
-  for (int w = 0; w < kNW; ++w) any_bad |= comb[w * kCombWaveFloats + 16 * kCombHeadStride + 32] != 0.f;
-
-  for (int idx = tid; idx < G * (kD / 4); idx += kNW * 64) {
-    const int h = idx / (kD / 4);
-    const int d4 = (idx % (kD / 4)) * 4;
-    float mw[kNW];
-    float m_all = neg_inf();
-#pragma unroll
-    for (int w = 0; w < kNW; ++w) {
-      mw[w] = comb[w * kCombWaveFloats + 16 * kCombHeadStride + h];
-      m_all = fmaxf(m_all, mw[w]);
-    }
-    float l_all = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int w = 0; w < kNW; ++w) {
-      const float corr = mw[w] == neg_inf() ? 0.f : fast_exp2((mw[w] - m_all) * c);
-      l_all += corr * comb[w * kCombWaveFloats + 16 * kCombHeadStride + 16 + h];
-      const f32x4 ow = *(const f32x4*)(comb + w * kCombWaveFloats + h * kCombHeadStride + d4);
-      acc += corr * ow;
-    }
-    const bool empty = !(l_all > 0.f);
-    const float lse_nat = empty ? neg_inf() : (m_all * c + fast_log2(l_all)) * kLn2;
-    if (direct) {
-      float den = l_all;
-      if (a.sinks != nullptr && !empty) den += fast_exp2(a.sinks[hq0 + h] * kLog2e - m_all * c);
-      const float inv = empty ? 0.f : 1.f / den;
-      f32x4 r = acc * inv;
-      if (any_bad) r = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
-      u32x2 packed = {pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
-      *(u32x2*)(a.out + (int64_t)b * a.o_sb + (int64_t)(hq0 + h) * a.o_sh + d4) = packed;
-      if (a.lse != nullptr && d4 == 0)
-        a.lse[(int64_t)b * a.lse_sb + hq0 + h] = any_bad ? __builtin_nanf("") : lse_nat;
-    } else {
-      const float inv = empty ? 0.f : 1.f / l_all;
-      float* slot = a.ws + ((int64_t)(b * a.Hq + hq0 + h) * S + split) * (kD + 1);
-      f32x4 r = acc * inv;
-      if (any_bad) r = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) slot[d4 + e] = r[e];
-      if (d4 == 0) slot[kD] = any_bad ? __builtin_nanf("") : lse_nat;
-    }
+    next_unit(cw);
   }
 }
 
 }  // namespace
 
-template <int NW, int NS>
-static hipError_t launch_variant(const GqaArgs& a, hipStream_t stream) {
-  dim3 grid(a.S, a.Hkv, a.B), block(NW * 64);
-  switch (a.P) {
-    case 16: hipLaunchKernelGGL((gqa_decode_kernel<16, NW, NS>), grid, block, 0, stream, a); break;
-    case 32: hipLaunchKernelGGL((gqa_decode_kernel<32, NW, NS>), grid, block, 0, stream, a); break;
-    default: return hipErrorInvalidValue;
+// Workgroups per launch: one per compute unit (the ring takes 128 KB of
+// LDS, so one workgroup fits a CU).  Queried once per device.
+static int grid_size() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev] = n;
   }
-  return hipGetLastError();
-}
-
-// Tuning override for sweeps (never needed for correctness): PD_GQA_TUNE =
-// "<waves>x<stages>" picks another compiled (waves, ring stages) variant.
-static int tune_variant() {
-  static int v = [] {
-    const char* e = getenv("PD_GQA_TUNE");
-    if (e == nullptr) return 0;
-    if (!strcmp(e, "4x2")) return 0;
-    if (!strcmp(e, "2x2")) return 1;
-    if (!strcmp(e, "2x4")) return 2;
-    if (!strcmp(e, "2x3")) return 3;
-    if (!strcmp(e, "1x4")) return 4;
-    return 0;
-  }();
-  return v;
+  return cached[dev];
 }
 
 hipError_t launch_gqa_decode(const GqaArgs& a, hipStream_t stream) {
-  switch (tune_variant()) {
-    case 1: return launch_variant<2, 2>(a, stream);
-    case 2: return launch_variant<2, 4>(a, stream);
-    case 3: return launch_variant<2, 3>(a, stream);
-    case 4: return launch_variant<1, 4>(a, stream);
-    default: return launch_variant<4, 2>(a, stream);
+  const int n = grid_size();
+  if (n <= 0) return hipErrorInvalidDevice;
+  dim3 grid(n), block(kNW * 64);
+  switch (a.P) {
+    case 16: hipLaunchKernelGGL((gqa_decode_kernel<16>), grid, block, 0, stream, a); break;
+    case 32: hipLaunchKernelGGL((gqa_decode_kernel<32>), grid, block, 0, stream, a); break;
+    default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
 }
 
 }  // namespace pd

@@ -9,33 +9,33 @@ namespace pd {
 
 // Token tile every kernel walks the keys in (one MFMA contraction depth).
 constexpr int kTileTokens = 32;
-// Fewest 32-token tiles a GQA split takes before the request uses fewer
-// splits (256 keys = 128 KB of K|V per kv head).
-constexpr int kGqaMinSplitTiles = 8;
-// Same for the MLA verify path (in 32-token tiles).
+// Fewest 32-token tiles an MLA verify split takes before the request uses
+// fewer splits.
 constexpr int kMlaMinSplitTiles = 4;
 
+// Strides are in elements and below 2^31 (checked on the host), so the
+// kernel keeps them in 32-bit scalar registers.
 struct GqaArgs {
   const uint16_t* q;
-  int64_t q_sb, q_sh;
+  int32_t q_sb, q_sh;
   const uint16_t* kv;
-  int64_t kv_sp, kv_sh;
+  int32_t kv_sp, kv_sh;
   int32_t num_pages;
   const int32_t* bt;
-  int64_t bt_sb;
+  int32_t bt_sb;
   int32_t max_blocks;
   const int32_t* seq_lens;
   const float* sinks;
   int32_t window;
   float scale_log2;  // sm_scale * log2(e)
   int32_t B, Hq, Hkv, G, P;
-  int32_t S;         // split cap
+  int32_t S;         // split cap: no (request, kv head) is cut into more pieces
   int32_t partials;  // 1: always write workspace partials (never O / LSE)
   float* ws;         // [B, Hq, S, D + 1] when S > 1 or partials
   uint16_t* out;
-  int64_t o_sb, o_sh;
+  int32_t o_sb, o_sh;
   float* lse;
-  int64_t lse_sb;
+  int32_t lse_sb;
 };
 
 struct MergeArgs {
