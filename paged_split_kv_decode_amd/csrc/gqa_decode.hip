@@ -16,7 +16,8 @@
 // * A wave streams its share as one pipeline that runs straight across unit
 //   boundaries: it has a private 2-stage ring of 16 KB tiles in LDS and
 //   issues tile k+1 (16 `global_load_lds_dwordx4`, 1 KB each, HBM -> LDS
-//   with no VGPR staging) while it computes tile k.  The physical page of
+//   with no VGPR staging, non-temporal: the cache is read once) while it
+//   computes tile k.  The physical page of
 //   each tile row comes from the block table through scalar loads made one
 //   tile ahead of their use, so their latency is hidden.  No workgroup
 //   barrier exists anywhere: the waves share nothing but the CU.
@@ -335,7 +336,7 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
       const uint32_t slot_tok = (uint32_t)(r & (P - 1));
       const uint32_t ch = (uint32_t)(cs ^ swz(r));
       const uint32_t voff = tp.ok[j] ? (slot_tok * (2 * kD) + ch * 8) * 2 : 0u;
-      global_to_lds_16_at<i * 1024>(pbase[j], voff, dst);
+      global_to_lds_16_stream<i * 1024>(pbase[j], voff, dst);
     };
     [&]<int... I>(std::integer_sequence<int, I...>) {
       (one(std::integral_constant<int, I>{}), ...);
