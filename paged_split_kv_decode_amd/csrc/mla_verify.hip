@@ -56,9 +56,10 @@ constexpr int kRowBytes8 = kLk;                                    // fp8 latent
 constexpr int kTileBytes8 = kTileTokens * kRowBytes8;              // 18 KB
 constexpr int kPageRegion8 = 16 * kRowBytes8;                      // 9 KB (fp8)
 constexpr int kKSteps = kLk / 16;                                  // 36
-constexpr int kKBatch = 6;                                         // K fragments per batch
+constexpr int kAhead = 3;                                          // fragment pairs in flight
+constexpr int kRopeSteps = 4;                                      // 64 rope dims = 4 k-steps
+constexpr int kRegSteps = kKSteps - kRopeSteps;                    // query k-steps kept in VGPRs
 constexpr int kVBlocks = kLv / 32;                                 // 16
-constexpr int kVBatch = 4;                                         // V^T blocks per batch
 // p = 2^(x - m_ref) stays below 2^64 while the row max has not grown more
 // than this above the reference (fp32 / bf16 hold 2^127; with up to 2^20
 // keys and |V| < 2^40 the accumulator cannot overflow).
@@ -75,9 +76,6 @@ constexpr float kRefHeadroomLog2 = 64.f;
 //    slots whose bank groups differ by the row XOR: both bank-conflict free.
 __device__ __forceinline__ int tile_slot(int c, int r16) { return 16 * c + (r16 ^ (4 * (c & 1))); }
 
-__device__ __forceinline__ uint32_t keep_mask(bool lo_ok, bool hi_ok) {
-  return (lo_ok ? 0x0000FFFFu : 0u) | (hi_ok ? 0xFFFF0000u : 0u);
-}
 
 template <int NS, bool FP8>
 __global__ __launch_bounds__(kWaves * 64, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -88,11 +86,13 @@ void mla_verify_kernel(MlaArgs a) {
   // bf16: 4 waves x 9 loads; fp8: waves 0 and 1 load one page (9 loads) each,
   // so every issuing wave has the same count for its vmcnt bookkeeping.
   constexpr int kIssueWaves = FP8 ? 2 : 4;
-  constexpr int kStageOff = NS * kRingTile;                         // fp8 -> bf16 tile
+  static_assert(NS == 4, "ring of 4 tiles: k-1 (product), k (scores), k+1, k+2 (loading)");
+  constexpr int kStageOff = NS * kRingTile;                         // 2 fp8 -> bf16 tiles
   constexpr int kLoadsPerWave = kLoadsPerTile / kIssueWaves;
   static_assert(kLoadsPerWave * kIssueWaves == kLoadsPerTile, "even load split");
-  constexpr int kFlagOff = kStageOff + (FP8 ? kTileBytes : 0);     // 2 pass flags
-  constexpr int kLdsBytes = kFlagOff + 16;
+  constexpr int kRopeOff = kStageOff + (FP8 ? 2 * kTileBytes : 0);  // query rope fragments
+  constexpr int kLdsBytes = kRopeOff + kWaves * kRopeSteps * 64 * 16;
+  static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
   PD_LDS char* lds = (PD_LDS char*)smem;
 
@@ -163,14 +163,21 @@ void mla_verify_kernel(MlaArgs a) {
   const float c = a.scale_log2 * kscale;   // log2-domain scale of raw scores
 
   // ---- Q fragment: B operand of S^T = K Q^T (32 rows x 576 dims) --------
-  bf16x8 qf[kKSteps];
+  // The first kRegSteps fragments stay in VGPRs; the last kRopeSteps (the
+  // 64 rope dims) live in this wave's LDS area and are read for the last
+  // MFMAs of every tile, which keeps the register file within budget.
+  bf16x8 qf[kRegSteps];
+  PD_LDS char* qrope = lds + kRopeOff + wave * (kRopeSteps * 64 * 16) + lane * 16;
   {
     const uint16_t* qp = a.q + q_row * a.q_srow + (int64_t)h_row * a.q_sh + 8 * g2;
 #pragma unroll
     for (int kk = 0; kk < kKSteps; ++kk) {
       u32x4 v = *(const u32x4*)(qp + 16 * kk);
       if (!row_ok) v = u32x4{0, 0, 0, 0};
-      qf[kk] = __builtin_bit_cast(bf16x8, v);
+      if (kk < kRegSteps)
+        qf[kk] = __builtin_bit_cast(bf16x8, v);
+      else
+        *(PD_LDS u32x4*)(qrope + (kk - kRegSteps) * 1024) = v;   // read after the first tile barrier
     }
   }
 
@@ -181,47 +188,59 @@ void mla_verify_kernel(MlaArgs a) {
   const PD_CONST int32_t* bt_row = as_const(a.bt) + (int64_t)b * a.bt_sb;
   bool bad = false;
 
-  // Issue this wave's share of the HBM->LDS loads of tile T into slot:
-  // issuing wave w loads page w / (waves per page), instructions
-  // (w % waves per page) * kLoadsPerWave + j of that page.
+  // ---- block-table entries of a tile (scalar loads, one iteration ahead) --
+  struct TilePages {
+    int id[2];
+    bool ok[2];   // page attended and its entry in range
+  };
+  auto fetch = [&](int T) {
+    TilePages tp;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int pidx = 2 * T + j;
+      const bool att = pidx < pg_hi;
+      const int id = att ? bt_row[pidx] : 0;
+      const bool inr = id >= 0 && id < a.num_pages;
+      // every wave checks both pages, so the flag is workgroup-uniform
+      bad |= att && !inr;
+      tp.id[j] = id;
+      tp.ok[j] = att && inr;
+    }
+    return tp;
+  };
+
+  // Issue this wave's share of the HBM->LDS loads of a tile into a ring
+  // slot: issuing wave w loads page w / (waves per page), instructions
+  // (w % waves per page) * kLoadsPerWave + j of that page.  An issuing wave
+  // always issues exactly kLoadsPerWave loads (a page that is not read comes
+  // from a harmless 16-byte source), so its vmcnt bookkeeping is exact.
   constexpr int kWavesPerPage = kIssueWaves / 2;
   const int my_page = wave / kWavesPerPage;
   const int i0 = (wave % kWavesPerPage) * kLoadsPerWave;   // first instruction of this wave
   const uint32_t lane_off = (uint32_t)((FP8 ? (lane & 15) : ((lane & 15) ^ (4 * ((lane >> 4) & 1)))) *
                                        st_bytes) + 16u * (uint32_t)(lane >> 4);
-  auto issue = [&](int T, int slot) {
-    // both pages of the tile are checked by every wave (indices < pg_hi), so
-    // the invalid-entry flag is workgroup-uniform
-    int pid[2];
-    bool pok[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int pidx = 2 * T + j;
-      pok[j] = pidx < pg_hi;
-      pid[j] = pok[j] ? bt_row[pidx] : 0;
-      if (pok[j] && (pid[j] < 0 || pid[j] >= a.num_pages)) {
-        bad = true;
-        pok[j] = false;
-      }
-    }
-    const bool ok = (my_page & 1) ? pok[1] : pok[0];
-    const int my_pid = (my_page & 1) ? pid[1] : pid[0];
-    if (wave >= kIssueWaves || !ok) return;
+  auto issue = [&](const TilePages& tp, int slot) {
+    if (wave >= kIssueWaves) return;
+    const bool ok = (my_page & 1) ? tp.ok[1] : tp.ok[0];
+    const int my_pid = (my_page & 1) ? tp.id[1] : tp.id[0];
     // instruction i of a page covers 16-byte slots [64 i, 64 i + 64): chunk
     // columns 4 i .. 4 i + 3, i.e. 64 more bytes into every row
-    const char* base = kv + (int64_t)my_pid * sp_bytes + 64 * i0;
+    const char* base = ok ? kv + (int64_t)my_pid * sp_bytes + 64 * i0 : (const char*)a.q;
+    const uint32_t voff = ok ? lane_off : 0u;
     PD_LDS char* dst = lds + slot * kRingTile + my_page * (FP8 ? kPageRegion8 : kPageRegion) + i0 * 1024;
 #pragma unroll
     for (int j = 0; j < kLoadsPerWave; ++j)
-      global_to_lds_16(base + 64 * j, lane_off, lds_addr(dst + j * 1024));
+      global_to_lds_16(base + (ok ? 64 * j : 0), voff, lds_addr(dst + j * 1024));
   };
 
   float m_seen = neg_inf();   // exact running max of this lane's row
   float m_ref = neg_inf();    // fixed reference of the current pass
   float l_run = 0.f;
-  f32x16 o[kVBlocks];
-  PD_LDS int* pass_flag = (PD_LDS int*)(lds + kFlagOff);
-  if (tid < 2) pass_flag[tid] = 0;   // ordered before use by the first tile barrier
+  // Output accumulator O^T (512 x 32 fp32).  Blocks 0..14 stay in AGPRs;
+  // block 15 is parked in VGPRs between tiles, which leaves 16 AGPRs for
+  // the score accumulator (all 256 AGPRs plus 16 = the register budget).
+  f32x16 o[kVBlocks - 1];
+  f32x16 o_last;
 
   // lane-constant parts of the transpose-read addresses
   const int q16 = lane >> 4;
@@ -232,83 +251,158 @@ void mla_verify_kernel(MlaArgs a) {
   const int vcc0 = vcol0 >> 3;                           // chunk column
   const uint32_t vlane_off = (uint32_t)(tile_slot(vcc0, vrow) * 16 + (vcol0 & 7) * 2);
 
+  // the bf16 view of tile t: its ring slot, or its fp8 staging buffer
+  auto tile_bf16 = [&](int t) -> PD_LDS char* {
+    if constexpr (FP8)
+      return lds + kStageOff + (t & 1) * kTileBytes;
+    else
+      return lds + (t & (NS - 1)) * kRingTile;
+  };
+
   for (int pass = 0; pass < 2; ++pass) {
   // pass 1 only runs if pass 0 saw a score too far above its reference
   m_ref = pass == 0 ? neg_inf() : m_seen;
   l_run = 0.f;
   bool overflow = false;
 #pragma unroll
-  for (int i = 0; i < kVBlocks; ++i)
+  for (int i = 0; i < kVBlocks - 1; ++i)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[i][e] = 0.f;
 #pragma unroll
-  for (int k = 0; k < NS - 1; ++k)
-    if (k < n) issue(tb + k, k);
+  for (int e = 0; e < 16; ++e) o_last[e] = 0.f;
 
-  for (int k = 0; k < n; ++k) {
-    const int kn = k + NS - 1;
-    if (kn - 1 >= n - 1)
-      wait_vmcnt<0>();
+  // Iteration k computes the scores of tile k interleaved with the P.V
+  // product of tile k-1 (whose probabilities pb_prev came out of iteration
+  // k-1), so the dependent score chain always has independent MFMAs
+  // between its steps.  Iteration 0 multiplies the zeroed view of "tile -1"
+  // by zero probabilities; iteration n computes throw-away scores on stale
+  // data to finish tile n-1's product.  Ring: tile t in slot t mod 4; tile
+  // k+2 is issued at iteration k into the slot of tile k-2.
+  {
+    // zero the view of tile -1 (read by iteration 0's product)
+    PD_LDS char* z = tile_bf16(-1);
+    for (int i = tid; i < kTileBytes / 16; i += kWaves * 64) *(PD_LDS u32x4*)(z + i * 16) = u32x4{0, 0, 0, 0};
+  }
+  bf16x8 pb_prev[2] = {bf16x8{}, bf16x8{}};
+  TilePages pg_next;
+  if (n > 0) issue(fetch(tb), 0);
+  if (n > 1) issue(fetch(tb + 1), 1);
+  if (n > 2) pg_next = fetch(tb + 2);
+
+  for (int k = 0; k <= n; ++k) {
+    const bool live = k < n;   // iteration n only finishes tile n-1
+    if (k + 1 < n)
+      wait_vmcnt<kLoadsPerWave>();
     else
-      wait_vmcnt<kLoadsPerWave * (NS - 2)>();
-    __syncthreads();  // tile k is in LDS; every wave is done with tile k-1
-    PD_LDS char* tl;
+      wait_vmcnt<0>();
+    __syncthreads();  // tile k is in LDS; every wave is done with iteration k-1
+    const int tok0 = (tb + k) * kTileTokens;
     if constexpr (FP8) {
-      // exact fp8 -> bf16 into the staging tile: item = (page, fp8 chunk
-      // column c8, row r16) -> bf16 chunk columns 2 c8 and 2 c8 + 1
-      PD_LDS char* src = lds + (k % NS) * kRingTile;
-      tl = lds + kStageOff;
-      for (int i = tid; i < 2 * 36 * 16; i += kWaves * 64) {
-        const int r16 = i & 15;
-        const int c8 = (i >> 4) % 36;
-        const int pg = i / (36 * 16);
-        const u32x4 w = *(PD_LDS u32x4*)(src + pg * kPageRegion8 + (16 * c8 + r16) * 16);
-        PD_LDS char* dpg = tl + pg * kPageRegion;
+      if (live) {
+        // exact fp8 -> bf16 into the staging buffer: item = (page, fp8
+        // chunk column c8, row r16) -> bf16 chunk columns 2 c8 and 2 c8 + 1
+        PD_LDS char* src = lds + (k & (NS - 1)) * kRingTile;
+        PD_LDS char* dst = tile_bf16(k);
+        for (int i = tid; i < 2 * 36 * 16; i += kWaves * 64) {
+          const int r16 = i & 15;
+          const int c8 = (i >> 4) % 36;
+          const int pg = i / (36 * 16);
+          const u32x4 w = *(PD_LDS u32x4*)(src + pg * kPageRegion8 + (16 * c8 + r16) * 16);
+          PD_LDS char* dpg = dst + pg * kPageRegion;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          u32x4 cv;
-          cv[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * h], 1.f, false));
-          cv[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * h], 1.f, true));
-          cv[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * h + 1], 1.f, false));
-          cv[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * h + 1], 1.f, true));
-          *(PD_LDS u32x4*)(dpg + tile_slot(2 * c8 + h, r16) * 16) = cv;
+          for (int h = 0; h < 2; ++h) {
+            u32x4 cv;
+            cv[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * h], 1.f, false));
+            cv[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * h], 1.f, true));
+            cv[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * h + 1], 1.f, false));
+            cv[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * h + 1], 1.f, true));
+            *(PD_LDS u32x4*)(dpg + tile_slot(2 * c8 + h, r16) * 16) = cv;
+          }
         }
+        __syncthreads();
+      }
+    }
+    PD_LDS char* tk = tile_bf16(k);       // scores of tile k
+    PD_LDS char* tv = tile_bf16(k - 1);   // product of tile k-1
+    if (live && tok0 + kTileTokens > hi_blk) {
+      // The block's last tile: token rows at or past its largest row limit
+      // (stale or never-loaded page slots) become zeros, so no score or V
+      // row there can carry a NaN into the products; a barrier orders the
+      // zeros before every read of the tile.
+      const int r0 = max(hi_blk - tok0, 0);
+      for (int i = tid; i < 2 * 72 * 16; i += kWaves * 64) {
+        const int r16 = i & 15, cc = (i >> 4) % 72, pg = i / (72 * 16);
+        if (16 * pg + r16 >= r0) *(PD_LDS u32x4*)(tk + pg * kPageRegion + tile_slot(cc, r16) * 16) = u32x4{0, 0, 0, 0};
       }
       __syncthreads();
-    } else {
-      tl = lds + (k % NS) * kRingTile;
     }
-    if (kn < n) issue(tb + kn, kn % NS);
+    if (k + 2 < n) {
+      issue(pg_next, (k + 2) & (NS - 1));
+      if (k + 3 < n) pg_next = fetch(tb + k + 3);
+    }
 
-    const int tok0 = (tb + k) * kTileTokens;
-
-    // ---- scores S^T[token, row] over all 576 dims -------------------------
-    // K fragments in batches of kKBatch read ahead of their MFMAs; two
-    // independent accumulation chains
-    f32x16 sacc, sacc2;
+    // ---- S^T(k) = K Q^T (36 MFMAs, one chain) with O^T += V^T P^T of tile
+    // k-1 (30 MFMAs for blocks 0..14) in between -----------------------------
+    // Fragments are read kAhead MFMA pairs ahead of their use; scheduling
+    // barriers pin that order (left alone, the scheduler moves every read
+    // next to its MFMA and the wave stalls on LDS latency at each step).
+    f32x16 sacc;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) sacc[e] = sacc2[e] = 0.f;
+    for (int e = 0; e < 16; ++e) sacc[e] = 0.f;
+    PD_LDS char* kpage = tk + (l32 >> 4) * kPageRegion;
+    const int r16 = l32 & 15;
+    auto kread = [&](int kk) { return *(PD_LDS bf16x8*)(kpage + tile_slot(g2 + 2 * kk, r16) * 16); };
+    // product step j: st = j / 15 (16-token half), blk = j % 15
+    auto vread = [&](int j, int blk_off) {
+      // read a: rows vrow.., read b: rows vrow + 8.. (slot + 8); block blk
+      // is 4 chunk columns (1 KB) further; step st is the next page
+      const int st = j / 15, blk = j % 15 + blk_off;
+      PD_LDS char* pa = tv + vlane_off + st * kPageRegion + blk * 1024;
+      const bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((PD_LDS bf16x4*)pa);
+      const bf16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((PD_LDS bf16x4*)(pa + 128));
+      const u32x2 ua = __builtin_bit_cast(u32x2, va);
+      const u32x2 ub = __builtin_bit_cast(u32x2, vb);
+      return __builtin_bit_cast(bf16x8, u32x4{ua[0], ua[1], ub[0], ub[1]});
+    };
+    constexpr int kPv = 2 * (kVBlocks - 1);   // 30 product MFMAs in the interleave
     {
-      PD_LDS char* kpage = tl + (l32 >> 4) * kPageRegion;
-      const int r16 = l32 & 15;
+      bf16x8 kf[kAhead], vf[kAhead], qr[kRopeSteps];
 #pragma unroll
-      for (int b0 = 0; b0 < kKSteps; b0 += kKBatch) {
-        bf16x8 kf[kKBatch];
+      for (int i = 0; i < kAhead; ++i) {
+        kf[i] = kread(i);
+        vf[i] = vread(i, 0);
+      }
 #pragma unroll
-        for (int i = 0; i < kKBatch; ++i)
-          kf[i] = *(PD_LDS bf16x8*)(kpage + tile_slot(g2 + 2 * (b0 + i), r16) * 16);
-#pragma unroll
-        for (int i = 0; i < kKBatch; ++i) {
-          if (i & 1)
-            sacc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[b0 + i], sacc2, 0, 0, 0);
-          else
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[b0 + i], sacc, 0, 0, 0);
+      for (int kk = 0; kk < kKSteps; ++kk) {
+        const bf16x8 qv = kk < kRegSteps ? qf[kk < kRegSteps ? kk : 0] : qr[kk < kRegSteps ? 0 : kk - kRegSteps];
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk % kAhead], qv, sacc, 0, 0, 0);
+        if (kk < kPv) {
+          const int st = kk / 15, blk = kk % 15;
+          o[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kk % kAhead], pb_prev[st], o[blk], 0, 0, 0);
         }
+        if (kk + kAhead < kKSteps) kf[kk % kAhead] = kread(kk + kAhead);
+        if (kk + kAhead < kPv) vf[kk % kAhead] = vread(kk + kAhead, 0);
+        if (kk + kAhead == kRegSteps) {
+#pragma unroll
+          for (int i = 0; i < kRopeSteps; ++i) qr[i] = *(PD_LDS bf16x8*)(qrope + i * 1024);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     float x[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) x[e] = (sacc[e] + sacc2[e]) * c;
+    for (int e = 0; e < 16; ++e) x[e] = sacc[e] * c;
+    {
+      // block 15 of tile k-1's product, after the score accumulator is free
+      const bf16x8 va = vread(14, 1), vb = vread(29, 1);   // (st 0, blk 15), (st 1, blk 15)
+      f32x16 o15 = o_last;
+      o15 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb_prev[0], o15, 0, 0, 0);
+      o15 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb, pb_prev[1], o15, 0, 0, 0);
+      o_last = o15;
+      asm volatile("" : "+v"(o_last));
+    }
+    if (!live) break;
+
     // causal limit of this lane's row: token tok0 + 8j + 4 g2 + i < hi_row
     if (tok0 + kTileTokens > hi_row) {
 #pragma unroll
@@ -335,50 +429,25 @@ void mla_verify_kernel(MlaArgs a) {
       p[e] = fast_exp2(x[e] - mref);
       l_run += p[e];
     }
-    bf16x8 pb[2];
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       const u32x4 w = {pack_bf16x2(p[8 * st + 0], p[8 * st + 1]), pack_bf16x2(p[8 * st + 2], p[8 * st + 3]),
                        pack_bf16x2(p[8 * st + 4], p[8 * st + 5]), pack_bf16x2(p[8 * st + 6], p[8 * st + 7])};
-      pb[st] = __builtin_bit_cast(bf16x8, w);
-    }
-
-    // ---- O^T += V^T P^T over all 512 output dims ----
-    const bool vedge = tok0 + kTileTokens > hi_blk;
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      u32x4 vkeep = {~0u, ~0u, ~0u, ~0u};
-      if (vedge) {
-        const int ta = tok0 + 16 * st + 4 * g2;    // first of the 4 tokens of read a
-        const int tbk = ta + 8;
-        vkeep = u32x4{keep_mask(ta + 0 < hi_blk, ta + 1 < hi_blk), keep_mask(ta + 2 < hi_blk, ta + 3 < hi_blk),
-                      keep_mask(tbk + 0 < hi_blk, tbk + 1 < hi_blk), keep_mask(tbk + 2 < hi_blk, tbk + 3 < hi_blk)};
-      }
-#pragma unroll
-      for (int b0 = 0; b0 < kVBlocks; b0 += kVBatch) {
-        u32x4 vop[kVBatch];
-#pragma unroll
-        for (int i = 0; i < kVBatch; ++i) {
-          // read a: rows vrow.., read b: rows vrow + 8.. (slot + 8); block
-          // blk is 4 chunk columns (1 KB) further; step st is the next page
-          PD_LDS char* pa = tl + vlane_off + st * kPageRegion + (b0 + i) * 1024;
-          bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((PD_LDS bf16x4*)pa);
-          bf16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((PD_LDS bf16x4*)(pa + 128));
-          const u32x2 ua = __builtin_bit_cast(u32x2, va);
-          const u32x2 ub = __builtin_bit_cast(u32x2, vb);
-          vop[i] = u32x4{ua[0], ua[1], ub[0], ub[1]} & vkeep;
-        }
-#pragma unroll
-        for (int i = 0; i < kVBatch; ++i)
-          o[b0 + i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vop[i]), pb[st],
-                                                              o[b0 + i], 0, 0, 0);
-      }
+      pb_prev[st] = __builtin_bit_cast(bf16x8, w);
     }
   }
-  // every wave is past its last LDS read of this pass; agree on a rerun
-  if (__ballot(overflow) != 0ull && lane == 0) pass_flag[pass] = 1;
+
+  // every wave is past its last LDS read of this pass: agree on a rerun
+  // through the (now idle) ring
   __syncthreads();
-  if (pass_flag[pass] == 0) break;
+  PD_LDS int* flags = (PD_LDS int*)lds;
+  if (lane == 0) flags[wave] = __ballot(overflow) != 0ull ? 1 : 0;
+  __syncthreads();
+  bool rerun = false;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) rerun |= flags[w] != 0;
+  __syncthreads();   // the flags are read before the next pass reuses the ring
+  if (!rerun) break;
   }
 
   // ---- epilogue: each wave writes its own 32 rows -------------------------
@@ -395,8 +464,9 @@ void mla_verify_kernel(MlaArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int d = 32 * blk + 8 * j + 4 * g2;
-        float x0 = o[blk][4 * j + 0] * inv, x1 = o[blk][4 * j + 1] * inv;
-        float x2 = o[blk][4 * j + 2] * inv, x3 = o[blk][4 * j + 3] * inv;
+        const f32x16& ob = blk < kVBlocks - 1 ? o[blk] : o_last;
+        float x0 = ob[4 * j + 0] * inv, x1 = ob[4 * j + 1] * inv;
+        float x2 = ob[4 * j + 2] * inv, x3 = ob[4 * j + 3] * inv;
         if (bad) x0 = x1 = x2 = x3 = qnan;
         *(u32x2*)(orow + d) = u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
       }
@@ -410,8 +480,9 @@ void mla_verify_kernel(MlaArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int d = 32 * blk + 8 * j + 4 * g2;
+        const f32x16& ob = blk < kVBlocks - 1 ? o[blk] : o_last;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) oslot[d + i] = bad ? qnan : o[blk][4 * j + i] * inv;
+        for (int i = 0; i < 4; ++i) oslot[d + i] = bad ? qnan : ob[4 * j + i] * inv;
       }
     if (g2 == 0) slot[kLv] = bad ? qnan : lse_nat;
   }
@@ -427,9 +498,9 @@ hipError_t launch_mla_verify(const MlaArgs& a, hipStream_t stream) {
   if (n_wg > 0x7fffffff) return hipErrorInvalidValue;
   dim3 grid((unsigned)n_wg), block(kWaves * 64);
   if (a.kv_fp8)
-    hipLaunchKernelGGL((mla_verify_kernel<3, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((mla_verify_kernel<4, true>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((mla_verify_kernel<3, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((mla_verify_kernel<4, false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
