@@ -270,26 +270,22 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
 
   // ---- block-table entries of one tile (scalar loads) -------------------
   constexpr int PPT = P >= kTileTokens ? 1 : kTileTokens / P;   // pages per tile
+  // The entries are only checked when the tile is issued, so the scalar
+  // loads stay in flight for a whole iteration.
   struct TilePages {
     int id[PPT];
-    bool ok[PPT];   // page attended and its entry in range
-    bool bad;       // an attended page has an out-of-range entry
+    bool att[PPT];   // page attended
   };
   auto fetch_pages = [&](const Cursor& cu) {
     TilePages tp;
-    tp.bad = false;
     const PD_CONST int32_t* bt_row = as_const(a.bt) + (int64_t)cu.b * a.bt_sb;
     const int tok0 = ((cu.r.lo >> 5) + cu.i) * kTileTokens;
     const int pg_lo = cu.r.lo / P, pg_hi = (cu.r.hi + P - 1) / P;
 #pragma unroll
     for (int j = 0; j < PPT; ++j) {
       const int pidx = tok0 / P + j;
-      const bool att = pidx >= pg_lo && pidx < pg_hi;
-      const int id = att ? bt_row[pidx] : 0;
-      const bool inr = id >= 0 && id < a.num_pages;
-      tp.id[j] = id;
-      tp.ok[j] = att && inr;
-      tp.bad |= att && !inr;
+      tp.att[j] = pidx >= pg_lo && pidx < pg_hi;
+      tp.id[j] = tp.att[j] ? bt_row[pidx] : 0;
     }
     return tp;
   };
@@ -297,9 +293,8 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
 #pragma unroll
   for (int j = 0; j < PPT; ++j) {
     pages_none.id[j] = 0;
-    pages_none.ok[j] = false;
+    pages_none.att[j] = false;
   }
-  pages_none.bad = false;
 
   // ---- HBM -> LDS loads of one tile (and of a new piece's query rows) ----
   // A tile is always exactly kLoadsPerTile loads (rows of a page that is not
@@ -318,7 +313,16 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
     }
     ++q_issued;
   };
+  // Issues the tile's loads; returns whether an attended page has an
+  // out-of-range entry (its rows then come from the harmless source).
   auto issue = [&](const Cursor& cu, const TilePages& tp, int slot) {
+    bool ok[PPT], bad_page = false;
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+      const bool inr = tp.id[j] >= 0 && tp.id[j] < a.num_pages;
+      ok[j] = tp.att[j] && inr;
+      bad_page |= tp.att[j] && !inr;
+    }
     if (piece_start(cu)) load_q(cu);
     const uint32_t dst = uniform((int)lds_addr(ring + slot * kTileBytes));
     const char* kv_head = (const char*)(a.kv + (int64_t)cu.kvh * a.kv_sh);
@@ -326,7 +330,7 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
     const char* pbase[PPT];
 #pragma unroll
     for (int j = 0; j < PPT; ++j)
-      pbase[j] = tp.ok[j] ? kv_head + (int64_t)tp.id[j] * a.kv_sp * 2 : (const char*)a.q;
+      pbase[j] = ok[j] ? kv_head + (int64_t)tp.id[j] * a.kv_sp * 2 : (const char*)a.q;
     auto one = [&](auto ic) {
       constexpr int i = decltype(ic)::value;
       constexpr int kRowsPerLoad = 2;
@@ -335,12 +339,13 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
       const int r = kRowsPerLoad * i + (lane >> 5);
       const uint32_t slot_tok = (uint32_t)(r & (P - 1));
       const uint32_t ch = (uint32_t)(cs ^ swz(r));
-      const uint32_t voff = tp.ok[j] ? (slot_tok * (2 * kD) + ch * 8) * 2 : 0u;
+      const uint32_t voff = ok[j] ? (slot_tok * (2 * kD) + ch * 8) * 2 : 0u;
       global_to_lds_16_stream<i * 1024>(pbase[j], voff, dst);
     };
     [&]<int... I>(std::integer_sequence<int, I...>) {
       (one(std::integral_constant<int, I>{}), ...);
     }(std::make_integer_sequence<int, kLoadsPerTile>{});
+    return bad_page;
   };
 
   // ---- per-piece state ----------------------------------------------------
@@ -393,8 +398,7 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
     // The block-table entries of the next tile to issue are fetched one
     // iteration ahead of their use.
     TilePages pg_next = fetch_pages(ci);
-    issue(ci, pg_next, 0);
-    bad_slots = pg_next.bad ? 1 : 0;
+    bad_slots = issue(ci, pg_next, 0) ? 1 : 0;
     advance(ci);
     pg_next = ci.b < a.B ? fetch_pages(ci) : pages_none;
 
@@ -412,8 +416,8 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
       if (issuing) {
         wait_lgkmcnt0();  // LDS reads of the slot (tile k-1) and of an old query slot are done
         const int slot = (k + 1) & 1;
-        issue(ci, pg_next, slot);
-        bad_slots = (bad_slots & ~(1 << slot)) | (pg_next.bad ? 1 << slot : 0);
+        const bool bad_tile = issue(ci, pg_next, slot);
+        bad_slots = (bad_slots & ~(1 << slot)) | (bad_tile ? 1 << slot : 0);
         advance(ci);
         pg_next = ci.b < a.B ? fetch_pages(ci) : pages_none;
       }

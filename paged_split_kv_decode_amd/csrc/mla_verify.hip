@@ -189,22 +189,19 @@ void mla_verify_kernel(MlaArgs a) {
   bool bad = false;
 
   // ---- block-table entries of a tile (scalar loads, one iteration ahead) --
+  // The entries are only checked when the tile is issued, so the scalar
+  // loads stay in flight for a whole iteration.
   struct TilePages {
     int id[2];
-    bool ok[2];   // page attended and its entry in range
+    bool att[2];   // page attended
   };
   auto fetch = [&](int T) {
     TilePages tp;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int pidx = 2 * T + j;
-      const bool att = pidx < pg_hi;
-      const int id = att ? bt_row[pidx] : 0;
-      const bool inr = id >= 0 && id < a.num_pages;
-      // every wave checks both pages, so the flag is workgroup-uniform
-      bad |= att && !inr;
-      tp.id[j] = id;
-      tp.ok[j] = att && inr;
+      tp.att[j] = pidx < pg_hi;
+      tp.id[j] = tp.att[j] ? bt_row[pidx] : 0;
     }
     return tp;
   };
@@ -220,8 +217,16 @@ void mla_verify_kernel(MlaArgs a) {
   const uint32_t lane_off = (uint32_t)((FP8 ? (lane & 15) : ((lane & 15) ^ (4 * ((lane >> 4) & 1)))) *
                                        st_bytes) + 16u * (uint32_t)(lane >> 4);
   auto issue = [&](const TilePages& tp, int slot) {
+    bool pok[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const bool inr = tp.id[j] >= 0 && tp.id[j] < a.num_pages;
+      // every wave checks both pages, so the flag is workgroup-uniform
+      bad |= tp.att[j] && !inr;
+      pok[j] = tp.att[j] && inr;
+    }
     if (wave >= kIssueWaves) return;
-    const bool ok = (my_page & 1) ? tp.ok[1] : tp.ok[0];
+    const bool ok = (my_page & 1) ? pok[1] : pok[0];
     const int my_pid = (my_page & 1) ? tp.id[1] : tp.id[0];
     // instruction i of a page covers 16-byte slots [64 i, 64 i + 64): chunk
     // columns 4 i .. 4 i + 3, i.e. 64 more bytes into every row
