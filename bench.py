@@ -28,6 +28,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "KV-read GB/s (% of HBM peak) and µs/call for paged decode, GQA and MLA verify"
 HBM_PEAK_GBS = 8000.0
+# The GPU clock climbs over the first ~100 ms of load after idle: the default
+# warmup runs at least this long.
+WARMUP_AUTO_S = 0.5
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 
 
@@ -35,7 +38,9 @@ def _parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=100)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=None,
+                   help="untimed warmup steps; by default as many as run in %.1f s (at least "
+                        "10), so the GPU clock has left its idle state before timing" % WARMUP_AUTO_S)
     p.add_argument("--config", default="gqa_sinks")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--splits", type=int, default=0, help="override the split cap")
@@ -211,8 +216,17 @@ def main():
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
-    for _ in range(args.warmup):
-        case["step"]()
+    if args.warmup is not None:
+        for _ in range(args.warmup):
+            case["step"]()
+    else:
+        args.warmup = 0
+        t_w = time.perf_counter()
+        while args.warmup < 10 or time.perf_counter() - t_w < WARMUP_AUTO_S:
+            for _ in range(10):
+                case["step"]()
+            args.warmup += 10
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

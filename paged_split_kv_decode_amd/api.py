@@ -25,7 +25,7 @@ MLA_BLOCK_H = 128            # verify rows (qlen * heads) per workgroup
 MLA_OCCUPANCY = 1.0
 MLA_MIN_WORK = 128
 MLA_MAX_SPLITS = 16
-MLA_BALANCE_CHUNK = 4096
+MLA_BALANCE_CHUNK = 2048
 
 
 def _ptr(t):

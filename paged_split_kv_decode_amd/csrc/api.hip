@@ -245,6 +245,14 @@ int paged_verify_mla(const void* q, int64_t q_stride_row, int64_t q_stride_h, co
     return PD_ERR_ALIGN;
   const int64_t rows = (int64_t)batch * qlen;
   if (rows > 0x7fffffff) return PD_ERR_UNSUPPORTED;
+  {
+    // the kernel's plan counts tiles over all (request, row block) units in int32
+    const int64_t rows_req = (int64_t)qlen * num_heads;
+    const int64_t keys = (int64_t)max_blocks * page_size;
+    if (rows_req > INT32_MAX / 2 || keys > INT32_MAX / 2 ||
+        (int64_t)batch * cdiv64(rows_req, 128) * cdiv64(keys, 32) > INT32_MAX / 2)
+      return PD_ERR_UNSUPPORTED;
+  }
   if (num_kv_splits > 1) {
     if (workspace == nullptr ||
         workspace_bytes < pd_workspace_bytes((int32_t)rows, num_heads, num_kv_splits, head_dim_v))

@@ -36,6 +36,28 @@ __device__ __forceinline__ float shfl_xor(float v, int mask) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(v)));
 }
 
+// Sum / max over the 64 lanes (every lane gets the result).
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __builtin_amdgcn_ds_bpermute((lane_id() ^ m) << 2, v);
+  return v;
+}
+__device__ __forceinline__ int wave_max(int v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = max(v, __builtin_amdgcn_ds_bpermute((lane_id() ^ m) << 2, v));
+  return v;
+}
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ int wave_incl_sum(int v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __builtin_amdgcn_ds_bpermute((lane >= d ? lane - d : lane) << 2, v);
+    if (lane >= d) v += y;
+  }
+  return v;
+}
+
 __device__ __forceinline__ float readlane(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }

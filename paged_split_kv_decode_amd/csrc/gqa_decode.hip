@@ -65,26 +65,6 @@ __device__ __forceinline__ uint32_t keep_mask(bool lo_ok, bool hi_ok) {
   return (lo_ok ? 0x0000FFFFu : 0u) | (hi_ok ? 0xFFFF0000u : 0u);
 }
 
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __builtin_amdgcn_ds_bpermute((lane_id() ^ m) << 2, v);
-  return v;
-}
-__device__ __forceinline__ int wave_max(int v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = max(v, __builtin_amdgcn_ds_bpermute((lane_id() ^ m) << 2, v));
-  return v;
-}
-// Inclusive prefix sum over the 64 lanes.
-__device__ __forceinline__ int wave_incl_sum(int v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __builtin_amdgcn_ds_bpermute((lane >= d ? lane - d : lane) << 2, v);
-    if (lane >= d) v += y;
-  }
-  return v;
-}
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // Key range of one request: positions [lo, hi), tiles lo / 32 ... lo / 32 + nt - 1.
