@@ -30,6 +30,7 @@ from .attention import (  # noqa: F401
     fp8_bits_to_f64,
     gqa_decode,
     gqa_partials,
+    gqa_verify,
     merge_partials,
     mla_verify,
     row_key_range,

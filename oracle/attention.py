@@ -25,6 +25,11 @@ Parity status per function (what pins it, see tests/test_oracle_pins.py):
                                    "Atención paginada", marker keys,
                                    permutation invariance, window and sink
                                    special cases.
+* ``gqa_verify``                   pinned: reduces to ``gqa_decode`` at
+                                   qlen = 1; each row equals a one-token
+                                   decode over its own prefix (hand-computed
+                                   limits); dense causal brute force with a
+                                   window and sinks; empty rows.
 * ``mla_verify``                   pinned: dense causal brute force, marker
                                    keys at the row limit, empty rows.
 * ``gqa_partials``/``merge_partials`` pinned: equality across split counts,
@@ -220,6 +225,48 @@ def gqa_decode(q_bits, kv_bits, block_table, seq_lens, sm_scale, sinks=None,
             sk = None if sinks is None else np.asarray(sinks, np.float64)[hs]
             O[b, hs], lse[b, hs] = attend(q[b, hs], rows[:, :D], rows[:, D:],
                                           sm_scale, sk)
+    return O, lse
+
+
+def gqa_verify(q_bits, kv_bits, block_table, seq_lens, qlen: int, sm_scale,
+               sinks=None, window: int = 0, real_seq_lens=None):
+    """Paged GQA causal verify: qlen query tokens per request, in float64.
+
+    The verify form of GQA decode.  The rows, their limits and the output
+    layout are those of "vllm.v1.attention.ops.triton_decode_attention",
+    ``decode_attention_fwd_verify`` (q [B * qlen, H, D] with the verify
+    tokens of a request contiguous; row t of request b attends keys below
+    ``hi = max(min(L - qlen + 1 + t, L_real), 0)``; one block-table row per
+    request); the cache layout, the query-head grouping, the sinks and the
+    sliding window are those of ``gqa_decode`` ("vllm.models.flint.ops.
+    decode_attention").  The window of row t covers its last ``window``
+    keys, ``[max(hi - window, 0), hi)``.
+
+    Returns ``(O [B * qlen, Hq, D], LSE [B * qlen, Hq])``.  With qlen = 1 and
+    no real lengths this is ``gqa_decode``.
+    """
+    q = bf16_bits_to_f64(q_bits)
+    kv = np.asarray(kv_bits)
+    rows, Hq, D = q.shape
+    _, Hkv, P, two_d = kv.shape
+    assert two_d == 2 * D and Hq % Hkv == 0 and rows % qlen == 0
+    G = Hq // Hkv
+    B = rows // qlen
+    O = np.zeros((rows, Hq, D))
+    lse = np.full((rows, Hq), -np.inf)
+    for b in range(B):
+        L = int(seq_lens[b])
+        L_real = None if real_seq_lens is None else int(real_seq_lens[b])
+        for t in range(qlen):
+            r = b * qlen + t
+            lo, hi = row_key_range(L, qlen, t, L_real, window)
+            pages, slots = _gather_positions(block_table[b], np.arange(lo, hi), P)
+            for kvh in range(Hkv):
+                kvrows = bf16_bits_to_f64(kv[pages, kvh, slots, :])   # [n, 2D]
+                hs = slice(kvh * G, (kvh + 1) * G)
+                sk = None if sinks is None else np.asarray(sinks, np.float64)[hs]
+                O[r, hs], lse[r, hs] = attend(q[r, hs], kvrows[:, :D], kvrows[:, D:],
+                                              sm_scale, sk)
     return O, lse
 
 

@@ -367,6 +367,70 @@ def test_merge_all_empty_and_nan_in_empty_slots():
 
 
 # ---------------------------------------------------------------------------
+# GQA causal verify
+# ---------------------------------------------------------------------------
+
+def _rand_gqa_verify(rng, lens, qlen, Hq, Hkv, D, P):
+    """Tiny random GQA verify inputs: q has qlen rows per request."""
+    q1, kv, bt, sl, sk = _rand_gqa(rng, len(lens), Hq, Hkv, D, P, lens, sinks=True)
+    q = _bf16(rng.standard_normal((len(lens) * qlen, Hq, D)))
+    return q, kv, bt, sl, sk
+
+
+def test_gqa_verify_qlen1_is_decode():
+    rng = np.random.default_rng(21)
+    lens = [7, 10, 0, 3]
+    q, kv, bt, sl, sk = _rand_gqa(rng, 4, 8, 2, 8, 4, lens, sinks=True)
+    for window in (0, 4):
+        O, lse = oracle.gqa_decode(q, kv, bt, sl, 0.3, sinks=sk, window=window)
+        O2, lse2 = oracle.gqa_verify(q, kv, bt, sl, 1, 0.3, sinks=sk, window=window)
+        assert np.array_equal(O, O2) and np.array_equal(lse, lse2)
+
+
+def test_gqa_verify_rows_are_prefix_decodes():
+    """Row t of a request is a one-token decode over the request's first
+    hi_t keys (limits worked out by hand for L = [9, 5, 2], L_real = [7, 5, 2],
+    qlen = 3), with its own sliding window."""
+    rng = np.random.default_rng(22)
+    lens, real, qlen, Hq, Hkv, D, P = [9, 5, 2], [7, 5, 2], 3, 4, 2, 8, 4
+    his = [[7, 7, 7], [3, 4, 5], [0, 1, 2]]
+    q, kv, bt, sl, sk = _rand_gqa_verify(rng, lens, qlen, Hq, Hkv, D, P)
+    for window in (0, 2):
+        O, lse = oracle.gqa_verify(q, kv, bt, sl, qlen, 0.3, sinks=sk, window=window,
+                                   real_seq_lens=np.array(real))
+        for b in range(3):
+            for t in range(qlen):
+                r = b * qlen + t
+                O1, lse1 = oracle.gqa_decode(q[r:r + 1], kv, bt[b:b + 1],
+                                             np.array([his[b][t]]), 0.3, sinks=sk, window=window)
+                np.testing.assert_array_equal(O[r], O1[0])
+                np.testing.assert_array_equal(lse[r], lse1[0])
+    # rows with no key: O = 0, LSE = -inf
+    assert np.all(O[6] == 0) and np.all(lse[6] == -np.inf)
+
+
+def test_gqa_verify_matches_causal_dense_brute_force():
+    rng = np.random.default_rng(23)
+    lens, qlen, Hq, Hkv, D, P, W = [11, 6], 4, 4, 2, 8, 4, 5
+    q, kv, bt, sl, sk = _rand_gqa_verify(rng, lens, qlen, Hq, Hkv, D, P)
+    O, lse = oracle.gqa_verify(q, kv, bt, sl, qlen, 0.3, sinks=sk, window=W)
+    qf = oa.bf16_bits_to_f64(q)
+    for b, L in enumerate(lens):
+        rows = np.stack([oa.bf16_bits_to_f64(kv[bt[b, j // P], :, j % P, :]) for j in range(L)])
+        for t in range(qlen):
+            r = b * qlen + t
+            last = L - qlen + t          # the token's own position: it sees keys 0..last
+            for kvh in range(Hkv):
+                hs = slice(2 * kvh, 2 * kvh + 2)
+                mask = np.zeros((2, L), bool)
+                mask[:, max(last + 1 - W, 0):last + 1] = True
+                O2, lse2 = _loop_attention(qf[r, hs], rows[:, kvh, :D], rows[:, kvh, D:], 0.3,
+                                           mask, sk[hs])
+                np.testing.assert_allclose(O[r, hs], O2, atol=1e-13, rtol=0)
+                np.testing.assert_allclose(lse[r, hs], lse2, atol=1e-13, rtol=0)
+
+
+# ---------------------------------------------------------------------------
 # MLA causal verify
 # ---------------------------------------------------------------------------
 
@@ -506,6 +570,24 @@ def test_mutant_row_limit_minus_one_is_caught(monkeypatch):
                          max(orig(L, qlen, t, real_len, window)[1] - 1, 0)))
     assert _fails(test_mla_marker_at_row_limit_and_empty_rows)
     assert _fails(test_gqa_worked_block_table_example, "reading_L")
+
+
+def test_mutant_verify_row_index_ignored_is_caught(monkeypatch):
+    orig = oa.row_key_range
+    monkeypatch.setattr(oa, "row_key_range",
+                        lambda L, qlen=1, t=0, real_len=None, window=0:
+                        orig(L, qlen, qlen - 1, real_len, window))
+    assert _fails(test_gqa_verify_rows_are_prefix_decodes)
+    assert _fails(test_gqa_verify_matches_causal_dense_brute_force)
+
+
+def test_mutant_row_limit_plus_one_is_caught_in_gqa_verify(monkeypatch):
+    orig = oa.row_key_range
+    monkeypatch.setattr(oa, "row_key_range",
+                        lambda L, qlen=1, t=0, real_len=None, window=0:
+                        (orig(L, qlen, t, real_len, window)[0],
+                         orig(L, qlen, t, real_len, window)[1] + 1))
+    assert _fails(test_gqa_verify_matches_causal_dense_brute_force)
 
 
 def test_mutant_window_off_by_one_is_caught(monkeypatch):
