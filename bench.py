@@ -10,7 +10,7 @@ Printed: ONE JSON line with KV-read GB/s (algorithmic K+V bytes of the
 attended keys / time per call), the roofline of the dominant kernel measured
 with HIP events on the launch stream, and the fp64 CPU oracle's rate on the
 same inputs.  ``--config`` selects another workload (gqa_window, gqa_skewed,
-tiny_gqa, mla_verify, mla_verify_fp8).
+tiny_gqa, gqa_verify, mla_verify, mla_verify_fp8).
 """
 
 from __future__ import annotations
@@ -58,9 +58,25 @@ def _gqa_case(name, torch, pd, splits):
     bt = torch.from_numpy(w.block_table).cuda()
     sl = torch.from_numpy(w.seq_lens).cuda()
     S = splits or pd.gqa_split_cap(w.B, w.Hkv, int(w.seq_lens.max()), w.window)
-    out = torch.empty((w.B, w.Hq, w.D), dtype=torch.bfloat16, device="cuda")
-    lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device="cuda")
-    ws = pd.alloc_workspace(w.B, w.Hq, max(S, 2), w.D, "cuda")
+    out = torch.empty((w.rows, w.Hq, w.D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.rows, w.Hq), dtype=torch.float32, device="cuda")
+    ws = pd.alloc_workspace(w.rows, w.Hq, max(S, 2), w.D, "cuda")
+
+    if w.qlen > 1 or w.real_seq_lens is not None:
+        real = None if w.real_seq_lens is None else torch.from_numpy(w.real_seq_lens).cuda()
+
+        def verify_step():
+            pd.paged_verify_gqa(vals["q"], vals["kv"], bt, sl, w.qlen, w.sm_scale,
+                                sinks=vals["sinks"], window=w.window, real_seq_lens=real,
+                                num_kv_splits=S, workspace=ws, out=out, lse=lse)
+
+        desc = (f"GQA causal verify with sinks: B={w.B}, qlen={w.qlen}, Hq={w.Hq}, "
+                f"Hkv={w.Hkv}, D={w.D}, page {w.P} HND bf16, seq_lens U[1024,8192], "
+                "real length L - U{0,1}, 40000-page pool")
+        # the kernel and its merge are timed together (no partials-only verify entry)
+        return dict(w=w, vals=vals, S=S, step=verify_step, kernel=None, rest=None,
+                    kv_bytes=w.kv_bytes(), flops=w.flops(), desc=desc, kind="gqa_verify",
+                    kernel_name="gqa_decode_kernel")
 
     def step():
         pd.paged_decode_gqa(vals["q"], vals["kv"], bt, sl, w.sm_scale, sinks=vals["sinks"],
@@ -177,6 +193,17 @@ def _cpu_baseline(case, budget_s=20.0):
             t_total += time.perf_counter() - t0
             lo = max(int(w.seq_lens[b]) - w.window, 0) if w.window > 0 else 0
             done_bytes += (int(w.seq_lens[b]) - lo) * w.Hkv * 2 * w.D * 2
+        elif case["kind"] == "gqa_verify":
+            rows = slice(b * w.qlen, (b + 1) * w.qlen)
+            q = vals["q"][rows].view(torch.int16).cpu().numpy().view(np.uint16)
+            sinks = None if vals["sinks"] is None else vals["sinks"].cpu().numpy()
+            real = None if w.real_seq_lens is None else w.real_seq_lens[b:b + 1]
+            t0 = time.perf_counter()
+            oracle.gqa_verify(q, kv, bt2, w.seq_lens[b:b + 1], w.qlen, w.sm_scale,
+                              sinks=sinks, window=w.window, real_seq_lens=real)
+            t_total += time.perf_counter() - t0
+            lo, hi = w.key_range(b)
+            done_bytes += max(hi - lo, 0) * w.Hkv * 2 * w.D * 2
         else:
             rows = slice(b * w.qlen, (b + 1) * w.qlen)
             q = vals["q"][rows].view(torch.int16).cpu().numpy().view(np.uint16)
@@ -258,7 +285,7 @@ def main():
 
     kv = case["kv_bytes"]
     value = kv / (ms_per_step * 1e-3) / 1e9
-    if case["kind"] == "gqa":
+    if case["kind"] in ("gqa", "gqa_verify"):
         roof = {"bound": "hbm", "achieved": round(kv / (k_ms * 1e-3) / 1e9, 2),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     else:

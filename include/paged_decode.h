@@ -6,6 +6,7 @@
  *
  *   paged_decode_gqa   one query token per request, grouped-query heads,
  *                      optional per-head sinks and a sliding window;
+ *   paged_verify_gqa   the same with qlen causal verify tokens per request;
  *   paged_verify_mla   qlen causal "verify" tokens per request over one shared
  *                      latent cache, V read as K[..., :Lv], bf16 or FP8 cache;
  *   num_kv_splits_cap  static split cap from static sizes (graph-capture safe);
@@ -163,6 +164,47 @@ PD_API int paged_decode_gqa(const void* q, int64_t q_stride_b, int64_t q_stride_
                      int32_t num_kv_splits, float* workspace, size_t workspace_bytes,
                      void* out, int64_t o_stride_b, int64_t o_stride_h,
                      float* lse, int64_t lse_stride_b, void* stream);
+
+/*
+ * paged_verify_gqa - paged GQA causal verify, qlen query tokens per request.
+ *
+ * The verify form of paged_decode_gqa.  Rows and limits follow
+ * "vllm.v1.attention.ops.triton_decode_attention",
+ * decode_attention_fwd_verify: the qlen verify tokens of request b are rows
+ * b*qlen + t (t = 0..qlen-1) of q, out and lse, and row t attends key
+ * positions [lo_t, hi_t) with
+ *   hi_t = max(min(L - qlen + 1 + t, L_real), 0),  L = seq_lens[b],
+ *   L_real = real_seq_lens[b] (or L when real_seq_lens is NULL),
+ *   lo_t = max(hi_t - window, 0) for window > 0 (its own last `window`
+ *   keys), else 0.
+ * The cache, the block table, the head grouping, the sinks and O / LSE are
+ * as for paged_decode_gqa (per row instead of per request); the block table
+ * has one row per request shared by its qlen rows.  A row with no key gets
+ * O = 0 and LSE = -inf.  qlen = 1 with real_seq_lens NULL is
+ * paged_decode_gqa.
+ *
+ * q            [B*qlen, Hq, D] bf16, strides (q_stride_row, q_stride_h, 1).
+ * real_seq_lens [B] int32 or NULL.
+ * out          [B*qlen, Hq, D] bf16, strides (o_stride_row, o_stride_h, 1).
+ * lse          [B*qlen, Hq] fp32 with row stride lse_stride_row, or NULL.
+ * workspace    >= pd_workspace_bytes(B*qlen, Hq, S, D) bytes when S > 1.
+ * Other arguments as for paged_decode_gqa.
+ *
+ * Supported: as paged_decode_gqa, with qlen * G <= 16 (the verify tokens of a
+ * kv head's query heads share one score tile, so a cache tile is read once
+ * for all of them); otherwise PD_ERR_UNSUPPORTED.  Also
+ * ((qlen-1)*q_stride_row + (G-1)*q_stride_h + D) * 2 < 2^31.
+ */
+PD_API int paged_verify_gqa(const void* q, int64_t q_stride_row, int64_t q_stride_h,
+                     const void* kv, int64_t kv_stride_page, int64_t kv_stride_head,
+                     int32_t num_pages, const int32_t* block_table, int64_t bt_stride_b,
+                     int32_t max_blocks, const int32_t* seq_lens,
+                     const int32_t* real_seq_lens, int32_t qlen, const float* sinks,
+                     int32_t window, float sm_scale, int32_t batch, int32_t num_q_heads,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                     int32_t num_kv_splits, float* workspace, size_t workspace_bytes,
+                     void* out, int64_t o_stride_row, int64_t o_stride_h,
+                     float* lse, int64_t lse_stride_row, void* stream);
 
 /*
  * paged_decode_gqa_partials - the split partials of paged_decode_gqa only.

@@ -26,6 +26,7 @@ EXPORTS = (
     "num_kv_splits_cap",
     "pd_workspace_bytes",
     "paged_decode_gqa",
+    "paged_verify_gqa",
     "paged_decode_gqa_partials",
     "paged_verify_mla",
     "merge_splits",
@@ -66,6 +67,18 @@ def _load():
         _c_vp, _c_i64, _c_vp,                   # lse, stride, stream
     ]
     lib.paged_decode_gqa.restype = ctypes.c_int
+    lib.paged_verify_gqa.argtypes = [
+        _c_vp, _c_i64, _c_i64,                  # q, strides
+        _c_vp, _c_i64, _c_i64, _c_i32,          # kv, page/head strides, num_pages
+        _c_vp, _c_i64, _c_i32,                  # block_table, row stride, max_blocks
+        _c_vp, _c_vp, _c_i32,                   # seq_lens, real_seq_lens, qlen
+        _c_vp, _c_i32, _c_f32,                  # sinks, window, sm_scale
+        _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,  # B, Hq, Hkv, D, P
+        _c_i32, _c_vp, _c_sz,                   # splits, workspace, bytes
+        _c_vp, _c_i64, _c_i64,                  # out, strides
+        _c_vp, _c_i64, _c_vp,                   # lse, stride, stream
+    ]
+    lib.paged_verify_gqa.restype = ctypes.c_int
     lib.paged_decode_gqa_partials.argtypes = [
         _c_vp, _c_i64, _c_i64,                  # q, strides
         _c_vp, _c_i64, _c_i64, _c_i32,          # kv, page/head strides, num_pages

@@ -138,6 +138,66 @@ def paged_decode_gqa(q, kv, block_table, seq_lens, sm_scale, sinks=None, window=
     return out, lse
 
 
+def paged_verify_gqa(q, kv, block_table, seq_lens, qlen, sm_scale, sinks=None, window=0,
+                     real_seq_lens=None, num_kv_splits=1, workspace=None, out=None, lse=None,
+                     stream=None, return_lse=True):
+    """Paged GQA causal verify (include/paged_decode.h: paged_verify_gqa).
+
+    q [B*qlen, Hq, D] bf16 (the qlen tokens of a request contiguous); kv
+    [num_pages, Hkv, P, 2D] bf16; block_table [B, max_blocks] int32; seq_lens
+    and real_seq_lens (or None) [B] int32; sinks [Hq] fp32 or None.
+    Returns (out [B*qlen, Hq, D] bf16, lse [B*qlen, Hq] fp32 or None).
+    """
+    _need(q, "q", torch.bfloat16, 3)
+    _need(kv, "kv", torch.bfloat16, 4)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    qlen = int(qlen)
+    rows, Hq, D = q.shape
+    if qlen < 1 or rows % qlen != 0:
+        raise ValueError("q must have qlen rows per request")
+    B = rows // qlen
+    num_pages, Hkv, P, two_d = kv.shape
+    if two_d != 2 * D or kv.stride(3) != 1 or kv.stride(2) != 2 * D or q.stride(2) != 1:
+        raise ValueError("kv must be [pages, Hkv, P, 2D] with contiguous token rows")
+    if block_table.shape[0] != B or seq_lens.shape[0] != B or block_table.stride(1) != 1:
+        raise ValueError("block_table / seq_lens must have one row per request")
+    if real_seq_lens is not None:
+        _need(real_seq_lens, "real_seq_lens", torch.int32, 1)
+        if real_seq_lens.shape[0] != B or real_seq_lens.stride(0) != 1:
+            raise ValueError("real_seq_lens must be a contiguous [B] tensor")
+    if sinks is not None:
+        _need(sinks, "sinks", torch.float32, 1)
+        if sinks.shape[0] != Hq or sinks.stride(0) != 1:
+            raise ValueError("sinks must be a contiguous [Hq] tensor")
+    if out is None:
+        out = torch.empty((rows, Hq, D), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", torch.bfloat16, 3)
+    if out.stride(2) != 1:
+        raise ValueError("out must have a contiguous last dim")
+    if lse is None and return_lse:
+        lse = torch.empty((rows, Hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 2)
+        if lse.stride(1) != 1:
+            raise ValueError("lse must have a contiguous last dim")
+    S = int(num_kv_splits)
+    if S > 1 and workspace is None:
+        workspace = alloc_workspace(rows, Hq, S, D, q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.paged_verify_gqa(
+        _ptr(q), q.stride(0), q.stride(1),
+        _ptr(kv), kv.stride(0), kv.stride(1), num_pages,
+        _ptr(block_table), block_table.stride(0), block_table.shape[1],
+        _ptr(seq_lens), _ptr(real_seq_lens), qlen,
+        _ptr(sinks), int(window or 0), float(sm_scale),
+        B, Hq, Hkv, D, P, S, _ptr(workspace), ws_bytes,
+        _ptr(out), out.stride(0), out.stride(1),
+        _ptr(lse), 0 if lse is None else lse.stride(0), _stream(stream))
+    check("paged_verify_gqa", st)
+    return out, lse
+
+
 def paged_decode_gqa_partials(q, kv, block_table, seq_lens, sm_scale, window=0,
                               num_kv_splits=1, workspace=None, stream=None):
     """Split partials of paged_decode_gqa without the merge

@@ -93,20 +93,23 @@ size_t pd_workspace_bytes(int32_t rows, int32_t num_heads, int32_t num_splits, i
 
 namespace {
 
+// GQA decode and verify.  Rows of q / out / lse are (request, verify token)
+// pairs, row b * qlen + t; decode is qlen = 1 with no real lengths.
 static int gqa_common(const void* q, int64_t q_stride_b, int64_t q_stride_h, const void* kv,
                int64_t kv_stride_page, int64_t kv_stride_head, int32_t num_pages,
                const int32_t* block_table, int64_t bt_stride_b, int32_t max_blocks,
-               const int32_t* seq_lens, const float* sinks, int32_t window, float sm_scale,
+               const int32_t* seq_lens, const int32_t* real_seq_lens, int32_t qlen,
+               const float* sinks, int32_t window, float sm_scale,
                int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                int32_t page_size, int32_t num_kv_splits, float* workspace,
                size_t workspace_bytes, void* out, int64_t o_stride_b, int64_t o_stride_h,
                float* lse, int64_t lse_stride_b, void* stream, bool partials_only) {
-  if (batch < 0 || num_q_heads < 1 || num_kv_heads < 1 || num_kv_splits < 1 ||
+  if (batch < 0 || qlen < 1 || num_q_heads < 1 || num_kv_heads < 1 || num_kv_splits < 1 ||
       num_pages < 0 || max_blocks < 0 || !std::isfinite(sm_scale) || !(sm_scale > 0.f))
     return PD_ERR_INVALID;
   if (num_q_heads % num_kv_heads != 0) return PD_ERR_INVALID;
   const int32_t G = num_q_heads / num_kv_heads;
-  if (head_dim != 128 || (page_size != 16 && page_size != 32) || G > 16)
+  if (head_dim != 128 || (page_size != 16 && page_size != 32) || (int64_t)qlen * G > 16)
     return PD_ERR_UNSUPPORTED;
   if (batch == 0) return PD_OK;
   if (q == nullptr || kv == nullptr || block_table == nullptr || seq_lens == nullptr ||
@@ -119,9 +122,11 @@ static int gqa_common(const void* q, int64_t q_stride_b, int64_t q_stride_h, con
       kv_stride_page % 8 || kv_stride_head % 8)
     return PD_ERR_ALIGN;
   if (!partials_only && (!aligned16(out) || o_stride_b % 8 || o_stride_h % 8)) return PD_ERR_ALIGN;
+  const int64_t rows = (int64_t)batch * qlen;
+  if (rows > 0x7fffffff) return PD_ERR_UNSUPPORTED;
   if (num_kv_splits > 1 || partials_only) {
     const int32_t ws_splits = num_kv_splits > 1 ? num_kv_splits : 2;
-    size_t need = pd_workspace_bytes(batch, num_q_heads, ws_splits, head_dim);
+    size_t need = pd_workspace_bytes((int32_t)rows, num_q_heads, ws_splits, head_dim);
     if (num_kv_splits == 1) need /= 2;
     if (workspace == nullptr || workspace_bytes < need) return PD_ERR_WORKSPACE;
     if (!aligned16(workspace)) return PD_ERR_ALIGN;
@@ -130,6 +135,9 @@ static int gqa_common(const void* q, int64_t q_stride_b, int64_t q_stride_h, con
   const int64_t kLim = INT32_MAX;
   if (q_stride_b > kLim || q_stride_h > kLim || kv_stride_page > kLim || kv_stride_head > kLim ||
       bt_stride_b > kLim || o_stride_b > kLim || o_stride_h > kLim || lse_stride_b > kLim)
+    return PD_ERR_UNSUPPORTED;
+  // a unit's query rows are addressed with a 32-bit byte offset from its first row
+  if (((int64_t)(qlen - 1) * q_stride_b + (int64_t)(G - 1) * q_stride_h + head_dim) * 2 > kLim)
     return PD_ERR_UNSUPPORTED;
   // the kernel indexes all (request, kv head, 32-token tile) triples with int32
   if ((int64_t)max_blocks * page_size > (int64_t)INT32_MAX / 2 ||
@@ -148,6 +156,8 @@ static int gqa_common(const void* q, int64_t q_stride_b, int64_t q_stride_h, con
   a.bt_sb = (int32_t)bt_stride_b;
   a.max_blocks = max_blocks;
   a.seq_lens = seq_lens;
+  a.real_lens = real_seq_lens;
+  a.qlen = qlen;
   a.sinks = sinks;
   a.window = window;
   a.scale_log2 = sm_scale * kLog2eHost;
@@ -169,7 +179,7 @@ static int gqa_common(const void* q, int64_t q_stride_b, int64_t q_stride_h, con
   if (num_kv_splits > 1 && !partials_only) {
     pd::MergeArgs m{};
     m.ws = workspace;
-    m.rows = batch;
+    m.rows = (int32_t)rows;
     m.H = num_q_heads;
     m.S = num_kv_splits;
     m.Dv = head_dim;
@@ -195,10 +205,26 @@ int paged_decode_gqa(const void* q, int64_t q_stride_b, int64_t q_stride_h, cons
                      size_t workspace_bytes, void* out, int64_t o_stride_b, int64_t o_stride_h,
                      float* lse, int64_t lse_stride_b, void* stream) {
   return gqa_common(q, q_stride_b, q_stride_h, kv, kv_stride_page, kv_stride_head, num_pages,
-                    block_table, bt_stride_b, max_blocks, seq_lens, sinks, window, sm_scale,
-                    batch, num_q_heads, num_kv_heads, head_dim, page_size, num_kv_splits,
-                    workspace, workspace_bytes, out, o_stride_b, o_stride_h, lse, lse_stride_b,
-                    stream, false);
+                    block_table, bt_stride_b, max_blocks, seq_lens, nullptr, 1, sinks, window,
+                    sm_scale, batch, num_q_heads, num_kv_heads, head_dim, page_size,
+                    num_kv_splits, workspace, workspace_bytes, out, o_stride_b, o_stride_h, lse,
+                    lse_stride_b, stream, false);
+}
+
+int paged_verify_gqa(const void* q, int64_t q_stride_row, int64_t q_stride_h, const void* kv,
+                     int64_t kv_stride_page, int64_t kv_stride_head, int32_t num_pages,
+                     const int32_t* block_table, int64_t bt_stride_b, int32_t max_blocks,
+                     const int32_t* seq_lens, const int32_t* real_seq_lens, int32_t qlen,
+                     const float* sinks, int32_t window, float sm_scale, int32_t batch,
+                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                     int32_t page_size, int32_t num_kv_splits, float* workspace,
+                     size_t workspace_bytes, void* out, int64_t o_stride_row, int64_t o_stride_h,
+                     float* lse, int64_t lse_stride_row, void* stream) {
+  return gqa_common(q, q_stride_row, q_stride_h, kv, kv_stride_page, kv_stride_head, num_pages,
+                    block_table, bt_stride_b, max_blocks, seq_lens, real_seq_lens, qlen, sinks,
+                    window, sm_scale, batch, num_q_heads, num_kv_heads, head_dim, page_size,
+                    num_kv_splits, workspace, workspace_bytes, out, o_stride_row, o_stride_h,
+                    lse, lse_stride_row, stream, false);
 }
 
 int paged_decode_gqa_partials(const void* q, int64_t q_stride_b, int64_t q_stride_h,
@@ -210,9 +236,10 @@ int paged_decode_gqa_partials(const void* q, int64_t q_stride_b, int64_t q_strid
                               int32_t page_size, int32_t num_kv_splits, float* workspace,
                               size_t workspace_bytes, void* stream) {
   return gqa_common(q, q_stride_b, q_stride_h, kv, kv_stride_page, kv_stride_head, num_pages,
-                    block_table, bt_stride_b, max_blocks, seq_lens, nullptr, window, sm_scale,
-                    batch, num_q_heads, num_kv_heads, head_dim, page_size, num_kv_splits,
-                    workspace, workspace_bytes, nullptr, 0, 0, nullptr, 0, stream, true);
+                    block_table, bt_stride_b, max_blocks, seq_lens, nullptr, 1, nullptr, window,
+                    sm_scale, batch, num_q_heads, num_kv_heads, head_dim, page_size,
+                    num_kv_splits, workspace, workspace_bytes, nullptr, 0, 0, nullptr, 0, stream,
+                    true);
 }
 
 int paged_verify_mla(const void* q, int64_t q_stride_row, int64_t q_stride_h, const void* kv,

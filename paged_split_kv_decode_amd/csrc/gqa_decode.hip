@@ -72,20 +72,39 @@ struct Req {
   int lo, hi, nt;
 };
 
-// Key range of a request of length L (clamped to the block-table row).
+// Length bound standing for "no real length given".
+constexpr int kNoReal = 1 << 30;
+
+// Key range of verify row t of a request of length L (clamped to the
+// block-table row) and real length Lr: [lo_t, hi_t) with
+// hi_t = max(min(L - qlen + 1 + t, Lr), 0) and, with a window,
+// lo_t = max(hi_t - window, 0).
 template <int P>
-__device__ __forceinline__ Req range_of(const GqaArgs& a, int L) {
+__device__ __forceinline__ int row_hi(const GqaArgs& a, int L, int Lr, int t) {
   L = min(max(L, 0), a.max_blocks * P);
+  return max(min(L - a.qlen + 1 + t, Lr), 0);
+}
+__device__ __forceinline__ int row_lo(const GqaArgs& a, int hi) {
+  return a.window > 0 ? max(hi - a.window, 0) : 0;
+}
+
+// Keys of a request: the union of its rows' ranges, [lo_0, hi_{qlen-1}).
+template <int P>
+__device__ __forceinline__ Req range_of(const GqaArgs& a, int L, int Lr) {
   Req r;
-  r.hi = L;
-  r.lo = a.window > 0 ? max(L - a.window, 0) : 0;
+  r.hi = row_hi<P>(a, L, Lr, a.qlen - 1);
+  r.lo = row_lo(a, row_hi<P>(a, L, Lr, 0));
   r.nt = r.hi > r.lo ? ((r.hi + 31) >> 5) - (r.lo >> 5) : 0;
   return r;
 }
 
+__device__ __forceinline__ int real_len(const GqaArgs& a, int b) {
+  return a.real_lens != nullptr ? (int)as_const(a.real_lens)[b] : kNoReal;
+}
+
 template <int P>
 __device__ __forceinline__ Req request_range(const GqaArgs& a, int b) {
-  return range_of<P>(a, as_const(a.seq_lens)[b]);
+  return range_of<P>(a, as_const(a.seq_lens)[b], real_len(a, b));
 }
 
 // A position in one wave's tile sequence (wave-uniform).  b == B: the share
@@ -109,7 +128,9 @@ constexpr int kQSlotBytes = 16 * kD * 2;                 // query rows of one pi
 constexpr int kWaveLds = kRingBytes + 2 * kQSlotBytes;    // ring + 2 query slots = 40 KB
 constexpr int kCachedChunks = 4;                          // request lengths kept in registers (x64)
 
-template <int P>
+// V: verify rows (qlen > 1 or real lengths); the decode instantiation has a
+// single column range per unit and none of the per-column limit work.
+template <int P, bool V>
 __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[kNW * kWaveLds];
 
@@ -119,6 +140,7 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
   const int g4 = lane >> 4;
   const int l16 = lane & 15;
   const int G = a.G;
+  const int R = V ? a.qlen * G : G;   // columns in use: (verify token, head) pairs
   const int S = a.S;
   const int Hkv = a.Hkv;
   const bool direct = S == 1 && !a.partials;
@@ -127,19 +149,23 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
   const int w = uniform(blockIdx.x * kNW + wave_in_wg);
   PD_LDS char* ring = (PD_LDS char*)smem + wave_in_wg * kWaveLds;
   PD_LDS char* qslots = ring + kRingBytes;
+  // this lane's score column: verify token t_col, head g_col of the kv head
+  const int t_col = V ? min(l16, R - 1) / G : 0;
+  const int g_col = V ? min(l16, R - 1) - t_col * G : l16;
 
   // ---- the plan: total tiles, longest request, this wave's share --------
   // Lane l of chunk c holds the length of request 64c + l (0 past the batch).
-  int Lc[kCachedChunks];
+  int Lc[kCachedChunks], Lrc[kCachedChunks];
 #pragma unroll
   for (int ch = 0; ch < kCachedChunks; ++ch) {
     const int b = 64 * ch + lane;
     Lc[ch] = b < a.B ? as_const(a.seq_lens)[b] : 0;
+    Lrc[ch] = b < a.B ? real_len(a, b) : 0;
   }
   int nt_sum = 0, nt_max = 0;
 #pragma unroll
   for (int ch = 0; ch < kCachedChunks; ++ch) {
-    const int nt = range_of<P>(a, Lc[ch]).nt;
+    const int nt = range_of<P>(a, Lc[ch], Lrc[ch]).nt;
     nt_sum += wave_sum(nt);
     nt_max = max(nt_max, wave_max(nt));
   }
@@ -167,12 +193,12 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
   // ---- first unit of the share ------------------------------------------
   // split: the unit holding tile g0, or an empty unit starting at or after
   // g0; whole units: the first unit starting at or after g0.
-  int b_s = -1, L_s = 0, cb_s = 0;
+  int b_s = -1, L_s = 0, Lr_s = 0, cb_s = 0;
   {
     int C = 0;  // tiles of the requests before this chunk (one kv head)
-    auto probe = [&](int base, int L) {
+    auto probe = [&](int base, int L, int Lr) {
       const bool in = base + lane < a.B;
-      const int nt = range_of<P>(a, L).nt;
+      const int nt = range_of<P>(a, L, Lr).nt;
       const int incl = wave_incl_sum(nt);
       const int cb1 = (C + incl) * Hkv;     // flat start of request b + 1
       const int cb = cb1 - nt * Hkv;         // flat start of request b
@@ -183,6 +209,7 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
         const int l0 = __builtin_ctzll(m);
         b_s = base + l0;
         L_s = __builtin_amdgcn_readlane(L, l0);
+        Lr_s = __builtin_amdgcn_readlane(Lr, l0);
         cb_s = __builtin_amdgcn_readlane(cb, l0);
         return true;
       }
@@ -192,13 +219,15 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
     bool found = false;
 #pragma unroll
     for (int ch = 0; ch < kCachedChunks; ++ch)
-      if (!found && 64 * ch < a.B) found = probe(64 * ch, Lc[ch]);
-    for (int base = 64 * kCachedChunks; !found && base < a.B; base += 64)
-      found = probe(base, base + lane < a.B ? as_const(a.seq_lens)[base + lane] : 0);
+      if (!found && 64 * ch < a.B) found = probe(64 * ch, Lc[ch], Lrc[ch]);
+    for (int base = 64 * kCachedChunks; !found && base < a.B; base += 64) {
+      const bool in = base + lane < a.B;
+      found = probe(base, in ? as_const(a.seq_lens)[base + lane] : 0, in ? real_len(a, base + lane) : 0);
+    }
   }
   if (b_s < 0) return;
   b_s = uniform(b_s);
-  const Req r_s = range_of<P>(a, uniform(L_s));
+  const Req r_s = range_of<P>(a, uniform(L_s), uniform(Lr_s));
   int kvh_s = 0;
   if (sh.g0 > cb_s)
     kvh_s = sh.split ? (sh.g0 - cb_s) / r_s.nt : (sh.g0 - cb_s + r_s.nt - 1) / r_s.nt;
@@ -284,11 +313,13 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
   int q_issued = 0, q_used = 0;   // pieces whose query rows were loaded / read
   auto load_q = [&](const Cursor& cu) {
     const uint32_t dst = uniform((int)lds_addr(qslots + (q_issued & 1) * kQSlotBytes));
-    const char* qbase = (const char*)(a.q + (int64_t)cu.b * a.q_sb + (int64_t)cu.kvh * G * a.q_sh);
+    const char* qbase =
+        (const char*)(a.q + (int64_t)cu.b * a.qlen * a.q_sb + (int64_t)cu.kvh * G * a.q_sh);
     const int chunk = lane & 15;
-    for (int i = 0; i < (G + 3) / 4; ++i) {   // 4 heads (1 KB) per load
-      const int h = min(4 * i + (lane >> 4), G - 1);
-      const uint32_t voff = (uint32_t)(h * a.q_sh + chunk * 8) * 2u;
+    for (int i = 0; i < (R + 3) / 4; ++i) {   // 4 columns (1 KB) per load
+      const int n = min(4 * i + (lane >> 4), R - 1);
+      const int t = n / G, g = n - t * G;
+      const uint32_t voff = (uint32_t)(t * a.q_sb + g * a.q_sh + chunk * 8) * 2u;
       global_to_lds_16(qbase, voff, dst + i * 1024);
     }
     ++q_issued;
@@ -335,12 +366,16 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
   f32x4 o[8];
   bool piece_bad = false;
   int bad_slots = 0;   // bit s: the tile in ring slot s read a bad page
+  // keys of this lane's column in the current piece's request, and the
+  // range every column attends (tiles inside it need no score mask)
+  int col_lo = 0, col_hi = 0, all_lo = 0, all_hi = 0;
 
   auto finish_piece = [&](const Cursor& cu) {
     const float l_tot_part = l_run + shfl_xor(l_run, 16);
     const float l_tot = l_tot_part + shfl_xor(l_tot_part, 32);
-    const int hq = cu.kvh * G + l16;
-    if (l16 < G) {
+    const int hq = cu.kvh * G + g_col;
+    const int64_t row = (int64_t)cu.b * a.qlen + t_col;
+    if (l16 < R) {
       const bool empty = !(l_tot > 0.f);
       const float lse_nat = empty ? neg_inf() : (m_run * c + fast_log2(l_tot)) * kLn2;
       const float nan = __builtin_nanf("");
@@ -348,7 +383,7 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
         float den = l_tot;
         if (a.sinks != nullptr && !empty) den += fast_exp2(a.sinks[hq] * kLog2e - m_run * c);
         const float inv = empty ? 0.f : 1.f / den;
-        uint16_t* orow = a.out + (int64_t)cu.b * a.o_sb + (int64_t)hq * a.o_sh + 4 * g4;
+        uint16_t* orow = a.out + row * a.o_sb + (int64_t)hq * a.o_sh + 4 * g4;
 #pragma unroll
         for (int blk = 0; blk < 8; ++blk) {
           f32x4 r = o[blk] * inv;
@@ -356,10 +391,10 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
           *(u32x2*)(orow + 16 * blk) = u32x2{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
         }
         if (a.lse != nullptr && g4 == 0)
-          a.lse[(int64_t)cu.b * a.lse_sb + hq] = piece_bad ? nan : lse_nat;
+          a.lse[row * a.lse_sb + hq] = piece_bad ? nan : lse_nat;
       } else {
         const int s = sh.split ? w - cu.p0 / sh.tpw : 0;
-        float* slot = a.ws + (((int64_t)cu.b * a.Hq + hq) * S + s) * (kD + 1);
+        float* slot = a.ws + ((row * a.Hq + hq) * S + s) * (kD + 1);
         const float inv = empty ? 0.f : 1.f / l_tot;
 #pragma unroll
         for (int blk = 0; blk < 8; ++blk) {
@@ -390,6 +425,13 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         piece_bad = false;
+        if constexpr (V) {
+          const int L = as_const(a.seq_lens)[cc.b], Lr = real_len(a, cc.b);
+          col_hi = row_hi<P>(a, L, Lr, t_col);
+          col_lo = row_lo(a, col_hi);
+          all_hi = uniform(row_hi<P>(a, L, Lr, 0));                 // first row's limit
+          all_lo = uniform(row_lo(a, row_hi<P>(a, L, Lr, a.qlen - 1)));   // last row's start
+        }
       }
 
       const bool issuing = ci.b < a.B;
@@ -413,7 +455,7 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const bf16x8 v = *(PD_LDS const bf16x8*)(qs + (8 * g4 + 32 * s) * 2);
-          qf[s] = l16 < G ? v : bf16x8{};
+          qf[s] = l16 < R ? v : bf16x8{};
         }
         ++q_used;
       }
@@ -436,6 +478,8 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
         s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[s], s1, 0, 0, 0);
       }
 
+      // V rows outside the request's keys are zeroed; scores outside the
+      // lane's column range are -inf (the two differ only for verify rows)
       const bool edge = tok0 < lo || tok0 + kTileTokens > hi;
       bool v0[4], v1[4];
 #pragma unroll
@@ -443,8 +487,14 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
         const int t0 = tok0 + 4 * g4 + i, t1 = t0 + 16;
         v0[i] = !edge || (t0 >= lo && t0 < hi);
         v1[i] = !edge || (t1 >= lo && t1 < hi);
-        if (!v0[i]) s0[i] = neg_inf();
-        if (!v1[i]) s1[i] = neg_inf();
+        if constexpr (V) {
+          const bool col_edge = tok0 < all_lo || tok0 + kTileTokens > all_hi;
+          if (col_edge && !(t0 >= col_lo && t0 < col_hi)) s0[i] = neg_inf();
+          if (col_edge && !(t1 >= col_lo && t1 < col_hi)) s1[i] = neg_inf();
+        } else {
+          if (!v0[i]) s0[i] = neg_inf();
+          if (!v1[i]) s1[i] = neg_inf();
+        }
       }
 
       // ---- online softmax (fp32, exp2, running max in unscaled logits) ----
@@ -512,24 +562,27 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
   cw.r = r_s;
   while (cw.b < a.B && (sh.last || cw.p0 < sh.g1)) {
     const int hq0 = cw.kvh * G;
+    // (row, query head) of column n of this unit
+    auto col_row = [&](int n) { return (int64_t)cw.b * a.qlen + n / G; };
+    auto col_head = [&](int n) { return hq0 + n % G; };
     if (cw.r.nt == 0) {
       if (direct) {
-        for (int i = lane; i < G * (kD / 8); i += 64) {
-          const int h = i / (kD / 8), d8 = (i % (kD / 8)) * 8;
-          *(u32x4*)(a.out + (int64_t)cw.b * a.o_sb + (int64_t)(hq0 + h) * a.o_sh + d8) = u32x4{0, 0, 0, 0};
+        for (int i = lane; i < R * (kD / 8); i += 64) {
+          const int n = i / (kD / 8), d8 = (i % (kD / 8)) * 8;
+          *(u32x4*)(a.out + col_row(n) * a.o_sb + (int64_t)col_head(n) * a.o_sh + d8) = u32x4{0, 0, 0, 0};
         }
-        if (a.lse != nullptr && lane < G) a.lse[(int64_t)cw.b * a.lse_sb + hq0 + lane] = neg_inf();
+        if (a.lse != nullptr && lane < R) a.lse[col_row(lane) * a.lse_sb + col_head(lane)] = neg_inf();
       } else {
-        for (int i = lane; i < G * S; i += 64) {
-          const int h = i / S, s = i % S;
-          a.ws[(((int64_t)cw.b * a.Hq + hq0 + h) * S + s) * (kD + 1) + kD] = neg_inf();
+        for (int i = lane; i < R * S; i += 64) {
+          const int n = i / S, s = i % S;
+          a.ws[((col_row(n) * a.Hq + col_head(n)) * S + s) * (kD + 1) + kD] = neg_inf();
         }
       }
     } else if (sh.split && cw.p0 >= sh.g0) {
       const int nseg = (cw.p0 + cw.r.nt - 1) / sh.tpw - cw.p0 / sh.tpw + 1;
-      for (int i = lane; i < G * (S - nseg); i += 64) {
-        const int h = i / (S - nseg), s = nseg + i % (S - nseg);
-        a.ws[(((int64_t)cw.b * a.Hq + hq0 + h) * S + s) * (kD + 1) + kD] = neg_inf();
+      for (int i = lane; i < R * (S - nseg); i += 64) {
+        const int n = i / (S - nseg), s = nseg + i % (S - nseg);
+        a.ws[((col_row(n) * a.Hq + col_head(n)) * S + s) * (kD + 1) + kD] = neg_inf();
       }
     }
     next_unit(cw);
@@ -556,9 +609,12 @@ hipError_t launch_gqa_decode(const GqaArgs& a, hipStream_t stream) {
   const int n = grid_size();
   if (n <= 0) return hipErrorInvalidDevice;
   dim3 grid(n), block(kNW * 64);
-  switch (a.P) {
-    case 16: hipLaunchKernelGGL((gqa_decode_kernel<16>), grid, block, 0, stream, a); break;
-    case 32: hipLaunchKernelGGL((gqa_decode_kernel<32>), grid, block, 0, stream, a); break;
+  const bool verify = a.qlen > 1 || a.real_lens != nullptr;
+  switch (a.P * 2 + (verify ? 1 : 0)) {
+    case 32: hipLaunchKernelGGL((gqa_decode_kernel<16, false>), grid, block, 0, stream, a); break;
+    case 33: hipLaunchKernelGGL((gqa_decode_kernel<16, true>), grid, block, 0, stream, a); break;
+    case 64: hipLaunchKernelGGL((gqa_decode_kernel<32, false>), grid, block, 0, stream, a); break;
+    case 65: hipLaunchKernelGGL((gqa_decode_kernel<32, true>), grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -15,9 +15,11 @@ constexpr int kMlaMinSplitTiles = 4;
 
 // Strides are in elements and below 2^31 (checked on the host), so the
 // kernel keeps them in 32-bit scalar registers.
+// GQA decode is the qlen = 1 case of GQA verify: q / out / lse rows are
+// (request, verify token) pairs, row b * qlen + t.
 struct GqaArgs {
   const uint16_t* q;
-  int32_t q_sb, q_sh;
+  int32_t q_sb, q_sh;   // q_sb: stride between rows
   const uint16_t* kv;
   int32_t kv_sp, kv_sh;
   int32_t num_pages;
@@ -25,13 +27,15 @@ struct GqaArgs {
   int32_t bt_sb;
   int32_t max_blocks;
   const int32_t* seq_lens;
+  const int32_t* real_lens;  // nullptr: equal to seq_lens
+  int32_t qlen;              // verify tokens per request; qlen * G <= 16
   const float* sinks;
   int32_t window;
   float scale_log2;  // sm_scale * log2(e)
   int32_t B, Hq, Hkv, G, P;
   int32_t S;         // split cap: no (request, kv head) is cut into more pieces
   int32_t partials;  // 1: always write workspace partials (never O / LSE)
-  float* ws;         // [B, Hq, S, D + 1] when S > 1 or partials
+  float* ws;         // [B * qlen, Hq, S, D + 1] when S > 1 or partials
   uint16_t* out;
   int32_t o_sb, o_sh;
   float* lse;

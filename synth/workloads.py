@@ -25,6 +25,9 @@ Recipe (one line per configuration, seeds: structure ``2000 + n``, values
 5. ``gqa_skewed``  B=256, Hq=32, Hkv=8, D=128, page 16,
    L = floor(exp(U[ln 16, ln 131072])) with 4 seeded requests at L = 0;
    pool = sum of pages, permuted, 8192 blocks per row, no sinks.
+6. ``gqa_verify``  GQA causal verify: as 2 (sinks, L ~ U[1024, 8192]) with
+   qlen = 2 verify tokens per request (q [B * 2, Hq, D]) and real length
+   L - U{0, 1}.
 
 Never-attended cache slots (unreferenced pages, slots past L, slots before a
 window) can be NaN-poisoned so that any stray read shows up in the output.
@@ -53,6 +56,9 @@ CONFIGS = {
     "gqa_skewed": dict(index=5, B=256, Hq=32, Hkv=8, D=128, P=16,
                        loguniform=(16, 131072), zero_lens=4, max_blocks=8192,
                        pool=0, window=0, sinks=False),
+    "gqa_verify": dict(index=6, B=64, Hq=64, Hkv=8, D=128, P=16, len_range=(1024, 8192),
+                       max_blocks=512, pool=40000, window=0, sinks=True, qlen=2,
+                       real_drop=(0, 1)),
 }
 
 
@@ -102,6 +108,8 @@ class GqaWorkload:
     window: int
     has_sinks: bool
     value_seed: int
+    qlen: int = 1                              # verify tokens per request
+    real_seq_lens: np.ndarray | None = None    # int32 [B] or None
 
     @property
     def sm_scale(self) -> float:
@@ -111,10 +119,23 @@ class GqaWorkload:
     def max_blocks(self) -> int:
         return int(self.block_table.shape[1])
 
-    def key_range(self, b: int):
+    @property
+    def rows(self) -> int:
+        return self.B * self.qlen
+
+    def row_range(self, b: int, t: int):
+        """Keys [lo, hi) of verify token t of request b (t = 0 for decode)."""
         L = int(self.seq_lens[b])
-        lo = max(L - self.window, 0) if self.window > 0 else 0
-        return lo, L
+        Lr = L if self.real_seq_lens is None else int(self.real_seq_lens[b])
+        hi = max(min(L - self.qlen + 1 + t, Lr), 0)
+        lo = max(hi - self.window, 0) if self.window > 0 else 0
+        return lo, hi
+
+    def key_range(self, b: int):
+        """Keys any row of request b attends: the union of its rows' ranges."""
+        lo, _ = self.row_range(b, 0)
+        _, hi = self.row_range(b, self.qlen - 1)
+        return lo, hi
 
     def attended_mask(self) -> np.ndarray:
         """bool [num_pages, P]: True where some request attends that slot."""
@@ -142,20 +163,21 @@ class GqaWorkload:
         return pages * self.Hkv * self.P * 2 * self.D * 2
 
     def flops(self) -> int:
-        n = sum(max(hi - lo, 0) for lo, hi in (self.key_range(b) for b in range(self.B)))
+        n = sum(max(hi - lo, 0) for b in range(self.B) for t in range(self.qlen)
+                for lo, hi in (self.row_range(b, t),))
         return int(n) * self.Hq * 4 * self.D
 
     def values(self, device="cpu", poison=True):
         """Draw q, the page pool and sinks as torch tensors on ``device``.
 
-        Returns dict(q bf16 [B, Hq, D], kv bf16 [pages, Hkv, P, 2D],
+        Returns dict(q bf16 [B * qlen, Hq, D], kv bf16 [pages, Hkv, P, 2D],
         sinks fp32 [Hq] or None).  With ``poison`` every never-attended slot
         holds bf16 NaN.
         """
         dev = torch.device(device)
         g = torch.Generator(device=dev)
         g.manual_seed(self.value_seed)
-        q = torch.randn((self.B, self.Hq, self.D), generator=g, device=dev,
+        q = torch.randn((self.rows, self.Hq, self.D), generator=g, device=dev,
                         dtype=torch.float32).to(torch.bfloat16)
         kv = torch.empty((self.num_pages, self.Hkv, self.P, 2 * self.D),
                          dtype=torch.bfloat16, device=dev)
@@ -175,18 +197,23 @@ class GqaWorkload:
 
 
 def gqa_workload(name: str, batch=None, len_range=None, seed_offset: int = 0,
-                 fixed_lens=None, loguniform=None, zero_lens=None) -> GqaWorkload:
+                 fixed_lens=None, loguniform=None, zero_lens=None, qlen=None,
+                 real_drop=None, fixed_real=None, heads=None, window=None,
+                 page_size=None) -> GqaWorkload:
     """Structure of a GQA configuration, optionally shrunk for oracle-sized tests.
 
     ``batch``/``len_range``/``fixed_lens``/``loguniform`` override the
     configuration's batch size and length distribution (same shapes
-    otherwise); ``seed_offset`` gives independent draws.
+    otherwise); ``seed_offset`` gives independent draws.  ``qlen``,
+    ``real_drop`` (real length = L - U{d0..d1}) and ``fixed_real`` make it a
+    verify workload; ``heads`` = (Hq, Hkv), ``window`` and ``page_size``
+    override those sizes.
     """
     c = CONFIGS[name]
     idx = c["index"]
     rng = np.random.Generator(np.random.PCG64(2000 + idx + 7919 * seed_offset))
     B = c["B"] if batch is None else int(batch)
-    P = c["P"]
+    P = c["P"] if page_size is None else int(page_size)
     fl = fixed_lens if fixed_lens is not None else c.get("fixed_lens")
     if fl is not None:
         lens = np.asarray(fl, dtype=np.int64)
@@ -212,10 +239,19 @@ def gqa_workload(name: str, batch=None, len_range=None, seed_offset: int = 0,
     if name == "tiny_gqa":
         pool = c["pool"]
     bt = _chunked_block_table(pages_per, pool, max_blocks, rng)
-    return GqaWorkload(name=name, B=B, Hq=c["Hq"], Hkv=c["Hkv"], D=c["D"], P=P,
+    ql = c.get("qlen", 1) if qlen is None else int(qlen)
+    real = None
+    rd = real_drop if real_drop is not None else c.get("real_drop")
+    if fixed_real is not None:
+        real = np.asarray(fixed_real, dtype=np.int64)
+    elif rd is not None:
+        real = lens - rng.integers(rd[0], rd[1], size=B, endpoint=True)
+    Hq, Hkv = (c["Hq"], c["Hkv"]) if heads is None else heads
+    return GqaWorkload(name=name, B=B, Hq=Hq, Hkv=Hkv, D=c["D"], P=P,
                        seq_lens=lens.astype(np.int32), block_table=bt, num_pages=pool,
-                       window=c["window"], has_sinks=c["sinks"],
-                       value_seed=1000 + idx + 7919 * seed_offset)
+                       window=c["window"] if window is None else int(window),
+                       has_sinks=c["sinks"], value_seed=1000 + idx + 7919 * seed_offset,
+                       qlen=ql, real_seq_lens=None if real is None else real.astype(np.int32))
 
 
 @dataclasses.dataclass

@@ -37,15 +37,21 @@ def compact_gqa(w, vals, requests):
     kv = bits16(vals["kv"].index_select(0, idx)) if len(used) else \
         np.zeros((0,) + tuple(vals["kv"].shape[1:]), np.uint16)
     bt2 = np.where(bt >= 0, remap[np.maximum(bt, 0)], -1).astype(np.int32)
-    q = bits16(vals["q"][requests])
+    rows = [b * w.qlen + t for b in requests for t in range(w.qlen)]
+    q = bits16(vals["q"][rows])
     sinks = None if vals["sinks"] is None else vals["sinks"].cpu().numpy().astype(np.float64)
     return q, kv, bt2, w.seq_lens[requests], sinks
 
 
 def oracle_gqa(w, vals, requests=None):
-    requests = range(w.B) if requests is None else requests
+    """Oracle O, LSE of a GQA workload's requests (rows b * qlen + t for verify)."""
+    requests = range(w.B) if requests is None else list(requests)
     q, kv, bt, sl, sk = compact_gqa(w, vals, requests)
-    return oracle.gqa_decode(q, kv, bt, sl, w.sm_scale, sinks=sk, window=w.window)
+    if w.qlen == 1 and w.real_seq_lens is None:
+        return oracle.gqa_decode(q, kv, bt, sl, w.sm_scale, sinks=sk, window=w.window)
+    real = None if w.real_seq_lens is None else w.real_seq_lens[list(requests)]
+    return oracle.gqa_verify(q, kv, bt, sl, w.qlen, w.sm_scale, sinks=sk, window=w.window,
+                             real_seq_lens=real)
 
 
 def compact_mla(w, vals, requests):

@@ -136,6 +136,31 @@ def test_gqa_argument_checks_happen_before_any_hip_call():
     assert _gqa(S=4, ws=FAKE + 4, wsb=need) == PD_ERR_ALIGN
 
 
+def _gqav(**kw):
+    a = dict(q=FAKE, qsr=64 * 128, qsh=128, kv=FAKE, kvsp=8 * 16 * 256, kvsh=16 * 256,
+             npages=10, bt=FAKE, btsb=4, maxb=4, sl=FAKE, real=NULL, qlen=2, sinks=NULL,
+             window=0, scale=0.088, B=2, Hq=64, Hkv=8, D=128, P=16, S=1, ws=NULL, wsb=0,
+             out=FAKE, osr=64 * 128, osh=128, lse=NULL, lser=64, stream=NULL)
+    a.update(kw)
+    return lib.paged_verify_gqa(*a.values())
+
+
+def test_gqa_verify_argument_checks_happen_before_any_hip_call():
+    assert _gqav(B=0, q=NULL, kv=NULL, bt=NULL, sl=NULL, out=NULL) == PD_OK
+    assert _gqav(qlen=0) == PD_ERR_INVALID
+    assert _gqav(q=NULL) == PD_ERR_INVALID
+    assert _gqav(scale=float("inf")) == PD_ERR_INVALID
+    assert _gqav(qlen=3) == PD_ERR_UNSUPPORTED                 # qlen * G = 24 > 16
+    assert _gqav(qlen=4, Hq=32, D=64) == PD_ERR_UNSUPPORTED
+    assert _gqav(osr=64 * 128 + 4) == PD_ERR_ALIGN
+    assert _gqav(S=4) == PD_ERR_WORKSPACE
+    need = lib.pd_workspace_bytes(2 * 2, 64, 4, 128)           # rows = B * qlen
+    assert _gqav(S=4, ws=FAKE, wsb=need - 4) == PD_ERR_WORKSPACE
+    assert _gqav(S=4, ws=FAKE + 4, wsb=need) == PD_ERR_ALIGN
+    # the query rows of a unit must be addressable with a 32-bit byte offset
+    assert _gqav(qsr=(1 << 30)) == PD_ERR_UNSUPPORTED
+
+
 def _mla(**kw):
     a = dict(q=FAKE, qsr=128 * 576, qsh=576, kv=FAKE, dt=0, sp=16 * 576, st=576, npages=10,
              ks=NULL, bt=FAKE, btsb=4, maxb=4, sl=FAKE, real=NULL, qlen=4, scale=0.07, B=2,
