@@ -31,6 +31,7 @@ from .attention import (  # noqa: F401
     gqa_decode,
     gqa_partials,
     gqa_verify,
+    kv_append,
     merge_partials,
     mla_verify,
     row_key_range,

@@ -32,6 +32,10 @@ Parity status per function (what pins it, see tests/test_oracle_pins.py):
                                    window and sinks; empty rows.
 * ``mla_verify``                   pinned: dense causal brute force, marker
                                    keys at the row limit, empty rows.
+* ``kv_append``                    pinned: the worked example's placement
+                                   of each new token, every other byte
+                                   unchanged, append-then-decode reads the
+                                   new token as the last key.
 * ``gqa_partials``/``merge_partials`` pinned: equality across split counts,
                                    LSE consistency.
 * ``verify_num_kv_splits``         pinned: hand-evaluated values.
@@ -325,6 +329,53 @@ def mla_verify(q_bits, kv, block_table, seq_lens, real_seq_lens, qlen: int,
             r = b * qlen + t
             O[r], lse[r] = attend(q[r], lat[: his[t]], lat[: his[t], :Lv], sm_scale)
     return O, lse
+
+
+# ---------------------------------------------------------------------------
+# KV append (the cache write that precedes decode / verify)
+# ---------------------------------------------------------------------------
+
+def kv_append(cache, block_table, seq_lens, qlen: int, src0, src1=None):
+    """Write the qlen newest tokens of every request into the paged cache.
+
+    The decode kernel of "Atención paginada" (Ruta de decodificación,
+    "Comportamiento de la caché") updates the paged cache in place through
+    the block table: token position j of request b lives at slot ``j % P`` of
+    page ``block_table[b][j // P]``.  Following "vllm.models.flint.ops.
+    decode_attention" (the current token's K/V is written before the decode
+    kernel reads the cache, and ``seq_lens`` counts it), the tokens written
+    are the last qlen positions of each request: token t (row ``b * qlen + t``
+    of the sources) goes to position ``seq_lens[b] - qlen + t``.
+
+    ``cache``  [num_pages, H, P, n] storage elements (any dtype: a byte copy);
+    ``src0``   [B * qlen, H, n0] elements copied to ``cache[..., :n0]``;
+    ``src1``   None or [B * qlen, H, n1] copied to ``cache[..., n0:n0 + n1]``
+               (GQA: K then V of an HND cache; MLA: the latent row alone).
+
+    A token whose position is negative, or whose page entry lies outside the
+    block table row or outside ``[0, num_pages)``, is not written (nothing is
+    ever written outside the cache).  Returns the updated copy of ``cache``.
+    """
+    out = np.array(cache, copy=True)
+    num_pages, H, P, _ = out.shape
+    s0 = np.asarray(src0)
+    n0 = s0.shape[2]
+    s1 = None if src1 is None else np.asarray(src1)
+    bt = np.asarray(block_table)
+    B = bt.shape[0]
+    for b in range(B):
+        for t in range(qlen):
+            pos = int(seq_lens[b]) - qlen + t
+            if pos < 0 or pos // P >= bt.shape[1]:
+                continue
+            page = int(bt[b, pos // P])
+            if page < 0 or page >= num_pages:
+                continue
+            r = b * qlen + t
+            out[page, :, pos % P, :n0] = s0[r]
+            if s1 is not None:
+                out[page, :, pos % P, n0:n0 + s1.shape[2]] = s1[r]
+    return out
 
 
 # ---------------------------------------------------------------------------

@@ -552,6 +552,65 @@ def _fails(fn, *a, **k):
     return False
 
 
+# ---------------------------------------------------------------------------
+# KV append
+# ---------------------------------------------------------------------------
+
+def test_kv_append_worked_example_placement():
+    """Each sequence's new token lands where the worked example places it;
+    every other element of the cache is unchanged."""
+    with open(os.path.join(GOLDEN, "worked_example_append.json")) as f:
+        ex = json.load(f)
+    P, D = ex["page_size"], 4
+    cache = np.arange(ex["num_pages"] * 1 * P * 2 * D, dtype=np.uint16).reshape(
+        ex["num_pages"], 1, P, 2 * D)
+    k = np.full((3, 1, D), 0xAAAA, np.uint16) + np.arange(3, dtype=np.uint16)[:, None, None]
+    v = np.full((3, 1, D), 0xBBBB, np.uint16) + np.arange(3, dtype=np.uint16)[:, None, None]
+    out = oracle.kv_append(cache, np.asarray(ex["block_table"]), np.asarray(ex["seq_lens_after"]),
+                           1, k, v)
+    changed = np.argwhere(np.any(out != cache, axis=-1))
+    want = sorted((p, 0, s) for p, s in zip(ex["new_token_page"], ex["new_token_slot"]))
+    assert sorted(map(tuple, changed.tolist())) == want
+    for b, (p, s) in enumerate(zip(ex["new_token_page"], ex["new_token_slot"])):
+        assert np.array_equal(out[p, 0, s, :D], k[b, 0]) and np.array_equal(out[p, 0, s, D:], v[b, 0])
+
+
+def test_kv_append_verify_rows_and_skips():
+    """qlen tokens land at positions L - qlen .. L - 1; a negative position or
+    an entry outside the table / pool writes nothing."""
+    P, H, n = 4, 2, 3
+    bt = np.array([[5, 1, -1], [0, 9, -1], [2, 3, 4]])
+    lens = np.array([6, 1, 12])       # request 1: positions -1, 0; request 2: 10, 11
+    cache = np.zeros((6, H, P, n), np.int32)
+    src = np.arange(3 * 2 * H * n, dtype=np.int32).reshape(6, H, n) + 100
+    out = oracle.kv_append(cache, bt, lens, 2, src)
+    assert np.array_equal(out[1, :, 0], src[0]) and np.array_equal(out[1, :, 1], src[1])
+    assert np.array_equal(out[0, :, 0], src[3])          # request 1, position 0 (t = 1)
+    assert np.array_equal(out[4, :, 2], src[4]) and np.array_equal(out[4, :, 3], src[5])
+    assert np.count_nonzero(out) == 5 * H * n            # nothing else was written
+    # entry 9 is outside the 6-page pool, position 12 // 4 = 3 is past the row
+    out2 = oracle.kv_append(cache, bt, np.array([0, 6, 13]), 1, src[::2])
+    assert np.count_nonzero(out2) == 0
+
+
+def test_kv_append_then_decode_attends_the_new_token():
+    """A marker written by kv_append at position L - 1 is the last key the
+    decode attends: with a dominant score its V comes out exactly."""
+    rng = np.random.default_rng(31)
+    lens, Hq, Hkv, D, P = [9, 16], 4, 2, 8, 4
+    q, kv, bt, sl, _ = _rand_gqa(rng, 2, Hq, Hkv, D, P, lens)
+    qf = np.zeros((2, Hq, D), np.float32)
+    qf[:, :, 0] = 1.0
+    k = np.zeros((2, Hkv, D), np.float32)
+    k[:, :, 0] = 200.0
+    v = rng.integers(-50, 50, (2, Hkv, D)).astype(np.float32)
+    kv2 = oracle.kv_append(kv, bt, sl, 1, _bf16(k), _bf16(v))
+    O, lse = oracle.gqa_decode(_bf16(qf), kv2, bt, sl, 1.0)
+    for b in range(2):
+        for h in range(Hq):
+            np.testing.assert_allclose(O[b, h], v[b, h // 2], atol=1e-12)
+
+
 def test_mutant_row_limit_plus_one_is_caught(monkeypatch):
     orig = oa.row_key_range
     monkeypatch.setattr(oa, "row_key_range",
@@ -588,6 +647,16 @@ def test_mutant_row_limit_plus_one_is_caught_in_gqa_verify(monkeypatch):
                         (orig(L, qlen, t, real_len, window)[0],
                          orig(L, qlen, t, real_len, window)[1] + 1))
     assert _fails(test_gqa_verify_matches_causal_dense_brute_force)
+
+
+def test_mutant_append_position_off_by_one_is_caught(monkeypatch):
+    orig = oa.kv_append
+
+    def shifted(cache, block_table, seq_lens, qlen, src0, src1=None):
+        return orig(cache, block_table, np.asarray(seq_lens) + 1, qlen, src0, src1)
+    monkeypatch.setattr(oracle, "kv_append", shifted)
+    assert _fails(test_kv_append_worked_example_placement)
+    assert _fails(test_kv_append_then_decode_attends_the_new_token)
 
 
 def test_mutant_window_off_by_one_is_caught(monkeypatch):
