@@ -10,7 +10,7 @@ Printed: ONE JSON line with KV-read GB/s (algorithmic K+V bytes of the
 attended keys / time per call), the roofline of the dominant kernel measured
 with HIP events on the launch stream, and the fp64 CPU oracle's rate on the
 same inputs.  ``--config`` selects another workload (gqa_window, gqa_skewed,
-tiny_gqa, gqa_verify, mla_verify, mla_verify_fp8).
+tiny_gqa, gqa_verify, kv_append, mla_verify, mla_verify_fp8).
 """
 
 from __future__ import annotations
@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "KV-read GB/s (% of HBM peak) and µs/call for paged decode, GQA and MLA verify"
 HBM_PEAK_GBS = 8000.0
+GRAPH_CALLS = 50      # calls per captured graph for launch-bound kernels
 # The GPU clock climbs over the first ~100 ms of load after idle: the default
 # warmup runs at least this long.
 WARMUP_AUTO_S = 0.5
@@ -105,6 +106,31 @@ def _gqa_case(name, torch, pd, splits):
                 kernel_name="gqa_decode_kernel")
 
 
+def _append_case(torch, pd):
+    from synth import gqa_workload
+
+    w = gqa_workload("gqa_sinks")
+    vals = w.values("cuda", poison=False)
+    bt = torch.from_numpy(w.block_table).cuda()
+    sl = torch.from_numpy(w.seq_lens).cuda()
+    g = torch.Generator(device="cuda").manual_seed(99)
+    k = torch.randn((w.B, w.Hkv, w.D), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((w.B, w.Hkv, w.D), generator=g, device="cuda").to(torch.bfloat16)
+
+    def step():
+        pd.paged_kv_append(vals["kv"], bt, sl, k, v)
+
+    desc = ("KV append of the current token: B=64, Hkv=8, D=128, K and V into the 16-token "
+            "HND pages of the 40000-page decode pool through the block table")
+    moved = 2 * w.B * w.Hkv * 2 * w.D * 2          # read + write, K and V
+    # The step loop is bound by the host-side binding, so the kernel's own
+    # time comes from a HIP graph of GRAPH_CALLS appends replayed back to back.
+    return dict(w=w, vals=vals, S=1, step=step, kernel=None, rest=None, kv_bytes=moved,
+                graph_calls=GRAPH_CALLS,
+                flops=0, desc=desc, kind="append", kernel_name="kv_append_kernel",
+                extra=dict(k=k, v=v))
+
+
 def _mla_case(fp8, torch, pd, splits):
     from synth import mla_workload
 
@@ -167,6 +193,27 @@ def _cpu_baseline(case, budget_s=20.0):
 
     w, vals = case["w"], case["vals"]
     threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] + [1])
+    if case["kind"] == "append":
+        # the pages the appends write, as a compact pool
+        pos = w.seq_lens.astype(np.int64) - 1
+        pages = w.block_table[np.arange(w.B), pos // w.P]
+        remap = {int(p): i for i, p in enumerate(np.unique(pages))}
+        idx = torch.from_numpy(np.unique(pages)).cuda()
+        cache = vals["kv"].index_select(0, idx).view(torch.int16).cpu().numpy().view(np.uint16)
+        bt2 = np.full_like(w.block_table, -1)
+        bt2[np.arange(w.B), pos // w.P] = [remap[int(p)] for p in pages]
+        k = case["extra"]["k"].view(torch.int16).cpu().numpy().view(np.uint16)
+        v = case["extra"]["v"].view(torch.int16).cpu().numpy().view(np.uint16)
+        reps, t_total = 0, 0.0
+        while t_total < 2.0:
+            t0 = time.perf_counter()
+            oracle.kv_append(cache, bt2, w.seq_lens, 1, k, v)
+            t_total += time.perf_counter() - t0
+            reps += 1
+        return {"value": round(case["kv_bytes"] * reps / t_total / 1e9, 4), "unit": "GB/s",
+                "cores": 1, "kind": "oracle",
+                "sample": f"all {w.B} requests' appends into a compact pool of their target "
+                          f"pages, {reps} calls in {t_total:.1f} s, NumPy"}
     done_bytes = 0
     t_total = 0.0
     n_req = 0
@@ -238,6 +285,8 @@ def main():
     name = args.config
     if name in ("mla_verify", "mla_verify_fp8"):
         case = _mla_case(name.endswith("fp8"), torch, pd, args.splits)
+    elif name == "kv_append":
+        case = _append_case(torch, pd)
     else:
         case = _gqa_case(name, torch, pd, args.splits)
     torch.cuda.synchronize()
@@ -269,7 +318,25 @@ def main():
     # dominant kernel alone: HIP events recorded on the launch stream right
     # around each launch of the split decode kernel
     kernel_ms = []
-    if case["kernel"] is not None:
+    if case.get("graph_calls"):
+        n_calls = case["graph_calls"]
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(n_calls):
+                case["step"]()
+        torch.cuda.synchronize()
+        for _ in range(3):
+            graph.replay()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = max(1, args.steps // n_calls)
+        gstream = torch.cuda.current_stream()
+        ev0.record(gstream)
+        for _ in range(reps):
+            graph.replay()
+        ev1.record(gstream)
+        torch.cuda.synchronize()
+        kernel_ms = [ev0.elapsed_time(ev1) / (reps * n_calls)]
+    elif case["kernel"] is not None:
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.steps)]
         for a, b in evs:
@@ -285,7 +352,7 @@ def main():
 
     kv = case["kv_bytes"]
     value = kv / (ms_per_step * 1e-3) / 1e9
-    if case["kind"] in ("gqa", "gqa_verify"):
+    if case["kind"] in ("gqa", "gqa_verify", "append"):
         roof = {"bound": "hbm", "achieved": round(kv / (k_ms * 1e-3) / 1e9, 2),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     else:

@@ -7,6 +7,7 @@
  *   paged_decode_gqa   one query token per request, grouped-query heads,
  *                      optional per-head sinks and a sliding window;
  *   paged_verify_gqa   the same with qlen causal verify tokens per request;
+ *   paged_kv_append    writes the newest tokens' K/V into the paged cache;
  *   paged_verify_mla   qlen causal "verify" tokens per request over one shared
  *                      latent cache, V read as K[..., :Lv], bf16 or FP8 cache;
  *   num_kv_splits_cap  static split cap from static sizes (graph-capture safe);
@@ -229,6 +230,47 @@ PD_API int paged_decode_gqa_partials(const void* q, int64_t q_stride_b, int64_t 
                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                               int32_t page_size, int32_t num_kv_splits, float* workspace,
                               size_t workspace_bytes, void* stream);
+
+/*
+ * paged_kv_append - write the qlen newest tokens of every request into the
+ * paged cache, through the block table (the cache write before a decode or
+ * verify call).
+ *
+ * Defined by "Atención paginada", section "Ruta de decodificación" (the
+ * decode kernel updates the paged cache in place through the block table:
+ * position j of request b is slot j % P of page block_table[b][j / P]), with
+ * the length convention of "vllm.models.flint.ops.decode_attention"
+ * (seq_lens counts the current token): token t of request b, row b*qlen + t
+ * of the sources, goes to position seq_lens[b] - qlen + t.  A byte copy,
+ * bit-exact for any element type.
+ *
+ * src0         [B*qlen, H, src0_elems], strides (src0_stride_tok,
+ *              src0_stride_h, 1): copied to elements [0, src0_elems) of the
+ *              token's cache row (GQA: K; MLA: the latent row).
+ * src1         [B*qlen, H, src1_elems] or NULL (then src1_elems = 0): copied
+ *              to elements [src0_elems, src0_elems + src1_elems) (GQA: V).
+ * elem_bytes   1 (FP8 codes) or 2 (bf16); every stride and element count is
+ *              in these elements.
+ * cache        page p, head h, slot s at p*cache_stride_page +
+ *              h*cache_stride_head + s*cache_stride_tok: the GQA HND cache
+ *              [num_pages, Hkv, P, 2D] or the MLA latent cache
+ *              [num_pages, P, 1, Lk] (H = 1).
+ * block_table  [B, max_blocks] int32; seq_lens [B] int32 (after the append).
+ *
+ * A token at a negative position (seq_lens[b] < qlen), past the block-table
+ * row, or behind an entry outside [0, num_pages) is not written: nothing is
+ * ever written outside the cache.  Pointers, strides and row sizes must be
+ * 16-byte multiples (PD_ERR_ALIGN), src0_elems + src1_elems <=
+ * cache_stride_tok.  Two appends in flight must not target the same slots.
+ */
+PD_API int paged_kv_append(const void* src0, int64_t src0_stride_tok, int64_t src0_stride_h,
+                    int32_t src0_elems, const void* src1, int64_t src1_stride_tok,
+                    int64_t src1_stride_h, int32_t src1_elems, int32_t elem_bytes,
+                    void* cache, int64_t cache_stride_page, int64_t cache_stride_head,
+                    int64_t cache_stride_tok, int32_t num_pages, const int32_t* block_table,
+                    int64_t bt_stride_b, int32_t max_blocks, const int32_t* seq_lens,
+                    int32_t qlen, int32_t batch, int32_t num_heads, int32_t page_size,
+                    void* stream);
 
 /*
  * paged_verify_mla - causal MLA verify over a per-request block table.

@@ -16,6 +16,7 @@ from .api import (  # noqa: F401
     num_kv_splits_cap,
     paged_decode_gqa,
     paged_decode_gqa_partials,
+    paged_kv_append,
     paged_verify_gqa,
     paged_verify_mla,
     workspace_bytes,

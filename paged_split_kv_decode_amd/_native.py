@@ -28,6 +28,7 @@ EXPORTS = (
     "paged_decode_gqa",
     "paged_verify_gqa",
     "paged_decode_gqa_partials",
+    "paged_kv_append",
     "paged_verify_mla",
     "merge_splits",
 )
@@ -79,6 +80,16 @@ def _load():
         _c_vp, _c_i64, _c_vp,                   # lse, stride, stream
     ]
     lib.paged_verify_gqa.restype = ctypes.c_int
+    lib.paged_kv_append.argtypes = [
+        _c_vp, _c_i64, _c_i64, _c_i32,          # src0, strides, elems
+        _c_vp, _c_i64, _c_i64, _c_i32,          # src1, strides, elems
+        _c_i32,                                 # elem_bytes
+        _c_vp, _c_i64, _c_i64, _c_i64, _c_i32,  # cache, page/head/token strides, num_pages
+        _c_vp, _c_i64, _c_i32,                  # block_table, row stride, max_blocks
+        _c_vp, _c_i32, _c_i32, _c_i32, _c_i32,  # seq_lens, qlen, B, H, P
+        _c_vp,                                  # stream
+    ]
+    lib.paged_kv_append.restype = ctypes.c_int
     lib.paged_decode_gqa_partials.argtypes = [
         _c_vp, _c_i64, _c_i64,                  # q, strides
         _c_vp, _c_i64, _c_i64, _c_i32,          # kv, page/head strides, num_pages

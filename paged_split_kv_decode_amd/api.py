@@ -198,6 +198,62 @@ def paged_verify_gqa(q, kv, block_table, seq_lens, qlen, sm_scale, sinks=None, w
     return out, lse
 
 
+def paged_kv_append(cache, block_table, seq_lens, src0, src1=None, qlen=1, layout="hnd",
+                    stream=None):
+    """Write the qlen newest tokens of each request into the paged cache
+    (include/paged_decode.h: paged_kv_append).  In place; returns ``cache``.
+
+    layout "hnd": cache [num_pages, H, P, row] (the GQA cache; src0 = K and
+    src1 = V, each [B*qlen, H, D]); layout "nhd": cache [num_pages, P, H, row]
+    (the MLA latent cache with H = 1; src0 = latent rows [B*qlen, 1, Lk] or
+    [B*qlen, Lk]).  Elements are bf16 or FP8 codes (uint8); the copy is
+    byte-exact.
+    """
+    if not isinstance(cache, torch.Tensor) or not cache.is_cuda or cache.dim() != 4:
+        raise ValueError("cache must be a 4-D device tensor")
+    if cache.dtype not in (torch.bfloat16, torch.uint8, torch.float8_e4m3fn):
+        raise TypeError("cache must be bf16 or FP8 (uint8 / float8_e4m3fn) elements")
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    qlen = int(qlen)
+    if src0.dim() == 2:
+        src0 = src0.unsqueeze(1)
+    if src1 is not None and src1.dim() == 2:
+        src1 = src1.unsqueeze(1)
+    for name, t in (("src0", src0), ("src1", src1)):
+        if t is None:
+            continue
+        if t.dtype != cache.dtype or not t.is_cuda or t.dim() != 3 or t.stride(2) != 1:
+            raise ValueError(f"{name} must be a [rows, H, n] device tensor of the cache dtype "
+                             "with a contiguous last dim")
+    if layout == "hnd":
+        num_pages, H, P, row = cache.shape
+        sp, sh, st = cache.stride(0), cache.stride(1), cache.stride(2)
+    elif layout == "nhd":
+        num_pages, P, H, row = cache.shape
+        sp, st, sh = cache.stride(0), cache.stride(1), cache.stride(2)
+    else:
+        raise ValueError("layout must be 'hnd' or 'nhd'")
+    if cache.stride(3) != 1:
+        raise ValueError("cache rows must be contiguous")
+    B = block_table.shape[0]
+    if seq_lens.shape[0] != B or block_table.stride(1) != 1:
+        raise ValueError("block_table / seq_lens must have one row per request")
+    if src0.shape[0] != B * qlen or src0.shape[1] != H or \
+            (src1 is not None and tuple(src1.shape[:2]) != (B * qlen, H)):
+        raise ValueError("sources must be [B * qlen, H, n]")
+    eb = cache.element_size()
+    st_ = lib.paged_kv_append(
+        _ptr(src0), src0.stride(0), src0.stride(1), src0.shape[2],
+        _ptr(src1), 0 if src1 is None else src1.stride(0), 0 if src1 is None else src1.stride(1),
+        0 if src1 is None else src1.shape[2], eb,
+        _ptr(cache), sp, sh, st, num_pages,
+        _ptr(block_table), block_table.stride(0), block_table.shape[1],
+        _ptr(seq_lens), qlen, B, H, P, _stream(stream))
+    check("paged_kv_append", st_)
+    return cache
+
+
 def paged_decode_gqa_partials(q, kv, block_table, seq_lens, sm_scale, window=0,
                               num_kv_splits=1, workspace=None, stream=None):
     """Split partials of paged_decode_gqa without the merge

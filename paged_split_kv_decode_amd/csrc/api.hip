@@ -242,6 +242,60 @@ int paged_decode_gqa_partials(const void* q, int64_t q_stride_b, int64_t q_strid
                     true);
 }
 
+int paged_kv_append(const void* src0, int64_t src0_stride_tok, int64_t src0_stride_h,
+                    int32_t src0_elems, const void* src1, int64_t src1_stride_tok,
+                    int64_t src1_stride_h, int32_t src1_elems, int32_t elem_bytes, void* cache,
+                    int64_t cache_stride_page, int64_t cache_stride_head,
+                    int64_t cache_stride_tok, int32_t num_pages, const int32_t* block_table,
+                    int64_t bt_stride_b, int32_t max_blocks, const int32_t* seq_lens,
+                    int32_t qlen, int32_t batch, int32_t num_heads, int32_t page_size,
+                    void* stream) {
+  if (batch < 0 || qlen < 1 || num_heads < 1 || page_size < 1 || num_pages < 0 ||
+      max_blocks < 0 || src0_elems < 1 || src1_elems < 0 || (elem_bytes != 1 && elem_bytes != 2))
+    return PD_ERR_INVALID;
+  if ((src1 == nullptr) != (src1_elems == 0)) return PD_ERR_INVALID;
+  if (batch == 0) return PD_OK;
+  if (src0 == nullptr || cache == nullptr || block_table == nullptr || seq_lens == nullptr)
+    return PD_ERR_INVALID;
+  if (src0_stride_tok < 0 || src0_stride_h < 0 || src1_stride_tok < 0 || src1_stride_h < 0 ||
+      cache_stride_page < 0 || cache_stride_head < 0 || cache_stride_tok < 0 || bt_stride_b < 0)
+    return PD_ERR_INVALID;
+  // a token's row (both sources) must fit its cache row
+  if ((int64_t)src0_elems + src1_elems > cache_stride_tok) return PD_ERR_INVALID;
+  const int64_t eb = elem_bytes;
+  auto a16 = [&](int64_t elems) { return (elems * eb) % 16 == 0; };
+  if (!aligned16(src0) || !aligned16(cache) || (src1 != nullptr && !aligned16(src1)) ||
+      !a16(src0_elems) || !a16(src1_elems) || !a16(src0_stride_tok) || !a16(src0_stride_h) ||
+      !a16(src1_stride_tok) || !a16(src1_stride_h) || !a16(cache_stride_page) ||
+      !a16(cache_stride_head) || !a16(cache_stride_tok))
+    return PD_ERR_ALIGN;
+  if ((int64_t)batch * qlen > 0x7fffffff) return PD_ERR_UNSUPPORTED;
+  pd::AppendArgs a{};
+  a.src0 = static_cast<const char*>(src0);
+  a.s0_tok = src0_stride_tok * eb;
+  a.s0_h = src0_stride_h * eb;
+  a.src1 = static_cast<const char*>(src1);
+  a.s1_tok = src1_stride_tok * eb;
+  a.s1_h = src1_stride_h * eb;
+  a.c0 = (int32_t)(src0_elems * eb / 16);
+  a.c1 = (int32_t)(src1_elems * eb / 16);
+  a.cache = static_cast<char*>(cache);
+  a.c_sp = cache_stride_page * eb;
+  a.c_sh = cache_stride_head * eb;
+  a.c_st = cache_stride_tok * eb;
+  a.num_pages = num_pages;
+  a.bt = block_table;
+  a.bt_sb = bt_stride_b;
+  a.max_blocks = max_blocks;
+  a.seq_lens = seq_lens;
+  a.qlen = qlen;
+  a.B = batch;
+  a.H = num_heads;
+  a.P = page_size;
+  if (pd::launch_kv_append(a, static_cast<hipStream_t>(stream)) != hipSuccess) return PD_ERR_HIP;
+  return PD_OK;
+}
+
 int paged_verify_mla(const void* q, int64_t q_stride_row, int64_t q_stride_h, const void* kv,
                      int32_t kv_dtype, int64_t kv_stride_page, int64_t kv_stride_tok,
                      int32_t num_pages, const float* k_scale, const int32_t* block_table,

@@ -76,7 +76,25 @@ struct MlaArgs {
   int64_t lse_srow;
 };
 
+// Byte strides; every pointer and stride 16-byte aligned (checked on the host).
+struct AppendArgs {
+  const char* src0;
+  int64_t s0_tok, s0_h;
+  const char* src1;            // nullptr when c1 == 0
+  int64_t s1_tok, s1_h;
+  int32_t c0, c1;              // 16-byte chunks per (token, head) row of each source
+  char* cache;
+  int64_t c_sp, c_sh, c_st;    // page, head, token strides of the cache
+  int32_t num_pages;
+  const int32_t* bt;
+  int64_t bt_sb;
+  int32_t max_blocks;
+  const int32_t* seq_lens;
+  int32_t qlen, B, H, P;
+};
+
 hipError_t launch_gqa_decode(const GqaArgs& a, hipStream_t stream);
+hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_mla_verify(const MlaArgs& a, hipStream_t stream);
 

@@ -199,7 +199,7 @@ class GqaWorkload:
 def gqa_workload(name: str, batch=None, len_range=None, seed_offset: int = 0,
                  fixed_lens=None, loguniform=None, zero_lens=None, qlen=None,
                  real_drop=None, fixed_real=None, heads=None, window=None,
-                 page_size=None) -> GqaWorkload:
+                 page_size=None, pool=None) -> GqaWorkload:
     """Structure of a GQA configuration, optionally shrunk for oracle-sized tests.
 
     ``batch``/``len_range``/``fixed_lens``/``loguniform`` override the
@@ -207,7 +207,8 @@ def gqa_workload(name: str, batch=None, len_range=None, seed_offset: int = 0,
     otherwise); ``seed_offset`` gives independent draws.  ``qlen``,
     ``real_drop`` (real length = L - U{d0..d1}) and ``fixed_real`` make it a
     verify workload; ``heads`` = (Hq, Hkv), ``window`` and ``page_size``
-    override those sizes.
+    override those sizes; ``pool`` = "tight" sizes the page pool to the pages
+    the requests use (plus 5).
     """
     c = CONFIGS[name]
     idx = c["index"]
@@ -235,9 +236,12 @@ def gqa_workload(name: str, batch=None, len_range=None, seed_offset: int = 0,
     max_blocks = max(c["max_blocks"], max(pages_per) if pages_per else 1)
     if len_range is not None or batch is not None or loguniform is not None:
         max_blocks = max(max(pages_per) if pages_per else 1, 1) + 3
-    pool = max(c["pool"], int(np.sum(pages_per)))
+    pool_n = max(c["pool"], int(np.sum(pages_per)))
     if name == "tiny_gqa":
-        pool = c["pool"]
+        pool_n = c["pool"]
+    if pool == "tight":
+        pool_n = int(np.sum(pages_per)) + 5
+    pool = pool_n
     bt = _chunked_block_table(pages_per, pool, max_blocks, rng)
     ql = c.get("qlen", 1) if qlen is None else int(qlen)
     real = None

@@ -161,6 +161,28 @@ def test_gqa_verify_argument_checks_happen_before_any_hip_call():
     assert _gqav(qsr=(1 << 30)) == PD_ERR_UNSUPPORTED
 
 
+def _app(**kw):
+    a = dict(s0=FAKE, s0t=8 * 128, s0h=128, n0=128, s1=FAKE, s1t=8 * 128, s1h=128, n1=128, eb=2,
+             cache=FAKE, csp=8 * 16 * 256, csh=16 * 256, cst=256, npages=10, bt=FAKE, btsb=4,
+             maxb=4, sl=FAKE, qlen=1, B=2, H=8, P=16, stream=NULL)
+    a.update(kw)
+    return lib.paged_kv_append(*a.values())
+
+
+def test_kv_append_argument_checks_happen_before_any_hip_call():
+    assert _app(B=0, s0=NULL, s1=NULL, n1=0, cache=NULL, bt=NULL, sl=NULL) == PD_OK
+    assert _app(qlen=0) == PD_ERR_INVALID
+    assert _app(eb=4) == PD_ERR_INVALID
+    assert _app(s1=NULL) == PD_ERR_INVALID                     # elements given, no source
+    assert _app(n1=0) == PD_ERR_INVALID                        # source given, no elements
+    assert _app(cache=NULL) == PD_ERR_INVALID
+    assert _app(cst=200) == PD_ERR_INVALID                     # K | V do not fit a token row
+    assert _app(n0=4, n1=4, cst=8) == PD_ERR_ALIGN             # 8-byte rows
+    assert _app(s0=FAKE + 8) == PD_ERR_ALIGN
+    assert _app(csh=16 * 256 + 4) == PD_ERR_ALIGN
+    assert _app(eb=1, n0=8, n1=8, cst=16) == PD_ERR_ALIGN       # FP8: 8-byte rows
+
+
 def _mla(**kw):
     a = dict(q=FAKE, qsr=128 * 576, qsh=576, kv=FAKE, dt=0, sp=16 * 576, st=576, npages=10,
              ks=NULL, bt=FAKE, btsb=4, maxb=4, sl=FAKE, real=NULL, qlen=4, scale=0.07, B=2,
