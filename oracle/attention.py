@@ -29,7 +29,10 @@ Parity status per function (what pins it, see tests/test_oracle_pins.py):
                                    qlen = 1; each row equals a one-token
                                    decode over its own prefix (hand-computed
                                    limits); dense causal brute force with a
-                                   window and sinks; empty rows.
+                                   window and sinks; empty rows; the FP8
+                                   cache equals the bf16 cache of its
+                                   dequantised values (torch's e4m3fn
+                                   decoding, power-of-two per-head scales).
 * ``mla_verify``                   pinned: dense causal brute force, marker
                                    keys at the row limit, empty rows.
 * ``kv_append``                    pinned: the worked example's placement
@@ -233,7 +236,8 @@ def gqa_decode(q_bits, kv_bits, block_table, seq_lens, sm_scale, sinks=None,
 
 
 def gqa_verify(q_bits, kv_bits, block_table, seq_lens, qlen: int, sm_scale,
-               sinks=None, window: int = 0, real_seq_lens=None):
+               sinks=None, window: int = 0, real_seq_lens=None, kv_dtype: str = "bf16",
+               k_scale=1.0, v_scale=1.0):
     """Paged GQA causal verify: qlen query tokens per request, in float64.
 
     The verify form of GQA decode.  The rows, their limits and the output
@@ -246,6 +250,13 @@ def gqa_verify(q_bits, kv_bits, block_table, seq_lens, qlen: int, sm_scale,
     decode_attention").  The window of row t covers its last ``window``
     keys, ``[max(hi - window, 0), hi)``.
 
+    An FP8 cache (``kv_dtype = "fp8_e4m3fn"``, uint8 codes) holds K and V
+    scaled by ``k_scale`` and ``v_scale``: value = code value * scale, as the
+    scalar ``k_scale`` dequantises an FP8 cache in
+    "vllm.v1.attention.ops.triton_decode_attention" (parameter ``k_scale``);
+    GQA's K and V are separate tensors, so each has its own scale, a scalar
+    or one per kv head.
+
     Returns ``(O [B * qlen, Hq, D], LSE [B * qlen, Hq])``.  With qlen = 1 and
     no real lengths this is ``gqa_decode``.
     """
@@ -255,6 +266,18 @@ def gqa_verify(q_bits, kv_bits, block_table, seq_lens, qlen: int, sm_scale,
     _, Hkv, P, two_d = kv.shape
     assert two_d == 2 * D and Hq % Hkv == 0 and rows % qlen == 0
     G = Hq // Hkv
+    ks = np.broadcast_to(np.asarray(k_scale, np.float64), (Hkv,))
+    vs = np.broadcast_to(np.asarray(v_scale, np.float64), (Hkv,))
+
+    def decode_rows(raw, kvh):
+        if kv_dtype == "bf16":
+            return bf16_bits_to_f64(raw)
+        if kv_dtype == "fp8_e4m3fn":
+            vals = fp8_bits_to_f64(raw)
+            vals[:, :D] *= ks[kvh]
+            vals[:, D:] *= vs[kvh]
+            return vals
+        raise ValueError(kv_dtype)
     B = rows // qlen
     O = np.zeros((rows, Hq, D))
     lse = np.full((rows, Hq), -np.inf)
@@ -266,7 +289,7 @@ def gqa_verify(q_bits, kv_bits, block_table, seq_lens, qlen: int, sm_scale,
             lo, hi = row_key_range(L, qlen, t, L_real, window)
             pages, slots = _gather_positions(block_table[b], np.arange(lo, hi), P)
             for kvh in range(Hkv):
-                kvrows = bf16_bits_to_f64(kv[pages, kvh, slots, :])   # [n, 2D]
+                kvrows = decode_rows(kv[pages, kvh, slots, :], kvh)    # [n, 2D]
                 hs = slice(kvh * G, (kvh + 1) * G)
                 sk = None if sinks is None else np.asarray(sinks, np.float64)[hs]
                 O[r, hs], lse[r, hs] = attend(q[r, hs], kvrows[:, :D], kvrows[:, D:],

@@ -552,6 +552,35 @@ def _fails(fn, *a, **k):
     return False
 
 
+def test_gqa_verify_fp8_cache_equals_bf16_of_dequantised_values():
+    """An FP8 cache with per-kv-head K and V scales gives the bf16 result of
+    the cache holding its dequantised values.  The values come from torch's
+    float8_e4m3fn decoding, and power-of-two scales keep them exact in bf16."""
+    rng = np.random.default_rng(24)
+    lens, qlen, Hq, Hkv, D, P = [13, 6], 2, 4, 2, 8, 4
+    q, kv, bt, sl, sk = _rand_gqa_verify(rng, lens, qlen, Hq, Hkv, D, P)
+    codes = rng.integers(0, 256, kv.shape, dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x3C                  # no NaN codes
+    ks, vs = np.array([0.5, 4.0]), np.array([2.0, 0.25])
+    vals = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    vals = vals.astype(np.float64)
+    vals[..., :D] *= ks[None, :, None, None]
+    vals[..., D:] *= vs[None, :, None, None]
+    kv_bf = _bf16(vals.astype(np.float32))
+    assert np.array_equal(oa.bf16_bits_to_f64(kv_bf), vals)          # exact in bf16
+    O1, l1 = oracle.gqa_verify(q, codes, bt, sl, qlen, 0.3, sinks=sk, kv_dtype="fp8_e4m3fn",
+                               k_scale=ks, v_scale=vs)
+    O2, l2 = oracle.gqa_verify(q, kv_bf, bt, sl, qlen, 0.3, sinks=sk)
+    np.testing.assert_array_equal(O1, O2)
+    np.testing.assert_array_equal(l1, l2)
+    # a scalar scale is the same as one per head
+    O3, _ = oracle.gqa_verify(q, codes, bt, sl, qlen, 0.3, sinks=sk, kv_dtype="fp8_e4m3fn",
+                              k_scale=2.0, v_scale=0.5)
+    O4, _ = oracle.gqa_verify(q, codes, bt, sl, qlen, 0.3, sinks=sk, kv_dtype="fp8_e4m3fn",
+                              k_scale=np.array([2.0, 2.0]), v_scale=np.array([0.5, 0.5]))
+    np.testing.assert_array_equal(O3, O4)
+
+
 # ---------------------------------------------------------------------------
 # KV append
 # ---------------------------------------------------------------------------
@@ -657,6 +686,15 @@ def test_mutant_append_position_off_by_one_is_caught(monkeypatch):
     monkeypatch.setattr(oracle, "kv_append", shifted)
     assert _fails(test_kv_append_worked_example_placement)
     assert _fails(test_kv_append_then_decode_attends_the_new_token)
+
+
+def test_mutant_swapped_kv_scales_are_caught(monkeypatch):
+    orig = oa.gqa_verify
+
+    def swapped(*a, k_scale=1.0, v_scale=1.0, **kw):
+        return orig(*a, k_scale=v_scale, v_scale=k_scale, **kw)
+    monkeypatch.setattr(oracle, "gqa_verify", swapped)
+    assert _fails(test_gqa_verify_fp8_cache_equals_bf16_of_dequantised_values)
 
 
 def test_mutant_window_off_by_one_is_caught(monkeypatch):
