@@ -10,7 +10,7 @@ Printed: ONE JSON line with KV-read GB/s (algorithmic K+V bytes of the
 attended keys / time per call), the roofline of the dominant kernel measured
 with HIP events on the launch stream, and the fp64 CPU oracle's rate on the
 same inputs.  ``--config`` selects another workload (gqa_window, gqa_skewed,
-tiny_gqa, gqa_verify, kv_append, mla_verify, mla_verify_fp8).
+tiny_gqa, gqa_verify, gqa_sinks_fp8, kv_append, mla_verify, mla_verify_fp8).
 """
 
 from __future__ import annotations
@@ -54,8 +54,10 @@ def _parse():
 def _gqa_case(name, torch, pd, splits):
     from synth import gqa_workload
 
-    w = gqa_workload(name)
-    vals = w.values("cuda", poison=False)
+    fp8 = name.endswith("_fp8")
+    base = name[:-4] if fp8 else name
+    w = gqa_workload(base)
+    vals = w.values("cuda", poison=False, fp8=fp8)
     bt = torch.from_numpy(w.block_table).cuda()
     sl = torch.from_numpy(w.seq_lens).cuda()
     S = splits or pd.gqa_split_cap(w.B, w.Hkv, int(w.seq_lens.max()), w.window)
@@ -63,21 +65,27 @@ def _gqa_case(name, torch, pd, splits):
     lse = torch.empty((w.rows, w.Hq), dtype=torch.float32, device="cuda")
     ws = pd.alloc_workspace(w.rows, w.Hq, max(S, 2), w.D, "cuda")
 
-    if w.qlen > 1 or w.real_seq_lens is not None:
+    if w.qlen > 1 or w.real_seq_lens is not None or fp8:
         real = None if w.real_seq_lens is None else torch.from_numpy(w.real_seq_lens).cuda()
 
         def verify_step():
             pd.paged_verify_gqa(vals["q"], vals["kv"], bt, sl, w.qlen, w.sm_scale,
                                 sinks=vals["sinks"], window=w.window, real_seq_lens=real,
-                                num_kv_splits=S, workspace=ws, out=out, lse=lse)
+                                num_kv_splits=S, workspace=ws, out=out, lse=lse,
+                                k_scale=vals.get("k_scale"), v_scale=vals.get("v_scale"))
 
-        desc = (f"GQA causal verify with sinks: B={w.B}, qlen={w.qlen}, Hq={w.Hq}, "
-                f"Hkv={w.Hkv}, D={w.D}, page {w.P} HND bf16, seq_lens U[1024,8192], "
-                "real length L - U{0,1}, 40000-page pool")
+        if fp8:
+            desc = ("GQA decode with sinks on an FP8 E4M3FN cache (per-kv-head K and V "
+                    "scales): B=64, Hq=64, Hkv=8, D=128, page 16 HND, seq_lens U[1024,8192], "
+                    "40000-page pool")
+        else:
+            desc = (f"GQA causal verify with sinks: B={w.B}, qlen={w.qlen}, Hq={w.Hq}, "
+                    f"Hkv={w.Hkv}, D={w.D}, page {w.P} HND bf16, seq_lens U[1024,8192], "
+                    "real length L - U{0,1}, 40000-page pool")
         # the kernel and its merge are timed together (no partials-only verify entry)
         return dict(w=w, vals=vals, S=S, step=verify_step, kernel=None, rest=None,
-                    kv_bytes=w.kv_bytes(), flops=w.flops(), desc=desc, kind="gqa_verify",
-                    kernel_name="gqa_decode_kernel")
+                    kv_bytes=w.kv_bytes() // (2 if fp8 else 1), flops=w.flops(), desc=desc,
+                    kind="gqa_fp8" if fp8 else "gqa_verify", kernel_name="gqa_decode_kernel")
 
     def step():
         pd.paged_decode_gqa(vals["q"], vals["kv"], bt, sl, w.sm_scale, sinks=vals["sinks"],
@@ -240,17 +248,23 @@ def _cpu_baseline(case, budget_s=20.0):
             t_total += time.perf_counter() - t0
             lo = max(int(w.seq_lens[b]) - w.window, 0) if w.window > 0 else 0
             done_bytes += (int(w.seq_lens[b]) - lo) * w.Hkv * 2 * w.D * 2
-        elif case["kind"] == "gqa_verify":
+        elif case["kind"] in ("gqa_verify", "gqa_fp8"):
+            fp8 = case["kind"] == "gqa_fp8"
             rows = slice(b * w.qlen, (b + 1) * w.qlen)
             q = vals["q"][rows].view(torch.int16).cpu().numpy().view(np.uint16)
             sinks = None if vals["sinks"] is None else vals["sinks"].cpu().numpy()
             real = None if w.real_seq_lens is None else w.real_seq_lens[b:b + 1]
+            scales = {}
+            if fp8:
+                scales = dict(kv_dtype="fp8_e4m3fn",
+                              k_scale=vals["k_scale"].cpu().numpy().astype(np.float64),
+                              v_scale=vals["v_scale"].cpu().numpy().astype(np.float64))
             t0 = time.perf_counter()
             oracle.gqa_verify(q, kv, bt2, w.seq_lens[b:b + 1], w.qlen, w.sm_scale,
-                              sinks=sinks, window=w.window, real_seq_lens=real)
+                              sinks=sinks, window=w.window, real_seq_lens=real, **scales)
             t_total += time.perf_counter() - t0
             lo, hi = w.key_range(b)
-            done_bytes += max(hi - lo, 0) * w.Hkv * 2 * w.D * 2
+            done_bytes += max(hi - lo, 0) * w.Hkv * 2 * w.D * (1 if fp8 else 2)
         else:
             rows = slice(b * w.qlen, (b + 1) * w.qlen)
             q = vals["q"][rows].view(torch.int16).cpu().numpy().view(np.uint16)
@@ -352,7 +366,7 @@ def main():
 
     kv = case["kv_bytes"]
     value = kv / (ms_per_step * 1e-3) / 1e9
-    if case["kind"] in ("gqa", "gqa_verify", "append"):
+    if case["kind"] in ("gqa", "gqa_verify", "gqa_fp8", "append"):
         roof = {"bound": "hbm", "achieved": round(kv / (k_ms * 1e-3) / 1e9, 2),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     else:

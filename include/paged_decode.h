@@ -185,6 +185,15 @@ PD_API int paged_decode_gqa(const void* q, int64_t q_stride_b, int64_t q_stride_
  * paged_decode_gqa.
  *
  * q            [B*qlen, Hq, D] bf16, strides (q_stride_row, q_stride_h, 1).
+ * kv_dtype     PD_KV_BF16, or PD_KV_FP8_E4M3FN: the cache holds E4M3FN codes
+ *              (1 byte each) and K_j = code * k_scale, V_j = code * v_scale,
+ *              as the scalar k_scale dequantises an FP8 cache in
+ *              decode_attention_fwd_verify; K and V are separate tensors, so
+ *              each has its own scale.
+ * k_scale,     device fp32: one value (scale_per_head = 0) or [Hkv]
+ * v_scale      (scale_per_head = 1); NULL means 1.  Ignored for bf16.  Each
+ *              scale must be finite and > 0 (the running max is kept in
+ *              unscaled scores).
  * real_seq_lens [B] int32 or NULL.
  * out          [B*qlen, Hq, D] bf16, strides (o_stride_row, o_stride_h, 1).
  * lse          [B*qlen, Hq] fp32 with row stride lse_stride_row, or NULL.
@@ -194,10 +203,13 @@ PD_API int paged_decode_gqa(const void* q, int64_t q_stride_b, int64_t q_stride_
  * Supported: as paged_decode_gqa, with qlen * G <= 16 (the verify tokens of a
  * kv head's query heads share one score tile, so a cache tile is read once
  * for all of them); otherwise PD_ERR_UNSUPPORTED.  Also
- * ((qlen-1)*q_stride_row + (G-1)*q_stride_h + D) * 2 < 2^31.
+ * ((qlen-1)*q_stride_row + (G-1)*q_stride_h + D) * 2 < 2^31.  FP8 cache
+ * strides must be multiples of 16.
  */
 PD_API int paged_verify_gqa(const void* q, int64_t q_stride_row, int64_t q_stride_h,
-                     const void* kv, int64_t kv_stride_page, int64_t kv_stride_head,
+                     const void* kv, int32_t kv_dtype, const float* k_scale,
+                     const float* v_scale, int32_t scale_per_head,
+                     int64_t kv_stride_page, int64_t kv_stride_head,
                      int32_t num_pages, const int32_t* block_table, int64_t bt_stride_b,
                      int32_t max_blocks, const int32_t* seq_lens,
                      const int32_t* real_seq_lens, int32_t qlen, const float* sinks,

@@ -70,7 +70,8 @@ def _load():
     lib.paged_decode_gqa.restype = ctypes.c_int
     lib.paged_verify_gqa.argtypes = [
         _c_vp, _c_i64, _c_i64,                  # q, strides
-        _c_vp, _c_i64, _c_i64, _c_i32,          # kv, page/head strides, num_pages
+        _c_vp, _c_i32, _c_vp, _c_vp, _c_i32,    # kv, kv_dtype, k_scale, v_scale, per-head flag
+        _c_i64, _c_i64, _c_i32,                 # kv page/head strides, num_pages
         _c_vp, _c_i64, _c_i32,                  # block_table, row stride, max_blocks
         _c_vp, _c_vp, _c_i32,                   # seq_lens, real_seq_lens, qlen
         _c_vp, _c_i32, _c_f32,                  # sinks, window, sm_scale

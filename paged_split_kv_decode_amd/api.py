@@ -140,16 +140,23 @@ def paged_decode_gqa(q, kv, block_table, seq_lens, sm_scale, sinks=None, window=
 
 def paged_verify_gqa(q, kv, block_table, seq_lens, qlen, sm_scale, sinks=None, window=0,
                      real_seq_lens=None, num_kv_splits=1, workspace=None, out=None, lse=None,
-                     stream=None, return_lse=True):
+                     stream=None, return_lse=True, k_scale=None, v_scale=None):
     """Paged GQA causal verify (include/paged_decode.h: paged_verify_gqa).
 
     q [B*qlen, Hq, D] bf16 (the qlen tokens of a request contiguous); kv
-    [num_pages, Hkv, P, 2D] bf16; block_table [B, max_blocks] int32; seq_lens
-    and real_seq_lens (or None) [B] int32; sinks [Hq] fp32 or None.
+    [num_pages, Hkv, P, 2D] bf16, or FP8 E4M3FN codes (uint8 or
+    float8_e4m3fn) with device fp32 k_scale / v_scale of one element (one
+    scale) or Hkv elements (one per kv head), None meaning 1; block_table
+    [B, max_blocks] int32; seq_lens and real_seq_lens (or None) [B] int32;
+    sinks [Hq] fp32 or None.
     Returns (out [B*qlen, Hq, D] bf16, lse [B*qlen, Hq] fp32 or None).
     """
     _need(q, "q", torch.bfloat16, 3)
-    _need(kv, "kv", torch.bfloat16, 4)
+    fp8 = kv.dtype in (torch.uint8, torch.float8_e4m3fn)
+    if not fp8:
+        _need(kv, "kv", torch.bfloat16, 4)
+    elif not kv.is_cuda or kv.dim() != 4:
+        raise ValueError("kv must be a 4-D device tensor")
     _need(block_table, "block_table", torch.int32, 2)
     _need(seq_lens, "seq_lens", torch.int32, 1)
     qlen = int(qlen)
@@ -181,13 +188,25 @@ def paged_verify_gqa(q, kv, block_table, seq_lens, qlen, sm_scale, sinks=None, w
         _need(lse, "lse", torch.float32, 2)
         if lse.stride(1) != 1:
             raise ValueError("lse must have a contiguous last dim")
+    per_head = 0
+    for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+        if t is None:
+            continue
+        _need(t, name, torch.float32)
+        if t.numel() not in (1, Hkv) or not t.is_contiguous():
+            raise ValueError(f"{name} must hold 1 or Hkv contiguous values")
+        if t.numel() == Hkv and Hkv > 1:
+            per_head = 1
+    if per_head and any(t is not None and t.numel() != Hkv for t in (k_scale, v_scale)):
+        raise ValueError("k_scale and v_scale must both be scalars or both per kv head")
     S = int(num_kv_splits)
     if S > 1 and workspace is None:
         workspace = alloc_workspace(rows, Hq, S, D, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.paged_verify_gqa(
         _ptr(q), q.stride(0), q.stride(1),
-        _ptr(kv), kv.stride(0), kv.stride(1), num_pages,
+        _ptr(kv), PD_KV_FP8_E4M3FN if fp8 else PD_KV_BF16, _ptr(k_scale), _ptr(v_scale), per_head,
+        kv.stride(0), kv.stride(1), num_pages,
         _ptr(block_table), block_table.stride(0), block_table.shape[1],
         _ptr(seq_lens), _ptr(real_seq_lens), qlen,
         _ptr(sinks), int(window or 0), float(sm_scale),

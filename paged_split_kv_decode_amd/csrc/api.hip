@@ -96,6 +96,8 @@ namespace {
 // GQA decode and verify.  Rows of q / out / lse are (request, verify token)
 // pairs, row b * qlen + t; decode is qlen = 1 with no real lengths.
 static int gqa_common(const void* q, int64_t q_stride_b, int64_t q_stride_h, const void* kv,
+               int32_t kv_dtype, const float* k_scale, const float* v_scale,
+               int32_t scale_per_head,
                int64_t kv_stride_page, int64_t kv_stride_head, int32_t num_pages,
                const int32_t* block_table, int64_t bt_stride_b, int32_t max_blocks,
                const int32_t* seq_lens, const int32_t* real_seq_lens, int32_t qlen,
@@ -108,6 +110,10 @@ static int gqa_common(const void* q, int64_t q_stride_b, int64_t q_stride_h, con
       num_pages < 0 || max_blocks < 0 || !std::isfinite(sm_scale) || !(sm_scale > 0.f))
     return PD_ERR_INVALID;
   if (num_q_heads % num_kv_heads != 0) return PD_ERR_INVALID;
+  if ((kv_dtype != PD_KV_BF16 && kv_dtype != PD_KV_FP8_E4M3FN) ||
+      (scale_per_head != 0 && scale_per_head != 1))
+    return PD_ERR_INVALID;
+  const bool fp8 = kv_dtype == PD_KV_FP8_E4M3FN;
   const int32_t G = num_q_heads / num_kv_heads;
   if (head_dim != 128 || (page_size != 16 && page_size != 32) || (int64_t)qlen * G > 16)
     return PD_ERR_UNSUPPORTED;
@@ -118,8 +124,9 @@ static int gqa_common(const void* q, int64_t q_stride_b, int64_t q_stride_h, con
   if (q_stride_b < 0 || q_stride_h < 0 || kv_stride_page < 0 || kv_stride_head < 0 ||
       bt_stride_b < 0 || o_stride_b < 0 || o_stride_h < 0 || lse_stride_b < 0)
     return PD_ERR_INVALID;
+  const int64_t kv_align = fp8 ? 16 : 8;   // 16-byte rows of the cache
   if (!aligned16(q) || !aligned16(kv) || q_stride_b % 8 || q_stride_h % 8 ||
-      kv_stride_page % 8 || kv_stride_head % 8)
+      kv_stride_page % kv_align || kv_stride_head % kv_align)
     return PD_ERR_ALIGN;
   if (!partials_only && (!aligned16(out) || o_stride_b % 8 || o_stride_h % 8)) return PD_ERR_ALIGN;
   const int64_t rows = (int64_t)batch * qlen;
@@ -158,6 +165,10 @@ static int gqa_common(const void* q, int64_t q_stride_b, int64_t q_stride_h, con
   a.seq_lens = seq_lens;
   a.real_lens = real_seq_lens;
   a.qlen = qlen;
+  a.kv_fp8 = fp8 ? 1 : 0;
+  a.k_scale = fp8 ? k_scale : nullptr;
+  a.v_scale = fp8 ? v_scale : nullptr;
+  a.scale_stride = scale_per_head;
   a.sinks = sinks;
   a.window = window;
   a.scale_log2 = sm_scale * kLog2eHost;
@@ -204,14 +215,17 @@ int paged_decode_gqa(const void* q, int64_t q_stride_b, int64_t q_stride_h, cons
                      int32_t page_size, int32_t num_kv_splits, float* workspace,
                      size_t workspace_bytes, void* out, int64_t o_stride_b, int64_t o_stride_h,
                      float* lse, int64_t lse_stride_b, void* stream) {
-  return gqa_common(q, q_stride_b, q_stride_h, kv, kv_stride_page, kv_stride_head, num_pages,
-                    block_table, bt_stride_b, max_blocks, seq_lens, nullptr, 1, sinks, window,
-                    sm_scale, batch, num_q_heads, num_kv_heads, head_dim, page_size,
-                    num_kv_splits, workspace, workspace_bytes, out, o_stride_b, o_stride_h, lse,
-                    lse_stride_b, stream, false);
+  return gqa_common(q, q_stride_b, q_stride_h, kv, PD_KV_BF16, nullptr, nullptr, 0,
+                    kv_stride_page, kv_stride_head, num_pages, block_table, bt_stride_b,
+                    max_blocks, seq_lens, nullptr, 1, sinks, window, sm_scale, batch,
+                    num_q_heads, num_kv_heads, head_dim, page_size, num_kv_splits, workspace,
+                    workspace_bytes, out, o_stride_b, o_stride_h, lse, lse_stride_b, stream,
+                    false);
 }
 
 int paged_verify_gqa(const void* q, int64_t q_stride_row, int64_t q_stride_h, const void* kv,
+                     int32_t kv_dtype, const float* k_scale, const float* v_scale,
+                     int32_t scale_per_head,
                      int64_t kv_stride_page, int64_t kv_stride_head, int32_t num_pages,
                      const int32_t* block_table, int64_t bt_stride_b, int32_t max_blocks,
                      const int32_t* seq_lens, const int32_t* real_seq_lens, int32_t qlen,
@@ -220,7 +234,8 @@ int paged_verify_gqa(const void* q, int64_t q_stride_row, int64_t q_stride_h, co
                      int32_t page_size, int32_t num_kv_splits, float* workspace,
                      size_t workspace_bytes, void* out, int64_t o_stride_row, int64_t o_stride_h,
                      float* lse, int64_t lse_stride_row, void* stream) {
-  return gqa_common(q, q_stride_row, q_stride_h, kv, kv_stride_page, kv_stride_head, num_pages,
+  return gqa_common(q, q_stride_row, q_stride_h, kv, kv_dtype, k_scale, v_scale,
+                    scale_per_head, kv_stride_page, kv_stride_head, num_pages,
                     block_table, bt_stride_b, max_blocks, seq_lens, real_seq_lens, qlen, sinks,
                     window, sm_scale, batch, num_q_heads, num_kv_heads, head_dim, page_size,
                     num_kv_splits, workspace, workspace_bytes, out, o_stride_row, o_stride_h,
@@ -235,7 +250,8 @@ int paged_decode_gqa_partials(const void* q, int64_t q_stride_b, int64_t q_strid
                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                               int32_t page_size, int32_t num_kv_splits, float* workspace,
                               size_t workspace_bytes, void* stream) {
-  return gqa_common(q, q_stride_b, q_stride_h, kv, kv_stride_page, kv_stride_head, num_pages,
+  return gqa_common(q, q_stride_b, q_stride_h, kv, PD_KV_BF16, nullptr, nullptr, 0,
+                    kv_stride_page, kv_stride_head, num_pages,
                     block_table, bt_stride_b, max_blocks, seq_lens, nullptr, 1, nullptr, window,
                     sm_scale, batch, num_q_heads, num_kv_heads, head_dim, page_size,
                     num_kv_splits, workspace, workspace_bytes, nullptr, 0, 0, nullptr, 0, stream,

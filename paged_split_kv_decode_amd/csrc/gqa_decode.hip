@@ -48,10 +48,13 @@ namespace {
 
 constexpr int kD = 128;
 constexpr int kNW = 4;                                  // waves per workgroup
-constexpr int kRowBytes = 2 * kD * 2;                   // K|V row of one token
+constexpr int kRowBytes = 2 * kD * 2;                   // K|V row of one token (bf16)
 constexpr int kTileBytes = kTileTokens * kRowBytes;     // 16 KB
-constexpr int kLoadsPerTile = kTileBytes / (64 * 16);   // 16 wave loads
-constexpr int kRingBytes = 2 * kTileBytes;              // per wave
+constexpr int kRowBytes8 = 2 * kD;                      // K|V row of one token (FP8)
+constexpr int kTileBytes8 = kTileTokens * kRowBytes8;   // 8 KB
+// Ring of a wave: 2 tiles as loaded; an FP8 ring is followed by the bf16
+// tile it is dequantised into, so both rings take 32 KB.
+constexpr int kRingBytes = 2 * kTileBytes;
 // Smallest share a wave takes: below it the per-wave start-up dominates.
 constexpr int kMinWaveTiles = 4;
 
@@ -130,8 +133,10 @@ constexpr int kCachedChunks = 4;                          // request lengths kep
 
 // V: verify rows (qlen > 1 or real lengths); the decode instantiation has a
 // single column range per unit and none of the per-column limit work.
-template <int P, bool V>
+template <int P, bool V, bool F8>
 __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
+  constexpr int kSlotBytes = F8 ? kTileBytes8 : kTileBytes;     // one tile as loaded
+  constexpr int kLoadsPerTile = kSlotBytes / (64 * 16);         // 16 (bf16) or 8 (FP8) loads
   __shared__ __attribute__((aligned(1024))) char smem[kNW * kWaveLds];
 
   const int tid = threadIdx.x;
@@ -144,7 +149,8 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
   const int S = a.S;
   const int Hkv = a.Hkv;
   const bool direct = S == 1 && !a.partials;
-  const float c = a.scale_log2;
+  float c = a.scale_log2;   // per piece: times the kv head's k_scale for FP8
+  float v_mult = 1.f;        // per piece: the kv head's v_scale for FP8
   const int n_waves = gridDim.x * kNW;
   const int w = uniform(blockIdx.x * kNW + wave_in_wg);
   PD_LDS char* ring = (PD_LDS char*)smem + wave_in_wg * kWaveLds;
@@ -335,22 +341,24 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
       bad_page |= tp.att[j] && !inr;
     }
     if (piece_start(cu)) load_q(cu);
-    const uint32_t dst = uniform((int)lds_addr(ring + slot * kTileBytes));
-    const char* kv_head = (const char*)(a.kv + (int64_t)cu.kvh * a.kv_sh);
-    const int cs = lane & 31;
+    const uint32_t dst = uniform((int)lds_addr(ring + slot * kSlotBytes));
+    constexpr int kElem = F8 ? 1 : 2;
+    const char* kv_head = (const char*)a.kv + (int64_t)cu.kvh * a.kv_sh * kElem;
     const char* pbase[PPT];
 #pragma unroll
     for (int j = 0; j < PPT; ++j)
-      pbase[j] = ok[j] ? kv_head + (int64_t)tp.id[j] * a.kv_sp * 2 : (const char*)a.q;
+      pbase[j] = ok[j] ? kv_head + (int64_t)tp.id[j] * a.kv_sp * kElem : (const char*)a.q;
     auto one = [&](auto ic) {
       constexpr int i = decltype(ic)::value;
-      constexpr int kRowsPerLoad = 2;
+      // bf16: 2 rows of 32 chunks per load, chunks XOR-swizzled per row;
+      // FP8: 4 rows of 16 chunks per load, plain
+      constexpr int kRowsPerLoad = F8 ? 4 : 2;
       constexpr int j = P >= kTileTokens ? 0 : (kRowsPerLoad * i) / P;
       // tiles start on a page boundary, so a row's slot in its page is r mod P
-      const int r = kRowsPerLoad * i + (lane >> 5);
+      const int r = kRowsPerLoad * i + (F8 ? (lane >> 4) : (lane >> 5));
       const uint32_t slot_tok = (uint32_t)(r & (P - 1));
-      const uint32_t ch = (uint32_t)(cs ^ swz(r));
-      const uint32_t voff = ok[j] ? (slot_tok * (2 * kD) + ch * 8) * 2 : 0u;
+      const uint32_t ch = F8 ? (uint32_t)(lane & 15) : (uint32_t)((lane & 31) ^ swz(r));
+      const uint32_t voff = ok[j] ? slot_tok * (2 * kD * kElem) + ch * 16 : 0u;
       global_to_lds_16_stream<i * 1024>(pbase[j], voff, dst);
     };
     [&]<int... I>(std::integer_sequence<int, I...>) {
@@ -382,7 +390,7 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
       if (direct) {
         float den = l_tot;
         if (a.sinks != nullptr && !empty) den += fast_exp2(a.sinks[hq] * kLog2e - m_run * c);
-        const float inv = empty ? 0.f : 1.f / den;
+        const float inv = empty ? 0.f : v_mult / den;
         uint16_t* orow = a.out + row * a.o_sb + (int64_t)hq * a.o_sh + 4 * g4;
 #pragma unroll
         for (int blk = 0; blk < 8; ++blk) {
@@ -395,7 +403,7 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
       } else {
         const int s = sh.split ? w - cu.p0 / sh.tpw : 0;
         float* slot = a.ws + ((row * a.Hq + hq) * S + s) * (kD + 1);
-        const float inv = empty ? 0.f : 1.f / l_tot;
+        const float inv = empty ? 0.f : v_mult / l_tot;
 #pragma unroll
         for (int blk = 0; blk < 8; ++blk) {
           f32x4 r = o[blk] * inv;
@@ -425,6 +433,11 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         piece_bad = false;
+        if constexpr (F8) {
+          const int si = cc.kvh * a.scale_stride;
+          c = a.scale_log2 * (a.k_scale != nullptr ? a.k_scale[si] : 1.f);
+          v_mult = a.v_scale != nullptr ? a.v_scale[si] : 1.f;
+        }
         if constexpr (V) {
           const int L = as_const(a.seq_lens)[cc.b], Lr = real_len(a, cc.b);
           col_hi = row_hi<P>(a, L, Lr, t_col);
@@ -462,7 +475,28 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
 
       const int slot = k & 1;
       piece_bad |= (bad_slots >> slot) & 1;
-      PD_LDS char* tl = ring + slot * kTileBytes;
+      PD_LDS char* tl = ring + slot * kSlotBytes;
+      if constexpr (F8) {
+        // exact FP8 -> bf16 into the bf16 tile after the ring, in the bf16
+        // layout: item (row r, FP8 chunk cf of 16 codes) -> bf16 chunks 2 cf
+        // and 2 cf + 1 of row r, XOR-swizzled
+        PD_LDS char* st = ring + 2 * kTileBytes8;
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+          const int r = 4 * it + (lane >> 4), cf = lane & 15;
+          const u32x4 w = *(PD_LDS const u32x4*)(tl + r * kRowBytes8 + cf * 16);
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            u32x4 cv;
+            cv[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * h], 1.f, false));
+            cv[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * h], 1.f, true));
+            cv[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * h + 1], 1.f, false));
+            cv[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * h + 1], 1.f, true));
+            *(PD_LDS u32x4*)(st + r * kRowBytes + (((2 * cf + h) ^ swz(r)) << 4)) = cv;
+          }
+        }
+        tl = st;
+      }
       const int lo = cc.r.lo, hi = cc.r.hi;
       const int tok0 = ((lo >> 5) + cc.i) * kTileTokens;
 
@@ -610,13 +644,18 @@ hipError_t launch_gqa_decode(const GqaArgs& a, hipStream_t stream) {
   if (n <= 0) return hipErrorInvalidDevice;
   dim3 grid(n), block(kNW * 64);
   const bool verify = a.qlen > 1 || a.real_lens != nullptr;
-  switch (a.P * 2 + (verify ? 1 : 0)) {
-    case 32: hipLaunchKernelGGL((gqa_decode_kernel<16, false>), grid, block, 0, stream, a); break;
-    case 33: hipLaunchKernelGGL((gqa_decode_kernel<16, true>), grid, block, 0, stream, a); break;
-    case 64: hipLaunchKernelGGL((gqa_decode_kernel<32, false>), grid, block, 0, stream, a); break;
-    case 65: hipLaunchKernelGGL((gqa_decode_kernel<32, true>), grid, block, 0, stream, a); break;
+#define PD_GQA_CASE(PP, VV, FF)                                                                 \
+  case PP * 4 + (VV ? 2 : 0) + (FF ? 1 : 0):                                                    \
+    hipLaunchKernelGGL((gqa_decode_kernel<PP, VV, FF>), grid, block, 0, stream, a);             \
+    break;
+  switch (a.P * 4 + (verify ? 2 : 0) + (a.kv_fp8 ? 1 : 0)) {
+    PD_GQA_CASE(16, false, false) PD_GQA_CASE(16, false, true)
+    PD_GQA_CASE(16, true, false) PD_GQA_CASE(16, true, true)
+    PD_GQA_CASE(32, false, false) PD_GQA_CASE(32, false, true)
+    PD_GQA_CASE(32, true, false) PD_GQA_CASE(32, true, true)
     default: return hipErrorInvalidValue;
   }
+#undef PD_GQA_CASE
   return hipGetLastError();
 }
 

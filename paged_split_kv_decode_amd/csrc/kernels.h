@@ -29,6 +29,10 @@ struct GqaArgs {
   const int32_t* seq_lens;
   const int32_t* real_lens;  // nullptr: equal to seq_lens
   int32_t qlen;              // verify tokens per request; qlen * G <= 16
+  int32_t kv_fp8;            // 1: FP8 E4M3FN codes, K scaled by k_scale, V by v_scale
+  const float* k_scale;      // nullptr: 1; else k_scale[kvh * scale_stride]
+  const float* v_scale;
+  int32_t scale_stride;      // 0: one scale for all kv heads, 1: one per kv head
   const float* sinks;
   int32_t window;
   float scale_log2;  // sm_scale * log2(e)

@@ -167,12 +167,15 @@ class GqaWorkload:
                 for lo, hi in (self.row_range(b, t),))
         return int(n) * self.Hq * 4 * self.D
 
-    def values(self, device="cpu", poison=True):
+    def values(self, device="cpu", poison=True, fp8=False):
         """Draw q, the page pool and sinks as torch tensors on ``device``.
 
         Returns dict(q bf16 [B * qlen, Hq, D], kv bf16 [pages, Hkv, P, 2D],
         sinks fp32 [Hq] or None).  With ``poison`` every never-attended slot
-        holds bf16 NaN.
+        holds bf16 NaN.  With ``fp8`` the cache is FP8 E4M3FN codes (uint8)
+        of the bf16 values divided by per-kv-head scales, k_scale / v_scale
+        [Hkv] fp32 = amax / 448 of that head's attended K / V values (NaN
+        code 0x7F where never attended, with ``poison``).
         """
         dev = torch.device(device)
         g = torch.Generator(device=dev)
@@ -189,6 +192,23 @@ class GqaWorkload:
         sinks = None
         if self.has_sinks:
             sinks = torch.randn((self.Hq,), generator=g, device=dev, dtype=torch.float32)
+        if fp8:
+            mask = torch.from_numpy(~self.attended_mask()).to(dev)
+            ks = torch.empty(self.Hkv, dtype=torch.float32, device=dev)
+            vs = torch.empty(self.Hkv, dtype=torch.float32, device=dev)
+            codes = torch.empty(kv.shape, dtype=torch.uint8, device=dev)
+            for h in range(self.Hkv):
+                x = kv[:, h].float().masked_fill(mask[:, :, None], 0.0)
+                ka, va = float(x[..., :self.D].abs().max()), float(x[..., self.D:].abs().max())
+                ks[h] = ka / 448.0 if ka > 0 else 1.0
+                vs[h] = va / 448.0 if va > 0 else 1.0
+                x = kv[:, h].float()
+                x[..., :self.D] /= ks[h]
+                x[..., self.D:] /= vs[h]
+                codes[:, h] = x.clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+            if poison:
+                codes.masked_fill_(mask[:, None, :, None], FP8_NAN_CODE)
+            return dict(q=q, kv=codes, sinks=sinks, k_scale=ks, v_scale=vs)
         if poison:
             mask = torch.from_numpy(~self.attended_mask()).to(dev)
             kv.view(torch.int16).masked_fill_(mask[:, None, :, None],

@@ -34,8 +34,13 @@ def compact_gqa(w, vals, requests):
     remap = np.full(w.num_pages, -1, np.int64)
     remap[used] = np.arange(len(used))
     idx = torch.from_numpy(used).to(vals["kv"].device)
-    kv = bits16(vals["kv"].index_select(0, idx)) if len(used) else \
-        np.zeros((0,) + tuple(vals["kv"].shape[1:]), np.uint16)
+    raw_dtype = np.uint8 if vals["kv"].dtype == torch.uint8 else np.uint16
+    if not len(used):
+        kv = np.zeros((0,) + tuple(vals["kv"].shape[1:]), raw_dtype)
+    elif raw_dtype == np.uint8:
+        kv = vals["kv"].index_select(0, idx).cpu().numpy()
+    else:
+        kv = bits16(vals["kv"].index_select(0, idx))
     bt2 = np.where(bt >= 0, remap[np.maximum(bt, 0)], -1).astype(np.int32)
     rows = [b * w.qlen + t for b in requests for t in range(w.qlen)]
     q = bits16(vals["q"][rows])
@@ -47,9 +52,15 @@ def oracle_gqa(w, vals, requests=None):
     """Oracle O, LSE of a GQA workload's requests (rows b * qlen + t for verify)."""
     requests = range(w.B) if requests is None else list(requests)
     q, kv, bt, sl, sk = compact_gqa(w, vals, requests)
-    if w.qlen == 1 and w.real_seq_lens is None:
+    fp8 = vals["kv"].dtype == torch.uint8
+    if w.qlen == 1 and w.real_seq_lens is None and not fp8:
         return oracle.gqa_decode(q, kv, bt, sl, w.sm_scale, sinks=sk, window=w.window)
     real = None if w.real_seq_lens is None else w.real_seq_lens[list(requests)]
+    if fp8:
+        return oracle.gqa_verify(q, kv, bt, sl, w.qlen, w.sm_scale, sinks=sk, window=w.window,
+                                 real_seq_lens=real, kv_dtype="fp8_e4m3fn",
+                                 k_scale=vals["k_scale"].cpu().numpy().astype(np.float64),
+                                 v_scale=vals["v_scale"].cpu().numpy().astype(np.float64))
     return oracle.gqa_verify(q, kv, bt, sl, w.qlen, w.sm_scale, sinks=sk, window=w.window,
                              real_seq_lens=real)
 

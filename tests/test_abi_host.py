@@ -137,7 +137,8 @@ def test_gqa_argument_checks_happen_before_any_hip_call():
 
 
 def _gqav(**kw):
-    a = dict(q=FAKE, qsr=64 * 128, qsh=128, kv=FAKE, kvsp=8 * 16 * 256, kvsh=16 * 256,
+    a = dict(q=FAKE, qsr=64 * 128, qsh=128, kv=FAKE, dt=0, ks=NULL, vs=NULL, per=0,
+             kvsp=8 * 16 * 256, kvsh=16 * 256,
              npages=10, bt=FAKE, btsb=4, maxb=4, sl=FAKE, real=NULL, qlen=2, sinks=NULL,
              window=0, scale=0.088, B=2, Hq=64, Hkv=8, D=128, P=16, S=1, ws=NULL, wsb=0,
              out=FAKE, osr=64 * 128, osh=128, lse=NULL, lser=64, stream=NULL)
@@ -159,6 +160,10 @@ def test_gqa_verify_argument_checks_happen_before_any_hip_call():
     assert _gqav(S=4, ws=FAKE + 4, wsb=need) == PD_ERR_ALIGN
     # the query rows of a unit must be addressable with a 32-bit byte offset
     assert _gqav(qsr=(1 << 30)) == PD_ERR_UNSUPPORTED
+    assert _gqav(dt=3) == PD_ERR_INVALID                      # unknown cache type
+    assert _gqav(dt=1, per=2) == PD_ERR_INVALID
+    assert _gqav(dt=1, kvsh=16 * 256 + 8) == PD_ERR_ALIGN     # FP8 rows: 16-byte strides
+    assert _gqav(dt=1, S=4) == PD_ERR_WORKSPACE
 
 
 def _app(**kw):
