@@ -410,8 +410,10 @@ def test_gqa_verify_rows_are_prefix_decodes():
 
 
 def test_gqa_verify_matches_causal_dense_brute_force():
-    rng = np.random.default_rng(23)
-    lens, qlen, Hq, Hkv, D, P, W = [11, 6], 4, 4, 2, 8, 4, 5
+    _check_gqa_verify_brute_force(np.random.default_rng(23), [11, 6], 4, 4, 2, 8, 4, 5)
+
+
+def _check_gqa_verify_brute_force(rng, lens, qlen, Hq, Hkv, D, P, W):
     q, kv, bt, sl, sk = _rand_gqa_verify(rng, lens, qlen, Hq, Hkv, D, P)
     O, lse = oracle.gqa_verify(q, kv, bt, sl, qlen, 0.3, sinks=sk, window=W)
     qf = oa.bf16_bits_to_f64(q)
@@ -456,8 +458,10 @@ def _rand_mla(rng, lens, qlen, H, Lk, P, fp8=False):
 
 
 def test_mla_matches_causal_dense_brute_force():
-    rng = np.random.default_rng(13)
-    lens, real, qlen, H, Lk, Lv, P = [9, 3, 6], [8, 3, 4], 3, 2, 12, 8, 4
+    _check_mla_brute_force(np.random.default_rng(13), [9, 3, 6], [8, 3, 4], 3, 2, 12, 8, 4)
+
+
+def _check_mla_brute_force(rng, lens, real, qlen, H, Lk, Lv, P):
     q, kv, bt = _rand_mla(rng, lens, qlen, H, Lk, P)
     O, lse = oracle.mla_verify(q, kv, bt, np.array(lens), np.array(real), qlen, 0.3, Lv)
     qf = oa.bf16_bits_to_f64(q)
@@ -522,6 +526,74 @@ def test_mla_3d_cache_view_is_the_same_cache():
     b = oracle.mla_verify(q, kv.reshape(-1, 1, 8), bt, np.array([6, 9]), None, 2, 0.5, 4,
                           page_size=4)
     np.testing.assert_array_equal(a[0], b[0])
+
+
+# ---------------------------------------------------------------------------
+# general page sizes ("vllm.v1.attention.ops.triton_decode_attention": the
+# module supports any page size >= 1)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("P", [1, 3, 8, 64])
+def test_gqa_verify_brute_force_at_page_size(P):
+    # lengths below, at and past one page, several pages, and a window
+    _check_gqa_verify_brute_force(np.random.default_rng(60 + P), [13, 1, 70], 2, 4, 2, 8, P, 9)
+
+
+@pytest.mark.parametrize("P", [1, 3, 32])
+def test_mla_brute_force_at_page_size(P):
+    _check_mla_brute_force(np.random.default_rng(70 + P), [9, 2, 40], [8, 2, 39], 3, 2, 12, 8, P)
+
+
+def _relayout_gqa(kv, bt, lens, P2, rng):
+    """The same logical cache stored with page size P2 in a shuffled pool."""
+    P = kv.shape[2]
+    pages_per = [-(-L // P2) for L in lens]
+    n_pages = sum(pages_per) + 1
+    perm = rng.permutation(n_pages)
+    bt2 = np.full((len(lens), max(pages_per + [1]) + 1), -1, np.int32)
+    kv2 = np.full((n_pages, kv.shape[1], P2, kv.shape[3]), NAN16, np.uint16)
+    off = 0
+    for b, L in enumerate(lens):
+        bt2[b, :pages_per[b]] = perm[off:off + pages_per[b]]
+        off += pages_per[b]
+        for j in range(L):
+            kv2[bt2[b, j // P2], :, j % P2] = kv[bt[b, j // P], :, j % P]
+    return kv2, bt2
+
+
+def test_gqa_result_does_not_depend_on_page_size():
+    """One logical cache laid out with page sizes 1, 2, 5, 16 and 64 gives
+    bitwise the same result: the page size only changes where a key lives."""
+    rng = np.random.default_rng(80)
+    lens, qlen = [37, 4, 0, 20], 2
+    q, kv, bt, sl, sk = _rand_gqa_verify(rng, lens, qlen, 4, 2, 8, 4)
+    ref = oracle.gqa_verify(q, kv, bt, sl, qlen, 0.3, sinks=sk, window=11)
+    for P2 in (1, 2, 5, 16, 64):
+        kv2, bt2 = _relayout_gqa(kv, bt, lens, P2, rng)
+        got = oracle.gqa_verify(q, kv2, bt2, sl, qlen, 0.3, sinks=sk, window=11)
+        np.testing.assert_array_equal(ref[0], got[0])
+        np.testing.assert_array_equal(ref[1], got[1])
+
+
+def test_mla_result_does_not_depend_on_page_size():
+    rng = np.random.default_rng(81)
+    lens, real, qlen, Lk = [21, 3], [20, 3], 2, 12
+    q, kv, bt = _rand_mla(rng, lens, qlen, 2, Lk, 4)
+    ref = oracle.mla_verify(q, kv, bt, np.array(lens), np.array(real), qlen, 0.3, 8)
+    for P2 in (1, 3, 8, 32):
+        pages_per = [-(-L // P2) for L in lens]
+        perm = rng.permutation(sum(pages_per))
+        bt2 = np.full((len(lens), max(pages_per)), -1, np.int32)
+        kv2 = np.full((sum(pages_per), P2, 1, Lk), NAN16, np.uint16)
+        off = 0
+        for b, L in enumerate(lens):
+            bt2[b, :pages_per[b]] = perm[off:off + pages_per[b]]
+            off += pages_per[b]
+            for j in range(L):
+                kv2[bt2[b, j // P2], j % P2] = kv[bt[b, j // 4], j % 4]
+        got = oracle.mla_verify(q, kv2, bt2, np.array(lens), np.array(real), qlen, 0.3, 8)
+        np.testing.assert_array_equal(ref[0], got[0])
+        np.testing.assert_array_equal(ref[1], got[1])
 
 
 # ---------------------------------------------------------------------------
@@ -716,6 +788,16 @@ def test_mutant_dropped_page_is_caught(monkeypatch):
     monkeypatch.setattr(oa, "_gather_positions", drop_first_page)
     assert _fails(test_gqa_worked_block_table_example, "reading_L")
     assert _fails(test_gqa_matches_dense_loop_brute_force)
+
+
+def test_mutant_fixed_page_size_is_caught(monkeypatch):
+    """A gather that assumes 16-token pages whatever the cache holds."""
+    orig = oa._gather_positions
+    monkeypatch.setattr(oa, "_gather_positions", lambda row, positions, page_size:
+                        orig(row, positions, 16))
+    assert _fails(test_gqa_verify_brute_force_at_page_size, 1)
+    assert _fails(test_gqa_verify_brute_force_at_page_size, 64)
+    assert _fails(test_mla_brute_force_at_page_size, 3)
 
 
 def test_mutant_sink_omitted_is_caught(monkeypatch):
