@@ -45,18 +45,22 @@ def _parse():
     p.add_argument("--config", default="gqa_sinks")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--splits", type=int, default=0, help="override the split cap")
+    p.add_argument("--page-size", type=int, default=0,
+                   help="GQA configs: store the same workload in pages of this many tokens "
+                        "(a power of two; the pool then holds exactly the pages in use)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="after timing, run one plain device copy of this many MiB (a "
                         "known-size reference for hardware byte counters)")
     return p.parse_args()
 
 
-def _gqa_case(name, torch, pd, splits):
+def _gqa_case(name, torch, pd, splits, page_size=0):
     from synth import gqa_workload
 
     fp8 = name.endswith("_fp8")
     base = name[:-4] if fp8 else name
-    w = gqa_workload(base)
+    w = gqa_workload(base, page_size=page_size, pool="tight") if page_size else gqa_workload(base)
+    pool = f"{w.num_pages}-page pool" if page_size else "40000-page pool"
     vals = w.values("cuda", poison=False, fp8=fp8)
     bt = torch.from_numpy(w.block_table).cuda()
     sl = torch.from_numpy(w.seq_lens).cuda()
@@ -76,12 +80,12 @@ def _gqa_case(name, torch, pd, splits):
 
         if fp8:
             desc = ("GQA decode with sinks on an FP8 E4M3FN cache (per-kv-head K and V "
-                    "scales): B=64, Hq=64, Hkv=8, D=128, page 16 HND, seq_lens U[1024,8192], "
-                    "40000-page pool")
+                    f"scales): B=64, Hq=64, Hkv=8, D=128, page {w.P} HND, seq_lens U[1024,8192], "
+                    f"{pool}")
         else:
             desc = (f"GQA causal verify with sinks: B={w.B}, qlen={w.qlen}, Hq={w.Hq}, "
                     f"Hkv={w.Hkv}, D={w.D}, page {w.P} HND bf16, seq_lens U[1024,8192], "
-                    "real length L - U{0,1}, 40000-page pool")
+                    f"real length L - U{{0,1}}, {pool}")
         # the kernel and its merge are timed together (no partials-only verify entry)
         return dict(w=w, vals=vals, S=S, step=verify_step, kernel=None, rest=None,
                     kv_bytes=w.kv_bytes() // (2 if fp8 else 1), flops=w.flops(), desc=desc,
@@ -100,11 +104,11 @@ def _gqa_case(name, torch, pd, splits):
             pd.merge_splits(ws, w.B, w.Hq, S, w.D, sinks=vals["sinks"], out=out, lse=lse)
 
     desc = {
-        "gqa_sinks": "GQA decode with sinks: B=64, Hq=64, Hkv=8, D=128, page 16 HND bf16, "
-                     "seq_lens U[1024,8192], 40000-page pool",
-        "gqa_window": "sliding-window GQA decode: B=64, Hq=64, Hkv=8, D=128, window 128, "
-                      "seq_lens U[4096,32768]",
-        "gqa_skewed": "skewed long-context GQA decode: B=256, Hq=32, Hkv=8, D=128, "
+        "gqa_sinks": f"GQA decode with sinks: B=64, Hq=64, Hkv=8, D=128, page {w.P} HND bf16, "
+                     f"seq_lens U[1024,8192], {pool}",
+        "gqa_window": f"sliding-window GQA decode: B=64, Hq=64, Hkv=8, D=128, page {w.P}, "
+                      "window 128, seq_lens U[4096,32768]",
+        "gqa_skewed": f"skewed long-context GQA decode: B=256, Hq=32, Hkv=8, D=128, page {w.P}, "
                       "seq_lens log-uniform [16,131072] with 4 empty",
         "tiny_gqa": "tiny GQA decode: B=3, seq_lens [30,32,70], page 32",
     }[name]
@@ -297,12 +301,18 @@ def main():
 
     torch.cuda.init()
     name = args.config
+    if args.page_size and (name in ("kv_append", "tiny_gqa") or name.startswith("mla")):
+        print("bench.py: --page-size applies to the GQA decode and verify configs only",
+              file=sys.stderr)
+        sys.exit(2)
     if name in ("mla_verify", "mla_verify_fp8"):
         case = _mla_case(name.endswith("fp8"), torch, pd, args.splits)
     elif name == "kv_append":
         case = _append_case(torch, pd)
     else:
-        case = _gqa_case(name, torch, pd, args.splits)
+        case = _gqa_case(name, torch, pd, args.splits, args.page_size)
+        if args.page_size:
+            name = f"{name}_p{args.page_size}"
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 

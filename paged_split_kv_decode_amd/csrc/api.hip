@@ -16,6 +16,10 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Page sizes with a kernel: every power of two up to 65536 tokens.
+constexpr int32_t kMaxPageSize = 1 << 16;
+bool pow2_page(int32_t p) { return p >= 1 && p <= kMaxPageSize && (p & (p - 1)) == 0; }
+
 }  // namespace
 
 extern "C" {
@@ -115,7 +119,8 @@ static int gqa_common(const void* q, int64_t q_stride_b, int64_t q_stride_h, con
     return PD_ERR_INVALID;
   const bool fp8 = kv_dtype == PD_KV_FP8_E4M3FN;
   const int32_t G = num_q_heads / num_kv_heads;
-  if (head_dim != 128 || (page_size != 16 && page_size != 32) || (int64_t)qlen * G > 16)
+  if (page_size < 1) return PD_ERR_INVALID;
+  if (head_dim != 128 || !pow2_page(page_size) || (int64_t)qlen * G > 16)
     return PD_ERR_UNSUPPORTED;
   if (batch == 0) return PD_OK;
   if (q == nullptr || kv == nullptr || block_table == nullptr || seq_lens == nullptr ||
@@ -177,6 +182,7 @@ static int gqa_common(const void* q, int64_t q_stride_b, int64_t q_stride_h, con
   a.Hkv = num_kv_heads;
   a.G = G;
   a.P = page_size;
+  a.p_shift = __builtin_ctz((unsigned)page_size);
   a.S = num_kv_splits;
   a.partials = partials_only ? 1 : 0;
   a.ws = workspace;
@@ -376,6 +382,7 @@ int paged_verify_mla(const void* q, int64_t q_stride_row, int64_t q_stride_h, co
   a.B = batch;
   a.H = num_heads;
   a.P = page_size;
+  a.p_shift = __builtin_ctz((unsigned)page_size);
   a.S = num_kv_splits;
   a.ws = workspace;
   a.out = static_cast<uint16_t*>(out);

@@ -121,6 +121,18 @@ __device__ __forceinline__ void global_to_lds_16_stream(const void* base, uint32
       : "s"(lds_base), "v"(voff), "s"(base), "i"(kOff)
       : "memory", "m0", "scc");
 }
+// Same, with a per-lane 64-bit source address (the instruction's vaddr
+// form): for rows of one load that come from different pages.
+template <uint32_t kOff>
+__device__ __forceinline__ void global_to_lds_16_stream_v(const void* src, uint32_t lds_base) {
+  asm volatile(
+      "s_add_u32 m0, %0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off nt"
+      :
+      : "s"(lds_base), "v"(src), "i"(kOff)
+      : "memory", "m0", "scc");
+}
 #pragma clang diagnostic pop
 
 __device__ __forceinline__ uint32_t lds_addr(PD_LDS const void* p) {

@@ -1,632 +1,22 @@
-// Paged GQA split-KV decode for gfx950 (one query token per request).
-//
-// Operation: "vllm.models.flint.ops.decode_attention", flint_decode_attention
-// and _FlintDecodeAttention.kernel (key range of a request, sliding-window
-// start, per-split partials, sink in the final denominator); block-table
-// addressing as in "Atención paginada", section "Ruta de decodificación".
-//
-// Design on CDNA4: a persistent, length-balanced stream
-// -----------------------------------------------------
-// * Work unit = (request b, kv head); its keys are cut into 32-token tiles
-//   (tile t covers positions [32t, 32t + 32), clipped to the request's key
-//   range).  All units' tiles, request-major then kv-head-major, form one
-//   flat sequence of U tiles.  The grid is one 4-wave workgroup per compute
-//   unit, and every wave takes an equal contiguous share of that sequence
-//   (tpw tiles), so the waves finish together whatever the length mix.
-// * A wave streams its share as one pipeline that runs straight across unit
-//   boundaries: it has a private 2-stage ring of 16 KB tiles in LDS and
-//   issues tile k+1 (16 `global_load_lds_dwordx4`, 1 KB each, HBM -> LDS
-//   with no VGPR staging, non-temporal: the cache is read once) while it
-//   computes tile k.  The physical page of
-//   each tile row comes from the block table through scalar loads made one
-//   tile ahead of their use, so their latency is hidden.  No workgroup
-//   barrier exists anywhere: the waves share nothing but the CU.
-// * Where a wave's share cuts a unit, each piece is a split: the wave writes
-//   its fp32 partial (O / l, lse) to the piece's slot, and the merge kernel
-//   combines them.  With the split cap S >= 2 the share size is raised
-//   until no unit spans more than S waves; the wave that holds a unit's
-//   first tile marks the unit's unused slots with lse = -inf.  With S == 1
-//   shares are rounded to whole units and the wave writes O and LSE
-//   directly.
-// * Scores S^T[token, head] = K . Q^T on v_mfma_f32_16x16x32_bf16 with the
-//   G query heads of the kv head in the N dimension (G <= 16, zero-padded).
-//   Online softmax in fp32 with exp2 and a running max in unscaled logits,
-//   reduced over the 4 lanes of a head with two lane exchanges.  P (bf16)
-//   is already in the B-operand layout of O^T[d, head] += V^T . P^T, and
-//   V^T is read from the LDS tile with ds_read_b64_tr_b16.
-// * Keys outside [lo, hi) get a -inf score and a zero V (select, never a
-//   multiply), so stale or NaN cache contents never reach the output.  A
-//   block-table entry outside [0, num_pages) is never dereferenced: its
-//   rows are loaded from a harmless address and the piece's result is NaN.
-#include <utility>
-
-#include "device_common.h"
-#include "kernels.h"
+// Paged GQA split-KV decode: launch dispatch over the page classes, and the
+// classes of 16-token pages and of pages of 32 tokens or more.  The kernel
+// itself is in gqa_decode_impl.h; the classes of smaller pages are
+// instantiated in gqa_decode_small_pages.hip.
+#include "gqa_decode_impl.h"
 
 namespace pd {
-namespace {
 
-constexpr int kD = 128;
-constexpr int kNW = 4;                                  // waves per workgroup
-constexpr int kRowBytes = 2 * kD * 2;                   // K|V row of one token (bf16)
-constexpr int kTileBytes = kTileTokens * kRowBytes;     // 16 KB
-constexpr int kRowBytes8 = 2 * kD;                      // K|V row of one token (FP8)
-constexpr int kTileBytes8 = kTileTokens * kRowBytes8;   // 8 KB
-// Ring of a wave: 2 tiles as loaded; an FP8 ring is followed by the bf16
-// tile it is dequantised into, so both rings take 32 KB.
-constexpr int kRingBytes = 2 * kTileBytes;
-// Smallest share a wave takes: below it the per-wave start-up dominates.
-constexpr int kMinWaveTiles = 4;
+// instantiated in gqa_decode_small_pages.hip
+extern template hipError_t launch_gqa_class<1>(const GqaArgs&, bool, int, hipStream_t);
+extern template hipError_t launch_gqa_class<2>(const GqaArgs&, bool, int, hipStream_t);
+extern template hipError_t launch_gqa_class<4>(const GqaArgs&, bool, int, hipStream_t);
+extern template hipError_t launch_gqa_class<8>(const GqaArgs&, bool, int, hipStream_t);
 
-// 16-byte chunk c of token row r is stored at chunk c ^ swz(r).  Rows
-// 0..7 get distinct low-3-bit patterns (K reads: 8 consecutive rows, same
-// chunk) and rows 4k..4k+3 distinct bits 2:1 (V transpose reads: 4 rows x a
-// 32-byte chunk pair).
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+template hipError_t launch_gqa_class<16>(const GqaArgs&, bool, int, hipStream_t);
+template hipError_t launch_gqa_class<32>(const GqaArgs&, bool, int, hipStream_t);
 
-__device__ __forceinline__ uint32_t keep_mask(bool lo_ok, bool hi_ok) {
-  return (lo_ok ? 0x0000FFFFu : 0u) | (hi_ok ? 0xFFFF0000u : 0u);
-}
-
-__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
-
-// Key range of one request: positions [lo, hi), tiles lo / 32 ... lo / 32 + nt - 1.
-struct Req {
-  int lo, hi, nt;
-};
-
-// Length bound standing for "no real length given".
-constexpr int kNoReal = 1 << 30;
-
-// Key range of verify row t of a request of length L (clamped to the
-// block-table row) and real length Lr: [lo_t, hi_t) with
-// hi_t = max(min(L - qlen + 1 + t, Lr), 0) and, with a window,
-// lo_t = max(hi_t - window, 0).
-template <int P>
-__device__ __forceinline__ int row_hi(const GqaArgs& a, int L, int Lr, int t) {
-  L = min(max(L, 0), a.max_blocks * P);
-  return max(min(L - a.qlen + 1 + t, Lr), 0);
-}
-__device__ __forceinline__ int row_lo(const GqaArgs& a, int hi) {
-  return a.window > 0 ? max(hi - a.window, 0) : 0;
-}
-
-// Keys of a request: the union of its rows' ranges, [lo_0, hi_{qlen-1}).
-template <int P>
-__device__ __forceinline__ Req range_of(const GqaArgs& a, int L, int Lr) {
-  Req r;
-  r.hi = row_hi<P>(a, L, Lr, a.qlen - 1);
-  r.lo = row_lo(a, row_hi<P>(a, L, Lr, 0));
-  r.nt = r.hi > r.lo ? ((r.hi + 31) >> 5) - (r.lo >> 5) : 0;
-  return r;
-}
-
-__device__ __forceinline__ int real_len(const GqaArgs& a, int b) {
-  return a.real_lens != nullptr ? (int)as_const(a.real_lens)[b] : kNoReal;
-}
-
-template <int P>
-__device__ __forceinline__ Req request_range(const GqaArgs& a, int b) {
-  return range_of<P>(a, as_const(a.seq_lens)[b], real_len(a, b));
-}
-
-// A position in one wave's tile sequence (wave-uniform).  b == B: the share
-// is done.
-struct Cursor {
-  int b, kvh;   // unit
-  int p0;       // flat index of the unit's first tile
-  int i, i_end; // current tile of the unit, end of this wave's piece of it
-  Req r;
-};
-
-// The wave's share of the flat tile sequence.
-struct Share {
-  int g0, g1;   // [g0, g1): raw share (the last used wave also owns every unit past g1)
-  int tpw;
-  bool last;
-  bool split;   // S >= 2: pieces may cut units; S == 1: whole units only
-};
-
-constexpr int kQSlotBytes = 16 * kD * 2;                 // query rows of one piece (G <= 16)
-constexpr int kWaveLds = kRingBytes + 2 * kQSlotBytes;    // ring + 2 query slots = 40 KB
-constexpr int kCachedChunks = 4;                          // request lengths kept in registers (x64)
-
-// V: verify rows (qlen > 1 or real lengths); the decode instantiation has a
-// single column range per unit and none of the per-column limit work.
-template <int P, bool V, bool F8>
-__global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
-  constexpr int kSlotBytes = F8 ? kTileBytes8 : kTileBytes;     // one tile as loaded
-  constexpr int kLoadsPerTile = kSlotBytes / (64 * 16);         // 16 (bf16) or 8 (FP8) loads
-  __shared__ __attribute__((aligned(1024))) char smem[kNW * kWaveLds];
-
-  const int tid = threadIdx.x;
-  const int wave_in_wg = uniform(tid >> 6);
-  const int lane = tid & 63;
-  const int g4 = lane >> 4;
-  const int l16 = lane & 15;
-  const int G = a.G;
-  const int R = V ? a.qlen * G : G;   // columns in use: (verify token, head) pairs
-  const int S = a.S;
-  const int Hkv = a.Hkv;
-  const bool direct = S == 1 && !a.partials;
-  float c = a.scale_log2;   // per piece: times the kv head's k_scale for FP8
-  float v_mult = 1.f;        // per piece: the kv head's v_scale for FP8
-  const int n_waves = gridDim.x * kNW;
-  const int w = uniform(blockIdx.x * kNW + wave_in_wg);
-  PD_LDS char* ring = (PD_LDS char*)smem + wave_in_wg * kWaveLds;
-  PD_LDS char* qslots = ring + kRingBytes;
-  // this lane's score column: verify token t_col, head g_col of the kv head
-  const int t_col = V ? min(l16, R - 1) / G : 0;
-  const int g_col = V ? min(l16, R - 1) - t_col * G : l16;
-
-  // ---- the plan: total tiles, longest request, this wave's share --------
-  // Lane l of chunk c holds the length of request 64c + l (0 past the batch).
-  int Lc[kCachedChunks], Lrc[kCachedChunks];
-#pragma unroll
-  for (int ch = 0; ch < kCachedChunks; ++ch) {
-    const int b = 64 * ch + lane;
-    Lc[ch] = b < a.B ? as_const(a.seq_lens)[b] : 0;
-    Lrc[ch] = b < a.B ? real_len(a, b) : 0;
-  }
-  int nt_sum = 0, nt_max = 0;
-#pragma unroll
-  for (int ch = 0; ch < kCachedChunks; ++ch) {
-    const int nt = range_of<P>(a, Lc[ch], Lrc[ch]).nt;
-    nt_sum += wave_sum(nt);
-    nt_max = max(nt_max, wave_max(nt));
-  }
-  for (int base = 64 * kCachedChunks; base < a.B; base += 64) {
-    const int nt = base + lane < a.B ? request_range<P>(a, base + lane).nt : 0;
-    nt_sum += wave_sum(nt);
-    nt_max = max(nt_max, wave_max(nt));
-  }
-  nt_sum = uniform(nt_sum);
-  nt_max = uniform(nt_max);
-  const int U = nt_sum * Hkv;
-  Share sh;
-  sh.split = S >= 2;
-  int tpw = max((U + n_waves - 1) / n_waves, kMinWaveTiles);
-  // a unit of n tiles cut every tpw tiles at an arbitrary offset spans at
-  // most floor((n - 1) / tpw) + 2 shares: keep that <= S
-  if (sh.split) tpw = max(tpw, (nt_max - 1) / (S - 1) + 1);
-  sh.tpw = tpw = uniform(tpw);
-  const int w_used = uniform(max((U + tpw - 1) / tpw, 1));
-  if (w >= w_used) return;
-  sh.g0 = w * tpw;
-  sh.last = w == w_used - 1;
-  sh.g1 = sh.last ? U : sh.g0 + tpw;
-
-  // ---- first unit of the share ------------------------------------------
-  // split: the unit holding tile g0, or an empty unit starting at or after
-  // g0; whole units: the first unit starting at or after g0.
-  int b_s = -1, L_s = 0, Lr_s = 0, cb_s = 0;
-  {
-    int C = 0;  // tiles of the requests before this chunk (one kv head)
-    auto probe = [&](int base, int L, int Lr) {
-      const bool in = base + lane < a.B;
-      const int nt = range_of<P>(a, L, Lr).nt;
-      const int incl = wave_incl_sum(nt);
-      const int cb1 = (C + incl) * Hkv;     // flat start of request b + 1
-      const int cb = cb1 - nt * Hkv;         // flat start of request b
-      const bool pred = in && (sh.split ? (cb1 > sh.g0 || cb >= sh.g0)
-                                        : (cb + (Hkv - 1) * nt >= sh.g0));
-      const uint64_t m = __ballot(pred);
-      if (m != 0) {
-        const int l0 = __builtin_ctzll(m);
-        b_s = base + l0;
-        L_s = __builtin_amdgcn_readlane(L, l0);
-        Lr_s = __builtin_amdgcn_readlane(Lr, l0);
-        cb_s = __builtin_amdgcn_readlane(cb, l0);
-        return true;
-      }
-      C += __builtin_amdgcn_readlane(incl, 63);
-      return false;
-    };
-    bool found = false;
-#pragma unroll
-    for (int ch = 0; ch < kCachedChunks; ++ch)
-      if (!found && 64 * ch < a.B) found = probe(64 * ch, Lc[ch], Lrc[ch]);
-    for (int base = 64 * kCachedChunks; !found && base < a.B; base += 64) {
-      const bool in = base + lane < a.B;
-      found = probe(base, in ? as_const(a.seq_lens)[base + lane] : 0, in ? real_len(a, base + lane) : 0);
-    }
-  }
-  if (b_s < 0) return;
-  b_s = uniform(b_s);
-  const Req r_s = range_of<P>(a, uniform(L_s), uniform(Lr_s));
-  int kvh_s = 0;
-  if (sh.g0 > cb_s)
-    kvh_s = sh.split ? (sh.g0 - cb_s) / r_s.nt : (sh.g0 - cb_s + r_s.nt - 1) / r_s.nt;
-  kvh_s = uniform(kvh_s);
-  const int p0_s = uniform(cb_s + kvh_s * r_s.nt);
-
-  // Step to the next unit (no range checks).
-  auto next_unit = [&](Cursor& cu) {
-    cu.p0 += cu.r.nt;
-    if (cu.kvh + 1 < Hkv) {
-      ++cu.kvh;
-    } else {
-      cu.kvh = 0;
-      ++cu.b;
-      if (cu.b < a.B) cu.r = request_range<P>(a, cu.b);
-    }
-  };
-  // Make the cursor point at a tile, skipping empty units; b = B once the
-  // share is done.
-  auto settle = [&](Cursor& cu) {
-    for (;;) {
-      if (cu.b >= a.B || (!sh.last && cu.p0 >= sh.g1)) {
-        cu.b = a.B;
-        return;
-      }
-      if (cu.r.nt > 0) {
-        cu.i = sh.split ? max(sh.g0 - cu.p0, 0) : 0;
-        cu.i_end = sh.split ? min(cu.r.nt, sh.g1 - cu.p0) : cu.r.nt;
-        return;
-      }
-      next_unit(cu);
-    }
-  };
-  // first tile of this wave's piece of the cursor's unit?
-  auto piece_start = [&](const Cursor& cu) { return cu.i == (sh.split ? max(sh.g0 - cu.p0, 0) : 0); };
-  auto advance = [&](Cursor& cu) {
-    if (++cu.i < cu.i_end) return;
-    next_unit(cu);
-    settle(cu);
-  };
-
-  Cursor cc;  // tile being computed
-  cc.b = b_s;
-  cc.kvh = kvh_s;
-  cc.p0 = p0_s;
-  cc.r = r_s;
-  settle(cc);
-  Cursor ci = cc;  // next tile to issue
-
-  // ---- block-table entries of one tile (scalar loads) -------------------
-  constexpr int PPT = P >= kTileTokens ? 1 : kTileTokens / P;   // pages per tile
-  // The entries are only checked when the tile is issued, so the scalar
-  // loads stay in flight for a whole iteration.
-  struct TilePages {
-    int id[PPT];
-    bool att[PPT];   // page attended
-  };
-  auto fetch_pages = [&](const Cursor& cu) {
-    TilePages tp;
-    const PD_CONST int32_t* bt_row = as_const(a.bt) + (int64_t)cu.b * a.bt_sb;
-    const int tok0 = ((cu.r.lo >> 5) + cu.i) * kTileTokens;
-    const int pg_lo = cu.r.lo / P, pg_hi = (cu.r.hi + P - 1) / P;
-#pragma unroll
-    for (int j = 0; j < PPT; ++j) {
-      const int pidx = tok0 / P + j;
-      tp.att[j] = pidx >= pg_lo && pidx < pg_hi;
-      tp.id[j] = tp.att[j] ? bt_row[pidx] : 0;
-    }
-    return tp;
-  };
-  TilePages pages_none;
-#pragma unroll
-  for (int j = 0; j < PPT; ++j) {
-    pages_none.id[j] = 0;
-    pages_none.att[j] = false;
-  }
-
-  // ---- HBM -> LDS loads of one tile (and of a new piece's query rows) ----
-  // A tile is always exactly kLoadsPerTile loads (rows of a page that is not
-  // read come from a harmless 16-byte source), so the vmcnt bookkeeping of
-  // the ring is exact.  Query rows go to one of two LDS slots before the
-  // tile's loads, so they have landed when the tile has.
-  int q_issued = 0, q_used = 0;   // pieces whose query rows were loaded / read
-  auto load_q = [&](const Cursor& cu) {
-    const uint32_t dst = uniform((int)lds_addr(qslots + (q_issued & 1) * kQSlotBytes));
-    const char* qbase =
-        (const char*)(a.q + (int64_t)cu.b * a.qlen * a.q_sb + (int64_t)cu.kvh * G * a.q_sh);
-    const int chunk = lane & 15;
-    for (int i = 0; i < (R + 3) / 4; ++i) {   // 4 columns (1 KB) per load
-      const int n = min(4 * i + (lane >> 4), R - 1);
-      const int t = n / G, g = n - t * G;
-      const uint32_t voff = (uint32_t)(t * a.q_sb + g * a.q_sh + chunk * 8) * 2u;
-      global_to_lds_16(qbase, voff, dst + i * 1024);
-    }
-    ++q_issued;
-  };
-  // Issues the tile's loads; returns whether an attended page has an
-  // out-of-range entry (its rows then come from the harmless source).
-  auto issue = [&](const Cursor& cu, const TilePages& tp, int slot) {
-    bool ok[PPT], bad_page = false;
-#pragma unroll
-    for (int j = 0; j < PPT; ++j) {
-      const bool inr = tp.id[j] >= 0 && tp.id[j] < a.num_pages;
-      ok[j] = tp.att[j] && inr;
-      bad_page |= tp.att[j] && !inr;
-    }
-    if (piece_start(cu)) load_q(cu);
-    const uint32_t dst = uniform((int)lds_addr(ring + slot * kSlotBytes));
-    constexpr int kElem = F8 ? 1 : 2;
-    const char* kv_head = (const char*)a.kv + (int64_t)cu.kvh * a.kv_sh * kElem;
-    const char* pbase[PPT];
-#pragma unroll
-    for (int j = 0; j < PPT; ++j)
-      pbase[j] = ok[j] ? kv_head + (int64_t)tp.id[j] * a.kv_sp * kElem : (const char*)a.q;
-    auto one = [&](auto ic) {
-      constexpr int i = decltype(ic)::value;
-      // bf16: 2 rows of 32 chunks per load, chunks XOR-swizzled per row;
-      // FP8: 4 rows of 16 chunks per load, plain
-      constexpr int kRowsPerLoad = F8 ? 4 : 2;
-      constexpr int j = P >= kTileTokens ? 0 : (kRowsPerLoad * i) / P;
-      // tiles start on a page boundary, so a row's slot in its page is r mod P
-      const int r = kRowsPerLoad * i + (F8 ? (lane >> 4) : (lane >> 5));
-      const uint32_t slot_tok = (uint32_t)(r & (P - 1));
-      const uint32_t ch = F8 ? (uint32_t)(lane & 15) : (uint32_t)((lane & 31) ^ swz(r));
-      const uint32_t voff = ok[j] ? slot_tok * (2 * kD * kElem) + ch * 16 : 0u;
-      global_to_lds_16_stream<i * 1024>(pbase[j], voff, dst);
-    };
-    [&]<int... I>(std::integer_sequence<int, I...>) {
-      (one(std::integral_constant<int, I>{}), ...);
-    }(std::make_integer_sequence<int, kLoadsPerTile>{});
-    return bad_page;
-  };
-
-  // ---- per-piece state ----------------------------------------------------
-  bf16x8 qf[4];
-  float m_run = neg_inf();
-  float l_run = 0.f;
-  f32x4 o[8];
-  bool piece_bad = false;
-  int bad_slots = 0;   // bit s: the tile in ring slot s read a bad page
-  // keys of this lane's column in the current piece's request, and the
-  // range every column attends (tiles inside it need no score mask)
-  int col_lo = 0, col_hi = 0, all_lo = 0, all_hi = 0;
-
-  auto finish_piece = [&](const Cursor& cu) {
-    const float l_tot_part = l_run + shfl_xor(l_run, 16);
-    const float l_tot = l_tot_part + shfl_xor(l_tot_part, 32);
-    const int hq = cu.kvh * G + g_col;
-    const int64_t row = (int64_t)cu.b * a.qlen + t_col;
-    if (l16 < R) {
-      const bool empty = !(l_tot > 0.f);
-      const float lse_nat = empty ? neg_inf() : (m_run * c + fast_log2(l_tot)) * kLn2;
-      const float nan = __builtin_nanf("");
-      if (direct) {
-        float den = l_tot;
-        if (a.sinks != nullptr && !empty) den += fast_exp2(a.sinks[hq] * kLog2e - m_run * c);
-        const float inv = empty ? 0.f : v_mult / den;
-        uint16_t* orow = a.out + row * a.o_sb + (int64_t)hq * a.o_sh + 4 * g4;
-#pragma unroll
-        for (int blk = 0; blk < 8; ++blk) {
-          f32x4 r = o[blk] * inv;
-          if (piece_bad) r = f32x4{nan, nan, nan, nan};
-          *(u32x2*)(orow + 16 * blk) = u32x2{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
-        }
-        if (a.lse != nullptr && g4 == 0)
-          a.lse[row * a.lse_sb + hq] = piece_bad ? nan : lse_nat;
-      } else {
-        const int s = sh.split ? w - cu.p0 / sh.tpw : 0;
-        float* slot = a.ws + ((row * a.Hq + hq) * S + s) * (kD + 1);
-        const float inv = empty ? 0.f : v_mult / l_tot;
-#pragma unroll
-        for (int blk = 0; blk < 8; ++blk) {
-          f32x4 r = o[blk] * inv;
-          if (piece_bad) r = f32x4{nan, nan, nan, nan};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) slot[16 * blk + 4 * g4 + e] = r[e];
-        }
-        if (g4 == 0) slot[kD] = piece_bad ? nan : lse_nat;
-      }
-    }
-  };
-
-  if (cc.b < a.B) {
-    // ---- prologue -----------------------------------------------------------
-    // The block-table entries of the next tile to issue are fetched one
-    // iteration ahead of their use.
-    TilePages pg_next = fetch_pages(ci);
-    bad_slots = issue(ci, pg_next, 0) ? 1 : 0;
-    advance(ci);
-    pg_next = ci.b < a.B ? fetch_pages(ci) : pages_none;
-
-    for (int k = 0; cc.b < a.B; ++k) {
-      const bool first = piece_start(cc);
-      if (first) {
-        m_run = neg_inf();
-        l_run = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-        piece_bad = false;
-        if constexpr (F8) {
-          const int si = cc.kvh * a.scale_stride;
-          c = a.scale_log2 * (a.k_scale != nullptr ? a.k_scale[si] : 1.f);
-          v_mult = a.v_scale != nullptr ? a.v_scale[si] : 1.f;
-        }
-        if constexpr (V) {
-          const int L = as_const(a.seq_lens)[cc.b], Lr = real_len(a, cc.b);
-          col_hi = row_hi<P>(a, L, Lr, t_col);
-          col_lo = row_lo(a, col_hi);
-          all_hi = uniform(row_hi<P>(a, L, Lr, 0));                 // first row's limit
-          all_lo = uniform(row_lo(a, row_hi<P>(a, L, Lr, a.qlen - 1)));   // last row's start
-        }
-      }
-
-      const bool issuing = ci.b < a.B;
-      if (issuing) {
-        wait_lgkmcnt0();  // LDS reads of the slot (tile k-1) and of an old query slot are done
-        const int slot = (k + 1) & 1;
-        const bool bad_tile = issue(ci, pg_next, slot);
-        bad_slots = (bad_slots & ~(1 << slot)) | (bad_tile ? 1 << slot : 0);
-        advance(ci);
-        pg_next = ci.b < a.B ? fetch_pages(ci) : pages_none;
-      }
-      if (issuing)
-        wait_vmcnt<kLoadsPerTile>();
-      else
-        wait_vmcnt<0>();
-
-      if (first) {
-        // the piece's query rows (loaded before its first tile): B operand
-        // of S^T = K Q^T, zero for padding heads
-        PD_LDS const char* qs = qslots + (q_used & 1) * kQSlotBytes + l16 * (kD * 2);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const bf16x8 v = *(PD_LDS const bf16x8*)(qs + (8 * g4 + 32 * s) * 2);
-          qf[s] = l16 < R ? v : bf16x8{};
-        }
-        ++q_used;
-      }
-
-      const int slot = k & 1;
-      piece_bad |= (bad_slots >> slot) & 1;
-      PD_LDS char* tl = ring + slot * kSlotBytes;
-      if constexpr (F8) {
-        // exact FP8 -> bf16 into the bf16 tile after the ring, in the bf16
-        // layout: item (row r, FP8 chunk cf of 16 codes) -> bf16 chunks 2 cf
-        // and 2 cf + 1 of row r, XOR-swizzled
-        PD_LDS char* st = ring + 2 * kTileBytes8;
-#pragma unroll
-        for (int it = 0; it < 8; ++it) {
-          const int r = 4 * it + (lane >> 4), cf = lane & 15;
-          const u32x4 w = *(PD_LDS const u32x4*)(tl + r * kRowBytes8 + cf * 16);
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            u32x4 cv;
-            cv[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * h], 1.f, false));
-            cv[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * h], 1.f, true));
-            cv[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * h + 1], 1.f, false));
-            cv[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * h + 1], 1.f, true));
-            *(PD_LDS u32x4*)(st + r * kRowBytes + (((2 * cf + h) ^ swz(r)) << 4)) = cv;
-          }
-        }
-        tl = st;
-      }
-      const int lo = cc.r.lo, hi = cc.r.hi;
-      const int tok0 = ((lo >> 5) + cc.i) * kTileTokens;
-
-      // ---- scores ----
-      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-      const int sw = swz(l16);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int ch = (g4 + 4 * s) ^ sw;
-        bf16x8 k0 = *(PD_LDS bf16x8*)(tl + l16 * kRowBytes + ch * 16);
-        bf16x8 k1 = *(PD_LDS bf16x8*)(tl + (16 + l16) * kRowBytes + ch * 16);
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[s], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[s], s1, 0, 0, 0);
-      }
-
-      // V rows outside the request's keys are zeroed; scores outside the
-      // lane's column range are -inf (the two differ only for verify rows)
-      const bool edge = tok0 < lo || tok0 + kTileTokens > hi;
-      bool v0[4], v1[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t0 = tok0 + 4 * g4 + i, t1 = t0 + 16;
-        v0[i] = !edge || (t0 >= lo && t0 < hi);
-        v1[i] = !edge || (t1 >= lo && t1 < hi);
-        if constexpr (V) {
-          const bool col_edge = tok0 < all_lo || tok0 + kTileTokens > all_hi;
-          if (col_edge && !(t0 >= col_lo && t0 < col_hi)) s0[i] = neg_inf();
-          if (col_edge && !(t1 >= col_lo && t1 < col_hi)) s1[i] = neg_inf();
-        } else {
-          if (!v0[i]) s0[i] = neg_inf();
-          if (!v1[i]) s1[i] = neg_inf();
-        }
-      }
-
-      // ---- online softmax (fp32, exp2, running max in unscaled logits) ----
-      float mx = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
-                       fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
-      mx = fmaxf(mx, shfl_xor(mx, 16));
-      mx = fmaxf(mx, shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_ref = m_new == neg_inf() ? 0.f : m_new;
-      const float mc = m_ref * c;
-      const float alpha = fast_exp2(m_run * c - mc);
-      float p0[4], p1[4];
-      float psum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p0[i] = fast_exp2(s0[i] * c - mc);
-        p1[i] = fast_exp2(s1[i] * c - mc);
-        psum += p0[i] + p1[i];
-      }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) o[i] *= alpha;
-
-      // P^T as the B operand: k = 8*g4 + j <-> tokens 4*g4 + j (j < 4) and
-      // 16 + 4*g4 + (j - 4) (j >= 4), exactly this lane's scores.
-      const u32x4 pw = {pack_bf16x2(p0[0], p0[1]), pack_bf16x2(p0[2], p0[3]),
-                        pack_bf16x2(p1[0], p1[1]), pack_bf16x2(p1[2], p1[3])};
-      const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
-      const u32x4 vkeep = {keep_mask(v0[0], v0[1]), keep_mask(v0[2], v0[3]),
-                           keep_mask(v1[0], v1[1]), keep_mask(v1[2], v1[3])};
-
-      // ---- O^T += V^T P^T ----
-      const int ra = 4 * g4 + (l16 >> 2);
-      const int rb = ra + 16;
-      const int swa = swz(ra);
-#pragma unroll
-      for (int blk = 0; blk < 8; ++blk) {
-        const int ch = 16 + 2 * blk + ((l16 & 3) >> 1);
-        const int within = (l16 & 1) * 8;
-        bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (PD_LDS bf16x4*)(tl + ra * kRowBytes + ((ch ^ swa) << 4) + within));
-        bf16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (PD_LDS bf16x4*)(tl + rb * kRowBytes + ((ch ^ swa) << 4) + within));
-        u32x2 ua = __builtin_bit_cast(u32x2, va);
-        u32x2 ub = __builtin_bit_cast(u32x2, vb);
-        u32x4 vv = {ua[0], ua[1], ub[0], ub[1]};
-        if (edge) vv &= vkeep;
-        o[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pf, o[blk], 0, 0, 0);
-      }
-
-      if (cc.i + 1 == cc.i_end) finish_piece(cc);
-      advance(cc);
-    }
-  }
-
-  // ---- units this wave answers for without streaming them ---------------
-  // Empty units owned by this share get O = 0 / LSE = -inf (or lse = -inf in
-  // every split slot); a unit whose first tile is in this share gets
-  // lse = -inf in the split slots no piece of it uses.
-  Cursor cw;
-  cw.b = b_s;
-  cw.kvh = kvh_s;
-  cw.p0 = p0_s;
-  cw.r = r_s;
-  while (cw.b < a.B && (sh.last || cw.p0 < sh.g1)) {
-    const int hq0 = cw.kvh * G;
-    // (row, query head) of column n of this unit
-    auto col_row = [&](int n) { return (int64_t)cw.b * a.qlen + n / G; };
-    auto col_head = [&](int n) { return hq0 + n % G; };
-    if (cw.r.nt == 0) {
-      if (direct) {
-        for (int i = lane; i < R * (kD / 8); i += 64) {
-          const int n = i / (kD / 8), d8 = (i % (kD / 8)) * 8;
-          *(u32x4*)(a.out + col_row(n) * a.o_sb + (int64_t)col_head(n) * a.o_sh + d8) = u32x4{0, 0, 0, 0};
-        }
-        if (a.lse != nullptr && lane < R) a.lse[col_row(lane) * a.lse_sb + col_head(lane)] = neg_inf();
-      } else {
-        for (int i = lane; i < R * S; i += 64) {
-          const int n = i / S, s = i % S;
-          a.ws[((col_row(n) * a.Hq + col_head(n)) * S + s) * (kD + 1) + kD] = neg_inf();
-        }
-      }
-    } else if (sh.split && cw.p0 >= sh.g0) {
-      const int nseg = (cw.p0 + cw.r.nt - 1) / sh.tpw - cw.p0 / sh.tpw + 1;
-      for (int i = lane; i < R * (S - nseg); i += 64) {
-        const int n = i / (S - nseg), s = nseg + i % (S - nseg);
-        a.ws[((col_row(n) * a.Hq + col_head(n)) * S + s) * (kD + 1) + kD] = neg_inf();
-      }
-    }
-    next_unit(cw);
-  }
-}
-
-}  // namespace
-
-// Workgroups per launch: one per compute unit (the ring takes 128 KB of
-// LDS, so one workgroup fits a CU).  Queried once per device.
+// Workgroups per launch: one per compute unit (a workgroup takes 160 KB of
+// LDS, so one fits a CU).  Queried once per device.
 static int grid_size() {
   static int cached[64] = {0};
   int dev = 0;
@@ -642,21 +32,16 @@ static int grid_size() {
 hipError_t launch_gqa_decode(const GqaArgs& a, hipStream_t stream) {
   const int n = grid_size();
   if (n <= 0) return hipErrorInvalidDevice;
-  dim3 grid(n), block(kNW * 64);
   const bool verify = a.qlen > 1 || a.real_lens != nullptr;
-#define PD_GQA_CASE(PP, VV, FF)                                                                 \
-  case PP * 4 + (VV ? 2 : 0) + (FF ? 1 : 0):                                                    \
-    hipLaunchKernelGGL((gqa_decode_kernel<PP, VV, FF>), grid, block, 0, stream, a);             \
-    break;
-  switch (a.P * 4 + (verify ? 2 : 0) + (a.kv_fp8 ? 1 : 0)) {
-    PD_GQA_CASE(16, false, false) PD_GQA_CASE(16, false, true)
-    PD_GQA_CASE(16, true, false) PD_GQA_CASE(16, true, true)
-    PD_GQA_CASE(32, false, false) PD_GQA_CASE(32, false, true)
-    PD_GQA_CASE(32, true, false) PD_GQA_CASE(32, true, true)
-    default: return hipErrorInvalidValue;
+  if (a.P <= 0 || (a.P & (a.P - 1)) != 0 || (1 << a.p_shift) != a.P) return hipErrorInvalidValue;
+  switch (a.P) {
+    case 1: return launch_gqa_class<1>(a, verify, n, stream);
+    case 2: return launch_gqa_class<2>(a, verify, n, stream);
+    case 4: return launch_gqa_class<4>(a, verify, n, stream);
+    case 8: return launch_gqa_class<8>(a, verify, n, stream);
+    case 16: return launch_gqa_class<16>(a, verify, n, stream);
+    default: return launch_gqa_class<32>(a, verify, n, stream);
   }
-#undef PD_GQA_CASE
-  return hipGetLastError();
 }
 
 }  // namespace pd

@@ -37,6 +37,7 @@ struct GqaArgs {
   int32_t window;
   float scale_log2;  // sm_scale * log2(e)
   int32_t B, Hq, Hkv, G, P;
+  int32_t p_shift;   // log2(P): the page size is a power of two
   int32_t S;         // split cap: no (request, kv head) is cut into more pieces
   int32_t partials;  // 1: always write workspace partials (never O / LSE)
   float* ws;         // [B * qlen, Hq, S, D + 1] when S > 1 or partials
@@ -72,6 +73,7 @@ struct MlaArgs {
   int32_t qlen;
   float scale_log2;
   int32_t B, H, P;
+  int32_t p_shift;   // log2(P): the page size is a power of two
   int32_t S;
   float* ws;
   uint16_t* out;
@@ -98,6 +100,10 @@ struct AppendArgs {
 };
 
 hipError_t launch_gqa_decode(const GqaArgs& a, hipStream_t stream);
+// One GQA page class (1, 2, 4, 8, 16, or 32 for every page of 32 tokens or
+// more); each class is instantiated in its own translation unit.
+template <int PS>
+hipError_t launch_gqa_class(const GqaArgs& a, bool verify, int n_wg, hipStream_t stream);
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_mla_verify(const MlaArgs& a, hipStream_t stream);

@@ -125,7 +125,9 @@ def test_gqa_argument_checks_happen_before_any_hip_call():
     assert _gqa(scale=0.0) == PD_ERR_INVALID                  # softmax scale must be > 0
     assert _gqa(scale=-0.088) == PD_ERR_INVALID
     assert _gqa(D=64) == PD_ERR_UNSUPPORTED
-    assert _gqa(P=8) == PD_ERR_UNSUPPORTED
+    assert _gqa(P=12) == PD_ERR_UNSUPPORTED                    # not a power of two
+    assert _gqa(P=1 << 17) == PD_ERR_UNSUPPORTED
+    assert _gqa(P=0) == PD_ERR_INVALID
     assert _gqa(Hq=136, Hkv=8) == PD_ERR_UNSUPPORTED          # G = 17
     assert _gqa(q=FAKE + 8) == PD_ERR_ALIGN
     assert _gqa(kvsp=8 * 16 * 256 + 4) == PD_ERR_ALIGN

@@ -1,0 +1,123 @@
+"""GPU parity of the GQA paths at general page sizes against the fp64 oracle.
+
+"vllm.v1.attention.ops.triton_decode_attention" states support for any page
+size of at least one token; the library takes every power of two.  Pages
+smaller than a 32-token tile put several pages in one tile (1, 2, 4, 8 and
+16 tokens: one block-table entry per page, and for 1 and 2 tokens a page per
+lane within one load); pages of 32 tokens or more hold whole tiles at an
+offset inside the page.  Covered: decode with sinks, verify with windows and
+real lengths, the FP8 cache, split counts, and bitwise equality of the
+outputs for one logical cache stored at different page sizes (the kernel's
+arithmetic does not depend on where a key lives).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from helpers import O_ATOL_FP8, check_attention, oracle_gqa
+from synth import gqa_workload
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X")]
+
+PAGE_SIZES = [1, 2, 4, 8, 64, 256]
+
+
+@pytest.fixture(scope="module")
+def pd():
+    import paged_split_kv_decode_amd as m
+    return m
+
+
+def _run(pd, w, vals, S, kv=None, bt=None, fp8=False):
+    real = None if w.real_seq_lens is None else torch.from_numpy(w.real_seq_lens).cuda()
+    scales = dict(k_scale=vals["k_scale"], v_scale=vals["v_scale"]) if fp8 else {}
+    out, lse = pd.paged_verify_gqa(vals["q"], vals["kv"] if kv is None else kv,
+                                   torch.from_numpy(w.block_table if bt is None else bt).cuda(),
+                                   torch.from_numpy(w.seq_lens).cuda(), w.qlen, w.sm_scale,
+                                   sinks=vals["sinks"], window=w.window, real_seq_lens=real,
+                                   num_kv_splits=S, **scales)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def _cap(pd, w):
+    return pd.gqa_split_cap(w.B, w.Hkv, int(w.seq_lens.max()), w.window)
+
+
+@pytest.mark.parametrize("P", PAGE_SIZES)
+@pytest.mark.parametrize("S", ["cap", 1, 3])
+def test_decode_with_sinks(pd, P, S):
+    w = gqa_workload("gqa_sinks", batch=6, len_range=(1, 700), page_size=P, pool="tight",
+                     seed_offset=P)
+    vals = w.values("cuda", poison=True)
+    S = _cap(pd, w) if S == "cap" else S
+    out, lse = _run(pd, w, vals, S)
+    O, L = oracle_gqa(w, vals)
+    check_attention(out, lse, O, L, what=f"decode P={P} S={S}")
+
+
+@pytest.mark.parametrize("P", PAGE_SIZES)
+@pytest.mark.parametrize("window", [0, 37])
+def test_verify_with_window(pd, P, window):
+    w = gqa_workload("gqa_verify", batch=5, len_range=(1, 600), qlen=4, heads=(32, 8),
+                     real_drop=(0, 2), window=window, page_size=P, pool="tight",
+                     seed_offset=P + window)
+    vals = w.values("cuda", poison=True)
+    for S in (1, 4):
+        out, lse = _run(pd, w, vals, S)
+        O, L = oracle_gqa(w, vals)
+        check_attention(out, lse, O, L, what=f"verify P={P} window={window} S={S}")
+
+
+@pytest.mark.parametrize("P", PAGE_SIZES)
+def test_fp8_cache(pd, P):
+    w = gqa_workload("gqa_sinks", batch=6, len_range=(1, 700), qlen=2, real_drop=(0, 1),
+                     page_size=P, pool="tight", seed_offset=3 * P)
+    vals = w.values("cuda", poison=True, fp8=True)
+    for S in (1, 3):
+        out, lse = _run(pd, w, vals, S, fp8=True)
+        O, L = oracle_gqa(w, vals)
+        check_attention(out, lse, O, L, o_atol=O_ATOL_FP8, what=f"fp8 P={P} S={S}")
+
+
+def _relayout(w, kv, P2, rng):
+    """The workload's cache stored with page size P2 in a shuffled pool, with
+    every never-attended slot copied from the source (NaN poison included)."""
+    P = w.P
+    src = kv.cpu()
+    Hkv, row = src.shape[1], src.shape[3]
+    cap = [-(-int(L) // P2) for L in w.seq_lens]
+    n_pages = sum(cap) + 2
+    perm = rng.permutation(n_pages)
+    bt = np.full((w.B, max(cap + [1]) + 1), -1, np.int32)
+    dst = torch.full((n_pages, Hkv, P2, row), float("nan"), dtype=src.dtype)
+    off = 0
+    for b, L in enumerate(w.seq_lens):
+        L = int(L)
+        bt[b, :cap[b]] = perm[off:off + cap[b]]
+        off += cap[b]
+        if L == 0:
+            continue
+        pos = np.arange(L)
+        rows = src[torch.from_numpy(w.block_table[b, pos // P]).long(), :,
+                   torch.from_numpy(pos % P).long()]                       # [L, Hkv, row]
+        dst[torch.from_numpy(bt[b, pos // P2]).long(), :, torch.from_numpy(pos % P2).long()] = rows
+    return dst.cuda(), bt
+
+
+@pytest.mark.parametrize("qlen,window", [(1, 0), (3, 50)])
+def test_outputs_bitwise_equal_across_page_sizes(pd, qlen, window):
+    w = gqa_workload("gqa_verify", batch=6, len_range=(1, 500), qlen=qlen, heads=(32, 8),
+                     real_drop=(0, 2) if qlen > 1 else None, window=window, page_size=16,
+                     pool="tight", seed_offset=7 + qlen)
+    vals = w.values("cuda", poison=True)
+    rng = np.random.default_rng(11)
+    for S in (1, 3):
+        ref_o, ref_l = _run(pd, w, vals, S)
+        for P2 in (1, 2, 8, 64):
+            kv2, bt2 = _relayout(w, vals["kv"], P2, rng)
+            o, l = _run(pd, w, vals, S, kv=kv2, bt=bt2)
+            assert torch.equal(o.view(torch.int16), ref_o.view(torch.int16)), (P2, S)
+            assert torch.equal(l.view(torch.int32), ref_l.view(torch.int32)), (P2, S)
