@@ -288,27 +288,61 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
   // ---- block-table entries of one tile (scalar loads) -------------------
   constexpr bool kBig = PS >= kTileTokens;
   constexpr int PPT = kBig ? 1 : kTileTokens / PS;   // pages per tile
+  // Pages of 1, 2 or 4 tokens (8 or more per tile): each lane computes its
+  // own row's source address and checks in vector registers; larger pages
+  // keep a per-page scalar address and check.
+  constexpr bool kLaneAddr = !kBig && PS <= 4;
   const int p_shift = kBig ? a.p_shift : __builtin_ctz(PS);
   auto tile_tok0 = [&](const Cursor& cu) { return ((cu.r.lo >> 5) + cu.i) * kTileTokens; };
   // The entries are only checked when the tile is issued, so the scalar
-  // loads stay in flight for a whole iteration.  Entries past the unit's
-  // last attended page are not read (the index is clamped to it), so every
-  // read stays inside the request's block-table row.
+  // loads stay in flight for a whole iteration.  Only entries of attended
+  // pages are read (lane-address classes: clamped to the last attended
+  // page), so every read stays inside the request's block-table row.
   struct TilePages {
     int id[PPT];
+    bool att[kLaneAddr ? 1 : PPT];   // page attended (scalar classes)
   };
   auto fetch_pages = [&](const Cursor& cu) {
     TilePages tp;
     const PD_CONST int32_t* bt_row = as_const(a.bt) + (int64_t)cu.b * a.bt_sb;
     const int pidx0 = tile_tok0(cu) >> p_shift;
-    const int last = (cu.r.hi - 1) >> p_shift;
+    if constexpr (kLaneAddr) {
+      if (PPT == 32 && pidx0 + PPT <= a.max_blocks) {
+        // the tile's window of entries lies inside the row: consecutive
+        // loads, merged into a few wide scalar loads (entries of pages
+        // that are not attended are read but never used)
+        typedef int32_t i32x8 __attribute__((ext_vector_type(8), aligned(4)));
+        const PD_CONST i32x8* w = (const PD_CONST i32x8*)(bt_row + pidx0);
 #pragma unroll
-    for (int j = 0; j < PPT; ++j) tp.id[j] = bt_row[min(pidx0 + j, last)];
+        for (int q = 0; q < (PPT + 7) / 8; ++q) {
+          if constexpr (PPT == 32) {
+            const i32x8 v = w[q];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) tp.id[8 * q + e] = v[e];
+          }
+        }
+      } else {
+        const int last = (cu.r.hi - 1) >> p_shift;
+#pragma unroll
+        for (int j = 0; j < PPT; ++j) tp.id[j] = bt_row[min(pidx0 + j, last)];
+      }
+    } else {
+      const int pg_lo = cu.r.lo >> p_shift, pg_end = ((cu.r.hi - 1) >> p_shift) + 1;
+#pragma unroll
+      for (int j = 0; j < PPT; ++j) {
+        tp.att[j] = pidx0 + j >= pg_lo && pidx0 + j < pg_end;
+        tp.id[j] = tp.att[j] ? bt_row[pidx0 + j] : 0;
+      }
+    }
     return tp;
   };
   TilePages pages_none;
 #pragma unroll
   for (int j = 0; j < PPT; ++j) pages_none.id[j] = 0;
+  if constexpr (!kLaneAddr) {
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) pages_none.att[j] = false;
+  }
 
   // ---- HBM -> LDS loads of one tile (and of a new piece's query rows) ----
   // A tile is always exactly kLoadsPerTile loads (rows of a page that is not
@@ -332,62 +366,87 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
   // Issues the tile's loads; returns whether an attended page has an
   // out-of-range entry (its rows then come from the harmless source).
   auto issue = [&](const Cursor& cu, const TilePages& tp, int slot) {
-    const int tok0 = tile_tok0(cu);
-    const int pidx0 = tok0 >> p_shift;
-    const int pg_lo = cu.r.lo >> p_shift, pg_end = ((cu.r.hi - 1) >> p_shift) + 1;
-    bool ok[PPT], bad_page = false;
-#pragma unroll
-    for (int j = 0; j < PPT; ++j) {
-      const bool att = pidx0 + j >= pg_lo && pidx0 + j < pg_end;   // page attended
-      const bool inr = tp.id[j] >= 0 && tp.id[j] < a.num_pages;
-      ok[j] = att && inr;
-      bad_page |= att && !inr;
-    }
     if (piece_start(cu)) load_q(cu);
     const uint32_t dst = uniform((int)lds_addr(ring + slot * kSlotBytes));
     constexpr int kElem = F8 ? 1 : 2;
+    constexpr uint32_t kRowB = 2 * kD * kElem;
+    // Every kernel argument the loads need is read here, before the first
+    // load: each load is an asm statement with a memory clobber, after which
+    // the compiler would read the arguments again.
     const char* kv_head = (const char*)a.kv + (int64_t)cu.kvh * a.kv_sh * kElem;
-    auto page_base = [&](int j) {
-      return ok[j] ? kv_head + (int64_t)tp.id[j] * a.kv_sp * kElem : (const char*)a.q;
-    };
+    const int64_t sp_bytes = (int64_t)a.kv_sp * kElem;
+    const uint32_t num_pages = (uint32_t)a.num_pages;
+    const char* const harmless = (const char*)a.q;
+    const int tok0 = tile_tok0(cu);
     // bf16: 2 rows of 32 chunks per load, chunks XOR-swizzled per row;
     // FP8: 4 rows of 16 chunks per load, plain
     constexpr int kRowsPerLoad = F8 ? 4 : 2;
     const int sub = F8 ? (lane >> 4) : (lane >> 5);   // this lane's row within a load
-    // token slot of the tile's first row in its page (a big page holds the
-    // whole tile; smaller pages start on tile boundaries)
-    const uint32_t slot0 = kBig ? (uint32_t)(tok0 & ((1 << p_shift) - 1)) : 0u;
-    auto one = [&](auto ic) {
-      constexpr int i = decltype(ic)::value;
-      const int r = kRowsPerLoad * i + sub;
-      const uint32_t ch = F8 ? (uint32_t)(lane & 15) : (uint32_t)((lane & 31) ^ swz(r));
-      if constexpr (kBig || PS >= kRowsPerLoad) {
-        // every row of the load is in one page
-        constexpr int j = kBig ? 0 : (kRowsPerLoad * i) / PS;
-        const uint32_t slot_tok = kBig ? slot0 + (uint32_t)r : (uint32_t)(r & (PS - 1));
-        const uint32_t voff = ok[j] ? slot_tok * (2 * kD * kElem) + ch * 16 : 0u;
-        global_to_lds_16_stream<i * 1024>(page_base(j), voff, dst);
-      } else {
-        // pages smaller than a load: the lane's own row picks its page among
-        // the load's kRowsPerLoad / PS pages
-        constexpr int kCand = kRowsPerLoad / PS;
-        constexpr int j0 = kCand * i;
-        const int cand = sub / PS;
-        const char* pb = page_base(j0);
-        bool okl = ok[j0];
+    auto chunk_of = [&](int r) {
+      return F8 ? (uint32_t)(lane & 15) : (uint32_t)((lane & 31) ^ swz(r));
+    };
+    bool bad_page = false;
+    if constexpr (kLaneAddr) {
+      // bit j: page j of the tile is attended
+      const int pidx0 = tok0 >> p_shift;
+      const int j_lo = min(max((cu.r.lo >> p_shift) - pidx0, 0), PPT);
+      const int j_hi = min(max(((cu.r.hi - 1) >> p_shift) + 1 - pidx0, 0), PPT);
+      const uint64_t att_mask = ((1ull << j_hi) - 1) & ~((1ull << j_lo) - 1);
+      bool bad_lane = false;
+      auto one = [&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        const int r = kRowsPerLoad * i + sub;
+        // the lane's row is in page j = r / PS of the tile: one of the
+        // load's kCand pages
+        constexpr int kCand = PS >= kRowsPerLoad ? 1 : kRowsPerLoad / PS;
+        constexpr int j0 = (kRowsPerLoad * i) / PS;
+        // The candidates are read as wave-uniform values first: a select
+        // between array elements would otherwise be folded into one load at
+        // a per-lane index, which puts the array in scratch memory.
+        const int cand = kCand > 1 ? sub / PS : 0;
+        int id = kCand > 1 ? uniform(tp.id[j0]) : tp.id[j0];
 #pragma unroll
         for (int c = 1; c < kCand; ++c) {
-          pb = cand == c ? page_base(j0 + c) : pb;
-          okl = cand == c ? ok[j0 + c] : okl;
+          const int idc = uniform(tp.id[j0 + c]);
+          id = cand == c ? idc : id;
         }
-        const uint32_t slot_tok = (uint32_t)(sub & (PS - 1));
-        const char* src = okl ? pb + (slot_tok * (2 * kD * kElem) + ch * 16) : (const char*)a.q;
+        const int j = j0 + cand;
+        const bool att = (att_mask >> j) & 1;
+        const bool inr = (uint32_t)id < num_pages;
+        bad_lane |= att && !inr;
+        const uint32_t off = (uint32_t)(r & (PS - 1)) * kRowB + chunk_of(r) * 16;
+        const char* src = att && inr ? kv_head + id * sp_bytes + off : harmless;
         global_to_lds_16_stream_v<i * 1024>(src, dst);
+      };
+      [&]<int... I>(std::integer_sequence<int, I...>) {
+        (one(std::integral_constant<int, I>{}), ...);
+      }(std::make_integer_sequence<int, kLoadsPerTile>{});
+      bad_page = __ballot(bad_lane) != 0;
+    } else {
+      bool ok[PPT];
+      const char* pbase[PPT];
+#pragma unroll
+      for (int j = 0; j < PPT; ++j) {
+        const bool inr = (uint32_t)tp.id[j] < num_pages;
+        ok[j] = tp.att[j] && inr;
+        bad_page |= tp.att[j] && !inr;
+        pbase[j] = ok[j] ? kv_head + tp.id[j] * sp_bytes : harmless;
       }
-    };
-    [&]<int... I>(std::integer_sequence<int, I...>) {
-      (one(std::integral_constant<int, I>{}), ...);
-    }(std::make_integer_sequence<int, kLoadsPerTile>{});
+      // token slot of the tile's first row in its page (a big page holds the
+      // whole tile; smaller pages start on tile boundaries)
+      const uint32_t slot0 = kBig ? (uint32_t)(tok0 & ((1 << p_shift) - 1)) : 0u;
+      auto one = [&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        const int r = kRowsPerLoad * i + sub;
+        constexpr int j = kBig ? 0 : (kRowsPerLoad * i) / PS;   // every row of the load is in page j
+        const uint32_t slot_tok = kBig ? slot0 + (uint32_t)r : (uint32_t)(r & (PS - 1));
+        const uint32_t voff = ok[j] ? slot_tok * kRowB + chunk_of(r) * 16 : 0u;
+        global_to_lds_16_stream<i * 1024>(pbase[j], voff, dst);
+      };
+      [&]<int... I>(std::integer_sequence<int, I...>) {
+        (one(std::integral_constant<int, I>{}), ...);
+      }(std::make_integer_sequence<int, kLoadsPerTile>{});
+    }
     return bad_page;
   };
 
