@@ -221,15 +221,19 @@ void mla_verify_kernel(MlaArgs a) {
     const float c = a.scale_log2 * kscale;   // log2-domain scale of raw scores
 
     // ---- Q fragment: B operand of S^T = K Q^T (32 rows x 576 dims) --------
+    // A row past the request's rows reads the request's first row instead:
+    // its scores are all masked (hi_row = 0) and its output is never
+    // written.  With no select on the loaded values, the 36 loads go
+    // straight into the fragment registers and are in flight together; one
+    // wait follows, before any tile load is issued (left to the compiler,
+    // the wait would sit at the fragment's first use inside the tile loop
+    // and drain the tile ring on every iteration).
     bf16x8 qf[kKSteps];
     {
       const uint16_t* qp = a.q + ((int64_t)b * a.qlen + t_row) * a.q_srow + (int64_t)h_row * a.q_sh + 8 * g2;
   #pragma unroll
-      for (int kk = 0; kk < kKSteps; ++kk) {
-        u32x4 v = *(const u32x4*)(qp + 16 * kk);
-        if (!row_ok) v = u32x4{0, 0, 0, 0};
-        qf[kk] = __builtin_bit_cast(bf16x8, v);
-      }
+      for (int kk = 0; kk < kKSteps; ++kk) qf[kk] = *(const bf16x8*)(qp + 16 * kk);
+      wait_vmcnt<0>();
     }
 
     const char* kv = (const char*)a.kv;
