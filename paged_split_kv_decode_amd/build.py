@@ -42,6 +42,7 @@ def sources() -> list[str]:
 # and the LDS operands.
 PER_SOURCE_FLAGS = {
     "mla_verify.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=0"],
+    "mla_verify_small_pages.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=0"],
 }
 
 

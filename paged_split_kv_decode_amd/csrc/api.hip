@@ -331,7 +331,8 @@ int paged_verify_mla(const void* q, int64_t q_stride_row, int64_t q_stride_h, co
       max_blocks < 0 || !std::isfinite(sm_scale) || !(sm_scale > 0.f))
     return PD_ERR_INVALID;
   if (kv_dtype != PD_KV_BF16 && kv_dtype != PD_KV_FP8_E4M3FN) return PD_ERR_INVALID;
-  if (head_dim_k != 576 || head_dim_v != 512 || page_size != 16 ||
+  if (page_size < 1) return PD_ERR_INVALID;
+  if (head_dim_k != 576 || head_dim_v != 512 || !pow2_page(page_size) ||
       ((int64_t)qlen * num_heads) % 32 != 0)
     return PD_ERR_UNSUPPORTED;
   if (batch == 0) return PD_OK;

@@ -123,6 +123,16 @@ __device__ __forceinline__ void global_to_lds_16_stream(const void* base, uint32
 }
 // Same, with a per-lane 64-bit source address (the instruction's vaddr
 // form): for rows of one load that come from different pages.
+__device__ __forceinline__ void global_to_lds_16_v(const void* src, uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off"
+      :
+      : "s"(lds_addr), "v"(src)
+      : "memory", "m0");
+}
+// The non-temporal variant of the vaddr form.
 template <uint32_t kOff>
 __device__ __forceinline__ void global_to_lds_16_stream_v(const void* src, uint32_t lds_base) {
   asm volatile(

@@ -107,5 +107,9 @@ hipError_t launch_gqa_class(const GqaArgs& a, bool verify, int n_wg, hipStream_t
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_mla_verify(const MlaArgs& a, hipStream_t stream);
+// One MLA page class (1, 2, 4, 8, or 16 for every page of 16 tokens or
+// more); the classes are instantiated in their own translation units.
+template <int PC>
+hipError_t launch_mla_class(const MlaArgs& a, int n_wg, hipStream_t stream);
 
 }  // namespace pd

@@ -1,670 +1,19 @@
-// Causal MLA verify for gfx950: qlen query tokens per request, all heads,
-// over one shared latent cache with V = K[..., :Lv].
-//
-// Operation: "vllm.v1.attention.ops.triton_decode_attention",
-// decode_attention_fwd_verify (row limit max(min(L - qlen + 1 + t, L_real), 0),
-// V read from K, natural-log LSE, [rows, H, S, Lv + 1] fp32 partials, scalar
-// k_scale for an FP8 cache); the split rule (a request's own length cut into
-// max(ceil(L / S), min) chunks) is the one its verify_num_kv_splits describes.
-//
-// Design on CDNA4
-// ---------------
-// * The qlen * H (token, head) pairs of a request are the "rows", cut into
-//   row blocks of 128.  A workgroup of 4 waves (one per SIMD, 512 registers
-//   each) runs one row block over a range of the request's keys.  The grid
-//   is persistent (one workgroup per CU); workgroups form groups that take
-//   the row blocks of the same requests over the same key range at the same
-//   time, on one XCD, so each latent tile is fetched from HBM once per group
-//   and served from L2 to the others.  Every group gets the same number of
-//   tiles whatever the length mix; a cut request writes one fp32 partial
-//   per piece.
-// * Latent tiles of 32 tokens (2 pages, 36 KB bf16 / 18 KB fp8) stream from
-//   HBM into a 4-slot LDS ring with global_load_lds_dwordx4, each bf16
-//   instruction filling 1 KB from 8 whole 128-byte lines.  A tile's loads
-//   are spread over the MFMA steps of the tile before (issued at once they
-//   fill the request queue and stall the wave).  The FP8 cache is
-//   dequantised exactly (v_cvt_scalef32_pk_bf16_fp8, scale 1) into a bf16
-//   staging tile; k_scale is folded into the softmax scale and the output.
-// * Scores: each wave owns 32 rows; S^T[token, row] = K . Q^T with
-//   v_mfma_f32_32x32x16_bf16, its query fragment (32 x 576 bf16, 144 VGPRs)
-//   held for the whole piece, K fragments read from LDS a few steps ahead.
-// * Product: each wave owns 128 of the 512 output dims for all 128 rows, so
-//   every V^T fragment (ds_read_b64_tr_b16 from the same tile) feeds four
-//   MFMAs.  The probabilities go through LDS: a wave's packed P of a key
-//   step is, lane by lane, the B operand every wave needs for its rows.  The
-//   output accumulator (128 dims x 128 rows fp32) takes all 256 AGPRs but
-//   one block, which is parked in VGPRs while the scores use its AGPRs.
-// * Iteration k runs the score MFMAs of tile k interleaved with the product
-//   of tile k-1, so the dependent score chain always has independent MFMAs
-//   between its steps; one barrier per tile.
-// * Online softmax in the exp2 domain (x = score * sm_scale * log2 e) with a
-//   fixed per-row reference: a row's reference max is its first non-empty
-//   tile's max and is never rescaled, so no vector instruction ever touches
-//   the accumulator (which is what keeps it in AGPRs).  The exact row max is
-//   tracked alongside; if a later score exceeds the reference by more than
-//   2^64 (overflow risk) the workgroup runs the piece a second time with the
-//   exact max as reference.  Real attention scores never trigger it.
-// * With one split, whole requests are written directly as bf16 O and LSE;
-//   with several, every piece writes its fp32 partial (slots no piece uses
-//   are marked empty) and the merge pass combines them.
-#include "device_common.h"
-#include "kernels.h"
+// Causal MLA verify: launch dispatch over the page classes, and the class of
+// pages of 16 tokens or more.  The kernel is in mla_verify_impl.h; the
+// classes of smaller pages are instantiated in mla_verify_small_pages.hip.
+#include "mla_verify_impl.h"
 
 namespace pd {
-namespace {
 
-constexpr int kLk = 576;
-constexpr int kLv = 512;
-constexpr int kWaves = 4;                                          // one per SIMD
-constexpr int kRowsPerWave = 32;
-constexpr int kRowsPerBlock = kWaves * kRowsPerWave;              // 128
-constexpr int kRowBytes = kLk * 2;                                 // bf16 latent row
-constexpr int kTileBytes = kTileTokens * kRowBytes;                // 36 KB
-constexpr int kPageRegion = 16 * kRowBytes;                        // 18 KB (bf16)
-constexpr int kRowBytes8 = kLk;                                    // fp8 latent row
-constexpr int kTileBytes8 = kTileTokens * kRowBytes8;              // 18 KB
-constexpr int kPageRegion8 = 16 * kRowBytes8;                      // 9 KB (fp8)
-constexpr int kKSteps = kLk / 16;                                  // 36
-constexpr int kKAhead = 3;                                         // K fragments in flight
-constexpr int kDimBlocksPerWave = kLv / 32 / kWaves;              // 4 output blocks of 32 dims
-constexpr int kPBufBytes = kWaves * 2 * 1024;                      // P^T of one tile: 4 row groups x 2 key steps
-// p = 2^(x - m_ref) stays below 2^64 while the row max has not grown more
-// than this above the reference (fp32 / bf16 hold 2^127; with up to 2^20
-// keys and |V| < 2^40 the accumulator cannot overflow).
-constexpr float kRefHeadroomLog2 = 64.f;
+// instantiated in mla_verify_small_pages.hip
+extern template hipError_t launch_mla_class<1>(const MlaArgs&, int, hipStream_t);
+extern template hipError_t launch_mla_class<2>(const MlaArgs&, int, hipStream_t);
+extern template hipError_t launch_mla_class<4>(const MlaArgs&, int, hipStream_t);
+extern template hipError_t launch_mla_class<8>(const MlaArgs&, int, hipStream_t);
 
-// LDS layout of a bf16 tile.  A 32-token tile is two 16-row page regions
-// of 18 blocks of 1 KB.  Block 2 C + R holds 16-byte chunks 8 C .. 8 C + 7
-// (one 128-byte line of the latent row) of rows 8 R .. 8 R + 7, chunk c of
-// row r at 16-byte slot 8 (r % 8) + ((c % 8) ^ (r % 8) ^ R).  So
-//  * one global_load_lds instruction (64 lanes x 16 bytes) fills one block
-//    from 8 whole 128-byte lines; the XOR only permutes lanes inside a line;
-//  * a K-operand read (rows 0..15 of a page, one chunk) and a transpose
-//    read of V (4 rows x 2 chunks) touch distinct 16-byte slots modulo the
-//    256 bytes of the 64 banks: both bank-conflict free.
-__device__ __forceinline__ int tile_off(int c, int r16) {
-  return ((c >> 3) * 2 + (r16 >> 3)) * 1024 + (8 * (r16 & 7) + ((c & 7) ^ (r16 & 7) ^ (r16 >> 3))) * 16;
-}
-// The fp8 ring (before dequantisation) keeps chunk-column-major pages: fp8
-// chunk c8 (16 bytes) of row r16 at slot 16 c8 + r16.
+template hipError_t launch_mla_class<16>(const MlaArgs&, int, hipStream_t);
 
-
-template <int NS, bool FP8>
-__global__ __launch_bounds__(kWaves * 64, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void mla_verify_kernel(MlaArgs a) {
-  constexpr int kRingTile = FP8 ? kTileBytes8 : kTileBytes;
-  constexpr int kLoadsPerTile = kRingTile / 1024;                  // 36 or 18
-  constexpr int kLoadsPerPage = kLoadsPerTile / 2;
-  // bf16: 4 waves x 9 loads; fp8: waves 0 and 1 load one page (9 loads) each,
-  // so every issuing wave has the same count for its vmcnt bookkeeping.
-  constexpr int kIssueWaves = FP8 ? 2 : 4;
-  static_assert(NS == 4, "ring of 4 tiles: k-1 (product), k (scores), k+1, k+2 (loading)");
-  constexpr int kStageOff = NS * kRingTile;                         // 2 fp8 -> bf16 tiles
-  constexpr int kLoadsPerWave = kLoadsPerTile / kIssueWaves;
-  static_assert(kLoadsPerWave * kIssueWaves == kLoadsPerTile, "even load split");
-  constexpr int kLoadSpacing = kKSteps / kLoadsPerWave;             // score steps between a wave's loads
-  static_assert(kLoadSpacing >= 1 && (kLoadsPerWave - 1) * kLoadSpacing < kKSteps, "loads fit the score steps");
-  constexpr int kPOff = kStageOff + (FP8 ? 2 * kTileBytes : 0);     // P^T of tiles k-1 and k
-  constexpr int kLdsBytes = kPOff + 2 * kPBufBytes;
-  static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
-  __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
-  PD_LDS char* lds = (PD_LDS char*)smem;
-
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  const int l32 = lane & 31;
-  const int g2 = lane >> 5;
-  const int S = a.S;
-  const bool direct = S == 1;
-
-  // ---- the plan ----------------------------------------------------------
-  // The rows of a request form n_rb row blocks of 128 (token, head) rows;
-  // every row block of a request reads the same latent tiles.  Workgroups
-  // are grouped gs = min(n_rb, grid) at a time; the members of a group take
-  // the row blocks m, m + gs, ... of the same requests over the same tile
-  // range at the same time, so a tile fetched from HBM by one member is an
-  // L2 hit for the others.  Logical workgroup ids are XCD-remapped (hardware
-  // hands consecutive ids to the 8 XCDs round-robin) so a group shares one
-  // XCD and its L2.  Request b counts nt_b tiles, those of its last row block
-  // (the largest row limit); all requests' tiles in order form one flat
-  // sequence of U tiles and group g takes the equal contiguous share
-  // [g T, g T + T): every group streams the same number of tiles whatever
-  // the length mix.  Where a share cuts a request, each piece is a split with
-  // its own partial slot; T is raised until no request spans more than S
-  // shares.  With S == 1 shares are rounded to whole requests and results
-  // are written directly.
-  const int n_wg = gridDim.x;
-  int sid = blockIdx.x;
-  const int per_xcd = n_wg / 8;
-  if (sid < per_xcd * 8) sid = (sid % 8) * per_xcd + sid / 8;
-  sid = __builtin_amdgcn_readfirstlane(sid);
-  const int rows_req = a.qlen * a.H;
-  const int n_rb = (rows_req + kRowsPerBlock - 1) / kRowsPerBlock;
-  const int gs = min(n_rb, n_wg);
-  const int n_groups = n_wg / gs;
-  const int grp = sid / gs, member = sid % gs;
-  if (grp >= n_groups) return;   // the whole workgroup: no barrier was passed
-  auto unit_len = [&](int b) { return min(max((int)as_const(a.seq_lens)[b], 0), a.max_blocks * a.P); };
-  auto unit_real = [&](int b, int L) { return a.real_lens != nullptr ? (int)as_const(a.real_lens)[b] : L; };
-  // largest row limit of row block rb of a request with lengths (L, Lr)
-  auto block_hi = [&](int L, int Lr, int rb) {
-    const int last_row = min(rb * kRowsPerBlock + kRowsPerBlock, rows_req) - 1;
-    return max(min(L - a.qlen + 1 + last_row / a.H, Lr), 0);
-  };
-  auto block_tiles = [&](int L, int Lr, int rb) { return (block_hi(L, Lr, rb) + kTileTokens - 1) / kTileTokens; };
-  auto req_tiles = [&](int b) {
-    const int L = unit_len(b);
-    return block_tiles(L, unit_real(b, L), n_rb - 1);
-  };
-
-  int nt_sum = 0, nt_max = 0;
-  for (int base = 0; base < a.B; base += 64) {
-    const int t = base + lane < a.B ? req_tiles(base + lane) : 0;
-    nt_sum += wave_sum(t);
-    nt_max = max(nt_max, wave_max(t));
-  }
-  const int U = __builtin_amdgcn_readfirstlane(nt_sum);
-  nt_max = __builtin_amdgcn_readfirstlane(nt_max);
-  const bool split_mode = S >= 2;
-  int T = max((U + n_groups - 1) / n_groups, kMlaMinSplitTiles);
-  // a request of n tiles cut every T tiles at an arbitrary offset spans at
-  // most floor((n - 1) / T) + 2 shares: keep that <= S
-  if (split_mode) T = max(T, (nt_max - 1) / (S - 1) + 1);
-  T = __builtin_amdgcn_readfirstlane(T);
-  const int g_used = __builtin_amdgcn_readfirstlane(max((U + T - 1) / T, 1));
-  if (grp >= g_used) return;
-  const int g0 = grp * T;
-  const bool last = grp == g_used - 1;
-  const int g1 = last ? U : g0 + T;
-
-  // first request holding tile g0, or starting at or after it
-  int b_s = -1, cb_s = 0;
-  {
-    int C = 0;
-    for (int base = 0; base < a.B; base += 64) {
-      const bool in = base + lane < a.B;
-      const int req = in ? req_tiles(base + lane) : 0;
-      const int incl = wave_incl_sum(req);
-      const int cb1 = C + incl, cb = cb1 - req;
-      const uint64_t m = __ballot(in && (cb1 > g0 || cb >= g0));
-      if (m != 0) {
-        const int l0 = __builtin_ctzll(m);
-        b_s = base + l0;
-        cb_s = __builtin_amdgcn_readlane(cb, l0);
-        break;
-      }
-      C += __builtin_amdgcn_readlane(incl, 63);
-    }
-  }
-  if (b_s < 0) return;
-  b_s = __builtin_amdgcn_readfirstlane(b_s);
-  cb_s = __builtin_amdgcn_readfirstlane(cb_s);
-
-  // ---- one piece: tiles [tb, tb + n) of unit (b, rb), split slot `split` --
-  auto run_piece = [&](const int b, const int rb, const int tb, const int n, const int split) {
-    // ---- score rows of this lane (the wave's own 32 rows) and their limits --
-    const int L = unit_len(b);
-    const int Lr = unit_real(b, L);
-    const int my_row = rb * kRowsPerBlock + wave * kRowsPerWave + l32;
-    const bool row_ok = my_row < rows_req;
-    const int t_row = row_ok ? my_row / a.H : 0;
-    const int h_row = row_ok ? my_row % a.H : 0;
-    const int hi_row = row_ok ? max(min(L - a.qlen + 1 + t_row, Lr), 0) : 0;
-    const int hi_blk = __builtin_amdgcn_readfirstlane(block_hi(L, Lr, rb));
-    const int pg_hi = __builtin_amdgcn_readfirstlane((hi_blk + a.P - 1) / a.P);
-
-    float kscale = 1.f;
-    if constexpr (FP8) {
-      if (a.k_scale != nullptr) kscale = a.k_scale[0];
-    }
-    const float c = a.scale_log2 * kscale;   // log2-domain scale of raw scores
-
-    // ---- Q fragment: B operand of S^T = K Q^T (32 rows x 576 dims) --------
-    // A row past the request's rows reads the request's first row instead:
-    // its scores are all masked (hi_row = 0) and its output is never
-    // written.  With no select on the loaded values, the 36 loads go
-    // straight into the fragment registers and are in flight together; one
-    // wait follows, before any tile load is issued (left to the compiler,
-    // the wait would sit at the fragment's first use inside the tile loop
-    // and drain the tile ring on every iteration).
-    bf16x8 qf[kKSteps];
-    {
-      const uint16_t* qp = a.q + ((int64_t)b * a.qlen + t_row) * a.q_srow + (int64_t)h_row * a.q_sh + 8 * g2;
-  #pragma unroll
-      for (int kk = 0; kk < kKSteps; ++kk) qf[kk] = *(const bf16x8*)(qp + 16 * kk);
-      wait_vmcnt<0>();
-    }
-
-    const char* kv = (const char*)a.kv;
-    const int elem = FP8 ? 1 : 2;
-    const int64_t sp_bytes = a.kv_sp * elem;
-    const int64_t st_bytes = a.kv_st * elem;
-    const PD_CONST int32_t* bt_row = as_const(a.bt) + (int64_t)b * a.bt_sb;
-    bool bad = false;
-
-    // ---- block-table entries of a tile (scalar loads, one iteration ahead) --
-    // The entries are only checked when the tile is issued, so the scalar
-    // loads stay in flight for a whole iteration.
-    struct TilePages {
-      int id[2];
-      bool att[2];   // page attended
-    };
-    auto fetch = [&](int T) {
-      TilePages tp;
-  #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int pidx = 2 * T + j;
-        tp.att[j] = pidx < pg_hi;
-        tp.id[j] = tp.att[j] ? bt_row[pidx] : 0;
-      }
-      return tp;
-    };
-
-    // Issue this wave's share of the HBM->LDS loads of a tile into a ring
-    // slot: issuing wave w loads page w / (waves per page), instructions
-    // (w % waves per page) * kLoadsPerWave + j of that page.  An issuing wave
-    // always issues exactly kLoadsPerWave loads (a page that is not read comes
-    // from a harmless 16-byte source), so its vmcnt bookkeeping is exact.
-    constexpr int kWavesPerPage = kIssueWaves / 2;
-    const int my_page = wave / kWavesPerPage;
-    const int i0 = (wave % kWavesPerPage) * kLoadsPerWave;   // first instruction of this wave
-    // fp8: instruction i of a page reads 64 bytes of each of its 16 rows;
-    // bf16: wave w reads rows 8 (w % 2) .. + 7 of its page, one 128-byte line
-    // of each per instruction (lanes permuted inside the line, see tile_off)
-    const uint32_t lane_off =
-        FP8 ? (uint32_t)((lane & 15) * st_bytes) + 16u * (uint32_t)(lane >> 4)
-            : (uint32_t)((8 * (wave & 1) + (lane >> 3)) * st_bytes) + 16u * (uint32_t)((lane & 7) ^ (lane >> 3) ^ (wave & 1));
-    constexpr int kGStep = FP8 ? 64 : 128;     // global bytes per instruction (into every row)
-    constexpr int kLStep = FP8 ? 1024 : 2048;  // LDS bytes per instruction
-    const int g_first = FP8 ? 64 * i0 : 0;
-    const int l_first = FP8 ? i0 * 1024 : (wave & 1) * 1024;
-    // A tile's loads for this wave, validated: load j reads base + gstep j
-    // into LDS address dst + j kLStep (gstep = 0 for a page that is not read).
-    struct TileLoads {
-      const char* base;
-      uint32_t voff;
-      uint32_t dst;
-      int gstep;
-    };
-    auto prepare = [&](const TilePages& tp, int slot) {
-      bool pok[2];
-  #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const bool inr = tp.id[j] >= 0 && tp.id[j] < a.num_pages;
-        // every wave checks both pages, so the flag is workgroup-uniform
-        bad |= tp.att[j] && !inr;
-        pok[j] = tp.att[j] && inr;
-      }
-      const bool ok = (my_page & 1) ? pok[1] : pok[0];
-      const int my_pid = (my_page & 1) ? tp.id[1] : tp.id[0];
-      TileLoads tl;
-      tl.base = ok ? kv + (int64_t)my_pid * sp_bytes + g_first : (const char*)a.q;
-      tl.voff = ok ? lane_off : 0u;
-      tl.dst = lds_addr(lds + slot * kRingTile + my_page * (FP8 ? kPageRegion8 : kPageRegion) + l_first);
-      tl.gstep = ok ? kGStep : 0;
-      return tl;
-    };
-    auto load_one = [&](const TileLoads& tl, int j) {
-      global_to_lds_16(tl.base + tl.gstep * j, tl.voff, tl.dst + j * kLStep);
-    };
-    auto issue = [&](const TilePages& tp, int slot) {
-      const TileLoads tl = prepare(tp, slot);
-      if (wave < kIssueWaves) {
-  #pragma unroll
-        for (int j = 0; j < kLoadsPerWave; ++j) load_one(tl, j);
-      }
-    };
-
-    float m_seen = neg_inf();   // exact running max of this lane's score row
-    float m_ref = neg_inf();    // fixed reference of the current pass
-    float l_run = 0.f;
-    // Output accumulator: O^T for the wave's 128 output dims (4 blocks d of
-    // 32) x the block's 128 rows (4 groups r of 32), block (d, r) = o[4 d + r].
-    // Blocks 0..14 stay in AGPRs; block (3, 3) is parked in VGPRs between
-    // tiles, which leaves 16 AGPRs for the score accumulator.
-    f32x16 o[15];
-    f32x16 o_last;
-
-    // lane-constant parts of the transpose-read addresses
-    const int q16 = lane >> 4;
-    const int L16 = lane & 15;
-    const int vrow = 4 * (q16 >> 1) + (L16 >> 2);          // + 16 s (+ 8): rows 0..15 of a page
-    const int vcol0 = 16 * (q16 & 1) + 4 * (L16 & 3);      // + 32 blk
-    // read a covers row vrow (row octet 0), read b row vrow + 8 (octet 1); chunk
-    // 4 blk + vcc0 of dim block blk = 4 wave + d sits in line 2 wave + d / 2 at
-    // slot 8 vrow + ((4 (d % 2) + vcc0) ^ vrow ^ octet)
-    const int vcc0 = vcol0 >> 3;                           // chunk column within the block
-    const int vya = vcc0 ^ vrow, vyb = vcc0 ^ vrow ^ 1;
-    const uint32_t vlane_off = (uint32_t)(wave * 4096 + 128 * vrow + (vcol0 & 7) * 2);
-
-    // the bf16 view of tile t: its ring slot, or its fp8 staging buffer
-    auto tile_bf16 = [&](int t) -> PD_LDS char* {
-      if constexpr (FP8)
-        return lds + kStageOff + (t & 1) * kTileBytes;
-      else
-        return lds + (t & (NS - 1)) * kRingTile;
-    };
-    // P^T fragment (row group r, key step s) of tile t: 64 lanes x 16 bytes
-    PD_LDS char* pbuf = lds + kPOff + lane * 16;
-    auto p_slot = [&](int t, int r, int s) { return pbuf + (t & 1) * kPBufBytes + (2 * r + s) * 1024; };
-
-    for (int pass = 0; pass < 2; ++pass) {
-    // pass 1 only runs if pass 0 saw a score too far above its reference
-    m_ref = pass == 0 ? neg_inf() : m_seen;
-    l_run = 0.f;
-    bool overflow = false;
-  #pragma unroll
-    for (int i = 0; i < 15; ++i)
-  #pragma unroll
-      for (int e = 0; e < 16; ++e) o[i][e] = 0.f;
-  #pragma unroll
-    for (int e = 0; e < 16; ++e) o_last[e] = 0.f;
-
-    // Iteration k computes the scores of tile k interleaved with the P.V
-    // product of tile k-1 (whose probabilities every wave published in
-    // iteration k-1), so the dependent score chain always has independent
-    // MFMAs between its steps.  Iteration 0 multiplies the zeroed view of
-    // "tile -1" by zeroed probabilities; iteration n computes throw-away
-    // scores on stale data to finish tile n-1's product.  Ring: tile t in
-    // slot t mod 4; tile k+2 is issued at iteration k into the slot of tile
-    // k-2.
-    {
-      PD_LDS char* z = tile_bf16(-1);
-      for (int i = tid; i < kTileBytes / 16; i += kWaves * 64) *(PD_LDS u32x4*)(z + i * 16) = u32x4{0, 0, 0, 0};
-      PD_LDS char* zp = lds + kPOff + ((-1) & 1) * kPBufBytes;
-      for (int i = tid; i < kPBufBytes / 16; i += kWaves * 64) *(PD_LDS u32x4*)(zp + i * 16) = u32x4{0, 0, 0, 0};
-    }
-    TilePages pg_next;
-    if (n > 0) issue(fetch(tb), 0);
-    if (n > 1) issue(fetch(tb + 1), 1);
-    if (n > 2) pg_next = fetch(tb + 2);
-
-    for (int k = 0; k <= n; ++k) {
-      const bool live = k < n;   // iteration n only finishes tile n-1
-      if (k + 1 < n)
-        wait_vmcnt<kLoadsPerWave>();
-      else
-        wait_vmcnt<0>();
-      // tile k is in LDS, so are the probabilities of tile k-1; every wave is
-      // done with iteration k-1
-      __syncthreads();
-      const int tok0 = (tb + k) * kTileTokens;
-      if constexpr (FP8) {
-        if (live) {
-          // exact fp8 -> bf16 into the staging buffer: item = (page, fp8
-          // chunk column c8, row r16) -> bf16 chunk columns 2 c8 and 2 c8 + 1
-          PD_LDS char* src = lds + (k & (NS - 1)) * kRingTile;
-          PD_LDS char* dst = tile_bf16(k);
-          for (int i = tid; i < 2 * 36 * 16; i += kWaves * 64) {
-            const int r16 = i & 15;
-            const int c8 = (i >> 4) % 36;
-            const int pg = i / (36 * 16);
-            const u32x4 w = *(PD_LDS u32x4*)(src + pg * kPageRegion8 + (16 * c8 + r16) * 16);
-            PD_LDS char* dpg = dst + pg * kPageRegion;
-  #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              u32x4 cv;
-              cv[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * h], 1.f, false));
-              cv[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * h], 1.f, true));
-              cv[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * h + 1], 1.f, false));
-              cv[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * h + 1], 1.f, true));
-              *(PD_LDS u32x4*)(dpg + tile_off(2 * c8 + h, r16)) = cv;
-            }
-          }
-          __syncthreads();
-        }
-      }
-      PD_LDS char* tk = tile_bf16(k);       // scores of tile k
-      PD_LDS char* tv = tile_bf16(k - 1);   // product of tile k-1
-      if (live && tok0 + kTileTokens > hi_blk) {
-        // The block's last tile: token rows at or past its largest row limit
-        // (stale or never-loaded page slots) become zeros, so no score or V
-        // row there can carry a NaN into the products; a barrier orders the
-        // zeros before every read of the tile.
-        const int r0 = max(hi_blk - tok0, 0);
-        for (int i = tid; i < 2 * 72 * 16; i += kWaves * 64) {
-          const int r16 = i & 15, cc = (i >> 4) % 72, pg = i / (72 * 16);
-          if (16 * pg + r16 >= r0) *(PD_LDS u32x4*)(tk + pg * kPageRegion + tile_off(cc, r16)) = u32x4{0, 0, 0, 0};
-        }
-        __syncthreads();
-      }
-      // Tile k+2 goes into the slot of tile k-2, which every wave finished in
-      // iteration k-1.  Its loads are spread over the score steps below: issued
-      // all at once they fill the memory request queue and stall the wave.
-      const bool load_next = k + 2 < n && wave < kIssueWaves;
-      TileLoads tl_next;
-      if (k + 2 < n) {
-        tl_next = prepare(pg_next, (k + 2) & (NS - 1));
-        if (k + 3 < n) pg_next = fetch(tb + k + 3);
-      }
-
-      // ---- S^T(k) = K Q^T (36 MFMAs, one chain) with O^T += V^T P^T of tile
-      // k-1 (30 MFMAs: every block but (3, 3)) in between ------------------
-      // Fragments are read a few MFMA pairs ahead of their use; scheduling
-      // barriers pin that order (left alone, the scheduler moves every read
-      // next to its MFMA and the wave stalls on LDS latency at each step).
-      f32x16 sacc;
-  #pragma unroll
-      for (int e = 0; e < 16; ++e) sacc[e] = 0.f;
-      // chunk 2 kk + g2 of row kr = l32 % 16: line kk / 4, slot
-      // 8 (kr % 8) + ((2 (kk % 4)) ^ kz) with the lane constant kz
-      const int kr = l32 & 15, kz = g2 ^ (kr & 7) ^ (kr >> 3);
-      PD_LDS char* kp = tk + (l32 >> 4) * kPageRegion + (kr >> 3) * 1024 + 128 * (kr & 7);
-      auto kread = [&](int kk) { return *(PD_LDS bf16x8*)(kp + (kk >> 2) * 2048 + 16 * ((2 * (kk & 3)) ^ kz)); };
-      // V^T fragment of key step s (one 16-token page) and this wave's dim
-      // block d: read a rows vrow.., read b rows vrow + 8.. (slot + 8)
-      PD_LDS char* vbase = tv + vlane_off;
-      auto vread = [&](int s, int d) {
-        PD_LDS char* pl = vbase + s * kPageRegion + (d >> 1) * 2048;
-        PD_LDS char* pa = pl + 16 * ((4 * (d & 1)) ^ vya);
-        PD_LDS char* pb = pl + 1024 + 16 * ((4 * (d & 1)) ^ vyb);
-        const bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((PD_LDS bf16x4*)pa);
-        const bf16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((PD_LDS bf16x4*)pb);
-        const u32x2 ua = __builtin_bit_cast(u32x2, va);
-        const u32x2 ub = __builtin_bit_cast(u32x2, vb);
-        return __builtin_bit_cast(bf16x8, u32x4{ua[0], ua[1], ub[0], ub[1]});
-      };
-      auto pread = [&](int r, int s) { return *(PD_LDS bf16x8*)p_slot(k - 1, r, s); };
-      // product step j (0..29): s = j / 15, block index 4 d + r = j % 15.  V^T
-      // fragment v = 4 s + d lives in vf[v & 1]; P^T fragment (r, s) in pf[r].
-      {
-        bf16x8 kf[kKAhead], vf[2], pf[4];
-  #pragma unroll
-        for (int i = 0; i < kKAhead; ++i) kf[i] = kread(i);
-        vf[0] = vread(0, 0);
-        vf[1] = vread(0, 1);
-  #pragma unroll
-        for (int r = 0; r < 4; ++r) pf[r] = pread(r, 0);
-  #pragma unroll
-        for (int kk = 0; kk < kKSteps; ++kk) {
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk % kKAhead], qf[kk], sacc, 0, 0, 0);
-          if (kk < 30) {
-            const int s = kk / 15, idx = kk % 15, d = idx >> 2, r = idx & 3, v = 4 * s + d;
-            o[idx] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[v & 1], pf[r], o[idx], 0, 0, 0);
-            // V^T fragment v is done after its last row group: fetch v + 2
-            const bool v_done = r == 3 || idx == 14;
-            if (v_done && v + 2 < 8) vf[v & 1] = vread((v + 2) >> 2, (v + 2) & 3);
-            // P^T (r, 0) is done after block d = 3 (d = 2 for r = 3): fetch (r, 1)
-            if (s == 0 && (d == 3 || (d == 2 && r == 3))) pf[r] = pread(r, 1);
-          }
-          if (kk + kKAhead < kKSteps) kf[kk % kKAhead] = kread(kk + kKAhead);
-          if (kk % kLoadSpacing == 0 && kk / kLoadSpacing < kLoadsPerWave && load_next)
-            load_one(tl_next, kk / kLoadSpacing);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        float x[16];
-  #pragma unroll
-        for (int e = 0; e < 16; ++e) x[e] = sacc[e] * c;
-        {
-          // block (3, 3) of tile k-1's product, after the score accumulator is
-          // free: V^T fragment 3 and P^T (3, 0) are read again, fragment 7 and
-          // P^T (3, 1) are still in registers
-          const bf16x8 va = vread(0, 3), pa = pread(3, 0);
-          f32x16 ob = o_last;
-          ob = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pa, ob, 0, 0, 0);
-          ob = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[1], pf[3], ob, 0, 0, 0);
-          o_last = ob;
-          asm volatile("" : "+v"(o_last));
-        }
-        if (!live) break;
-
-        // causal limit of this lane's row: token tok0 + 8j + 4 g2 + i < hi_row
-        if (tok0 + kTileTokens > hi_row) {
-  #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int tok = tok0 + 8 * (e >> 2) + 4 * g2 + (e & 3);
-            if (tok >= hi_row) x[e] = neg_inf();
-          }
-        }
-
-        // ---- online softmax against the fixed row reference ----
-        float mt = x[0];
-  #pragma unroll
-        for (int e = 1; e < 16; ++e) mt = fmaxf(mt, x[e]);
-        mt = fmaxf(mt, shfl_xor(mt, 32));
-        m_seen = fmaxf(m_seen, mt);
-        // first non-empty tile of the row: take its max as the reference (the
-        // accumulator and l are still exactly 0, so nothing needs rescaling)
-        if (m_ref == neg_inf()) m_ref = mt;
-        overflow |= mt - m_ref > kRefHeadroomLog2;           // false while -inf
-        const float mref = m_ref == neg_inf() ? 0.f : m_ref;
-        float p[16];
-  #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          p[e] = fast_exp2(x[e] - mref);
-          l_run += p[e];
-        }
-        // Publish P^T (this wave's row group, key step st): the score
-        // accumulator's element order (keys 8 (e / 4) + 4 g2 + e % 4) is the
-        // key order of the V^T fragments, so each lane's 8 probabilities of a
-        // key step are its B-operand fragment as they stand.
-  #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const u32x4 w = {pack_bf16x2(p[8 * st + 0], p[8 * st + 1]), pack_bf16x2(p[8 * st + 2], p[8 * st + 3]),
-                           pack_bf16x2(p[8 * st + 4], p[8 * st + 5]), pack_bf16x2(p[8 * st + 6], p[8 * st + 7])};
-          *(PD_LDS u32x4*)p_slot(k, wave, st) = w;
-        }
-      }
-    }
-
-    // every wave is past its last LDS read of this pass: agree on a rerun and
-    // publish the row statistics through the (now idle) ring
-    __syncthreads();
-    l_run += shfl_xor(l_run, 32);
-    PD_LDS int* flags = (PD_LDS int*)lds;
-    PD_LDS float* row_l = (PD_LDS float*)(lds + 64);
-    PD_LDS float* row_m = row_l + kRowsPerBlock;
-    if (lane == 0) flags[wave] = __ballot(overflow) != 0ull ? 1 : 0;
-    if (g2 == 0) {
-      row_l[wave * kRowsPerWave + l32] = l_run;
-      row_m[wave * kRowsPerWave + l32] = m_ref;
-    }
-    __syncthreads();
-    bool rerun = false;
-  #pragma unroll
-    for (int w = 0; w < kWaves; ++w) rerun |= flags[w] != 0;
-    float lr[4];
-  #pragma unroll
-    for (int r = 0; r < 4; ++r) lr[r] = row_l[r * kRowsPerWave + l32];
-    __syncthreads();   // the statistics are read before the next pass reuses the ring
-    if (!rerun) {
-      // ---- epilogue: O for this wave's 128 dims of all 128 rows; the row
-      // owner (wave r) also writes the row's LSE ------------------------------
-      const float qnan = __builtin_nanf("");
-      if (row_ok) {
-        const bool empty = !(l_run > 0.f);
-        const float lse_nat = empty ? neg_inf() : (m_ref + fast_log2(l_run)) * kLn2;
-        const int64_t q_row = (int64_t)b * a.qlen + t_row;
-        if (direct) {
-          if (a.lse != nullptr && g2 == 0) a.lse[q_row * a.lse_srow + h_row] = bad ? qnan : lse_nat;
-        } else {
-          if (g2 == 0) a.ws[((q_row * a.H + h_row) * S + split) * (kLv + 1) + kLv] = bad ? qnan : lse_nat;
-        }
-      }
-  #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = rb * kRowsPerBlock + r * kRowsPerWave + l32;
-        if (row < rows_req) {
-          const int64_t q_row = (int64_t)b * a.qlen + row / a.H;
-          const int h = row % a.H;
-          const float inv = lr[r] > 0.f ? kscale / lr[r] : 0.f;
-          if (direct) {
-            uint16_t* orow = a.out + q_row * a.o_srow + (int64_t)h * a.o_sh + 32 * kDimBlocksPerWave * wave;
-  #pragma unroll
-            for (int d = 0; d < kDimBlocksPerWave; ++d)
-  #pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const f32x16& ob = 4 * d + r < 15 ? o[4 * d + r < 15 ? 4 * d + r : 0] : o_last;
-                float x0 = ob[4 * j + 0] * inv, x1 = ob[4 * j + 1] * inv;
-                float x2 = ob[4 * j + 2] * inv, x3 = ob[4 * j + 3] * inv;
-                if (bad) x0 = x1 = x2 = x3 = qnan;
-                *(u32x2*)(orow + 32 * d + 8 * j + 4 * g2) = u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
-              }
-          } else {
-            float* oslot = a.ws + ((q_row * a.H + h) * S + split) * (kLv + 1) + 32 * kDimBlocksPerWave * wave;
-  #pragma unroll
-            for (int d = 0; d < kDimBlocksPerWave; ++d)
-  #pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const f32x16& ob = 4 * d + r < 15 ? o[4 * d + r < 15 ? 4 * d + r : 0] : o_last;
-  #pragma unroll
-                for (int i = 0; i < 4; ++i) oslot[32 * d + 8 * j + 4 * g2 + i] = bad ? qnan : ob[4 * j + i] * inv;
-              }
-          }
-        }
-      }
-      break;
-    }
-    }
-  };
-
-  // ---- walk the requests of the share --------------------------------------
-  int ub = b_s, up0 = cb_s;
-  while (ub < a.B && (last || up0 < g1)) {
-    const int L = unit_len(ub), Lr = unit_real(ub, L);
-    const int ntb = __builtin_amdgcn_readfirstlane(block_tiles(L, Lr, n_rb - 1));
-    const bool owner = up0 >= g0;   // the request starts in this share
-    int i0 = 0, i1 = ntb;
-    if (split_mode) {
-      i0 = max(g0 - up0, 0);
-      i1 = min(ntb, g1 - up0);
-    } else if (!owner) {
-      i1 = 0;   // whole requests only: it belongs to an earlier share
-    }
-    const int slot = split_mode ? __builtin_amdgcn_readfirstlane(grp - up0 / T) : 0;
-    for (int rb = member; rb < n_rb; rb += gs) {
-      const int nt = __builtin_amdgcn_readfirstlane(block_tiles(L, Lr, rb));
-      const int j1 = min(i1, nt);
-      if (i0 < j1) run_piece(ub, rb, i0, j1 - i0, slot);
-      if (owner && (nt == 0 || split_mode)) {
-        // lse = -inf in the split slots no piece of the unit uses (all of
-        // them for a unit with no key), or O = 0 / LSE = -inf written directly
-        const int nseg = nt > 0 ? (up0 + nt - 1) / T - up0 / T + 1 : 0;
-        const int my_row = rb * kRowsPerBlock + wave * kRowsPerWave + l32;
-        if (my_row < rows_req) {
-          const int t_row = my_row / a.H, h_row = my_row % a.H;
-          const int64_t q_row = (int64_t)ub * a.qlen + t_row;
-          if (direct) {
-            uint16_t* orow = a.out + q_row * a.o_srow + (int64_t)h_row * a.o_sh;
-            for (int d = g2 * 8; d < kLv; d += 16) *(u32x4*)(orow + d) = u32x4{0, 0, 0, 0};
-            if (a.lse != nullptr && g2 == 0) a.lse[q_row * a.lse_srow + h_row] = neg_inf();
-          } else {
-            for (int sl = nseg + g2; sl < S; sl += 2)
-              a.ws[((q_row * a.H + h_row) * S + sl) * (kLv + 1) + kLv] = neg_inf();
-          }
-        }
-      }
-    }
-    up0 += ntb;
-    ++ub;
-  }
-}
-
-}  // namespace
-
-// Workgroups per launch: one per compute unit (the kernel's LDS fits one
-// workgroup per CU).  Queried once per device.
+// Workgroups per launch: one per compute unit.  Queried once per device.
 static int mla_grid_size() {
   static int cached[64] = {0};
   int dev = 0;
@@ -681,12 +30,14 @@ hipError_t launch_mla_verify(const MlaArgs& a, hipStream_t stream) {
   if (a.B == 0) return hipSuccess;
   const int n = mla_grid_size();
   if (n <= 0) return hipErrorInvalidDevice;
-  dim3 grid(n), block(kWaves * 64);
-  if (a.kv_fp8)
-    hipLaunchKernelGGL((mla_verify_kernel<4, true>), grid, block, 0, stream, a);
-  else
-    hipLaunchKernelGGL((mla_verify_kernel<4, false>), grid, block, 0, stream, a);
-  return hipGetLastError();
+  if (a.P <= 0 || (a.P & (a.P - 1)) != 0 || (1 << a.p_shift) != a.P) return hipErrorInvalidValue;
+  switch (a.P) {
+    case 1: return launch_mla_class<1>(a, n, stream);
+    case 2: return launch_mla_class<2>(a, n, stream);
+    case 4: return launch_mla_class<4>(a, n, stream);
+    case 8: return launch_mla_class<8>(a, n, stream);
+    default: return launch_mla_class<16>(a, n, stream);
+  }
 }
 
 }  // namespace pd

@@ -363,12 +363,12 @@ class MlaWorkload:
 
 def mla_workload(name: str = "mla_verify", batch=None, len_range=None, qlen=None,
                  heads=None, seed_offset: int = 0, fixed_lens=None,
-                 fixed_real=None, no_real=False) -> MlaWorkload:
+                 fixed_real=None, no_real=False, page_size=None) -> MlaWorkload:
     c = CONFIGS[name]
     idx = c["index"]
     rng = np.random.Generator(np.random.PCG64(2000 + idx + 7919 * seed_offset))
     B = c["B"] if batch is None else int(batch)
-    P = c["P"]
+    P = c["P"] if page_size is None else int(page_size)
     ql = c["qlen"] if qlen is None else int(qlen)
     if fixed_lens is not None:
         lens = np.asarray(fixed_lens, dtype=np.int64)

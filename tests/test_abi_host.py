@@ -207,7 +207,9 @@ def test_mla_argument_checks_happen_before_any_hip_call():
     assert _mla(scale=-0.07) == PD_ERR_INVALID
     assert _mla(Lk=512) == PD_ERR_UNSUPPORTED
     assert _mla(Lv=256) == PD_ERR_UNSUPPORTED
-    assert _mla(P=32) == PD_ERR_UNSUPPORTED
+    assert _mla(P=24) == PD_ERR_UNSUPPORTED                    # not a power of two
+    assert _mla(P=1 << 17) == PD_ERR_UNSUPPORTED
+    assert _mla(P=0) == PD_ERR_INVALID
     assert _mla(H=7, qlen=1) == PD_ERR_UNSUPPORTED             # rows per block
     assert _mla(out=FAKE + 2) == PD_ERR_ALIGN
     assert _mla(dt=1, st=576 + 8) == PD_ERR_ALIGN              # fp8 rows need 16 B

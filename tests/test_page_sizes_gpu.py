@@ -1,4 +1,5 @@
-"""GPU parity of the GQA paths at general page sizes against the fp64 oracle.
+"""GPU parity of the GQA and MLA paths at general page sizes against the fp64
+oracle.
 
 "vllm.v1.attention.ops.triton_decode_attention" states support for any page
 size of at least one token; the library takes every power of two.  Pages
@@ -8,15 +9,19 @@ lane within one load); pages of 32 tokens or more hold whole tiles at an
 offset inside the page.  Covered: decode with sinks, verify with windows and
 real lengths, the FP8 cache, split counts, and bitwise equality of the
 outputs for one logical cache stored at different page sizes (the kernel's
-arithmetic does not depend on where a key lives).
+arithmetic does not depend on where a key lives).  The MLA verify kernel
+reads 16-row regions of its 32-token tiles: pages of 16 tokens or more hold
+whole regions, smaller pages are picked per lane; covered at 1 to 64 tokens
+per page, bf16 and FP8, with rows that have no key, an out-of-range entry
+(NaN for its request) and bitwise equality across page sizes.
 """
 
 import numpy as np
 import pytest
 import torch
 
-from helpers import O_ATOL_FP8, check_attention, oracle_gqa
-from synth import gqa_workload
+from helpers import O_ATOL_FP8, check_attention, oracle_gqa, oracle_mla
+from synth import gqa_workload, mla_workload
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X")]
@@ -119,5 +124,104 @@ def test_outputs_bitwise_equal_across_page_sizes(pd, qlen, window):
         for P2 in (1, 2, 8, 64):
             kv2, bt2 = _relayout(w, vals["kv"], P2, rng)
             o, l = _run(pd, w, vals, S, kv=kv2, bt=bt2)
+            assert torch.equal(o.view(torch.int16), ref_o.view(torch.int16)), (P2, S)
+            assert torch.equal(l.view(torch.int32), ref_l.view(torch.int32)), (P2, S)
+
+
+# ---------------------------------------------------------------------------
+# MLA causal verify
+# ---------------------------------------------------------------------------
+
+MLA_PAGE_SIZES = [1, 2, 4, 8, 32, 64]
+
+
+def _run_mla(pd, w, vals, S, fp8=False, kv=None, bt=None):
+    real = None if w.real_seq_lens is None else torch.from_numpy(w.real_seq_lens).cuda()
+    ks = torch.tensor([vals["k_scale"]], dtype=torch.float32, device="cuda") if fp8 else None
+    out, lse = pd.paged_verify_mla(vals["q"], vals["kv"] if kv is None else kv,
+                                   torch.from_numpy(w.block_table if bt is None else bt).cuda(),
+                                   torch.from_numpy(w.seq_lens).cuda(), real, w.qlen, w.sm_scale,
+                                   head_dim_v=w.Lv, k_scale=ks, num_kv_splits=S)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def _check_mla(w, vals, out, lse, fp8, what, requests=None):
+    O, L = oracle_mla(w, vals, requests=requests, fp8=fp8)
+    check_attention(out, lse, O.reshape(out.shape), L, o_atol=O_ATOL_FP8 if fp8 else 2e-2,
+                    what=what)
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("P", MLA_PAGE_SIZES)
+def test_mla_verify(pd, P, fp8):
+    w = mla_workload(batch=3, len_range=(1, 400), page_size=P, seed_offset=P)
+    vals = w.values("cuda", poison=True, fp8=fp8)
+    for S in (1, 3):
+        out, lse = _run_mla(pd, w, vals, S, fp8)
+        _check_mla(w, vals, out, lse, fp8, f"mla P={P} fp8={fp8} S={S}")
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("P", [1, 4, 64])
+def test_mla_rows_without_keys(pd, P, fp8):
+    """L < qlen and L = 0 at small and large pages, 16 heads (rows past the
+    request's 64 rows in the 128-row block)."""
+    w = mla_workload(fixed_lens=[2, 5, 40, 0, 97], fixed_real=[2, 4, 39, 0, 95], heads=16,
+                     page_size=P)
+    vals = w.values("cuda", poison=True, fp8=fp8)
+    out, lse = _run_mla(pd, w, vals, 2, fp8)
+    _check_mla(w, vals, out, lse, fp8, f"mla keyless P={P}")
+    assert torch.all(out[0:2].float() == 0) and torch.all(torch.isneginf(lse[0:2]))
+    assert torch.all(out[12:16].float() == 0)                 # L = 0
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("P", [1, 2, 8, 32])
+def test_mla_out_of_range_entry_gives_nan(pd, P, fp8):
+    """An attended out-of-range entry NaNs its request's rows; every wave
+    learns it through the end-of-piece exchange, whichever wave read it."""
+    w = mla_workload(fixed_lens=[90, 90], fixed_real=[90, 90], heads=16, page_size=P)
+    vals = w.values("cuda", poison=True, fp8=fp8)
+    bt = w.block_table.copy()
+    bt[1, (70 // P)] = w.num_pages + 3
+    for S in (1, 2):
+        out, lse = _run_mla(pd, w, vals, S, fp8, bt=bt)
+        rows = slice(w.qlen, 2 * w.qlen)
+        assert torch.all(torch.isnan(out[rows].float())) and torch.all(torch.isnan(lse[rows]))
+        _check_mla(w, vals, out[:w.qlen], lse[:w.qlen], fp8, f"valid neighbour P={P}",
+                   requests=[0])
+
+
+def _relayout_mla(w, kv, P2, rng):
+    P = w.P
+    src = kv.cpu()
+    cap = [-(-int(L) // P2) for L in w.seq_lens]
+    n_pages = sum(cap) + 2
+    perm = rng.permutation(n_pages)
+    bt = np.full((w.B, max(cap + [1]) + 1), -1, np.int32)
+    dst = torch.zeros((n_pages, P2, 1, src.shape[-1]), dtype=src.dtype)
+    off = 0
+    for b, L in enumerate(w.seq_lens):
+        L = int(L)
+        bt[b, :cap[b]] = perm[off:off + cap[b]]
+        off += cap[b]
+        pos = np.arange(L)
+        if L:
+            dst[torch.from_numpy(bt[b, pos // P2]).long(), torch.from_numpy(pos % P2).long()] = \
+                src[torch.from_numpy(w.block_table[b, pos // P]).long(), torch.from_numpy(pos % P).long()]
+    return dst.cuda(), bt
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+def test_mla_outputs_bitwise_equal_across_page_sizes(pd, fp8):
+    w = mla_workload(batch=3, len_range=(1, 300), page_size=16, seed_offset=5)
+    vals = w.values("cuda", poison=True, fp8=fp8)
+    rng = np.random.default_rng(13)
+    for S in (1, 2):
+        ref_o, ref_l = _run_mla(pd, w, vals, S, fp8)
+        for P2 in (1, 2, 4, 8, 64):
+            kv2, bt2 = _relayout_mla(w, vals["kv"], P2, rng)
+            o, l = _run_mla(pd, w, vals, S, fp8, kv=kv2, bt=bt2)
             assert torch.equal(o.view(torch.int16), ref_o.view(torch.int16)), (P2, S)
             assert torch.equal(l.view(torch.int32), ref_l.view(torch.int32)), (P2, S)
