@@ -355,9 +355,12 @@ void mla_verify_kernel(MlaArgs a) {
         const bool ok = tp.first + cand <= last_page && (uint32_t)id < num_pages;
         const uint32_t chunk = FP8 ? 16u * (uint32_t)(lane >> 4) + (uint32_t)g_first
                                    : 16u * (uint32_t)((lane & 7) ^ (lane >> 3) ^ (wave & 1));
+        // bf16: a lane whose page is not read steps through the first bytes
+        // of q (at least 32 rows of 1152 bytes), so the step stays
+        // wave-uniform, one register less (measured faster for bf16 only)
         tl.base = ok ? kv + (int64_t)id * sp_bytes + (row & (PC - 1)) * st_bytes + chunk : (const char*)a.q;
         tl.voff = 0u;
-        tl.gstep = ok ? kGStep : 0;
+        tl.gstep = (FP8 && !ok) ? 0 : kGStep;
       }
       return tl;
     };
