@@ -46,8 +46,8 @@ def _parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--splits", type=int, default=0, help="override the split cap")
     p.add_argument("--page-size", type=int, default=0,
-                   help="GQA configs: store the same workload in pages of this many tokens "
-                        "(a power of two; the pool then holds exactly the pages in use)")
+                   help="decode / verify configs: store the same workload in pages of this many "
+                        "tokens (a power of two; a GQA pool then holds exactly the pages in use)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="after timing, run one plain device copy of this many MiB (a "
                         "known-size reference for hardware byte counters)")
@@ -143,10 +143,10 @@ def _append_case(torch, pd):
                 extra=dict(k=k, v=v))
 
 
-def _mla_case(fp8, torch, pd, splits):
+def _mla_case(fp8, torch, pd, splits, page_size=0):
     from synth import mla_workload
 
-    w = mla_workload("mla_verify")
+    w = mla_workload("mla_verify", page_size=page_size or None)
     vals = w.values("cuda", poison=False, fp8=fp8)
     bt = torch.from_numpy(w.block_table).cuda()
     sl = torch.from_numpy(w.seq_lens).cuda()
@@ -162,7 +162,7 @@ def _mla_case(fp8, torch, pd, splits):
                             head_dim_v=w.Lv, k_scale=k_scale if fp8 else None,
                             num_kv_splits=S, workspace=ws, out=out, lse=lse)
 
-    desc = ("MLA causal verify: B=32, qlen=4, H=128, Lk=576, Lv=512, page 16, "
+    desc = (f"MLA causal verify: B=32, qlen=4, H=128, Lk=576, Lv=512, page {w.P}, "
             f"seq_lens U[2048,16384], {'fp8 e4m3fn' if fp8 else 'bf16'} latent cache")
     return dict(w=w, vals=vals, S=S, step=step, kernel=None, rest=None,
                 kv_bytes=w.kv_bytes(1 if fp8 else 2), flops=w.flops(), desc=desc,
@@ -301,12 +301,14 @@ def main():
 
     torch.cuda.init()
     name = args.config
-    if args.page_size and (name in ("kv_append", "tiny_gqa") or name.startswith("mla")):
-        print("bench.py: --page-size applies to the GQA decode and verify configs only",
+    if args.page_size and name in ("kv_append", "tiny_gqa"):
+        print("bench.py: --page-size applies to the decode and verify configs only",
               file=sys.stderr)
         sys.exit(2)
     if name in ("mla_verify", "mla_verify_fp8"):
-        case = _mla_case(name.endswith("fp8"), torch, pd, args.splits)
+        case = _mla_case(name.endswith("fp8"), torch, pd, args.splits, args.page_size)
+        if args.page_size:
+            name = f"{name}_p{args.page_size}"
     elif name == "kv_append":
         case = _append_case(torch, pd)
     else:
