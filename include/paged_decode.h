@@ -151,7 +151,10 @@ PD_API size_t pd_workspace_bytes(int32_t rows, int32_t num_heads, int32_t num_sp
  * out          [B, Hq, D] bf16, strides (o_stride_b, o_stride_h, 1).
  * lse          [B, Hq] fp32 with row stride lse_stride_b, or NULL.
  *
- * Supported: D = 128; P in {16, 32}; Hq = G * Hkv with 1 <= G <= 16.
+ * Supported: D = 128; P any power of two from 1 to 65536 (the verify module
+ * of "vllm.v1.attention.ops.triton_decode_attention" takes any page size of
+ * at least one token; P < 1 gives PD_ERR_INVALID, other sizes
+ * PD_ERR_UNSUPPORTED); Hq = G * Hkv with 1 <= G <= 16.
  * q, kv, out, workspace 16-byte aligned; q/kv/out strides multiples of 8.
  * A workspace must not be shared by calls in flight on different streams.
  */
@@ -308,7 +311,8 @@ PD_API int paged_kv_append(const void* src0, int64_t src0_stride_tok, int64_t sr
  * out          [B*qlen, H, Lv] bf16, strides (o_stride_row, o_stride_h, 1).
  * lse          [B*qlen, H] fp32 with row stride lse_stride_row, or NULL.
  *
- * Supported: Lk = 576, Lv = 512 (512 + 64 rope dims); P = 16;
+ * Supported: Lk = 576, Lv = 512 (512 + 64 rope dims); P any power of two
+ * from 1 to 65536 (the module states support for page size >= 1);
  * qlen * H a multiple of 32; pointers 16-byte aligned; strides multiples of
  * 16 bytes.
  */
