@@ -54,9 +54,12 @@ constexpr int kRowBytes = 2 * kD * 2;                   // K|V row of one token 
 constexpr int kTileBytes = kTileTokens * kRowBytes;     // 16 KB
 constexpr int kRowBytes8 = 2 * kD;                      // K|V row of one token (FP8)
 constexpr int kTileBytes8 = kTileTokens * kRowBytes8;   // 8 KB
-// Ring of a wave: 2 tiles as loaded; an FP8 ring is followed by the bf16
-// tile it is dequantised into, so both rings take 32 KB.
+// Ring of a wave, 32 KB either way: bf16, 2 tiles of 16 KB (one computed,
+// one loading); FP8, 3 tiles of 8 KB as loaded (one computed, two loading)
+// and the 8 KB bf16 V half of the computed tile.
 constexpr int kRingBytes = 2 * kTileBytes;
+constexpr int kStage8 = 3 * kTileBytes8;   // FP8: offset of the bf16 V tile
+static_assert(kStage8 + kTileTokens * kD * 2 == kRingBytes, "FP8 ring + V tile = 32 KB");
 // Smallest share a wave takes: below it the per-wave start-up dominates.
 constexpr int kMinWaveTiles = 4;
 
@@ -382,8 +385,10 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
     // FP8: 4 rows of 16 chunks per load, plain
     constexpr int kRowsPerLoad = F8 ? 4 : 2;
     const int sub = F8 ? (lane >> 4) : (lane >> 5);   // this lane's row within a load
+    // bf16: chunk c of row r at position c ^ swz(r); FP8: at c ^ (r mod 16)
+    // (position = lane, so the lane fetches the chunk that lands there)
     auto chunk_of = [&](int r) {
-      return F8 ? (uint32_t)(lane & 15) : (uint32_t)((lane & 31) ^ swz(r));
+      return F8 ? (uint32_t)((lane & 15) ^ (r & 15)) : (uint32_t)((lane & 31) ^ swz(r));
     };
     bool bad_page = false;
     if constexpr (kLaneAddr) {
@@ -507,6 +512,18 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
     bad_slots = issue(ci, pg_next, 0) ? 1 : 0;
     advance(ci);
     pg_next = ci.b < a.B ? fetch_pages(ci) : pages_none;
+    // FP8: a second tile in flight from the start (ring of 3)
+    int issued = 1;            // tiles issued so far
+    int slot_k = 0, slot_i = 1;   // ring slot of the computed tile, of the next issue
+    if constexpr (F8) {
+      if (ci.b < a.B) {
+        bad_slots |= issue(ci, pg_next, 1) ? 2 : 0;
+        advance(ci);
+        pg_next = ci.b < a.B ? fetch_pages(ci) : pages_none;
+        issued = 2;
+        slot_i = 2;
+      }
+    }
 
     for (int k = 0; cc.b < a.B; ++k) {
       const bool first = piece_start(cc);
@@ -530,19 +547,30 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
         }
       }
 
-      const bool issuing = ci.b < a.B;
-      if (issuing) {
-        wait_lgkmcnt0();  // LDS reads of the slot (tile k-1) and of an old query slot are done
-        const int slot = (k + 1) & 1;
-        const bool bad_tile = issue(ci, pg_next, slot);
-        bad_slots = (bad_slots & ~(1 << slot)) | (bad_tile ? 1 << slot : 0);
+      auto issue_next = [&]() {
+        wait_lgkmcnt0();  // LDS reads of the slot's old tile and of an old query slot are done
+        const bool bad_tile = issue(ci, pg_next, slot_i);
+        bad_slots = (bad_slots & ~(1 << slot_i)) | (bad_tile ? 1 << slot_i : 0);
         advance(ci);
         pg_next = ci.b < a.B ? fetch_pages(ci) : pages_none;
+        ++issued;
+        slot_i = F8 ? (slot_i == 2 ? 0 : slot_i + 1) : slot_i ^ 1;
+      };
+      if constexpr (F8) {
+        // tile k has landed once at most the tile issued after it is in
+        // flight (its query rows were loaded before it, so they are in too)
+        if (issued > k + 1)
+          wait_vmcnt<kLoadsPerTile>();
+        else
+          wait_vmcnt<0>();
+      } else {
+        const bool issuing = ci.b < a.B;
+        if (issuing) issue_next();
+        if (issuing)
+          wait_vmcnt<kLoadsPerTile>();
+        else
+          wait_vmcnt<0>();
       }
-      if (issuing)
-        wait_vmcnt<kLoadsPerTile>();
-      else
-        wait_vmcnt<0>();
 
       if (first) {
         // the piece's query rows (loaded before its first tile): B operand
@@ -555,30 +583,40 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
         }
         ++q_used;
       }
-
-      const int slot = k & 1;
-      piece_bad |= (bad_slots >> slot) & 1;
-      PD_LDS char* tl = ring + slot * kSlotBytes;
+      // FP8: the next issue goes after the query read, so the query slot
+      // of this piece is free again and two slots serve two tiles in flight
       if constexpr (F8) {
-        // exact FP8 -> bf16 into the bf16 tile after the ring, in the bf16
-        // layout: item (row r, FP8 chunk cf of 16 codes) -> bf16 chunks 2 cf
-        // and 2 cf + 1 of row r, XOR-swizzled
-        PD_LDS char* st = ring + 2 * kTileBytes8;
+        if (ci.b < a.B) issue_next();
+      }
+
+      piece_bad |= (bad_slots >> slot_k) & 1;
+      PD_LDS char* tl = ring + slot_k * kSlotBytes;   // tile k as loaded
+      // bf16: the V half is read from the tile (row stride 512 bytes, chunk
+      // 16 + c at position (16 + c) ^ swz(r)); FP8: from the bf16 V tile
+      // (row stride 256 bytes, chunk c at position c ^ swz(r))
+      PD_LDS char* vt = F8 ? ring + kStage8 : tl + 256;
+      constexpr int kVRowBytes = F8 ? kD * 2 : kRowBytes;
+      constexpr std::false_type kLo{};
+      constexpr std::true_type kHi{};
+      // two FP8 codes of a dword (low or high half) -> two packed bf16
+      auto cvt8 = [](uint32_t w, auto hi) {
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, decltype(hi)::value));
+      };
+      if constexpr (F8) {
+        // exact FP8 -> bf16 of the V half (scale 1: every E4M3FN value is a
+        // bf16 value): item (row r, V chunk cf of 16 codes) -> bf16 chunks
+        // 2 cf and 2 cf + 1 of row r of the V tile
 #pragma unroll
-        for (int it = 0; it < 8; ++it) {
-          const int r = 4 * it + (lane >> 4), cf = lane & 15;
-          const u32x4 w = *(PD_LDS const u32x4*)(tl + r * kRowBytes8 + cf * 16);
+        for (int it = 0; it < 4; ++it) {
+          const int r = 8 * it + (lane >> 3), cf = lane & 7;
+          const u32x4 w = *(PD_LDS const u32x4*)(tl + r * kRowBytes8 + (((8 + cf) ^ (r & 15)) << 4));
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
-            u32x4 cv;
-            cv[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * h], 1.f, false));
-            cv[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * h], 1.f, true));
-            cv[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * h + 1], 1.f, false));
-            cv[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * h + 1], 1.f, true));
-            *(PD_LDS u32x4*)(st + r * kRowBytes + (((2 * cf + h) ^ swz(r)) << 4)) = cv;
+            const u32x4 cv = {cvt8(w[2 * h], kLo), cvt8(w[2 * h], kHi),
+                              cvt8(w[2 * h + 1], kLo), cvt8(w[2 * h + 1], kHi)};
+            *(PD_LDS u32x4*)(vt + r * kVRowBytes + (((2 * cf + h) ^ swz(r)) << 4)) = cv;
           }
         }
-        tl = st;
       }
       const int lo = cc.r.lo, hi = cc.r.hi;
       const int tok0 = ((lo >> 5) + cc.i) * kTileTokens;
@@ -588,9 +626,22 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
       const int sw = swz(l16);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const int ch = (g4 + 4 * s) ^ sw;
-        bf16x8 k0 = *(PD_LDS bf16x8*)(tl + l16 * kRowBytes + ch * 16);
-        bf16x8 k1 = *(PD_LDS bf16x8*)(tl + (16 + l16) * kRowBytes + ch * 16);
+        bf16x8 k0, k1;
+        if constexpr (F8) {
+          // dims 32 s + 8 g4 .. + 7 of rows l16 and 16 + l16: half g4 % 2 of
+          // FP8 chunk 2 s + g4 / 2, converted in registers
+          const int off = (((2 * s + (g4 >> 1)) ^ l16) << 4) + (g4 & 1) * 8;
+          const u32x2 w0 = *(PD_LDS const u32x2*)(tl + l16 * kRowBytes8 + off);
+          const u32x2 w1 = *(PD_LDS const u32x2*)(tl + (16 + l16) * kRowBytes8 + off);
+          k0 = __builtin_bit_cast(bf16x8, u32x4{cvt8(w0[0], kLo), cvt8(w0[0], kHi),
+                                                cvt8(w0[1], kLo), cvt8(w0[1], kHi)});
+          k1 = __builtin_bit_cast(bf16x8, u32x4{cvt8(w1[0], kLo), cvt8(w1[0], kHi),
+                                                cvt8(w1[1], kLo), cvt8(w1[1], kHi)});
+        } else {
+          const int ch = (g4 + 4 * s) ^ sw;
+          k0 = *(PD_LDS bf16x8*)(tl + l16 * kRowBytes + ch * 16);
+          k1 = *(PD_LDS bf16x8*)(tl + (16 + l16) * kRowBytes + ch * 16);
+        }
         s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[s], s0, 0, 0, 0);
         s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[s], s1, 0, 0, 0);
       }
@@ -650,12 +701,13 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
       const int swa = swz(ra);
 #pragma unroll
       for (int blk = 0; blk < 8; ++blk) {
-        const int ch = 16 + 2 * blk + ((l16 & 3) >> 1);
+        // V chunk (16 dims) of this block: position c ^ swz(row) in the V half
+        const int ch = 2 * blk + ((l16 & 3) >> 1);
         const int within = (l16 & 1) * 8;
         bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (PD_LDS bf16x4*)(tl + ra * kRowBytes + ((ch ^ swa) << 4) + within));
+            (PD_LDS bf16x4*)(vt + ra * kVRowBytes + ((ch ^ swa) << 4) + within));
         bf16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (PD_LDS bf16x4*)(tl + rb * kRowBytes + ((ch ^ swa) << 4) + within));
+            (PD_LDS bf16x4*)(vt + rb * kVRowBytes + ((ch ^ swa) << 4) + within));
         u32x2 ua = __builtin_bit_cast(u32x2, va);
         u32x2 ub = __builtin_bit_cast(u32x2, vb);
         u32x4 vv = {ua[0], ua[1], ub[0], ub[1]};
@@ -665,6 +717,7 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
 
       if (cc.i + 1 == cc.i_end) finish_piece(cc);
       advance(cc);
+      slot_k = F8 ? (slot_k == 2 ? 0 : slot_k + 1) : slot_k ^ 1;
     }
   }
 
