@@ -55,11 +55,15 @@ constexpr int kTileBytes = kTileTokens * kRowBytes;     // 16 KB
 constexpr int kRowBytes8 = 2 * kD;                      // K|V row of one token (FP8)
 constexpr int kTileBytes8 = kTileTokens * kRowBytes8;   // 8 KB
 // Ring of a wave, 32 KB either way: bf16, 2 tiles of 16 KB (one computed,
-// one loading); FP8, 3 tiles of 8 KB as loaded (one computed, two loading)
-// and the 8 KB bf16 V half of the computed tile.
+// one loading); FP8, 4 tiles of 8 KB (one computed, up to three loading).
 constexpr int kRingBytes = 2 * kTileBytes;
-constexpr int kStage8 = 3 * kTileBytes8;   // FP8: offset of the bf16 V tile
-static_assert(kStage8 + kTileTokens * kD * 2 == kRingBytes, "FP8 ring + V tile = 32 KB");
+static_assert(4 * kTileBytes8 == kRingBytes, "FP8 ring of 4 tiles");
+
+// FP8 tile: 16-byte chunk c of token row r (256 bytes) is stored at chunk
+// c ^ f8(r).  Rows 0..15 (and 16..31) get distinct values (K reads: 16 rows,
+// one chunk), and the 8 rows a 16-lane group reads for a V^T fragment
+// (4 g .. 4 g + 3 and 16 + 4 g .. 16 + 4 g + 3) too.
+__device__ __forceinline__ int f8(int r) { return (r & 15) ^ ((r >> 4) << 2); }
 // Smallest share a wave takes: below it the per-wave start-up dominates.
 constexpr int kMinWaveTiles = 4;
 
@@ -385,10 +389,10 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
     // FP8: 4 rows of 16 chunks per load, plain
     constexpr int kRowsPerLoad = F8 ? 4 : 2;
     const int sub = F8 ? (lane >> 4) : (lane >> 5);   // this lane's row within a load
-    // bf16: chunk c of row r at position c ^ swz(r); FP8: at c ^ (r mod 16)
+    // bf16: chunk c of row r at position c ^ swz(r); FP8: at c ^ f8(r)
     // (position = lane, so the lane fetches the chunk that lands there)
     auto chunk_of = [&](int r) {
-      return F8 ? (uint32_t)((lane & 15) ^ (r & 15)) : (uint32_t)((lane & 31) ^ swz(r));
+      return F8 ? (uint32_t)((lane & 15) ^ f8(r)) : (uint32_t)((lane & 31) ^ swz(r));
     };
     bool bad_page = false;
     if constexpr (kLaneAddr) {
@@ -512,18 +516,26 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
     bad_slots = issue(ci, pg_next, 0) ? 1 : 0;
     advance(ci);
     pg_next = ci.b < a.B ? fetch_pages(ci) : pages_none;
-    // FP8: a second tile in flight from the start (ring of 3)
-    int issued = 1;            // tiles issued so far
+    int issued = 1;               // tiles issued so far
     int slot_k = 0, slot_i = 1;   // ring slot of the computed tile, of the next issue
-    if constexpr (F8) {
-      if (ci.b < a.B) {
-        bad_slots |= issue(ci, pg_next, 1) ? 2 : 0;
-        advance(ci);
-        pg_next = ci.b < a.B ? fetch_pages(ci) : pages_none;
-        issued = 2;
-        slot_i = 2;
-      }
-    }
+    constexpr int kSlots = F8 ? 4 : 2;
+    auto issue_next = [&]() {
+      wait_lgkmcnt0();  // LDS reads of the slot's old tile and of an old query slot are done
+      const bool bad_tile = issue(ci, pg_next, slot_i);
+      bad_slots = (bad_slots & ~(1 << slot_i)) | (bad_tile ? 1 << slot_i : 0);
+      advance(ci);
+      pg_next = ci.b < a.B ? fetch_pages(ci) : pages_none;
+      ++issued;
+      slot_i = (slot_i + 1) & (kSlots - 1);
+    };
+    // FP8: up to three tiles in flight.  A tile that starts a piece also
+    // needs one of the two query slots; a slot is free again once its
+    // piece's first tile has read it into registers.
+    auto fill_ring = [&](int k_now) {
+      while (ci.b < a.B && issued < k_now + kSlots && (!piece_start(ci) || q_issued - q_used < 2))
+        issue_next();
+    };
+    if constexpr (F8) fill_ring(-1);
 
     for (int k = 0; cc.b < a.B; ++k) {
       const bool first = piece_start(cc);
@@ -547,19 +559,14 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
         }
       }
 
-      auto issue_next = [&]() {
-        wait_lgkmcnt0();  // LDS reads of the slot's old tile and of an old query slot are done
-        const bool bad_tile = issue(ci, pg_next, slot_i);
-        bad_slots = (bad_slots & ~(1 << slot_i)) | (bad_tile ? 1 << slot_i : 0);
-        advance(ci);
-        pg_next = ci.b < a.B ? fetch_pages(ci) : pages_none;
-        ++issued;
-        slot_i = F8 ? (slot_i == 2 ? 0 : slot_i + 1) : slot_i ^ 1;
-      };
       if constexpr (F8) {
-        // tile k has landed once at most the tile issued after it is in
-        // flight (its query rows were loaded before it, so they are in too)
-        if (issued > k + 1)
+        // tile k has landed once at most the tiles issued after it are in
+        // flight (their query rows were loaded before them, so they count
+        // as part of the wait)
+        const int after = issued - k - 1;
+        if (after >= 2)
+          wait_vmcnt<2 * kLoadsPerTile>();
+        else if (after == 1)
           wait_vmcnt<kLoadsPerTile>();
         else
           wait_vmcnt<0>();
@@ -583,41 +590,21 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
         }
         ++q_used;
       }
-      // FP8: the next issue goes after the query read, so the query slot
-      // of this piece is free again and two slots serve two tiles in flight
-      if constexpr (F8) {
-        if (ci.b < a.B) issue_next();
-      }
+      // FP8: the next issues go after the query read, so this piece's query
+      // slot is free again
+      if constexpr (F8) fill_ring(k);
 
       piece_bad |= (bad_slots >> slot_k) & 1;
       PD_LDS char* tl = ring + slot_k * kSlotBytes;   // tile k as loaded
-      // bf16: the V half is read from the tile (row stride 512 bytes, chunk
-      // 16 + c at position (16 + c) ^ swz(r)); FP8: from the bf16 V tile
-      // (row stride 256 bytes, chunk c at position c ^ swz(r))
-      PD_LDS char* vt = F8 ? ring + kStage8 : tl + 256;
-      constexpr int kVRowBytes = F8 ? kD * 2 : kRowBytes;
+      // bf16: the V half of the tile, row stride 512 bytes, chunk 16 + c at
+      // position (16 + c) ^ swz(r)
+      PD_LDS char* vt = tl + 256;
       constexpr std::false_type kLo{};
       constexpr std::true_type kHi{};
       // two FP8 codes of a dword (low or high half) -> two packed bf16
       auto cvt8 = [](uint32_t w, auto hi) {
         return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, decltype(hi)::value));
       };
-      if constexpr (F8) {
-        // exact FP8 -> bf16 of the V half (scale 1: every E4M3FN value is a
-        // bf16 value): item (row r, V chunk cf of 16 codes) -> bf16 chunks
-        // 2 cf and 2 cf + 1 of row r of the V tile
-#pragma unroll
-        for (int it = 0; it < 4; ++it) {
-          const int r = 8 * it + (lane >> 3), cf = lane & 7;
-          const u32x4 w = *(PD_LDS const u32x4*)(tl + r * kRowBytes8 + (((8 + cf) ^ (r & 15)) << 4));
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const u32x4 cv = {cvt8(w[2 * h], kLo), cvt8(w[2 * h], kHi),
-                              cvt8(w[2 * h + 1], kLo), cvt8(w[2 * h + 1], kHi)};
-            *(PD_LDS u32x4*)(vt + r * kVRowBytes + (((2 * cf + h) ^ swz(r)) << 4)) = cv;
-          }
-        }
-      }
       const int lo = cc.r.lo, hi = cc.r.hi;
       const int tok0 = ((lo >> 5) + cc.i) * kTileTokens;
 
@@ -629,10 +616,12 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
         bf16x8 k0, k1;
         if constexpr (F8) {
           // dims 32 s + 8 g4 .. + 7 of rows l16 and 16 + l16: half g4 % 2 of
-          // FP8 chunk 2 s + g4 / 2, converted in registers
-          const int off = (((2 * s + (g4 >> 1)) ^ l16) << 4) + (g4 & 1) * 8;
-          const u32x2 w0 = *(PD_LDS const u32x2*)(tl + l16 * kRowBytes8 + off);
-          const u32x2 w1 = *(PD_LDS const u32x2*)(tl + (16 + l16) * kRowBytes8 + off);
+          // FP8 chunk 2 s + g4 / 2, converted in registers (exact: every
+          // E4M3FN value is a bf16 value)
+          const int c8 = 2 * s + (g4 >> 1), h8 = (g4 & 1) * 8;
+          const u32x2 w0 = *(PD_LDS const u32x2*)(tl + l16 * kRowBytes8 + ((c8 ^ f8(l16)) << 4) + h8);
+          const u32x2 w1 =
+              *(PD_LDS const u32x2*)(tl + (16 + l16) * kRowBytes8 + ((c8 ^ f8(16 + l16)) << 4) + h8);
           k0 = __builtin_bit_cast(bf16x8, u32x4{cvt8(w0[0], kLo), cvt8(w0[0], kHi),
                                                 cvt8(w0[1], kLo), cvt8(w0[1], kHi)});
           k1 = __builtin_bit_cast(bf16x8, u32x4{cvt8(w1[0], kLo), cvt8(w1[0], kHi),
@@ -699,25 +688,41 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
       const int ra = 4 * g4 + (l16 >> 2);
       const int rb = ra + 16;
       const int swa = swz(ra);
+      // FP8 V^T: the 8-bit transpose read gives lane i of a 16-lane group
+      // byte i % 8 of the 8 bytes read by lanes 2 e + (i >= 8), e = 0..7; so
+      // lane s reads dims 16 blk + 8 (s % 2) .. + 7 of token T(s / 2), with
+      // T(e) = 4 g4 + e (e < 4) and 16 + 4 g4 + e - 4 (the k order of P^T)
+      const int tv = (l16 >> 1) < 4 ? 4 * g4 + (l16 >> 1) : 12 + 4 * g4 + (l16 >> 1);
+      PD_LDS char* vrow8 = tl + tv * kRowBytes8 + (l16 & 1) * 8;
+      const int fv = f8(tv);
 #pragma unroll
       for (int blk = 0; blk < 8; ++blk) {
-        // V chunk (16 dims) of this block: position c ^ swz(row) in the V half
-        const int ch = 2 * blk + ((l16 & 3) >> 1);
-        const int within = (l16 & 1) * 8;
-        bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (PD_LDS bf16x4*)(vt + ra * kVRowBytes + ((ch ^ swa) << 4) + within));
-        bf16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (PD_LDS bf16x4*)(vt + rb * kVRowBytes + ((ch ^ swa) << 4) + within));
-        u32x2 ua = __builtin_bit_cast(u32x2, va);
-        u32x2 ub = __builtin_bit_cast(u32x2, vb);
-        u32x4 vv = {ua[0], ua[1], ub[0], ub[1]};
+        u32x4 vv;
+        if constexpr (F8) {
+          typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
+          const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (PD_LDS i32x2*)(vrow8 + (((8 + blk) ^ fv) << 4)));
+          const uint32_t w_lo = (uint32_t)w[0], w_hi = (uint32_t)w[1];
+          vv = u32x4{cvt8(w_lo, kLo), cvt8(w_lo, kHi), cvt8(w_hi, kLo), cvt8(w_hi, kHi)};
+        } else {
+          // V chunk (16 dims) of this block: position c ^ swz(row) in the V half
+          const int ch = 2 * blk + ((l16 & 3) >> 1);
+          const int within = (l16 & 1) * 8;
+          bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (PD_LDS bf16x4*)(vt + ra * kRowBytes + ((ch ^ swa) << 4) + within));
+          bf16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (PD_LDS bf16x4*)(vt + rb * kRowBytes + ((ch ^ swa) << 4) + within));
+          u32x2 ua = __builtin_bit_cast(u32x2, va);
+          u32x2 ub = __builtin_bit_cast(u32x2, vb);
+          vv = u32x4{ua[0], ua[1], ub[0], ub[1]};
+        }
         if (edge) vv &= vkeep;
         o[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pf, o[blk], 0, 0, 0);
       }
 
       if (cc.i + 1 == cc.i_end) finish_piece(cc);
       advance(cc);
-      slot_k = F8 ? (slot_k == 2 ? 0 : slot_k + 1) : slot_k ^ 1;
+      slot_k = (slot_k + 1) & (kSlots - 1);
     }
   }
 
