@@ -103,12 +103,12 @@ void mla_verify_kernel(MlaArgs a) {
   // so every issuing wave has the same count for its vmcnt bookkeeping.
   constexpr int kIssueWaves = FP8 ? 2 : 4;
   static_assert(NS == 4, "ring of 4 tiles: k-1 (product), k (scores), k+1, k+2 (loading)");
-  constexpr int kStageOff = NS * kRingTile;                         // 2 fp8 -> bf16 tiles
+  constexpr int kStageOff = NS * kRingTile;
   constexpr int kLoadsPerWave = kLoadsPerTile / kIssueWaves;
   static_assert(kLoadsPerWave * kIssueWaves == kLoadsPerTile, "even load split");
   constexpr int kLoadSpacing = kKSteps / kLoadsPerWave;             // score steps between a wave's loads
   static_assert(kLoadSpacing >= 1 && (kLoadsPerWave - 1) * kLoadSpacing < kKSteps, "loads fit the score steps");
-  constexpr int kPOff = kStageOff + (FP8 ? 2 * kTileBytes : 0);     // P^T of tiles k-1 and k
+  constexpr int kPOff = kStageOff;                                  // P^T of tiles k-1 and k
   constexpr int kLdsBytes = kPOff + 2 * kPBufBytes;
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
@@ -233,9 +233,10 @@ void mla_verify_kernel(MlaArgs a) {
     // and drain the tile ring on every iteration).
     bf16x8 qf[kKSteps];
     {
-      const uint16_t* qp = a.q + ((int64_t)b * a.qlen + t_row) * a.q_srow + (int64_t)h_row * a.q_sh + 8 * g2;
+      const uint16_t* qp = a.q + ((int64_t)b * a.qlen + t_row) * a.q_srow + (int64_t)h_row * a.q_sh;
+      // step kk takes dims 16 kk + 8 g2 .. + 7
   #pragma unroll
-      for (int kk = 0; kk < kKSteps; ++kk) qf[kk] = *(const bf16x8*)(qp + 16 * kk);
+      for (int kk = 0; kk < kKSteps; ++kk) qf[kk] = *(const bf16x8*)(qp + 16 * kk + 8 * g2);
       wait_vmcnt<0>();
     }
 
@@ -296,8 +297,12 @@ void mla_verify_kernel(MlaArgs a) {
     // fp8: instruction i of a page reads 64 bytes of each of its 16 rows;
     // bf16: wave w reads rows 8 (w % 2) .. + 7 of its page, one 128-byte line
     // of each per instruction (lanes permuted inside the line, see tile_off)
+    // fp8: instruction i fills chunks c8 = 4 i + lane / 16 of the region,
+    // chunk c8 of row r at slot 16 c8 + (r ^ 4 (c8 % 2)), so the lane loads
+    // row (lane % 16) ^ 4 ((lane / 16) % 2)
+    const int row8 = (lane & 15) ^ (((lane >> 4) & 1) << 2);
     const uint32_t lane_off =
-        FP8 ? (uint32_t)((lane & 15) * st_bytes) + 16u * (uint32_t)(lane >> 4)
+        FP8 ? (uint32_t)(row8 * st_bytes) + 16u * (uint32_t)(lane >> 4)
             : (uint32_t)((8 * (wave & 1) + (lane >> 3)) * st_bytes) + 16u * (uint32_t)((lane & 7) ^ (lane >> 3) ^ (wave & 1));
     constexpr int kGStep = FP8 ? 64 : 128;     // global bytes per instruction (into every row)
     constexpr int kLStep = FP8 ? 1024 : 2048;  // LDS bytes per instruction
@@ -342,7 +347,7 @@ void mla_verify_kernel(MlaArgs a) {
         // candidate page row / PC; a select tree over wave-uniform values (a
         // select chain over the array would become a per-lane index into
         // scratch memory)
-        const int row = FP8 ? (lane & 15) : (lane >> 3);
+        const int row = FP8 ? row8 : (lane >> 3);
         const int cand = row >> __builtin_ctz(PC);
         int v[kCand];
   #pragma unroll
@@ -400,13 +405,19 @@ void mla_verify_kernel(MlaArgs a) {
     const int vya = vcc0 ^ vrow, vyb = vcc0 ^ vrow ^ 1;
     const uint32_t vlane_off = (uint32_t)(wave * 4096 + 128 * vrow + (vcol0 & 7) * 2);
 
-    // the bf16 view of tile t: its ring slot, or its fp8 staging buffer
-    auto tile_bf16 = [&](int t) -> PD_LDS char* {
-      if constexpr (FP8)
-        return lds + kStageOff + (t & 1) * kTileBytes;
-      else
-        return lds + (t & (NS - 1)) * kRingTile;
-    };
+    // tile t as loaded: its ring slot (bf16 layout, or fp8 chunk-column-major)
+    auto tile_bf16 = [&](int t) -> PD_LDS char* { return lds + (t & (NS - 1)) * kRingTile; };
+    // FP8 chunk c8 (16 codes) of row r of a page region: slot 16 c8 + (r ^ 4 (c8 % 2))
+    auto slot8 = [](int c8, int r) { return 16 * c8 + (r ^ ((c8 & 1) << 2)); };
+    // FP8 V^T (8-bit transpose read): in a 16-lane group, lane j receives
+    // byte j % 8 of the 8 bytes addressed by lanes 2 e + (j >= 8), e = 0..7.
+    // Lane s of group (m16 = lane / 16 % 2, g = lane / 32) addresses dims
+    // 16 m16 + 8 (s % 2) .. + 7 of the block, key 8 (e / 4) + 4 g + e % 4 for
+    // e = s / 2: the key order of the P^T operand.
+    const int v8e = L16 >> 1;
+    const int v8key = 8 * (v8e >> 2) + 4 * g2 + (v8e & 3);
+    const int v8m = (lane >> 4) & 1;
+    const uint32_t v8lane_off = (uint32_t)(v8m * 256 + ((v8key ^ (v8m << 2)) << 4) + (L16 & 1) * 8);
     // P^T fragment (row group r, key step s) of tile t: 64 lanes x 16 bytes
     PD_LDS char* pbuf = lds + kPOff + lane * 16;
     auto p_slot = [&](int t, int r, int s) { return pbuf + (t & 1) * kPBufBytes + (2 * r + s) * 1024; };
@@ -433,7 +444,7 @@ void mla_verify_kernel(MlaArgs a) {
     // k-2.
     {
       PD_LDS char* z = tile_bf16(-1);
-      for (int i = tid; i < kTileBytes / 16; i += kWaves * 64) *(PD_LDS u32x4*)(z + i * 16) = u32x4{0, 0, 0, 0};
+      for (int i = tid; i < kRingTile / 16; i += kWaves * 64) *(PD_LDS u32x4*)(z + i * 16) = u32x4{0, 0, 0, 0};
       PD_LDS char* zp = lds + kPOff + ((-1) & 1) * kPBufBytes;
       for (int i = tid; i < kPBufBytes / 16; i += kWaves * 64) *(PD_LDS u32x4*)(zp + i * 16) = u32x4{0, 0, 0, 0};
     }
@@ -452,31 +463,6 @@ void mla_verify_kernel(MlaArgs a) {
       // done with iteration k-1
       __syncthreads();
       const int tok0 = (tb + k) * kTileTokens;
-      if constexpr (FP8) {
-        if (live) {
-          // exact fp8 -> bf16 into the staging buffer: item = (page, fp8
-          // chunk column c8, row r16) -> bf16 chunk columns 2 c8 and 2 c8 + 1
-          PD_LDS char* src = lds + (k & (NS - 1)) * kRingTile;
-          PD_LDS char* dst = tile_bf16(k);
-          for (int i = tid; i < 2 * 36 * 16; i += kWaves * 64) {
-            const int r16 = i & 15;
-            const int c8 = (i >> 4) % 36;
-            const int pg = i / (36 * 16);
-            const u32x4 w = *(PD_LDS u32x4*)(src + pg * kPageRegion8 + (16 * c8 + r16) * 16);
-            PD_LDS char* dpg = dst + pg * kPageRegion;
-  #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              u32x4 cv;
-              cv[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * h], 1.f, false));
-              cv[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * h], 1.f, true));
-              cv[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * h + 1], 1.f, false));
-              cv[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * h + 1], 1.f, true));
-              *(PD_LDS u32x4*)(dpg + tile_off(2 * c8 + h, r16)) = cv;
-            }
-          }
-          __syncthreads();
-        }
-      }
       PD_LDS char* tk = tile_bf16(k);       // scores of tile k
       PD_LDS char* tv = tile_bf16(k - 1);   // product of tile k-1
       if (live && tok0 + kTileTokens > hi_blk) {
@@ -485,9 +471,14 @@ void mla_verify_kernel(MlaArgs a) {
         // row there can carry a NaN into the products; a barrier orders the
         // zeros before every read of the tile.
         const int r0 = max(hi_blk - tok0, 0);
-        for (int i = tid; i < 2 * 72 * 16; i += kWaves * 64) {
-          const int r16 = i & 15, cc = (i >> 4) % 72, pg = i / (72 * 16);
-          if (16 * pg + r16 >= r0) *(PD_LDS u32x4*)(tk + pg * kPageRegion + tile_off(cc, r16)) = u32x4{0, 0, 0, 0};
+        constexpr int kChunks = FP8 ? 36 : 72;   // 16-byte chunks per row
+        for (int i = tid; i < 2 * kChunks * 16; i += kWaves * 64) {
+          const int r16 = i & 15, cc = (i >> 4) % kChunks, pg = i / (kChunks * 16);
+          if (16 * pg + r16 >= r0) {
+            PD_LDS char* zc = FP8 ? tk + pg * kPageRegion8 + slot8(cc, r16) * 16
+                                  : tk + pg * kPageRegion + tile_off(cc, r16);
+            *(PD_LDS u32x4*)zc = u32x4{0, 0, 0, 0};
+          }
         }
         __syncthreads();
       }
@@ -514,10 +505,30 @@ void mla_verify_kernel(MlaArgs a) {
       const int kr = l32 & 15, kz = g2 ^ (kr & 7) ^ (kr >> 3);
       PD_LDS char* kp = tk + (l32 >> 4) * kPageRegion + (kr >> 3) * 1024 + 128 * (kr & 7);
       auto kread = [&](int kk) { return *(PD_LDS bf16x8*)(kp + (kk >> 2) * 2048 + 16 * ((2 * (kk & 3)) ^ kz)); };
+      // FP8: 8 codes -> bf16x8, exact (scale 1: every E4M3FN value is a bf16 value)
+      auto cvt8x8 = [](uint32_t lo, uint32_t hi) {
+        const u32x4 w = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.f, false)),
+                         __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.f, true)),
+                         __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.f, false)),
+                         __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.f, true))};
+        return __builtin_bit_cast(bf16x8, w);
+      };
+      // FP8 K of step kk (dims 16 kk + 8 g2 .. + 7 of row l32): half g2 of
+      // chunk kk of row l32 % 16 in region l32 / 16 (the bf16 path's dim
+      // order, so the two paths round alike)
+      PD_LDS char* kp8 = tk + (l32 >> 4) * kPageRegion8 + g2 * 8;
+      const int kr8 = l32 & 15;
+      auto kread8 = [&](int kk) { return *(PD_LDS u32x2*)(kp8 + slot8(kk, kr8) * 16); };
       // V^T fragment of key step s (one 16-token page) and this wave's dim
       // block d: read a rows vrow.., read b rows vrow + 8.. (slot + 8)
       PD_LDS char* vbase = tv + vlane_off;
       auto vread = [&](int s, int d) {
+        if constexpr (FP8) {
+          typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
+          const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (PD_LDS i32x2*)(tv + s * kPageRegion8 + (4 * wave + d) * 512 + v8lane_off));
+          return cvt8x8((uint32_t)w[0], (uint32_t)w[1]);
+        }
         PD_LDS char* pl = vbase + s * kPageRegion + (d >> 1) * 2048;
         PD_LDS char* pa = pl + 16 * ((4 * (d & 1)) ^ vya);
         PD_LDS char* pb = pl + 1024 + 16 * ((4 * (d & 1)) ^ vyb);
@@ -532,15 +543,26 @@ void mla_verify_kernel(MlaArgs a) {
       // fragment v = 4 s + d lives in vf[v & 1]; P^T fragment (r, s) in pf[r].
       {
         bf16x8 kf[kKAhead], vf[2], pf[4];
+        u32x2 kw[kKAhead];   // FP8: raw K codes, a few steps ahead
+        if constexpr (FP8) {
   #pragma unroll
-        for (int i = 0; i < kKAhead; ++i) kf[i] = kread(i);
+          for (int i = 0; i < kKAhead; ++i) kw[i] = kread8(i);
+        } else {
+  #pragma unroll
+          for (int i = 0; i < kKAhead; ++i) kf[i] = kread(i);
+        }
         vf[0] = vread(0, 0);
         vf[1] = vread(0, 1);
   #pragma unroll
         for (int r = 0; r < 4; ++r) pf[r] = pread(r, 0);
   #pragma unroll
         for (int kk = 0; kk < kKSteps; ++kk) {
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk % kKAhead], qf[kk], sacc, 0, 0, 0);
+          if constexpr (FP8) {
+            const u32x2 w = kw[kk % kKAhead];
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cvt8x8(w[0], w[1]), qf[kk], sacc, 0, 0, 0);
+          } else {
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk % kKAhead], qf[kk], sacc, 0, 0, 0);
+          }
           if (kk < 30) {
             const int s = kk / 15, idx = kk % 15, d = idx >> 2, r = idx & 3, v = 4 * s + d;
             o[idx] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[v & 1], pf[r], o[idx], 0, 0, 0);
@@ -550,7 +572,11 @@ void mla_verify_kernel(MlaArgs a) {
             // P^T (r, 0) is done after block d = 3 (d = 2 for r = 3): fetch (r, 1)
             if (s == 0 && (d == 3 || (d == 2 && r == 3))) pf[r] = pread(r, 1);
           }
-          if (kk + kKAhead < kKSteps) kf[kk % kKAhead] = kread(kk + kKAhead);
+          if constexpr (FP8) {
+            if (kk + kKAhead < kKSteps) kw[kk % kKAhead] = kread8(kk + kKAhead);
+          } else {
+            if (kk + kKAhead < kKSteps) kf[kk % kKAhead] = kread(kk + kKAhead);
+          }
           if (kk % kLoadSpacing == 0 && kk / kLoadSpacing < kLoadsPerWave && load_next)
             load_one(tl_next, kk / kLoadSpacing);
           __builtin_amdgcn_sched_barrier(0);
