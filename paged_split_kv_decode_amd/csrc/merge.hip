@@ -7,11 +7,12 @@
 // "vllm.v1.attention.ops.triton_decode_attention" (attn_logits:
 // [rows, H, S, Lv + 1]).
 //
-// One wave per (row, head).  Lane s first reads lse_s (S <= 64 per pass) to
-// form the wave max M; then the wave walks the splits in order, each lane
-// accumulating the Lv / 64 contiguous output dims it owns, weighted by
-// w_s = 2^((lse_s - M) log2 e).  A split with lse_s = -inf is skipped (never
-// multiplied), so its O_s may hold anything.  A NaN lse_s (a partial that
+// One wave per (row, head).  Lane s reads lse_s (S <= 64 per pass) to form
+// the wave max M and the weights w_s = 2^((lse_s - M) log2 e); the splits
+// with lse_s > -inf are then gathered in batches of four, every load of a
+// batch issued before any is used, each lane accumulating the Lv / 64
+// contiguous output dims it owns.  A split with lse_s = -inf is never read
+// or multiplied, so its O_s may hold anything.  A NaN lse_s (a partial that
 // saw an invalid block-table entry) makes the result NaN.
 #include "device_common.h"
 #include "kernels.h"
@@ -35,8 +36,8 @@ __global__ __launch_bounds__(kWaves * 64) void merge_kernel(MergeArgs a) {
 
   float M = neg_inf();
   bool nan_seen = false;
-  for (int s = lane; s < S; s += 64) {
-    const float l = base[(int64_t)s * stride + a.Dv];
+  for (int s0 = 0; s0 < S; s0 += 64) {
+    const float l = s0 + lane < S ? base[(int64_t)(s0 + lane) * stride + a.Dv] : neg_inf();
     nan_seen |= l != l;
     M = fmaxf(M, l);
   }
@@ -49,16 +50,42 @@ __global__ __launch_bounds__(kWaves * 64) void merge_kernel(MergeArgs a) {
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
   float wsum = 0.f;
   const bool empty = M == neg_inf();
-  if (!empty) {
+  if (!empty && !nan_seen) {
     const float Ml = M * kLog2e;
-    for (int s = 0; s < S; ++s) {
-      const float* slot = base + (int64_t)s * stride;
-      const float l = slot[a.Dv];
-      if (l == neg_inf()) continue;
-      const float w = fast_exp2(l * kLog2e - Ml);
-      wsum += w;
+    for (int s0 = 0; s0 < S; s0 += 64) {
+      // this pass's splits: lane s holds w_{s0 + s}; the used ones as a bit mask
+      const float l = s0 + lane < S ? base[(int64_t)(s0 + lane) * stride + a.Dv] : neg_inf();
+      const float w = l == neg_inf() ? 0.f : fast_exp2(l * kLog2e - Ml);
+      uint64_t used = __ballot(l != neg_inf());
+      while (used != 0ull) {
+        // up to four used splits: all loads first, then the sums
+        int idx[4];
+        int n = 0;
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] += w * slot[lane * E + e];
+        for (int j = 0; j < 4; ++j) {
+          idx[j] = used != 0ull ? __builtin_ctzll(used) : -1;
+          if (used != 0ull) {
+            used &= used - 1;
+            ++n;
+          }
+        }
+        float v[4][E];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float* slot = base + (int64_t)(s0 + (idx[j] < 0 ? idx[0] : idx[j])) * stride + lane * E;
+#pragma unroll
+          for (int e = 0; e < E; ++e) v[j][e] = slot[e];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (j < n) {
+            const float wj = readlane(w, idx[j]);
+            wsum += wj;
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[e] += wj * v[j][e];
+          }
+        }
+      }
     }
   }
 
