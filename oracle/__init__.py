@@ -31,9 +31,11 @@ from .attention import (  # noqa: F401
     gqa_decode,
     gqa_partials,
     gqa_verify,
+    gqa_verify_varlen,
     kv_append,
     merge_partials,
     mla_verify,
     row_key_range,
+    varlen_row_requests,
     verify_num_kv_splits,
 )

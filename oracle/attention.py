@@ -33,6 +33,12 @@ Parity status per function (what pins it, see tests/test_oracle_pins.py):
                                    cache equals the bf16 cache of its
                                    dequantised values (torch's e4m3fn
                                    decoding, power-of-two per-head scales).
+* ``varlen_row_requests``          pinned: the row -> request map of the
+                                   worked varlen example (golden fixture).
+* ``gqa_verify_varlen``            pinned: equals ``gqa_verify`` bitwise when
+                                   every request has the same qlen; dense
+                                   causal brute force with per-request qlen
+                                   (0 included), window and sinks.
 * ``mla_verify``                   pinned: dense causal brute force, marker
                                    keys at the row limit, empty rows.
 * ``kv_append``                    pinned: the worked example's placement
@@ -300,6 +306,68 @@ def gqa_verify(q_bits, kv_bits, block_table, seq_lens, qlen: int, sm_scale,
 # ---------------------------------------------------------------------------
 # MLA causal verify
 # ---------------------------------------------------------------------------
+
+def varlen_row_requests(cu_seqlens_q) -> np.ndarray:
+    """Request index of every query row of a variable-length batch.
+
+    The rows of request b are ``cu_seqlens_q[b] .. cu_seqlens_q[b + 1] - 1``:
+    cumulative query lengths map each query token to its sequence ("Atención
+    paginada", Ruta Varlen, Mecanismo de indexación and its example).
+    """
+    cu = np.asarray(cu_seqlens_q, dtype=np.int64)
+    return np.repeat(np.arange(len(cu) - 1), np.diff(cu))
+
+
+def gqa_verify_varlen(q_bits, kv_bits, block_table, seq_lens, cu_seqlens_q, sm_scale,
+                      sinks=None, window: int = 0, real_seq_lens=None,
+                      kv_dtype: str = "bf16", k_scale=1.0, v_scale=1.0):
+    """Paged GQA causal verify with a query length per request, in float64.
+
+    Request b has ``qlen_b = cu_seqlens_q[b + 1] - cu_seqlens_q[b]`` query
+    tokens in rows ``cu_seqlens_q[b] + t`` ("Atención paginada", Ruta
+    Varlen: cumulative query lengths index the rows; a request may have no
+    query token).  Row t attends the keys ``row_key_range(L, qlen_b, t,
+    L_real, window)``: the verify rule of "vllm.v1.attention.ops.
+    triton_decode_attention" with the request's own qlen.  Cache, grouping,
+    sinks, window and FP8 scales as in ``gqa_verify``.
+
+    Returns ``(O [total_rows, Hq, D], LSE [total_rows, Hq])``.
+    """
+    q = bf16_bits_to_f64(q_bits)
+    kv = np.asarray(kv_bits)
+    rows, Hq, D = q.shape
+    _, Hkv, P, two_d = kv.shape
+    cu = np.asarray(cu_seqlens_q, dtype=np.int64)
+    assert two_d == 2 * D and Hq % Hkv == 0 and cu[-1] == rows and np.all(np.diff(cu) >= 0)
+    G = Hq // Hkv
+    ks = np.broadcast_to(np.asarray(k_scale, np.float64), (Hkv,))
+    vs = np.broadcast_to(np.asarray(v_scale, np.float64), (Hkv,))
+    O = np.zeros((rows, Hq, D))
+    lse = np.full((rows, Hq), -np.inf)
+    for b in range(len(cu) - 1):
+        L = int(seq_lens[b])
+        L_real = None if real_seq_lens is None else int(real_seq_lens[b])
+        n = int(cu[b + 1] - cu[b])
+        for t in range(n):
+            r = int(cu[b]) + t
+            lo, hi = row_key_range(L, n, t, L_real, window)
+            pages, slots = _gather_positions(block_table[b], np.arange(lo, hi), P)
+            for kvh in range(Hkv):
+                raw = kv[pages, kvh, slots, :]
+                if kv_dtype == "bf16":
+                    kvrows = bf16_bits_to_f64(raw)
+                elif kv_dtype == "fp8_e4m3fn":
+                    kvrows = fp8_bits_to_f64(raw)
+                    kvrows[:, :D] *= ks[kvh]
+                    kvrows[:, D:] *= vs[kvh]
+                else:
+                    raise ValueError(kv_dtype)
+                hs = slice(kvh * G, (kvh + 1) * G)
+                sk = None if sinks is None else np.asarray(sinks, np.float64)[hs]
+                O[r, hs], lse[r, hs] = attend(q[r, hs], kvrows[:, :D], kvrows[:, D:],
+                                              sm_scale, sk)
+    return O, lse
+
 
 def mla_verify(q_bits, kv, block_table, seq_lens, real_seq_lens, qlen: int,
                sm_scale: float, Lv: int, kv_dtype: str = "bf16",

@@ -529,6 +529,60 @@ def test_mla_3d_cache_view_is_the_same_cache():
 
 
 # ---------------------------------------------------------------------------
+# variable query length per request ("Atención paginada", Ruta Varlen)
+# ---------------------------------------------------------------------------
+
+def test_varlen_row_requests_worked_example():
+    ex = json.load(open(os.path.join(GOLDEN, "worked_example_varlen.json")))
+    cu = np.concatenate([[0], np.cumsum(ex["query_lengths"])])
+    assert list(cu) == ex["cu_seq_lens_q"]
+    assert list(oracle.varlen_row_requests(ex["cu_seq_lens_q"])) == ex["q_request_index"]
+    assert max(np.diff(cu)) == ex["max_length_q"]
+
+
+def test_gqa_verify_varlen_uniform_qlen_is_verify():
+    rng = np.random.default_rng(90)
+    lens, qlen = [11, 6, 0, 30], 3
+    q, kv, bt, sl, sk = _rand_gqa_verify(rng, lens, qlen, 4, 2, 8, 4)
+    cu = np.arange(len(lens) + 1) * qlen
+    for window in (0, 5):
+        a = oracle.gqa_verify(q, kv, bt, sl, qlen, 0.3, sinks=sk, window=window,
+                              real_seq_lens=np.array([10, 6, 0, 29]))
+        b = oracle.gqa_verify_varlen(q, kv, bt, sl, cu, 0.3, sinks=sk, window=window,
+                                     real_seq_lens=np.array([10, 6, 0, 29]))
+        np.testing.assert_array_equal(a[0], b[0])
+        np.testing.assert_array_equal(a[1], b[1])
+
+
+def test_gqa_verify_varlen_matches_causal_dense_brute_force():
+    """Per-request query lengths [2, 0, 4, 1] (the second request has no
+    query row): row t of request b sees keys 0 .. L - qlen_b + t, the last
+    W of them, through the block table."""
+    rng = np.random.default_rng(91)
+    lens, qlens, Hq, Hkv, D, P, W = [9, 5, 13, 3], [2, 0, 4, 1], 4, 2, 8, 4, 6
+    q1, kv, bt, sl, sk = _rand_gqa(rng, len(lens), Hq, Hkv, D, P, lens, sinks=True)
+    cu = np.concatenate([[0], np.cumsum(qlens)])
+    q = _bf16(rng.standard_normal((int(cu[-1]), Hq, D)))
+    O, lse = oracle.gqa_verify_varlen(q, kv, bt, sl, cu, 0.3, sinks=sk, window=W)
+    qf = oa.bf16_bits_to_f64(q)
+    req = oracle.varlen_row_requests(cu)
+    for r in range(int(cu[-1])):
+        b = int(req[r])
+        t = r - int(cu[b])
+        L = lens[b]
+        rows = np.stack([oa.bf16_bits_to_f64(kv[bt[b, j // P], :, j % P, :]) for j in range(L)])
+        last = L - qlens[b] + t          # the token's own position
+        for kvh in range(Hkv):
+            hs = slice(2 * kvh, 2 * kvh + 2)
+            mask = np.zeros((2, L), bool)
+            mask[:, max(last + 1 - W, 0):max(last + 1, 0)] = True
+            O2, lse2 = _loop_attention(qf[r, hs], rows[:, kvh, :D], rows[:, kvh, D:], 0.3,
+                                       mask, sk[hs])
+            np.testing.assert_allclose(O[r, hs], O2, atol=1e-13, rtol=0)
+            np.testing.assert_allclose(lse[r, hs], lse2, atol=1e-13, rtol=0)
+
+
+# ---------------------------------------------------------------------------
 # general page sizes ("vllm.v1.attention.ops.triton_decode_attention": the
 # module supports any page size >= 1)
 # ---------------------------------------------------------------------------
@@ -798,6 +852,14 @@ def test_mutant_fixed_page_size_is_caught(monkeypatch):
     assert _fails(test_gqa_verify_brute_force_at_page_size, 1)
     assert _fails(test_gqa_verify_brute_force_at_page_size, 64)
     assert _fails(test_mla_brute_force_at_page_size, 3)
+
+
+def test_mutant_uniform_qlen_in_varlen_is_caught(monkeypatch):
+    """A varlen oracle that used the batch's largest qlen for every request."""
+    orig = oa.row_key_range
+    monkeypatch.setattr(oa, "row_key_range", lambda L, qlen=1, t=0, real_len=None, window=0:
+                        orig(L, 4, t, real_len, window))
+    assert _fails(test_gqa_verify_varlen_matches_causal_dense_brute_force)
 
 
 def test_mutant_sink_omitted_is_caught(monkeypatch):
