@@ -10,7 +10,8 @@ Printed: ONE JSON line with KV-read GB/s (algorithmic K+V bytes of the
 attended keys / time per call), the roofline of the dominant kernel measured
 with HIP events on the launch stream, and the fp64 CPU oracle's rate on the
 same inputs.  ``--config`` selects another workload (gqa_window, gqa_skewed,
-tiny_gqa, gqa_verify, gqa_sinks_fp8, kv_append, mla_verify, mla_verify_fp8).
+tiny_gqa, gqa_verify, gqa_verify_varlen, gqa_sinks_fp8, kv_append, mla_verify,
+mla_verify_fp8).
 """
 
 from __future__ import annotations
@@ -116,6 +117,45 @@ def _gqa_case(name, torch, pd, splits, page_size=0):
     return dict(w=w, vals=vals, S=S, step=step, kernel=kernel_only, rest=rest,
                 kv_bytes=w.kv_bytes(), flops=w.flops(), desc=desc, kind="gqa",
                 kernel_name="gqa_decode_kernel")
+
+
+def _varlen_case(torch, pd, splits, page_size=0):
+    """The GQA verify config with a query length per request, U{1, 2}
+    (seeded), rows indexed by cumulative query lengths."""
+    from synth import gqa_workload
+
+    w = gqa_workload("gqa_verify", page_size=page_size, pool="tight") if page_size else \
+        gqa_workload("gqa_verify")
+    vals = w.values("cuda", poison=False)
+    rng = np.random.default_rng(2016)
+    qlens = rng.integers(1, w.qlen + 1, size=w.B)
+    cu = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    rows = np.concatenate([b * w.qlen + np.arange(n) for b, n in enumerate(qlens)])
+    q = vals["q"][torch.from_numpy(rows).cuda()].contiguous()
+    bt = torch.from_numpy(w.block_table).cuda()
+    sl = torch.from_numpy(w.seq_lens).cuda()
+    real = torch.from_numpy(w.real_seq_lens).cuda()
+    cu_d = torch.from_numpy(cu).cuda()
+    S = splits or pd.gqa_split_cap(w.B, w.Hkv, int(w.seq_lens.max()), w.window)
+    total = int(cu[-1])
+    out = torch.empty((total, w.Hq, w.D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((total, w.Hq), dtype=torch.float32, device="cuda")
+    ws = pd.alloc_workspace(total, w.Hq, max(S, 2), w.D, "cuda")
+
+    def step():
+        pd.paged_verify_gqa_varlen(q, vals["kv"], bt, sl, cu_d, w.qlen, w.sm_scale,
+                                   sinks=vals["sinks"], window=w.window, real_seq_lens=real,
+                                   num_kv_splits=S, workspace=ws, out=out, lse=lse)
+
+    # keys of request b: rows t < n_b see [0, min(L, L_real)) at most (no window)
+    keys = sum(max(min(int(L), int(Lr)), 0) for L, Lr in zip(w.seq_lens, w.real_seq_lens))
+    desc = (f"GQA causal verify, variable query length U{{1,2}} per request (cumulative query "
+            f"lengths, {total} rows): B={w.B}, Hq={w.Hq}, Hkv={w.Hkv}, D={w.D}, page {w.P} HND "
+            f"bf16, seq_lens U[1024,8192], real length L - U{{0,1}}")
+    return dict(w=w, vals=vals, S=S, step=step, kernel=None, rest=None,
+                kv_bytes=keys * w.Hkv * 2 * w.D * 2, flops=w.flops(), desc=desc,
+                kind="gqa_varlen", kernel_name="gqa_decode_kernel",
+                extra=dict(q=q, cu=cu, qlens=qlens))
 
 
 def _append_case(torch, pd):
@@ -252,6 +292,16 @@ def _cpu_baseline(case, budget_s=20.0):
             t_total += time.perf_counter() - t0
             lo = max(int(w.seq_lens[b]) - w.window, 0) if w.window > 0 else 0
             done_bytes += (int(w.seq_lens[b]) - lo) * w.Hkv * 2 * w.D * 2
+        elif case["kind"] == "gqa_varlen":
+            cu, qlens = case["extra"]["cu"], case["extra"]["qlens"]
+            q = case["extra"]["q"][int(cu[b]):int(cu[b + 1])].view(torch.int16).cpu().numpy()
+            sinks = None if vals["sinks"] is None else vals["sinks"].cpu().numpy()
+            t0 = time.perf_counter()
+            oracle.gqa_verify_varlen(q.view(np.uint16), kv, bt2, w.seq_lens[b:b + 1],
+                                     np.array([0, int(qlens[b])]), w.sm_scale, sinks=sinks,
+                                     window=w.window, real_seq_lens=w.real_seq_lens[b:b + 1])
+            t_total += time.perf_counter() - t0
+            done_bytes += max(min(int(w.seq_lens[b]), int(w.real_seq_lens[b])), 0) * w.Hkv * 2 * w.D * 2
         elif case["kind"] in ("gqa_verify", "gqa_fp8"):
             fp8 = case["kind"] == "gqa_fp8"
             rows = slice(b * w.qlen, (b + 1) * w.qlen)
@@ -311,6 +361,10 @@ def main():
             name = f"{name}_p{args.page_size}"
     elif name == "kv_append":
         case = _append_case(torch, pd)
+    elif name == "gqa_verify_varlen":
+        case = _varlen_case(torch, pd, args.splits, args.page_size)
+        if args.page_size:
+            name = f"{name}_p{args.page_size}"
     else:
         case = _gqa_case(name, torch, pd, args.splits, args.page_size)
         if args.page_size:
@@ -378,7 +432,7 @@ def main():
 
     kv = case["kv_bytes"]
     value = kv / (ms_per_step * 1e-3) / 1e9
-    if case["kind"] in ("gqa", "gqa_verify", "gqa_fp8", "append"):
+    if case["kind"] in ("gqa", "gqa_verify", "gqa_fp8", "gqa_varlen", "append"):
         roof = {"bound": "hbm", "achieved": round(kv / (k_ms * 1e-3) / 1e9, 2),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     else:

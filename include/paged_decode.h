@@ -223,6 +223,43 @@ PD_API int paged_verify_gqa(const void* q, int64_t q_stride_row, int64_t q_strid
                      float* lse, int64_t lse_stride_row, void* stream);
 
 /*
+ * paged_verify_gqa_varlen - paged GQA causal verify with a query length per
+ * request.
+ *
+ * Defined by "Atención paginada", section Ruta Varlen (cumulative query
+ * lengths map each query token to its sequence; a sequence may have none)
+ * with the verify rule of paged_verify_gqa applied per request: request b
+ * has qlen_b = cu_seqlens_q[b+1] - cu_seqlens_q[b] query tokens in rows
+ * cu_seqlens_q[b] + t, and row t attends the keys below
+ * hi = max(min(L - qlen_b + 1 + t, L_real), 0), the last `window` of them.
+ *
+ * cu_seqlens_q [B+1] int32 on the device: cu[0] = 0, non-decreasing,
+ *              cu[B] = total_rows.
+ * max_qlen     host int >= every qlen_b; max_qlen * (Hq / Hkv) <= 16 (one
+ *              score tile holds a kv head's rows).  Rows of a request past
+ *              max_qlen are not computed (their output is unspecified).
+ * total_rows   host int: rows of q, out and lse; 0 is a no-op.
+ * q, out, lse  [total_rows, Hq, D] / [total_rows, Hq]; workspace
+ *              >= pd_workspace_bytes(total_rows, Hq, S, D) bytes when S > 1.
+ * Other arguments as for paged_verify_gqa.  cu_seqlens_q is read on the
+ * device only, so the call stays graph-capture safe.  Returns
+ * PD_ERR_INVALID for a NULL cu_seqlens_q (B > 0) or total_rows < 0.
+ */
+PD_API int paged_verify_gqa_varlen(const void* q, int64_t q_stride_row, int64_t q_stride_h,
+                     const void* kv, int32_t kv_dtype, const float* k_scale,
+                     const float* v_scale, int32_t scale_per_head,
+                     int64_t kv_stride_page, int64_t kv_stride_head,
+                     int32_t num_pages, const int32_t* block_table, int64_t bt_stride_b,
+                     int32_t max_blocks, const int32_t* seq_lens,
+                     const int32_t* real_seq_lens, const int32_t* cu_seqlens_q,
+                     int32_t max_qlen, int32_t total_rows, const float* sinks,
+                     int32_t window, float sm_scale, int32_t batch, int32_t num_q_heads,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                     int32_t num_kv_splits, float* workspace, size_t workspace_bytes,
+                     void* out, int64_t o_stride_row, int64_t o_stride_h,
+                     float* lse, int64_t lse_stride_row, void* stream);
+
+/*
  * paged_decode_gqa_partials - the split partials of paged_decode_gqa only.
  *
  * Same arguments and key ranges as paged_decode_gqa (no sinks, no outputs):

@@ -27,6 +27,7 @@ EXPORTS = (
     "pd_workspace_bytes",
     "paged_decode_gqa",
     "paged_verify_gqa",
+    "paged_verify_gqa_varlen",
     "paged_decode_gqa_partials",
     "paged_kv_append",
     "paged_verify_mla",
@@ -81,6 +82,20 @@ def _load():
         _c_vp, _c_i64, _c_vp,                   # lse, stride, stream
     ]
     lib.paged_verify_gqa.restype = ctypes.c_int
+    lib.paged_verify_gqa_varlen.argtypes = [
+        _c_vp, _c_i64, _c_i64,                  # q, strides
+        _c_vp, _c_i32, _c_vp, _c_vp, _c_i32,    # kv, kv_dtype, k_scale, v_scale, per-head flag
+        _c_i64, _c_i64, _c_i32,                 # kv page/head strides, num_pages
+        _c_vp, _c_i64, _c_i32,                  # block_table, row stride, max_blocks
+        _c_vp, _c_vp,                           # seq_lens, real_seq_lens
+        _c_vp, _c_i32, _c_i32,                  # cu_seqlens_q, max_qlen, total_rows
+        _c_vp, _c_i32, _c_f32,                  # sinks, window, sm_scale
+        _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,  # B, Hq, Hkv, D, P
+        _c_i32, _c_vp, _c_sz,                   # splits, workspace, bytes
+        _c_vp, _c_i64, _c_i64,                  # out, strides
+        _c_vp, _c_i64, _c_vp,                   # lse, stride, stream
+    ]
+    lib.paged_verify_gqa_varlen.restype = ctypes.c_int
     lib.paged_kv_append.argtypes = [
         _c_vp, _c_i64, _c_i64, _c_i32,          # src0, strides, elems
         _c_vp, _c_i64, _c_i64, _c_i32,          # src1, strides, elems

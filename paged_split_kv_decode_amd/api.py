@@ -151,6 +151,44 @@ def paged_verify_gqa(q, kv, block_table, seq_lens, qlen, sm_scale, sinks=None, w
     sinks [Hq] fp32 or None.
     Returns (out [B*qlen, Hq, D] bf16, lse [B*qlen, Hq] fp32 or None).
     """
+    qlen = int(qlen)
+    rows = q.shape[0] if q.dim() == 3 else -1
+    if qlen < 1 or rows % qlen != 0:
+        raise ValueError("q must have qlen rows per request")
+    return _verify_gqa(q, kv, block_table, seq_lens, rows // qlen, qlen, None, sm_scale, sinks,
+                       window, real_seq_lens, num_kv_splits, workspace, out, lse, stream,
+                       return_lse, k_scale, v_scale)
+
+
+def paged_verify_gqa_varlen(q, kv, block_table, seq_lens, cu_seqlens_q, max_qlen, sm_scale,
+                            sinks=None, window=0, real_seq_lens=None, num_kv_splits=1,
+                            workspace=None, out=None, lse=None, stream=None, return_lse=True,
+                            k_scale=None, v_scale=None):
+    """Paged GQA causal verify with a query length per request
+    (include/paged_decode.h: paged_verify_gqa_varlen).
+
+    q [total_rows, Hq, D] bf16 with request b's query tokens in rows
+    cu_seqlens_q[b] .. cu_seqlens_q[b + 1] - 1; cu_seqlens_q [B + 1] int32 on
+    the device (cu[0] = 0, non-decreasing, cu[B] = total_rows); max_qlen a
+    host int >= every request's query length, with max_qlen * Hq / Hkv <= 16.
+    Other arguments as for paged_verify_gqa.
+    Returns (out [total_rows, Hq, D] bf16, lse [total_rows, Hq] fp32 or None).
+    """
+    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1)
+    B = seq_lens.shape[0]
+    if cu_seqlens_q.shape[0] != B + 1 or cu_seqlens_q.stride(0) != 1:
+        raise ValueError("cu_seqlens_q must be a contiguous [B + 1] tensor")
+    max_qlen = int(max_qlen)
+    if max_qlen < 1:
+        raise ValueError("max_qlen must be >= 1")
+    return _verify_gqa(q, kv, block_table, seq_lens, B, max_qlen, cu_seqlens_q, sm_scale, sinks,
+                       window, real_seq_lens, num_kv_splits, workspace, out, lse, stream,
+                       return_lse, k_scale, v_scale)
+
+
+def _verify_gqa(q, kv, block_table, seq_lens, B, qlen, cu_seqlens_q, sm_scale, sinks, window,
+                real_seq_lens, num_kv_splits, workspace, out, lse, stream, return_lse, k_scale,
+                v_scale):
     _need(q, "q", torch.bfloat16, 3)
     fp8 = kv.dtype in (torch.uint8, torch.float8_e4m3fn)
     if not fp8:
@@ -159,11 +197,7 @@ def paged_verify_gqa(q, kv, block_table, seq_lens, qlen, sm_scale, sinks=None, w
         raise ValueError("kv must be a 4-D device tensor")
     _need(block_table, "block_table", torch.int32, 2)
     _need(seq_lens, "seq_lens", torch.int32, 1)
-    qlen = int(qlen)
     rows, Hq, D = q.shape
-    if qlen < 1 or rows % qlen != 0:
-        raise ValueError("q must have qlen rows per request")
-    B = rows // qlen
     num_pages, Hkv, P, two_d = kv.shape
     if two_d != 2 * D or kv.stride(3) != 1 or kv.stride(2) != 2 * D or q.stride(2) != 1:
         raise ValueError("kv must be [pages, Hkv, P, 2D] with contiguous token rows")
@@ -203,17 +237,21 @@ def paged_verify_gqa(q, kv, block_table, seq_lens, qlen, sm_scale, sinks=None, w
     if S > 1 and workspace is None:
         workspace = alloc_workspace(rows, Hq, S, D, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib.paged_verify_gqa(
-        _ptr(q), q.stride(0), q.stride(1),
-        _ptr(kv), PD_KV_FP8_E4M3FN if fp8 else PD_KV_BF16, _ptr(k_scale), _ptr(v_scale), per_head,
-        kv.stride(0), kv.stride(1), num_pages,
-        _ptr(block_table), block_table.stride(0), block_table.shape[1],
-        _ptr(seq_lens), _ptr(real_seq_lens), qlen,
-        _ptr(sinks), int(window or 0), float(sm_scale),
-        B, Hq, Hkv, D, P, S, _ptr(workspace), ws_bytes,
-        _ptr(out), out.stride(0), out.stride(1),
-        _ptr(lse), 0 if lse is None else lse.stride(0), _stream(stream))
-    check("paged_verify_gqa", st)
+    common = (_ptr(q), q.stride(0), q.stride(1),
+              _ptr(kv), PD_KV_FP8_E4M3FN if fp8 else PD_KV_BF16, _ptr(k_scale), _ptr(v_scale),
+              per_head, kv.stride(0), kv.stride(1), num_pages,
+              _ptr(block_table), block_table.stride(0), block_table.shape[1],
+              _ptr(seq_lens), _ptr(real_seq_lens))
+    tail_args = (_ptr(sinks), int(window or 0), float(sm_scale),
+                 B, Hq, Hkv, D, P, S, _ptr(workspace), ws_bytes,
+                 _ptr(out), out.stride(0), out.stride(1),
+                 _ptr(lse), 0 if lse is None else lse.stride(0), _stream(stream))
+    if cu_seqlens_q is None:
+        st = lib.paged_verify_gqa(*common, qlen, *tail_args)
+        check("paged_verify_gqa", st)
+    else:
+        st = lib.paged_verify_gqa_varlen(*common, _ptr(cu_seqlens_q), qlen, rows, *tail_args)
+        check("paged_verify_gqa_varlen", st)
     return out, lse
 
 

@@ -109,7 +109,8 @@ static int gqa_common(const void* q, int64_t q_stride_b, int64_t q_stride_h, con
                int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                int32_t page_size, int32_t num_kv_splits, float* workspace,
                size_t workspace_bytes, void* out, int64_t o_stride_b, int64_t o_stride_h,
-               float* lse, int64_t lse_stride_b, void* stream, bool partials_only) {
+               float* lse, int64_t lse_stride_b, void* stream, bool partials_only,
+               const int32_t* cu_seqlens_q = nullptr, int32_t total_rows = -1) {
   if (batch < 0 || qlen < 1 || num_q_heads < 1 || num_kv_heads < 1 || num_kv_splits < 1 ||
       num_pages < 0 || max_blocks < 0 || !std::isfinite(sm_scale) || !(sm_scale > 0.f))
     return PD_ERR_INVALID;
@@ -134,7 +135,8 @@ static int gqa_common(const void* q, int64_t q_stride_b, int64_t q_stride_h, con
       kv_stride_page % kv_align || kv_stride_head % kv_align)
     return PD_ERR_ALIGN;
   if (!partials_only && (!aligned16(out) || o_stride_b % 8 || o_stride_h % 8)) return PD_ERR_ALIGN;
-  const int64_t rows = (int64_t)batch * qlen;
+  if (cu_seqlens_q != nullptr && total_rows < 0) return PD_ERR_INVALID;
+  const int64_t rows = cu_seqlens_q != nullptr ? (int64_t)total_rows : (int64_t)batch * qlen;
   if (rows > 0x7fffffff) return PD_ERR_UNSUPPORTED;
   if (num_kv_splits > 1 || partials_only) {
     const int32_t ws_splits = num_kv_splits > 1 ? num_kv_splits : 2;
@@ -170,6 +172,8 @@ static int gqa_common(const void* q, int64_t q_stride_b, int64_t q_stride_h, con
   a.seq_lens = seq_lens;
   a.real_lens = real_seq_lens;
   a.qlen = qlen;
+  a.cu_q = cu_seqlens_q;
+  a.total_rows = (int32_t)rows;
   a.kv_fp8 = fp8 ? 1 : 0;
   a.k_scale = fp8 ? k_scale : nullptr;
   a.v_scale = fp8 ? v_scale : nullptr;
@@ -246,6 +250,29 @@ int paged_verify_gqa(const void* q, int64_t q_stride_row, int64_t q_stride_h, co
                     window, sm_scale, batch, num_q_heads, num_kv_heads, head_dim, page_size,
                     num_kv_splits, workspace, workspace_bytes, out, o_stride_row, o_stride_h,
                     lse, lse_stride_row, stream, false);
+}
+
+int paged_verify_gqa_varlen(const void* q, int64_t q_stride_row, int64_t q_stride_h,
+                            const void* kv, int32_t kv_dtype, const float* k_scale,
+                            const float* v_scale, int32_t scale_per_head,
+                            int64_t kv_stride_page, int64_t kv_stride_head, int32_t num_pages,
+                            const int32_t* block_table, int64_t bt_stride_b, int32_t max_blocks,
+                            const int32_t* seq_lens, const int32_t* real_seq_lens,
+                            const int32_t* cu_seqlens_q, int32_t max_qlen, int32_t total_rows,
+                            const float* sinks, int32_t window, float sm_scale, int32_t batch,
+                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t page_size, int32_t num_kv_splits, float* workspace,
+                            size_t workspace_bytes, void* out, int64_t o_stride_row,
+                            int64_t o_stride_h, float* lse, int64_t lse_stride_row, void* stream) {
+  if (cu_seqlens_q == nullptr && batch > 0) return PD_ERR_INVALID;
+  if (total_rows < 0) return PD_ERR_INVALID;
+  if (batch > 0 && total_rows == 0) return PD_OK;   // no query row at all
+  return gqa_common(q, q_stride_row, q_stride_h, kv, kv_dtype, k_scale, v_scale,
+                    scale_per_head, kv_stride_page, kv_stride_head, num_pages,
+                    block_table, bt_stride_b, max_blocks, seq_lens, real_seq_lens, max_qlen,
+                    sinks, window, sm_scale, batch, num_q_heads, num_kv_heads, head_dim,
+                    page_size, num_kv_splits, workspace, workspace_bytes, out, o_stride_row,
+                    o_stride_h, lse, lse_stride_row, stream, false, cu_seqlens_q, total_rows);
 }
 
 int paged_decode_gqa_partials(const void* q, int64_t q_stride_b, int64_t q_stride_h,

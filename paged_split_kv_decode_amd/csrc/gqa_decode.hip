@@ -32,7 +32,7 @@ static int grid_size() {
 hipError_t launch_gqa_decode(const GqaArgs& a, hipStream_t stream) {
   const int n = grid_size();
   if (n <= 0) return hipErrorInvalidDevice;
-  const bool verify = a.qlen > 1 || a.real_lens != nullptr;
+  const bool verify = a.qlen > 1 || a.real_lens != nullptr || a.cu_q != nullptr;
   if (a.P <= 0 || (a.P & (a.P - 1)) != 0 || (1 << a.p_shift) != a.P) return hipErrorInvalidValue;
   switch (a.P) {
     case 1: return launch_gqa_class<1>(a, verify, n, stream);

@@ -82,38 +82,61 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 // Key range of one request: positions [lo, hi), tiles lo / 32 ... lo / 32 + nt - 1.
 struct Req {
   int lo, hi, nt;
+  int n, row0;   // query rows of the request: n tokens from row row0
 };
 
 // Length bound standing for "no real length given".
 constexpr int kNoReal = 1 << 30;
 
-// Key range of verify row t of a request of length L (clamped to the
-// block-table row) and real length Lr: [lo_t, hi_t) with
-// hi_t = max(min(L - qlen + 1 + t, Lr), 0) and, with a window,
+// Key range of verify row t of a request with n query tokens, length L
+// (clamped to the block-table row) and real length Lr: [lo_t, hi_t) with
+// hi_t = max(min(L - n + 1 + t, Lr), 0) and, with a window,
 // lo_t = max(hi_t - window, 0).
-__device__ __forceinline__ int row_hi(const GqaArgs& a, int L, int Lr, int t) {
+__device__ __forceinline__ int row_hi(const GqaArgs& a, int L, int Lr, int t, int n) {
   L = min(max(L, 0), a.max_blocks * a.P);
-  return max(min(L - a.qlen + 1 + t, Lr), 0);
+  return max(min(L - n + 1 + t, Lr), 0);
 }
 __device__ __forceinline__ int row_lo(const GqaArgs& a, int hi) {
   return a.window > 0 ? max(hi - a.window, 0) : 0;
 }
 
-// Keys of a request: the union of its rows' ranges, [lo_0, hi_{qlen-1}).
-__device__ __forceinline__ Req range_of(const GqaArgs& a, int L, int Lr) {
+// Keys of a request with n >= 0 query tokens: the union of its rows'
+// ranges, [lo_0, hi_{n-1}) (none for n = 0).
+__device__ __forceinline__ Req range_of(const GqaArgs& a, int L, int Lr, int n) {
   Req r;
-  r.hi = row_hi(a, L, Lr, a.qlen - 1);
-  r.lo = row_lo(a, row_hi(a, L, Lr, 0));
+  r.n = n;
+  r.row0 = 0;
+  r.hi = n > 0 ? row_hi(a, L, Lr, n - 1, n) : 0;
+  r.lo = row_lo(a, row_hi(a, L, Lr, 0, n));
   r.nt = r.hi > r.lo ? ((r.hi + 31) >> 5) - (r.lo >> 5) : 0;
   return r;
+}
+
+// Query rows of request b: rows row0 .. row0 + n - 1.  Uniform: b * qlen and
+// qlen.  Variable ("cumulative query lengths"): cu_q[b] .. cu_q[b + 1] - 1,
+// clamped to [0, total_rows) and to at most qlen rows (the column bound).
+struct QRows {
+  int row0, n;
+};
+__device__ __forceinline__ QRows query_rows(const GqaArgs& a, int b) {
+  if (a.cu_q == nullptr) return QRows{b * a.qlen, a.qlen};
+  const int r0 = min(max((int)as_const(a.cu_q)[b], 0), a.total_rows);
+  const int r1 = min(max((int)as_const(a.cu_q)[b + 1], r0), a.total_rows);
+  return QRows{r0, min(r1 - r0, a.qlen)};
 }
 
 __device__ __forceinline__ int real_len(const GqaArgs& a, int b) {
   return a.real_lens != nullptr ? (int)as_const(a.real_lens)[b] : kNoReal;
 }
 
+// V: the verify instantiation (query rows from query_rows); decode: one
+// query row per request, row b.
+template <bool V>
 __device__ __forceinline__ Req request_range(const GqaArgs& a, int b) {
-  return range_of(a, as_const(a.seq_lens)[b], real_len(a, b));
+  const QRows qr = V ? query_rows(a, b) : QRows{b, 1};
+  Req r = range_of(a, as_const(a.seq_lens)[b], real_len(a, b), qr.n);
+  r.row0 = qr.row0;
+  return r;
 }
 
 // A position in one wave's tile sequence (wave-uniform).  b == B: the share
@@ -154,7 +177,9 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
   const int g4 = lane >> 4;
   const int l16 = lane & 15;
   const int G = a.G;
-  const int R = V ? a.qlen * G : G;   // columns in use: (verify token, head) pairs
+  // columns in use: (verify token, head) pairs of the current piece (verify:
+  // n * G for a request with n query rows; decode: the G heads)
+  int R = G;
   const int S = a.S;
   const int Hkv = a.Hkv;
   const bool direct = S == 1 && !a.partials;
@@ -165,27 +190,27 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
   PD_LDS char* ring = (PD_LDS char*)smem + wave_in_wg * kWaveLds;
   PD_LDS char* qslots = ring + kRingBytes;
   // this lane's score column: verify token t_col, head g_col of the kv head
-  const int t_col = V ? min(l16, R - 1) / G : 0;
-  const int g_col = V ? min(l16, R - 1) - t_col * G : l16;
+  int t_col = 0, g_col = l16;
 
   // ---- the plan: total tiles, longest request, this wave's share --------
   // Lane l of chunk c holds the length of request 64c + l (0 past the batch).
-  int Lc[kCachedChunks], Lrc[kCachedChunks];
+  int Lc[kCachedChunks], Lrc[kCachedChunks], Nc[kCachedChunks];
 #pragma unroll
   for (int ch = 0; ch < kCachedChunks; ++ch) {
     const int b = 64 * ch + lane;
     Lc[ch] = b < a.B ? as_const(a.seq_lens)[b] : 0;
     Lrc[ch] = b < a.B ? real_len(a, b) : 0;
+    Nc[ch] = b < a.B ? (V ? query_rows(a, b).n : 1) : 0;
   }
   int nt_sum = 0, nt_max = 0;
 #pragma unroll
   for (int ch = 0; ch < kCachedChunks; ++ch) {
-    const int nt = range_of(a, Lc[ch], Lrc[ch]).nt;
+    const int nt = range_of(a, Lc[ch], Lrc[ch], Nc[ch]).nt;
     nt_sum += wave_sum(nt);
     nt_max = max(nt_max, wave_max(nt));
   }
   for (int base = 64 * kCachedChunks; base < a.B; base += 64) {
-    const int nt = base + lane < a.B ? request_range(a, base + lane).nt : 0;
+    const int nt = base + lane < a.B ? request_range<V>(a, base + lane).nt : 0;
     nt_sum += wave_sum(nt);
     nt_max = max(nt_max, wave_max(nt));
   }
@@ -208,12 +233,12 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
   // ---- first unit of the share ------------------------------------------
   // split: the unit holding tile g0, or an empty unit starting at or after
   // g0; whole units: the first unit starting at or after g0.
-  int b_s = -1, L_s = 0, Lr_s = 0, cb_s = 0;
+  int b_s = -1, L_s = 0, Lr_s = 0, N_s = 0, cb_s = 0;
   {
     int C = 0;  // tiles of the requests before this chunk (one kv head)
-    auto probe = [&](int base, int L, int Lr) {
+    auto probe = [&](int base, int L, int Lr, int N) {
       const bool in = base + lane < a.B;
-      const int nt = range_of(a, L, Lr).nt;
+      const int nt = range_of(a, L, Lr, N).nt;
       const int incl = wave_incl_sum(nt);
       const int cb1 = (C + incl) * Hkv;     // flat start of request b + 1
       const int cb = cb1 - nt * Hkv;         // flat start of request b
@@ -225,6 +250,7 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
         b_s = base + l0;
         L_s = __builtin_amdgcn_readlane(L, l0);
         Lr_s = __builtin_amdgcn_readlane(Lr, l0);
+        N_s = __builtin_amdgcn_readlane(N, l0);
         cb_s = __builtin_amdgcn_readlane(cb, l0);
         return true;
       }
@@ -234,15 +260,17 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
     bool found = false;
 #pragma unroll
     for (int ch = 0; ch < kCachedChunks; ++ch)
-      if (!found && 64 * ch < a.B) found = probe(64 * ch, Lc[ch], Lrc[ch]);
+      if (!found && 64 * ch < a.B) found = probe(64 * ch, Lc[ch], Lrc[ch], Nc[ch]);
     for (int base = 64 * kCachedChunks; !found && base < a.B; base += 64) {
       const bool in = base + lane < a.B;
-      found = probe(base, in ? as_const(a.seq_lens)[base + lane] : 0, in ? real_len(a, base + lane) : 0);
+      found = probe(base, in ? as_const(a.seq_lens)[base + lane] : 0, in ? real_len(a, base + lane) : 0,
+                    in ? (V ? query_rows(a, base + lane).n : 1) : 0);
     }
   }
   if (b_s < 0) return;
   b_s = uniform(b_s);
-  const Req r_s = range_of(a, uniform(L_s), uniform(Lr_s));
+  Req r_s = range_of(a, uniform(L_s), uniform(Lr_s), uniform(N_s));
+  r_s.row0 = uniform(V ? query_rows(a, b_s).row0 : b_s);
   int kvh_s = 0;
   if (sh.g0 > cb_s)
     kvh_s = sh.split ? (sh.g0 - cb_s) / r_s.nt : (sh.g0 - cb_s + r_s.nt - 1) / r_s.nt;
@@ -257,7 +285,7 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
     } else {
       cu.kvh = 0;
       ++cu.b;
-      if (cu.b < a.B) cu.r = request_range(a, cu.b);
+      if (cu.b < a.B) cu.r = request_range<V>(a, cu.b);
     }
   };
   // Make the cursor point at a tile, skipping empty units; b = B once the
@@ -360,10 +388,11 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
   auto load_q = [&](const Cursor& cu) {
     const uint32_t dst = uniform((int)lds_addr(qslots + (q_issued & 1) * kQSlotBytes));
     const char* qbase =
-        (const char*)(a.q + (int64_t)cu.b * a.qlen * a.q_sb + (int64_t)cu.kvh * G * a.q_sh);
+        (const char*)(a.q + (int64_t)cu.r.row0 * a.q_sb + (int64_t)cu.kvh * G * a.q_sh);
     const int chunk = lane & 15;
-    for (int i = 0; i < (R + 3) / 4; ++i) {   // 4 columns (1 KB) per load
-      const int n = min(4 * i + (lane >> 4), R - 1);
+    const int Rq = V ? cu.r.n * G : G;   // the piece's columns
+    for (int i = 0; i < (Rq + 3) / 4; ++i) {   // 4 columns (1 KB) per load
+      const int n = min(4 * i + (lane >> 4), Rq - 1);
       const int t = n / G, g = n - t * G;
       const uint32_t voff = (uint32_t)(t * a.q_sb + g * a.q_sh + chunk * 8) * 2u;
       global_to_lds_16(qbase, voff, dst + i * 1024);
@@ -474,7 +503,7 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
     const float l_tot_part = l_run + shfl_xor(l_run, 16);
     const float l_tot = l_tot_part + shfl_xor(l_tot_part, 32);
     const int hq = cu.kvh * G + g_col;
-    const int64_t row = (int64_t)cu.b * a.qlen + t_col;
+    const int64_t row = (int64_t)cu.r.row0 + t_col;
     if (l16 < R) {
       const bool empty = !(l_tot > 0.f);
       const float lse_nat = empty ? neg_inf() : (m_run * c + fast_log2(l_tot)) * kLn2;
@@ -551,11 +580,15 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
           v_mult = a.v_scale != nullptr ? a.v_scale[si] : 1.f;
         }
         if constexpr (V) {
+          const int n = cc.r.n;   // >= 1: a unit with tiles has query rows
+          R = n * G;
+          t_col = min(l16, R - 1) / G;
+          g_col = min(l16, R - 1) - t_col * G;
           const int L = as_const(a.seq_lens)[cc.b], Lr = real_len(a, cc.b);
-          col_hi = row_hi(a, L, Lr, t_col);
+          col_hi = row_hi(a, L, Lr, t_col, n);
           col_lo = row_lo(a, col_hi);
-          all_hi = uniform(row_hi(a, L, Lr, 0));                 // first row's limit
-          all_lo = uniform(row_lo(a, row_hi(a, L, Lr, a.qlen - 1)));   // last row's start
+          all_hi = uniform(row_hi(a, L, Lr, 0, n));                 // first row's limit
+          all_lo = uniform(row_lo(a, row_hi(a, L, Lr, n - 1, n)));   // last row's start
         }
       }
 
@@ -737,8 +770,9 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
   cw.r = r_s;
   while (cw.b < a.B && (sh.last || cw.p0 < sh.g1)) {
     const int hq0 = cw.kvh * G;
+    R = V ? cw.r.n * G : G;   // this unit's columns
     // (row, query head) of column n of this unit
-    auto col_row = [&](int n) { return (int64_t)cw.b * a.qlen + n / G; };
+    auto col_row = [&](int n) { return (int64_t)cw.r.row0 + n / G; };
     auto col_head = [&](int n) { return hq0 + n % G; };
     if (cw.r.nt == 0) {
       if (direct) {

@@ -28,7 +28,10 @@ struct GqaArgs {
   int32_t max_blocks;
   const int32_t* seq_lens;
   const int32_t* real_lens;  // nullptr: equal to seq_lens
-  int32_t qlen;              // verify tokens per request; qlen * G <= 16
+  int32_t qlen;              // verify tokens per request (the most, with cu_q); qlen * G <= 16
+  const int32_t* cu_q;       // nullptr: request b has rows b * qlen + t; else [B + 1]
+                             // cumulative query lengths (rows cu_q[b] .. cu_q[b + 1] - 1)
+  int32_t total_rows;        // rows of q / out / lse (B * qlen, or cu_q[B])
   int32_t kv_fp8;            // 1: FP8 E4M3FN codes, K scaled by k_scale, V by v_scale
   const float* k_scale;      // nullptr: 1; else k_scale[kvh * scale_stride]
   const float* v_scale;

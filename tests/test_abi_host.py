@@ -148,6 +148,29 @@ def _gqav(**kw):
     return lib.paged_verify_gqa(*a.values())
 
 
+def _gqavl(**kw):
+    a = dict(q=FAKE, qsr=64 * 128, qsh=128, kv=FAKE, dt=0, ks=NULL, vs=NULL, per=0,
+             kvsp=8 * 16 * 256, kvsh=16 * 256,
+             npages=10, bt=FAKE, btsb=4, maxb=4, sl=FAKE, real=NULL, cu=FAKE, maxq=2, rows=3,
+             sinks=NULL, window=0, scale=0.088, B=2, Hq=64, Hkv=8, D=128, P=16, S=1, ws=NULL,
+             wsb=0, out=FAKE, osr=64 * 128, osh=128, lse=NULL, lser=64, stream=NULL)
+    a.update(kw)
+    return lib.paged_verify_gqa_varlen(*a.values())
+
+
+def test_gqa_verify_varlen_argument_checks_happen_before_any_hip_call():
+    assert _gqavl(B=0, q=NULL, kv=NULL, bt=NULL, sl=NULL, out=NULL, cu=NULL) == PD_OK
+    assert _gqavl(rows=0, q=NULL) == PD_OK                    # no query row at all
+    assert _gqavl(cu=NULL) == PD_ERR_INVALID
+    assert _gqavl(rows=-1) == PD_ERR_INVALID
+    assert _gqavl(maxq=0) == PD_ERR_INVALID
+    assert _gqavl(maxq=3) == PD_ERR_UNSUPPORTED                # max_qlen * G = 24 > 16
+    assert _gqavl(S=4) == PD_ERR_WORKSPACE
+    need = lib.pd_workspace_bytes(3, 64, 4, 128)               # rows = total_rows
+    assert _gqavl(S=4, ws=FAKE, wsb=need - 4) == PD_ERR_WORKSPACE
+    assert _gqavl(S=4, ws=FAKE + 4, wsb=need) == PD_ERR_ALIGN
+
+
 def test_gqa_verify_argument_checks_happen_before_any_hip_call():
     assert _gqav(B=0, q=NULL, kv=NULL, bt=NULL, sl=NULL, out=NULL) == PD_OK
     assert _gqav(qlen=0) == PD_ERR_INVALID
