@@ -371,6 +371,7 @@ def main():
             name = f"{name}_p{args.page_size}"
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
+    eager_step = case["step"]
 
     if args.warmup is not None:
         for _ in range(args.warmup):
@@ -403,7 +404,7 @@ def main():
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             for _ in range(n_calls):
-                case["step"]()
+                eager_step()
         torch.cuda.synchronize()
         for _ in range(3):
             graph.replay()

@@ -196,3 +196,16 @@ def test_full_size_verify_config_sampled(pd):
     O, L = oracle_gqa(w, vals, sample)
     rows = [b * w.qlen + t for b in sample for t in range(w.qlen)]
     check_attention(out[rows], lse[rows], O, L, what="gqa_verify full")
+
+
+@pytest.mark.parametrize("qlen", [1, 2])
+def test_batch_beyond_cached_lengths(pd, qlen):
+    """B = 300 requests: the plan keeps the first 256 lengths in registers and
+    reads the rest in its loops; every request checked against the oracle."""
+    w = gqa_workload("gqa_verify", batch=300, len_range=(0, 90), qlen=qlen, heads=(16, 8),
+                     real_drop=(0, 1), pool="tight", seed_offset=31 + qlen)
+    vals = w.values("cuda", poison=True)
+    for S in (1, 3):
+        out, lse = _run(pd, w, vals, S)
+        O, L = oracle_gqa(w, vals)
+        check_attention(out, lse, O, L, what=f"B=300 qlen={qlen} S={S}")

@@ -205,3 +205,12 @@ def test_full_size_config_sampled(pd, fp8):
     rows = [b * w.qlen + t for b in pick for t in range(w.qlen)]
     check_attention(out[rows], lse[rows], O.reshape(len(rows), w.H, w.Lv), L,
                     o_atol=O_ATOL_FP8 if fp8 else 2e-2, what=f"mla full S={S} fp8={fp8}")
+
+
+def test_batch_beyond_one_wave_of_requests(pd):
+    """B = 70 requests (the plan scans requests 64 at a time)."""
+    w = mla_workload(batch=70, len_range=(0, 40), heads=16, seed_offset=21)
+    vals = w.values("cuda", poison=True)
+    for S in (1, 2):
+        out, lse = _run(pd, w, vals, S)
+        _check(w, vals, out, lse, False, f"B=70 S={S}")
