@@ -36,27 +36,34 @@ __device__ __forceinline__ float shfl_xor(float v, int mask) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(v)));
 }
 
-// Sum / max over the 64 lanes (every lane gets the result).
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __builtin_amdgcn_ds_bpermute((lane_id() ^ m) << 2, v);
-  return v;
+// Wave64 inclusive prefix sum / prefix max with DPP: four row shifts scan
+// each 16-lane row, then two row broadcasts carry the totals of rows 0..2
+// forward (row_shr:n = 0x110 + n, row_bcast:15 = 0x142 into rows 1 and 3,
+// row_bcast:31 = 0x143 into rows 2 and 3).  Lanes a shift leaves without a
+// source take the identity.
+__device__ __forceinline__ int wave_incl_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);
+  return x;
 }
-__device__ __forceinline__ int wave_max(int v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = max(v, __builtin_amdgcn_ds_bpermute((lane_id() ^ m) << 2, v));
-  return v;
+__device__ __forceinline__ int wave_incl_max(int x) {
+  constexpr int kMin = -0x7fffffff - 1;
+  x = max(x, __builtin_amdgcn_update_dpp(kMin, x, 0x111, 0xf, 0xf, false));
+  x = max(x, __builtin_amdgcn_update_dpp(kMin, x, 0x112, 0xf, 0xf, false));
+  x = max(x, __builtin_amdgcn_update_dpp(kMin, x, 0x114, 0xf, 0xf, false));
+  x = max(x, __builtin_amdgcn_update_dpp(kMin, x, 0x118, 0xf, 0xf, false));
+  x = max(x, __builtin_amdgcn_update_dpp(kMin, x, 0x142, 0xa, 0xf, false));
+  x = max(x, __builtin_amdgcn_update_dpp(kMin, x, 0x143, 0xc, 0xf, false));
+  return x;
 }
-// Inclusive prefix sum over the 64 lanes.
-__device__ __forceinline__ int wave_incl_sum(int v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __builtin_amdgcn_ds_bpermute((lane >= d ? lane - d : lane) << 2, v);
-    if (lane >= d) v += y;
-  }
-  return v;
-}
+// Sum / max over the 64 lanes (every lane gets the result): the last lane
+// of the inclusive scan.
+__device__ __forceinline__ int wave_sum(int v) { return __builtin_amdgcn_readlane(wave_incl_sum(v), 63); }
+__device__ __forceinline__ int wave_max(int v) { return __builtin_amdgcn_readlane(wave_incl_max(v), 63); }
 
 __device__ __forceinline__ float readlane(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));

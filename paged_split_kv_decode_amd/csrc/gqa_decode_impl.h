@@ -205,6 +205,7 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
   int nt_sum = 0, nt_max = 0;
 #pragma unroll
   for (int ch = 0; ch < kCachedChunks; ++ch) {
+    if (64 * ch >= a.B) break;   // chunks past the batch add nothing
     const int nt = range_of(a, Lc[ch], Lrc[ch], Nc[ch]).nt;
     nt_sum += wave_sum(nt);
     nt_max = max(nt_max, wave_max(nt));
