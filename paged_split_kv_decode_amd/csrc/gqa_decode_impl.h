@@ -501,8 +501,7 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
   int col_lo = 0, col_hi = 0, all_lo = 0, all_hi = 0;
 
   auto finish_piece = [&](const Cursor& cu) {
-    const float l_tot_part = l_run + shfl_xor(l_run, 16);
-    const float l_tot = l_tot_part + shfl_xor(l_tot_part, 32);
+    const float l_tot = sum_xor32(sum_xor16(l_run));
     const int hq = cu.kvh * G + g_col;
     const int64_t row = (int64_t)cu.r.row0 + t_col;
     if (l16 < R) {
@@ -691,8 +690,7 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
       // ---- online softmax (fp32, exp2, running max in unscaled logits) ----
       float mx = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
                        fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
-      mx = fmaxf(mx, shfl_xor(mx, 16));
-      mx = fmaxf(mx, shfl_xor(mx, 32));
+      mx = max_xor32(max_xor16(mx));
       const float m_new = fmaxf(m_run, mx);
       const float m_ref = m_new == neg_inf() ? 0.f : m_new;
       const float mc = m_ref * c;

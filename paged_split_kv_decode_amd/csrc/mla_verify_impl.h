@@ -610,7 +610,7 @@ void mla_verify_kernel(MlaArgs a) {
         float mt = x[0];
   #pragma unroll
         for (int e = 1; e < 16; ++e) mt = fmaxf(mt, x[e]);
-        mt = fmaxf(mt, shfl_xor(mt, 32));
+        mt = max_xor32(mt);
         m_seen = fmaxf(m_seen, mt);
         // first non-empty tile of the row: take its max as the reference (the
         // accumulator and l are still exactly 0, so nothing needs rescaling)
@@ -639,7 +639,7 @@ void mla_verify_kernel(MlaArgs a) {
     // every wave is past its last LDS read of this pass: agree on a rerun and
     // publish the row statistics through the (now idle) ring
     __syncthreads();
-    l_run += shfl_xor(l_run, 32);
+    l_run = sum_xor32(l_run);
     PD_LDS int* flags = (PD_LDS int*)lds;
     PD_LDS float* row_l = (PD_LDS float*)(lds + 64);
     PD_LDS float* row_m = row_l + kRowsPerBlock;
