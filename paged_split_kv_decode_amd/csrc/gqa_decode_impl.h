@@ -687,6 +687,47 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
         }
       }
 
+      // ---- V^T fragments of the tile, read before the softmax so their LDS
+      // latency overlaps it (they do not depend on the probabilities) ----
+      // bf16: two 16-bit transpose reads per block of 16 dims, rows
+      // ra = 4 g4 + l16 / 4 and ra + 16 (the k order of P^T).
+      // FP8: the 8-bit transpose read gives lane i of a 16-lane group byte
+      // i % 8 of the 8 bytes read by lanes 2 e + (i >= 8), e = 0..7; so lane
+      // s reads dims 16 blk + 8 (s % 2) .. + 7 of token T(s / 2), with
+      // T(e) = 4 g4 + e (e < 4) and 16 + 4 g4 + e - 4 (the same k order);
+      // its codes are converted at the product.
+      u32x4 vraw[8];
+      {
+        const int ra = 4 * g4 + (l16 >> 2);
+        const int rb = ra + 16;
+        const int swa = swz(ra);
+        const int tv = (l16 >> 1) < 4 ? 4 * g4 + (l16 >> 1) : 12 + 4 * g4 + (l16 >> 1);
+        PD_LDS char* vrow8 = tl + tv * kRowBytes8 + (l16 & 1) * 8;
+        const int fv = f8(tv);
+#pragma unroll
+        for (int blk = 0; blk < 8; ++blk) {
+          if constexpr (F8) {
+            typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
+            const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (PD_LDS i32x2*)(vrow8 + (((8 + blk) ^ fv) << 4)));
+            vraw[blk] = u32x4{(uint32_t)w[0], (uint32_t)w[1], 0u, 0u};
+          } else {
+            const int ch = 2 * blk + ((l16 & 3) >> 1);   // V chunk (16 dims) of this block
+            const int within = (l16 & 1) * 8;
+            const bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (PD_LDS bf16x4*)(vt + ra * kRowBytes + ((ch ^ swa) << 4) + within));
+            const bf16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (PD_LDS bf16x4*)(vt + rb * kRowBytes + ((ch ^ swa) << 4) + within));
+            const u32x2 ua = __builtin_bit_cast(u32x2, va);
+            const u32x2 ub = __builtin_bit_cast(u32x2, vb);
+            vraw[blk] = u32x4{ua[0], ua[1], ub[0], ub[1]};
+          }
+        }
+      }
+      // keep the reads here (left alone, the scheduler moves them next to
+      // their products, behind the softmax)
+      __builtin_amdgcn_sched_barrier(0);
+
       // ---- online softmax (fp32, exp2, running max in unscaled logits) ----
       float mx = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
                        fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
@@ -717,37 +758,12 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
                            keep_mask(v1[0], v1[1]), keep_mask(v1[2], v1[3])};
 
       // ---- O^T += V^T P^T ----
-      const int ra = 4 * g4 + (l16 >> 2);
-      const int rb = ra + 16;
-      const int swa = swz(ra);
-      // FP8 V^T: the 8-bit transpose read gives lane i of a 16-lane group
-      // byte i % 8 of the 8 bytes read by lanes 2 e + (i >= 8), e = 0..7; so
-      // lane s reads dims 16 blk + 8 (s % 2) .. + 7 of token T(s / 2), with
-      // T(e) = 4 g4 + e (e < 4) and 16 + 4 g4 + e - 4 (the k order of P^T)
-      const int tv = (l16 >> 1) < 4 ? 4 * g4 + (l16 >> 1) : 12 + 4 * g4 + (l16 >> 1);
-      PD_LDS char* vrow8 = tl + tv * kRowBytes8 + (l16 & 1) * 8;
-      const int fv = f8(tv);
 #pragma unroll
       for (int blk = 0; blk < 8; ++blk) {
-        u32x4 vv;
-        if constexpr (F8) {
-          typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
-          const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              (PD_LDS i32x2*)(vrow8 + (((8 + blk) ^ fv) << 4)));
-          const uint32_t w_lo = (uint32_t)w[0], w_hi = (uint32_t)w[1];
-          vv = u32x4{cvt8(w_lo, kLo), cvt8(w_lo, kHi), cvt8(w_hi, kLo), cvt8(w_hi, kHi)};
-        } else {
-          // V chunk (16 dims) of this block: position c ^ swz(row) in the V half
-          const int ch = 2 * blk + ((l16 & 3) >> 1);
-          const int within = (l16 & 1) * 8;
-          bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (PD_LDS bf16x4*)(vt + ra * kRowBytes + ((ch ^ swa) << 4) + within));
-          bf16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (PD_LDS bf16x4*)(vt + rb * kRowBytes + ((ch ^ swa) << 4) + within));
-          u32x2 ua = __builtin_bit_cast(u32x2, va);
-          u32x2 ub = __builtin_bit_cast(u32x2, vb);
-          vv = u32x4{ua[0], ua[1], ub[0], ub[1]};
-        }
+        u32x4 vv = vraw[blk];
+        if constexpr (F8)
+          vv = u32x4{cvt8(vraw[blk][0], kLo), cvt8(vraw[blk][0], kHi), cvt8(vraw[blk][1], kLo),
+                     cvt8(vraw[blk][1], kHi)};
         if (edge) vv &= vkeep;
         o[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pf, o[blk], 0, 0, 0);
       }
