@@ -55,6 +55,15 @@ def _parse():
     return p.parse_args()
 
 
+def _kernel_split(S, step, partials, merge):
+    """(kernel, rest) callables whose sequence is one step: with S > 1 the
+    attention kernel alone (the partials-only entry) and then the merge; with
+    S = 1 the step itself is the one kernel."""
+    if S > 1:
+        return partials, merge
+    return step, (lambda: None)
+
+
 def _gqa_case(name, torch, pd, splits, page_size=0):
     from synth import gqa_workload
 
@@ -87,8 +96,17 @@ def _gqa_case(name, torch, pd, splits, page_size=0):
             desc = (f"GQA causal verify with sinks: B={w.B}, qlen={w.qlen}, Hq={w.Hq}, "
                     f"Hkv={w.Hkv}, D={w.D}, page {w.P} HND bf16, seq_lens U[1024,8192], "
                     f"real length L - U{{0,1}}, {pool}")
-        # the kernel and its merge are timed together (no partials-only verify entry)
-        return dict(w=w, vals=vals, S=S, step=verify_step, kernel=None, rest=None,
+        def verify_kernel():
+            pd.paged_verify_gqa_partials(vals["q"], vals["kv"], bt, sl, w.qlen, w.sm_scale,
+                                         window=w.window, real_seq_lens=real, num_kv_splits=S,
+                                         workspace=ws, k_scale=vals.get("k_scale"),
+                                         v_scale=vals.get("v_scale"))
+
+        def verify_rest():
+            pd.merge_splits(ws, w.rows, w.Hq, S, w.D, sinks=vals["sinks"], out=out, lse=lse)
+
+        kernel, rest = _kernel_split(S, verify_step, verify_kernel, verify_rest)
+        return dict(w=w, vals=vals, S=S, step=verify_step, kernel=kernel, rest=rest,
                     kv_bytes=w.kv_bytes() // (2 if fp8 else 1), flops=w.flops(), desc=desc,
                     kind="gqa_fp8" if fp8 else "gqa_verify", kernel_name="gqa_decode_kernel")
 
@@ -101,8 +119,7 @@ def _gqa_case(name, torch, pd, splits, page_size=0):
                                      num_kv_splits=S, workspace=ws)
 
     def rest():
-        if S > 1:
-            pd.merge_splits(ws, w.B, w.Hq, S, w.D, sinks=vals["sinks"], out=out, lse=lse)
+        pd.merge_splits(ws, w.B, w.Hq, S, w.D, sinks=vals["sinks"], out=out, lse=lse)
 
     desc = {
         "gqa_sinks": f"GQA decode with sinks: B=64, Hq=64, Hkv=8, D=128, page {w.P} HND bf16, "
@@ -114,7 +131,8 @@ def _gqa_case(name, torch, pd, splits, page_size=0):
         "tiny_gqa": "tiny GQA decode: B=3, seq_lens [30,32,70], page 32",
     }[name]
 
-    return dict(w=w, vals=vals, S=S, step=step, kernel=kernel_only, rest=rest,
+    kernel, rest = _kernel_split(S, step, kernel_only, rest)
+    return dict(w=w, vals=vals, S=S, step=step, kernel=kernel, rest=rest,
                 kv_bytes=w.kv_bytes(), flops=w.flops(), desc=desc, kind="gqa",
                 kernel_name="gqa_decode_kernel")
 
@@ -147,12 +165,21 @@ def _varlen_case(torch, pd, splits, page_size=0):
                                    sinks=vals["sinks"], window=w.window, real_seq_lens=real,
                                    num_kv_splits=S, workspace=ws, out=out, lse=lse)
 
+    def kernel_only():
+        pd.paged_verify_gqa_partials(q, vals["kv"], bt, sl, w.qlen, w.sm_scale, window=w.window,
+                                     real_seq_lens=real, cu_seqlens_q=cu_d, num_kv_splits=S,
+                                     workspace=ws)
+
+    def rest():
+        pd.merge_splits(ws, total, w.Hq, S, w.D, sinks=vals["sinks"], out=out, lse=lse)
+
+    kernel, rest = _kernel_split(S, step, kernel_only, rest)
     # keys of request b: rows t < n_b see [0, min(L, L_real)) at most (no window)
     keys = sum(max(min(int(L), int(Lr)), 0) for L, Lr in zip(w.seq_lens, w.real_seq_lens))
     desc = (f"GQA causal verify, variable query length U{{1,2}} per request (cumulative query "
             f"lengths, {total} rows): B={w.B}, Hq={w.Hq}, Hkv={w.Hkv}, D={w.D}, page {w.P} HND "
             f"bf16, seq_lens U[1024,8192], real length L - U{{0,1}}")
-    return dict(w=w, vals=vals, S=S, step=step, kernel=None, rest=None,
+    return dict(w=w, vals=vals, S=S, step=step, kernel=kernel, rest=rest,
                 kv_bytes=keys * w.Hkv * 2 * w.D * 2, flops=w.flops(), desc=desc,
                 kind="gqa_varlen", kernel_name="gqa_decode_kernel",
                 extra=dict(q=q, cu=cu, qlens=qlens))
@@ -202,9 +229,18 @@ def _mla_case(fp8, torch, pd, splits, page_size=0):
                             head_dim_v=w.Lv, k_scale=k_scale if fp8 else None,
                             num_kv_splits=S, workspace=ws, out=out, lse=lse)
 
+    def kernel_only():
+        pd.paged_verify_mla_partials(vals["q"], vals["kv"], bt, sl, real, w.qlen, w.sm_scale,
+                                     head_dim_v=w.Lv, k_scale=k_scale if fp8 else None,
+                                     num_kv_splits=S, workspace=ws)
+
+    def rest():
+        pd.merge_splits(ws, w.rows, w.H, S, w.Lv, out=out, lse=lse)
+
+    kernel, rest = _kernel_split(S, step, kernel_only, rest)
     desc = (f"MLA causal verify: B=32, qlen=4, H=128, Lk=576, Lv=512, page {w.P}, "
             f"seq_lens U[2048,16384], {'fp8 e4m3fn' if fp8 else 'bf16'} latent cache")
-    return dict(w=w, vals=vals, S=S, step=step, kernel=None, rest=None,
+    return dict(w=w, vals=vals, S=S, step=step, kernel=kernel, rest=rest,
                 kv_bytes=w.kv_bytes(1 if fp8 else 2), flops=w.flops(), desc=desc,
                 kind="mla_fp8" if fp8 else "mla", kernel_name="mla_verify_kernel")
 

@@ -6,10 +6,12 @@
  *
  *   paged_decode_gqa   one query token per request, grouped-query heads,
  *                      optional per-head sinks and a sliding window;
- *   paged_verify_gqa   the same with qlen causal verify tokens per request;
+ *   paged_verify_gqa   the same with qlen causal verify tokens per request
+ *                      (paged_verify_gqa_varlen: a query length per request);
  *   paged_kv_append    writes the newest tokens' K/V into the paged cache;
  *   paged_verify_mla   qlen causal "verify" tokens per request over one shared
  *                      latent cache, V read as K[..., :Lv], bf16 or FP8 cache;
+ *   *_partials         the split partials of a call, without the merge;
  *   num_kv_splits_cap  static split cap from static sizes (graph-capture safe);
  *   merge_splits       merges fp32 split partials into O and a natural-log LSE.
  *
@@ -284,6 +286,34 @@ PD_API int paged_decode_gqa_partials(const void* q, int64_t q_stride_b, int64_t 
                               size_t workspace_bytes, void* stream);
 
 /*
+ * paged_verify_gqa_partials - the split partials of paged_verify_gqa (or,
+ * with cu_seqlens_q, of paged_verify_gqa_varlen) only.
+ *
+ * Same key ranges, scales and argument meanings as those two calls, with no
+ * sinks and no outputs.  cu_seqlens_q NULL: rows are b*qlen + t and
+ * total_rows is ignored; cu_seqlens_q non-NULL: qlen is max_qlen and the
+ * rows are the varlen ones (total_rows of them; total_rows = 0 with B > 0
+ * returns PD_OK at once).  Writes every (row, query head, split) slot of
+ * `workspace` ([rows, Hq, S, D + 1] fp32, S = num_kv_splits >= 1) and
+ * launches no merge; a slot a row does not use gets lse = -inf.
+ * merge_splits over that workspace, with the sinks, gives exactly the full
+ * call's result.  The per-shard half of split-KV for verify, as
+ * paged_decode_gqa_partials is for decode.  Workspace bytes >=
+ * rows * Hq * S * (D + 1) * 4.
+ */
+PD_API int paged_verify_gqa_partials(const void* q, int64_t q_stride_row, int64_t q_stride_h,
+                              const void* kv, int32_t kv_dtype, const float* k_scale,
+                              const float* v_scale, int32_t scale_per_head,
+                              int64_t kv_stride_page, int64_t kv_stride_head, int32_t num_pages,
+                              const int32_t* block_table, int64_t bt_stride_b,
+                              int32_t max_blocks, const int32_t* seq_lens,
+                              const int32_t* real_seq_lens, const int32_t* cu_seqlens_q,
+                              int32_t qlen, int32_t total_rows, int32_t window, float sm_scale,
+                              int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t page_size, int32_t num_kv_splits,
+                              float* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * paged_kv_append - write the qlen newest tokens of every request into the
  * paged cache, through the block table (the cache write before a decode or
  * verify call).
@@ -363,6 +393,27 @@ PD_API int paged_verify_mla(const void* q, int64_t q_stride_row, int64_t q_strid
                      int32_t num_kv_splits, float* workspace, size_t workspace_bytes,
                      void* out, int64_t o_stride_row, int64_t o_stride_h,
                      float* lse, int64_t lse_stride_row, void* stream);
+
+/*
+ * paged_verify_mla_partials - the split partials of paged_verify_mla only.
+ *
+ * Same arguments and row limits as paged_verify_mla, with no outputs: writes
+ * every (row, head, split) slot of `workspace` ([B*qlen, H, S, Lv + 1]
+ * fp32, S = num_kv_splits >= 1, O already multiplied by k_scale) and
+ * launches no merge; a slot a row does not use gets lse = -inf.
+ * merge_splits over that workspace (no sinks) gives exactly
+ * paged_verify_mla's result: the per-shard half of split-KV for MLA verify.
+ * Workspace bytes >= B * qlen * H * S * (Lv + 1) * 4.
+ */
+PD_API int paged_verify_mla_partials(const void* q, int64_t q_stride_row, int64_t q_stride_h,
+                              const void* kv, int32_t kv_dtype, int64_t kv_stride_page,
+                              int64_t kv_stride_tok, int32_t num_pages, const float* k_scale,
+                              const int32_t* block_table, int64_t bt_stride_b,
+                              int32_t max_blocks, const int32_t* seq_lens,
+                              const int32_t* real_seq_lens, int32_t qlen, float sm_scale,
+                              int32_t batch, int32_t num_heads, int32_t head_dim_k,
+                              int32_t head_dim_v, int32_t page_size, int32_t num_kv_splits,
+                              float* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * merge_splits - merge fp32 split partials into O (bf16) and LSE (fp32).

@@ -18,8 +18,10 @@ from .api import (  # noqa: F401
     paged_decode_gqa_partials,
     paged_kv_append,
     paged_verify_gqa,
+    paged_verify_gqa_partials,
     paged_verify_gqa_varlen,
     paged_verify_mla,
+    paged_verify_mla_partials,
     workspace_bytes,
 )
 from ._native import LIB_PATH, PagedDecodeError  # noqa: F401

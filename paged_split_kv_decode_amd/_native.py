@@ -29,8 +29,10 @@ EXPORTS = (
     "paged_verify_gqa",
     "paged_verify_gqa_varlen",
     "paged_decode_gqa_partials",
+    "paged_verify_gqa_partials",
     "paged_kv_append",
     "paged_verify_mla",
+    "paged_verify_mla_partials",
     "merge_splits",
 )
 
@@ -115,6 +117,18 @@ def _load():
         _c_i32, _c_vp, _c_sz, _c_vp,            # splits, workspace, bytes, stream
     ]
     lib.paged_decode_gqa_partials.restype = ctypes.c_int
+    lib.paged_verify_gqa_partials.argtypes = [
+        _c_vp, _c_i64, _c_i64,                  # q, strides
+        _c_vp, _c_i32, _c_vp, _c_vp, _c_i32,    # kv, kv_dtype, k_scale, v_scale, per-head flag
+        _c_i64, _c_i64, _c_i32,                 # kv page/head strides, num_pages
+        _c_vp, _c_i64, _c_i32,                  # block_table, row stride, max_blocks
+        _c_vp, _c_vp,                           # seq_lens, real_seq_lens
+        _c_vp, _c_i32, _c_i32,                  # cu_seqlens_q, qlen (max_qlen), total_rows
+        _c_i32, _c_f32,                         # window, sm_scale
+        _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,  # B, Hq, Hkv, D, P
+        _c_i32, _c_vp, _c_sz, _c_vp,            # splits, workspace, bytes, stream
+    ]
+    lib.paged_verify_gqa_partials.restype = ctypes.c_int
     lib.paged_verify_mla.argtypes = [
         _c_vp, _c_i64, _c_i64,                  # q
         _c_vp, _c_i32, _c_i64, _c_i64, _c_i32,  # kv, dtype, page/token strides, num_pages
@@ -128,6 +142,17 @@ def _load():
         _c_vp, _c_i64, _c_vp,                   # lse, stride, stream
     ]
     lib.paged_verify_mla.restype = ctypes.c_int
+    lib.paged_verify_mla_partials.argtypes = [
+        _c_vp, _c_i64, _c_i64,                  # q
+        _c_vp, _c_i32, _c_i64, _c_i64, _c_i32,  # kv, dtype, page/token strides, num_pages
+        _c_vp,                                  # k_scale
+        _c_vp, _c_i64, _c_i32,                  # block table
+        _c_vp, _c_vp,                           # seq_lens, real_seq_lens
+        _c_i32, _c_f32,                         # qlen, sm_scale
+        _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,  # B, H, Lk, Lv, P
+        _c_i32, _c_vp, _c_sz, _c_vp,            # splits, workspace, bytes, stream
+    ]
+    lib.paged_verify_mla_partials.restype = ctypes.c_int
     lib.merge_splits.argtypes = [_c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_vp,
                                  _c_vp, _c_i64, _c_i64, _c_vp, _c_i64, _c_vp]
     lib.merge_splits.restype = ctypes.c_int

@@ -186,9 +186,35 @@ def paged_verify_gqa_varlen(q, kv, block_table, seq_lens, cu_seqlens_q, max_qlen
                        return_lse, k_scale, v_scale)
 
 
+def paged_verify_gqa_partials(q, kv, block_table, seq_lens, qlen, sm_scale, window=0,
+                              real_seq_lens=None, cu_seqlens_q=None, num_kv_splits=1,
+                              workspace=None, stream=None, k_scale=None, v_scale=None):
+    """Split partials of paged_verify_gqa (cu_seqlens_q None) or of
+    paged_verify_gqa_varlen (qlen is then max_qlen) without the merge
+    (include/paged_decode.h: paged_verify_gqa_partials).  No sinks: they
+    enter in merge_splits.  Returns the fp32 workspace viewed as
+    [rows, Hq, S, D + 1]."""
+    qlen = int(qlen)
+    if qlen < 1:
+        raise ValueError("qlen must be >= 1")
+    if cu_seqlens_q is None:
+        rows = q.shape[0] if q.dim() == 3 else -1
+        if rows % qlen != 0:
+            raise ValueError("q must have qlen rows per request")
+        B = rows // qlen
+    else:
+        _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1)
+        B = seq_lens.shape[0]
+        if cu_seqlens_q.shape[0] != B + 1 or cu_seqlens_q.stride(0) != 1:
+            raise ValueError("cu_seqlens_q must be a contiguous [B + 1] tensor")
+    return _verify_gqa(q, kv, block_table, seq_lens, B, qlen, cu_seqlens_q, sm_scale, None,
+                       window, real_seq_lens, num_kv_splits, workspace, None, None, stream,
+                       False, k_scale, v_scale, partials_only=True)
+
+
 def _verify_gqa(q, kv, block_table, seq_lens, B, qlen, cu_seqlens_q, sm_scale, sinks, window,
                 real_seq_lens, num_kv_splits, workspace, out, lse, stream, return_lse, k_scale,
-                v_scale):
+                v_scale, partials_only=False):
     _need(q, "q", torch.bfloat16, 3)
     fp8 = kv.dtype in (torch.uint8, torch.float8_e4m3fn)
     if not fp8:
@@ -211,17 +237,18 @@ def _verify_gqa(q, kv, block_table, seq_lens, B, qlen, cu_seqlens_q, sm_scale, s
         _need(sinks, "sinks", torch.float32, 1)
         if sinks.shape[0] != Hq or sinks.stride(0) != 1:
             raise ValueError("sinks must be a contiguous [Hq] tensor")
-    if out is None:
-        out = torch.empty((rows, Hq, D), dtype=torch.bfloat16, device=q.device)
-    _need(out, "out", torch.bfloat16, 3)
-    if out.stride(2) != 1:
-        raise ValueError("out must have a contiguous last dim")
-    if lse is None and return_lse:
-        lse = torch.empty((rows, Hq), dtype=torch.float32, device=q.device)
-    if lse is not None:
-        _need(lse, "lse", torch.float32, 2)
-        if lse.stride(1) != 1:
-            raise ValueError("lse must have a contiguous last dim")
+    if not partials_only:
+        if out is None:
+            out = torch.empty((rows, Hq, D), dtype=torch.bfloat16, device=q.device)
+        _need(out, "out", torch.bfloat16, 3)
+        if out.stride(2) != 1:
+            raise ValueError("out must have a contiguous last dim")
+        if lse is None and return_lse:
+            lse = torch.empty((rows, Hq), dtype=torch.float32, device=q.device)
+        if lse is not None:
+            _need(lse, "lse", torch.float32, 2)
+            if lse.stride(1) != 1:
+                raise ValueError("lse must have a contiguous last dim")
     per_head = 0
     for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
         if t is None:
@@ -234,7 +261,12 @@ def _verify_gqa(q, kv, block_table, seq_lens, B, qlen, cu_seqlens_q, sm_scale, s
     if per_head and any(t is not None and t.numel() != Hkv for t in (k_scale, v_scale)):
         raise ValueError("k_scale and v_scale must both be scalars or both per kv head")
     S = int(num_kv_splits)
-    if S > 1 and workspace is None:
+    if partials_only:
+        n = rows * Hq * S * (D + 1)
+        if workspace is None:
+            workspace = torch.empty(max(n, 1), dtype=torch.float32, device=q.device)
+        _need(workspace, "workspace", torch.float32)
+    elif S > 1 and workspace is None:
         workspace = alloc_workspace(rows, Hq, S, D, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     common = (_ptr(q), q.stride(0), q.stride(1),
@@ -242,6 +274,12 @@ def _verify_gqa(q, kv, block_table, seq_lens, B, qlen, cu_seqlens_q, sm_scale, s
               per_head, kv.stride(0), kv.stride(1), num_pages,
               _ptr(block_table), block_table.stride(0), block_table.shape[1],
               _ptr(seq_lens), _ptr(real_seq_lens))
+    if partials_only:
+        st = lib.paged_verify_gqa_partials(
+            *common, _ptr(cu_seqlens_q), qlen, rows, int(window or 0), float(sm_scale),
+            B, Hq, Hkv, D, P, S, _ptr(workspace), ws_bytes, _stream(stream))
+        check("paged_verify_gqa_partials", st)
+        return workspace[:n].view(rows, Hq, S, D + 1)
     tail_args = (_ptr(sinks), int(window or 0), float(sm_scale),
                  B, Hq, Hkv, D, P, S, _ptr(workspace), ws_bytes,
                  _ptr(out), out.stride(0), out.stride(1),
@@ -350,6 +388,24 @@ def paged_verify_mla(q, kv, block_table, seq_lens, real_seq_lens, qlen, sm_scale
     as bf16, or as uint8 FP8 E4M3FN codes with ``k_scale`` a 1-element fp32
     device tensor.  Returns (out [B*qlen, H, Lv] bf16, lse [B*qlen, H] fp32).
     """
+    return _verify_mla(q, kv, block_table, seq_lens, real_seq_lens, qlen, sm_scale,
+                       head_dim_v, page_size, k_scale, num_kv_splits, workspace, out, lse,
+                       stream, False)
+
+
+def paged_verify_mla_partials(q, kv, block_table, seq_lens, real_seq_lens, qlen, sm_scale,
+                              head_dim_v=512, page_size=None, k_scale=None, num_kv_splits=1,
+                              workspace=None, stream=None):
+    """Split partials of paged_verify_mla without the merge
+    (include/paged_decode.h: paged_verify_mla_partials).  Returns the fp32
+    workspace viewed as [B*qlen, H, S, Lv + 1]."""
+    return _verify_mla(q, kv, block_table, seq_lens, real_seq_lens, qlen, sm_scale,
+                       head_dim_v, page_size, k_scale, num_kv_splits, workspace, None, None,
+                       stream, True)
+
+
+def _verify_mla(q, kv, block_table, seq_lens, real_seq_lens, qlen, sm_scale, head_dim_v,
+                page_size, k_scale, num_kv_splits, workspace, out, lse, stream, partials_only):
     _need(q, "q", torch.bfloat16, 3)
     _need(block_table, "block_table", torch.int32, 2)
     _need(seq_lens, "seq_lens", torch.int32, 1)
@@ -388,20 +444,31 @@ def paged_verify_mla(q, kv, block_table, seq_lens, real_seq_lens, qlen, sm_scale
     if k_scale is not None:
         _need(k_scale, "k_scale", torch.float32)
     Lv = int(head_dim_v)
+    S = int(num_kv_splits)
+    head = (_ptr(q), q.stride(0), q.stride(1),
+            _ptr(kv), kv_dtype, s_page, s_tok, num_pages, _ptr(k_scale),
+            _ptr(block_table), block_table.stride(0), block_table.shape[1],
+            _ptr(seq_lens), _ptr(real_seq_lens), int(qlen), float(sm_scale),
+            B, H, Lk, Lv, P, S)
+    if partials_only:
+        n = rows * H * S * (Lv + 1)
+        if workspace is None:
+            workspace = torch.empty(max(n, 1), dtype=torch.float32, device=q.device)
+        _need(workspace, "workspace", torch.float32)
+        st = lib.paged_verify_mla_partials(*head, _ptr(workspace),
+                                           workspace.numel() * workspace.element_size(),
+                                           _stream(stream))
+        check("paged_verify_mla_partials", st)
+        return workspace[:n].view(rows, H, S, Lv + 1)
     if out is None:
         out = torch.empty((rows, H, Lv), dtype=torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty((rows, H), dtype=torch.float32, device=q.device)
-    S = int(num_kv_splits)
     if S > 1 and workspace is None:
         workspace = alloc_workspace(rows, H, S, Lv, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.paged_verify_mla(
-        _ptr(q), q.stride(0), q.stride(1),
-        _ptr(kv), kv_dtype, s_page, s_tok, num_pages, _ptr(k_scale),
-        _ptr(block_table), block_table.stride(0), block_table.shape[1],
-        _ptr(seq_lens), _ptr(real_seq_lens), int(qlen), float(sm_scale),
-        B, H, Lk, Lv, P, S, _ptr(workspace), ws_bytes,
+        *head, _ptr(workspace), ws_bytes,
         _ptr(out), out.stride(0), out.stride(1),
         _ptr(lse), lse.stride(0), _stream(stream))
     check("paged_verify_mla", st)
@@ -433,7 +500,8 @@ def merge_splits(workspace, rows, num_heads, num_splits, head_dim_v, sinks=None,
 
 __all__ = [
     "PD_KV_BF16", "PD_KV_FP8_E4M3FN", "alloc_workspace", "gqa_split_cap", "merge_splits",
-    "paged_decode_gqa_partials",
-    "mla_split_cap", "num_kv_splits_cap", "paged_decode_gqa", "paged_verify_mla",
+    "mla_split_cap", "num_kv_splits_cap", "paged_decode_gqa", "paged_decode_gqa_partials",
+    "paged_kv_append", "paged_verify_gqa", "paged_verify_gqa_partials",
+    "paged_verify_gqa_varlen", "paged_verify_mla", "paged_verify_mla_partials",
     "workspace_bytes", "_native",
 ]

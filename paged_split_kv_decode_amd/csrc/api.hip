@@ -291,6 +291,29 @@ int paged_decode_gqa_partials(const void* q, int64_t q_stride_b, int64_t q_strid
                     true);
 }
 
+int paged_verify_gqa_partials(const void* q, int64_t q_stride_row, int64_t q_stride_h,
+                              const void* kv, int32_t kv_dtype, const float* k_scale,
+                              const float* v_scale, int32_t scale_per_head,
+                              int64_t kv_stride_page, int64_t kv_stride_head, int32_t num_pages,
+                              const int32_t* block_table, int64_t bt_stride_b,
+                              int32_t max_blocks, const int32_t* seq_lens,
+                              const int32_t* real_seq_lens, const int32_t* cu_seqlens_q,
+                              int32_t qlen, int32_t total_rows, int32_t window, float sm_scale,
+                              int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t page_size, int32_t num_kv_splits,
+                              float* workspace, size_t workspace_bytes, void* stream) {
+  if (cu_seqlens_q != nullptr) {
+    if (total_rows < 0) return PD_ERR_INVALID;
+    if (batch > 0 && total_rows == 0) return PD_OK;   // no query row at all
+  }
+  return gqa_common(q, q_stride_row, q_stride_h, kv, kv_dtype, k_scale, v_scale,
+                    scale_per_head, kv_stride_page, kv_stride_head, num_pages, block_table,
+                    bt_stride_b, max_blocks, seq_lens, real_seq_lens, qlen, nullptr, window,
+                    sm_scale, batch, num_q_heads, num_kv_heads, head_dim, page_size,
+                    num_kv_splits, workspace, workspace_bytes, nullptr, 0, 0, nullptr, 0, stream,
+                    true, cu_seqlens_q, cu_seqlens_q != nullptr ? total_rows : -1);
+}
+
 int paged_kv_append(const void* src0, int64_t src0_stride_tok, int64_t src0_stride_h,
                     int32_t src0_elems, const void* src1, int64_t src1_stride_tok,
                     int64_t src1_stride_h, int32_t src1_elems, int32_t elem_bytes, void* cache,
@@ -345,15 +368,19 @@ int paged_kv_append(const void* src0, int64_t src0_stride_tok, int64_t src0_stri
   return PD_OK;
 }
 
-int paged_verify_mla(const void* q, int64_t q_stride_row, int64_t q_stride_h, const void* kv,
-                     int32_t kv_dtype, int64_t kv_stride_page, int64_t kv_stride_tok,
-                     int32_t num_pages, const float* k_scale, const int32_t* block_table,
-                     int64_t bt_stride_b, int32_t max_blocks, const int32_t* seq_lens,
-                     const int32_t* real_seq_lens, int32_t qlen, float sm_scale, int32_t batch,
-                     int32_t num_heads, int32_t head_dim_k, int32_t head_dim_v,
-                     int32_t page_size, int32_t num_kv_splits, float* workspace,
-                     size_t workspace_bytes, void* out, int64_t o_stride_row,
-                     int64_t o_stride_h, float* lse, int64_t lse_stride_row, void* stream) {
+namespace {
+
+// MLA verify; with partials_only, the split partials without the merge.
+int mla_common(const void* q, int64_t q_stride_row, int64_t q_stride_h, const void* kv,
+               int32_t kv_dtype, int64_t kv_stride_page, int64_t kv_stride_tok,
+               int32_t num_pages, const float* k_scale, const int32_t* block_table,
+               int64_t bt_stride_b, int32_t max_blocks, const int32_t* seq_lens,
+               const int32_t* real_seq_lens, int32_t qlen, float sm_scale, int32_t batch,
+               int32_t num_heads, int32_t head_dim_k, int32_t head_dim_v,
+               int32_t page_size, int32_t num_kv_splits, float* workspace,
+               size_t workspace_bytes, void* out, int64_t o_stride_row,
+               int64_t o_stride_h, float* lse, int64_t lse_stride_row, void* stream,
+               bool partials_only) {
   if (batch < 0 || qlen < 1 || num_heads < 1 || num_kv_splits < 1 || num_pages < 0 ||
       max_blocks < 0 || !std::isfinite(sm_scale) || !(sm_scale > 0.f))
     return PD_ERR_INVALID;
@@ -364,15 +391,16 @@ int paged_verify_mla(const void* q, int64_t q_stride_row, int64_t q_stride_h, co
     return PD_ERR_UNSUPPORTED;
   if (batch == 0) return PD_OK;
   if (q == nullptr || kv == nullptr || block_table == nullptr || seq_lens == nullptr ||
-      out == nullptr)
+      (!partials_only && out == nullptr))
     return PD_ERR_INVALID;
   if (q_stride_row < 0 || q_stride_h < 0 || kv_stride_page < 0 || kv_stride_tok < 0 ||
       bt_stride_b < 0 || o_stride_row < 0 || o_stride_h < 0 || lse_stride_row < 0)
     return PD_ERR_INVALID;
   const int64_t kv_align = kv_dtype == PD_KV_BF16 ? 8 : 16;
-  if (!aligned16(q) || !aligned16(kv) || !aligned16(out) || q_stride_row % 8 ||
-      q_stride_h % 8 || kv_stride_page % kv_align || kv_stride_tok % kv_align ||
-      o_stride_row % 8 || o_stride_h % 8)
+  if (!aligned16(q) || !aligned16(kv) || q_stride_row % 8 || q_stride_h % 8 ||
+      kv_stride_page % kv_align || kv_stride_tok % kv_align)
+    return PD_ERR_ALIGN;
+  if (!partials_only && (!aligned16(out) || o_stride_row % 8 || o_stride_h % 8))
     return PD_ERR_ALIGN;
   const int64_t rows = (int64_t)batch * qlen;
   if (rows > 0x7fffffff) return PD_ERR_UNSUPPORTED;
@@ -384,10 +412,11 @@ int paged_verify_mla(const void* q, int64_t q_stride_row, int64_t q_stride_h, co
         (int64_t)batch * cdiv64(rows_req, 128) * cdiv64(keys, 32) > INT32_MAX / 2)
       return PD_ERR_UNSUPPORTED;
   }
-  if (num_kv_splits > 1) {
-    if (workspace == nullptr ||
-        workspace_bytes < pd_workspace_bytes((int32_t)rows, num_heads, num_kv_splits, head_dim_v))
-      return PD_ERR_WORKSPACE;
+  if (num_kv_splits > 1 || partials_only) {
+    const int32_t ws_splits = num_kv_splits > 1 ? num_kv_splits : 2;
+    size_t need = pd_workspace_bytes((int32_t)rows, num_heads, ws_splits, head_dim_v);
+    if (num_kv_splits == 1) need /= 2;
+    if (workspace == nullptr || workspace_bytes < need) return PD_ERR_WORKSPACE;
     if (!aligned16(workspace)) return PD_ERR_ALIGN;
   }
   pd::MlaArgs a{};
@@ -412,6 +441,7 @@ int paged_verify_mla(const void* q, int64_t q_stride_row, int64_t q_stride_h, co
   a.P = page_size;
   a.p_shift = __builtin_ctz((unsigned)page_size);
   a.S = num_kv_splits;
+  a.partials = partials_only ? 1 : 0;
   a.ws = workspace;
   a.out = static_cast<uint16_t*>(out);
   a.o_srow = o_stride_row;
@@ -420,7 +450,7 @@ int paged_verify_mla(const void* q, int64_t q_stride_row, int64_t q_stride_h, co
   a.lse_srow = lse_stride_row;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (pd::launch_mla_verify(a, s) != hipSuccess) return PD_ERR_HIP;
-  if (num_kv_splits > 1) {
+  if (num_kv_splits > 1 && !partials_only) {
     pd::MergeArgs m{};
     m.ws = workspace;
     m.rows = (int32_t)rows;
@@ -436,6 +466,40 @@ int paged_verify_mla(const void* q, int64_t q_stride_row, int64_t q_stride_h, co
     if (pd::launch_merge(m, s) != hipSuccess) return PD_ERR_HIP;
   }
   return PD_OK;
+}
+
+}  // namespace
+
+int paged_verify_mla(const void* q, int64_t q_stride_row, int64_t q_stride_h, const void* kv,
+                     int32_t kv_dtype, int64_t kv_stride_page, int64_t kv_stride_tok,
+                     int32_t num_pages, const float* k_scale, const int32_t* block_table,
+                     int64_t bt_stride_b, int32_t max_blocks, const int32_t* seq_lens,
+                     const int32_t* real_seq_lens, int32_t qlen, float sm_scale, int32_t batch,
+                     int32_t num_heads, int32_t head_dim_k, int32_t head_dim_v,
+                     int32_t page_size, int32_t num_kv_splits, float* workspace,
+                     size_t workspace_bytes, void* out, int64_t o_stride_row,
+                     int64_t o_stride_h, float* lse, int64_t lse_stride_row, void* stream) {
+  return mla_common(q, q_stride_row, q_stride_h, kv, kv_dtype, kv_stride_page, kv_stride_tok,
+                    num_pages, k_scale, block_table, bt_stride_b, max_blocks, seq_lens,
+                    real_seq_lens, qlen, sm_scale, batch, num_heads, head_dim_k, head_dim_v,
+                    page_size, num_kv_splits, workspace, workspace_bytes, out, o_stride_row,
+                    o_stride_h, lse, lse_stride_row, stream, false);
+}
+
+int paged_verify_mla_partials(const void* q, int64_t q_stride_row, int64_t q_stride_h,
+                              const void* kv, int32_t kv_dtype, int64_t kv_stride_page,
+                              int64_t kv_stride_tok, int32_t num_pages, const float* k_scale,
+                              const int32_t* block_table, int64_t bt_stride_b,
+                              int32_t max_blocks, const int32_t* seq_lens,
+                              const int32_t* real_seq_lens, int32_t qlen, float sm_scale,
+                              int32_t batch, int32_t num_heads, int32_t head_dim_k,
+                              int32_t head_dim_v, int32_t page_size, int32_t num_kv_splits,
+                              float* workspace, size_t workspace_bytes, void* stream) {
+  return mla_common(q, q_stride_row, q_stride_h, kv, kv_dtype, kv_stride_page, kv_stride_tok,
+                    num_pages, k_scale, block_table, bt_stride_b, max_blocks, seq_lens,
+                    real_seq_lens, qlen, sm_scale, batch, num_heads, head_dim_k, head_dim_v,
+                    page_size, num_kv_splits, workspace, workspace_bytes, nullptr, 0, 0, nullptr,
+                    0, stream, true);
 }
 
 int merge_splits(const float* workspace, int32_t rows, int32_t num_heads, int32_t num_splits,

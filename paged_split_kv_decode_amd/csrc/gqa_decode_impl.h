@@ -14,10 +14,10 @@
 //   unit, and every wave takes an equal contiguous share of that sequence
 //   (tpw tiles), so the waves finish together whatever the length mix.
 // * A wave streams its share as one pipeline that runs straight across unit
-//   boundaries: it has a private 2-stage ring of 16 KB tiles in LDS and
-//   issues tile k+1 (16 `global_load_lds_dwordx4`, 1 KB each, HBM -> LDS
-//   with no VGPR staging, non-temporal: the cache is read once) while it
-//   computes tile k.  The physical page of
+//   boundaries: it has a private ring in LDS (bf16: 2 slots of 16 KB; FP8:
+//   4 slots of 8 KB, up to three tiles in flight) and issues the next tiles
+//   (`global_load_lds_dwordx4`, 1 KB each, HBM -> LDS with no VGPR staging,
+//   non-temporal: the cache is read once) while it computes tile k.  The physical page of
 //   each tile row comes from the block table through scalar loads made one
 //   tile ahead of their use, so their latency is hidden.  No workgroup
 //   barrier exists anywhere: the waves share nothing but the CU.
@@ -31,9 +31,12 @@
 // * Scores S^T[token, head] = K . Q^T on v_mfma_f32_16x16x32_bf16 with the
 //   G query heads of the kv head in the N dimension (G <= 16, zero-padded).
 //   Online softmax in fp32 with exp2 and a running max in unscaled logits,
-//   reduced over the 4 lanes of a head with two lane exchanges.  P (bf16)
-//   is already in the B-operand layout of O^T[d, head] += V^T . P^T, and
-//   V^T is read from the LDS tile with ds_read_b64_tr_b16.
+//   reduced over the 4 lanes of a head with two lane swaps
+//   (v_permlane16_swap, v_permlane32_swap).  P (bf16) is already in the
+//   B-operand layout of O^T[d, head] += V^T . P^T, and V^T is read from the
+//   LDS tile with ds_read_b64_tr_b16 (FP8: ds_read_b64_tr_b8, then an exact
+//   in-register conversion to bf16), ahead of the softmax so that the LDS
+//   latency overlaps it.
 // * Keys outside [lo, hi) get a -inf score and a zero V (select, never a
 //   multiply), so stale or NaN cache contents never reach the output.  A
 //   block-table entry outside [0, num_pages) is never dereferenced: its

@@ -78,6 +78,7 @@ struct MlaArgs {
   int32_t B, H, P;
   int32_t p_shift;   // log2(P): the page size is a power of two
   int32_t S;
+  int32_t partials;  // write split partials even with S == 1 (no merge follows)
   float* ws;
   uint16_t* out;
   int64_t o_srow, o_sh;

@@ -22,9 +22,11 @@
 //   HBM into a 4-slot LDS ring with global_load_lds_dwordx4, each bf16
 //   instruction filling 1 KB from 8 whole 128-byte lines.  A tile's loads
 //   are spread over the MFMA steps of the tile before (issued at once they
-//   fill the request queue and stall the wave).  The FP8 cache is
-//   dequantised exactly (v_cvt_scalef32_pk_bf16_fp8, scale 1) into a bf16
-//   staging tile; k_scale is folded into the softmax scale and the output.
+//   fill the request queue and stall the wave).  FP8 fragments are read
+//   from the FP8 tile itself (K with 8-byte reads, V^T with
+//   ds_read_b64_tr_b8) and converted in registers, exactly
+//   (v_cvt_scalef32_pk_bf16_fp8, scale 1); k_scale is folded into the
+//   softmax scale and the output.
 // * Scores: each wave owns 32 rows; S^T[token, row] = K . Q^T with
 //   v_mfma_f32_32x32x16_bf16, its query fragment (32 x 576 bf16, 144 VGPRs)
 //   held for the whole piece, K fragments read from LDS a few steps ahead.
@@ -44,9 +46,10 @@
 //   tracked alongside; if a later score exceeds the reference by more than
 //   2^64 (overflow risk) the workgroup runs the piece a second time with the
 //   exact max as reference.  Real attention scores never trigger it.
-// * With one split, whole requests are written directly as bf16 O and LSE;
-//   with several, every piece writes its fp32 partial (slots no piece uses
-//   are marked empty) and the merge pass combines them.
+// * With one split, whole requests are written directly as bf16 O and LSE
+//   (unless the caller asked for partials only); with several, every piece
+//   writes its fp32 partial (slots no piece uses are marked empty) and the
+//   merge pass combines them.
 #pragma once
 
 #include "device_common.h"
@@ -120,7 +123,7 @@ void mla_verify_kernel(MlaArgs a) {
   const int l32 = lane & 31;
   const int g2 = lane >> 5;
   const int S = a.S;
-  const bool direct = S == 1;
+  const bool direct = S == 1 && !a.partials;
 
   // ---- the plan ----------------------------------------------------------
   // The rows of a request form n_rb row blocks of 128 (token, head) rows;
@@ -137,7 +140,7 @@ void mla_verify_kernel(MlaArgs a) {
   // the length mix.  Where a share cuts a request, each piece is a split with
   // its own partial slot; T is raised until no request spans more than S
   // shares.  With S == 1 shares are rounded to whole requests and results
-  // are written directly.
+  // are written directly (or as the one partial of slot 0).
   const int n_wg = gridDim.x;
   int sid = blockIdx.x;
   const int per_xcd = n_wg / 8;

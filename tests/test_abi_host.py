@@ -246,3 +246,67 @@ def test_merge_argument_checks():
     assert f(FAKE, 4, 8, 2, 96, NULL, FAKE, 1024, 128, NULL, 8, NULL) == PD_ERR_UNSUPPORTED
     assert f(FAKE, 4, 8, 0, 128, NULL, FAKE, 1024, 128, NULL, 8, NULL) == PD_ERR_INVALID
     assert f(FAKE, 4, 8, 2, 128, NULL, FAKE + 2, 1024, 128, NULL, 8, NULL) == PD_ERR_ALIGN
+
+
+def _gqap(**kw):
+    a = dict(q=FAKE, qsb=64 * 128, qsh=128, kv=FAKE, kvsp=8 * 16 * 256, kvsh=16 * 256, npages=10,
+             bt=FAKE, btsb=4, maxb=4, sl=FAKE, window=0, scale=0.088, B=2, Hq=64, Hkv=8, D=128,
+             P=16, S=1, ws=FAKE, wsb=2 * 64 * 129 * 4, stream=NULL)
+    a.update(kw)
+    return lib.paged_decode_gqa_partials(*a.values())
+
+
+def test_gqa_partials_argument_checks_happen_before_any_hip_call():
+    assert _gqap(B=0, q=NULL, kv=NULL, bt=NULL, sl=NULL, ws=NULL, wsb=0) == PD_OK
+    assert _gqap(q=NULL) == PD_ERR_INVALID
+    assert _gqap(S=0) == PD_ERR_INVALID
+    assert _gqap(D=64) == PD_ERR_UNSUPPORTED
+    # a partial slot per (row, head, split) even with S = 1: no direct output
+    assert _gqap(ws=NULL, wsb=0) == PD_ERR_WORKSPACE
+    assert _gqap(wsb=2 * 64 * 129 * 4 - 4) == PD_ERR_WORKSPACE
+    assert _gqap(ws=FAKE + 4) == PD_ERR_ALIGN
+    assert _gqap(S=3, wsb=lib.pd_workspace_bytes(2, 64, 3, 128) - 4) == PD_ERR_WORKSPACE
+
+
+def _gqavp(**kw):
+    a = dict(q=FAKE, qsr=64 * 128, qsh=128, kv=FAKE, dt=0, ks=NULL, vs=NULL, per=0,
+             kvsp=8 * 16 * 256, kvsh=16 * 256, npages=10, bt=FAKE, btsb=4, maxb=4, sl=FAKE,
+             real=NULL, cu=NULL, qlen=2, rows=-1, window=0, scale=0.088, B=2, Hq=64, Hkv=8,
+             D=128, P=16, S=1, ws=FAKE, wsb=4 * 64 * 129 * 4, stream=NULL)
+    a.update(kw)
+    return lib.paged_verify_gqa_partials(*a.values())
+
+
+def test_gqa_verify_partials_argument_checks_happen_before_any_hip_call():
+    assert _gqavp(B=0, q=NULL, kv=NULL, bt=NULL, sl=NULL, ws=NULL, wsb=0) == PD_OK
+    assert _gqavp(qlen=0) == PD_ERR_INVALID
+    assert _gqavp(qlen=3) == PD_ERR_UNSUPPORTED                # qlen * G = 24 > 16
+    assert _gqavp(dt=1, per=2) == PD_ERR_INVALID
+    # fixed qlen: rows = B * qlen, total_rows ignored
+    assert _gqavp(wsb=4 * 64 * 129 * 4 - 4) == PD_ERR_WORKSPACE
+    assert _gqavp(ws=NULL, wsb=0) == PD_ERR_WORKSPACE
+    # varlen: rows = total_rows
+    assert _gqavp(cu=FAKE, rows=-1) == PD_ERR_INVALID
+    assert _gqavp(cu=FAKE, rows=0, q=NULL, ws=NULL) == PD_OK   # no query row at all
+    assert _gqavp(cu=FAKE, rows=3, wsb=3 * 64 * 129 * 4 - 4) == PD_ERR_WORKSPACE
+    assert _gqavp(cu=FAKE, rows=3, ws=FAKE + 4, wsb=3 * 64 * 129 * 4) == PD_ERR_ALIGN
+
+
+def _mlap(**kw):
+    a = dict(q=FAKE, qsr=128 * 576, qsh=576, kv=FAKE, dt=0, sp=16 * 576, st=576, npages=10,
+             ks=NULL, bt=FAKE, btsb=4, maxb=4, sl=FAKE, real=NULL, qlen=4, scale=0.07, B=2,
+             H=128, Lk=576, Lv=512, P=16, S=1, ws=FAKE, wsb=8 * 128 * 513 * 4, stream=NULL)
+    a.update(kw)
+    return lib.paged_verify_mla_partials(*a.values())
+
+
+def test_mla_partials_argument_checks_happen_before_any_hip_call():
+    assert _mlap(B=0, q=NULL, kv=NULL, bt=NULL, sl=NULL, ws=NULL, wsb=0) == PD_OK
+    assert _mlap(kv=NULL) == PD_ERR_INVALID
+    assert _mlap(qlen=0) == PD_ERR_INVALID
+    assert _mlap(Lv=256) == PD_ERR_UNSUPPORTED
+    assert _mlap(P=24) == PD_ERR_UNSUPPORTED
+    assert _mlap(ws=NULL, wsb=0) == PD_ERR_WORKSPACE           # S = 1 still writes partials
+    assert _mlap(wsb=8 * 128 * 513 * 4 - 4) == PD_ERR_WORKSPACE
+    assert _mlap(ws=FAKE + 4) == PD_ERR_ALIGN
+    assert _mlap(S=2, wsb=lib.pd_workspace_bytes(8, 128, 2, 512) - 4) == PD_ERR_WORKSPACE
