@@ -554,10 +554,12 @@ void mla_verify_kernel(MlaArgs a) {
   #pragma unroll
           for (int i = 0; i < kKAhead; ++i) kf[i] = kread(i);
         }
-        vf[0] = vread(0, 0);
-        vf[1] = vread(0, 1);
+        if constexpr (FP8) {
+          vf[0] = vread(0, 0);
+          vf[1] = vread(0, 1);
   #pragma unroll
-        for (int r = 0; r < 4; ++r) pf[r] = pread(r, 0);
+          for (int r = 0; r < 4; ++r) pf[r] = pread(r, 0);
+        }
   #pragma unroll
         for (int kk = 0; kk < kKSteps; ++kk) {
           if constexpr (FP8) {
@@ -566,7 +568,7 @@ void mla_verify_kernel(MlaArgs a) {
           } else {
             sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk % kKAhead], qf[kk], sacc, 0, 0, 0);
           }
-          if (kk < 30) {
+          if (FP8 && kk < 30) {
             const int s = kk / 15, idx = kk % 15, d = idx >> 2, r = idx & 3, v = 4 * s + d;
             o[idx] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[v & 1], pf[r], o[idx], 0, 0, 0);
             // V^T fragment v is done after its last row group: fetch v + 2
@@ -594,47 +596,119 @@ void mla_verify_kernel(MlaArgs a) {
           const bf16x8 va = vread(0, 3), pa = pread(3, 0);
           f32x16 ob = o_last;
           ob = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pa, ob, 0, 0, 0);
-          ob = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[1], pf[3], ob, 0, 0, 0);
+          if constexpr (FP8)
+            ob = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[1], pf[3], ob, 0, 0, 0);
+          else
+            ob = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread(1, 3), pread(3, 1), ob, 0, 0, 0);
           o_last = ob;
           asm volatile("" : "+v"(o_last));
         }
-        if (!live) break;
+        if constexpr (!FP8) {
+          // bf16: tile k-1's 30 remaining products with tile k's softmax
+          // interleaved by hand, one product and a slice of the softmax per
+          // step, a scheduling barrier closing each step (the products do not
+          // depend on the softmax; in the score loop they only padded the
+          // score chain, which issues back to back on its own).  The softmax
+          // runs on the last pass too (its state only changes for a live
+          // tile), so the products and the softmax stay in one block.
+          float mt = 0.f, m_a = 0.f, m_ref_n = 0.f, mref = 0.f, lsum = 0.f;
+          bool ovf_n = false;
+          float p[16];
+          u32x4 pw0 = {0, 0, 0, 0}, pw1 = {0, 0, 0, 0};
+          // V^T fragment v = 4 s + d in vr[v % 2], P^T (r, s) in pr[r]
+          bf16x8 vr[2], pr[4];
+          vr[0] = vread(0, 0);
+          vr[1] = vread(0, 1);
+  #pragma unroll
+          for (int r = 0; r < 4; ++r) pr[r] = pread(r, 0);
+  #pragma unroll
+          for (int j = 0; j < 30; ++j) {
+            const int s = j / 15, idx = j % 15, d = idx >> 2, r = idx & 3, v = 4 * s + d;
+            o[idx] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[v & 1], pr[r], o[idx], 0, 0, 0);
+            const bool v_done = r == 3 || idx == 14;
+            if (v_done && v + 2 < 8) vr[v & 1] = vread((v + 2) >> 2, (v + 2) & 3);
+            if (s == 0 && (d == 3 || (d == 2 && r == 3))) pr[r] = pread(r, 1);
+            if (j < 2) {
+              // causal limit of this lane's row: token tok0 + 8 (e / 4) + 4 g2 + e % 4 < hi_row
+  #pragma unroll
+              for (int e = 8 * j; e < 8 * j + 8; ++e) {
+                const int tok = tok0 + 8 * (e >> 2) + 4 * g2 + (e & 3);
+                x[e] = tok >= hi_row ? neg_inf() : x[e];
+              }
+            } else if (j == 2) {
+              m_a = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+            } else if (j == 3) {
+              const float m_b = fmaxf(fmaxf(fmaxf(x[8], x[9]), fmaxf(x[10], x[11])),
+                                      fmaxf(fmaxf(x[12], x[13]), fmaxf(x[14], x[15])));
+              mt = max_xor32(fmaxf(m_a, m_b));
+            } else if (j == 4) {
+              // first non-empty tile of the row: its max becomes the reference
+              m_ref_n = m_ref == neg_inf() ? mt : m_ref;
+              ovf_n = mt - m_ref_n > kRefHeadroomLog2;   // false while -inf
+              mref = m_ref_n == neg_inf() ? 0.f : m_ref_n;
+            } else if (j >= 5 && j < 21) {
+              p[j - 5] = fast_exp2(x[j - 5] - mref);
+              lsum += p[j - 5];
+            } else if (j == 21) {
+              pw0 = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                          pack_bf16x2(p[6], p[7])};
+            } else if (j == 22) {
+              pw1 = u32x4{pack_bf16x2(p[8], p[9]), pack_bf16x2(p[10], p[11]), pack_bf16x2(p[12], p[13]),
+                          pack_bf16x2(p[14], p[15])};
+            } else if (j == 23) {
+              // publish P^T of this wave's row group (key steps 0 and 1); on
+              // the last pass the slot is never read
+              *(PD_LDS u32x4*)p_slot(k, wave, 0) = pw0;
+              *(PD_LDS u32x4*)p_slot(k, wave, 1) = pw1;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          m_seen = live ? fmaxf(m_seen, mt) : m_seen;
+          m_ref = live ? m_ref_n : m_ref;
+          overflow = overflow || (live && ovf_n);
+          l_run = live ? l_run + lsum : l_run;
+          if (!live) break;
+        } else {
+          if (!live) break;
 
-        // causal limit of this lane's row: token tok0 + 8j + 4 g2 + i < hi_row
-        if (tok0 + kTileTokens > hi_row) {
+          // causal limit of this lane's row: token tok0 + 8j + 4 g2 + i < hi_row
+          if (tok0 + kTileTokens > hi_row) {
+  #pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int tok = tok0 + 8 * (e >> 2) + 4 * g2 + (e & 3);
+              if (tok >= hi_row) x[e] = neg_inf();
+            }
+          }
+
+          // ---- online softmax against the fixed row reference ----
+          float mt = x[0];
+  #pragma unroll
+          for (int e = 1; e < 16; ++e) mt = fmaxf(mt, x[e]);
+          mt = max_xor32(mt);
+          m_seen = fmaxf(m_seen, mt);
+          // first non-empty tile of the row: take its max as the reference (the
+          // accumulator and l are still exactly 0, so nothing needs rescaling)
+          if (m_ref == neg_inf()) m_ref = mt;
+          overflow |= mt - m_ref > kRefHeadroomLog2;           // false while -inf
+          const float mref = m_ref == neg_inf() ? 0.f : m_ref;
+          float p[16];
+          float lsum = 0.f;   // summed as on the bf16 path, so the two round alike
   #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            const int tok = tok0 + 8 * (e >> 2) + 4 * g2 + (e & 3);
-            if (tok >= hi_row) x[e] = neg_inf();
+            p[e] = fast_exp2(x[e] - mref);
+            lsum += p[e];
           }
-        }
-
-        // ---- online softmax against the fixed row reference ----
-        float mt = x[0];
+          l_run += lsum;
+          // Publish P^T (this wave's row group, key step st): the score
+          // accumulator's element order (keys 8 (e / 4) + 4 g2 + e % 4) is the
+          // key order of the V^T fragments, so each lane's 8 probabilities of a
+          // key step are its B-operand fragment as they stand.
   #pragma unroll
-        for (int e = 1; e < 16; ++e) mt = fmaxf(mt, x[e]);
-        mt = max_xor32(mt);
-        m_seen = fmaxf(m_seen, mt);
-        // first non-empty tile of the row: take its max as the reference (the
-        // accumulator and l are still exactly 0, so nothing needs rescaling)
-        if (m_ref == neg_inf()) m_ref = mt;
-        overflow |= mt - m_ref > kRefHeadroomLog2;           // false while -inf
-        const float mref = m_ref == neg_inf() ? 0.f : m_ref;
-        float p[16];
-  #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          p[e] = fast_exp2(x[e] - mref);
-          l_run += p[e];
-        }
-        // Publish P^T (this wave's row group, key step st): the score
-        // accumulator's element order (keys 8 (e / 4) + 4 g2 + e % 4) is the
-        // key order of the V^T fragments, so each lane's 8 probabilities of a
-        // key step are its B-operand fragment as they stand.
-  #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const u32x4 w = {pack_bf16x2(p[8 * st + 0], p[8 * st + 1]), pack_bf16x2(p[8 * st + 2], p[8 * st + 3]),
-                           pack_bf16x2(p[8 * st + 4], p[8 * st + 5]), pack_bf16x2(p[8 * st + 6], p[8 * st + 7])};
-          *(PD_LDS u32x4*)p_slot(k, wave, st) = w;
+          for (int st = 0; st < 2; ++st) {
+            const u32x4 w = {pack_bf16x2(p[8 * st + 0], p[8 * st + 1]), pack_bf16x2(p[8 * st + 2], p[8 * st + 3]),
+                             pack_bf16x2(p[8 * st + 4], p[8 * st + 5]), pack_bf16x2(p[8 * st + 6], p[8 * st + 7])};
+            *(PD_LDS u32x4*)p_slot(k, wave, st) = w;
+          }
         }
       }
     }
