@@ -11,8 +11,9 @@
 //   (tile t covers positions [32t, 32t + 32), clipped to the request's key
 //   range).  All units' tiles, request-major then kv-head-major, form one
 //   flat sequence of U tiles.  The grid is one 4-wave workgroup per compute
-//   unit, and every wave takes an equal contiguous share of that sequence
-//   (tpw tiles), so the waves finish together whatever the length mix.
+//   unit, and every wave takes a contiguous share of that sequence, equal
+//   up to a fixed skew between even and odd XCDs (which stream at different
+//   rates), so the waves finish together whatever the length mix.
 // * A wave streams its share as one pipeline that runs straight across unit
 //   boundaries: it has a private ring in LDS (bf16: 2 slots of 16 KB; FP8:
 //   4 slots of 8 KB, up to three tiles in flight) and issues the next tiles
@@ -69,6 +70,15 @@ static_assert(4 * kTileBytes8 == kRingBytes, "FP8 ring of 4 tiles");
 __device__ __forceinline__ int f8(int r) { return (r & 15) ^ ((r >> 4) << 2); }
 // Smallest share a wave takes: below it the per-wave start-up dominates.
 constexpr int kMinWaveTiles = 4;
+// Share skew between XCDs, per mille of the mean share.  On MI355X the odd
+// XCDs stream the page pattern of a decode batch about 9% slower than the
+// even ones (per-wave timestamps, every box measured), so with equal shares
+// the kernel ends with them.  Waves on even XCDs take 8% more tiles, waves
+// on odd XCDs 8% fewer: 1.7-2.2% less time per bf16 call at page sizes of 16
+// and more.  Where the per-tile compute, not HBM, sets the pace (the FP8
+// cache, pages below 16 tokens) the skew only idles the odd XCDs early, so
+// there it is 0.
+constexpr int kXcdSkewPerMille = 80;
 
 // 16-byte chunk c of token row r is stored at chunk c ^ swz(r).  Rows
 // 0..7 get distinct low-3-bit patterns (K reads: 8 consecutive rows, same
@@ -154,9 +164,22 @@ struct Cursor {
 // The wave's share of the flat tile sequence.
 struct Share {
   int g0, g1;   // [g0, g1): raw share (the last used wave also owns every unit past g1)
-  int tpw;
+  int te, to;   // tiles per share of a wave on an even / an odd XCD
   bool last;
   bool split;   // S >= 2: pieces may cut units; S == 1: whole units only
+  // First tile of share j, the share of wave j = 4 b + i (lane-wave i of
+  // workgroup b, which the dispatcher places on XCD b mod 8): each pair of
+  // workgroups covers 4 (te + to) tiles.
+  __device__ int start(int j) const {
+    const int b = j >> 2, i = j & 3;
+    return (b >> 1) * 4 * (te + to) + ((b & 1) ? 4 * te + i * to : i * te);
+  }
+  // the share holding tile p (the inverse of start)
+  __device__ int of(int p) const {
+    const int pair = p / (4 * (te + to));
+    const int rem = p - pair * 4 * (te + to);
+    return rem < 4 * te ? 8 * pair + rem / te : 8 * pair + 4 + (rem - 4 * te) / to;
+  }
 };
 
 constexpr int kQSlotBytes = 16 * kD * 2;                 // query rows of one piece (G <= 16)
@@ -223,16 +246,20 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
   const int U = nt_sum * Hkv;
   Share sh;
   sh.split = S >= 2;
-  int tpw = max((U + n_waves - 1) / n_waves, kMinWaveTiles);
-  // a unit of n tiles cut every tpw tiles at an arbitrary offset spans at
-  // most floor((n - 1) / tpw) + 2 shares: keep that <= S
-  if (sh.split) tpw = max(tpw, (nt_max - 1) / (S - 1) + 1);
-  sh.tpw = tpw = uniform(tpw);
-  const int w_used = uniform(max((U + tpw - 1) / tpw, 1));
+  // a unit of n tiles cut every t tiles at an arbitrary offset spans at
+  // most floor((n - 1) / t) + 2 shares: keep that <= S for the smaller share
+  const int t_min = sh.split ? max((nt_max - 1) / (S - 1) + 1, kMinWaveTiles) : kMinWaveTiles;
+  const int tpw = uniform(max((U + n_waves - 1) / n_waves, t_min));   // mean share
+  // the skew needs the round-robin placement of workgroups on the 8 XCDs
+  constexpr int kSkew = (F8 || PS < 16) ? 0 : kXcdSkewPerMille;
+  const int dx = uniform((gridDim.x & 7) == 0 ? min(tpw * kSkew / 1000, tpw - t_min) : 0);
+  sh.te = tpw + dx;
+  sh.to = tpw - dx;
+  const int w_used = uniform(U > 0 ? sh.of(U - 1) + 1 : 1);
   if (w >= w_used) return;
-  sh.g0 = w * tpw;
+  sh.g0 = sh.start(w);
   sh.last = w == w_used - 1;
-  sh.g1 = sh.last ? U : sh.g0 + tpw;
+  sh.g1 = sh.last ? U : sh.start(w + 1);
 
   // ---- first unit of the share ------------------------------------------
   // split: the unit holding tile g0, or an empty unit starting at or after
@@ -525,7 +552,7 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
         if (a.lse != nullptr && g4 == 0)
           a.lse[row * a.lse_sb + hq] = piece_bad ? nan : lse_nat;
       } else {
-        const int s = sh.split ? w - cu.p0 / sh.tpw : 0;
+        const int s = sh.split ? w - sh.of(cu.p0) : 0;
         float* slot = a.ws + ((row * a.Hq + hq) * S + s) * (kD + 1);
         const float inv = empty ? 0.f : v_mult / l_tot;
 #pragma unroll
@@ -806,7 +833,7 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
         }
       }
     } else if (sh.split && cw.p0 >= sh.g0) {
-      const int nseg = (cw.p0 + cw.r.nt - 1) / sh.tpw - cw.p0 / sh.tpw + 1;
+      const int nseg = sh.of(cw.p0 + cw.r.nt - 1) - sh.of(cw.p0) + 1;
       for (int i = lane; i < R * (S - nseg); i += 64) {
         const int n = i / (S - nseg), s = nseg + i % (S - nseg);
         a.ws[((col_row(n) * a.Hq + col_head(n)) * S + s) * (kD + 1) + kD] = neg_inf();
