@@ -74,9 +74,9 @@ constexpr int kMinWaveTiles = 4;
 // XCDs stream the page pattern of a decode batch about 9% slower than the
 // even ones (per-wave timestamps, every box measured), so with equal shares
 // the kernel ends with them.  Waves on even XCDs take 8% more tiles, waves
-// on odd XCDs 8% fewer: 1.7-2.2% less time per bf16 call at page sizes of 16
+// on odd XCDs 8% fewer: 1.5-3.8% less time per bf16 call at page sizes of 4
 // and more.  Where the per-tile compute, not HBM, sets the pace (the FP8
-// cache, pages below 16 tokens) the skew only idles the odd XCDs early, so
+// cache, pages of 1 or 2 tokens) the skew only idles the odd XCDs early, so
 // there it is 0.
 constexpr int kXcdSkewPerMille = 80;
 
@@ -251,7 +251,7 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
   const int t_min = sh.split ? max((nt_max - 1) / (S - 1) + 1, kMinWaveTiles) : kMinWaveTiles;
   const int tpw = uniform(max((U + n_waves - 1) / n_waves, t_min));   // mean share
   // the skew needs the round-robin placement of workgroups on the 8 XCDs
-  constexpr int kSkew = (F8 || PS < 16) ? 0 : kXcdSkewPerMille;
+  constexpr int kSkew = (F8 || PS < 4) ? 0 : kXcdSkewPerMille;
   const int dx = uniform((gridDim.x & 7) == 0 ? min(tpw * kSkew / 1000, tpw - t_min) : 0);
   sh.te = tpw + dx;
   sh.to = tpw - dx;
