@@ -77,6 +77,15 @@ constexpr int kPBufBytes = kWaves * 2 * 1024;                      // P^T of one
 // than this above the reference (fp32 / bf16 hold 2^127; with up to 2^20
 // keys and |V| < 2^40 the accumulator cannot overflow).
 constexpr float kRefHeadroomLog2 = 64.f;
+// Fixed cost of a piece in tiles' worth of time: its query fragments, the
+// refill of the tile ring and the epilogue (statistics through LDS, the
+// partial or output write).  Per-workgroup timestamps at the verify config
+// put it near 16 us, about 7 tiles: workgroups with three pieces ended 30 us
+// after those with one.  The plan counts it as virtual tiles at the start
+// of every request, so a share that starts more pieces gets fewer real
+// tiles (kernel time -1.4% bf16, -3.7% FP8, -3.9% at page size 1; 4 to 10
+// tiles measured, 7 and 10 alike).
+constexpr int kPieceTiles = 8;
 
 // LDS layout of a bf16 tile.  A 32-token tile is two 16-row page regions
 // of 18 blocks of 1 KB.  Block 2 C + R holds 16-byte chunks 8 C .. 8 C + 7
@@ -134,9 +143,10 @@ void mla_verify_kernel(MlaArgs a) {
   // L2 hit for the others.  Logical workgroup ids are XCD-remapped (hardware
   // hands consecutive ids to the 8 XCDs round-robin) so a group shares one
   // XCD and its L2.  Request b counts nt_b tiles, those of its last row block
-  // (the largest row limit); all requests' tiles in order form one flat
+  // (the largest row limit), preceded by kPieceTiles virtual tiles standing
+  // for a piece's fixed cost; all requests' tiles in order form one flat
   // sequence of U tiles and group g takes the equal contiguous share
-  // [g T, g T + T): every group streams the same number of tiles whatever
+  // [g T, g T + T): every group gets the same time's worth of work whatever
   // the length mix.  Where a share cuts a request, each piece is a split with
   // its own partial slot; T is raised until no request spans more than S
   // shares.  With S == 1 shares are rounded to whole requests and results
@@ -165,10 +175,12 @@ void mla_verify_kernel(MlaArgs a) {
     return block_tiles(L, unit_real(b, L), n_rb - 1);
   };
 
+  // U counts every request's tiles plus kPieceTiles virtual ones before them
   int nt_sum = 0, nt_max = 0;
   for (int base = 0; base < a.B; base += 64) {
-    const int t = base + lane < a.B ? req_tiles(base + lane) : 0;
-    nt_sum += wave_sum(t);
+    const bool in = base + lane < a.B;
+    const int t = in ? req_tiles(base + lane) : 0;
+    nt_sum += wave_sum(in ? t + kPieceTiles : 0);
     nt_max = max(nt_max, wave_max(t));
   }
   const int U = __builtin_amdgcn_readfirstlane(nt_sum);
@@ -191,7 +203,7 @@ void mla_verify_kernel(MlaArgs a) {
     int C = 0;
     for (int base = 0; base < a.B; base += 64) {
       const bool in = base + lane < a.B;
-      const int req = in ? req_tiles(base + lane) : 0;
+      const int req = in ? req_tiles(base + lane) + kPieceTiles : 0;
       const int incl = wave_incl_sum(req);
       const int cb1 = C + incl, cb = cb1 - req;
       const uint64_t m = __ballot(in && (cb1 > g0 || cb >= g0));
@@ -794,15 +806,17 @@ void mla_verify_kernel(MlaArgs a) {
   while (ub < a.B && (last || up0 < g1)) {
     const int L = unit_len(ub), Lr = unit_real(ub, L);
     const int ntb = __builtin_amdgcn_readfirstlane(block_tiles(L, Lr, n_rb - 1));
-    const bool owner = up0 >= g0;   // the request starts in this share
+    const bool owner = up0 >= g0;   // the request (its virtual tiles) starts in this share
+    const int rs = up0 + kPieceTiles;   // its first real tile
     int i0 = 0, i1 = ntb;
     if (split_mode) {
-      i0 = max(g0 - up0, 0);
-      i1 = min(ntb, g1 - up0);
+      i0 = max(g0 - rs, 0);
+      i1 = min(ntb, g1 - rs);
     } else if (!owner) {
       i1 = 0;   // whole requests only: it belongs to an earlier share
     }
-    const int slot = split_mode ? __builtin_amdgcn_readfirstlane(grp - up0 / T) : 0;
+    // slots count from the share that holds the request's first real tile
+    const int slot = split_mode ? __builtin_amdgcn_readfirstlane(grp - rs / T) : 0;
     for (int rb = member; rb < n_rb; rb += gs) {
       const int nt = __builtin_amdgcn_readfirstlane(block_tiles(L, Lr, rb));
       const int j1 = min(i1, nt);
@@ -810,7 +824,7 @@ void mla_verify_kernel(MlaArgs a) {
       if (owner && (nt == 0 || split_mode)) {
         // lse = -inf in the split slots no piece of the unit uses (all of
         // them for a unit with no key), or O = 0 / LSE = -inf written directly
-        const int nseg = nt > 0 ? (up0 + nt - 1) / T - up0 / T + 1 : 0;
+        const int nseg = nt > 0 ? (rs + nt - 1) / T - rs / T + 1 : 0;
         const int my_row = rb * kRowsPerBlock + wave * kRowsPerWave + l32;
         if (my_row < rows_req) {
           const int t_row = my_row / a.H, h_row = my_row % a.H;
@@ -826,7 +840,7 @@ void mla_verify_kernel(MlaArgs a) {
         }
       }
     }
-    up0 += ntb;
+    up0 += ntb + kPieceTiles;
     ++ub;
   }
 }
