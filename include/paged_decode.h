@@ -294,8 +294,9 @@ PD_API int paged_decode_gqa_partials(const void* q, int64_t q_stride_b, int64_t 
  * total_rows is ignored; cu_seqlens_q non-NULL: qlen is max_qlen and the
  * rows are the varlen ones (total_rows of them; total_rows = 0 with B > 0
  * returns PD_OK at once).  Writes every (row, query head, split) slot of
- * `workspace` ([rows, Hq, S, D + 1] fp32, S = num_kv_splits >= 1) and
- * launches no merge; a slot a row does not use gets lse = -inf.
+ * `workspace` ([rows, Hq, S, D + 1] fp32, S = num_kv_splits >= 1; for an
+ * FP8 cache O is already multiplied by v_scale) and launches no merge; a
+ * slot a row does not use gets lse = -inf.
  * merge_splits over that workspace, with the sinks, gives exactly the full
  * call's result.  The per-shard half of split-KV for verify, as
  * paged_decode_gqa_partials is for decode.  Workspace bytes >=
