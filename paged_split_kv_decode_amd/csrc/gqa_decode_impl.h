@@ -250,9 +250,11 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
   // most floor((n - 1) / t) + 2 shares: keep that <= S for the smaller share
   const int t_min = sh.split ? max((nt_max - 1) / (S - 1) + 1, kMinWaveTiles) : kMinWaveTiles;
   const int tpw = uniform(max((U + n_waves - 1) / n_waves, t_min));   // mean share
-  // the skew needs the round-robin placement of workgroups on the 8 XCDs
+  // the skew needs the round-robin placement of workgroups on the 8 XCDs of
+  // the whole chip (one workgroup per CU: 256); a partitioned device places
+  // them otherwise and gets equal shares
   constexpr int kSkew = (F8 || PS < 4) ? 0 : kXcdSkewPerMille;
-  const int dx = uniform((gridDim.x & 7) == 0 ? min(tpw * kSkew / 1000, tpw - t_min) : 0);
+  const int dx = uniform(gridDim.x == 256 ? min(tpw * kSkew / 1000, tpw - t_min) : 0);
   sh.te = tpw + dx;
   sh.to = tpw - dx;
   const int w_used = uniform(U > 0 ? sh.of(U - 1) + 1 : 1);
