@@ -12,7 +12,8 @@
  *   paged_verify_mla   qlen causal "verify" tokens per request over one shared
  *                      latent cache, V read as K[..., :Lv], bf16 or FP8 cache;
  *   *_partials         the split partials of a call, without the merge;
- *   num_kv_splits_cap  static split cap from static sizes (graph-capture safe);
+ *   num_kv_splits_cap  static split cap from static sizes (graph-capture safe;
+ *                      pd_gqa_split_cap / pd_mla_split_cap / pd_split_rule);
  *   merge_splits       merges fp32 split partials into O and a natural-log LSE.
  *
  * Conventions shared by every entry point
@@ -77,7 +78,47 @@ typedef enum { PD_KV_BF16 = 0, PD_KV_FP8_E4M3FN = 1 } pd_kv_dtype;
 PD_API const char* pd_status_string(int status);
 
 /*
- * num_kv_splits_cap - static upper bound on KV splits per request.
+ * num_kv_splits_cap - [host] the static split cap this library's kernels
+ * are tuned for, from static sizes only (graph-capture safe).
+ *
+ * head_dim_k == 576 with num_kv_heads == 1 selects the MLA verify kernel
+ * (a program is one (request, 128-row block) pair); head_dim_k == 128 the
+ * GQA kernel (a program is one (request, kv head) pair, whatever qlen: the
+ * verify tokens of a kv head share its key stream).  The cap is
+ * pd_split_rule with that kernel's policy:
+ *   GQA: block_h 1, occupancy 1, min_work_per_split 256, max_splits 64,
+ *        balance_chunk 1024;
+ *   MLA: block_h 128, occupancy 1, min_work_per_split 128, max_splits 16,
+ *        balance_chunk 2048;
+ * num_cus = the compute units of `device` (< 0: the current device).
+ * max_splits > 0 lowers the policy's max_splits to it; <= 0 keeps it.
+ * For a GQA call with a sliding window use pd_gqa_split_cap, which bounds
+ * the keys by the window.  Returns the cap (>= 1), PD_ERR_INVALID for
+ * negative sizes or num_q_heads % num_kv_heads != 0, PD_ERR_UNSUPPORTED for
+ * another head_dim_k, PD_ERR_HIP if the device query fails.
+ */
+PD_API int32_t num_kv_splits_cap(int32_t max_seq_len, int32_t batch, int32_t qlen,
+                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim_k,
+                          int32_t max_splits, int32_t device);
+
+/*
+ * [host] The GQA policy of num_kv_splits_cap with a window: the keys of a
+ * (request, kv head) are min(max_seq_len, window) for window > 0, else
+ * max_seq_len.  The cap paged_decode_gqa / paged_verify_gqa(_varlen) are
+ * tuned for.  num_cus <= 0 queries the current device.  Same return values.
+ */
+PD_API int32_t pd_gqa_split_cap(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len,
+                                int32_t window, int32_t num_cus);
+
+/*
+ * [host] The MLA policy of num_kv_splits_cap: the cap paged_verify_mla is
+ * tuned for.  num_cus <= 0 queries the current device.  Same return values.
+ */
+PD_API int32_t pd_mla_split_cap(int32_t batch, int32_t qlen, int32_t num_heads,
+                                int32_t max_seq_len, int32_t num_cus);
+
+/*
+ * pd_split_rule - [host] the split rule itself, with every knob exposed.
  *
  * Restates "vllm.v1.attention.ops.triton_decode_attention",
  * verify_num_kv_splits: a program is one (request, row block) pair, with
@@ -96,16 +137,14 @@ PD_API const char* pd_status_string(int status);
  * keys any one split of the longest request can hold.  balance_chunk <= 0
  * gives the unmodified rule.
  *
- * For GQA decode pass qlen = 1, num_heads = num_kv_heads, block_h = 1 (one
- * program per (request, kv head)).  num_cus <= 0 queries the current device.
- * Pure host function; it reads no device data.  Returns the cap (>= 1), or a
- * negative pd_status for negative sizes, block_h < 1, occupancy <= 0,
- * max_splits < 1, or a failed device query.
+ * num_cus <= 0 queries the current device.  Reads no device data.  Returns
+ * the cap (>= 1), or a negative pd_status for negative sizes, block_h < 1,
+ * occupancy <= 0, max_splits < 1, or a failed device query.
  */
-PD_API int32_t num_kv_splits_cap(int32_t max_seq_len, int32_t batch, int32_t qlen,
-                          int32_t num_heads, int32_t block_h, int32_t num_cus,
-                          float occupancy, int32_t min_work_per_split,
-                          int32_t max_splits, int32_t balance_chunk);
+PD_API int32_t pd_split_rule(int32_t max_seq_len, int32_t batch, int32_t qlen,
+                             int32_t num_heads, int32_t block_h, int32_t num_cus,
+                             float occupancy, int32_t min_work_per_split,
+                             int32_t max_splits, int32_t balance_chunk);
 
 /*
  * [host] Bytes of fp32 workspace a call with `num_splits` > 1 needs:

@@ -584,18 +584,26 @@ def verify_num_kv_splits(max_seq_len: int, batch: int, qlen: int, num_heads: int
       5% of the best;
     * the result is clamped to ``[1, min(ideal, 2 * sm_count)]``.
     """
-    row_blocks = _cdiv(qlen * num_heads, block_h)
-    per_split = max(1, batch) * row_blocks
+    # programs in flight for one split of every request
+    programs = max(1, batch) * _cdiv(qlen * num_heads, block_h)
     ideal = _cdiv(max(1, max_seq_len), max(1, min_work_per_split))
     slots = max(1, int(occupancy * sm_count))
-    if per_split <= slots:
-        n = slots // per_split
+    if programs <= slots:
+        # a single round holds one split of every request: fill that round
+        n = slots // programs
     else:
-        costs = [(_cdiv(k * per_split, slots) / k, k)
-                 for k in range(1, max(1, min(ideal, max_splits)) + 1)]
-        best = min(c for c, _ in costs)
-        n = min(k for c, k in costs if c <= best * 1.05)
-    return max(1, min(ideal, n, sm_count * 2))
+        # rounds each split costs, for 1 .. limit splits; the fewest splits
+        # whose cost is within 5% of the lowest
+        limit = max(1, min(ideal, max_splits))
+        cost = {}
+        for k in range(1, limit + 1):
+            cost[k] = _cdiv(k * programs, slots) / k
+        lowest = min(cost.values())
+        n = 1
+        while cost[n] > lowest * 1.05:
+            n += 1
+    n = min(n, ideal, 2 * sm_count)
+    return max(n, 1)
 
 
 __all__ = [

@@ -22,6 +22,7 @@ from .api import (  # noqa: F401
     paged_verify_gqa_varlen,
     paged_verify_mla,
     paged_verify_mla_partials,
+    split_rule,
     workspace_bytes,
 )
 from ._native import LIB_PATH, PagedDecodeError  # noqa: F401

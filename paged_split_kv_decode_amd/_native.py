@@ -24,6 +24,9 @@ PD_KV_FP8_E4M3FN = 1
 EXPORTS = (
     "pd_status_string",
     "num_kv_splits_cap",
+    "pd_gqa_split_cap",
+    "pd_mla_split_cap",
+    "pd_split_rule",
     "pd_workspace_bytes",
     "paged_decode_gqa",
     "paged_verify_gqa",
@@ -55,9 +58,15 @@ def _load():
     lib = ctypes.CDLL(LIB_PATH)
     lib.pd_status_string.argtypes = [ctypes.c_int]
     lib.pd_status_string.restype = ctypes.c_char_p
-    lib.num_kv_splits_cap.argtypes = [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f32,
-                                      _c_i32, _c_i32, _c_i32]
+    lib.num_kv_splits_cap.argtypes = [_c_i32] * 8
     lib.num_kv_splits_cap.restype = _c_i32
+    lib.pd_gqa_split_cap.argtypes = [_c_i32] * 5
+    lib.pd_gqa_split_cap.restype = _c_i32
+    lib.pd_mla_split_cap.argtypes = [_c_i32] * 5
+    lib.pd_mla_split_cap.restype = _c_i32
+    lib.pd_split_rule.argtypes = [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f32,
+                                  _c_i32, _c_i32, _c_i32]
+    lib.pd_split_rule.restype = _c_i32
     lib.pd_workspace_bytes.argtypes = [_c_i32, _c_i32, _c_i32, _c_i32]
     lib.pd_workspace_bytes.restype = _c_sz
     lib.paged_decode_gqa.argtypes = [

@@ -16,17 +16,6 @@ import torch
 from . import _native
 from ._native import PD_KV_BF16, PD_KV_FP8_E4M3FN, check, lib
 
-# Split-cap policy of this build (arguments of num_kv_splits_cap).
-GQA_OCCUPANCY = 1.0          # resident decode workgroups per CU (128 KB LDS each)
-GQA_MIN_WORK = 256           # keys per split before a request uses fewer splits
-GQA_MAX_SPLITS = 64
-GQA_BALANCE_CHUNK = 1024     # skew bound: pieces of the longest request may be this short
-MLA_BLOCK_H = 128            # verify rows (qlen * heads) per workgroup
-MLA_OCCUPANCY = 1.0
-MLA_MIN_WORK = 128
-MLA_MAX_SPLITS = 16
-MLA_BALANCE_CHUNK = 2048
-
 
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
@@ -49,31 +38,43 @@ def _need(t, name, dtype, dim=None):
         raise ValueError(f"{name} must be {dim}-D, got shape {tuple(t.shape)}")
 
 
-def num_kv_splits_cap(max_seq_len: int, batch: int, qlen: int, num_heads: int, block_h: int,
-                      num_cus: int = 0, occupancy: float = 1.0, min_work_per_split: int = 64,
-                      max_splits: int = 8, balance_chunk: int = 0) -> int:
-    """Static split cap (see include/paged_decode.h); a pure host function."""
-    r = lib.num_kv_splits_cap(int(max_seq_len), int(batch), int(qlen), int(num_heads),
-                              int(block_h), int(num_cus), float(occupancy),
-                              int(min_work_per_split), int(max_splits), int(balance_chunk))
+def _cap(fn: str, r: int) -> int:
     if r < 0:
-        check("num_kv_splits_cap", r)
+        check(fn, r)
     return int(r)
+
+
+def num_kv_splits_cap(max_seq_len: int, batch: int, qlen: int, num_q_heads: int,
+                      num_kv_heads: int, head_dim_k: int, max_splits: int = 0,
+                      device: int = -1) -> int:
+    """Static split cap the kernels are tuned for (include/paged_decode.h:
+    num_kv_splits_cap); a pure host function."""
+    return _cap("num_kv_splits_cap", lib.num_kv_splits_cap(
+        int(max_seq_len), int(batch), int(qlen), int(num_q_heads), int(num_kv_heads),
+        int(head_dim_k), int(max_splits), int(device)))
 
 
 def gqa_split_cap(batch: int, num_kv_heads: int, max_seq_len: int, window: int = 0,
                   num_cus: int = 0) -> int:
-    """Split cap for paged_decode_gqa: one program per (request, kv head)."""
-    eff = min(max_seq_len, window) if window and window > 0 else max_seq_len
-    return num_kv_splits_cap(eff, batch, 1, num_kv_heads, 1, num_cus, GQA_OCCUPANCY,
-                             GQA_MIN_WORK, GQA_MAX_SPLITS, GQA_BALANCE_CHUNK)
+    """Split cap for the GQA calls (include/paged_decode.h: pd_gqa_split_cap)."""
+    return _cap("pd_gqa_split_cap", lib.pd_gqa_split_cap(
+        int(batch), int(num_kv_heads), int(max_seq_len), int(window or 0), int(num_cus)))
 
 
 def mla_split_cap(batch: int, qlen: int, num_heads: int, max_seq_len: int,
                   num_cus: int = 0) -> int:
-    """Split cap for paged_verify_mla: one program per (request, row block)."""
-    return num_kv_splits_cap(max_seq_len, batch, qlen, num_heads, MLA_BLOCK_H, num_cus,
-                             MLA_OCCUPANCY, MLA_MIN_WORK, MLA_MAX_SPLITS, MLA_BALANCE_CHUNK)
+    """Split cap for paged_verify_mla (include/paged_decode.h: pd_mla_split_cap)."""
+    return _cap("pd_mla_split_cap", lib.pd_mla_split_cap(
+        int(batch), int(qlen), int(num_heads), int(max_seq_len), int(num_cus)))
+
+
+def split_rule(max_seq_len: int, batch: int, qlen: int, num_heads: int, block_h: int,
+               num_cus: int = 0, occupancy: float = 1.0, min_work_per_split: int = 64,
+               max_splits: int = 8, balance_chunk: int = 0) -> int:
+    """The split rule with every knob (include/paged_decode.h: pd_split_rule)."""
+    return _cap("pd_split_rule", lib.pd_split_rule(
+        int(max_seq_len), int(batch), int(qlen), int(num_heads), int(block_h), int(num_cus),
+        float(occupancy), int(min_work_per_split), int(max_splits), int(balance_chunk)))
 
 
 def workspace_bytes(rows: int, num_heads: int, num_splits: int, head_dim_v: int) -> int:
@@ -101,6 +102,8 @@ def paged_decode_gqa(q, kv, block_table, seq_lens, sm_scale, sinks=None, window=
     _need(kv, "kv", torch.bfloat16, 4)
     _need(block_table, "block_table", torch.int32, 2)
     _need(seq_lens, "seq_lens", torch.int32, 1)
+    if seq_lens.stride(0) != 1:
+        raise ValueError("seq_lens must be contiguous")
     B, Hq, D = q.shape
     num_pages, Hkv, P, two_d = kv.shape
     if two_d != 2 * D or kv.stride(3) != 1 or kv.stride(2) != 2 * D or q.stride(2) != 1:
@@ -223,6 +226,8 @@ def _verify_gqa(q, kv, block_table, seq_lens, B, qlen, cu_seqlens_q, sm_scale, s
         raise ValueError("kv must be a 4-D device tensor")
     _need(block_table, "block_table", torch.int32, 2)
     _need(seq_lens, "seq_lens", torch.int32, 1)
+    if seq_lens.stride(0) != 1:
+        raise ValueError("seq_lens must be contiguous")
     rows, Hq, D = q.shape
     num_pages, Hkv, P, two_d = kv.shape
     if two_d != 2 * D or kv.stride(3) != 1 or kv.stride(2) != 2 * D or q.stride(2) != 1:
@@ -310,6 +315,8 @@ def paged_kv_append(cache, block_table, seq_lens, src0, src1=None, qlen=1, layou
         raise TypeError("cache must be bf16 or FP8 (uint8 / float8_e4m3fn) elements")
     _need(block_table, "block_table", torch.int32, 2)
     _need(seq_lens, "seq_lens", torch.int32, 1)
+    if seq_lens.stride(0) != 1:
+        raise ValueError("seq_lens must be contiguous")
     qlen = int(qlen)
     if src0.dim() == 2:
         src0 = src0.unsqueeze(1)
@@ -358,12 +365,14 @@ def paged_decode_gqa_partials(q, kv, block_table, seq_lens, sm_scale, window=0,
     _need(kv, "kv", torch.bfloat16, 4)
     _need(block_table, "block_table", torch.int32, 2)
     _need(seq_lens, "seq_lens", torch.int32, 1)
+    if seq_lens.stride(0) != 1:
+        raise ValueError("seq_lens must be contiguous")
     B, Hq, D = q.shape
     num_pages, Hkv, P, two_d = kv.shape
     if two_d != 2 * D or kv.stride(3) != 1 or kv.stride(2) != 2 * D or q.stride(2) != 1:
         raise ValueError("kv must be [pages, Hkv, P, 2D] with contiguous token rows")
-    if block_table.stride(1) != 1:
-        raise ValueError("block_table rows must be contiguous")
+    if block_table.shape[0] != B or seq_lens.shape[0] != B or block_table.stride(1) != 1:
+        raise ValueError("block_table / seq_lens must have one row per request")
     S = int(num_kv_splits)
     n = B * Hq * S * (D + 1)
     if workspace is None:
@@ -409,6 +418,8 @@ def _verify_mla(q, kv, block_table, seq_lens, real_seq_lens, qlen, sm_scale, hea
     _need(q, "q", torch.bfloat16, 3)
     _need(block_table, "block_table", torch.int32, 2)
     _need(seq_lens, "seq_lens", torch.int32, 1)
+    if seq_lens.stride(0) != 1:
+        raise ValueError("seq_lens must be contiguous")
     rows, H, Lk = q.shape
     if kv.dtype == torch.bfloat16:
         kv_dtype = PD_KV_BF16
@@ -436,13 +447,20 @@ def _verify_mla(q, kv, block_table, seq_lens, real_seq_lens, qlen, sm_scale, hea
         raise ValueError("kv must be 3-D or 4-D")
     if kv.shape[-1] != Lk or kv.stride(-1) != 1 or q.stride(2) != 1:
         raise ValueError("cache / q last dims must match Lk and be contiguous")
-    if rows % qlen:
+    qlen = int(qlen)
+    if qlen < 1 or rows % qlen:
         raise ValueError("q rows must be a multiple of qlen")
     B = rows // qlen
+    if block_table.shape[0] != B or seq_lens.shape[0] != B or block_table.stride(1) != 1:
+        raise ValueError("block_table / seq_lens must have one contiguous row per request")
     if real_seq_lens is not None:
         _need(real_seq_lens, "real_seq_lens", torch.int32, 1)
+        if real_seq_lens.shape[0] != B or real_seq_lens.stride(0) != 1:
+            raise ValueError("real_seq_lens must be a contiguous [B] tensor")
     if k_scale is not None:
         _need(k_scale, "k_scale", torch.float32)
+        if k_scale.numel() < 1:
+            raise ValueError("k_scale must hold one value")
     Lv = int(head_dim_v)
     S = int(num_kv_splits)
     head = (_ptr(q), q.stride(0), q.stride(1),
@@ -491,6 +509,14 @@ def merge_splits(workspace, rows, num_heads, num_splits, head_dim_v, sinks=None,
         lse = torch.empty((rows, num_heads), dtype=torch.float32, device=dev)
     if sinks is not None:
         _need(sinks, "sinks", torch.float32, 1)
+        if sinks.shape[0] != int(num_heads) or sinks.stride(0) != 1:
+            raise ValueError("sinks must be a contiguous [num_heads] tensor")
+    _need(out, "out", torch.bfloat16, 3)
+    _need(lse, "lse", torch.float32, 2)
+    for name, t, shape in (("out", out, (rows, num_heads, head_dim_v)),
+                           ("lse", lse, (rows, num_heads))):
+        if tuple(t.shape) != tuple(int(x) for x in shape) or t.stride(-1) != 1:
+            raise ValueError(f"{name} must be {tuple(shape)} with a contiguous last dim")
     st = lib.merge_splits(_ptr(workspace), int(rows), int(num_heads), int(num_splits),
                           int(head_dim_v), _ptr(sinks), _ptr(out), out.stride(0),
                           out.stride(1), _ptr(lse), lse.stride(0), _stream(stream))
@@ -503,5 +529,5 @@ __all__ = [
     "mla_split_cap", "num_kv_splits_cap", "paged_decode_gqa", "paged_decode_gqa_partials",
     "paged_kv_append", "paged_verify_gqa", "paged_verify_gqa_partials",
     "paged_verify_gqa_varlen", "paged_verify_mla", "paged_verify_mla_partials",
-    "workspace_bytes", "_native",
+    "split_rule", "workspace_bytes", "_native",
 ]

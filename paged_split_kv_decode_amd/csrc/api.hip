@@ -20,6 +20,37 @@ int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 constexpr int32_t kMaxPageSize = 1 << 16;
 bool pow2_page(int32_t p) { return p >= 1 && p <= kMaxPageSize && (p & (p - 1)) == 0; }
 
+constexpr int32_t kGqaHeadDim = 128;
+constexpr int32_t kMlaHeadDimK = 576;
+
+// Split policy the kernels are tuned for: the arguments this library passes
+// to pd_split_rule.  GQA: one program per (request, kv head), one decode
+// workgroup per CU; MLA: one program per (request, 128-row block).
+struct SplitPolicy {
+  int32_t block_h;
+  float occupancy;
+  int32_t min_work;       // keys per split before a request uses fewer splits
+  int32_t max_splits;
+  int32_t balance_chunk;  // skew bound: pieces of the longest request may be this short
+};
+constexpr SplitPolicy kGqaPolicy{1, 1.0f, 256, 64, 1024};
+constexpr SplitPolicy kMlaPolicy{128, 1.0f, 128, 16, 2048};
+
+// Compute units of a device (< 0: the current one), queried once per device;
+// 0 if the query fails.
+int32_t device_cus(int32_t device) {
+  static int32_t cached[64] = {0};
+  int dev = device;
+  if (dev < 0 && hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -36,19 +67,15 @@ const char* pd_status_string(int status) {
   }
 }
 
-int32_t num_kv_splits_cap(int32_t max_seq_len, int32_t batch, int32_t qlen, int32_t num_heads,
-                          int32_t block_h, int32_t num_cus, float occupancy,
-                          int32_t min_work_per_split, int32_t max_splits,
-                          int32_t balance_chunk) {
+int32_t pd_split_rule(int32_t max_seq_len, int32_t batch, int32_t qlen, int32_t num_heads,
+                      int32_t block_h, int32_t num_cus, float occupancy,
+                      int32_t min_work_per_split, int32_t max_splits, int32_t balance_chunk) {
   if (max_seq_len < 0 || batch < 0 || qlen < 1 || num_heads < 1 || block_h < 1 ||
       !(occupancy > 0.f) || max_splits < 1)
     return PD_ERR_INVALID;
   if (num_cus <= 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return PD_ERR_HIP;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return PD_ERR_HIP;
-    num_cus = n;
+    num_cus = device_cus(-1);
+    if (num_cus <= 0) return PD_ERR_HIP;
   }
   const int64_t row_blocks = cdiv64((int64_t)qlen * num_heads, block_h);
   const int64_t per_split = (int64_t)(batch > 1 ? batch : 1) * row_blocks;
@@ -87,6 +114,46 @@ int32_t num_kv_splits_cap(int32_t max_seq_len, int32_t batch, int32_t qlen, int3
     if (bal > cap) cap = bal;
   }
   return (int32_t)cap;
+}
+
+int32_t pd_gqa_split_cap(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len,
+                         int32_t window, int32_t num_cus) {
+  if (batch < 0 || num_kv_heads < 1 || max_seq_len < 0) return PD_ERR_INVALID;
+  const int32_t cus = num_cus > 0 ? num_cus : device_cus(-1);
+  if (cus <= 0) return PD_ERR_HIP;
+  // keys one (request, kv head) can attend: the window bounds them
+  const int32_t keys = window > 0 && window < max_seq_len ? window : max_seq_len;
+  return pd_split_rule(keys, batch, 1, num_kv_heads, 1, cus, kGqaPolicy.occupancy,
+                       kGqaPolicy.min_work, kGqaPolicy.max_splits, kGqaPolicy.balance_chunk);
+}
+
+int32_t pd_mla_split_cap(int32_t batch, int32_t qlen, int32_t num_heads, int32_t max_seq_len,
+                         int32_t num_cus) {
+  if (batch < 0 || qlen < 1 || num_heads < 1 || max_seq_len < 0) return PD_ERR_INVALID;
+  const int32_t cus = num_cus > 0 ? num_cus : device_cus(-1);
+  if (cus <= 0) return PD_ERR_HIP;
+  return pd_split_rule(max_seq_len, batch, qlen, num_heads, kMlaPolicy.block_h, cus,
+                       kMlaPolicy.occupancy, kMlaPolicy.min_work, kMlaPolicy.max_splits,
+                       kMlaPolicy.balance_chunk);
+}
+
+int32_t num_kv_splits_cap(int32_t max_seq_len, int32_t batch, int32_t qlen,
+                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim_k,
+                          int32_t max_splits, int32_t device) {
+  if (max_seq_len < 0 || batch < 0 || qlen < 1 || num_q_heads < 1 || num_kv_heads < 1 ||
+      num_q_heads % num_kv_heads != 0)
+    return PD_ERR_INVALID;
+  const bool mla = head_dim_k == kMlaHeadDimK && num_kv_heads == 1;
+  if (!mla && head_dim_k != kGqaHeadDim) return PD_ERR_UNSUPPORTED;
+  const SplitPolicy& pol = mla ? kMlaPolicy : kGqaPolicy;
+  const int32_t cus = device_cus(device);
+  if (cus <= 0) return PD_ERR_HIP;
+  const int32_t top = max_splits > 0 && max_splits < pol.max_splits ? max_splits : pol.max_splits;
+  if (mla)
+    return pd_split_rule(max_seq_len, batch, qlen, num_q_heads, pol.block_h, cus, pol.occupancy,
+                         pol.min_work, top, pol.balance_chunk);
+  return pd_split_rule(max_seq_len, batch, 1, num_kv_heads, pol.block_h, cus, pol.occupancy,
+                       pol.min_work, top, pol.balance_chunk);
 }
 
 size_t pd_workspace_bytes(int32_t rows, int32_t num_heads, int32_t num_splits, int32_t head_dim_v) {

@@ -50,7 +50,7 @@ def test_status_strings():
 
 
 def _cap(*a):
-    return lib.num_kv_splits_cap(*a)
+    return lib.pd_split_rule(*a)
 
 
 @pytest.mark.parametrize("args,want", [
@@ -89,6 +89,60 @@ def test_split_cap_balance_extension():
     assert _cap(8192, 64, 1, 8, 1, 256, 1.0, 256, 64, 1024) == 8
     # and never above ideal = ceil(max_len / min_work)
     assert _cap(128, 64, 1, 8, 1, 256, 1.0, 256, 64, 16) == 1
+
+
+def _cdiv(a, b):
+    return -(-a // b)
+
+
+def _policy_want(keys, programs_batch, qlen, heads, block_h, cus, min_work, max_splits, chunk):
+    """The oracle's restated rule plus the documented skew bound."""
+    base = oracle.verify_num_kv_splits(keys, programs_batch, qlen, heads, cus, block_h, 1.0,
+                                       min_work, max_splits)
+    ideal = _cdiv(max(keys, 1), min_work)
+    return max(base, min(max_splits, ideal, _cdiv(max(keys, 1), chunk)))
+
+
+def test_gqa_policy_cap_matches_oracle_rule_and_skew_bound():
+    rng = random.Random(1)
+    for _ in range(2000):
+        msl = rng.choice([0, 1, 100, 1024, 8192, 32768, 131072, rng.randint(0, 300000)])
+        batch = rng.choice([1, 3, 64, 256, rng.randint(0, 4000)])
+        hkv = rng.choice([1, 2, 8, 16])
+        window = rng.choice([0, 0, 128, 4096, rng.randint(-5, 70000)])
+        cus = rng.choice([80, 256, 304])
+        keys = min(msl, window) if window > 0 else msl
+        want = _policy_want(keys, batch, 1, hkv, 1, cus, 256, 64, 1024)
+        assert lib.pd_gqa_split_cap(batch, hkv, msl, window, cus) == want
+
+
+def test_mla_policy_cap_matches_oracle_rule_and_skew_bound():
+    rng = random.Random(2)
+    for _ in range(2000):
+        msl = rng.choice([0, 1, 2048, 16384, 65536, rng.randint(0, 200000)])
+        batch = rng.choice([1, 4, 32, 128, rng.randint(0, 1000)])
+        qlen = rng.randint(1, 8)
+        heads = rng.choice([8, 16, 32, 128])
+        cus = rng.choice([80, 256, 304])
+        want = _policy_want(msl, batch, qlen, heads, 128, cus, 128, 16, 2048)
+        assert lib.pd_mla_split_cap(batch, qlen, heads, msl, cus) == want
+
+
+def test_policy_caps_at_the_configs():
+    # GQA with sinks, window, skewed batch; MLA verify (256 compute units)
+    assert lib.pd_gqa_split_cap(64, 8, 8192, 0, 256) == 8
+    assert lib.pd_gqa_split_cap(64, 8, 32768, 128, 256) == 1
+    assert lib.pd_gqa_split_cap(256, 8, 131072, 0, 256) == 64
+    assert lib.pd_mla_split_cap(32, 4, 128, 16384, 256) == 8
+
+
+def test_num_kv_splits_cap_checks_before_the_device_query():
+    f = lib.num_kv_splits_cap
+    assert f(-1, 1, 1, 8, 8, 128, 0, -1) == PD_ERR_INVALID
+    assert f(10, 1, 0, 8, 8, 128, 0, -1) == PD_ERR_INVALID
+    assert f(10, 1, 1, 12, 8, 128, 0, -1) == PD_ERR_INVALID        # Hq % Hkv
+    assert f(10, 1, 1, 8, 8, 64, 0, -1) == PD_ERR_UNSUPPORTED      # no kernel for D = 64
+    assert f(10, 1, 1, 8, 2, 576, 0, -1) == PD_ERR_UNSUPPORTED     # latent width needs one kv head
 
 
 def test_split_cap_rejects_bad_arguments():
