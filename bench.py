@@ -1,24 +1,44 @@
 """Benchmark of the paged split-KV decode hot path on one MI355X.
 
-Default workload: the GQA decode-with-sinks configuration (B=64 requests,
-Hq=64, Hkv=8, head_dim 128, 16-token HND pages in a 40000-page pool, seq_lens
-uniform in [1024, 8192], per-head sinks), seeded synthetic bf16 data resident
-in HBM.  One step is one full paged_decode_gqa call: the split decode kernel
-plus the split merge.
+Default workload: the skewed long-context GQA decode batch, the largest
+configuration that fits one GPU: B=256 requests, Hq=32, Hkv=8, head_dim 128,
+16-token HND pages, seq_lens log-uniform over [16, 131072] with 4 empty
+requests, a pool of exactly the pages in use (about 15 GB of bf16 KV per
+call).  Seeded synthetic data, resident in HBM before timing starts.  One
+step is one full paged_decode_gqa call: the split decode kernel plus the
+split merge.
 
-Printed: ONE JSON line with KV-read GB/s (algorithmic K+V bytes of the
-attended keys / time per call), the roofline of the dominant kernel measured
-with HIP events on the launch stream, and the fp64 CPU oracle's rate on the
-same inputs.  ``--config`` selects another workload (gqa_window, gqa_skewed,
-tiny_gqa, gqa_verify, gqa_verify_varlen, gqa_sinks_fp8, kv_append, mla_verify,
-mla_verify_fp8).
+Printed: ONE JSON line.
+* ``value``: algorithmic KV bytes per call / time per call (GB/s), over the
+  K timed steps (eager launches on the current stream, HIP events around
+  all of them, after W warm-up steps).
+* ``roofline``: the attention kernel alone, from HIP-graph replays of
+  back-to-back launches (the partials-only entry when the call splits), the
+  median of 5 passes of at least 50 ms; ``achieved`` = algorithmic bytes
+  (MLA: flops) / that time.  ``kernel_le_call`` checks that it does not
+  exceed the full call's time.
+* ``stream_ceiling``: the machine's streaming-read rate measured in the same
+  run with the library's read probe (4 GiB, non-temporal 16-byte loads).
+* ``cpu_baseline``: the fp64 oracle on a bounded sample of the same inputs.
+
+When a call's KV working set is below 1 GiB (4x the 256 MB Infinity Cache)
+the calls rotate over R independent copies so that each reads cold data:
+R block tables over the same large pool (sliding window; FP8 cache), or R
+copies of a pool that holds only the pages in use (MLA).  The hot figures
+(one copy) are reported beside them.
+
+``--config`` selects another workload: gqa_sinks, gqa_window, tiny_gqa,
+gqa_verify, gqa_verify_varlen, gqa_sinks_fp8, kv_append, mla_verify,
+mla_verify_fp8.
 """
 
 from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
+import statistics
 import sys
 import time
 
@@ -29,39 +49,36 @@ sys.path.insert(0, ROOT)
 
 METRIC = "KV-read GB/s (% of HBM peak) and µs/call for paged decode, GQA and MLA verify"
 HBM_PEAK_GBS = 8000.0
-GRAPH_CALLS = 50      # calls per captured graph for launch-bound kernels
-# The GPU clock climbs over the first ~100 ms of load after idle: the default
-# warmup runs at least this long.
-WARMUP_AUTO_S = 0.5
 BF16_MFMA_PEAK_TFLOPS = 2500.0
+COLD_SET_BYTES = 1 << 30      # per-call KV below this: rotate over independent copies
+PASS_S = 0.05                 # a timing pass lasts at least this long
+PASSES = 5
+CLOCK_WARM_S = 0.5            # the GPU clock climbs over the first ~100 ms of load
+PROBE_BYTES = 4 << 30
+DEFAULT_CONFIG = "gqa_skewed"
 
 
 def _parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=100)
-    p.add_argument("--warmup", type=int, default=None,
-                   help="untimed warmup steps; by default as many as run in %.1f s (at least "
-                        "10), so the GPU clock has left its idle state before timing" % WARMUP_AUTO_S)
-    p.add_argument("--config", default="gqa_sinks")
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--config", default=DEFAULT_CONFIG)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-graph", action="store_true",
+                   help="skip the graph-replay and probe measurements (for counter runs): the "
+                        "kernel time is then taken from eager back-to-back launches")
+    p.add_argument("--cold", choices=("auto", "on", "off"), default="auto",
+                   help="rotate over independent copies of the KV (auto: when a call reads "
+                        "less than 1 GiB)")
     p.add_argument("--splits", type=int, default=0, help="override the split cap")
     p.add_argument("--page-size", type=int, default=0,
                    help="decode / verify configs: store the same workload in pages of this many "
-                        "tokens (a power of two; a GQA pool then holds exactly the pages in use)")
+                        "tokens (a GQA pool then holds exactly the pages in use)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="after timing, run one plain device copy of this many MiB (a "
                         "known-size reference for hardware byte counters)")
     return p.parse_args()
-
-
-def _kernel_split(S, step, partials, merge):
-    """(kernel, rest) callables whose sequence is one step: with S > 1 the
-    attention kernel alone (the partials-only entry) and then the merge; with
-    S = 1 the step itself is the one kernel."""
-    if S > 1:
-        return partials, merge
-    return step, (lambda: None)
 
 
 def _gqa_case(name, torch, pd, splits, page_size=0):
@@ -70,71 +87,70 @@ def _gqa_case(name, torch, pd, splits, page_size=0):
     fp8 = name.endswith("_fp8")
     base = name[:-4] if fp8 else name
     w = gqa_workload(base, page_size=page_size, pool="tight") if page_size else gqa_workload(base)
-    pool = f"{w.num_pages}-page pool" if page_size else "40000-page pool"
+    pool = f"{w.num_pages}-page pool"
     vals = w.values("cuda", poison=False, fp8=fp8)
     bt = torch.from_numpy(w.block_table).cuda()
     sl = torch.from_numpy(w.seq_lens).cuda()
+    real = None if w.real_seq_lens is None else torch.from_numpy(w.real_seq_lens).cuda()
     S = splits or pd.gqa_split_cap(w.B, w.Hkv, int(w.seq_lens.max()), w.window)
     out = torch.empty((w.rows, w.Hq, w.D), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((w.rows, w.Hq), dtype=torch.float32, device="cuda")
     ws = pd.alloc_workspace(w.rows, w.Hq, max(S, 2), w.D, "cuda")
+    verify = w.qlen > 1 or w.real_seq_lens is not None or fp8
+    ks, vs = vals.get("k_scale"), vals.get("v_scale")
 
-    if w.qlen > 1 or w.real_seq_lens is not None or fp8:
-        real = None if w.real_seq_lens is None else torch.from_numpy(w.real_seq_lens).cuda()
+    def calls(var):
+        kv, tab = var["kv"], var["bt"]
+        if verify:
+            def step():
+                pd.paged_verify_gqa(vals["q"], kv, tab, sl, w.qlen, w.sm_scale,
+                                    sinks=vals["sinks"], window=w.window, real_seq_lens=real,
+                                    num_kv_splits=S, workspace=ws, out=out, lse=lse,
+                                    k_scale=ks, v_scale=vs)
 
-        def verify_step():
-            pd.paged_verify_gqa(vals["q"], vals["kv"], bt, sl, w.qlen, w.sm_scale,
-                                sinks=vals["sinks"], window=w.window, real_seq_lens=real,
-                                num_kv_splits=S, workspace=ws, out=out, lse=lse,
-                                k_scale=vals.get("k_scale"), v_scale=vals.get("v_scale"))
-
-        if fp8:
-            desc = ("GQA decode with sinks on an FP8 E4M3FN cache (per-kv-head K and V "
-                    f"scales): B=64, Hq=64, Hkv=8, D=128, page {w.P} HND, seq_lens U[1024,8192], "
-                    f"{pool}")
+            def kernel():
+                pd.paged_verify_gqa_partials(vals["q"], kv, tab, sl, w.qlen, w.sm_scale,
+                                             window=w.window, real_seq_lens=real,
+                                             num_kv_splits=S, workspace=ws, k_scale=ks,
+                                             v_scale=vs)
         else:
-            desc = (f"GQA causal verify with sinks: B={w.B}, qlen={w.qlen}, Hq={w.Hq}, "
-                    f"Hkv={w.Hkv}, D={w.D}, page {w.P} HND bf16, seq_lens U[1024,8192], "
-                    f"real length L - U{{0,1}}, {pool}")
-        def verify_kernel():
-            pd.paged_verify_gqa_partials(vals["q"], vals["kv"], bt, sl, w.qlen, w.sm_scale,
-                                         window=w.window, real_seq_lens=real, num_kv_splits=S,
-                                         workspace=ws, k_scale=vals.get("k_scale"),
-                                         v_scale=vals.get("v_scale"))
+            def step():
+                pd.paged_decode_gqa(vals["q"], kv, tab, sl, w.sm_scale, sinks=vals["sinks"],
+                                    window=w.window, num_kv_splits=S, workspace=ws, out=out,
+                                    lse=lse)
 
-        def verify_rest():
+            def kernel():
+                pd.paged_decode_gqa_partials(vals["q"], kv, tab, sl, w.sm_scale,
+                                             window=w.window, num_kv_splits=S, workspace=ws)
+
+        def merge():
             pd.merge_splits(ws, w.rows, w.Hq, S, w.D, sinks=vals["sinks"], out=out, lse=lse)
 
-        kernel, rest = _kernel_split(S, verify_step, verify_kernel, verify_rest)
-        return dict(w=w, vals=vals, S=S, step=verify_step, kernel=kernel, rest=rest,
-                    kv_bytes=w.kv_bytes() // (2 if fp8 else 1), flops=w.flops(), desc=desc,
-                    kind="gqa_fp8" if fp8 else "gqa_verify", kernel_name="gqa_decode_kernel")
+        return (step, kernel, merge) if S > 1 else (step, step, None)
 
-    def step():
-        pd.paged_decode_gqa(vals["q"], vals["kv"], bt, sl, w.sm_scale, sinks=vals["sinks"],
-                            window=w.window, num_kv_splits=S, workspace=ws, out=out, lse=lse)
-
-    def kernel_only():
-        pd.paged_decode_gqa_partials(vals["q"], vals["kv"], bt, sl, w.sm_scale, window=w.window,
-                                     num_kv_splits=S, workspace=ws)
-
-    def rest():
-        pd.merge_splits(ws, w.B, w.Hq, S, w.D, sinks=vals["sinks"], out=out, lse=lse)
-
-    desc = {
-        "gqa_sinks": f"GQA decode with sinks: B=64, Hq=64, Hkv=8, D=128, page {w.P} HND bf16, "
-                     f"seq_lens U[1024,8192], {pool}",
-        "gqa_window": f"sliding-window GQA decode: B=64, Hq=64, Hkv=8, D=128, page {w.P}, "
-                      "window 128, seq_lens U[4096,32768]",
-        "gqa_skewed": f"skewed long-context GQA decode: B=256, Hq=32, Hkv=8, D=128, page {w.P}, "
-                      "seq_lens log-uniform [16,131072] with 4 empty",
-        "tiny_gqa": "tiny GQA decode: B=3, seq_lens [30,32,70], page 32",
-    }[name]
-
-    kernel, rest = _kernel_split(S, step, kernel_only, rest)
-    return dict(w=w, vals=vals, S=S, step=step, kernel=kernel, rest=rest,
-                kv_bytes=w.kv_bytes(), flops=w.flops(), desc=desc, kind="gqa",
-                kernel_name="gqa_decode_kernel")
+    if fp8:
+        desc = ("GQA decode with sinks on an FP8 E4M3FN cache (per-kv-head K and V scales): "
+                f"B=64, Hq=64, Hkv=8, D=128, page {w.P} HND, seq_lens U[1024,8192], {pool}")
+        kind = "gqa_fp8"
+    elif verify:
+        desc = (f"GQA causal verify with sinks: B={w.B}, qlen={w.qlen}, Hq={w.Hq}, Hkv={w.Hkv}, "
+                f"D={w.D}, page {w.P} HND bf16, seq_lens U[1024,8192], real length L - U{{0,1}}, "
+                f"{pool}")
+        kind = "gqa_verify"
+    else:
+        desc = {
+            "gqa_sinks": f"GQA decode with sinks: B=64, Hq=64, Hkv=8, D=128, page {w.P} HND "
+                         f"bf16, seq_lens U[1024,8192], {pool}",
+            "gqa_window": f"sliding-window GQA decode: B=64, Hq=64, Hkv=8, D=128, page {w.P} "
+                          f"HND bf16, window 128, seq_lens U[4096,32768], {pool}",
+            "gqa_skewed": f"skewed long-context GQA decode: B=256, Hq=32, Hkv=8, D=128, page "
+                          f"{w.P} HND bf16, seq_lens log-uniform [16,131072] with 4 empty, {pool}",
+            "tiny_gqa": "tiny GQA decode: B=3, Hq=8, Hkv=1, D=128, seq_lens [30,32,70], page 32",
+        }[name]
+        kind = "gqa"
+    return dict(w=w, vals=vals, S=S, calls=calls, variants=[dict(kv=vals["kv"], bt=bt)],
+                kv_bytes=w.kv_bytes() // (2 if fp8 else 1), flops=w.flops(), desc=desc,
+                kind=kind, kernel_name="gqa_decode_kernel", rotatable=name != "tiny_gqa")
 
 
 def _varlen_case(torch, pd, splits, page_size=0):
@@ -160,28 +176,32 @@ def _varlen_case(torch, pd, splits, page_size=0):
     lse = torch.empty((total, w.Hq), dtype=torch.float32, device="cuda")
     ws = pd.alloc_workspace(total, w.Hq, max(S, 2), w.D, "cuda")
 
-    def step():
-        pd.paged_verify_gqa_varlen(q, vals["kv"], bt, sl, cu_d, w.qlen, w.sm_scale,
-                                   sinks=vals["sinks"], window=w.window, real_seq_lens=real,
-                                   num_kv_splits=S, workspace=ws, out=out, lse=lse)
+    def calls(var):
+        kv, tab = var["kv"], var["bt"]
 
-    def kernel_only():
-        pd.paged_verify_gqa_partials(q, vals["kv"], bt, sl, w.qlen, w.sm_scale, window=w.window,
-                                     real_seq_lens=real, cu_seqlens_q=cu_d, num_kv_splits=S,
-                                     workspace=ws)
+        def step():
+            pd.paged_verify_gqa_varlen(q, kv, tab, sl, cu_d, w.qlen, w.sm_scale,
+                                       sinks=vals["sinks"], window=w.window, real_seq_lens=real,
+                                       num_kv_splits=S, workspace=ws, out=out, lse=lse)
 
-    def rest():
-        pd.merge_splits(ws, total, w.Hq, S, w.D, sinks=vals["sinks"], out=out, lse=lse)
+        def kernel():
+            pd.paged_verify_gqa_partials(q, kv, tab, sl, w.qlen, w.sm_scale, window=w.window,
+                                         real_seq_lens=real, cu_seqlens_q=cu_d,
+                                         num_kv_splits=S, workspace=ws)
 
-    kernel, rest = _kernel_split(S, step, kernel_only, rest)
+        def merge():
+            pd.merge_splits(ws, total, w.Hq, S, w.D, sinks=vals["sinks"], out=out, lse=lse)
+
+        return (step, kernel, merge) if S > 1 else (step, step, None)
+
     # keys of request b: rows t < n_b see [0, min(L, L_real)) at most (no window)
     keys = sum(max(min(int(L), int(Lr)), 0) for L, Lr in zip(w.seq_lens, w.real_seq_lens))
     desc = (f"GQA causal verify, variable query length U{{1,2}} per request (cumulative query "
             f"lengths, {total} rows): B={w.B}, Hq={w.Hq}, Hkv={w.Hkv}, D={w.D}, page {w.P} HND "
             f"bf16, seq_lens U[1024,8192], real length L - U{{0,1}}")
-    return dict(w=w, vals=vals, S=S, step=step, kernel=kernel, rest=rest,
+    return dict(w=w, vals=vals, S=S, calls=calls, variants=[dict(kv=vals["kv"], bt=bt)],
                 kv_bytes=keys * w.Hkv * 2 * w.D * 2, flops=w.flops(), desc=desc,
-                kind="gqa_varlen", kernel_name="gqa_decode_kernel",
+                kind="gqa_varlen", kernel_name="gqa_decode_kernel", rotatable=True,
                 extra=dict(q=q, cu=cu, qlens=qlens))
 
 
@@ -196,18 +216,17 @@ def _append_case(torch, pd):
     k = torch.randn((w.B, w.Hkv, w.D), generator=g, device="cuda").to(torch.bfloat16)
     v = torch.randn((w.B, w.Hkv, w.D), generator=g, device="cuda").to(torch.bfloat16)
 
-    def step():
-        pd.paged_kv_append(vals["kv"], bt, sl, k, v)
+    def calls(var):
+        def step():
+            pd.paged_kv_append(var["kv"], var["bt"], sl, k, v)
+        return step, step, None
 
     desc = ("KV append of the current token: B=64, Hkv=8, D=128, K and V into the 16-token "
             "HND pages of the 40000-page decode pool through the block table")
     moved = 2 * w.B * w.Hkv * 2 * w.D * 2          # read + write, K and V
-    # The step loop is bound by the host-side binding, so the kernel's own
-    # time comes from a HIP graph of GRAPH_CALLS appends replayed back to back.
-    return dict(w=w, vals=vals, S=1, step=step, kernel=None, rest=None, kv_bytes=moved,
-                graph_calls=GRAPH_CALLS,
-                flops=0, desc=desc, kind="append", kernel_name="kv_append_kernel",
-                extra=dict(k=k, v=v))
+    return dict(w=w, vals=vals, S=1, calls=calls, variants=[dict(kv=vals["kv"], bt=bt)],
+                kv_bytes=moved, flops=0, desc=desc, kind="append",
+                kernel_name="kv_append_kernel", rotatable=False, extra=dict(k=k, v=v))
 
 
 def _mla_case(fp8, torch, pd, splits, page_size=0):
@@ -223,26 +242,66 @@ def _mla_case(fp8, torch, pd, splits, page_size=0):
     out = torch.empty((w.rows, w.H, w.Lv), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((w.rows, w.H), dtype=torch.float32, device="cuda")
     ws = pd.alloc_workspace(w.rows, w.H, max(S, 2), w.Lv, "cuda")
+    ksc = k_scale if fp8 else None
 
-    def step():
-        pd.paged_verify_mla(vals["q"], vals["kv"], bt, sl, real, w.qlen, w.sm_scale,
-                            head_dim_v=w.Lv, k_scale=k_scale if fp8 else None,
-                            num_kv_splits=S, workspace=ws, out=out, lse=lse)
+    def calls(var):
+        kv, tab = var["kv"], var["bt"]
 
-    def kernel_only():
-        pd.paged_verify_mla_partials(vals["q"], vals["kv"], bt, sl, real, w.qlen, w.sm_scale,
-                                     head_dim_v=w.Lv, k_scale=k_scale if fp8 else None,
-                                     num_kv_splits=S, workspace=ws)
+        def step():
+            pd.paged_verify_mla(vals["q"], kv, tab, sl, real, w.qlen, w.sm_scale,
+                                head_dim_v=w.Lv, k_scale=ksc, num_kv_splits=S, workspace=ws,
+                                out=out, lse=lse)
 
-    def rest():
-        pd.merge_splits(ws, w.rows, w.H, S, w.Lv, out=out, lse=lse)
+        def kernel():
+            pd.paged_verify_mla_partials(vals["q"], kv, tab, sl, real, w.qlen, w.sm_scale,
+                                         head_dim_v=w.Lv, k_scale=ksc, num_kv_splits=S,
+                                         workspace=ws)
 
-    kernel, rest = _kernel_split(S, step, kernel_only, rest)
+        def merge():
+            pd.merge_splits(ws, w.rows, w.H, S, w.Lv, out=out, lse=lse)
+
+        return (step, kernel, merge) if S > 1 else (step, step, None)
+
     desc = (f"MLA causal verify: B=32, qlen=4, H=128, Lk=576, Lv=512, page {w.P}, "
-            f"seq_lens U[2048,16384], {'fp8 e4m3fn' if fp8 else 'bf16'} latent cache")
-    return dict(w=w, vals=vals, S=S, step=step, kernel=kernel, rest=rest,
+            f"seq_lens U[2048,16384], real length L - U{{0,1,2}}, "
+            f"{'fp8 e4m3fn' if fp8 else 'bf16'} latent cache")
+    return dict(w=w, vals=vals, S=S, calls=calls, variants=[dict(kv=vals["kv"], bt=bt)],
                 kv_bytes=w.kv_bytes(1 if fp8 else 2), flops=w.flops(), desc=desc,
-                kind="mla_fp8" if fp8 else "mla", kernel_name="mla_verify_kernel")
+                kind="mla_fp8" if fp8 else "mla", kernel_name="mla_verify_kernel",
+                rotatable=True)
+
+
+def _rotate(case, torch, mode):
+    """Independent copies of the KV so successive calls read cold data.
+
+    A pool much larger than one call's working set gets R block tables, each
+    the original table with every page renumbered through its own seeded
+    permutation of the pool; a pool that holds only the pages in use gets R
+    copies (same table).  R copies together hold at least COLD_SET_BYTES of
+    KV per call's worth.  Results differ between copies only in values,
+    never in the work done."""
+    kv_call = case["kv_bytes"]
+    if mode == "off" or not case["rotatable"] or (mode == "auto" and kv_call >= COLD_SET_BYTES):
+        return 1, None
+    base = case["variants"][0]
+    kv, bt = base["kv"], base["bt"]
+    pool_bytes = kv.numel() * kv.element_size()
+    R = max(2, math.ceil(COLD_SET_BYTES / max(kv_call, 1)))
+    if pool_bytes >= 4 * kv_call:
+        how = "tables"
+        R = min(R, 64)
+        g = torch.Generator(device="cuda").manual_seed(4242)
+        n = kv.shape[0]
+        for _ in range(R - 1):
+            perm = torch.randperm(n, generator=g, device="cuda").to(torch.int32)
+            tab = torch.where(bt >= 0, perm[bt.clamp(min=0).long()], bt).contiguous()
+            case["variants"].append(dict(kv=kv, bt=tab))
+    else:
+        how = "pools"
+        R = max(2, min(R, (8 << 30) // max(pool_bytes, 1)))
+        for _ in range(R - 1):
+            case["variants"].append(dict(kv=kv.clone(), bt=bt))
+    return R, how
 
 
 def _profiled_traffic(kernel, config):
@@ -379,6 +438,85 @@ def _cpu_baseline(case, budget_s=20.0, min_s=10.0):
                       f"({done_bytes / 1e6:.1f} MB of KV) in {t_total:.1f} s, fp64 NumPy"}
 
 
+def _events(torch):
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def _graph_time(torch, fns, warm_s):
+    """Microseconds per call of the callables ``fns`` (cycled, one call each)
+    from HIP-graph replays on the current stream: a graph of N calls (a
+    replay lasting at least PASS_S), replayed for ``warm_s`` untimed, then
+    PASSES timed replays.  Returns (median, per-pass values, N)."""
+    stream = torch.cuda.current_stream()
+    for f in fns:
+        f()
+    torch.cuda.synchronize()
+    a, b = _events(torch)
+    a.record(stream)
+    for f in fns:
+        f()
+    b.record(stream)
+    torch.cuda.synchronize()
+    est_s = max(a.elapsed_time(b) * 1e-3 / len(fns), 1e-6)
+    n = min(max(math.ceil(PASS_S / est_s), len(fns)), 4000)
+    n = math.ceil(n / len(fns)) * len(fns)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(n):
+            fns[i % len(fns)]()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while True:
+        graph.replay()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= warm_s:
+            break
+    per = []
+    for _ in range(PASSES):
+        a, b = _events(torch)
+        a.record(stream)
+        graph.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        per.append(a.elapsed_time(b) * 1e3 / n)
+    del graph
+    return statistics.median(per), per, n
+
+
+def _eager_time(torch, fns, n):
+    """Microseconds per call of n eager back-to-back calls (fns cycled)."""
+    stream = torch.cuda.current_stream()
+    for f in fns:
+        f()
+    torch.cuda.synchronize()
+    a, b = _events(torch)
+    a.record(stream)
+    for i in range(n):
+        fns[i % len(fns)]()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / n
+
+
+def _stream_ceiling(torch, pd):
+    """The machine's streaming-read rate: the library's read probe over a
+    4 GiB buffer (16 times the Infinity Cache) at a few grid sizes, best of."""
+    buf = torch.empty(PROBE_BYTES, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(8192, dtype=torch.int32, device="cuda")
+    best = None
+    for wgs in (256, 512, 1024, 2048):
+        us, per, n = _graph_time(torch, [lambda wgs=wgs: pd.stream_read_probe(buf, sink, wgs)],
+                                 0.1)
+        gbs = PROBE_BYTES / (us * 1e-6) / 1e9
+        if best is None or gbs > best["value"]:
+            best = {"value": round(gbs, 1), "unit": "GB/s",
+                    "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "bytes": PROBE_BYTES,
+                    "workgroups": wgs, "kernel": "stream_read_kernel"}
+    del buf, sink
+    torch.cuda.empty_cache()
+    return best
+
+
 def main():
     args = _parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -397,94 +535,80 @@ def main():
         print("bench.py: --page-size applies to the decode and verify configs only",
               file=sys.stderr)
         sys.exit(2)
+    print(f"# building workload {name}", file=sys.stderr, flush=True)
     if name in ("mla_verify", "mla_verify_fp8"):
         case = _mla_case(name.endswith("fp8"), torch, pd, args.splits, args.page_size)
-        if args.page_size:
-            name = f"{name}_p{args.page_size}"
     elif name == "kv_append":
         case = _append_case(torch, pd)
     elif name == "gqa_verify_varlen":
         case = _varlen_case(torch, pd, args.splits, args.page_size)
-        if args.page_size:
-            name = f"{name}_p{args.page_size}"
     else:
         case = _gqa_case(name, torch, pd, args.splits, args.page_size)
-        if args.page_size:
-            name = f"{name}_p{args.page_size}"
+    if args.page_size:
+        name = f"{name}_p{args.page_size}"
+    R, how = _rotate(case, torch, args.cold)
+    torch.cuda.synchronize()
+    per_var = [case["calls"](v) for v in case["variants"]]
+    steps = [c[0] for c in per_var]
+    kernels = [c[1] for c in per_var]
+    merges = [c[2] for c in per_var if c[2] is not None]
+    kv = case["kv_bytes"]
+
+    ceiling = None
+    graph = {}
+    if not args.no_graph:
+        print("# streaming-read probe", file=sys.stderr, flush=True)
+        ceiling = _stream_ceiling(torch, pd)
+        print("# graph timing", file=sys.stderr, flush=True)
+        graph["kernel"] = _graph_time(torch, kernels, CLOCK_WARM_S)
+        graph["call"] = _graph_time(torch, steps, 0.1)
+        if merges:
+            graph["merge"] = _graph_time(torch, merges, 0.1)
+        if R > 1:
+            graph["kernel_hot"] = _graph_time(torch, kernels[:1], 0.1)
+            graph["call_hot"] = _graph_time(torch, steps[:1], 0.1)
+
+    # the contract: W untimed warm-up steps, then K timed steps
+    for i in range(args.warmup):
+        steps[i % R]()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    eager_step = case["step"]
-
-    if args.warmup is not None:
-        for _ in range(args.warmup):
-            case["step"]()
-    else:
-        args.warmup = 0
-        t_w = time.perf_counter()
-        while args.warmup < 10 or time.perf_counter() - t_w < WARMUP_AUTO_S:
-            for _ in range(10):
-                case["step"]()
-            args.warmup += 10
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0, ev1 = _events(torch)
     ev0.record(stream)
-    for _ in range(args.steps):
-        case["step"]()
+    for i in range(args.steps):
+        steps[i % R]()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
-    print(f"# timed {args.steps} steps in {wall:.3f} s wall", file=sys.stderr)
+    print(f"# timed {args.steps} steps in {wall:.3f} s wall", file=sys.stderr, flush=True)
 
-    # dominant kernel alone: HIP events recorded on the launch stream right
-    # around each launch of the split decode kernel
-    kernel_ms = []
-    if case.get("graph_calls"):
-        n_calls = case["graph_calls"]
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for _ in range(n_calls):
-                eager_step()
-        torch.cuda.synchronize()
-        for _ in range(3):
-            graph.replay()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = max(1, args.steps // n_calls)
-        gstream = torch.cuda.current_stream()
-        ev0.record(gstream)
-        for _ in range(reps):
-            graph.replay()
-        ev1.record(gstream)
-        torch.cuda.synchronize()
-        kernel_ms = [ev0.elapsed_time(ev1) / (reps * n_calls)]
-    elif case["kernel"] is not None:
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
-        for a, b in evs:
-            a.record(stream)
-            case["kernel"]()
-            b.record(stream)
-            case["rest"]()
-        torch.cuda.synchronize()
-        kernel_ms = [a.elapsed_time(b) for a, b in evs]
+    if graph:
+        k_us, k_passes = graph["kernel"][0], graph["kernel"][1]
     else:
-        kernel_ms = [ms_per_step]
-    k_ms = float(np.mean(kernel_ms))
-
-    kv = case["kv_bytes"]
-    value = kv / (ms_per_step * 1e-3) / 1e9
-    if case["kind"] in ("gqa", "gqa_verify", "gqa_fp8", "gqa_varlen", "append"):
-        roof = {"bound": "hbm", "achieved": round(kv / (k_ms * 1e-3) / 1e9, 2),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s"}
-    else:
-        roof = {"bound": "mfma", "achieved": round(case["flops"] / (k_ms * 1e-3) / 1e12, 2),
+        k_us = _eager_time(torch, kernels, max(args.steps, len(kernels)))
+        k_passes = [k_us]
+    us_per_call = ms_per_step * 1e3
+    value = kv / (us_per_call * 1e-6) / 1e9
+    if case["kind"] in ("mla", "mla_fp8"):
+        roof = {"bound": "mfma", "achieved": round(case["flops"] / (k_us * 1e-6) / 1e12, 2),
                 "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(kv / (k_us * 1e-6) / 1e9, 2),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = _profiled_traffic(case["kernel_name"], name)
     roof["kernel"] = case["kernel_name"]
-    roof["kernel_us"] = round(k_ms * 1e3, 2)
+    roof["kernel_us"] = round(k_us, 2)
+    roof["kernel_us_passes"] = [round(x, 2) for x in k_passes]
+    roof["timing"] = ("HIP-graph replay of back-to-back launches, median of 5 passes"
+                      if graph else "HIP events around eager back-to-back launches")
+    roof["kernel_le_call"] = bool(k_us <= us_per_call)
+    if ceiling is not None and roof["bound"] == "hbm":
+        roof["frac_of_ceiling"] = round(roof["achieved"] / ceiling["value"], 4)
+    if "kernel_hot" in graph:
+        roof["kernel_us_hot"] = round(graph["kernel_hot"][0], 2)
 
     if args.calib_copy_mib > 0:
         n = args.calib_copy_mib << 20
@@ -498,8 +622,26 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
+        print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
         cpu = _cpu_baseline(case)
 
+    cfg = {
+        "workload": case["desc"],
+        "name": name,
+        "num_kv_splits": case["S"],
+        "kv_bytes_per_call": kv,
+        "us_per_call": round(us_per_call, 2),
+        "hbm_frac_per_call": round(value / HBM_PEAK_GBS, 4),
+        "cold_rotation": R,
+    }
+    if how:
+        cfg["rotation"] = how
+    if graph:
+        cfg["us_per_call_graph"] = round(graph["call"][0], 2)
+        if "merge" in graph:
+            cfg["merge_us"] = round(graph["merge"][0], 2)
+        if "call_hot" in graph:
+            cfg["us_per_call_hot"] = round(graph["call_hot"][0], 2)
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -513,15 +655,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {
-            "workload": case["desc"],
-            "name": name,
-            "num_kv_splits": case["S"],
-            "kv_bytes_per_call": kv,
-            "us_per_call": round(ms_per_step * 1e3, 2),
-            "hbm_frac_per_call": round(value / HBM_PEAK_GBS, 4),
-        },
+        "config": cfg,
         "roofline": roof,
+        "stream_ceiling": ceiling,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))

@@ -479,6 +479,20 @@ PD_API int merge_splits(const float* workspace, int32_t rows, int32_t num_heads,
                  void* out, int64_t o_stride_row, int64_t o_stride_h,
                  float* lse, int64_t lse_stride_row, void* stream);
 
+/*
+ * pd_stream_read_probe - measurement helper, not part of the attention path.
+ *
+ * Reads `bytes` (rounded down to 16) from `src` once with 16-byte
+ * non-temporal loads spread over `workgroups` workgroups of 256 threads and
+ * keeps nothing: its rate is the streaming-read ceiling of the machine, the
+ * figure the HBM-bound kernels above are compared with.  `sink` holds
+ * `workgroups` uint32 values the kernel may write (almost never does).
+ * src 16-byte aligned.  Returns PD_ERR_INVALID / PD_ERR_ALIGN on bad
+ * arguments, PD_ERR_HIP if the launch fails.
+ */
+PD_API int pd_stream_read_probe(const void* src, size_t bytes, uint32_t* sink,
+                                int32_t workgroups, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

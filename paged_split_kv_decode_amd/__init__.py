@@ -23,6 +23,7 @@ from .api import (  # noqa: F401
     paged_verify_mla,
     paged_verify_mla_partials,
     split_rule,
+    stream_read_probe,
     workspace_bytes,
 )
 from ._native import LIB_PATH, PagedDecodeError  # noqa: F401

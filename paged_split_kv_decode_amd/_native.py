@@ -37,6 +37,7 @@ EXPORTS = (
     "paged_verify_mla",
     "paged_verify_mla_partials",
     "merge_splits",
+    "pd_stream_read_probe",
 )
 
 _c_i32, _c_i64, _c_f32, _c_sz, _c_vp = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
@@ -165,6 +166,8 @@ def _load():
     lib.merge_splits.argtypes = [_c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_vp,
                                  _c_vp, _c_i64, _c_i64, _c_vp, _c_i64, _c_vp]
     lib.merge_splits.restype = ctypes.c_int
+    lib.pd_stream_read_probe.argtypes = [_c_vp, _c_sz, _c_vp, _c_i32, _c_vp]
+    lib.pd_stream_read_probe.restype = ctypes.c_int
     return lib
 
 

@@ -524,10 +524,24 @@ def merge_splits(workspace, rows, num_heads, num_splits, head_dim_v, sinks=None,
     return out, lse
 
 
+def stream_read_probe(buf, sink, workgroups, stream=None):
+    """Streaming-read ceiling probe (include/paged_decode.h:
+    pd_stream_read_probe): reads ``buf`` once; ``sink`` is an int32 device
+    tensor of at least ``workgroups`` elements."""
+    if not isinstance(buf, torch.Tensor) or not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    _need(sink, "sink", torch.int32, 1)
+    if sink.numel() < int(workgroups):
+        raise ValueError("sink must hold one value per workgroup")
+    st = lib.pd_stream_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                  int(workgroups), _stream(stream))
+    check("pd_stream_read_probe", st)
+
+
 __all__ = [
     "PD_KV_BF16", "PD_KV_FP8_E4M3FN", "alloc_workspace", "gqa_split_cap", "merge_splits",
     "mla_split_cap", "num_kv_splits_cap", "paged_decode_gqa", "paged_decode_gqa_partials",
     "paged_kv_append", "paged_verify_gqa", "paged_verify_gqa_partials",
     "paged_verify_gqa_varlen", "paged_verify_mla", "paged_verify_mla_partials",
-    "split_rule", "workspace_bytes", "_native",
+    "split_rule", "stream_read_probe", "workspace_bytes", "_native",
 ]

@@ -205,7 +205,8 @@ static int gqa_common(const void* q, int64_t q_stride_b, int64_t q_stride_h, con
   if (cu_seqlens_q != nullptr && total_rows < 0) return PD_ERR_INVALID;
   const int64_t rows = cu_seqlens_q != nullptr ? (int64_t)total_rows : (int64_t)batch * qlen;
   if (rows > 0x7fffffff) return PD_ERR_UNSUPPORTED;
-  if (num_kv_splits > 1 || partials_only) {
+  const bool needs_ws = num_kv_splits > 1 || partials_only;
+  if (needs_ws) {
     const int32_t ws_splits = num_kv_splits > 1 ? num_kv_splits : 2;
     size_t need = pd_workspace_bytes((int32_t)rows, num_q_heads, ws_splits, head_dim);
     if (num_kv_splits == 1) need /= 2;

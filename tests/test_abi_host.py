@@ -364,3 +364,4 @@ def test_mla_partials_argument_checks_happen_before_any_hip_call():
     assert _mlap(wsb=8 * 128 * 513 * 4 - 4) == PD_ERR_WORKSPACE
     assert _mlap(ws=FAKE + 4) == PD_ERR_ALIGN
     assert _mlap(S=2, wsb=lib.pd_workspace_bytes(8, 128, 2, 512) - 4) == PD_ERR_WORKSPACE
+
