@@ -264,6 +264,38 @@ PD_API int paged_verify_gqa(const void* q, int64_t q_stride_row, int64_t q_strid
                      float* lse, int64_t lse_stride_row, void* stream);
 
 /*
+ * paged_verify_gqa_noalloc - paged_verify_gqa for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  No workspace argument.
+ *
+ * Same operation, arguments (minus workspace / workspace_bytes), kernels and
+ * results as paged_verify_gqa (bit for bit).  With num_kv_splits > 1 the
+ * split partials go to a scratch array the library holds in device memory,
+ * one per GPU it runs on, 64 MiB each (67108864 bytes), kept until the
+ * process ends.  A call whose partials would not fit,
+ * B*qlen * Hq * S * (D + 1) * 4 > 67108864, returns PD_ERR_WORKSPACE and
+ * enqueues nothing (use a smaller num_kv_splits or paged_verify_gqa).  The
+ * call allocates nothing; it never needs the scratch cleared (every slot the
+ * merge reads is written by the same call).  Every call on one GPU shares
+ * that GPU's array: calls in flight at the same time on different streams of
+ * one GPU race and give wrong results; calls on one stream are safe.  The
+ * first call on a device looks up the array's device address (a HIP call,
+ * made after every argument check); it fails with PD_ERR_HIP if that lookup
+ * does.
+ */
+PD_API int paged_verify_gqa_noalloc(const void* q, int64_t q_stride_row, int64_t q_stride_h,
+                     const void* kv, int32_t kv_dtype, const float* k_scale,
+                     const float* v_scale, int32_t scale_per_head,
+                     int64_t kv_stride_page, int64_t kv_stride_head,
+                     int32_t num_pages, const int32_t* block_table, int64_t bt_stride_b,
+                     int32_t max_blocks, const int32_t* seq_lens,
+                     const int32_t* real_seq_lens, int32_t qlen, const float* sinks,
+                     int32_t window, float sm_scale, int32_t batch, int32_t num_q_heads,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                     int32_t num_kv_splits, void* out, int64_t o_stride_row,
+                     int64_t o_stride_h, float* lse, int64_t lse_stride_row, void* stream);
+
+/*
  * paged_verify_gqa_varlen - paged GQA causal verify with a query length per
  * request.
  *

@@ -4,6 +4,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/paged_decode.h"
 #include "kernels.h"
@@ -49,6 +50,28 @@ int32_t device_cus(int32_t device) {
     cached[dev] = n;
   }
   return cached[dev];
+}
+
+// Split partials of the allocation-free entry point (paged_verify_gqa_noalloc):
+// one array per GPU the library runs on, held until the process ends.
+constexpr size_t kScratchBytes = size_t{64} << 20;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+// Device address of this GPU's scratch array, looked up once per device with
+// the device current (host code never uses the array's own name: on the host
+// it is a stand-in, not a device address).  nullptr if the lookup fails.
+float* scratch_ptr() {
+  static std::mutex mu;
+  static void* ptrs[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptrs[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    ptrs[dev] = p;
+  }
+  return static_cast<float*>(ptrs[dev]);
 }
 
 }  // namespace
@@ -177,7 +200,8 @@ static int gqa_common(const void* q, int64_t q_stride_b, int64_t q_stride_h, con
                int32_t page_size, int32_t num_kv_splits, float* workspace,
                size_t workspace_bytes, void* out, int64_t o_stride_b, int64_t o_stride_h,
                float* lse, int64_t lse_stride_b, void* stream, bool partials_only,
-               const int32_t* cu_seqlens_q = nullptr, int32_t total_rows = -1) {
+               const int32_t* cu_seqlens_q = nullptr, int32_t total_rows = -1,
+               bool use_scratch = false) {
   if (batch < 0 || qlen < 1 || num_q_heads < 1 || num_kv_heads < 1 || num_kv_splits < 1 ||
       num_pages < 0 || max_blocks < 0 || !std::isfinite(sm_scale) || !(sm_scale > 0.f))
     return PD_ERR_INVALID;
@@ -210,8 +234,12 @@ static int gqa_common(const void* q, int64_t q_stride_b, int64_t q_stride_h, con
     const int32_t ws_splits = num_kv_splits > 1 ? num_kv_splits : 2;
     size_t need = pd_workspace_bytes((int32_t)rows, num_q_heads, ws_splits, head_dim);
     if (num_kv_splits == 1) need /= 2;
-    if (workspace == nullptr || workspace_bytes < need) return PD_ERR_WORKSPACE;
-    if (!aligned16(workspace)) return PD_ERR_ALIGN;
+    if (use_scratch) {
+      if (need > kScratchBytes) return PD_ERR_WORKSPACE;
+    } else {
+      if (workspace == nullptr || workspace_bytes < need) return PD_ERR_WORKSPACE;
+      if (!aligned16(workspace)) return PD_ERR_ALIGN;
+    }
   }
   if (num_kv_heads > 65535 || batch > 65535 || num_kv_splits > 65535) return PD_ERR_UNSUPPORTED;
   const int64_t kLim = INT32_MAX;
@@ -225,6 +253,12 @@ static int gqa_common(const void* q, int64_t q_stride_b, int64_t q_stride_h, con
   if ((int64_t)max_blocks * page_size > (int64_t)INT32_MAX / 2 ||
       (int64_t)batch * num_kv_heads * cdiv64((int64_t)max_blocks * page_size, 32) > INT32_MAX / 2)
     return PD_ERR_UNSUPPORTED;
+
+  if (use_scratch && needs_ws) {
+    // every argument check has passed: the first HIP call of the entry point
+    workspace = scratch_ptr();
+    if (workspace == nullptr) return PD_ERR_HIP;
+  }
 
   pd::GqaArgs a{};
   a.q = static_cast<const uint16_t*>(q);
@@ -318,6 +352,25 @@ int paged_verify_gqa(const void* q, int64_t q_stride_row, int64_t q_stride_h, co
                     window, sm_scale, batch, num_q_heads, num_kv_heads, head_dim, page_size,
                     num_kv_splits, workspace, workspace_bytes, out, o_stride_row, o_stride_h,
                     lse, lse_stride_row, stream, false);
+}
+
+int paged_verify_gqa_noalloc(const void* q, int64_t q_stride_row, int64_t q_stride_h,
+                             const void* kv, int32_t kv_dtype, const float* k_scale,
+                             const float* v_scale, int32_t scale_per_head,
+                             int64_t kv_stride_page, int64_t kv_stride_head, int32_t num_pages,
+                             const int32_t* block_table, int64_t bt_stride_b, int32_t max_blocks,
+                             const int32_t* seq_lens, const int32_t* real_seq_lens, int32_t qlen,
+                             const float* sinks, int32_t window, float sm_scale, int32_t batch,
+                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t page_size, int32_t num_kv_splits, void* out,
+                             int64_t o_stride_row, int64_t o_stride_h, float* lse,
+                             int64_t lse_stride_row, void* stream) {
+  return gqa_common(q, q_stride_row, q_stride_h, kv, kv_dtype, k_scale, v_scale,
+                    scale_per_head, kv_stride_page, kv_stride_head, num_pages,
+                    block_table, bt_stride_b, max_blocks, seq_lens, real_seq_lens, qlen, sinks,
+                    window, sm_scale, batch, num_q_heads, num_kv_heads, head_dim, page_size,
+                    num_kv_splits, nullptr, 0, out, o_stride_row, o_stride_h,
+                    lse, lse_stride_row, stream, false, nullptr, -1, true);
 }
 
 int paged_verify_gqa_varlen(const void* q, int64_t q_stride_row, int64_t q_stride_h,

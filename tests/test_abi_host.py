@@ -365,3 +365,25 @@ def test_mla_partials_argument_checks_happen_before_any_hip_call():
     assert _mlap(ws=FAKE + 4) == PD_ERR_ALIGN
     assert _mlap(S=2, wsb=lib.pd_workspace_bytes(8, 128, 2, 512) - 4) == PD_ERR_WORKSPACE
 
+
+def _noalloc(**kw):
+    a = dict(q=FAKE, qsr=64 * 128, qsh=128, kv=FAKE, dt=0, ks=NULL, vs=NULL, ph=0,
+             kvsp=8 * 16 * 256, kvsh=16 * 256, npages=10, bt=FAKE, btsb=4, maxb=4, sl=FAKE,
+             real=NULL, qlen=2, sinks=NULL, window=0, scale=0.088, B=2, Hq=64, Hkv=8, D=128,
+             P=16, S=1, out=FAKE, osr=64 * 128, osh=128, lse=NULL, lsesr=64, stream=NULL)
+    a.update(kw)
+    return lib.paged_verify_gqa_noalloc(*a.values())
+
+
+def test_noalloc_checks_happen_before_the_scratch_lookup():
+    # every refusal below comes from the host checks, before any HIP call
+    assert _noalloc(B=0, q=NULL, kv=NULL, bt=NULL, sl=NULL, out=NULL) == PD_OK
+    assert _noalloc(q=NULL) == PD_ERR_INVALID
+    assert _noalloc(Hq=60) == PD_ERR_INVALID
+    assert _noalloc(scale=-1.0) == PD_ERR_INVALID
+    assert _noalloc(P=0) == PD_ERR_INVALID
+    assert _noalloc(D=64) == PD_ERR_UNSUPPORTED
+    assert _noalloc(q=FAKE + 8) == PD_ERR_ALIGN
+    # partials of 128 rows x 64 heads x 16 splits x 129 fp32 exceed the 64 MiB scratch
+    assert _noalloc(B=64, S=16) == PD_ERR_WORKSPACE
+    assert _noalloc(B=64 * 16, S=2, maxb=1) == PD_ERR_WORKSPACE
