@@ -46,8 +46,10 @@ def sources() -> list[str]:
 PER_SOURCE_FLAGS = {
     "mla_verify.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=0"],
     "mla_verify_small_pages.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=0"],
+    "mla_verify_general_pages.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=0"],
     "gqa_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "gqa_decode_small_pages.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "gqa_decode_general_pages.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 
 

@@ -17,9 +17,11 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Page sizes with a kernel: every power of two up to 65536 tokens.
+// Page sizes with a kernel: every size from 1 to 65536 tokens.
 constexpr int32_t kMaxPageSize = 1 << 16;
-bool pow2_page(int32_t p) { return p >= 1 && p <= kMaxPageSize && (p & (p - 1)) == 0; }
+bool page_ok(int32_t p) { return p >= 1 && p <= kMaxPageSize; }
+// log2 of a power-of-two page size, else 0 (the general page classes divide)
+int32_t page_shift(int32_t p) { return (p & (p - 1)) == 0 ? __builtin_ctz((unsigned)p) : 0; }
 
 constexpr int32_t kGqaHeadDim = 128;
 constexpr int32_t kMlaHeadDimK = 576;
@@ -212,7 +214,7 @@ static int gqa_common(const void* q, int64_t q_stride_b, int64_t q_stride_h, con
   const bool fp8 = kv_dtype == PD_KV_FP8_E4M3FN;
   const int32_t G = num_q_heads / num_kv_heads;
   if (page_size < 1) return PD_ERR_INVALID;
-  if (head_dim != 128 || !pow2_page(page_size) || (int64_t)qlen * G > 16)
+  if (head_dim != 128 || !page_ok(page_size) || (int64_t)qlen * G > 16)
     return PD_ERR_UNSUPPORTED;
   if (batch == 0) return PD_OK;
   if (q == nullptr || kv == nullptr || block_table == nullptr || seq_lens == nullptr ||
@@ -288,7 +290,7 @@ static int gqa_common(const void* q, int64_t q_stride_b, int64_t q_stride_h, con
   a.Hkv = num_kv_heads;
   a.G = G;
   a.P = page_size;
-  a.p_shift = __builtin_ctz((unsigned)page_size);
+  a.p_shift = page_shift(page_size);
   a.S = num_kv_splits;
   a.partials = partials_only ? 1 : 0;
   a.ws = workspace;
@@ -507,9 +509,7 @@ int mla_common(const void* q, int64_t q_stride_row, int64_t q_stride_h, const vo
     return PD_ERR_INVALID;
   if (kv_dtype != PD_KV_BF16 && kv_dtype != PD_KV_FP8_E4M3FN) return PD_ERR_INVALID;
   if (page_size < 1) return PD_ERR_INVALID;
-  if (head_dim_k != 576 || head_dim_v != 512 || !pow2_page(page_size) ||
-      ((int64_t)qlen * num_heads) % 32 != 0)
-    return PD_ERR_UNSUPPORTED;
+  if (head_dim_k != 576 || head_dim_v != 512 || !page_ok(page_size)) return PD_ERR_UNSUPPORTED;
   if (batch == 0) return PD_OK;
   if (q == nullptr || kv == nullptr || block_table == nullptr || seq_lens == nullptr ||
       (!partials_only && out == nullptr))
@@ -560,7 +560,7 @@ int mla_common(const void* q, int64_t q_stride_row, int64_t q_stride_h, const vo
   a.B = batch;
   a.H = num_heads;
   a.P = page_size;
-  a.p_shift = __builtin_ctz((unsigned)page_size);
+  a.p_shift = page_shift(page_size);
   a.S = num_kv_splits;
   a.partials = partials_only ? 1 : 0;
   a.ws = workspace;

@@ -1,12 +1,14 @@
 // Paged GQA split-KV decode: launch dispatch over the page classes, and the
-// classes of 16-token pages and of pages of 32 tokens or more.  The kernel
-// itself is in gqa_decode_impl.h; the classes of smaller pages are
-// instantiated in gqa_decode_small_pages.hip.
+// classes of 16-token pages and of power-of-two pages of 32 tokens or more.
+// The kernel itself is in gqa_decode_impl.h; the classes of smaller pages are
+// instantiated in gqa_decode_small_pages.hip, the class of every other page
+// size in gqa_decode_general_pages.hip.
 #include "gqa_decode_impl.h"
 
 namespace pd {
 
-// instantiated in gqa_decode_small_pages.hip
+// instantiated in gqa_decode_small_pages.hip and gqa_decode_general_pages.hip
+extern template hipError_t launch_gqa_class<0>(const GqaArgs&, bool, int, hipStream_t);
 extern template hipError_t launch_gqa_class<1>(const GqaArgs&, bool, int, hipStream_t);
 extern template hipError_t launch_gqa_class<2>(const GqaArgs&, bool, int, hipStream_t);
 extern template hipError_t launch_gqa_class<4>(const GqaArgs&, bool, int, hipStream_t);
@@ -33,7 +35,10 @@ hipError_t launch_gqa_decode(const GqaArgs& a, hipStream_t stream) {
   const int n = grid_size();
   if (n <= 0) return hipErrorInvalidDevice;
   const bool verify = a.qlen > 1 || a.real_lens != nullptr || a.cu_q != nullptr;
-  if (a.P <= 0 || (a.P & (a.P - 1)) != 0 || (1 << a.p_shift) != a.P) return hipErrorInvalidValue;
+  if (a.P <= 0) return hipErrorInvalidValue;
+  if ((a.P & (a.P - 1)) != 0) return a.P >= 3 ? launch_gqa_class<0>(a, verify, n, stream)
+                                               : hipErrorInvalidValue;
+  if ((1 << a.p_shift) != a.P) return hipErrorInvalidValue;
   switch (a.P) {
     case 1: return launch_gqa_class<1>(a, verify, n, stream);
     case 2: return launch_gqa_class<2>(a, verify, n, stream);

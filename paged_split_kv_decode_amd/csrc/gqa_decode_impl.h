@@ -68,6 +68,11 @@ static_assert(4 * kTileBytes8 == kRingBytes, "FP8 ring of 4 tiles");
 // one chunk), and the 8 rows a 16-lane group reads for a V^T fragment
 // (4 g .. 4 g + 3 and 16 + 4 g .. 16 + 4 g + 3) too.
 __device__ __forceinline__ int f8(int r) { return (r & 15) ^ ((r >> 4) << 2); }
+// 1 KB of zeros in device memory: the source of rows of pages that are not
+// read in the general page class (any 16-byte chunk of a 512-byte row stays
+// inside it).
+__device__ __attribute__((aligned(1024))) uint32_t g_zero_rows[256];
+
 // Smallest share a wave takes: below it the per-wave start-up dominates.
 constexpr int kMinWaveTiles = 4;
 // Share skew between XCDs, per mille of the mean share.  On MI355X the odd
@@ -190,7 +195,9 @@ constexpr int kCachedChunks = 4;                          // request lengths kep
 // single column range per unit and none of the per-column limit work.
 // PS: the page class.  1, 2, 4, 8 or 16: the page size itself (pages
 // smaller than a tile); 32: any power-of-two page of 32 tokens or more (a
-// tile then lies inside one page; log2 of the size comes in a.p_shift).
+// tile then lies inside one page; log2 of the size comes in a.p_shift);
+// 0: any other page size of 3 tokens or more (a tile spans at most 12 pages
+// and a load's 2 or 4 rows at most 2).
 template <int PS, bool V, bool F8>
 __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
   constexpr int kSlotBytes = F8 ? kTileBytes8 : kTileBytes;     // one tile as loaded
@@ -253,7 +260,7 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
   // the skew needs the round-robin placement of workgroups on the 8 XCDs of
   // the whole chip (one workgroup per CU: 256); a partitioned device places
   // them otherwise and gets equal shares
-  constexpr int kSkew = (F8 || PS < 4) ? 0 : kXcdSkewPerMille;
+  constexpr int kSkew = (F8 || (PS != 0 && PS < 4)) ? 0 : kXcdSkewPerMille;
   const int dx = uniform(gridDim.x == 256 ? min(tpw * kSkew / 1000, tpw - t_min) : 0);
   sh.te = tpw + dx;
   sh.to = tpw - dx;
@@ -354,13 +361,20 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
   Cursor ci = cc;  // next tile to issue
 
   // ---- block-table entries of one tile (scalar loads) -------------------
+  constexpr bool kGen = PS == 0;
   constexpr bool kBig = PS >= kTileTokens;
-  constexpr int PPT = kBig ? 1 : kTileTokens / PS;   // pages per tile
+  // General pages: a window of 16 consecutive entries from the tile's first
+  // page, of which a tile of 32 rows uses at most 12 (pages of 3 tokens or
+  // more).
+  constexpr int kGenWindow = 16;
+  constexpr int kGenPages = 12;
+  constexpr int PPT = kGen ? kGenWindow : kBig ? 1 : kTileTokens / (PS > 0 ? PS : 1);   // pages per tile
   // Pages of 1, 2 or 4 tokens (8 or more per tile): each lane computes its
-  // own row's source address and checks in vector registers; larger pages
-  // keep a per-page scalar address and check.
-  constexpr bool kLaneAddr = !kBig && PS <= 4;
-  const int p_shift = kBig ? a.p_shift : __builtin_ctz(PS);
+  // own row's source address and checks in vector registers; larger
+  // power-of-two pages keep a per-page scalar address and check.  General
+  // pages also use per-lane addresses.
+  constexpr bool kLaneAddr = !kGen && !kBig && PS <= 4;
+  const int p_shift = kBig ? a.p_shift : kGen ? 0 : __builtin_ctz(PS > 0 ? PS : 1);
   auto tile_tok0 = [&](const Cursor& cu) { return ((cu.r.lo >> 5) + cu.i) * kTileTokens; };
   // The entries are only checked when the tile is issued, so the scalar
   // loads stay in flight for a whole iteration.  Only entries of attended
@@ -368,11 +382,36 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
   // page), so every read stays inside the request's block-table row.
   struct TilePages {
     int id[PPT];
-    bool att[kLaneAddr ? 1 : PPT];   // page attended (scalar classes)
+    bool att[(kLaneAddr || kGen) ? 1 : PPT];   // page attended (scalar classes)
+    int first;                                 // general pages: page of the tile's first row
   };
   auto fetch_pages = [&](const Cursor& cu) {
     TilePages tp;
     const PD_CONST int32_t* bt_row = as_const(a.bt) + (int64_t)cu.b * a.bt_sb;
+    if constexpr (kGen) {
+      // entries of pages first .. first + 15, inside the row: one wide read
+      // when the whole window lies in the row, else entry by entry clamped to
+      // the last attended page (entries of pages not attended are never used)
+      const int first = tile_tok0(cu) / a.P;
+      tp.first = first;
+      tp.att[0] = false;
+      if (first + kGenWindow <= a.max_blocks) {
+        typedef int32_t i32x8 __attribute__((ext_vector_type(8), aligned(4)));
+        const PD_CONST i32x8* wv = (const PD_CONST i32x8*)(bt_row + first);
+#pragma unroll
+        for (int q = 0; q < kGenWindow / 8; ++q) {
+          const i32x8 v = wv[q];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) tp.id[8 * q + e] = v[e];
+        }
+      } else {
+        const int last = (cu.r.hi - 1) / a.P;
+#pragma unroll
+        for (int j = 0; j < kGenWindow; ++j) tp.id[j] = bt_row[min(first + j, last)];
+      }
+      return tp;
+    }
+    tp.first = 0;
     const int pidx0 = tile_tok0(cu) >> p_shift;
     if constexpr (kLaneAddr) {
       if (PPT == 32 && pidx0 + PPT <= a.max_blocks) {
@@ -407,9 +446,12 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
   TilePages pages_none;
 #pragma unroll
   for (int j = 0; j < PPT; ++j) pages_none.id[j] = 0;
-  if constexpr (!kLaneAddr) {
+  pages_none.first = 0;
+  if constexpr (!kLaneAddr && !kGen) {
 #pragma unroll
     for (int j = 0; j < PPT; ++j) pages_none.att[j] = false;
+  } else {
+    pages_none.att[0] = false;
   }
 
   // ---- HBM -> LDS loads of one tile (and of a new piece's query rows) ----
@@ -457,7 +499,51 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
       return F8 ? (uint32_t)((lane & 15) ^ f8(r)) : (uint32_t)((lane & 31) ^ swz(r));
     };
     bool bad_page = false;
-    if constexpr (kLaneAddr) {
+    if constexpr (kGen) {
+      // Every row's source address is computed once per tile, row rho by
+      // lanes rho and 32 + rho; each load then fetches its rows' addresses
+      // from those lanes with ds_bpermute.  A row of a page that is not read
+      // points at a zero block in device memory, so the loads need no mask.
+      const int P = a.P;
+      // lane j: the entry of page first + j (a tile spans at most 12 pages)
+      int win = 0;
+#pragma unroll
+      for (int j = 0; j < kGenPages; ++j) win = lane == j ? tp.id[j] : win;
+      const int pg_lo = cu.r.lo / P, pg_end = (cu.r.hi - 1) / P + 1;   // attended pages
+      const int s0 = tok0 - tp.first * P;   // slot of the tile's first row
+      const int rho = lane & 31;
+      const int e = (s0 + rho) / P;         // page of row rho, from the tile's first page
+      const int slot = s0 + rho - e * P;
+      const int id = __builtin_amdgcn_ds_bpermute(e << 2, win);
+      const int pg = tp.first + e;
+      const bool att = pg >= pg_lo && pg < pg_end;
+      const bool inr = (uint32_t)id < num_pages;
+      bad_page = __ballot(att && !inr) != 0;
+      const uint64_t row_src =
+          att && inr ? (uint64_t)(uintptr_t)(kv_head + (int64_t)id * sp_bytes + (uint32_t)slot * kRowB)
+                     : (uint64_t)(uintptr_t)g_zero_rows;
+      const int rs_lo = (int)(uint32_t)row_src, rs_hi = (int)(uint32_t)(row_src >> 32);
+      // all the loads' addresses first (one wait for the lane exchanges),
+      // then the loads
+      uint32_t lo[kLoadsPerTile], hi[kLoadsPerTile];
+#pragma unroll
+      for (int i = 0; i < kLoadsPerTile; ++i) {
+        const int r = kRowsPerLoad * i + sub;
+        lo[i] = (uint32_t)__builtin_amdgcn_ds_bpermute(r << 2, rs_lo);
+        hi[i] = (uint32_t)__builtin_amdgcn_ds_bpermute(r << 2, rs_hi);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      auto one = [&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        const int r = kRowsPerLoad * i + sub;
+        const char* src =
+            (const char*)(uintptr_t)(((uint64_t)hi[i] << 32) | lo[i]) + chunk_of(r) * 16;
+        global_to_lds_16_stream_v<i * 1024>(src, dst);
+      };
+      [&]<int... I>(std::integer_sequence<int, I...>) {
+        (one(std::integral_constant<int, I>{}), ...);
+      }(std::make_integer_sequence<int, kLoadsPerTile>{});
+    } else if constexpr (kLaneAddr) {
       // bit j: page j of the tile is attended
       const int pidx0 = tok0 >> p_shift;
       const int j_lo = min(max((cu.r.lo >> p_shift) - pidx0, 0), PPT);

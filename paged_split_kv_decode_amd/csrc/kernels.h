@@ -40,7 +40,7 @@ struct GqaArgs {
   int32_t window;
   float scale_log2;  // sm_scale * log2(e)
   int32_t B, Hq, Hkv, G, P;
-  int32_t p_shift;   // log2(P): the page size is a power of two
+  int32_t p_shift;   // log2(P) when the page size is a power of two, else 0
   int32_t S;         // split cap: no (request, kv head) is cut into more pieces
   int32_t partials;  // 1: always write workspace partials (never O / LSE)
   float* ws;         // [B * qlen, Hq, S, D + 1] when S > 1 or partials
@@ -76,7 +76,7 @@ struct MlaArgs {
   int32_t qlen;
   float scale_log2;
   int32_t B, H, P;
-  int32_t p_shift;   // log2(P): the page size is a power of two
+  int32_t p_shift;   // log2(P) when the page size is a power of two, else 0
   int32_t S;
   int32_t partials;  // write split partials even with S == 1 (no merge follows)
   float* ws;
@@ -104,15 +104,17 @@ struct AppendArgs {
 };
 
 hipError_t launch_gqa_decode(const GqaArgs& a, hipStream_t stream);
-// One GQA page class (1, 2, 4, 8, 16, or 32 for every page of 32 tokens or
-// more); each class is instantiated in its own translation unit.
+// One GQA page class (1, 2, 4, 8, 16, 32 for every power-of-two page of 32
+// tokens or more, or 0 for every other page size); the classes are
+// instantiated in their own translation units.
 template <int PS>
 hipError_t launch_gqa_class(const GqaArgs& a, bool verify, int n_wg, hipStream_t stream);
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_mla_verify(const MlaArgs& a, hipStream_t stream);
-// One MLA page class (1, 2, 4, 8, or 16 for every page of 16 tokens or
-// more); the classes are instantiated in their own translation units.
+// One MLA page class (1, 2, 4, 8, 16 for every power-of-two page of 16
+// tokens or more, or 0 for every other page size); the classes are
+// instantiated in their own translation units.
 template <int PC>
 hipError_t launch_mla_class(const MlaArgs& a, int n_wg, hipStream_t stream);
 

@@ -1,11 +1,13 @@
 // Causal MLA verify: launch dispatch over the page classes, and the class of
-// pages of 16 tokens or more.  The kernel is in mla_verify_impl.h; the
-// classes of smaller pages are instantiated in mla_verify_small_pages.hip.
+// power-of-two pages of 16 tokens or more.  The kernel is in mla_verify_impl.h;
+// the classes of smaller pages are instantiated in mla_verify_small_pages.hip,
+// the class of every other page size in mla_verify_general_pages.hip.
 #include "mla_verify_impl.h"
 
 namespace pd {
 
-// instantiated in mla_verify_small_pages.hip
+// instantiated in mla_verify_small_pages.hip and mla_verify_general_pages.hip
+extern template hipError_t launch_mla_class<0>(const MlaArgs&, int, hipStream_t);
 extern template hipError_t launch_mla_class<1>(const MlaArgs&, int, hipStream_t);
 extern template hipError_t launch_mla_class<2>(const MlaArgs&, int, hipStream_t);
 extern template hipError_t launch_mla_class<4>(const MlaArgs&, int, hipStream_t);
@@ -30,7 +32,9 @@ hipError_t launch_mla_verify(const MlaArgs& a, hipStream_t stream) {
   if (a.B == 0) return hipSuccess;
   const int n = mla_grid_size();
   if (n <= 0) return hipErrorInvalidDevice;
-  if (a.P <= 0 || (a.P & (a.P - 1)) != 0 || (1 << a.p_shift) != a.P) return hipErrorInvalidValue;
+  if (a.P <= 0) return hipErrorInvalidValue;
+  if ((a.P & (a.P - 1)) != 0) return a.P >= 3 ? launch_mla_class<0>(a, n, stream) : hipErrorInvalidValue;
+  if ((1 << a.p_shift) != a.P) return hipErrorInvalidValue;
   switch (a.P) {
     case 1: return launch_mla_class<1>(a, n, stream);
     case 2: return launch_mla_class<2>(a, n, stream);

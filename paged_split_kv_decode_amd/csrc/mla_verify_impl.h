@@ -103,8 +103,10 @@ __device__ __forceinline__ int tile_off(int c, int r16) {
 // chunk c8 (16 bytes) of row r16 at slot 16 c8 + r16.
 
 
-// PC: the page class, 1, 2, 4 or 8 (the page size) or 16 (every
-// power-of-two page of 16 tokens or more; log2 of the size in a.p_shift).
+// PC: the page class, 1, 2, 4 or 8 (the page size), 16 (every power-of-two
+// page of 16 tokens or more; log2 of the size in a.p_shift) or 0 (every
+// other page size, 3 tokens or more: an issuing wave's 8 (bf16) or 16 (FP8)
+// rows span at most 4 or 6 pages, and each lane divides to find its row's).
 template <int NS, bool FP8, int PC>
 __global__ __launch_bounds__(kWaves * 64, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_verify_kernel(MlaArgs a) {
@@ -271,15 +273,19 @@ void mla_verify_kernel(MlaArgs a) {
     // one page (entry j: region j, at token slot slot0[j]).  PC < 16: each
     // issuing wave reads the entries of its own rows' pages only (kCand of
     // them), and each lane picks its row's page.
+    constexpr bool kGen = PC == 0;
     constexpr bool kBigP = PC >= 16;
     constexpr int kWaveRows = FP8 ? 16 : 8;                 // rows of a tile one issuing wave loads
-    constexpr int kCand = kBigP ? 2 : kWaveRows / PC;
-    const int p_shift = kBigP ? a.p_shift : __builtin_ctz(PC);
-    const int last_page = (hi_blk - 1) >> p_shift;          // hi_blk >= 1 whenever a tile is read
+    // candidate pages of an issuing wave's rows
+    constexpr int kCand = kBigP ? 2 : kGen ? (FP8 ? 6 : 4) : kWaveRows / (PC > 0 ? PC : 1);
+    const int p_shift = kBigP ? a.p_shift : kGen ? 0 : __builtin_ctz(PC > 0 ? PC : 1);
+    // hi_blk >= 1 whenever a tile is read
+    const int last_page = kGen ? (hi_blk - 1) / a.P : (hi_blk - 1) >> p_shift;
     struct TilePages {
       int id[kCand];
       bool att[kBigP ? 2 : 1];       // region attended (PC = 16)
-      int slot0[kBigP ? 2 : 1];      // token slot of the region's first row (PC = 16)
+      int slot0[kBigP ? 2 : 1];      // token slot of the region's (PC = 16) or the wave's
+                                     // (general pages) first row
       int first;                     // page index of entry 0 (PC < 16)
     };
     auto fetch = [&](int T) {
@@ -294,7 +300,14 @@ void mla_verify_kernel(MlaArgs a) {
         }
       } else {
         // this wave's rows are tile tokens kWaveRows * w .. + kWaveRows - 1
-        tp.first = (32 * T + kWaveRows * (wave & (FP8 ? 1 : 3))) >> p_shift;
+        const int tok = 32 * T + kWaveRows * (wave & (FP8 ? 1 : 3));
+        if constexpr (kGen) {
+          tp.first = tok / a.P;
+          tp.slot0[0] = tok - tp.first * a.P;
+        } else {
+          tp.first = tok >> p_shift;
+          tp.slot0[0] = 0;
+        }
   #pragma unroll
         for (int c = 0; c < kCand; ++c) tp.id[c] = bt_row[min(tp.first + c, last_page)];
       }
@@ -352,18 +365,29 @@ void mla_verify_kernel(MlaArgs a) {
         tl.gstep = ok ? kGStep : 0;
       } else {
         // every entry this wave read is of an attended page if at or below
-        // the block's last page
+        // the block's last page; general pages: candidates past the page of
+        // the wave's last row are read (inside the attended pages) but are
+        // not this wave's, so they are neither used nor checked here
+        const int n_cand = kGen ? (tp.slot0[0] + kWaveRows - 1) / a.P + 1 : kCand;
         if (wave < kIssueWaves) {
   #pragma unroll
           for (int c = 0; c < kCand; ++c)
-            bad |= tp.first + c <= last_page && (uint32_t)tp.id[c] >= num_pages;
+            bad |= c < n_cand && tp.first + c <= last_page && (uint32_t)tp.id[c] >= num_pages;
         }
         // the lane's row (0 .. kWaveRows - 1 of this wave's rows) is in
-        // candidate page row / PC; a select tree over wave-uniform values (a
-        // select chain over the array would become a per-lane index into
-        // scratch memory)
+        // candidate page row / PC (general pages: (slot0 + row) / P); a
+        // select tree over wave-uniform values (a select chain over the array
+        // would become a per-lane index into scratch memory)
         const int row = FP8 ? row8 : (lane >> 3);
-        const int cand = row >> __builtin_ctz(PC);
+        int cand, slot;
+        if constexpr (kGen) {
+          const int rr = tp.slot0[0] + row;
+          cand = rr / a.P;
+          slot = rr - cand * a.P;
+        } else {
+          cand = row >> __builtin_ctz(PC > 0 ? PC : 1);
+          slot = row & ((PC > 0 ? PC : 1) - 1);
+        }
         int v[kCand];
   #pragma unroll
         for (int c = 0; c < kCand; ++c) v[c] = __builtin_amdgcn_readfirstlane(tp.id[c]);
@@ -378,7 +402,7 @@ void mla_verify_kernel(MlaArgs a) {
         // bf16: a lane whose page is not read steps through the first bytes
         // of q (at least 32 rows of 1152 bytes), so the step stays
         // wave-uniform, one register less (measured faster for bf16 only)
-        tl.base = ok ? kv + (int64_t)id * sp_bytes + (row & (PC - 1)) * st_bytes + chunk : (const char*)a.q;
+        tl.base = ok ? kv + (int64_t)id * sp_bytes + slot * st_bytes + chunk : (const char*)a.q;
         tl.voff = 0u;
         tl.gstep = (FP8 && !ok) ? 0 : kGStep;
       }
@@ -734,7 +758,11 @@ void mla_verify_kernel(MlaArgs a) {
     PD_LDS float* row_m = row_l + kRowsPerBlock;
     // bit 0: a row overflowed its reference; bit 1: this wave read an
     // out-of-range attended block-table entry
-    if (lane == 0) flags[wave] = (__ballot(overflow) != 0ull ? 1 : 0) | (bad ? 2 : 0);
+    // (the ballots run with the whole wave active: inside the lane-0 branch
+    // they would see lane 0 alone)
+    const bool wave_ovf = __ballot(overflow) != 0ull;
+    const bool wave_bad = __ballot(bad) != 0ull;
+    if (lane == 0) flags[wave] = (wave_ovf ? 1 : 0) | (wave_bad ? 2 : 0);
     if (g2 == 0) {
       row_l[wave * kRowsPerWave + l32] = l_run;
       row_m[wave * kRowsPerWave + l32] = m_ref;

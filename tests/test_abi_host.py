@@ -179,8 +179,8 @@ def test_gqa_argument_checks_happen_before_any_hip_call():
     assert _gqa(scale=0.0) == PD_ERR_INVALID                  # softmax scale must be > 0
     assert _gqa(scale=-0.088) == PD_ERR_INVALID
     assert _gqa(D=64) == PD_ERR_UNSUPPORTED
-    assert _gqa(P=12) == PD_ERR_UNSUPPORTED                    # not a power of two
     assert _gqa(P=1 << 17) == PD_ERR_UNSUPPORTED
+    assert _gqa(P=(1 << 16) + 1) == PD_ERR_UNSUPPORTED
     assert _gqa(P=0) == PD_ERR_INVALID
     assert _gqa(Hq=136, Hkv=8) == PD_ERR_UNSUPPORTED          # G = 17
     assert _gqa(q=FAKE + 8) == PD_ERR_ALIGN
@@ -284,10 +284,8 @@ def test_mla_argument_checks_happen_before_any_hip_call():
     assert _mla(scale=-0.07) == PD_ERR_INVALID
     assert _mla(Lk=512) == PD_ERR_UNSUPPORTED
     assert _mla(Lv=256) == PD_ERR_UNSUPPORTED
-    assert _mla(P=24) == PD_ERR_UNSUPPORTED                    # not a power of two
     assert _mla(P=1 << 17) == PD_ERR_UNSUPPORTED
     assert _mla(P=0) == PD_ERR_INVALID
-    assert _mla(H=7, qlen=1) == PD_ERR_UNSUPPORTED             # rows per block
     assert _mla(out=FAKE + 2) == PD_ERR_ALIGN
     assert _mla(dt=1, st=576 + 8) == PD_ERR_ALIGN              # fp8 rows need 16 B
     assert _mla(S=2) == PD_ERR_WORKSPACE
@@ -359,7 +357,6 @@ def test_mla_partials_argument_checks_happen_before_any_hip_call():
     assert _mlap(kv=NULL) == PD_ERR_INVALID
     assert _mlap(qlen=0) == PD_ERR_INVALID
     assert _mlap(Lv=256) == PD_ERR_UNSUPPORTED
-    assert _mlap(P=24) == PD_ERR_UNSUPPORTED
     assert _mlap(ws=NULL, wsb=0) == PD_ERR_WORKSPACE           # S = 1 still writes partials
     assert _mlap(wsb=8 * 128 * 513 * 4 - 4) == PD_ERR_WORKSPACE
     assert _mlap(ws=FAKE + 4) == PD_ERR_ALIGN

@@ -89,7 +89,8 @@ def test_worked_example_block_table(pd, reading, S):
 
 
 @pytest.mark.parametrize("P,G", [(16, 8), (32, 8), (16, 4), (16, 1), (32, 16),
-                                 (1, 8), (2, 4), (4, 8), (8, 8), (64, 8), (128, 2)])
+                                 (1, 8), (2, 4), (4, 8), (8, 8), (64, 8), (128, 2),
+                                 (3, 8), (5, 1), (12, 4), (33, 16), (48, 8), (96, 2)])
 def test_marker_keys_are_bit_exact(pd, P, G):
     """Request b attends L keys; key `target_b` scores 256 above every other
     (scale 1), so all other weights underflow to exactly 0 in fp32 and O must

@@ -74,7 +74,8 @@ def test_reduced_config(pd, S, fp8):
     _check(w, vals, out, lse, fp8, f"reduced S={S} fp8={fp8}")
 
 
-@pytest.mark.parametrize("H,qlen", [(128, 4), (16, 2), (32, 1), (64, 3)])
+@pytest.mark.parametrize("H,qlen", [(128, 4), (16, 2), (32, 1), (64, 3), (16, 1), (8, 1),
+                                    (16, 3), (128, 3), (32, 5), (8, 7), (1, 1), (20, 2)])
 def test_head_and_qlen_shapes(pd, H, qlen):
     w = mla_workload(batch=2, len_range=(30, 300), heads=H, qlen=qlen)
     vals = w.values("cuda", poison=True)
@@ -83,7 +84,8 @@ def test_head_and_qlen_shapes(pd, H, qlen):
         _check(w, vals, out, lse, False, f"H={H} qlen={qlen} S={S}")
 
 
-def test_marker_keys_at_the_row_limit(pd):
+@pytest.mark.parametrize("P,H", [(16, 16), (16, 8), (3, 16), (12, 6), (48, 16)])
+def test_marker_keys_at_the_row_limit(pd, P, H):
     """q = e0 for every row, so a key's score is its K[0].  Request b targets
     row t = b: the key at hi_t - 1 (the last one row t may attend) carries a
     marker (K[0] = 300) and the key at hi_t (the first one it must not
@@ -92,7 +94,7 @@ def test_marker_keys_at_the_row_limit(pd):
     the decoy's or another key's V.  Keys past the request's largest limit
     are NaN and must never leak (keys that some row of the request attends
     hold finite data, as a real cache does)."""
-    qlen, H, Lk, Lv, P = 4, 16, 576, 512, 16
+    qlen, Lk, Lv = 4, 576, 512
     L = 53
     B = qlen - 1                       # t = qlen - 1 has no key past its limit
     rng = np.random.default_rng(9)

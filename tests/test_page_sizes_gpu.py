@@ -2,18 +2,21 @@
 oracle.
 
 "vllm.v1.attention.ops.triton_decode_attention" states support for any page
-size of at least one token; the library takes every power of two.  Pages
+size of at least one token, and so does the library.  Power-of-two pages
 smaller than a 32-token tile put several pages in one tile (1, 2, 4, 8 and
 16 tokens: one block-table entry per page, and for 1 and 2 tokens a page per
-lane within one load); pages of 32 tokens or more hold whole tiles at an
-offset inside the page.  Covered: decode with sinks, verify with windows and
-real lengths, the FP8 cache, split counts, and bitwise equality of the
-outputs for one logical cache stored at different page sizes (the kernel's
-arithmetic does not depend on where a key lives).  The MLA verify kernel
-reads 16-row regions of its 32-token tiles: pages of 16 tokens or more hold
-whole regions, smaller pages are picked per lane; covered at 1 to 64 tokens
-per page, bf16 and FP8, with rows that have no key, an out-of-range entry
-(NaN for its request) and bitwise equality across page sizes.
+lane within one load); power-of-two pages of 32 tokens or more hold whole
+tiles at an offset inside the page; every other size (3, 5, 12, 33, 48 and
+96 here) goes through the general class, whose loads may straddle a page
+boundary anywhere in a tile.  Covered: decode with sinks, verify with
+windows and real lengths, the FP8 cache, split counts, out-of-range entries
+and bitwise equality of the outputs for one logical cache stored at
+different page sizes (the kernel's arithmetic does not depend on where a key
+lives).  The MLA verify kernel reads 16-row regions of its 32-token tiles:
+power-of-two pages of 16 tokens or more hold whole regions, smaller and
+non-power-of-two pages are picked per lane; covered at 1 to 96 tokens per
+page, bf16 and FP8, with rows that have no key, an out-of-range entry (NaN
+for its request) and bitwise equality across page sizes.
 """
 
 import numpy as np
@@ -26,7 +29,7 @@ from synth import gqa_workload, mla_workload
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X")]
 
-PAGE_SIZES = [1, 2, 4, 8, 64, 256]
+PAGE_SIZES = [1, 2, 3, 4, 8, 12, 48, 64, 96, 256]
 
 
 @pytest.fixture(scope="module")
@@ -51,7 +54,7 @@ def _cap(pd, w):
     return pd.gqa_split_cap(w.B, w.Hkv, int(w.seq_lens.max()), w.window)
 
 
-@pytest.mark.parametrize("P", PAGE_SIZES)
+@pytest.mark.parametrize("P", PAGE_SIZES + [5, 33])
 @pytest.mark.parametrize("S", ["cap", 1, 3])
 def test_decode_with_sinks(pd, P, S):
     w = gqa_workload("gqa_sinks", batch=6, len_range=(1, 700), page_size=P, pool="tight",
@@ -85,6 +88,23 @@ def test_fp8_cache(pd, P):
         out, lse = _run(pd, w, vals, S, fp8=True)
         O, L = oracle_gqa(w, vals)
         check_attention(out, lse, O, L, o_atol=O_ATOL_FP8, what=f"fp8 P={P} S={S}")
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("P", [3, 12, 48])
+def test_out_of_range_entry_gives_nan(pd, P, fp8):
+    """An attended out-of-range entry NaNs its request (every kv head); the
+    neighbour request, read by the same waves, stays exact."""
+    w = gqa_workload("gqa_sinks", fixed_lens=[300, 300], page_size=P, pool="tight")
+    vals = w.values("cuda", poison=True, fp8=fp8)
+    bt = w.block_table.copy()
+    bt[1, 170 // P] = w.num_pages + 3
+    for S in (1, 2):
+        out, lse = _run(pd, w, vals, S, bt=bt, fp8=fp8)
+        assert torch.all(torch.isnan(out[1].float())) and torch.all(torch.isnan(lse[1]))
+        O, L = oracle_gqa(w, vals, requests=[0])
+        check_attention(out[:1], lse[:1], O, L, o_atol=O_ATOL_FP8 if fp8 else 2e-2,
+                        what=f"valid neighbour P={P}")
 
 
 def _relayout(w, kv, P2, rng):
@@ -121,7 +141,7 @@ def test_outputs_bitwise_equal_across_page_sizes(pd, qlen, window):
     rng = np.random.default_rng(11)
     for S in (1, 3):
         ref_o, ref_l = _run(pd, w, vals, S)
-        for P2 in (1, 2, 8, 64):
+        for P2 in (1, 2, 3, 8, 12, 48, 64, 96):
             kv2, bt2 = _relayout(w, vals["kv"], P2, rng)
             o, l = _run(pd, w, vals, S, kv=kv2, bt=bt2)
             assert torch.equal(o.view(torch.int16), ref_o.view(torch.int16)), (P2, S)
@@ -132,7 +152,7 @@ def test_outputs_bitwise_equal_across_page_sizes(pd, qlen, window):
 # MLA causal verify
 # ---------------------------------------------------------------------------
 
-MLA_PAGE_SIZES = [1, 2, 4, 8, 32, 64]
+MLA_PAGE_SIZES = [1, 2, 3, 4, 8, 12, 32, 48, 64, 96]
 
 
 def _run_mla(pd, w, vals, S, fp8=False, kv=None, bt=None):
@@ -163,7 +183,7 @@ def test_mla_verify(pd, P, fp8):
 
 
 @pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
-@pytest.mark.parametrize("P", [1, 4, 64])
+@pytest.mark.parametrize("P", [1, 3, 4, 48, 64])
 def test_mla_rows_without_keys(pd, P, fp8):
     """L < qlen and L = 0 at small and large pages, 16 heads (rows past the
     request's 64 rows in the 128-row block)."""
@@ -177,7 +197,7 @@ def test_mla_rows_without_keys(pd, P, fp8):
 
 
 @pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
-@pytest.mark.parametrize("P", [1, 2, 8, 32])
+@pytest.mark.parametrize("P", [1, 2, 3, 8, 12, 32, 96])
 def test_mla_out_of_range_entry_gives_nan(pd, P, fp8):
     """An attended out-of-range entry NaNs its request's rows; every wave
     learns it through the end-of-piece exchange, whichever wave read it."""
@@ -220,7 +240,7 @@ def test_mla_outputs_bitwise_equal_across_page_sizes(pd, fp8):
     rng = np.random.default_rng(13)
     for S in (1, 2):
         ref_o, ref_l = _run_mla(pd, w, vals, S, fp8)
-        for P2 in (1, 2, 4, 8, 64):
+        for P2 in (1, 2, 3, 4, 8, 12, 48, 64):
             kv2, bt2 = _relayout_mla(w, vals["kv"], P2, rng)
             o, l = _run_mla(pd, w, vals, S, fp8, kv=kv2, bt=bt2)
             assert torch.equal(o.view(torch.int16), ref_o.view(torch.int16)), (P2, S)
