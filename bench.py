@@ -28,8 +28,8 @@ copies of a pool that holds only the pages in use (MLA).  The hot figures
 (one copy) are reported beside them.
 
 ``--config`` selects another workload: gqa_sinks, gqa_window, tiny_gqa,
-gqa_verify, gqa_verify_varlen, gqa_sinks_fp8, kv_append, mla_verify,
-mla_verify_fp8.
+gqa_verify, gqa_verify4, gqa_verify_varlen, gqa_sinks_fp8, kv_append,
+mla_verify, mla_verify_fp8.
 """
 
 from __future__ import annotations
@@ -133,9 +133,10 @@ def _gqa_case(name, torch, pd, splits, page_size=0):
                 f"B=64, Hq=64, Hkv=8, D=128, page {w.P} HND, seq_lens U[1024,8192], {pool}")
         kind = "gqa_fp8"
     elif verify:
+        drop = 3 if name == "gqa_verify4" else 1
         desc = (f"GQA causal verify with sinks: B={w.B}, qlen={w.qlen}, Hq={w.Hq}, Hkv={w.Hkv}, "
-                f"D={w.D}, page {w.P} HND bf16, seq_lens U[1024,8192], real length L - U{{0,1}}, "
-                f"{pool}")
+                f"D={w.D}, page {w.P} HND bf16, seq_lens U[1024,8192], real length "
+                f"L - U{{0,{drop}}}, {pool}")
         kind = "gqa_verify"
     else:
         desc = {

@@ -192,10 +192,10 @@ PD_API size_t pd_workspace_bytes(int32_t rows, int32_t num_heads, int32_t num_sp
  * out          [B, Hq, D] bf16, strides (o_stride_b, o_stride_h, 1).
  * lse          [B, Hq] fp32 with row stride lse_stride_b, or NULL.
  *
- * Supported: D = 128; P any power of two from 1 to 65536 (the verify module
- * of "vllm.v1.attention.ops.triton_decode_attention" takes any page size of
- * at least one token; P < 1 gives PD_ERR_INVALID, other sizes
- * PD_ERR_UNSUPPORTED); Hq = G * Hkv with 1 <= G <= 16.
+ * Supported: D = 128; any page size P from 1 to 65536 tokens (the verify
+ * module of "vllm.v1.attention.ops.triton_decode_attention" takes any page
+ * size of at least one token; P < 1 gives PD_ERR_INVALID, P > 65536
+ * PD_ERR_UNSUPPORTED); Hq = G * Hkv with 1 <= G <= 64.
  * q, kv, out, workspace 16-byte aligned; q/kv/out strides multiples of 8.
  * A workspace must not be shared by calls in flight on different streams.
  */
@@ -244,9 +244,10 @@ PD_API int paged_decode_gqa(const void* q, int64_t q_stride_b, int64_t q_stride_
  * workspace    >= pd_workspace_bytes(B*qlen, Hq, S, D) bytes when S > 1.
  * Other arguments as for paged_decode_gqa.
  *
- * Supported: as paged_decode_gqa, with qlen * G <= 16 (the verify tokens of a
- * kv head's query heads share one score tile, so a cache tile is read once
- * for all of them); otherwise PD_ERR_UNSUPPORTED.  Also
+ * Supported: as paged_decode_gqa, with qlen * G <= 64 (the verify tokens of a
+ * kv head's query heads share the score tiles, groups of 16 (token, head)
+ * columns, so a cache tile is read once for all of them); otherwise
+ * PD_ERR_UNSUPPORTED.  Also
  * ((qlen-1)*q_stride_row + (G-1)*q_stride_h + D) * 2 < 2^31.  FP8 cache
  * strides must be multiples of 16.
  */
@@ -308,9 +309,11 @@ PD_API int paged_verify_gqa_noalloc(const void* q, int64_t q_stride_row, int64_t
  *
  * cu_seqlens_q [B+1] int32 on the device: cu[0] = 0, non-decreasing,
  *              cu[B] = total_rows.
- * max_qlen     host int >= every qlen_b; max_qlen * (Hq / Hkv) <= 16 (one
- *              score tile holds a kv head's rows).  Rows of a request past
- *              max_qlen are not computed (their output is unspecified).
+ * max_qlen     host int >= every qlen_b; max_qlen * (Hq / Hkv) <= 64 (the
+ *              score tiles hold a kv head's rows).  A request with more
+ *              query rows than max_qlen breaks this contract: all its rows
+ *              get NaN O and LSE (partials: NaN in every split slot), as
+ *              for an invalid block-table entry.
  * total_rows   host int: rows of q, out and lse; 0 is a no-op.
  * q, out, lse  [total_rows, Hq, D] / [total_rows, Hq]; workspace
  *              >= pd_workspace_bytes(total_rows, Hq, S, D) bytes when S > 1.
@@ -450,10 +453,10 @@ PD_API int paged_kv_append(const void* src0, int64_t src0_stride_tok, int64_t sr
  * out          [B*qlen, H, Lv] bf16, strides (o_stride_row, o_stride_h, 1).
  * lse          [B*qlen, H] fp32 with row stride lse_stride_row, or NULL.
  *
- * Supported: Lk = 576, Lv = 512 (512 + 64 rope dims); P any power of two
- * from 1 to 65536 (the module states support for page size >= 1);
- * qlen * H a multiple of 32; pointers 16-byte aligned; strides multiples of
- * 16 bytes.
+ * Supported: Lk = 576, Lv = 512 (512 + 64 rope dims); any page size P from
+ * 1 to 65536 tokens (the module states support for page size >= 1); any
+ * qlen * H >= 1 (rows are processed in blocks of 128: fewer rows leave part
+ * of a block idle); pointers 16-byte aligned; strides multiples of 16 bytes.
  */
 PD_API int paged_verify_mla(const void* q, int64_t q_stride_row, int64_t q_stride_h,
                      const void* kv, int32_t kv_dtype, int64_t kv_stride_page,

@@ -173,7 +173,7 @@ def paged_verify_gqa_varlen(q, kv, block_table, seq_lens, cu_seqlens_q, max_qlen
     q [total_rows, Hq, D] bf16 with request b's query tokens in rows
     cu_seqlens_q[b] .. cu_seqlens_q[b + 1] - 1; cu_seqlens_q [B + 1] int32 on
     the device (cu[0] = 0, non-decreasing, cu[B] = total_rows); max_qlen a
-    host int >= every request's query length, with max_qlen * Hq / Hkv <= 16.
+    host int >= every request's query length, with max_qlen * Hq / Hkv <= 64.
     Other arguments as for paged_verify_gqa.
     Returns (out [total_rows, Hq, D] bf16, lse [total_rows, Hq] fp32 or None).
     """

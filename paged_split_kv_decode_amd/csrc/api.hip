@@ -214,7 +214,7 @@ static int gqa_common(const void* q, int64_t q_stride_b, int64_t q_stride_h, con
   const bool fp8 = kv_dtype == PD_KV_FP8_E4M3FN;
   const int32_t G = num_q_heads / num_kv_heads;
   if (page_size < 1) return PD_ERR_INVALID;
-  if (head_dim != 128 || !page_ok(page_size) || (int64_t)qlen * G > 16)
+  if (head_dim != 128 || !page_ok(page_size) || (int64_t)qlen * G > 64)
     return PD_ERR_UNSUPPORTED;
   if (batch == 0) return PD_OK;
   if (q == nullptr || kv == nullptr || block_table == nullptr || seq_lens == nullptr ||

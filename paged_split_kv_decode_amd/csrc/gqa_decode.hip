@@ -34,7 +34,8 @@ static int grid_size() {
 hipError_t launch_gqa_decode(const GqaArgs& a, hipStream_t stream) {
   const int n = grid_size();
   if (n <= 0) return hipErrorInvalidDevice;
-  const bool verify = a.qlen > 1 || a.real_lens != nullptr || a.cu_q != nullptr;
+  // the verify instantiations also take decode with more than 16 heads per kv head
+  const bool verify = a.qlen > 1 || a.real_lens != nullptr || a.cu_q != nullptr || a.G > 16;
   if (a.P <= 0) return hipErrorInvalidValue;
   if ((a.P & (a.P - 1)) != 0) return a.P >= 3 ? launch_gqa_class<0>(a, verify, n, stream)
                                                : hipErrorInvalidValue;

@@ -143,6 +143,14 @@ __device__ __forceinline__ QRows query_rows(const GqaArgs& a, int b) {
   return QRows{r0, min(r1 - r0, a.qlen)};
 }
 
+// Variable query length: request b has more query rows than the max_qlen
+// bound (its rows are then all NaN, as for an invalid block-table entry).
+__device__ __forceinline__ bool rows_over_bound(const GqaArgs& a, int b, const QRows& qr) {
+  if (a.cu_q == nullptr) return false;
+  const int r1 = min(max((int)as_const(a.cu_q)[b + 1], qr.row0), a.total_rows);
+  return r1 - qr.row0 > qr.n;
+}
+
 __device__ __forceinline__ int real_len(const GqaArgs& a, int b) {
   return a.real_lens != nullptr ? (int)as_const(a.real_lens)[b] : kNoReal;
 }
@@ -198,8 +206,11 @@ constexpr int kCachedChunks = 4;                          // request lengths kep
 // tile then lies inside one page; log2 of the size comes in a.p_shift);
 // 0: any other page size of 3 tokens or more (a tile spans at most 12 pages
 // and a load's 2 or 4 rows at most 2).
-template <int PS, bool V, bool F8>
+// NC: score column groups of 16 (verify: qlen * G <= 16 NC columns; the
+// verify tokens of all groups share each K and V tile as loaded).
+template <int PS, bool V, bool F8, int NC>
 __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
+  static_assert(NC == 1 || (V && (NC == 2 || NC == 4)), "column groups: decode 1, verify 1, 2 or 4");
   constexpr int kSlotBytes = F8 ? kTileBytes8 : kTileBytes;     // one tile as loaded
   constexpr int kLoadsPerTile = kSlotBytes / (64 * 16);         // 16 (bf16) or 8 (FP8) loads
   __shared__ __attribute__((aligned(1024))) char smem[kNW * kWaveLds];
@@ -222,8 +233,14 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
   const int w = uniform(blockIdx.x * kNW + wave_in_wg);
   PD_LDS char* ring = (PD_LDS char*)smem + wave_in_wg * kWaveLds;
   PD_LDS char* qslots = ring + kRingBytes;
-  // this lane's score column: verify token t_col, head g_col of the kv head
-  int t_col = 0, g_col = l16;
+  // this lane's score column of group c: verify token t_col[c], head g_col[c]
+  // of the kv head (column 16 c + l16)
+  int t_col[NC], g_col[NC];
+#pragma unroll
+  for (int cg = 0; cg < NC; ++cg) {
+    t_col[cg] = 0;
+    g_col[cg] = 16 * cg + l16;
+  }
 
   // ---- the plan: total tiles, longest request, this wave's share --------
   // Lane l of chunk c holds the length of request 64c + l (0 past the batch).
@@ -477,7 +494,11 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
   // Issues the tile's loads; returns whether an attended page has an
   // out-of-range entry (its rows then come from the harmless source).
   auto issue = [&](const Cursor& cu, const TilePages& tp, int slot) {
-    if (piece_start(cu)) load_q(cu);
+    // (more than 16 columns: the query fragments come straight from global
+    // memory when the piece starts)
+    if constexpr (NC == 1) {
+      if (piece_start(cu)) load_q(cu);
+    }
     const uint32_t dst = uniform((int)lds_addr(ring + slot * kSlotBytes));
     constexpr int kElem = F8 ? 1 : 2;
     constexpr uint32_t kRowB = 2 * kD * kElem;
@@ -608,32 +629,43 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
   };
 
   // ---- per-piece state ----------------------------------------------------
-  bf16x8 qf[4];
-  float m_run = neg_inf();
-  float l_run = 0.f;
-  f32x4 o[8];
+  bf16x8 qf[NC][4];
+  float m_run[NC], l_run[NC];
+  f32x4 o[NC][8];
   bool piece_bad = false;
   int bad_slots = 0;   // bit s: the tile in ring slot s read a bad page
-  // keys of this lane's column in the current piece's request, and the
-  // range every column attends (tiles inside it need no score mask)
-  int col_lo = 0, col_hi = 0, all_lo = 0, all_hi = 0;
+  // keys of this lane's column (per group) in the current piece's request,
+  // and the range every column attends (tiles inside it need no score mask)
+  int col_lo[NC], col_hi[NC], all_lo = 0, all_hi = 0;
+#pragma unroll
+  for (int cg = 0; cg < NC; ++cg) {
+    m_run[cg] = neg_inf();
+    l_run[cg] = 0.f;
+    col_lo[cg] = col_hi[cg] = 0;
+  }
 
   auto finish_piece = [&](const Cursor& cu) {
-    const float l_tot = sum_xor32(sum_xor16(l_run));
-    const int hq = cu.kvh * G + g_col;
-    const int64_t row = (int64_t)cu.r.row0 + t_col;
-    if (l16 < R) {
-      const bool empty = !(l_tot > 0.f);
-      const float lse_nat = empty ? neg_inf() : (m_run * c + fast_log2(l_tot)) * kLn2;
+    // (the lane exchanges run with the whole wave active, before the
+    // per-column branch)
+    float l_tot[NC];
+#pragma unroll
+    for (int cg = 0; cg < NC; ++cg) l_tot[cg] = sum_xor32(sum_xor16(l_run[cg]));
+#pragma unroll
+    for (int cg = 0; cg < NC; ++cg) {
+      if (16 * cg + l16 >= R) continue;
+      const int hq = cu.kvh * G + g_col[cg];
+      const int64_t row = (int64_t)cu.r.row0 + t_col[cg];
+      const bool empty = !(l_tot[cg] > 0.f);
+      const float lse_nat = empty ? neg_inf() : (m_run[cg] * c + fast_log2(l_tot[cg])) * kLn2;
       const float nan = __builtin_nanf("");
       if (direct) {
-        float den = l_tot;
-        if (a.sinks != nullptr && !empty) den += fast_exp2(a.sinks[hq] * kLog2e - m_run * c);
+        float den = l_tot[cg];
+        if (a.sinks != nullptr && !empty) den += fast_exp2(a.sinks[hq] * kLog2e - m_run[cg] * c);
         const float inv = empty ? 0.f : v_mult / den;
         uint16_t* orow = a.out + row * a.o_sb + (int64_t)hq * a.o_sh + 4 * g4;
 #pragma unroll
         for (int blk = 0; blk < 8; ++blk) {
-          f32x4 r = o[blk] * inv;
+          f32x4 r = o[cg][blk] * inv;
           if (piece_bad) r = f32x4{nan, nan, nan, nan};
           *(u32x2*)(orow + 16 * blk) = u32x2{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
         }
@@ -642,10 +674,10 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
       } else {
         const int s = sh.split ? w - sh.of(cu.p0) : 0;
         float* slot = a.ws + ((row * a.Hq + hq) * S + s) * (kD + 1);
-        const float inv = empty ? 0.f : v_mult / l_tot;
+        const float inv = empty ? 0.f : v_mult / l_tot[cg];
 #pragma unroll
         for (int blk = 0; blk < 8; ++blk) {
-          f32x4 r = o[blk] * inv;
+          f32x4 r = o[cg][blk] * inv;
           if (piece_bad) r = f32x4{nan, nan, nan, nan};
 #pragma unroll
           for (int e = 0; e < 4; ++e) slot[16 * blk + 4 * g4 + e] = r[e];
@@ -687,10 +719,13 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
     for (int k = 0; cc.b < a.B; ++k) {
       const bool first = piece_start(cc);
       if (first) {
-        m_run = neg_inf();
-        l_run = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int cg = 0; cg < NC; ++cg) {
+          m_run[cg] = neg_inf();
+          l_run[cg] = 0.f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) o[cg][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
         piece_bad = false;
         if constexpr (F8) {
           const int si = cc.kvh * a.scale_stride;
@@ -700,13 +735,34 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
         if constexpr (V) {
           const int n = cc.r.n;   // >= 1: a unit with tiles has query rows
           R = n * G;
-          t_col = min(l16, R - 1) / G;
-          g_col = min(l16, R - 1) - t_col * G;
           const int L = as_const(a.seq_lens)[cc.b], Lr = real_len(a, cc.b);
-          col_hi = row_hi(a, L, Lr, t_col, n);
-          col_lo = row_lo(a, col_hi);
+#pragma unroll
+          for (int cg = 0; cg < NC; ++cg) {
+            const int nn = min(16 * cg + l16, R - 1);
+            t_col[cg] = nn / G;
+            g_col[cg] = nn - t_col[cg] * G;
+            col_hi[cg] = row_hi(a, L, Lr, t_col[cg], n);
+            col_lo[cg] = row_lo(a, col_hi[cg]);
+          }
           all_hi = uniform(row_hi(a, L, Lr, 0, n));                 // first row's limit
           all_lo = uniform(row_lo(a, row_hi(a, L, Lr, n - 1, n)));   // last row's start
+          piece_bad |= rows_over_bound(a, cc.b, QRows{cc.r.row0, n});
+        }
+        if constexpr (NC > 1) {
+          // More than 16 columns: the query fragments are loaded here, into
+          // registers, and waited for at once (a piece start drains the
+          // tiles in flight; the query slots in LDS hold 16 columns only).
+          // Column 16 c + l16 past the piece's columns reads the last one:
+          // its scores are never written.
+#pragma unroll
+          for (int cg = 0; cg < NC; ++cg) {
+            const bf16x8* qp =
+                (const bf16x8*)(a.q + (int64_t)(cc.r.row0 + t_col[cg]) * a.q_sb +
+                                (int64_t)(cc.kvh * G + g_col[cg]) * a.q_sh + 8 * g4);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) qf[cg][s] = qp[4 * s];
+          }
+          wait_vmcnt<0>();
         }
       }
 
@@ -730,14 +786,14 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
           wait_vmcnt<0>();
       }
 
-      if (first) {
+      if (NC == 1 && first) {
         // the piece's query rows (loaded before its first tile): B operand
         // of S^T = K Q^T, zero for padding heads
         PD_LDS const char* qs = qslots + (q_used & 1) * kQSlotBytes + l16 * (kD * 2);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const bf16x8 v = *(PD_LDS const bf16x8*)(qs + (8 * g4 + 32 * s) * 2);
-          qf[s] = l16 < R ? v : bf16x8{};
+          qf[0][s] = l16 < R ? v : bf16x8{};
         }
         ++q_used;
       }
@@ -760,7 +816,14 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
       const int tok0 = ((lo >> 5) + cc.i) * kTileTokens;
 
       // ---- scores ----
-      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+      // group c is in use while its first column is one of the piece's
+      // (wave-uniform); group 0 always is
+      bool act[NC];
+#pragma unroll
+      for (int cg = 0; cg < NC; ++cg) act[cg] = cg == 0 || 16 * cg < R;
+      f32x4 s0[NC], s1[NC];
+#pragma unroll
+      for (int cg = 0; cg < NC; ++cg) s0[cg] = s1[cg] = f32x4{0.f, 0.f, 0.f, 0.f};
       const int sw = swz(l16);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -782,8 +845,12 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
           k0 = *(PD_LDS bf16x8*)(tl + l16 * kRowBytes + ch * 16);
           k1 = *(PD_LDS bf16x8*)(tl + (16 + l16) * kRowBytes + ch * 16);
         }
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[s], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[s], s1, 0, 0, 0);
+#pragma unroll
+        for (int cg = 0; cg < NC; ++cg) {
+          if (!act[cg]) continue;
+          s0[cg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[cg][s], s0[cg], 0, 0, 0);
+          s1[cg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[cg][s], s1[cg], 0, 0, 0);
+        }
       }
 
       // V rows outside the request's keys are zeroed; scores outside the
@@ -797,11 +864,14 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
         v1[i] = !edge || (t1 >= lo && t1 < hi);
         if constexpr (V) {
           const bool col_edge = tok0 < all_lo || tok0 + kTileTokens > all_hi;
-          if (col_edge && !(t0 >= col_lo && t0 < col_hi)) s0[i] = neg_inf();
-          if (col_edge && !(t1 >= col_lo && t1 < col_hi)) s1[i] = neg_inf();
+#pragma unroll
+          for (int cg = 0; cg < NC; ++cg) {
+            if (col_edge && !(t0 >= col_lo[cg] && t0 < col_hi[cg])) s0[cg][i] = neg_inf();
+            if (col_edge && !(t1 >= col_lo[cg] && t1 < col_hi[cg])) s1[cg][i] = neg_inf();
+          }
         } else {
-          if (!v0[i]) s0[i] = neg_inf();
-          if (!v1[i]) s1[i] = neg_inf();
+          if (!v0[i]) s0[0][i] = neg_inf();
+          if (!v1[i]) s1[0][i] = neg_inf();
         }
       }
 
@@ -847,35 +917,39 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
       __builtin_amdgcn_sched_barrier(0);
 
       // ---- online softmax (fp32, exp2, running max in unscaled logits) ----
-      float mx = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
-                       fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
-      mx = max_xor32(max_xor16(mx));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_ref = m_new == neg_inf() ? 0.f : m_new;
-      const float mc = m_ref * c;
-      const float alpha = fast_exp2(m_run * c - mc);
-      float p0[4], p1[4];
-      float psum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p0[i] = fast_exp2(s0[i] * c - mc);
-        p1[i] = fast_exp2(s1[i] * c - mc);
-        psum += p0[i] + p1[i];
-      }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) o[i] *= alpha;
-
       // P^T as the B operand: k = 8*g4 + j <-> tokens 4*g4 + j (j < 4) and
       // 16 + 4*g4 + (j - 4) (j >= 4), exactly this lane's scores.
-      const u32x4 pw = {pack_bf16x2(p0[0], p0[1]), pack_bf16x2(p0[2], p0[3]),
-                        pack_bf16x2(p1[0], p1[1]), pack_bf16x2(p1[2], p1[3])};
-      const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
+      bf16x8 pf[NC];
+#pragma unroll
+      for (int cg = 0; cg < NC; ++cg) {
+        if (!act[cg]) continue;
+        float mx = fmaxf(fmaxf(fmaxf(s0[cg][0], s0[cg][1]), fmaxf(s0[cg][2], s0[cg][3])),
+                         fmaxf(fmaxf(s1[cg][0], s1[cg][1]), fmaxf(s1[cg][2], s1[cg][3])));
+        mx = max_xor32(max_xor16(mx));
+        const float m_new = fmaxf(m_run[cg], mx);
+        const float m_ref = m_new == neg_inf() ? 0.f : m_new;
+        const float mc = m_ref * c;
+        const float alpha = fast_exp2(m_run[cg] * c - mc);
+        float p0[4], p1[4];
+        float psum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p0[i] = fast_exp2(s0[cg][i] * c - mc);
+          p1[i] = fast_exp2(s1[cg][i] * c - mc);
+          psum += p0[i] + p1[i];
+        }
+        l_run[cg] = l_run[cg] * alpha + psum;
+        m_run[cg] = m_new;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[cg][i] *= alpha;
+        const u32x4 pw = {pack_bf16x2(p0[0], p0[1]), pack_bf16x2(p0[2], p0[3]),
+                          pack_bf16x2(p1[0], p1[1]), pack_bf16x2(p1[2], p1[3])};
+        pf[cg] = __builtin_bit_cast(bf16x8, pw);
+      }
       const u32x4 vkeep = {keep_mask(v0[0], v0[1]), keep_mask(v0[2], v0[3]),
                            keep_mask(v1[0], v1[1]), keep_mask(v1[2], v1[3])};
 
-      // ---- O^T += V^T P^T ----
+      // ---- O^T += V^T P^T (one V^T fragment for every column group) ----
 #pragma unroll
       for (int blk = 0; blk < 8; ++blk) {
         u32x4 vv = vraw[blk];
@@ -883,7 +957,12 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
           vv = u32x4{cvt8(vraw[blk][0], kLo), cvt8(vraw[blk][0], kHi), cvt8(vraw[blk][1], kLo),
                      cvt8(vraw[blk][1], kHi)};
         if (edge) vv &= vkeep;
-        o[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pf, o[blk], 0, 0, 0);
+#pragma unroll
+        for (int cg = 0; cg < NC; ++cg) {
+          if (!act[cg]) continue;
+          o[cg][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pf[cg],
+                                                              o[cg][blk], 0, 0, 0);
+        }
       }
 
       if (cc.i + 1 == cc.i_end) finish_piece(cc);
@@ -907,7 +986,9 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
     // (row, query head) of column n of this unit
     auto col_row = [&](int n) { return (int64_t)cw.r.row0 + n / G; };
     auto col_head = [&](int n) { return hq0 + n % G; };
-    if (cw.r.nt == 0) {
+    // a request past the max_qlen bound is written NaN below instead
+    const bool over = V && rows_over_bound(a, cw.b, QRows{cw.r.row0, cw.r.n});
+    if (cw.r.nt == 0 && !over) {
       if (direct) {
         for (int i = lane; i < R * (kD / 8); i += 64) {
           const int n = i / (kD / 8), d8 = (i % (kD / 8)) * 8;
@@ -927,6 +1008,36 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
         a.ws[((col_row(n) * a.Hq + col_head(n)) * S + s) * (kD + 1) + kD] = neg_inf();
       }
     }
+    if constexpr (V) {
+      // Variable query length: rows of the request past the max_qlen bound
+      // are not computed; the unit's owner writes them NaN (O and LSE, or
+      // every split slot), as for an invalid block-table entry.  (The rows
+      // it streams are NaN too: the piece is marked bad, or, for a unit
+      // with no key, written NaN here.)
+      const bool owner = cw.r.nt == 0 || !sh.split || cw.p0 >= sh.g0;
+      if (owner && over) {
+        const int r1 = min(max((int)as_const(a.cu_q)[cw.b + 1], cw.r.row0), a.total_rows);
+        // every row for a unit with no key, else the rows past the first n
+        const int first_row = cw.r.nt == 0 ? 0 : cw.r.n;
+        const int rows_nan = uniform(r1 - cw.r.row0 - first_row);
+        const float nan = __builtin_nanf("");
+        for (int i = lane; i < rows_nan * G; i += 64) {
+          const int64_t row = (int64_t)cw.r.row0 + first_row + i / G;
+          const int hq = hq0 + i % G;
+          if (direct) {
+            uint16_t* orow = a.out + row * a.o_sb + (int64_t)hq * a.o_sh;
+            for (int d = 0; d < kD; d += 8)
+              *(u32x4*)(orow + d) = u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
+            if (a.lse != nullptr) a.lse[row * a.lse_sb + hq] = nan;
+          } else {
+            for (int sl = 0; sl < S; ++sl) {
+              float* slot = a.ws + ((row * a.Hq + hq) * S + sl) * (kD + 1);
+              for (int d = 0; d <= kD; ++d) slot[d] = nan;
+            }
+          }
+        }
+      }
+    }
     next_unit(cw);
   }
 }
@@ -939,15 +1050,28 @@ template <int PS>
 hipError_t launch_gqa_class(const GqaArgs& a, bool verify, int n_wg, hipStream_t stream) {
   const dim3 grid(n_wg), block(kNW * 64);
   if (verify) {
-    if (a.kv_fp8)
-      hipLaunchKernelGGL((gqa_decode_kernel<PS, true, true>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((gqa_decode_kernel<PS, true, false>), grid, block, 0, stream, a);
+    // score column groups of 16 for the (verify token, head) pairs
+    const int cols = a.qlen * a.G;
+    if (a.kv_fp8) {
+      if (cols <= 16)
+        hipLaunchKernelGGL((gqa_decode_kernel<PS, true, true, 1>), grid, block, 0, stream, a);
+      else if (cols <= 32)
+        hipLaunchKernelGGL((gqa_decode_kernel<PS, true, true, 2>), grid, block, 0, stream, a);
+      else
+        hipLaunchKernelGGL((gqa_decode_kernel<PS, true, true, 4>), grid, block, 0, stream, a);
+    } else {
+      if (cols <= 16)
+        hipLaunchKernelGGL((gqa_decode_kernel<PS, true, false, 1>), grid, block, 0, stream, a);
+      else if (cols <= 32)
+        hipLaunchKernelGGL((gqa_decode_kernel<PS, true, false, 2>), grid, block, 0, stream, a);
+      else
+        hipLaunchKernelGGL((gqa_decode_kernel<PS, true, false, 4>), grid, block, 0, stream, a);
+    }
   } else {
     if (a.kv_fp8)
-      hipLaunchKernelGGL((gqa_decode_kernel<PS, false, true>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((gqa_decode_kernel<PS, false, true, 1>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((gqa_decode_kernel<PS, false, false>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((gqa_decode_kernel<PS, false, false, 1>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
 }

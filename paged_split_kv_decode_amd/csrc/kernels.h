@@ -28,7 +28,7 @@ struct GqaArgs {
   int32_t max_blocks;
   const int32_t* seq_lens;
   const int32_t* real_lens;  // nullptr: equal to seq_lens
-  int32_t qlen;              // verify tokens per request (the most, with cu_q); qlen * G <= 16
+  int32_t qlen;              // verify tokens per request (the most, with cu_q); qlen * G <= 64
   const int32_t* cu_q;       // nullptr: request b has rows b * qlen + t; else [B + 1]
                              // cumulative query lengths (rows cu_q[b] .. cu_q[b + 1] - 1)
   int32_t total_rows;        // rows of q / out / lse (B * qlen, or cu_q[B])

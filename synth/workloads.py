@@ -28,6 +28,8 @@ Recipe (one line per configuration, seeds: structure ``2000 + n``, values
 6. ``gqa_verify``  GQA causal verify: as 2 (sinks, L ~ U[1024, 8192]) with
    qlen = 2 verify tokens per request (q [B * 2, Hq, D]) and real length
    L - U{0, 1}.
+7. ``gqa_verify4`` as 6 with qlen = 4 (32 score columns per kv head) and
+   real length L - U{0, 3}.
 
 Never-attended cache slots (unreferenced pages, slots past L, slots before a
 window) can be NaN-poisoned so that any stray read shows up in the output.
@@ -59,6 +61,9 @@ CONFIGS = {
     "gqa_verify": dict(index=6, B=64, Hq=64, Hkv=8, D=128, P=16, len_range=(1024, 8192),
                        max_blocks=512, pool=40000, window=0, sinks=True, qlen=2,
                        real_drop=(0, 1)),
+    "gqa_verify4": dict(index=7, B=64, Hq=64, Hkv=8, D=128, P=16, len_range=(1024, 8192),
+                        max_blocks=512, pool=40000, window=0, sinks=True, qlen=4,
+                        real_drop=(0, 3)),
 }
 
 

@@ -182,7 +182,6 @@ def test_gqa_argument_checks_happen_before_any_hip_call():
     assert _gqa(P=1 << 17) == PD_ERR_UNSUPPORTED
     assert _gqa(P=(1 << 16) + 1) == PD_ERR_UNSUPPORTED
     assert _gqa(P=0) == PD_ERR_INVALID
-    assert _gqa(Hq=136, Hkv=8) == PD_ERR_UNSUPPORTED          # G = 17
     assert _gqa(q=FAKE + 8) == PD_ERR_ALIGN
     assert _gqa(kvsp=8 * 16 * 256 + 4) == PD_ERR_ALIGN
     assert _gqa(osh=132) == PD_ERR_ALIGN
@@ -218,7 +217,7 @@ def test_gqa_verify_varlen_argument_checks_happen_before_any_hip_call():
     assert _gqavl(cu=NULL) == PD_ERR_INVALID
     assert _gqavl(rows=-1) == PD_ERR_INVALID
     assert _gqavl(maxq=0) == PD_ERR_INVALID
-    assert _gqavl(maxq=3) == PD_ERR_UNSUPPORTED                # max_qlen * G = 24 > 16
+    assert _gqavl(maxq=9) == PD_ERR_UNSUPPORTED                # max_qlen * G = 72 > 64
     assert _gqavl(S=4) == PD_ERR_WORKSPACE
     need = lib.pd_workspace_bytes(3, 64, 4, 128)               # rows = total_rows
     assert _gqavl(S=4, ws=FAKE, wsb=need - 4) == PD_ERR_WORKSPACE
@@ -230,7 +229,8 @@ def test_gqa_verify_argument_checks_happen_before_any_hip_call():
     assert _gqav(qlen=0) == PD_ERR_INVALID
     assert _gqav(q=NULL) == PD_ERR_INVALID
     assert _gqav(scale=float("inf")) == PD_ERR_INVALID
-    assert _gqav(qlen=3) == PD_ERR_UNSUPPORTED                 # qlen * G = 24 > 16
+    assert _gqav(qlen=9) == PD_ERR_UNSUPPORTED                 # qlen * G = 72 > 64
+    assert _gqa(Hq=8 * 65, Hkv=8) == PD_ERR_UNSUPPORTED       # G = 65
     assert _gqav(qlen=4, Hq=32, D=64) == PD_ERR_UNSUPPORTED
     assert _gqav(osr=64 * 128 + 4) == PD_ERR_ALIGN
     assert _gqav(S=4) == PD_ERR_WORKSPACE
@@ -332,7 +332,7 @@ def _gqavp(**kw):
 def test_gqa_verify_partials_argument_checks_happen_before_any_hip_call():
     assert _gqavp(B=0, q=NULL, kv=NULL, bt=NULL, sl=NULL, ws=NULL, wsb=0) == PD_OK
     assert _gqavp(qlen=0) == PD_ERR_INVALID
-    assert _gqavp(qlen=3) == PD_ERR_UNSUPPORTED                # qlen * G = 24 > 16
+    assert _gqavp(qlen=9) == PD_ERR_UNSUPPORTED                # qlen * G = 72 > 64
     assert _gqavp(dt=1, per=2) == PD_ERR_INVALID
     # fixed qlen: rows = B * qlen, total_rows ignored
     assert _gqavp(wsb=4 * 64 * 129 * 4 - 4) == PD_ERR_WORKSPACE

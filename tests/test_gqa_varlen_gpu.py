@@ -65,6 +65,8 @@ CASES = [
     ([4, 1, 3, 0, 2], [90, 5, 2, 40, 400], 2, (32, 8), 37),
     ([16, 1, 7], [200, 3, 100], 0, (8, 8), 0),
     ([3, 3, 1, 2], [1, 64, 65, 500], 1, (20, 4), 5),
+    ([8, 2, 0, 5], [400, 9, 30, 120], 1, (64, 8), 0),
+    ([6, 13, 1], [77, 260, 3], 0, (16, 4), 50),
 ]
 
 
@@ -104,12 +106,14 @@ def test_uniform_query_lengths_match_verify_bitwise(pd, S):
     assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
 
 
+@pytest.mark.parametrize("heads", [(4, 4), (16, 4)], ids=["g1", "g4"])
 @pytest.mark.parametrize("S", [1, 2])
-def test_worked_varlen_example(pd, S):
+def test_worked_varlen_example(pd, S, heads):
     """Query lengths [10, 3, 1] over key lengths [0, 1, 7] with the verify
     rule: request 0 has no key (10 keyless rows), request 1's first two rows
-    have none, its last row sees key 0, request 2's row sees all 7."""
-    w = gqa_workload("gqa_verify", fixed_lens=[0, 1, 7], fixed_real=[0, 1, 7], heads=(4, 4),
+    have none, its last row sees key 0, request 2's row sees all 7.  With 4
+    query heads per kv head, request 0's 10 rows fill 40 score columns."""
+    w = gqa_workload("gqa_verify", fixed_lens=[0, 1, 7], fixed_real=[0, 1, 7], heads=heads,
                      qlen=10, pool="tight", seed_offset=3)
     vals = w.values("cuda", poison=True)
     cu = [0, 10, 13, 14]
@@ -125,9 +129,8 @@ def test_worked_varlen_example(pd, S):
 @pytest.mark.parametrize("seed", range(6))
 def test_random_query_lengths(pd, seed):
     rng = np.random.default_rng(700 + seed)
-    G = int(rng.choice([1, 2, 4, 8]))
-    max_q = 16 // G if G > 1 else int(rng.integers(1, 17))
-    max_q = min(max_q, 8)
+    G = int(rng.choice([1, 2, 4, 8, 16]))
+    max_q = min(64 // G, 12)
     B = int(rng.integers(1, 8))
     qlens = rng.integers(0, max_q + 1, size=B)
     lens = rng.integers(0, 500, size=B)
@@ -144,3 +147,23 @@ def test_random_query_lengths(pd, seed):
     out, lse = _run(pd, w, vals, q, cu, max(int(qlens.max()), 1), int(rng.choice([1, 3])))
     O, L = _oracle(w, vals, q, cu)
     check_attention(out, lse, O, L, what=f"seed={seed} qlens={list(qlens)} lens={list(lens)}")
+
+
+@pytest.mark.parametrize("S", [1, 3])
+def test_request_past_max_qlen_is_nan(pd, S):
+    """A request with more query rows than max_qlen breaks the call's
+    contract: all its rows are NaN (O and LSE), as for an invalid
+    block-table entry; every other request stays exact.  Covered for a
+    request with keys and for one with none."""
+    qlens, lens = [3, 1, 5, 2, 4], [200, 40, 300, 90, 0]
+    w = gqa_workload("gqa_verify", fixed_lens=lens, fixed_real=lens, heads=(32, 8), qlen=5,
+                     pool="tight", seed_offset=61)
+    vals = w.values("cuda", poison=True)
+    cu = _cu(qlens)
+    q = _q(int(cu[-1]), w.Hq, w.D, 62)
+    out, lse = _run(pd, w, vals, q, cu, 3, S)
+    O, L = _oracle(w, vals, q, cu)
+    over = list(range(int(cu[2]), int(cu[3]))) + list(range(int(cu[4]), int(cu[5])))
+    keep = [r for r in range(int(cu[-1])) if r not in over]
+    assert torch.all(torch.isnan(out[over].float())) and torch.all(torch.isnan(lse[over]))
+    check_attention(out[keep], lse[keep], O[keep], L[keep], what=f"past max_qlen S={S}")

@@ -2,8 +2,8 @@
 
 Every call goes through the C ABI (ctypes binding).  Inputs are seeded
 ``synth`` workloads with every never-attended cache slot NaN-poisoned.  The
-tests cover qlen x G up to the 16 columns of a score tile, windows, real
-lengths, both page sizes and split counts, rows with no key, bit-exact
+tests cover qlen x G up to 64 columns (one to four score tiles of 16),
+decode with up to 64 heads per kv head, windows, real lengths, both page sizes and split counts, rows with no key, bit-exact
 marker keys at each row's own causal limit and window start, bitwise
 agreement with paged_decode_gqa at qlen = 1, invariance to page placement,
 determinism, the NaN contract, and the full-size verify configuration on
@@ -43,8 +43,10 @@ def _run(pd, w, vals, S, kv=None, bt=None):
     return out, lse
 
 
-# (qlen, (Hq, Hkv)): qlen * G from 2 to 16
-SHAPES = [(2, (64, 8)), (4, (32, 8)), (8, (16, 8)), (16, (8, 8)), (3, (20, 4)), (1, (64, 8))]
+# (qlen, (Hq, Hkv)): qlen * G from 2 to 64 (1, 2 or 4 column groups of 16)
+SHAPES = [(2, (64, 8)), (4, (32, 8)), (8, (16, 8)), (16, (8, 8)), (3, (20, 4)), (1, (64, 8)),
+          (3, (64, 8)), (4, (64, 8)), (8, (64, 8)), (5, (48, 4)), (2, (64, 2)), (64, (8, 8)),
+          (7, (18, 2))]
 
 
 @pytest.mark.parametrize("qlen,heads", SHAPES, ids=[f"q{q}g{h[0] // h[1]}" for q, h in SHAPES])
@@ -60,10 +62,11 @@ def test_reduced_verify(pd, qlen, heads, S):
     check_attention(out, lse, O, L, what=f"qlen={qlen} heads={heads} S={S}")
 
 
+@pytest.mark.parametrize("qlen,heads", [(4, (32, 8)), (8, (64, 8))])
 @pytest.mark.parametrize("window", [1, 5, 100])
-@pytest.mark.parametrize("P", [16, 32])
-def test_verify_window_and_page_size(pd, window, P):
-    w = gqa_workload("gqa_verify", batch=5, len_range=(1, 700), qlen=4, heads=(32, 8),
+@pytest.mark.parametrize("P", [16, 32, 12])
+def test_verify_window_and_page_size(pd, window, P, qlen, heads):
+    w = gqa_workload("gqa_verify", batch=5, len_range=(1, 700), qlen=qlen, heads=heads,
                      real_drop=(0, 2), window=window, page_size=P, seed_offset=window)
     vals = w.values("cuda", poison=True)
     for S in (1, 4):
@@ -90,15 +93,17 @@ def test_rows_without_keys_are_exact(pd, S):
                 assert torch.all(torch.isneginf(lse[r])), (b, t)
 
 
+@pytest.mark.parametrize("heads", [(16, 4), (64, 4)], ids=["cols16", "cols64"])
 @pytest.mark.parametrize("order", ["last", "first"])
 @pytest.mark.parametrize("P", [16, 32])
-def test_marker_at_each_rows_limit_is_bit_exact(pd, order, P):
+def test_marker_at_each_rows_limit_is_bit_exact(pd, order, P, heads):
     """Key j scores 128 * m_j with m_j = j ("last") or 200 - j ("first"), so
     each row's result is exactly the V row of its largest attended key: its
     own last key hi_t - 1, or its first key lo_t (window start).  Keys past a
     row's limit are still attended by the later rows, so a causal-mask slip
     selects a different V row."""
-    D, qlen, Hq, Hkv, W = 128, 4, 16, 4, 37
+    D, qlen, W = 128, 4, 37
+    Hq, Hkv = heads
     lens = [70, 33, 95, 4]
     B = len(lens)
     rng = np.random.default_rng(11 + P)
@@ -209,3 +214,18 @@ def test_batch_beyond_cached_lengths(pd, qlen):
         out, lse = _run(pd, w, vals, S)
         O, L = oracle_gqa(w, vals)
         check_attention(out, lse, O, L, what=f"B=300 qlen={qlen} S={S}")
+
+
+@pytest.mark.parametrize("heads", [(256, 8), (128, 2), (96, 3)], ids=["g32", "g64", "g32b"])
+def test_decode_with_large_head_groups(pd, heads):
+    """paged_decode_gqa with more than 16 query heads per kv head (the
+    verify kernel's column groups at qlen = 1)."""
+    w = gqa_workload("gqa_sinks", batch=5, len_range=(1, 800), heads=heads, seed_offset=heads[0])
+    vals = w.values("cuda", poison=True)
+    bt, sl, _ = _dev(w)
+    for S in (1, 3):
+        out, lse = pd.paged_decode_gqa(vals["q"], vals["kv"], bt, sl, w.sm_scale,
+                                       sinks=vals["sinks"], num_kv_splits=S)
+        torch.cuda.synchronize()
+        O, L = oracle_gqa(w, vals)
+        check_attention(out, lse, O, L, what=f"decode heads={heads} S={S}")
