@@ -102,43 +102,48 @@ int32_t pd_split_rule(int32_t max_seq_len, int32_t batch, int32_t qlen, int32_t 
     num_cus = device_cus(-1);
     if (num_cus <= 0) return PD_ERR_HIP;
   }
-  const int64_t row_blocks = cdiv64((int64_t)qlen * num_heads, block_h);
-  const int64_t per_split = (int64_t)(batch > 1 ? batch : 1) * row_blocks;
-  const int64_t ideal =
-      cdiv64(max_seq_len > 1 ? max_seq_len : 1, min_work_per_split > 1 ? min_work_per_split : 1);
-  int64_t slots = (int64_t)((double)occupancy * (double)num_cus);
-  if (slots < 1) slots = 1;
-  int64_t n;
+  // 128-bit integers: the products below stay exact for any int32 sizes
+  typedef __int128 i128;
+  auto cdiv128 = [](i128 x, i128 y) { return (x + y - 1) / y; };
+  const i128 row_blocks = cdiv128((i128)qlen * num_heads, block_h);
+  const i128 per_split = (i128)(batch > 1 ? batch : 1) * row_blocks;
+  const i128 ideal =
+      cdiv128(max_seq_len > 1 ? max_seq_len : 1, min_work_per_split > 1 ? min_work_per_split : 1);
+  // resident programs; the float product is clamped before its conversion
+  const double slots_d = (double)occupancy * (double)num_cus;
+  const i128 slots = slots_d >= 4.0e18 ? (i128)4000000000000000000LL
+                                       : slots_d < 1.0 ? (i128)1 : (i128)(int64_t)slots_d;
+  i128 n;
   if (per_split <= slots) {
     n = slots / per_split;
   } else {
-    const int64_t top = ideal < max_splits ? ideal : max_splits;
-    const int64_t hi = top > 1 ? top : 1;
+    const i128 top = ideal < max_splits ? ideal : (i128)max_splits;
+    const int64_t hi = top > 1 ? (int64_t)top : 1;
     double best = 1e300;
     for (int64_t k = 1; k <= hi; ++k) {
-      const double cost = (double)cdiv64(k * per_split, slots) / (double)k;
+      const double cost = (double)cdiv128(k * per_split, slots) / (double)k;
       if (cost < best) best = cost;
     }
     n = hi;
     for (int64_t k = 1; k <= hi; ++k) {
-      const double cost = (double)cdiv64(k * per_split, slots) / (double)k;
+      const double cost = (double)cdiv128(k * per_split, slots) / (double)k;
       if (cost <= best * 1.05) {
         n = k;
         break;
       }
     }
   }
-  int64_t cap = n;
+  i128 cap = n;
   if (ideal < cap) cap = ideal;
-  if (2 * (int64_t)num_cus < cap) cap = 2 * (int64_t)num_cus;
+  if (2 * (i128)num_cus < cap) cap = 2 * (i128)num_cus;
   if (cap < 1) cap = 1;
   if (balance_chunk > 0) {
-    int64_t bal = cdiv64(max_seq_len > 1 ? max_seq_len : 1, balance_chunk);
+    i128 bal = cdiv128(max_seq_len > 1 ? max_seq_len : 1, balance_chunk);
     if (bal > max_splits) bal = max_splits;
     if (bal > ideal) bal = ideal;
     if (bal > cap) cap = bal;
   }
-  return (int32_t)cap;
+  return (int32_t)(cap < INT32_MAX ? cap : (i128)INT32_MAX);
 }
 
 int32_t pd_gqa_split_cap(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len,
@@ -183,7 +188,7 @@ int32_t num_kv_splits_cap(int32_t max_seq_len, int32_t batch, int32_t qlen,
 
 size_t pd_workspace_bytes(int32_t rows, int32_t num_heads, int32_t num_splits, int32_t head_dim_v) {
   if (rows <= 0 || num_heads <= 0 || num_splits <= 1 || head_dim_v <= 0) return 0;
-  return (size_t)rows * (size_t)num_heads * (size_t)num_splits * (size_t)(head_dim_v + 1) *
+  return (size_t)rows * (size_t)num_heads * (size_t)num_splits * ((size_t)head_dim_v + 1) *
          sizeof(float);
 }
 
@@ -530,7 +535,7 @@ int mla_common(const void* q, int64_t q_stride_row, int64_t q_stride_h, const vo
     const int64_t rows_req = (int64_t)qlen * num_heads;
     const int64_t keys = (int64_t)max_blocks * page_size;
     if (rows_req > INT32_MAX / 2 || keys > INT32_MAX / 2 ||
-        (int64_t)batch * cdiv64(rows_req, 128) * cdiv64(keys, 32) > INT32_MAX / 2)
+        (__int128)batch * cdiv64(rows_req, 128) * cdiv64(keys, 32) > INT32_MAX / 2)
       return PD_ERR_UNSUPPORTED;
   }
   if (num_kv_splits > 1 || partials_only) {

@@ -1,0 +1,18 @@
+// Launch records of the stand-in kernel launchers (stub_launch.cpp).
+#pragma once
+
+#include "../../paged_split_kv_decode_amd/csrc/kernels.h"
+
+namespace pd_stub {
+
+struct Record {
+  pd::GqaArgs gqa{};
+  pd::MlaArgs mla{};
+  pd::MergeArgs merge{};
+  pd::AppendArgs append{};
+  int n_gqa = 0, n_mla = 0, n_merge = 0, n_append = 0;
+};
+
+extern Record g_rec;
+
+}  // namespace pd_stub

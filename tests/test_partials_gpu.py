@@ -11,7 +11,8 @@ Each call goes through the C ABI.  The partials are checked two ways:
     bit for bit when S > 1 (the same kernel plan and the same merge), and
     match it to the parity tolerance when S = 1 (the full call then writes
     O directly, without the fp32 partial).
-Every slot's LSE is finite or -inf (unused slots), never NaN.
+Every workspace and output starts NaN-filled: every slot's LSE must end
+finite or -inf (unused slots), never NaN, and every used slot's O finite.
 """
 
 import numpy as np
@@ -41,14 +42,36 @@ def _sinks_np(vals):
     return None if vals["sinks"] is None else vals["sinks"].cpu().numpy().astype(np.float64)
 
 
+def _nan_ws(rows, H, S, Dv):
+    """A workspace that starts as NaN: a slot the plan fails to write stays NaN."""
+    return torch.full((rows * H * max(S, 1) * (Dv + 1),), float("nan"), dtype=torch.float32,
+                      device="cuda")
+
+
+def _nan_out(rows, H, Dv):
+    return (torch.full((rows, H, Dv), float("nan"), dtype=torch.bfloat16, device="cuda"),
+            torch.full((rows, H), float("nan"), dtype=torch.float32, device="cuda"))
+
+
+def _full_kw(rows, H, S, Dv):
+    """NaN-filled outputs (and workspace) for the full call."""
+    out, lse = _nan_out(rows, H, Dv)
+    kw = dict(out=out, lse=lse)
+    if S > 1:
+        kw["workspace"] = _nan_ws(rows, H, S, Dv)
+    return kw
+
+
 def _check_partials(pd, ws, S, Dv, sinks_t, O_ref, L_ref, full, o_atol, what):
     """ws: [rows, H, S, Dv + 1] partials; full: (out, lse) of the full call."""
     torch.cuda.synchronize()
     assert tuple(ws.shape[2:]) == (S, Dv + 1)
     wsn = ws.double().cpu().numpy()
     lse_p = wsn[..., Dv]
-    assert not np.isnan(lse_p).any(), f"{what}: NaN split LSE"
+    assert not np.isnan(lse_p).any(), f"{what}: NaN split LSE (a slot never written?)"
     assert np.all(np.isfinite(lse_p) | np.isneginf(lse_p)), f"{what}: +inf split LSE"
+    used = np.isfinite(lse_p)
+    assert np.all(np.isfinite(wsn[..., :Dv][used])), f"{what}: used slot with unwritten O"
     sinks = None if sinks_t is None else sinks_t.double().cpu().numpy()
     O_h, L_h = oracle.merge_partials(wsn[..., :Dv], lse_p, sinks)
     check_attention(torch.from_numpy(O_h), torch.from_numpy(L_h), O_ref.reshape(O_h.shape),
@@ -75,9 +98,11 @@ def test_decode_partials(pd, S, window):
     if S == "cap":
         S = pd.gqa_split_cap(w.B, w.Hkv, int(w.seq_lens.max()), w.window)
     ws = pd.paged_decode_gqa_partials(vals["q"], vals["kv"], bt, sl, w.sm_scale,
-                                      window=w.window, num_kv_splits=S)
+                                      window=w.window, num_kv_splits=S,
+                                      workspace=_nan_ws(w.rows, w.Hq, S, w.D))
     full = pd.paged_decode_gqa(vals["q"], vals["kv"], bt, sl, w.sm_scale, sinks=vals["sinks"],
-                               window=w.window, num_kv_splits=S)
+                               window=w.window, num_kv_splits=S,
+                               **_full_kw(w.rows, w.Hq, S, w.D))
     O, L = oracle_gqa(w, vals)
     _check_partials(pd, ws, S, w.D, vals["sinks"], O, L, full, 2e-2,
                     f"decode S={S} window={window}")
@@ -97,10 +122,10 @@ def test_verify_partials(pd, qlen, heads, S, fp8):
     scales = dict(k_scale=vals["k_scale"], v_scale=vals["v_scale"]) if fp8 else {}
     ws = pd.paged_verify_gqa_partials(vals["q"], vals["kv"], bt, sl, w.qlen, w.sm_scale,
                                       window=w.window, real_seq_lens=real, num_kv_splits=S,
-                                      **scales)
+                                      workspace=_nan_ws(w.rows, w.Hq, S, w.D), **scales)
     full = pd.paged_verify_gqa(vals["q"], vals["kv"], bt, sl, w.qlen, w.sm_scale,
                                sinks=vals["sinks"], window=w.window, real_seq_lens=real,
-                               num_kv_splits=S, **scales)
+                               num_kv_splits=S, **_full_kw(w.rows, w.Hq, S, w.D), **scales)
     O, L = oracle_gqa(w, vals)
     _check_partials(pd, ws, S, w.D, vals["sinks"], O, L, full, O_ATOL_FP8 if fp8 else 2e-2,
                     f"verify qlen={qlen} S={S} fp8={fp8}")
@@ -121,12 +146,13 @@ def test_varlen_partials(pd, S, fp8):
     bt, sl, real_d = _dev(w)
     cu_d = torch.from_numpy(cu).cuda()
     scales = dict(k_scale=vals["k_scale"], v_scale=vals["v_scale"]) if fp8 else {}
+    rows = int(cu[-1])
     ws = pd.paged_verify_gqa_partials(q, vals["kv"], bt, sl, max(qlens), w.sm_scale,
                                       real_seq_lens=real_d, cu_seqlens_q=cu_d, num_kv_splits=S,
-                                      **scales)
+                                      workspace=_nan_ws(rows, w.Hq, S, w.D), **scales)
     full = pd.paged_verify_gqa_varlen(q, vals["kv"], bt, sl, cu_d, max(qlens), w.sm_scale,
                                       sinks=vals["sinks"], real_seq_lens=real_d,
-                                      num_kv_splits=S, **scales)
+                                      num_kv_splits=S, **_full_kw(rows, w.Hq, S, w.D), **scales)
     kv = vals["kv"].cpu().numpy() if fp8 else vals["kv"].view(torch.int16).cpu().numpy().view(
         np.uint16)
     kw = {}
@@ -150,9 +176,11 @@ def test_mla_partials(pd, S, fp8):
     bt, sl, real = _dev(w)
     ks = torch.tensor([vals["k_scale"]], dtype=torch.float32, device="cuda") if fp8 else None
     ws = pd.paged_verify_mla_partials(vals["q"], vals["kv"], bt, sl, real, w.qlen, w.sm_scale,
-                                      head_dim_v=w.Lv, k_scale=ks, num_kv_splits=S)
+                                      head_dim_v=w.Lv, k_scale=ks, num_kv_splits=S,
+                                      workspace=_nan_ws(w.rows, w.H, S, w.Lv))
     full = pd.paged_verify_mla(vals["q"], vals["kv"], bt, sl, real, w.qlen, w.sm_scale,
-                               head_dim_v=w.Lv, k_scale=ks, num_kv_splits=S)
+                               head_dim_v=w.Lv, k_scale=ks, num_kv_splits=S,
+                               **_full_kw(w.rows, w.H, S, w.Lv))
     O, L = oracle_mla(w, vals, fp8=fp8)
     _check_partials(pd, ws, S, w.Lv, None, O, L, full, O_ATOL_FP8 if fp8 else 2e-2,
                     f"mla S={S} fp8={fp8}")
@@ -166,8 +194,9 @@ def test_mla_partials_reduced_config(pd):
     bt, sl, real = _dev(w)
     S = pd.mla_split_cap(w.B, w.qlen, w.H, int(w.seq_lens.max()))
     ws = pd.paged_verify_mla_partials(vals["q"], vals["kv"], bt, sl, real, w.qlen, w.sm_scale,
-                                      head_dim_v=w.Lv, num_kv_splits=S)
+                                      head_dim_v=w.Lv, num_kv_splits=S,
+                                      workspace=_nan_ws(w.rows, w.H, S, w.Lv))
     full = pd.paged_verify_mla(vals["q"], vals["kv"], bt, sl, real, w.qlen, w.sm_scale,
-                               head_dim_v=w.Lv, num_kv_splits=S)
+                               head_dim_v=w.Lv, num_kv_splits=S, **_full_kw(w.rows, w.H, S, w.Lv))
     O, L = oracle_mla(w, vals)
     _check_partials(pd, ws, S, w.Lv, None, O, L, full, 2e-2, f"mla cap S={S}")
