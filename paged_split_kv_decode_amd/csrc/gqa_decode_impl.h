@@ -53,15 +53,18 @@ namespace pd {
 namespace {
 
 constexpr int kD = 128;
-constexpr int kNW = 4;                                  // waves per workgroup
+// Waves per workgroup: 4 (one per SIMD, a 2-tile bf16 ring each), or 8 for
+// the FP8 cache (two per SIMD, so one wave's per-tile conversions and
+// products overlap the other's waits; a 2-tile FP8 ring and one query slot
+// each keep the 8 waves within the CU's LDS).
+__host__ __device__ constexpr int gqa_waves(bool f8, int nc) { return (f8 && nc == 1) ? 8 : 4; }
 constexpr int kRowBytes = 2 * kD * 2;                   // K|V row of one token (bf16)
 constexpr int kTileBytes = kTileTokens * kRowBytes;     // 16 KB
 constexpr int kRowBytes8 = 2 * kD;                      // K|V row of one token (FP8)
 constexpr int kTileBytes8 = kTileTokens * kRowBytes8;   // 8 KB
-// Ring of a wave, 32 KB either way: bf16, 2 tiles of 16 KB (one computed,
-// one loading); FP8, 4 tiles of 8 KB (one computed, up to three loading).
-constexpr int kRingBytes = 2 * kTileBytes;
-static_assert(4 * kTileBytes8 == kRingBytes, "FP8 ring of 4 tiles");
+// Ring of a wave: bf16, 2 tiles of 16 KB (one computed, one loading); FP8,
+// 4 tiles of 8 KB (one computed, up to three loading) with 4 waves per
+// workgroup, 2 tiles with 8.
 
 // FP8 tile: 16-byte chunk c of token row r (256 bytes) is stored at chunk
 // c ^ f8(r).  Rows 0..15 (and 16..31) get distinct values (K reads: 16 rows,
@@ -73,8 +76,11 @@ __device__ __forceinline__ int f8(int r) { return (r & 15) ^ ((r >> 4) << 2); }
 // inside it).
 __device__ __attribute__((aligned(1024))) uint32_t g_zero_rows[256];
 
-// Smallest share a wave takes: below it the per-wave start-up dominates.
-constexpr int kMinWaveTiles = 4;
+// Smallest share a wave takes, in tiles.  Short units (a sliding window of
+// 128 keys is 4-5 tiles) are latency-bound, and smaller shares let more
+// waves stream at once: 2 measured 6% faster than 4 at the window config
+// (11.9 against 12.7 us per call).
+constexpr int kMinWaveTiles = 2;
 // Share skew between XCDs, per mille of the mean share.  On MI355X the odd
 // XCDs stream the page pattern of a decode batch about 9% slower than the
 // even ones (per-wave timestamps, every box measured), so with equal shares
@@ -180,23 +186,23 @@ struct Share {
   int te, to;   // tiles per share of a wave on an even / an odd XCD
   bool last;
   bool split;   // S >= 2: pieces may cut units; S == 1: whole units only
-  // First tile of share j, the share of wave j = 4 b + i (lane-wave i of
+  int nw;       // waves per workgroup
+  // First tile of share j, the share of wave j = nw b + i (wave i of
   // workgroup b, which the dispatcher places on XCD b mod 8): each pair of
-  // workgroups covers 4 (te + to) tiles.
+  // workgroups covers nw (te + to) tiles.
   __device__ int start(int j) const {
-    const int b = j >> 2, i = j & 3;
-    return (b >> 1) * 4 * (te + to) + ((b & 1) ? 4 * te + i * to : i * te);
+    const int b = j / nw, i = j - (j / nw) * nw;
+    return (b >> 1) * nw * (te + to) + ((b & 1) ? nw * te + i * to : i * te);
   }
   // the share holding tile p (the inverse of start)
   __device__ int of(int p) const {
-    const int pair = p / (4 * (te + to));
-    const int rem = p - pair * 4 * (te + to);
-    return rem < 4 * te ? 8 * pair + rem / te : 8 * pair + 4 + (rem - 4 * te) / to;
+    const int pair = p / (nw * (te + to));
+    const int rem = p - pair * nw * (te + to);
+    return rem < nw * te ? 2 * nw * pair + rem / te : 2 * nw * pair + nw + (rem - nw * te) / to;
   }
 };
 
-constexpr int kQSlotBytes = 16 * kD * 2;                 // query rows of one piece (G <= 16)
-constexpr int kWaveLds = kRingBytes + 2 * kQSlotBytes;    // ring + 2 query slots = 40 KB
+constexpr int kQSlotBytes = 16 * kD * 2;                 // query rows of one piece (16 columns)
 constexpr int kCachedChunks = 4;                          // request lengths kept in registers (x64)
 
 // V: verify rows (qlen > 1 or real lengths); the decode instantiation has a
@@ -209,10 +215,16 @@ constexpr int kCachedChunks = 4;                          // request lengths kep
 // NC: score column groups of 16 (verify: qlen * G <= 16 NC columns; the
 // verify tokens of all groups share each K and V tile as loaded).
 template <int PS, bool V, bool F8, int NC>
-__global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
+__global__ __launch_bounds__(gqa_waves(F8, NC) * 64) void gqa_decode_kernel(GqaArgs a) {
   static_assert(NC == 1 || (V && (NC == 2 || NC == 4)), "column groups: decode 1, verify 1, 2 or 4");
   constexpr int kSlotBytes = F8 ? kTileBytes8 : kTileBytes;     // one tile as loaded
   constexpr int kLoadsPerTile = kSlotBytes / (64 * 16);         // 16 (bf16) or 8 (FP8) loads
+  constexpr int kNW = gqa_waves(F8, NC);
+  constexpr int kSlots = F8 ? (kNW == 8 ? 2 : 4) : 2;           // ring slots
+  constexpr int kQSlots = kNW == 8 ? 1 : 2;                      // query slots
+  constexpr int kRingBytes = kSlots * kSlotBytes;
+  constexpr int kWaveLds = kRingBytes + kQSlots * kQSlotBytes;   // 40 KB (4 waves), 20 KB (8)
+  static_assert(kNW * kWaveLds <= 160 * 1024, "LDS of one workgroup per CU");
   __shared__ __attribute__((aligned(1024))) char smem[kNW * kWaveLds];
 
   const int tid = threadIdx.x;
@@ -270,6 +282,7 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
   const int U = nt_sum * Hkv;
   Share sh;
   sh.split = S >= 2;
+  sh.nw = kNW;
   // a unit of n tiles cut every t tiles at an arbitrary offset spans at
   // most floor((n - 1) / t) + 2 shares: keep that <= S for the smaller share
   const int t_min = sh.split ? max((nt_max - 1) / (S - 1) + 1, kMinWaveTiles) : kMinWaveTiles;
@@ -478,7 +491,7 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
   // tile's loads, so they have landed when the tile has.
   int q_issued = 0, q_used = 0;   // pieces whose query rows were loaded / read
   auto load_q = [&](const Cursor& cu) {
-    const uint32_t dst = uniform((int)lds_addr(qslots + (q_issued & 1) * kQSlotBytes));
+    const uint32_t dst = uniform((int)lds_addr(qslots + (q_issued % kQSlots) * kQSlotBytes));
     const char* qbase =
         (const char*)(a.q + (int64_t)cu.r.row0 * a.q_sb + (int64_t)cu.kvh * G * a.q_sh);
     const int chunk = lane & 15;
@@ -697,7 +710,6 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
     pg_next = ci.b < a.B ? fetch_pages(ci) : pages_none;
     int issued = 1;               // tiles issued so far
     int slot_k = 0, slot_i = 1;   // ring slot of the computed tile, of the next issue
-    constexpr int kSlots = F8 ? 4 : 2;
     auto issue_next = [&]() {
       wait_lgkmcnt0();  // LDS reads of the slot's old tile and of an old query slot are done
       const bool bad_tile = issue(ci, pg_next, slot_i);
@@ -711,7 +723,8 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
     // needs one of the two query slots; a slot is free again once its
     // piece's first tile has read it into registers.
     auto fill_ring = [&](int k_now) {
-      while (ci.b < a.B && issued < k_now + kSlots && (!piece_start(ci) || q_issued - q_used < 2))
+      while (ci.b < a.B && issued < k_now + kSlots &&
+             (!piece_start(ci) || q_issued - q_used < kQSlots))
         issue_next();
     };
     if constexpr (F8) fill_ring(-1);
@@ -789,7 +802,7 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
       if (NC == 1 && first) {
         // the piece's query rows (loaded before its first tile): B operand
         // of S^T = K Q^T, zero for padding heads
-        PD_LDS const char* qs = qslots + (q_used & 1) * kQSlotBytes + l16 * (kD * 2);
+        PD_LDS const char* qs = qslots + (q_used % kQSlots) * kQSlotBytes + l16 * (kD * 2);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const bf16x8 v = *(PD_LDS const bf16x8*)(qs + (8 * g4 + 32 * s) * 2);
@@ -1048,13 +1061,13 @@ __global__ __launch_bounds__(kNW * 64) void gqa_decode_kernel(GqaArgs a) {
 // cache; one workgroup per compute unit.
 template <int PS>
 hipError_t launch_gqa_class(const GqaArgs& a, bool verify, int n_wg, hipStream_t stream) {
-  const dim3 grid(n_wg), block(kNW * 64);
+  const dim3 grid(n_wg), block(gqa_waves(false, 1) * 64), block8(gqa_waves(true, 1) * 64);
   if (verify) {
     // score column groups of 16 for the (verify token, head) pairs
     const int cols = a.qlen * a.G;
     if (a.kv_fp8) {
       if (cols <= 16)
-        hipLaunchKernelGGL((gqa_decode_kernel<PS, true, true, 1>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((gqa_decode_kernel<PS, true, true, 1>), grid, block8, 0, stream, a);
       else if (cols <= 32)
         hipLaunchKernelGGL((gqa_decode_kernel<PS, true, true, 2>), grid, block, 0, stream, a);
       else
@@ -1069,7 +1082,7 @@ hipError_t launch_gqa_class(const GqaArgs& a, bool verify, int n_wg, hipStream_t
     }
   } else {
     if (a.kv_fp8)
-      hipLaunchKernelGGL((gqa_decode_kernel<PS, false, true, 1>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((gqa_decode_kernel<PS, false, true, 1>), grid, block8, 0, stream, a);
     else
       hipLaunchKernelGGL((gqa_decode_kernel<PS, false, false, 1>), grid, block, 0, stream, a);
   }
