@@ -28,8 +28,10 @@ copies of a pool that holds only the pages in use (MLA).  The hot figures
 (one copy) are reported beside them.
 
 ``--config`` selects another workload: gqa_sinks, gqa_window, tiny_gqa,
-gqa_verify, gqa_verify4, gqa_verify_varlen, gqa_sinks_fp8, kv_append,
-mla_verify, mla_verify_fp8.
+gqa_verify, gqa_verify4, gqa_verify_varlen, gqa_sinks_fp8, gqa_sinks_append (the
+current token's K/V append fused into the decode call; the two-call sequence is
+timed beside it as ``us_per_call_unfused``), kv_append, mla_verify,
+mla_verify_fp8.
 """
 
 from __future__ import annotations
@@ -85,7 +87,8 @@ def _gqa_case(name, torch, pd, splits, page_size=0):
     from synth import gqa_workload
 
     fp8 = name.endswith("_fp8")
-    base = name[:-4] if fp8 else name
+    append = name.endswith("_append")
+    base = name[:-4] if fp8 else name[:-7] if append else name
     w = gqa_workload(base, page_size=page_size, pool="tight") if page_size else gqa_workload(base)
     pool = f"{w.num_pages}-page pool"
     vals = w.values("cuda", poison=False, fp8=fp8)
@@ -98,9 +101,29 @@ def _gqa_case(name, torch, pd, splits, page_size=0):
     ws = pd.alloc_workspace(w.rows, w.Hq, max(S, 2), w.D, "cuda")
     verify = w.qlen > 1 or w.real_seq_lens is not None or fp8
     ks, vs = vals.get("k_scale"), vals.get("v_scale")
+    if append:
+        g = torch.Generator(device="cuda").manual_seed(99)
+        k_new = torch.randn((w.B, w.Hkv, w.D), generator=g, device="cuda").to(torch.bfloat16)
+        v_new = torch.randn((w.B, w.Hkv, w.D), generator=g, device="cuda").to(torch.bfloat16)
 
     def calls(var):
         kv, tab = var["kv"], var["bt"]
+        if append:
+            # the fused call; the same work as two calls (append, then decode)
+            # is timed beside it
+            def step():
+                pd.paged_verify_gqa_append(vals["q"], kv, tab, sl, k_new, v_new, 1, w.sm_scale,
+                                           sinks=vals["sinks"], window=w.window,
+                                           num_kv_splits=S, workspace=ws, out=out, lse=lse)
+
+            def unfused():
+                pd.paged_kv_append(kv, tab, sl, k_new, v_new)
+                pd.paged_decode_gqa(vals["q"], kv, tab, sl, w.sm_scale, sinks=vals["sinks"],
+                                    window=w.window, num_kv_splits=S, workspace=ws, out=out,
+                                    lse=lse)
+
+            var["unfused"] = unfused
+            return step, step, None
         if verify:
             def step():
                 pd.paged_verify_gqa(vals["q"], kv, tab, sl, w.qlen, w.sm_scale,
@@ -128,7 +151,12 @@ def _gqa_case(name, torch, pd, splits, page_size=0):
 
         return (step, kernel, merge) if S > 1 else (step, step, None)
 
-    if fp8:
+    if append:
+        desc = ("GQA decode with sinks and the current token's K/V append fused in (one call "
+                f"writes each request's newest row and attends it): B=64, Hq=64, Hkv=8, D=128, "
+                f"page {w.P} HND bf16, seq_lens U[1024,8192], {pool}")
+        kind = "gqa"
+    elif fp8:
         desc = ("GQA decode with sinks on an FP8 E4M3FN cache (per-kv-head K and V scales): "
                 f"B=64, Hq=64, Hkv=8, D=128, page {w.P} HND, seq_lens U[1024,8192], {pool}")
         kind = "gqa_fp8"
@@ -568,6 +596,9 @@ def main():
         if R > 1:
             graph["kernel_hot"] = _graph_time(torch, kernels[:1], 0.1)
             graph["call_hot"] = _graph_time(torch, steps[:1], 0.1)
+        unfused = [v["unfused"] for v in case["variants"] if "unfused" in v]
+        if unfused:
+            graph["unfused"] = _graph_time(torch, unfused, 0.1)
 
     # the contract: W untimed warm-up steps, then K timed steps
     for i in range(args.warmup):
@@ -643,6 +674,8 @@ def main():
             cfg["merge_us"] = round(graph["merge"][0], 2)
         if "call_hot" in graph:
             cfg["us_per_call_hot"] = round(graph["call_hot"][0], 2)
+        if "unfused" in graph:
+            cfg["us_per_call_unfused"] = round(graph["unfused"][0], 2)
     line = {
         "metric": METRIC,
         "value": round(value, 2),

@@ -8,7 +8,8 @@
  *                      optional per-head sinks and a sliding window;
  *   paged_verify_gqa   the same with qlen causal verify tokens per request
  *                      (paged_verify_gqa_varlen: a query length per request);
- *   paged_kv_append    writes the newest tokens' K/V into the paged cache;
+ *   paged_kv_append    writes the newest tokens' K/V into the paged cache
+ *                      (paged_verify_gqa_append: fused with the GQA call);
  *   paged_verify_mla   qlen causal "verify" tokens per request over one shared
  *                      latent cache, V read as K[..., :Lv], bf16 or FP8 cache;
  *   *_partials         the split partials of a call, without the merge;
@@ -263,6 +264,49 @@ PD_API int paged_verify_gqa(const void* q, int64_t q_stride_row, int64_t q_strid
                      int32_t num_kv_splits, float* workspace, size_t workspace_bytes,
                      void* out, int64_t o_stride_row, int64_t o_stride_h,
                      float* lse, int64_t lse_stride_row, void* stream);
+
+/*
+ * paged_verify_gqa_append - paged_kv_append of the newest qlen tokens and
+ * paged_verify_gqa over the cache that holds them, in one launch.
+ *
+ * "vllm.models.flint.ops.decode_attention" (module description) notes that
+ * of all the pages a decode call reads, only the one holding the current
+ * token depends on the kernel before it, the one writing that token's K/V;
+ * "Atención paginada" (Ruta de decodificación) has the decode kernel update
+ * the paged cache in place through the block table.  Here the attention
+ * kernel does both: the rows of the newest qlen tokens of request b
+ * (positions seq_lens[b] - qlen + t, t = 0..qlen-1) are read from k_new /
+ * v_new, never from the cache, and the same launch writes them into the
+ * cache.  Results (out, lse and the cache bytes) are bit for bit those of
+ * paged_kv_append(k_new, v_new) followed by paged_verify_gqa on the same
+ * stream; qlen = 1 with real_seq_lens NULL is decode.
+ *
+ * k_new, v_new [B*qlen, Hkv, D] in the cache's element type (bf16, or FP8
+ *              E4M3FN codes already scaled like the cache), strides
+ *              (*_stride_row, *_stride_h, 1) in elements (multiples of 16
+ *              bytes, at most INT32_MAX, else PD_ERR_ALIGN / PD_ERR_UNSUPPORTED),
+ *              16-byte aligned; row b*qlen + t is token t of request b.
+ * kv           written: the new tokens' rows, as paged_kv_append writes
+ *              them (a token at a negative position, past the block-table
+ *              row or behind an entry outside [0, num_pages) is skipped).
+ * Other arguments, supported sizes and errors as for paged_verify_gqa.
+ * The new tokens' pages must not be read or written by another call in
+ * flight, nor shared with another request.
+ */
+PD_API int paged_verify_gqa_append(const void* q, int64_t q_stride_row, int64_t q_stride_h,
+                     void* kv, int32_t kv_dtype, const float* k_scale,
+                     const float* v_scale, int32_t scale_per_head,
+                     int64_t kv_stride_page, int64_t kv_stride_head,
+                     int32_t num_pages, const int32_t* block_table, int64_t bt_stride_b,
+                     int32_t max_blocks, const int32_t* seq_lens,
+                     const int32_t* real_seq_lens, int32_t qlen,
+                     const void* k_new, int64_t k_new_stride_row, int64_t k_new_stride_h,
+                     const void* v_new, int64_t v_new_stride_row, int64_t v_new_stride_h,
+                     const float* sinks, int32_t window, float sm_scale, int32_t batch,
+                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                     int32_t page_size, int32_t num_kv_splits, float* workspace,
+                     size_t workspace_bytes, void* out, int64_t o_stride_row,
+                     int64_t o_stride_h, float* lse, int64_t lse_stride_row, void* stream);
 
 /*
  * paged_verify_gqa_noalloc - paged_verify_gqa for callers that cannot

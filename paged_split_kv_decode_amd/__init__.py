@@ -18,6 +18,7 @@ from .api import (  # noqa: F401
     paged_decode_gqa_partials,
     paged_kv_append,
     paged_verify_gqa,
+    paged_verify_gqa_append,
     paged_verify_gqa_partials,
     paged_verify_gqa_varlen,
     paged_verify_mla,

@@ -32,6 +32,7 @@ EXPORTS = (
     "paged_verify_gqa",
     "paged_verify_gqa_varlen",
     "paged_verify_gqa_noalloc",
+    "paged_verify_gqa_append",
     "paged_decode_gqa_partials",
     "paged_verify_gqa_partials",
     "paged_kv_append",
@@ -95,6 +96,21 @@ def _load():
         _c_vp, _c_i64, _c_vp,                   # lse, stride, stream
     ]
     lib.paged_verify_gqa.restype = ctypes.c_int
+    lib.paged_verify_gqa_append.argtypes = [
+        _c_vp, _c_i64, _c_i64,                  # q, strides
+        _c_vp, _c_i32, _c_vp, _c_vp, _c_i32,    # kv, kv_dtype, k_scale, v_scale, per-head flag
+        _c_i64, _c_i64, _c_i32,                 # kv page/head strides, num_pages
+        _c_vp, _c_i64, _c_i32,                  # block_table, row stride, max_blocks
+        _c_vp, _c_vp, _c_i32,                   # seq_lens, real_seq_lens, qlen
+        _c_vp, _c_i64, _c_i64,                  # k_new, strides
+        _c_vp, _c_i64, _c_i64,                  # v_new, strides
+        _c_vp, _c_i32, _c_f32,                  # sinks, window, sm_scale
+        _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,  # B, Hq, Hkv, D, P
+        _c_i32, _c_vp, _c_sz,                   # splits, workspace, bytes
+        _c_vp, _c_i64, _c_i64,                  # out, strides
+        _c_vp, _c_i64, _c_vp,                   # lse, stride, stream
+    ]
+    lib.paged_verify_gqa_append.restype = ctypes.c_int
     lib.paged_verify_gqa_noalloc.argtypes = [
         _c_vp, _c_i64, _c_i64,                  # q, strides
         _c_vp, _c_i32, _c_vp, _c_vp, _c_i32,    # kv, kv_dtype, k_scale, v_scale, per-head flag

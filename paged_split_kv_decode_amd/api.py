@@ -163,6 +163,29 @@ def paged_verify_gqa(q, kv, block_table, seq_lens, qlen, sm_scale, sinks=None, w
                        return_lse, k_scale, v_scale)
 
 
+def paged_verify_gqa_append(q, kv, block_table, seq_lens, k_new, v_new, qlen, sm_scale,
+                            sinks=None, window=0, real_seq_lens=None, num_kv_splits=1,
+                            workspace=None, out=None, lse=None, stream=None, return_lse=True,
+                            k_scale=None, v_scale=None):
+    """The newest qlen tokens appended to the cache and attended in one call
+    (include/paged_decode.h: paged_verify_gqa_append): the result of
+    paged_kv_append(kv, block_table, seq_lens, k_new, v_new, qlen) followed
+    by paged_verify_gqa(...), bit for bit.
+
+    k_new, v_new [B*qlen, Hkv, D] of the cache's element type (bf16, or FP8
+    codes as uint8 / float8_e4m3fn), row b*qlen + t for token t of request
+    b.  kv is written in place.  Other arguments as for paged_verify_gqa.
+    Returns (out, lse).
+    """
+    qlen = int(qlen)
+    rows = q.shape[0] if q.dim() == 3 else -1
+    if qlen < 1 or rows % qlen != 0:
+        raise ValueError("q must have qlen rows per request")
+    return _verify_gqa(q, kv, block_table, seq_lens, rows // qlen, qlen, None, sm_scale, sinks,
+                       window, real_seq_lens, num_kv_splits, workspace, out, lse, stream,
+                       return_lse, k_scale, v_scale, new_kv=(k_new, v_new))
+
+
 def paged_verify_gqa_varlen(q, kv, block_table, seq_lens, cu_seqlens_q, max_qlen, sm_scale,
                             sinks=None, window=0, real_seq_lens=None, num_kv_splits=1,
                             workspace=None, out=None, lse=None, stream=None, return_lse=True,
@@ -217,7 +240,7 @@ def paged_verify_gqa_partials(q, kv, block_table, seq_lens, qlen, sm_scale, wind
 
 def _verify_gqa(q, kv, block_table, seq_lens, B, qlen, cu_seqlens_q, sm_scale, sinks, window,
                 real_seq_lens, num_kv_splits, workspace, out, lse, stream, return_lse, k_scale,
-                v_scale, partials_only=False):
+                v_scale, partials_only=False, new_kv=None):
     _need(q, "q", torch.bfloat16, 3)
     fp8 = kv.dtype in (torch.uint8, torch.float8_e4m3fn)
     if not fp8:
@@ -289,7 +312,17 @@ def _verify_gqa(q, kv, block_table, seq_lens, B, qlen, cu_seqlens_q, sm_scale, s
                  B, Hq, Hkv, D, P, S, _ptr(workspace), ws_bytes,
                  _ptr(out), out.stride(0), out.stride(1),
                  _ptr(lse), 0 if lse is None else lse.stride(0), _stream(stream))
-    if cu_seqlens_q is None:
+    if new_kv is not None:
+        srcs = []
+        for name, t in zip(("k_new", "v_new"), new_kv):
+            if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != kv.dtype or \
+                    t.dim() != 3 or tuple(t.shape) != (rows, Hkv, D) or t.stride(2) != 1:
+                raise ValueError(f"{name} must be a [B*qlen, Hkv, D] device tensor of the "
+                                 "cache's dtype with a contiguous last dim")
+            srcs += [_ptr(t), t.stride(0), t.stride(1)]
+        st = lib.paged_verify_gqa_append(*common, qlen, *srcs, *tail_args)
+        check("paged_verify_gqa_append", st)
+    elif cu_seqlens_q is None:
         st = lib.paged_verify_gqa(*common, qlen, *tail_args)
         check("paged_verify_gqa", st)
     else:

@@ -50,6 +50,8 @@ PER_SOURCE_FLAGS = {
     "gqa_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "gqa_decode_small_pages.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "gqa_decode_general_pages.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "gqa_append.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "gqa_append_small_pages.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 
 

@@ -194,6 +194,14 @@ size_t pd_workspace_bytes(int32_t rows, int32_t num_heads, int32_t num_splits, i
 
 namespace {
 
+// New tokens' K and V for the fused append (element strides).
+struct AppendSrc {
+  const void* k;
+  int64_t k_srow, k_sh;
+  const void* v;
+  int64_t v_srow, v_sh;
+};
+
 // GQA decode and verify.  Rows of q / out / lse are (request, verify token)
 // pairs, row b * qlen + t; decode is qlen = 1 with no real lengths.
 static int gqa_common(const void* q, int64_t q_stride_b, int64_t q_stride_h, const void* kv,
@@ -208,7 +216,7 @@ static int gqa_common(const void* q, int64_t q_stride_b, int64_t q_stride_h, con
                size_t workspace_bytes, void* out, int64_t o_stride_b, int64_t o_stride_h,
                float* lse, int64_t lse_stride_b, void* stream, bool partials_only,
                const int32_t* cu_seqlens_q = nullptr, int32_t total_rows = -1,
-               bool use_scratch = false) {
+               bool use_scratch = false, const AppendSrc* app = nullptr) {
   if (batch < 0 || qlen < 1 || num_q_heads < 1 || num_kv_heads < 1 || num_kv_splits < 1 ||
       num_pages < 0 || max_blocks < 0 || !std::isfinite(sm_scale) || !(sm_scale > 0.f))
     return PD_ERR_INVALID;
@@ -233,6 +241,19 @@ static int gqa_common(const void* q, int64_t q_stride_b, int64_t q_stride_h, con
       kv_stride_page % kv_align || kv_stride_head % kv_align)
     return PD_ERR_ALIGN;
   if (!partials_only && (!aligned16(out) || o_stride_b % 8 || o_stride_h % 8)) return PD_ERR_ALIGN;
+  if (app != nullptr) {
+    if (app->k == nullptr || app->v == nullptr || app->k_srow < 0 || app->k_sh < 0 ||
+        app->v_srow < 0 || app->v_sh < 0)
+      return PD_ERR_INVALID;
+    // 16-byte chunks of every source row
+    if (!aligned16(app->k) || !aligned16(app->v) || app->k_srow % kv_align ||
+        app->k_sh % kv_align || app->v_srow % kv_align || app->v_sh % kv_align)
+      return PD_ERR_ALIGN;
+    // byte offsets row * stride stay inside int64 for any row count
+    if (app->k_srow > INT32_MAX || app->k_sh > INT32_MAX || app->v_srow > INT32_MAX ||
+        app->v_sh > INT32_MAX)
+      return PD_ERR_UNSUPPORTED;
+  }
   if (cu_seqlens_q != nullptr && total_rows < 0) return PD_ERR_INVALID;
   const int64_t rows = cu_seqlens_q != nullptr ? (int64_t)total_rows : (int64_t)batch * qlen;
   if (rows > 0x7fffffff) return PD_ERR_UNSUPPORTED;
@@ -304,6 +325,15 @@ static int gqa_common(const void* q, int64_t q_stride_b, int64_t q_stride_h, con
   a.o_sh = (int32_t)o_stride_h;
   a.lse = lse;
   a.lse_sb = (int32_t)lse_stride_b;
+  if (app != nullptr) {
+    const int64_t eb = fp8 ? 1 : 2;   // bytes per element
+    a.kn = static_cast<const char*>(app->k);
+    a.vn = static_cast<const char*>(app->v);
+    a.kn_srow = app->k_srow * eb;
+    a.kn_sh = app->k_sh * eb;
+    a.vn_srow = app->v_srow * eb;
+    a.vn_sh = app->v_sh * eb;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (pd::launch_gqa_decode(a, s) != hipSuccess) return PD_ERR_HIP;
   if (num_kv_splits > 1 && !partials_only) {
@@ -359,6 +389,29 @@ int paged_verify_gqa(const void* q, int64_t q_stride_row, int64_t q_stride_h, co
                     window, sm_scale, batch, num_q_heads, num_kv_heads, head_dim, page_size,
                     num_kv_splits, workspace, workspace_bytes, out, o_stride_row, o_stride_h,
                     lse, lse_stride_row, stream, false);
+}
+
+int paged_verify_gqa_append(const void* q, int64_t q_stride_row, int64_t q_stride_h, void* kv,
+                            int32_t kv_dtype, const float* k_scale, const float* v_scale,
+                            int32_t scale_per_head, int64_t kv_stride_page,
+                            int64_t kv_stride_head, int32_t num_pages,
+                            const int32_t* block_table, int64_t bt_stride_b, int32_t max_blocks,
+                            const int32_t* seq_lens, const int32_t* real_seq_lens, int32_t qlen,
+                            const void* k_new, int64_t k_new_stride_row, int64_t k_new_stride_h,
+                            const void* v_new, int64_t v_new_stride_row, int64_t v_new_stride_h,
+                            const float* sinks, int32_t window, float sm_scale, int32_t batch,
+                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t page_size, int32_t num_kv_splits, float* workspace,
+                            size_t workspace_bytes, void* out, int64_t o_stride_row,
+                            int64_t o_stride_h, float* lse, int64_t lse_stride_row, void* stream) {
+  const AppendSrc app{k_new, k_new_stride_row, k_new_stride_h, v_new, v_new_stride_row,
+                      v_new_stride_h};
+  return gqa_common(q, q_stride_row, q_stride_h, kv, kv_dtype, k_scale, v_scale,
+                    scale_per_head, kv_stride_page, kv_stride_head, num_pages,
+                    block_table, bt_stride_b, max_blocks, seq_lens, real_seq_lens, qlen, sinks,
+                    window, sm_scale, batch, num_q_heads, num_kv_heads, head_dim, page_size,
+                    num_kv_splits, workspace, workspace_bytes, out, o_stride_row, o_stride_h,
+                    lse, lse_stride_row, stream, false, nullptr, -1, false, &app);
 }
 
 int paged_verify_gqa_noalloc(const void* q, int64_t q_stride_row, int64_t q_stride_h,

@@ -122,9 +122,20 @@ __device__ __forceinline__ const PD_CONST int32_t* as_const(const int32_t* p) {
 // the ordering instead: `wait_vmcnt<N>()` before reading a slot (vector
 // memory ops complete in order) and `wait_lgkmcnt0()` before refilling a
 // slot that was just read.  The `s_nop` covers the M0-write -> LDS-DMA hazard.
+// A wave-uniform 64-bit address that the asm takes in a scalar register
+// pair: read from the first lane, so a value the compiler happened to keep in
+// vector registers still fits the "s" operand (free when already scalar).
+__device__ __forceinline__ const void* scalar_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void global_to_lds_16(const void* base, uint32_t voff, uint32_t lds_addr) {
+  base = scalar_ptr(base);
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
@@ -141,6 +152,7 @@ __device__ __forceinline__ void global_to_lds_16(const void* base, uint32_t voff
 // about 7.1 TB/s against about 6.0 TB/s without it.
 template <uint32_t kOff>
 __device__ __forceinline__ void global_to_lds_16_stream(const void* base, uint32_t voff, uint32_t lds_base) {
+  base = scalar_ptr(base);
   asm volatile(
       "s_add_u32 m0, %0, %3\n\t"
       "s_nop 0\n\t"

@@ -5,6 +5,6 @@
 
 namespace pd {
 
-template hipError_t launch_gqa_class<0>(const GqaArgs&, bool, int, hipStream_t);
+template hipError_t launch_gqa_class<0, false>(const GqaArgs&, bool, int, hipStream_t);
 
 }  // namespace pd

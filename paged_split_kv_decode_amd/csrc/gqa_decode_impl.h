@@ -107,6 +107,7 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 struct Req {
   int lo, hi, nt;
   int n, row0;   // query rows of the request: n tokens from row row0
+  int L;         // seq_lens[b] as given (the fused append's tokens end there)
 };
 
 // Length bound standing for "no real length given".
@@ -130,6 +131,7 @@ __device__ __forceinline__ Req range_of(const GqaArgs& a, int L, int Lr, int n) 
   Req r;
   r.n = n;
   r.row0 = 0;
+  r.L = L;
   r.hi = n > 0 ? row_hi(a, L, Lr, n - 1, n) : 0;
   r.lo = row_lo(a, row_hi(a, L, Lr, 0, n));
   r.nt = r.hi > r.lo ? ((r.hi + 31) >> 5) - (r.lo >> 5) : 0;
@@ -214,7 +216,9 @@ constexpr int kCachedChunks = 4;                          // request lengths kep
 // and a load's 2 or 4 rows at most 2).
 // NC: score column groups of 16 (verify: qlen * G <= 16 NC columns; the
 // verify tokens of all groups share each K and V tile as loaded).
-template <int PS, bool V, bool F8, int NC>
+// AP: the fused append (the new tokens' rows come from the sources a.kn /
+// a.vn and are written into the cache).
+template <int PS, bool V, bool F8, int NC, bool AP>
 __global__ __launch_bounds__(gqa_waves(F8, NC) * 64) void gqa_decode_kernel(GqaArgs a) {
   static_assert(NC == 1 || (V && (NC == 2 || NC == 4)), "column groups: decode 1, verify 1, 2 or 4");
   constexpr int kSlotBytes = F8 ? kTileBytes8 : kTileBytes;     // one tile as loaded
@@ -532,6 +536,45 @@ __global__ __launch_bounds__(gqa_waves(F8, NC) * 64) void gqa_decode_kernel(GqaA
     auto chunk_of = [&](int r) {
       return F8 ? (uint32_t)((lane & 15) ^ f8(r)) : (uint32_t)((lane & 31) ^ swz(r));
     };
+    // Fused append: rows of the request's newest n tokens (positions
+    // L - n .. L - 1) are loaded from the new-token sources instead of the
+    // cache (written only at the end of the kernel).  Such a tile takes
+    // every load in the per-lane address form.
+    const int new_lo = cu.r.L - cu.r.n, new_hi = cu.r.L;
+    const bool has_new = AP && max(tok0, new_lo) < min(tok0 + kTileTokens, new_hi);
+    const char* kn_u = nullptr;
+    const char* vn_u = nullptr;
+    int64_t kn_srow = 0, vn_srow = 0;
+    if (has_new) {
+      kn_srow = a.kn_srow;
+      vn_srow = a.vn_srow;
+      kn_u = a.kn + (int64_t)cu.r.row0 * kn_srow + (int64_t)cu.kvh * a.kn_sh;
+      vn_u = a.vn + (int64_t)cu.r.row0 * vn_srow + (int64_t)cu.kvh * a.vn_sh;
+    }
+    // the source of this lane's chunk of row r of the tile (cache_src if
+    // the row is not a new token)
+    auto new_src = [&](int r, const char* cache_src) -> const char* {
+      constexpr uint32_t kHalf = F8 ? 8u : 16u;   // K chunks of a row
+      const int pos = tok0 + r;
+      const int t = pos - new_lo;
+      const uint32_t c = chunk_of(r);
+      const bool kp = c < kHalf;
+      const char* s = (kp ? kn_u : vn_u) + (int64_t)t * (kp ? kn_srow : vn_srow) +
+                      (kp ? c : c - kHalf) * 16u;
+      return pos >= new_lo && pos < new_hi ? s : cache_src;
+    };
+    // the tile's kLoadsPerTile loads, in the new-row form or not
+    auto for_loads = [&](auto one) {
+      if (has_new) {
+        [&]<int... I>(std::integer_sequence<int, I...>) {
+          (one(std::integral_constant<int, I>{}, std::true_type{}), ...);
+        }(std::make_integer_sequence<int, kLoadsPerTile>{});
+      } else {
+        [&]<int... I>(std::integer_sequence<int, I...>) {
+          (one(std::integral_constant<int, I>{}, std::false_type{}), ...);
+        }(std::make_integer_sequence<int, kLoadsPerTile>{});
+      }
+    };
     bool bad_page = false;
     if constexpr (kGen) {
       // Every row's source address is computed once per tile, row rho by
@@ -567,16 +610,15 @@ __global__ __launch_bounds__(gqa_waves(F8, NC) * 64) void gqa_decode_kernel(GqaA
         hi[i] = (uint32_t)__builtin_amdgcn_ds_bpermute(r << 2, rs_hi);
       }
       __builtin_amdgcn_sched_barrier(0);
-      auto one = [&](auto ic) {
+      auto one = [&](auto ic, auto nw) {
         constexpr int i = decltype(ic)::value;
         const int r = kRowsPerLoad * i + sub;
         const char* src =
             (const char*)(uintptr_t)(((uint64_t)hi[i] << 32) | lo[i]) + chunk_of(r) * 16;
+        if constexpr (decltype(nw)::value) src = new_src(r, src);
         global_to_lds_16_stream_v<i * 1024>(src, dst);
       };
-      [&]<int... I>(std::integer_sequence<int, I...>) {
-        (one(std::integral_constant<int, I>{}), ...);
-      }(std::make_integer_sequence<int, kLoadsPerTile>{});
+      for_loads(one);
     } else if constexpr (kLaneAddr) {
       // bit j: page j of the tile is attended
       const int pidx0 = tok0 >> p_shift;
@@ -584,7 +626,7 @@ __global__ __launch_bounds__(gqa_waves(F8, NC) * 64) void gqa_decode_kernel(GqaA
       const int j_hi = min(max(((cu.r.hi - 1) >> p_shift) + 1 - pidx0, 0), PPT);
       const uint64_t att_mask = ((1ull << j_hi) - 1) & ~((1ull << j_lo) - 1);
       bool bad_lane = false;
-      auto one = [&](auto ic) {
+      auto one = [&](auto ic, auto nw) {
         constexpr int i = decltype(ic)::value;
         const int r = kRowsPerLoad * i + sub;
         // the lane's row is in page j = r / PS of the tile: one of the
@@ -607,11 +649,10 @@ __global__ __launch_bounds__(gqa_waves(F8, NC) * 64) void gqa_decode_kernel(GqaA
         bad_lane |= att && !inr;
         const uint32_t off = (uint32_t)(r & (PS - 1)) * kRowB + chunk_of(r) * 16;
         const char* src = att && inr ? kv_head + id * sp_bytes + off : harmless;
+        if constexpr (decltype(nw)::value) src = new_src(r, src);
         global_to_lds_16_stream_v<i * 1024>(src, dst);
       };
-      [&]<int... I>(std::integer_sequence<int, I...>) {
-        (one(std::integral_constant<int, I>{}), ...);
-      }(std::make_integer_sequence<int, kLoadsPerTile>{});
+      for_loads(one);
       bad_page = __ballot(bad_lane) != 0;
     } else {
       bool ok[PPT];
@@ -626,17 +667,18 @@ __global__ __launch_bounds__(gqa_waves(F8, NC) * 64) void gqa_decode_kernel(GqaA
       // token slot of the tile's first row in its page (a big page holds the
       // whole tile; smaller pages start on tile boundaries)
       const uint32_t slot0 = kBig ? (uint32_t)(tok0 & ((1 << p_shift) - 1)) : 0u;
-      auto one = [&](auto ic) {
+      auto one = [&](auto ic, auto nw) {
         constexpr int i = decltype(ic)::value;
         const int r = kRowsPerLoad * i + sub;
         constexpr int j = kBig ? 0 : (kRowsPerLoad * i) / PS;   // every row of the load is in page j
         const uint32_t slot_tok = kBig ? slot0 + (uint32_t)r : (uint32_t)(r & (PS - 1));
         const uint32_t voff = ok[j] ? slot_tok * kRowB + chunk_of(r) * 16 : 0u;
-        global_to_lds_16_stream<i * 1024>(pbase[j], voff, dst);
+        if constexpr (decltype(nw)::value)
+          global_to_lds_16_stream_v<i * 1024>(new_src(r, pbase[j] + voff), dst);
+        else
+          global_to_lds_16_stream<i * 1024>(pbase[j], voff, dst);
       };
-      [&]<int... I>(std::integer_sequence<int, I...>) {
-        (one(std::integral_constant<int, I>{}), ...);
-      }(std::make_integer_sequence<int, kLoadsPerTile>{});
+      for_loads(one);
     }
     return bad_page;
   };
@@ -697,6 +739,26 @@ __global__ __launch_bounds__(gqa_waves(F8, NC) * 64) void gqa_decode_kernel(GqaA
         }
         if (g4 == 0) slot[kD] = piece_bad ? nan : lse_nat;
       }
+    }
+  };
+
+  // Fused append: row r of a landed tile (token position pos, a new token of
+  // the cursor's unit) to its cache row, skipping a position past the
+  // block-table row or behind an entry outside the pool.
+  auto store_new_row = [&](const Cursor& cu, PD_LDS const char* tl, int r, int pos) {
+    constexpr int kElem = F8 ? 1 : 2;
+    constexpr int kRowB = 2 * kD * kElem;
+    constexpr int kChunks = kRowB / 16;
+    const int pidx = kGen ? pos / a.P : pos >> p_shift;
+    if (pidx >= a.max_blocks) return;
+    const int page = as_const(a.bt)[(int64_t)cu.b * a.bt_sb + pidx];
+    if ((uint32_t)page >= (uint32_t)a.num_pages) return;
+    if (lane < kChunks) {
+      const u32x4 v = *(PD_LDS const u32x4*)(tl + r * kRowB + lane * 16);
+      const int c = F8 ? (lane ^ f8(r)) : (lane ^ swz(r));   // the chunk this position holds
+      char* row = const_cast<char*>((const char*)a.kv) + (int64_t)page * a.kv_sp * kElem +
+                  (int64_t)cu.kvh * a.kv_sh * kElem + (int64_t)(pos - pidx * a.P) * kRowB;
+      *(u32x4*)(row + c * 16) = v;
     }
   };
 
@@ -816,6 +878,15 @@ __global__ __launch_bounds__(gqa_waves(F8, NC) * 64) void gqa_decode_kernel(GqaA
 
       piece_bad |= (bad_slots >> slot_k) & 1;
       PD_LDS char* tl = ring + slot_k * kSlotBytes;   // tile k as loaded
+      if constexpr (AP) {
+        // Fused append: the new tokens' rows of this tile came from the
+        // sources; copy them from LDS into their cache rows.  (A store does
+        // not upset the ring's vmcnt bookkeeping: it can only delay a wait,
+        // since loads complete in order.)
+        const int t0 = ((cc.r.lo >> 5) + cc.i) * kTileTokens;
+        const int p_lo = max(cc.r.L - cc.r.n, t0), p_hi = min(cc.r.L, t0 + kTileTokens);
+        for (int pos = p_lo; pos < p_hi; ++pos) store_new_row(cc, tl, pos - t0, pos);
+      }
       // bf16: the V half of the tile, row stride 512 bytes, chunk 16 + c at
       // position (16 + c) ^ swz(r)
       PD_LDS char* vt = tl + 256;
@@ -988,6 +1059,43 @@ __global__ __launch_bounds__(gqa_waves(F8, NC) * 64) void gqa_decode_kernel(GqaA
   // Empty units owned by this share get O = 0 / LSE = -inf (or lse = -inf in
   // every split slot); a unit whose first tile is in this share gets
   // lse = -inf in the split slots no piece of it uses.
+  // Fused append: the unit's owner writes the new tokens' K and V that no
+  // tile of the unit covers (past its attended range) into the cache (a byte
+  // copy, skipping positions below 0, past the block-table row or behind an
+  // entry outside the pool).  The covered rows are written by the waves that
+  // stream their tiles.
+  auto append_rows = [&](const Cursor& cu) {
+    constexpr int kElem = F8 ? 1 : 2;
+    constexpr int kChunks = 2 * kD * kElem / 16;   // 16-byte chunks of a K|V row
+    constexpr int kHalf = kChunks / 2;
+    constexpr int kPer = 64 / kChunks;             // rows per pass of the wave
+    const int n = cu.r.n, L = cu.r.L;
+    // tiles of the unit cover positions [c_lo, c_hi); their rows were
+    // written by the waves that streamed them
+    const int c_lo = (cu.r.lo >> 5) * kTileTokens, c_hi = c_lo + cu.r.nt * kTileTokens;
+    const int ch = lane % kChunks;
+    const bool kp = ch < kHalf;
+    const int64_t srow = kp ? a.kn_srow : a.vn_srow;
+    const char* src0 = kp ? a.kn + (int64_t)cu.r.row0 * a.kn_srow + (int64_t)cu.kvh * a.kn_sh + ch * 16
+                          : a.vn + (int64_t)cu.r.row0 * a.vn_srow + (int64_t)cu.kvh * a.vn_sh +
+                                (ch - kHalf) * 16;
+    // the cache is written here only (the argument is const for the reads)
+    char* dst0 = const_cast<char*>((const char*)a.kv) + (int64_t)cu.kvh * a.kv_sh * kElem + ch * 16;
+    const int64_t sp_bytes = (int64_t)a.kv_sp * kElem;
+    const int32_t* bt_row = a.bt + (int64_t)cu.b * a.bt_sb;
+    for (int t0 = 0; t0 < n; t0 += kPer) {
+      const int t = t0 + lane / kChunks;
+      const int pos = L - n + t;
+      if (t >= n || pos < 0 || (pos >= c_lo && pos < c_hi)) continue;
+      const int pidx = pos / a.P;
+      if (pidx >= a.max_blocks) continue;
+      const int page = bt_row[pidx];
+      if ((uint32_t)page >= (uint32_t)a.num_pages) continue;
+      *(u32x4*)(dst0 + (int64_t)page * sp_bytes + (int64_t)(pos - pidx * a.P) * (2 * kD * kElem)) =
+          *(const u32x4*)(src0 + (int64_t)t * srow);
+    }
+  };
+
   Cursor cw;
   cw.b = b_s;
   cw.kvh = kvh_s;
@@ -1051,6 +1159,9 @@ __global__ __launch_bounds__(gqa_waves(F8, NC) * 64) void gqa_decode_kernel(GqaA
         }
       }
     }
+    // a unit is owned by the share holding its first tile (an empty unit, by
+    // the one share that visits it)
+    if (AP && (cw.r.nt == 0 || !sh.split || cw.p0 >= sh.g0)) append_rows(cw);
     next_unit(cw);
   }
 }
@@ -1058,8 +1169,8 @@ __global__ __launch_bounds__(gqa_waves(F8, NC) * 64) void gqa_decode_kernel(GqaA
 }  // namespace
 
 // Launches page class PS for a decode or verify call with a bf16 or FP8
-// cache; one workgroup per compute unit.
-template <int PS>
+// cache, with the fused append or not (AP); one workgroup per compute unit.
+template <int PS, bool AP>
 hipError_t launch_gqa_class(const GqaArgs& a, bool verify, int n_wg, hipStream_t stream) {
   const dim3 grid(n_wg), block(gqa_waves(false, 1) * 64), block8(gqa_waves(true, 1) * 64);
   if (verify) {
@@ -1067,24 +1178,24 @@ hipError_t launch_gqa_class(const GqaArgs& a, bool verify, int n_wg, hipStream_t
     const int cols = a.qlen * a.G;
     if (a.kv_fp8) {
       if (cols <= 16)
-        hipLaunchKernelGGL((gqa_decode_kernel<PS, true, true, 1>), grid, block8, 0, stream, a);
+        hipLaunchKernelGGL((gqa_decode_kernel<PS, true, true, 1, AP>), grid, block8, 0, stream, a);
       else if (cols <= 32)
-        hipLaunchKernelGGL((gqa_decode_kernel<PS, true, true, 2>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((gqa_decode_kernel<PS, true, true, 2, AP>), grid, block, 0, stream, a);
       else
-        hipLaunchKernelGGL((gqa_decode_kernel<PS, true, true, 4>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((gqa_decode_kernel<PS, true, true, 4, AP>), grid, block, 0, stream, a);
     } else {
       if (cols <= 16)
-        hipLaunchKernelGGL((gqa_decode_kernel<PS, true, false, 1>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((gqa_decode_kernel<PS, true, false, 1, AP>), grid, block, 0, stream, a);
       else if (cols <= 32)
-        hipLaunchKernelGGL((gqa_decode_kernel<PS, true, false, 2>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((gqa_decode_kernel<PS, true, false, 2, AP>), grid, block, 0, stream, a);
       else
-        hipLaunchKernelGGL((gqa_decode_kernel<PS, true, false, 4>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((gqa_decode_kernel<PS, true, false, 4, AP>), grid, block, 0, stream, a);
     }
   } else {
     if (a.kv_fp8)
-      hipLaunchKernelGGL((gqa_decode_kernel<PS, false, true, 1>), grid, block8, 0, stream, a);
+      hipLaunchKernelGGL((gqa_decode_kernel<PS, false, true, 1, AP>), grid, block8, 0, stream, a);
     else
-      hipLaunchKernelGGL((gqa_decode_kernel<PS, false, false, 1>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((gqa_decode_kernel<PS, false, false, 1, AP>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
 }

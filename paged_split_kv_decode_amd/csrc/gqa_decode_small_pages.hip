@@ -4,9 +4,9 @@
 
 namespace pd {
 
-template hipError_t launch_gqa_class<1>(const GqaArgs&, bool, int, hipStream_t);
-template hipError_t launch_gqa_class<2>(const GqaArgs&, bool, int, hipStream_t);
-template hipError_t launch_gqa_class<4>(const GqaArgs&, bool, int, hipStream_t);
-template hipError_t launch_gqa_class<8>(const GqaArgs&, bool, int, hipStream_t);
+template hipError_t launch_gqa_class<1, false>(const GqaArgs&, bool, int, hipStream_t);
+template hipError_t launch_gqa_class<2, false>(const GqaArgs&, bool, int, hipStream_t);
+template hipError_t launch_gqa_class<4, false>(const GqaArgs&, bool, int, hipStream_t);
+template hipError_t launch_gqa_class<8, false>(const GqaArgs&, bool, int, hipStream_t);
 
 }  // namespace pd

@@ -48,6 +48,14 @@ struct GqaArgs {
   int32_t o_sb, o_sh;
   float* lse;
   int32_t lse_sb;
+  // Fused append (kn == nullptr: none).  The n newest tokens of request b
+  // (positions seq_lens[b] - n .. seq_lens[b] - 1, n its query rows) are
+  // rows row0 .. row0 + n - 1 of these sources (byte strides): K of kv head
+  // h at kn + row * kn_srow + h * kn_sh, V likewise from vn.  The kernel
+  // attends them from the sources and writes them into the cache.
+  const char* kn;
+  const char* vn;
+  int64_t kn_srow, kn_sh, vn_srow, vn_sh;
 };
 
 struct MergeArgs {
@@ -105,9 +113,9 @@ struct AppendArgs {
 
 hipError_t launch_gqa_decode(const GqaArgs& a, hipStream_t stream);
 // One GQA page class (1, 2, 4, 8, 16, 32 for every power-of-two page of 32
-// tokens or more, or 0 for every other page size); the classes are
-// instantiated in their own translation units.
-template <int PS>
+// tokens or more, or 0 for every other page size), with the fused append
+// (AP) or not; the classes are instantiated in their own translation units.
+template <int PS, bool AP>
 hipError_t launch_gqa_class(const GqaArgs& a, bool verify, int n_wg, hipStream_t stream);
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);

@@ -81,6 +81,13 @@ struct Gqa {
                                      total_rows, window, scale, B, Hq, Hkv, D, P, S, ws, wsb,
                                      nullptr);
   }
+  int append(const void* kn, int64_t kn_sr, int64_t kn_sh, const void* vn, int64_t vn_sr,
+             int64_t vn_sh) const {
+    return paged_verify_gqa_append(q, q_sr, q_sh, const_cast<void*>(kv), dtype, ks, vs, per_head,
+                                   kv_sp, kv_sh, num_pages, bt, bt_sb, max_blocks, sl, real, qlen,
+                                   kn, kn_sr, kn_sh, vn, vn_sr, vn_sh, sinks, window, scale, B, Hq,
+                                   Hkv, D, P, S, ws, wsb, out, o_sr, o_sh, lse, lse_sr, nullptr);
+  }
   int noalloc() const {
     return paged_verify_gqa_noalloc(q, q_sr, q_sh, kv, dtype, ks, vs, per_head, kv_sp, kv_sh,
                                     num_pages, bt, bt_sb, max_blocks, sl, real, qlen, sinks,
@@ -279,6 +286,19 @@ void check_gqa() {
   na.S = 2;
   const int st = na.noalloc();
   EXPECT(st == PD_OK || st == PD_ERR_HIP);
+
+  // fused append: the sources reach the launch as byte addresses and strides
+  const char* kn = static_cast<const char*>(kFake);
+  int n_app = r.n_gqa;
+  EXPECT(g.append(kn, 8 * 128, 128, kn + 4096, 8 * 128, 128) == PD_OK && r.n_gqa == n_app + 1);
+  EXPECT(r.gqa.kn == kn && r.gqa.vn == kn + 4096 && r.gqa.kn_srow == 8 * 128 * 2 &&
+         r.gqa.kn_sh == 128 * 2 && r.gqa.vn_srow == 8 * 128 * 2 && r.gqa.vn_sh == 128 * 2);
+  EXPECT(g.append(nullptr, 8 * 128, 128, kn, 8 * 128, 128) == PD_ERR_INVALID);
+  EXPECT(g.append(kn + 8, 8 * 128, 128, kn, 8 * 128, 128) == PD_ERR_ALIGN);
+  EXPECT(g.append(kn, (int64_t)INT32_MAX - 7, 128, kn, 8 * 128, 128) == PD_OK);
+  EXPECT(g.append(kn, (int64_t)INT32_MAX + 1, 128, kn, 8 * 128, 128) == PD_ERR_UNSUPPORTED);
+  // the plain calls launch with no append source
+  EXPECT(g.verify() == PD_OK && r.gqa.kn == nullptr);
 }
 
 void check_mla() {

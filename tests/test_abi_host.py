@@ -384,3 +384,29 @@ def test_noalloc_checks_happen_before_the_scratch_lookup():
     # partials of 128 rows x 64 heads x 16 splits x 129 fp32 exceed the 64 MiB scratch
     assert _noalloc(B=64, S=16) == PD_ERR_WORKSPACE
     assert _noalloc(B=64 * 16, S=2, maxb=1) == PD_ERR_WORKSPACE
+
+
+def _gqaa(**kw):
+    a = dict(q=FAKE, qsr=64 * 128, qsh=128, kv=FAKE, dt=0, ks=NULL, vs=NULL, per=0,
+             kvsp=8 * 16 * 256, kvsh=16 * 256,
+             npages=10, bt=FAKE, btsb=4, maxb=4, sl=FAKE, real=NULL, qlen=2,
+             kn=FAKE, knr=8 * 128, knh=128, vn=FAKE + 4096, vnr=8 * 128, vnh=128,
+             sinks=NULL, window=0, scale=0.088, B=2, Hq=64, Hkv=8, D=128, P=16, S=1, ws=NULL,
+             wsb=0, out=FAKE, osr=64 * 128, osh=128, lse=NULL, lser=64, stream=NULL)
+    a.update(kw)
+    return lib.paged_verify_gqa_append(*a.values())
+
+
+def test_fused_append_argument_checks_happen_before_any_hip_call():
+    assert _gqaa(B=0, q=NULL, kv=NULL, bt=NULL, sl=NULL, out=NULL, kn=NULL, vn=NULL) == PD_OK
+    assert _gqaa(kn=NULL) == PD_ERR_INVALID
+    assert _gqaa(vn=NULL) == PD_ERR_INVALID
+    assert _gqaa(knr=-128) == PD_ERR_INVALID
+    assert _gqaa(kn=FAKE + 8) == PD_ERR_ALIGN                 # rows in 16-byte chunks
+    assert _gqaa(vnh=128 + 4) == PD_ERR_ALIGN
+    assert _gqaa(dt=1, knr=8 * 128 + 8) == PD_ERR_ALIGN       # FP8: strides of 16 codes
+    assert _gqaa(qlen=9) == PD_ERR_UNSUPPORTED                 # qlen * G = 72 > 64, as verify
+    assert _gqaa(knr=1 << 31) == PD_ERR_UNSUPPORTED
+    assert _gqaa(S=4) == PD_ERR_WORKSPACE
+    need = lib.pd_workspace_bytes(2 * 2, 64, 4, 128)
+    assert _gqaa(S=4, ws=FAKE + 4, wsb=need) == PD_ERR_ALIGN
