@@ -10,13 +10,13 @@
 // * Work unit = (request b, kv head); its keys are cut into 32-token tiles
 //   (tile t covers positions [32t, 32t + 32), clipped to the request's key
 //   range).  All units' tiles, request-major then kv-head-major, form one
-//   flat sequence of U tiles.  The grid is one 4-wave workgroup per compute
-//   unit, and every wave takes a contiguous share of that sequence, equal
-//   up to a fixed skew between even and odd XCDs (which stream at different
-//   rates), so the waves finish together whatever the length mix.
+//   flat sequence of U tiles.  The grid is one workgroup per compute unit
+//   (4 waves; 8 for FP8 decode), and every wave takes an equal contiguous
+//   share of that sequence, so the waves finish together whatever the
+//   length mix.
 // * A wave streams its share as one pipeline that runs straight across unit
 //   boundaries: it has a private ring in LDS (bf16: 2 slots of 16 KB; FP8:
-//   4 slots of 8 KB, up to three tiles in flight) and issues the next tiles
+//   2 or 4 slots of 8 KB) and issues the next tiles
 //   (`global_load_lds_dwordx4`, 1 KB each, HBM -> LDS with no VGPR staging,
 //   non-temporal: the cache is read once) while it computes tile k.  The physical page of
 //   each tile row comes from the block table through scalar loads made one
@@ -81,15 +81,11 @@ __device__ __attribute__((aligned(1024))) uint32_t g_zero_rows[256];
 // waves stream at once: 2 measured 6% faster than 4 at the window config
 // (11.9 against 12.7 us per call).
 constexpr int kMinWaveTiles = 2;
-// Share skew between XCDs, per mille of the mean share.  On MI355X the odd
-// XCDs stream the page pattern of a decode batch about 9% slower than the
-// even ones (per-wave timestamps, every box measured), so with equal shares
-// the kernel ends with them.  Waves on even XCDs take 8% more tiles, waves
-// on odd XCDs 8% fewer: 1.5-3.8% less time per bf16 call at page sizes of 4
-// and more.  Where the per-tile compute, not HBM, sets the pace (the FP8
-// cache, pages of 1 or 2 tokens) the skew only idles the odd XCDs early, so
-// there it is 0.
-constexpr int kXcdSkewPerMille = 80;
+// Every wave takes an equal share.  (Shares skewed by a fixed amount
+// between even and odd XCDs, which had streamed at different rates, lost
+// against equal shares with this kernel: at 2, 3, 4, 6, 8, 10 and 12% on the
+// skewed decode batch, at 2 and 8% on the sinks, verify and 8-token-page
+// decode workloads; 1.4-2.2% at 8%.)
 
 // 16-byte chunk c of token row r is stored at chunk c ^ swz(r).  Rows
 // 0..7 get distinct low-3-bit patterns (K reads: 8 consecutive rows, same
@@ -185,23 +181,12 @@ struct Cursor {
 // The wave's share of the flat tile sequence.
 struct Share {
   int g0, g1;   // [g0, g1): raw share (the last used wave also owns every unit past g1)
-  int te, to;   // tiles per share of a wave on an even / an odd XCD
+  int t;        // tiles per share
   bool last;
   bool split;   // S >= 2: pieces may cut units; S == 1: whole units only
-  int nw;       // waves per workgroup
-  // First tile of share j, the share of wave j = nw b + i (wave i of
-  // workgroup b, which the dispatcher places on XCD b mod 8): each pair of
-  // workgroups covers nw (te + to) tiles.
-  __device__ int start(int j) const {
-    const int b = j / nw, i = j - (j / nw) * nw;
-    return (b >> 1) * nw * (te + to) + ((b & 1) ? nw * te + i * to : i * te);
-  }
-  // the share holding tile p (the inverse of start)
-  __device__ int of(int p) const {
-    const int pair = p / (nw * (te + to));
-    const int rem = p - pair * nw * (te + to);
-    return rem < nw * te ? 2 * nw * pair + rem / te : 2 * nw * pair + nw + (rem - nw * te) / to;
-  }
+  // first tile of the share of wave j, and the share holding tile p
+  __device__ int start(int j) const { return j * t; }
+  __device__ int of(int p) const { return p / t; }
 };
 
 constexpr int kQSlotBytes = 16 * kD * 2;                 // query rows of one piece (16 columns)
@@ -286,18 +271,10 @@ __global__ __launch_bounds__(gqa_waves(F8, NC) * 64) void gqa_decode_kernel(GqaA
   const int U = nt_sum * Hkv;
   Share sh;
   sh.split = S >= 2;
-  sh.nw = kNW;
   // a unit of n tiles cut every t tiles at an arbitrary offset spans at
-  // most floor((n - 1) / t) + 2 shares: keep that <= S for the smaller share
+  // most floor((n - 1) / t) + 2 shares: keep that <= S
   const int t_min = sh.split ? max((nt_max - 1) / (S - 1) + 1, kMinWaveTiles) : kMinWaveTiles;
-  const int tpw = uniform(max((U + n_waves - 1) / n_waves, t_min));   // mean share
-  // the skew needs the round-robin placement of workgroups on the 8 XCDs of
-  // the whole chip (one workgroup per CU: 256); a partitioned device places
-  // them otherwise and gets equal shares
-  constexpr int kSkew = (F8 || (PS != 0 && PS < 4)) ? 0 : kXcdSkewPerMille;
-  const int dx = uniform(gridDim.x == 256 ? min(tpw * kSkew / 1000, tpw - t_min) : 0);
-  sh.te = tpw + dx;
-  sh.to = tpw - dx;
+  sh.t = uniform(max((U + n_waves - 1) / n_waves, t_min));
   const int w_used = uniform(U > 0 ? sh.of(U - 1) + 1 : 1);
   if (w >= w_used) return;
   sh.g0 = sh.start(w);
