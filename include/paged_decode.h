@@ -546,6 +546,12 @@ PD_API int paged_verify_mla_partials(const void* q, int64_t q_stride_row, int64_
  * splits, per-split weights, weighted l and O, sink in the final
  * denominator) restated for normalised partials and natural logs.  A split
  * whose lse_s is -inf is skipped, so its O_s may hold anything (even NaN).
+ * An lse_s of +inf ends the (row, head)'s list: the sums above run over the
+ * slots before it, and nothing after it is read.  (The library's decode and
+ * verify calls that merge themselves end each list that way, one store in
+ * place of an lse = -inf in every slot no split uses; the *_partials entry
+ * points still write -inf into every unused slot.)  A NaN lse_s makes the
+ * (row, head) NaN.
  *
  * workspace  fp32 [rows, num_heads, num_splits, head_dim_v + 1], contiguous.
  * sinks      [num_heads] fp32 or NULL.

@@ -22,6 +22,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+// lse = +inf ends a split-slot list (the slots after it are not read)
+__device__ __forceinline__ float end_of_slots() { return __builtin_inff(); }
 
 // 2^x on the hardware transcendental unit (v_exp_f32); exp2(-inf) = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

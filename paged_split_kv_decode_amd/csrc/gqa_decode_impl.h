@@ -1033,9 +1033,12 @@ __global__ __launch_bounds__(gqa_waves(F8, NC) * 64) void gqa_decode_kernel(GqaA
   }
 
   // ---- units this wave answers for without streaming them ---------------
-  // Empty units owned by this share get O = 0 / LSE = -inf (or lse = -inf in
-  // every split slot); a unit whose first tile is in this share gets
-  // lse = -inf in the split slots no piece of it uses.
+  // Empty units owned by this share get O = 0 / LSE = -inf; a unit whose
+  // first tile is in this share gets its slot list ended after the slots its
+  // pieces use.  Partials only: every slot no piece uses gets lse = -inf,
+  // as the partials entries promise; a call that merges itself writes just
+  // lse = +inf into the first unused slot (the merge reads no further), one
+  // store per column instead of one per unused slot.
   // Fused append: the unit's owner writes the new tokens' K and V that no
   // tile of the unit covers (past its attended range) into the cache (a byte
   // copy, skipping positions below 0, past the block-table row or behind an
@@ -1093,17 +1096,23 @@ __global__ __launch_bounds__(gqa_waves(F8, NC) * 64) void gqa_decode_kernel(GqaA
           *(u32x4*)(a.out + col_row(n) * a.o_sb + (int64_t)col_head(n) * a.o_sh + d8) = u32x4{0, 0, 0, 0};
         }
         if (a.lse != nullptr && lane < R) a.lse[col_row(lane) * a.lse_sb + col_head(lane)] = neg_inf();
-      } else {
+      } else if (a.partials) {
         for (int i = lane; i < R * S; i += 64) {
           const int n = i / S, s = i % S;
           a.ws[((col_row(n) * a.Hq + col_head(n)) * S + s) * (kD + 1) + kD] = neg_inf();
         }
+      } else if (lane < R) {
+        a.ws[((col_row(lane) * a.Hq + col_head(lane)) * S) * (kD + 1) + kD] = end_of_slots();
       }
     } else if (sh.split && cw.p0 >= sh.g0) {
       const int nseg = sh.of(cw.p0 + cw.r.nt - 1) - sh.of(cw.p0) + 1;
-      for (int i = lane; i < R * (S - nseg); i += 64) {
-        const int n = i / (S - nseg), s = nseg + i % (S - nseg);
-        a.ws[((col_row(n) * a.Hq + col_head(n)) * S + s) * (kD + 1) + kD] = neg_inf();
+      if (a.partials) {
+        for (int i = lane; i < R * (S - nseg); i += 64) {
+          const int n = i / (S - nseg), s = nseg + i % (S - nseg);
+          a.ws[((col_row(n) * a.Hq + col_head(n)) * S + s) * (kD + 1) + kD] = neg_inf();
+        }
+      } else if (nseg < S && lane < R) {
+        a.ws[((col_row(lane) * a.Hq + col_head(lane)) * S + nseg) * (kD + 1) + kD] = end_of_slots();
       }
     }
     if constexpr (V) {

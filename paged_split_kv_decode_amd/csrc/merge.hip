@@ -7,13 +7,17 @@
 // "vllm.v1.attention.ops.triton_decode_attention" (attn_logits:
 // [rows, H, S, Lv + 1]).
 //
-// One wave per (row, head).  Lane s reads lse_s (S <= 64 per pass) to form
-// the wave max M and the weights w_s = 2^((lse_s - M) log2 e); the splits
-// with lse_s > -inf are then gathered in batches of four, every load of a
-// batch issued before any is used, each lane accumulating the Lv / 64
-// contiguous output dims it owns.  A split with lse_s = -inf is never read
-// or multiplied, so its O_s may hold anything.  A NaN lse_s (a partial that
-// saw an invalid block-table entry) makes the result NaN.
+// One wave per (row, head).  The slot list is slots 0 .. n - 1, n the first
+// slot whose lse is +inf (S if none): the library's own calls end a list
+// that way instead of marking every slot past it, and nothing after the end
+// is read.  The first 8 slots' lse are read first (most lists end there);
+// lane s then holds lse_s (64 slots per pass) to form the wave max M and the
+// weights w_s = 2^((lse_s - M) log2 e); the splits with lse_s > -inf are
+// gathered in batches of four, every load of a batch issued before any is
+// used, each lane accumulating the Lv / 64 contiguous output dims it owns.
+// A split with lse_s = -inf is never read or multiplied, so its O_s may hold
+// anything.  A NaN lse_s (a partial that saw an invalid block-table entry)
+// makes the result NaN.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -33,11 +37,36 @@ __global__ __launch_bounds__(kWaves * 64) void merge_kernel(MergeArgs a) {
   const int S = a.S;
   const int stride = a.Dv + 1;
   const float* base = a.ws + pair * (int64_t)S * stride;
+  auto lse_at = [&](int s) { return base[(int64_t)s * stride + a.Dv]; };
+
+  // the end of the list: the first 8 slots, then 64 at a time
+  int n = S;
+  const int c8 = S < 8 ? S : 8;
+  const float l8 = lane < c8 ? lse_at(lane) : neg_inf();
+  uint64_t end = __ballot(lane < c8 && l8 == end_of_slots());
+  if (end != 0ull) {
+    n = __builtin_ctzll(end);
+  } else {
+    for (int s0 = c8; s0 < S; s0 += 64) {
+      const bool in = s0 + lane < S;
+      const float l = in ? lse_at(s0 + lane) : neg_inf();
+      end = __ballot(in && l == end_of_slots());
+      if (end != 0ull) {
+        n = s0 + __builtin_ctzll(end);
+        break;
+      }
+    }
+  }
+  // lane s's lse in the pass from s0 (slots >= n read as -inf)
+  auto lse_pass = [&](int s0) {
+    const int s = s0 + lane;
+    return s >= n ? neg_inf() : (s < 8 ? l8 : lse_at(s));
+  };
 
   float M = neg_inf();
   bool nan_seen = false;
-  for (int s0 = 0; s0 < S; s0 += 64) {
-    const float l = s0 + lane < S ? base[(int64_t)(s0 + lane) * stride + a.Dv] : neg_inf();
+  for (int s0 = 0; s0 < n; s0 += 64) {
+    const float l = lse_pass(s0);
     nan_seen |= l != l;
     M = fmaxf(M, l);
   }
@@ -52,21 +81,21 @@ __global__ __launch_bounds__(kWaves * 64) void merge_kernel(MergeArgs a) {
   const bool empty = M == neg_inf();
   if (!empty && !nan_seen) {
     const float Ml = M * kLog2e;
-    for (int s0 = 0; s0 < S; s0 += 64) {
+    for (int s0 = 0; s0 < n; s0 += 64) {
       // this pass's splits: lane s holds w_{s0 + s}; the used ones as a bit mask
-      const float l = s0 + lane < S ? base[(int64_t)(s0 + lane) * stride + a.Dv] : neg_inf();
+      const float l = lse_pass(s0);
       const float w = l == neg_inf() ? 0.f : fast_exp2(l * kLog2e - Ml);
       uint64_t used = __ballot(l != neg_inf());
       while (used != 0ull) {
         // up to four used splits: all loads first, then the sums
         int idx[4];
-        int n = 0;
+        int nb = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           idx[j] = used != 0ull ? __builtin_ctzll(used) : -1;
           if (used != 0ull) {
             used &= used - 1;
-            ++n;
+            ++nb;
           }
         }
         float v[4][E];
@@ -78,7 +107,7 @@ __global__ __launch_bounds__(kWaves * 64) void merge_kernel(MergeArgs a) {
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          if (j < n) {
+          if (j < nb) {
             const float wj = readlane(w, idx[j]);
             wsum += wj;
 #pragma unroll

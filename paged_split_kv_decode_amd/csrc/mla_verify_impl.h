@@ -850,8 +850,10 @@ void mla_verify_kernel(MlaArgs a) {
       const int j1 = min(i1, nt);
       if (i0 < j1) run_piece(ub, rb, i0, j1 - i0, slot);
       if (owner && (nt == 0 || split_mode)) {
-        // lse = -inf in the split slots no piece of the unit uses (all of
-        // them for a unit with no key), or O = 0 / LSE = -inf written directly
+        // Partials only: lse = -inf in the split slots no piece of the unit
+        // uses (all of them for a unit with no key); a call that merges
+        // itself ends the slot list with lse = +inf in the first unused slot
+        // (the merge reads no further); or O = 0 / LSE = -inf written directly
         const int nseg = nt > 0 ? (rs + nt - 1) / T - rs / T + 1 : 0;
         const int my_row = rb * kRowsPerBlock + wave * kRowsPerWave + l32;
         if (my_row < rows_req) {
@@ -861,9 +863,11 @@ void mla_verify_kernel(MlaArgs a) {
             uint16_t* orow = a.out + q_row * a.o_srow + (int64_t)h_row * a.o_sh;
             for (int d = g2 * 8; d < kLv; d += 16) *(u32x4*)(orow + d) = u32x4{0, 0, 0, 0};
             if (a.lse != nullptr && g2 == 0) a.lse[q_row * a.lse_srow + h_row] = neg_inf();
-          } else {
+          } else if (a.partials) {
             for (int sl = nseg + g2; sl < S; sl += 2)
               a.ws[((q_row * a.H + h_row) * S + sl) * (kLv + 1) + kLv] = neg_inf();
+          } else if (nseg < S && g2 == 0) {
+            a.ws[((q_row * a.H + h_row) * S + nseg) * (kLv + 1) + kLv] = end_of_slots();
           }
         }
       }

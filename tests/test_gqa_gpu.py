@@ -236,6 +236,35 @@ def test_merge_splits_against_oracle(pd, S, Dv):
     check_attention(out, lse, O, L, lse_atol=1e-5, what="merge")
 
 
+@pytest.mark.parametrize("S", [2, 8, 9, 70])
+def test_merge_stops_at_the_end_of_list_marker(pd, S):
+    """lse = +inf ends a (row, head)'s slot list: the merge equals the
+    oracle's merge of the slots before it, whatever lies after (NaN, huge
+    lse values); a list ending at slot 0 is keyless (O = 0, LSE = -inf)."""
+    rng = np.random.default_rng(S)
+    rows, H, Dv = 5, 4, 128
+    Op = rng.standard_normal((rows, H, S, Dv))
+    lp = rng.standard_normal((rows, H, S)) * 3.0
+    lp[rng.random((rows, H, S)) < 0.2] = -np.inf
+    ends = rng.integers(0, S + 1, size=(rows, H))        # S: no marker
+    ends[0, 0] = 0
+    ends[1, 1] = min(S, 8)
+    keep = np.arange(S)[None, None, :] < ends[..., None]
+    lp_ref = np.where(keep, lp, -np.inf)
+    O, L = oracle.merge_partials(Op, lp_ref, None)
+    for r in range(rows):
+        for h in range(H):
+            e = ends[r, h]
+            if e < S:
+                lp[r, h, e] = np.inf
+                lp[r, h, e + 1:] = 1e30                  # never read
+                Op[r, h, e:] = np.nan
+    ws = np.concatenate([Op, lp[..., None]], axis=-1).astype(np.float32)
+    out, lse = pd.merge_splits(torch.from_numpy(ws).cuda(), rows, H, S, Dv)
+    torch.cuda.synchronize()
+    check_attention(out, lse, O, L, lse_atol=1e-5, what=f"merge S={S} with end markers")
+
+
 FULL = ["gqa_sinks", "gqa_window", "gqa_skewed"]
 
 
