@@ -66,11 +66,17 @@ constexpr int kTileBytes8 = kTileTokens * kRowBytes8;   // 8 KB
 // 4 tiles of 8 KB (one computed, up to three loading) with 4 waves per
 // workgroup, 2 tiles with 8.
 
-// FP8 tile: 16-byte chunk c of token row r (256 bytes) is stored at chunk
-// c ^ f8(r).  Rows 0..15 (and 16..31) get distinct values (K reads: 16 rows,
-// one chunk), and the 8 rows a 16-lane group reads for a V^T fragment
-// (4 g .. 4 g + 3 and 16 + 4 g .. 16 + 4 g + 3) too.
-__device__ __forceinline__ int f8(int r) { return (r & 15) ^ ((r >> 4) << 2); }
+// LDS bank model (measured with the SQ_LDS_BANK_CONFLICT counter on
+// MI355X): 64 banks of 4 bytes; an 8-byte-per-lane read (ds_read_b64, the
+// transpose reads) serves 32 lanes per cycle, which must then touch the 16
+// distinct 16-byte slots of a 256-byte bank row in both 8-byte halves.
+//
+// FP8 tile: 16-byte chunk c of token row r (256 bytes, one bank row) is
+// stored at chunk c ^ f8(r).  f8 is a permutation of rows 0..15 and of
+// 16..31 (K reads: 32 lanes = 16 rows x 2 halves of one chunk) and of the 16
+// rows {0..7, 16..23} and {8..15, 24..31} (V^T transpose reads: the first
+// and the second 32 lanes read 16 such rows, 2 halves each).
+__device__ __forceinline__ int f8(int r) { return (r & 7) | ((((r >> 3) ^ (r >> 4)) & 1) << 3); }
 // 1 KB of zeros in device memory: the source of rows of pages that are not
 // read in the general page class (any 16-byte chunk of a 512-byte row stays
 // inside it).
@@ -87,11 +93,13 @@ constexpr int kMinWaveTiles = 2;
 // skewed decode batch, at 2 and 8% on the sinks, verify and 8-token-page
 // decode workloads; 1.4-2.2% at 8%.)
 
-// 16-byte chunk c of token row r is stored at chunk c ^ swz(r).  Rows
-// 0..7 get distinct low-3-bit patterns (K reads: 8 consecutive rows, same
-// chunk) and rows 4k..4k+3 distinct bits 2:1 (V transpose reads: 4 rows x a
-// 32-byte chunk pair).
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// bf16 tile: 16-byte chunk c of token row r (512 bytes, two bank rows) is
+// stored at chunk c ^ swz(r), inside the row's K or V half.  swz permutes
+// rows 0..15 (K reads: 16 rows, one chunk) and its bits 3:1 permute each 8
+// consecutive rows (V^T transpose reads: 32 lanes = 8 rows x a chunk pair
+// x 2 halves).  The earlier 3-bit swizzle repeated every 8 rows and left
+// every transpose read 2-way conflicted.
+__device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 
 __device__ __forceinline__ uint32_t keep_mask(bool lo_ok, bool hi_ok) {
   return (lo_ok ? 0x0000FFFFu : 0u) | (hi_ok ? 0xFFFF0000u : 0u);

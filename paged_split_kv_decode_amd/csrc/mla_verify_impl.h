@@ -93,9 +93,14 @@ constexpr int kPieceTiles = 8;
 // row r at 16-byte slot 8 (r % 8) + ((c % 8) ^ (r % 8) ^ R).  So
 //  * one global_load_lds instruction (64 lanes x 16 bytes) fills one block
 //    from 8 whole 128-byte lines; the XOR only permutes lanes inside a line;
-//  * a K-operand read (rows 0..15 of a page, one chunk) and a transpose
-//    read of V (4 rows x 2 chunks) touch distinct 16-byte slots modulo the
-//    256 bytes of the 64 banks: both bank-conflict free.
+//  * a K-operand read (rows 0..15 of a page, one chunk) touches distinct
+//    16-byte slots modulo the 256 bytes of the 64 banks.  A transpose read
+//    of V serves 32 lanes (4 rows x 4 chunks x 2 halves) per cycle, and rows
+//    4k and 4k + 2 share a bank row and chunk group here, so the rocprofv3
+//    bank-conflict counter shows it 2-way conflicted.  A layout with bits 1
+//    and 2 of the row exchanged in the XOR removes the conflict (measured)
+//    but ran 0.6% slower per call on the same box: these reads are not what
+//    bounds the kernel, so the layout stays.
 __device__ __forceinline__ int tile_off(int c, int r16) {
   return ((c >> 3) * 2 + (r16 >> 3)) * 1024 + (8 * (r16 & 7) + ((c & 7) ^ (r16 & 7) ^ (r16 >> 3))) * 16;
 }
