@@ -42,8 +42,10 @@
  *
  * Numerics (module docstring of "vllm.models.flint.ops.decode_attention"):
  * scores are bf16 x bf16 products accumulated in fp32; softmax runs in fp32 as
- * exp2(s * c - m * c) with c = sm_scale * log2(e) and a running max m of the
- * unscaled scores; probabilities are rounded to bf16 for the P.V product
+ * exp2(s * c - m * c) with c = sm_scale * log2(e) and a reference m of the
+ * unscaled scores (GQA: the running max, moved only when a score passes it
+ * by more than 8 / c, so p <= 2^8; MLA: a row's first tile max);
+ * probabilities are rounded to bf16 for the P.V product
  * (fp32 accumulation); split partials stay fp32.
  */
 #ifndef PAGED_DECODE_H_

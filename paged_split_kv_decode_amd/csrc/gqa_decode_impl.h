@@ -31,7 +31,8 @@
 //   directly.
 // * Scores S^T[token, head] = K . Q^T on v_mfma_f32_16x16x32_bf16 with the
 //   G query heads of the kv head in the N dimension (G <= 16, zero-padded).
-//   Online softmax in fp32 with exp2 and a running max in unscaled logits,
+//   Online softmax in fp32 with exp2 and a reference max in unscaled logits
+//   (moved, with a rescale, only when a score passes it by 2^8),
 //   reduced over the 4 lanes of a head with two lane swaps
 //   (v_permlane16_swap, v_permlane32_swap).  P (bf16) is already in the
 //   B-operand layout of O^T[d, head] += V^T . P^T, and V^T is read from the
@@ -44,6 +45,7 @@
 //   rows are loaded from a harmless address and the piece's result is NaN.
 #pragma once
 
+#include <algorithm>
 #include <utility>
 
 #include "device_common.h"
@@ -87,6 +89,12 @@ __device__ __attribute__((aligned(1024))) uint32_t g_zero_rows[256];
 // waves stream at once: 2 measured 6% faster than 4 at the window config
 // (11.9 against 12.7 us per call).
 constexpr int kMinWaveTiles = 2;
+// How far (log2 units of exp2) a score may pass a column's reference max
+// before the reference moves: the rescale of O and l (32 multiplies per
+// column group) then runs only on the few tiles that raise the max by that
+// much, and probabilities stay below 2^8 (with the relative precision they
+// have below 1).
+constexpr float kRescaleLog2 = 8.f;
 // Every wave takes an equal share.  (Shares skewed by a fixed amount
 // between even and odd XCDs, which had streamed at different rates, lost
 // against equal shares with this kernel: at 2, 3, 4, 6, 8, 10 and 12% on the
@@ -192,6 +200,7 @@ struct Share {
   int t;        // tiles per share
   bool last;
   bool split;   // S >= 2: pieces may cut units; S == 1: whole units only
+  int64_t u_end;   // unit mode: units from this index on are another wave's
   // first tile of the share of wave j, and the share holding tile p
   __device__ int start(int j) const { return j * t; }
   __device__ int of(int p) const { return p / t; }
@@ -251,7 +260,38 @@ __global__ __launch_bounds__(gqa_waves(F8, NC) * 64) void gqa_decode_kernel(GqaA
     g_col[cg] = 16 * cg + l16;
   }
 
-  // ---- the plan: total tiles, longest request, this wave's share --------
+  // ---- the plan ----------------------------------------------------------
+  Share sh;
+  int b_s = -1, kvh_s = 0, p0_s = 0;
+  Req r_s;
+  // Whole units with no more units than waves: one unit per wave, the best
+  // whole-unit schedule whatever the lengths, and no wave scans the batch.
+  // Unit j goes to wave j / grid of workgroup j % grid, so the busy waves
+  // spread over every compute unit (the launch has no more workgroups than
+  // units): a window decode of 512 units ran 11% slower on 4 waves of 128
+  // workgroups than on 2 waves of 256.
+  const bool unit_mode = S == 1 && (int64_t)a.B * Hkv <= n_waves;
+  if (unit_mode) {
+    const int j = uniform(wave_in_wg * (int)gridDim.x + (int)blockIdx.x);
+    if (j >= a.B * Hkv) return;
+    b_s = uniform(j / Hkv);
+    kvh_s = uniform(j - b_s * Hkv);
+    r_s = request_range<V>(a, b_s);
+    r_s.lo = uniform(r_s.lo);
+    r_s.hi = uniform(r_s.hi);
+    r_s.nt = uniform(r_s.nt);
+    r_s.n = uniform(r_s.n);
+    r_s.row0 = uniform(r_s.row0);
+    r_s.L = uniform(r_s.L);
+    // flat positions are not needed: the cursor stops at unit j + 1
+    sh.split = false;
+    sh.t = 1;
+    sh.g0 = 0;
+    sh.g1 = INT32_MAX;
+    sh.last = false;
+    sh.u_end = j + 1;
+  } else {
+  // ---- total tiles, longest request, this wave's share ------------------
   // Lane l of chunk c holds the length of request 64c + l (0 past the batch).
   int Lc[kCachedChunks], Lrc[kCachedChunks], Nc[kCachedChunks];
 #pragma unroll
@@ -277,8 +317,8 @@ __global__ __launch_bounds__(gqa_waves(F8, NC) * 64) void gqa_decode_kernel(GqaA
   nt_sum = uniform(nt_sum);
   nt_max = uniform(nt_max);
   const int U = nt_sum * Hkv;
-  Share sh;
   sh.split = S >= 2;
+  sh.u_end = INT32_MAX;
   // a unit of n tiles cut every t tiles at an arbitrary offset spans at
   // most floor((n - 1) / t) + 2 shares: keep that <= S
   const int t_min = sh.split ? max((nt_max - 1) / (S - 1) + 1, kMinWaveTiles) : kMinWaveTiles;
@@ -292,7 +332,7 @@ __global__ __launch_bounds__(gqa_waves(F8, NC) * 64) void gqa_decode_kernel(GqaA
   // ---- first unit of the share ------------------------------------------
   // split: the unit holding tile g0, or an empty unit starting at or after
   // g0; whole units: the first unit starting at or after g0.
-  int b_s = -1, L_s = 0, Lr_s = 0, N_s = 0, cb_s = 0;
+  int L_s = 0, Lr_s = 0, N_s = 0, cb_s = 0;
   {
     int C = 0;  // tiles of the requests before this chunk (one kv head)
     auto probe = [&](int base, int L, int Lr, int N) {
@@ -328,13 +368,15 @@ __global__ __launch_bounds__(gqa_waves(F8, NC) * 64) void gqa_decode_kernel(GqaA
   }
   if (b_s < 0) return;
   b_s = uniform(b_s);
-  Req r_s = range_of(a, uniform(L_s), uniform(Lr_s), uniform(N_s));
+  r_s = range_of(a, uniform(L_s), uniform(Lr_s), uniform(N_s));
   r_s.row0 = uniform(V ? query_rows(a, b_s).row0 : b_s);
-  int kvh_s = 0;
   if (sh.g0 > cb_s)
     kvh_s = sh.split ? (sh.g0 - cb_s) / r_s.nt : (sh.g0 - cb_s + r_s.nt - 1) / r_s.nt;
   kvh_s = uniform(kvh_s);
-  const int p0_s = uniform(cb_s + kvh_s * r_s.nt);
+  p0_s = uniform(cb_s + kvh_s * r_s.nt);
+  }
+  // the cursor has passed the share's last unit (unit mode)
+  auto past_units = [&](const Cursor& cu) { return (int64_t)cu.b * Hkv + cu.kvh >= sh.u_end; };
 
   // Step to the next unit (no range checks).
   auto next_unit = [&](Cursor& cu) {
@@ -351,7 +393,7 @@ __global__ __launch_bounds__(gqa_waves(F8, NC) * 64) void gqa_decode_kernel(GqaA
   // share is done.
   auto settle = [&](Cursor& cu) {
     for (;;) {
-      if (cu.b >= a.B || (!sh.last && cu.p0 >= sh.g1)) {
+      if (cu.b >= a.B || (!sh.last && cu.p0 >= sh.g1) || past_units(cu)) {
         cu.b = a.B;
         return;
       }
@@ -985,7 +1027,7 @@ __global__ __launch_bounds__(gqa_waves(F8, NC) * 64) void gqa_decode_kernel(GqaA
       // their products, behind the softmax)
       __builtin_amdgcn_sched_barrier(0);
 
-      // ---- online softmax (fp32, exp2, running max in unscaled logits) ----
+      // ---- online softmax (fp32, exp2, reference max in unscaled logits) ----
       // P^T as the B operand: k = 8*g4 + j <-> tokens 4*g4 + j (j < 4) and
       // 16 + 4*g4 + (j - 4) (j >= 4), exactly this lane's scores.
       bf16x8 pf[NC];
@@ -995,10 +1037,20 @@ __global__ __launch_bounds__(gqa_waves(F8, NC) * 64) void gqa_decode_kernel(GqaA
         float mx = fmaxf(fmaxf(fmaxf(s0[cg][0], s0[cg][1]), fmaxf(s0[cg][2], s0[cg][3])),
                          fmaxf(fmaxf(s1[cg][0], s1[cg][1]), fmaxf(s1[cg][2], s1[cg][3])));
         mx = max_xor32(max_xor16(mx));
-        const float m_new = fmaxf(m_run[cg], mx);
-        const float m_ref = m_new == neg_inf() ? 0.f : m_new;
-        const float mc = m_ref * c;
-        const float alpha = fast_exp2(m_run[cg] * c - mc);
+        // The reference m_run moves (and O and l are rescaled) only when a
+        // score passes it by more than kRescaleLog2 in the exp2 domain, so
+        // p <= 2^kRescaleLog2.  The branch is taken by the whole wave;
+        // columns that did not grow keep alpha = 1 (their reference may
+        // still be -inf: a verify column whose keys start later).
+        const bool grow = (mx - m_run[cg]) * c > kRescaleLog2;   // false while both are -inf
+        if (__ballot(grow) != 0ull) {
+          const float alpha = grow ? fast_exp2((m_run[cg] - mx) * c) : 1.f;
+          l_run[cg] *= alpha;
+          m_run[cg] = grow ? mx : m_run[cg];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) o[cg][i] *= alpha;
+        }
+        const float mc = (m_run[cg] == neg_inf() ? 0.f : m_run[cg]) * c;
         float p0[4], p1[4];
         float psum = 0.f;
 #pragma unroll
@@ -1007,10 +1059,7 @@ __global__ __launch_bounds__(gqa_waves(F8, NC) * 64) void gqa_decode_kernel(GqaA
           p1[i] = fast_exp2(s1[cg][i] * c - mc);
           psum += p0[i] + p1[i];
         }
-        l_run[cg] = l_run[cg] * alpha + psum;
-        m_run[cg] = m_new;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) o[cg][i] *= alpha;
+        l_run[cg] += psum;
         const u32x4 pw = {pack_bf16x2(p0[0], p0[1]), pack_bf16x2(p0[2], p0[3]),
                           pack_bf16x2(p1[0], p1[1]), pack_bf16x2(p1[2], p1[3])};
         pf[cg] = __builtin_bit_cast(bf16x8, pw);
@@ -1089,7 +1138,7 @@ __global__ __launch_bounds__(gqa_waves(F8, NC) * 64) void gqa_decode_kernel(GqaA
   cw.kvh = kvh_s;
   cw.p0 = p0_s;
   cw.r = r_s;
-  while (cw.b < a.B && (sh.last || cw.p0 < sh.g1)) {
+  while (cw.b < a.B && (sh.last || cw.p0 < sh.g1) && !past_units(cw)) {
     const int hq0 = cw.kvh * G;
     R = V ? cw.r.n * G : G;   // this unit's columns
     // (row, query head) of column n of this unit
@@ -1164,15 +1213,20 @@ __global__ __launch_bounds__(gqa_waves(F8, NC) * 64) void gqa_decode_kernel(GqaA
 
 // Launches page class PS for a decode or verify call with a bf16 or FP8
 // cache, with the fused append or not (AP); one workgroup per compute unit.
+// With one split (whole units) the grid has no more workgroups than units
+// (the kernel's unit mode spreads one unit per wave over them).
 template <int PS, bool AP>
 hipError_t launch_gqa_class(const GqaArgs& a, bool verify, int n_wg, hipStream_t stream) {
-  const dim3 grid(n_wg), block(gqa_waves(false, 1) * 64), block8(gqa_waves(true, 1) * 64);
+  const int64_t units = (int64_t)a.B * a.Hkv;
+  const dim3 grid((unsigned)(a.S == 1 ? std::max<int64_t>(1, std::min<int64_t>(n_wg, units)) : n_wg));
+  const dim3 grid8 = grid;
+  const dim3 block(gqa_waves(false, 1) * 64), block8(gqa_waves(true, 1) * 64);
   if (verify) {
     // score column groups of 16 for the (verify token, head) pairs
     const int cols = a.qlen * a.G;
     if (a.kv_fp8) {
       if (cols <= 16)
-        hipLaunchKernelGGL((gqa_decode_kernel<PS, true, true, 1, AP>), grid, block8, 0, stream, a);
+        hipLaunchKernelGGL((gqa_decode_kernel<PS, true, true, 1, AP>), grid8, block8, 0, stream, a);
       else if (cols <= 32)
         hipLaunchKernelGGL((gqa_decode_kernel<PS, true, true, 2, AP>), grid, block, 0, stream, a);
       else
@@ -1187,7 +1241,7 @@ hipError_t launch_gqa_class(const GqaArgs& a, bool verify, int n_wg, hipStream_t
     }
   } else {
     if (a.kv_fp8)
-      hipLaunchKernelGGL((gqa_decode_kernel<PS, false, true, 1, AP>), grid, block8, 0, stream, a);
+      hipLaunchKernelGGL((gqa_decode_kernel<PS, false, true, 1, AP>), grid8, block8, 0, stream, a);
     else
       hipLaunchKernelGGL((gqa_decode_kernel<PS, false, false, 1, AP>), grid, block, 0, stream, a);
   }
