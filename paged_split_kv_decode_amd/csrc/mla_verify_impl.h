@@ -249,17 +249,17 @@ void mla_verify_kernel(MlaArgs a) {
     // A row past the request's rows reads the request's first row instead:
     // its scores are all masked (hi_row = 0) and its output is never
     // written.  With no select on the loaded values, the 36 loads go
-    // straight into the fragment registers and are in flight together; one
-    // wait follows, before any tile load is issued (left to the compiler,
-    // the wait would sit at the fragment's first use inside the tile loop
-    // and drain the tile ring on every iteration).
+    // straight into the fragment registers and are in flight together, with
+    // the block-table reads and the loads of the first two tiles; one wait
+    // for all of them precedes the tile loop (left to the compiler, the wait
+    // would sit at the fragment's first use inside the tile loop, which does
+    // not see the tile loads, and drain the ring on every iteration).
     bf16x8 qf[kKSteps];
     {
       const uint16_t* qp = a.q + ((int64_t)b * a.qlen + t_row) * a.q_srow + (int64_t)h_row * a.q_sh;
       // step kk takes dims 16 kk + 8 g2 .. + 7
   #pragma unroll
       for (int kk = 0; kk < kKSteps; ++kk) qf[kk] = *(const bf16x8*)(qp + 16 * kk + 8 * g2);
-      wait_vmcnt<0>();
     }
 
     const char* kv = (const char*)a.kv;
@@ -496,6 +496,7 @@ void mla_verify_kernel(MlaArgs a) {
     if (n > 0) issue(fetch(tb), 0);
     if (n > 1) issue(fetch(tb + 1), 1);
     if (n > 2) pg_next = fetch(tb + 2);
+    wait_vmcnt<0>();   // the query fragments (and tiles 0 and 1)
 
     for (int k = 0; k <= n; ++k) {
       const bool live = k < n;   // iteration n only finishes tile n-1

@@ -206,6 +206,40 @@ def test_out_of_range_block_table_entry_gives_nan(pd):
         check_attention(out[:1], lse[:1], O, L, what="valid neighbour")
 
 
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+def test_one_split_unit_per_wave_boundary(pd, fp8):
+    """One split with exactly as many units (request, kv head) as the grid has
+    waves (one unit per wave, no plan scan) and with one request more (the
+    scanned whole-unit plan): both agree with the oracle on sampled requests,
+    and the first batch's requests are bit for bit the larger batch's."""
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    waves = n_cu * (8 if fp8 else 4)
+    b_unit = waves // 8                              # Hkv = 8: units == waves
+    w = gqa_workload("gqa_sinks", batch=b_unit + 1, len_range=(1, 300), seed_offset=41 + fp8,
+                     pool="tight")
+    assert w.B * w.Hkv == waves + w.Hkv
+    vals = w.values("cuda", poison=True, fp8=fp8)
+    bt, sl = _dev(w)
+    scales = dict(k_scale=vals.get("k_scale"), v_scale=vals.get("v_scale")) if fp8 else {}
+
+    def call(nb):
+        # qlen = 1 without real lengths: the decode kernel (8 waves per
+        # workgroup for the FP8 cache)
+        out, lse = pd.paged_verify_gqa(vals["q"][:nb], vals["kv"], bt[:nb], sl[:nb], 1, w.sm_scale,
+                                       sinks=vals["sinks"], num_kv_splits=1, **scales)
+        torch.cuda.synchronize()
+        return out, lse
+
+    big = call(w.B)
+    unit = call(b_unit)
+    assert torch.equal(big[0][:b_unit].view(torch.int16), unit[0].view(torch.int16))
+    assert torch.equal(big[1][:b_unit].view(torch.int32), unit[1].view(torch.int32))
+    sample = [0, 1, b_unit // 2, b_unit - 1, b_unit]
+    O, L = oracle_gqa(w, vals, sample)
+    check_attention(big[0][sample], big[1][sample], O, L,
+                    o_atol=5e-2 if fp8 else 2e-2, what=f"one split, fp8={fp8}")
+
+
 def test_repeated_calls_are_bitwise_deterministic(pd):
     w = gqa_workload("gqa_skewed", batch=16, loguniform=(16, 5000), zero_lens=1)
     vals = w.values("cuda", poison=True)
