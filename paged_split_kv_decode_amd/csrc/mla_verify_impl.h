@@ -431,11 +431,9 @@ void mla_verify_kernel(MlaArgs a) {
     float m_ref = neg_inf();    // fixed reference of the current pass
     float l_run = 0.f;
     // Output accumulator: O^T for the wave's 128 output dims (4 blocks d of
-    // 32) x the block's 128 rows (4 groups r of 32), block (d, r) = o[4 d + r].
-    // Blocks 0..14 stay in AGPRs; block (3, 3) is parked in VGPRs between
-    // tiles, which leaves 16 AGPRs for the score accumulator.
-    f32x16 o[15];
-    f32x16 o_last;
+    // 32) x the block's 128 rows (4 groups r of 32), block (d, r) = o[4 d + r],
+    // in all 256 AGPRs.  (The score accumulator is in arch VGPRs.)
+    f32x16 o[16];
 
     // lane-constant parts of the transpose-read addresses
     const int q16 = lane >> 4;
@@ -472,11 +470,9 @@ void mla_verify_kernel(MlaArgs a) {
     l_run = 0.f;
     bool overflow = false;
   #pragma unroll
-    for (int i = 0; i < 15; ++i)
+    for (int i = 0; i < 16; ++i)
   #pragma unroll
       for (int e = 0; e < 16; ++e) o[i][e] = 0.f;
-  #pragma unroll
-    for (int e = 0; e < 16; ++e) o_last[e] = 0.f;
 
     // Iteration k computes the scores of tile k interleaved with the P.V
     // product of tile k-1 (whose probabilities every wave published in
@@ -537,14 +533,21 @@ void mla_verify_kernel(MlaArgs a) {
         if (k + 3 < n) pg_next = fetch(tb + k + 3);
       }
 
-      // ---- S^T(k) = K Q^T (36 MFMAs, one chain) with O^T += V^T P^T of tile
-      // k-1 (30 MFMAs: every block but (3, 3)) in between ------------------
+      // ---- S^T(k) = K Q^T (36 MFMAs, one chain); FP8: with O^T += V^T P^T of
+      // tile k-1 (32 MFMAs) in between ---------------------------------------
       // Fragments are read a few MFMA pairs ahead of their use; scheduling
       // barriers pin that order (left alone, the scheduler moves every read
       // next to its MFMA and the wave stalls on LDS latency at each step).
+      // The score accumulator lives in arch VGPRs: the chain is issued in the
+      // asm form of the MFMA, with a VGPR destination (compiled MFMAs put
+      // every accumulator in AGPRs, where the output blocks take all 256).
+      // The hardware forwards a dependent accumulator between back-to-back
+      // MFMAs of one shape; the asm carries the wait states the compiler
+      // would otherwise insert: 3 before an MFMA reads operands a vector ALU
+      // instruction has just written (the FP8 conversions; 2 required), and
+      // 24 after the last one before a vector ALU instruction reads the
+      // result (11 required after an 8-pass MFMA, 19 after a 16-pass one).
       f32x16 sacc;
-  #pragma unroll
-      for (int e = 0; e < 16; ++e) sacc[e] = 0.f;
       // chunk 2 kk + g2 of row kr = l32 % 16: line kk / 4, slot
       // 8 (kr % 8) + ((2 (kk % 4)) ^ kz) with the lane constant kz
       const int kr = l32 & 15, kz = g2 ^ (kr & 7) ^ (kr >> 3);
@@ -604,20 +607,43 @@ void mla_verify_kernel(MlaArgs a) {
         }
   #pragma unroll
         for (int kk = 0; kk < kKSteps; ++kk) {
-          if constexpr (FP8) {
-            const u32x2 w = kw[kk % kKAhead];
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cvt8x8(w[0], w[1]), qf[kk], sacc, 0, 0, 0);
-          } else {
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk % kKAhead], qf[kk], sacc, 0, 0, 0);
+          {
+            bf16x8 kop;
+            if constexpr (FP8) {
+              const u32x2 w = kw[kk % kKAhead];
+              kop = cvt8x8(w[0], w[1]);
+            } else {
+              kop = kf[kk % kKAhead];
+            }
+            // (FP8: 3 wait states after the conversions; last step: 24 before
+            // the vector ALU reads the result)
+#define PD_MFMA_S(PRE, C, POST)                                                         \
+  asm volatile(PRE "v_mfma_f32_32x32x16_bf16 %0, %1, %2, " C POST                      \
+               : "+v"(sacc) : "v"(kop), "v"(qf[kk]))
+            if constexpr (FP8) {
+              if (kk == 0)
+                PD_MFMA_S("s_nop 2\n\t", "0", "");
+              else if (kk + 1 < kKSteps)
+                PD_MFMA_S("s_nop 2\n\t", "%0", "");
+              else
+                PD_MFMA_S("s_nop 2\n\t", "%0", "\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
+            } else {
+              if (kk == 0)
+                PD_MFMA_S("", "0", "");
+              else if (kk + 1 < kKSteps)
+                PD_MFMA_S("", "%0", "");
+              else
+                PD_MFMA_S("", "%0", "\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
+            }
+#undef PD_MFMA_S
           }
-          if (FP8 && kk < 30) {
-            const int s = kk / 15, idx = kk % 15, d = idx >> 2, r = idx & 3, v = 4 * s + d;
+          if (FP8 && kk < 32) {
+            const int s = kk / 16, idx = kk % 16, d = idx >> 2, r = idx & 3, v = 4 * s + d;
             o[idx] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[v & 1], pf[r], o[idx], 0, 0, 0);
             // V^T fragment v is done after its last row group: fetch v + 2
-            const bool v_done = r == 3 || idx == 14;
-            if (v_done && v + 2 < 8) vf[v & 1] = vread((v + 2) >> 2, (v + 2) & 3);
-            // P^T (r, 0) is done after block d = 3 (d = 2 for r = 3): fetch (r, 1)
-            if (s == 0 && (d == 3 || (d == 2 && r == 3))) pf[r] = pread(r, 1);
+            if (r == 3 && v + 2 < 8) vf[v & 1] = vread((v + 2) >> 2, (v + 2) & 3);
+            // P^T (r, 0) is done after block d = 3: fetch (r, 1)
+            if (s == 0 && d == 3) pf[r] = pread(r, 1);
           }
           if constexpr (FP8) {
             if (kk + kKAhead < kKSteps) kw[kk % kKAhead] = kread8(kk + kKAhead);
@@ -631,22 +657,8 @@ void mla_verify_kernel(MlaArgs a) {
         float x[16];
   #pragma unroll
         for (int e = 0; e < 16; ++e) x[e] = sacc[e] * c;
-        {
-          // block (3, 3) of tile k-1's product, after the score accumulator is
-          // free: V^T fragment 3 and P^T (3, 0) are read again, fragment 7 and
-          // P^T (3, 1) are still in registers
-          const bf16x8 va = vread(0, 3), pa = pread(3, 0);
-          f32x16 ob = o_last;
-          ob = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pa, ob, 0, 0, 0);
-          if constexpr (FP8)
-            ob = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[1], pf[3], ob, 0, 0, 0);
-          else
-            ob = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread(1, 3), pread(3, 1), ob, 0, 0, 0);
-          o_last = ob;
-          asm volatile("" : "+v"(o_last));
-        }
         if constexpr (!FP8) {
-          // bf16: tile k-1's 30 remaining products with tile k's softmax
+          // bf16: tile k-1's 32 products with tile k's softmax
           // interleaved by hand, one product and a slice of the softmax per
           // step, a scheduling barrier closing each step (the products do not
           // depend on the softmax; in the score loop they only padded the
@@ -664,12 +676,11 @@ void mla_verify_kernel(MlaArgs a) {
   #pragma unroll
           for (int r = 0; r < 4; ++r) pr[r] = pread(r, 0);
   #pragma unroll
-          for (int j = 0; j < 30; ++j) {
-            const int s = j / 15, idx = j % 15, d = idx >> 2, r = idx & 3, v = 4 * s + d;
+          for (int j = 0; j < 32; ++j) {
+            const int s = j / 16, idx = j % 16, d = idx >> 2, r = idx & 3, v = 4 * s + d;
             o[idx] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[v & 1], pr[r], o[idx], 0, 0, 0);
-            const bool v_done = r == 3 || idx == 14;
-            if (v_done && v + 2 < 8) vr[v & 1] = vread((v + 2) >> 2, (v + 2) & 3);
-            if (s == 0 && (d == 3 || (d == 2 && r == 3))) pr[r] = pread(r, 1);
+            if (r == 3 && v + 2 < 8) vr[v & 1] = vread((v + 2) >> 2, (v + 2) & 3);
+            if (s == 0 && d == 3) pr[r] = pread(r, 1);
             if (j < 2) {
               // causal limit of this lane's row: token tok0 + 8 (e / 4) + 4 g2 + e % 4 < hi_row
   #pragma unroll
@@ -811,7 +822,7 @@ void mla_verify_kernel(MlaArgs a) {
             for (int d = 0; d < kDimBlocksPerWave; ++d)
   #pragma unroll
               for (int j = 0; j < 4; ++j) {
-                const f32x16& ob = 4 * d + r < 15 ? o[4 * d + r < 15 ? 4 * d + r : 0] : o_last;
+                const f32x16& ob = o[4 * d + r];
                 float x0 = ob[4 * j + 0] * inv, x1 = ob[4 * j + 1] * inv;
                 float x2 = ob[4 * j + 2] * inv, x3 = ob[4 * j + 3] * inv;
                 if (bad) x0 = x1 = x2 = x3 = qnan;
@@ -823,7 +834,7 @@ void mla_verify_kernel(MlaArgs a) {
             for (int d = 0; d < kDimBlocksPerWave; ++d)
   #pragma unroll
               for (int j = 0; j < 4; ++j) {
-                const f32x16& ob = 4 * d + r < 15 ? o[4 * d + r < 15 ? 4 * d + r : 0] : o_last;
+                const f32x16& ob = o[4 * d + r];
   #pragma unroll
                 for (int i = 0; i < 4; ++i) oslot[32 * d + 8 * j + 4 * g2 + i] = bad ? qnan : ob[4 * j + i] * inv;
               }
