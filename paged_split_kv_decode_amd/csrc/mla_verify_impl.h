@@ -70,7 +70,12 @@ constexpr int kRowBytes8 = kLk;                                    // fp8 latent
 constexpr int kTileBytes8 = kTileTokens * kRowBytes8;              // 18 KB
 constexpr int kPageRegion8 = 16 * kRowBytes8;                      // 9 KB (fp8)
 constexpr int kKSteps = kLk / 16;                                  // 36
-constexpr int kKAhead = 3;                                         // K fragments in flight
+// K fragments read ahead of their score step.  bf16: 5 (the score chain's
+// 16-byte reads saturate the LDS, so each queues behind the other waves';
+// 3 -> 5 took 2-3% off the kernel, 6, 7 and 9 gained less); FP8: 3 (8-byte
+// reads; 4 equal, 5 slower).
+constexpr int kKAheadBf16 = 5;
+constexpr int kKAheadFp8 = 3;
 constexpr int kDimBlocksPerWave = kLv / 32 / kWaves;              // 4 output blocks of 32 dims
 constexpr int kPBufBytes = kWaves * 2 * 1024;                      // P^T of one tile: 4 row groups x 2 key steps
 // p = 2^(x - m_ref) stays below 2^64 while the row max has not grown more
@@ -590,6 +595,7 @@ void mla_verify_kernel(MlaArgs a) {
       // product step j (0..29): s = j / 15, block index 4 d + r = j % 15.  V^T
       // fragment v = 4 s + d lives in vf[v & 1]; P^T fragment (r, s) in pf[r].
       {
+        constexpr int kKAhead = FP8 ? kKAheadFp8 : kKAheadBf16;
         bf16x8 kf[kKAhead], vf[2], pf[4];
         u32x2 kw[kKAhead];   // FP8: raw K codes, a few steps ahead
         if constexpr (FP8) {
