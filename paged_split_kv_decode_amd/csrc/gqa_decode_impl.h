@@ -200,6 +200,7 @@ struct Share {
   int t;        // tiles per share
   bool last;
   bool split;   // S >= 2: pieces may cut units; S == 1: whole units only
+  bool range;   // the cursor keeps to [g0, g1) inside units (split, or a pair's half)
   int64_t u_end;   // unit mode: units from this index on are another wave's
   // first tile of the share of wave j, and the share holding tile p
   __device__ int start(int j) const { return j * t; }
@@ -270,26 +271,52 @@ __global__ __launch_bounds__(gqa_waves(F8, NC) * 64) void gqa_decode_kernel(GqaA
   // spread over every compute unit (the launch has no more workgroups than
   // units): a window decode of 512 units ran 11% slower on 4 waves of 128
   // workgroups than on 2 waves of 256.
-  const bool unit_mode = S == 1 && (int64_t)a.B * Hkv <= n_waves;
+  // Pair mode (a.pair, set by the launcher for at most two units per four
+  // waves): unit j goes to waves 2 (j / grid) and 2 (j / grid) + 1 of
+  // workgroup j % grid, the first streaming its first ceil(nt / 2) tiles, the
+  // second the rest; the second hands its (m, l, O) to the first through
+  // LDS at the end, and the first merges and writes the unit's result.  A
+  // wave with no unit still meets that workgroup barrier.
+  const bool pair_mode = NC == 1 && a.pair != 0;
+  const int half = pair_mode ? (wave_in_wg & 1) : 0;
+  bool idle = false;
+  const bool unit_mode = pair_mode || (S == 1 && (int64_t)a.B * Hkv <= n_waves);
   if (unit_mode) {
-    const int j = uniform(wave_in_wg * (int)gridDim.x + (int)blockIdx.x);
-    if (j >= a.B * Hkv) return;
-    b_s = uniform(j / Hkv);
-    kvh_s = uniform(j - b_s * Hkv);
-    r_s = request_range<V>(a, b_s);
-    r_s.lo = uniform(r_s.lo);
-    r_s.hi = uniform(r_s.hi);
-    r_s.nt = uniform(r_s.nt);
-    r_s.n = uniform(r_s.n);
-    r_s.row0 = uniform(r_s.row0);
-    r_s.L = uniform(r_s.L);
-    // flat positions are not needed: the cursor stops at unit j + 1
+    const int j = uniform((pair_mode ? (wave_in_wg >> 1) : wave_in_wg) * (int)gridDim.x + (int)blockIdx.x);
+    if (j >= a.B * Hkv) {
+      if (!pair_mode) return;
+      idle = true;
+    }
     sh.split = false;
+    sh.range = false;
     sh.t = 1;
     sh.g0 = 0;
     sh.g1 = INT32_MAX;
     sh.last = false;
     sh.u_end = j + 1;
+    if (idle) {
+      b_s = a.B;   // nothing to stream or to answer for
+    } else {
+      b_s = uniform(j / Hkv);
+      kvh_s = uniform(j - b_s * Hkv);
+      r_s = request_range<V>(a, b_s);
+      r_s.lo = uniform(r_s.lo);
+      r_s.hi = uniform(r_s.hi);
+      r_s.nt = uniform(r_s.nt);
+      r_s.n = uniform(r_s.n);
+      r_s.row0 = uniform(r_s.row0);
+      r_s.L = uniform(r_s.L);
+      // flat positions are not needed: the cursor stops at unit j + 1 (the
+      // unit's first flat tile is 0; a pair's half keeps to its tile range)
+      if (pair_mode) {
+        // (the first half's range ends past flat tile 0 even for a unit with
+        // no tile, so its final pass still answers for that unit)
+        const int h = (r_s.nt + 1) >> 1;
+        sh.range = true;
+        sh.g0 = uniform(half ? h : 0);
+        sh.g1 = uniform(half ? r_s.nt : max(h, 1));
+      }
+    }
   } else {
   // ---- total tiles, longest request, this wave's share ------------------
   // Lane l of chunk c holds the length of request 64c + l (0 past the batch).
@@ -318,6 +345,7 @@ __global__ __launch_bounds__(gqa_waves(F8, NC) * 64) void gqa_decode_kernel(GqaA
   nt_max = uniform(nt_max);
   const int U = nt_sum * Hkv;
   sh.split = S >= 2;
+  sh.range = sh.split;
   sh.u_end = INT32_MAX;
   // a unit of n tiles cut every t tiles at an arbitrary offset spans at
   // most floor((n - 1) / t) + 2 shares: keep that <= S
@@ -398,15 +426,15 @@ __global__ __launch_bounds__(gqa_waves(F8, NC) * 64) void gqa_decode_kernel(GqaA
         return;
       }
       if (cu.r.nt > 0) {
-        cu.i = sh.split ? max(sh.g0 - cu.p0, 0) : 0;
-        cu.i_end = sh.split ? min(cu.r.nt, sh.g1 - cu.p0) : cu.r.nt;
-        return;
+        cu.i = sh.range ? max(sh.g0 - cu.p0, 0) : 0;
+        cu.i_end = sh.range ? min(cu.r.nt, sh.g1 - cu.p0) : cu.r.nt;
+        if (cu.i < cu.i_end) return;   // (a pair's empty second half: none)
       }
       next_unit(cu);
     }
   };
   // first tile of this wave's piece of the cursor's unit?
-  auto piece_start = [&](const Cursor& cu) { return cu.i == (sh.split ? max(sh.g0 - cu.p0, 0) : 0); };
+  auto piece_start = [&](const Cursor& cu) { return cu.i == (sh.range ? max(sh.g0 - cu.p0, 0) : 0); };
   auto advance = [&](Cursor& cu) {
     if (++cu.i < cu.i_end) return;
     next_unit(cu);
@@ -725,6 +753,11 @@ __global__ __launch_bounds__(gqa_waves(F8, NC) * 64) void gqa_decode_kernel(GqaA
     l_run[cg] = 0.f;
     col_lo[cg] = col_hi[cg] = 0;
   }
+  // (a pair's second half may stream nothing: its accumulator is merged)
+#pragma unroll
+  for (int cg = 0; cg < NC; ++cg)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[cg][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto finish_piece = [&](const Cursor& cu) {
     // (the lane exchanges run with the whole wave active, before the
@@ -1083,9 +1116,47 @@ __global__ __launch_bounds__(gqa_waves(F8, NC) * 64) void gqa_decode_kernel(GqaA
         }
       }
 
-      if (cc.i + 1 == cc.i_end) finish_piece(cc);
+      if (cc.i + 1 == cc.i_end && !pair_mode) finish_piece(cc);
       advance(cc);
       slot_k = (slot_k + 1) & (kSlots - 1);
+    }
+  }
+
+  // ---- pair mode: the second half's (m, l, O) to the first, which merges
+  // them and writes the unit's result ---------------------------------------
+  if (pair_mode) {
+    // through the second half's own ring (no tile load is in flight now)
+    constexpr int kXO = 8 * 64 * 16;   // O: 8 blocks x 64 lanes x 16 bytes
+    if (half == 1) {
+#pragma unroll
+      for (int blk = 0; blk < 8; ++blk) *(PD_LDS f32x4*)(ring + (blk * 64 + lane) * 16) = o[0][blk];
+      ((PD_LDS float*)(ring + kXO))[lane] = m_run[0];
+      ((PD_LDS float*)(ring + kXO + 256))[lane] = l_run[0];
+      ((PD_LDS int*)(ring + kXO + 512))[lane] = piece_bad ? 1 : 0;
+    }
+    __syncthreads();
+    if (half == 0 && !idle && r_s.nt > 0) {
+      PD_LDS const char* pb = ring + kWaveLds;
+      const float mb = ((PD_LDS const float*)(pb + kXO))[lane];
+      const float lb = ((PD_LDS const float*)(pb + kXO + 256))[lane];
+      const bool bb = ((PD_LDS const int*)(pb + kXO + 512))[lane] != 0;
+      const float ma = m_run[0];
+      const float mm = fmaxf(ma, mb);
+      const float wa = ma == neg_inf() ? 0.f : fast_exp2((ma - mm) * c);
+      const float wb = mb == neg_inf() ? 0.f : fast_exp2((mb - mm) * c);
+      l_run[0] = l_run[0] * wa + lb * wb;
+#pragma unroll
+      for (int blk = 0; blk < 8; ++blk)
+        o[0][blk] = o[0][blk] * wa + *(PD_LDS const f32x4*)(pb + (blk * 64 + lane) * 16) * wb;
+      m_run[0] = mm;
+      piece_bad = piece_bad || bb;
+      Cursor cu;
+      cu.b = b_s;
+      cu.kvh = kvh_s;
+      cu.p0 = 0;
+      cu.i = cu.i_end = 0;
+      cu.r = r_s;
+      finish_piece(cu);
     }
   }
 
@@ -1138,7 +1209,8 @@ __global__ __launch_bounds__(gqa_waves(F8, NC) * 64) void gqa_decode_kernel(GqaA
   cw.kvh = kvh_s;
   cw.p0 = p0_s;
   cw.r = r_s;
-  while (cw.b < a.B && (sh.last || cw.p0 < sh.g1) && !past_units(cw)) {
+  // (pair mode: the first half answers for the unit)
+  while (cw.b < a.B && (sh.last || cw.p0 < sh.g1) && !past_units(cw) && half == 0) {
     const int hq0 = cw.kvh * G;
     R = V ? cw.r.n * G : G;   // this unit's columns
     // (row, query head) of column n of this unit
@@ -1215,9 +1287,15 @@ __global__ __launch_bounds__(gqa_waves(F8, NC) * 64) void gqa_decode_kernel(GqaA
 // cache, with the fused append or not (AP); one workgroup per compute unit.
 // With one split (whole units) the grid has no more workgroups than units
 // (the kernel's unit mode spreads one unit per wave over them).
+// Pair mode (two waves per unit) when every unit fits two waves of the
+// 4-wave grid, with at most 16 score columns; the rule does not depend on
+// the kernel's waves per workgroup, so the bf16 and FP8 paths take the same
+// mode (and round alike).
 template <int PS, bool AP>
-hipError_t launch_gqa_class(const GqaArgs& a, bool verify, int n_wg, hipStream_t stream) {
-  const int64_t units = (int64_t)a.B * a.Hkv;
+hipError_t launch_gqa_class(const GqaArgs& args, bool verify, int n_wg, hipStream_t stream) {
+  const int64_t units = (int64_t)args.B * args.Hkv;
+  GqaArgs a = args;
+  a.pair = (a.S == 1 && 2 * units <= 4 * (int64_t)n_wg && (!verify || a.qlen * a.G <= 16)) ? 1 : 0;
   const dim3 grid((unsigned)(a.S == 1 ? std::max<int64_t>(1, std::min<int64_t>(n_wg, units)) : n_wg));
   const dim3 grid8 = grid;
   const dim3 block(gqa_waves(false, 1) * 64), block8(gqa_waves(true, 1) * 64);

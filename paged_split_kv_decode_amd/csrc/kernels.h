@@ -43,6 +43,9 @@ struct GqaArgs {
   int32_t p_shift;   // log2(P) when the page size is a power of two, else 0
   int32_t S;         // split cap: no (request, kv head) is cut into more pieces
   int32_t partials;  // 1: always write workspace partials (never O / LSE)
+  int32_t pair;      // 1 (set by the launcher; one split, at most 16 columns, few units):
+                     // every unit is streamed by two waves of one workgroup, which merge
+                     // their halves through LDS
   float* ws;         // [B * qlen, Hq, S, D + 1] when S > 1 or partials
   uint16_t* out;
   int32_t o_sb, o_sh;

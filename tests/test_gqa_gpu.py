@@ -240,6 +240,34 @@ def test_one_split_unit_per_wave_boundary(pd, fp8):
                     o_atol=5e-2 if fp8 else 2e-2, what=f"one split, fp8={fp8}")
 
 
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+def test_one_split_pair_mode_boundary(pd, fp8):
+    """One split with two waves per unit (at most 2 units per compute unit)
+    and just past that bound (one wave per unit): both agree with the oracle
+    on sampled requests, including units of one tile (the second wave of the
+    pair streams nothing), empty requests and a window."""
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    b_pair = 2 * n_cu // 8                           # Hkv = 8: 2 units per CU
+    lens = np.random.default_rng(5).integers(1, 400, size=b_pair + 1)
+    lens[[0, 3, b_pair]] = [0, 1, 33]               # empty, one key, two tiles
+    lens[1:3] = [31, 32]                             # one tile
+    for nb, window in ((b_pair, 0), (b_pair + 1, 0), (b_pair, 40)):
+        w = gqa_workload("gqa_sinks", fixed_lens=lens[:nb], seed_offset=43 + fp8, pool="tight",
+                         window=window)
+        vals = w.values("cuda", poison=True, fp8=fp8)
+        bt, sl = _dev(w)
+        scales = dict(k_scale=vals.get("k_scale"), v_scale=vals.get("v_scale")) if fp8 else {}
+        out, lse = pd.paged_verify_gqa(vals["q"], vals["kv"], bt, sl, 1, w.sm_scale,
+                                       sinks=vals["sinks"], window=w.window, num_kv_splits=1,
+                                       **scales)
+        torch.cuda.synchronize()
+        assert torch.all(out[0].float() == 0) and torch.all(torch.isneginf(lse[0]))
+        sample = [0, 1, 2, 3, 4, nb // 2, nb - 1]
+        O, L = oracle_gqa(w, vals, sample)
+        check_attention(out[sample], lse[sample], O, L, o_atol=5e-2 if fp8 else 2e-2,
+                        what=f"one split B={nb} window={window} fp8={fp8}")
+
+
 def test_repeated_calls_are_bitwise_deterministic(pd):
     w = gqa_workload("gqa_skewed", batch=16, loguniform=(16, 5000), zero_lens=1)
     vals = w.values("cuda", poison=True)
