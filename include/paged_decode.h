@@ -34,9 +34,9 @@
  *   capacity (max_blocks * page_size) is clamped to it, and an attended
  *   block-table entry outside [0, num_pages) is never dereferenced: the
  *   affected (request, head) outputs are written as NaN instead.
- * - sm_scale must be finite and > 0 (the GQA kernel keeps its running
- *   maximum in unscaled scores, which orders them only for a positive
- *   scale); any other value returns PD_ERR_INVALID.
+ * - sm_scale must be finite and > 0 (the GQA kernel keeps its softmax
+ *   reference, a running maximum, in unscaled scores, which orders them only
+ *   for a positive scale); any other value returns PD_ERR_INVALID.
  * - bf16 values are IEEE binary32 truncated to their upper 16 bits (round to
  *   nearest even on output); FP8 is OCP E4M3FN.
  *
@@ -239,8 +239,8 @@ PD_API int paged_decode_gqa(const void* q, int64_t q_stride_b, int64_t q_stride_
  *              each has its own scale.
  * k_scale,     device fp32: one value (scale_per_head = 0) or [Hkv]
  * v_scale      (scale_per_head = 1); NULL means 1.  Ignored for bf16.  Each
- *              scale must be finite and > 0 (the running max is kept in
- *              unscaled scores).
+ *              scale must be finite and > 0 (the softmax reference, a
+ *              running maximum, is kept in unscaled scores).
  * real_seq_lens [B] int32 or NULL.
  * out          [B*qlen, Hq, D] bf16, strides (o_stride_row, o_stride_h, 1).
  * lse          [B*qlen, Hq] fp32 with row stride lse_stride_row, or NULL.

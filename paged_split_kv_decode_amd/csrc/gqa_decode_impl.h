@@ -20,15 +20,18 @@
 //   (`global_load_lds_dwordx4`, 1 KB each, HBM -> LDS with no VGPR staging,
 //   non-temporal: the cache is read once) while it computes tile k.  The physical page of
 //   each tile row comes from the block table through scalar loads made one
-//   tile ahead of their use, so their latency is hidden.  No workgroup
-//   barrier exists anywhere: the waves share nothing but the CU.
+//   tile ahead of their use, so their latency is hidden.  The waves share
+//   nothing but the CU (one workgroup barrier exists, in pair mode below).
 // * Where a wave's share cuts a unit, each piece is a split: the wave writes
 //   its fp32 partial (O / l, lse) to the piece's slot, and the merge kernel
 //   combines them.  With the split cap S >= 2 the share size is raised
 //   until no unit spans more than S waves; the wave that holds a unit's
-//   first tile marks the unit's unused slots with lse = -inf.  With S == 1
-//   shares are rounded to whole units and the wave writes O and LSE
-//   directly.
+//   first tile marks the end of the unit's slot list.  With S == 1 shares
+//   are rounded to whole units and the wave writes O and LSE directly.
+// * With S == 1 and no more units than waves, each wave takes one unit
+//   without scanning the batch (unit mode); with at most two units per
+//   compute unit, two waves of a workgroup take half a unit each and merge
+//   through LDS (pair mode).
 // * Scores S^T[token, head] = K . Q^T on v_mfma_f32_16x16x32_bf16 with the
 //   G query heads of the kv head in the N dimension (G <= 16, zero-padded).
 //   Online softmax in fp32 with exp2 and a reference max in unscaled logits

@@ -29,16 +29,16 @@
 //   softmax scale and the output.
 // * Scores: each wave owns 32 rows; S^T[token, row] = K . Q^T with
 //   v_mfma_f32_32x32x16_bf16, its query fragment (32 x 576 bf16, 144 VGPRs)
-//   held for the whole piece, K fragments read from LDS a few steps ahead.
+//   held for the whole piece, K fragments read from LDS a few steps ahead,
+//   the score accumulator in arch VGPRs (the MFMA's asm form).
 // * Product: each wave owns 128 of the 512 output dims for all 128 rows, so
 //   every V^T fragment (ds_read_b64_tr_b16 from the same tile) feeds four
 //   MFMAs.  The probabilities go through LDS: a wave's packed P of a key
 //   step is, lane by lane, the B operand every wave needs for its rows.  The
-//   output accumulator (128 dims x 128 rows fp32) takes all 256 AGPRs but
-//   one block, which is parked in VGPRs while the scores use its AGPRs.
-// * Iteration k runs the score MFMAs of tile k interleaved with the product
-//   of tile k-1, so the dependent score chain always has independent MFMAs
-//   between its steps; one barrier per tile.
+//   output accumulator (128 dims x 128 rows fp32) takes all 256 AGPRs.
+// * Iteration k runs the score MFMAs of tile k and the product of tile k-1:
+//   FP8 interleaves the two, bf16 runs the product after the score chain,
+//   interleaved with tile k's softmax; one barrier per tile.
 // * Online softmax in the exp2 domain (x = score * sm_scale * log2 e) with a
 //   fixed per-row reference: a row's reference max is its first non-empty
 //   tile's max and is never rescaled, so no vector instruction ever touches
@@ -479,10 +479,10 @@ void mla_verify_kernel(MlaArgs a) {
   #pragma unroll
       for (int e = 0; e < 16; ++e) o[i][e] = 0.f;
 
-    // Iteration k computes the scores of tile k interleaved with the P.V
-    // product of tile k-1 (whose probabilities every wave published in
-    // iteration k-1), so the dependent score chain always has independent
-    // MFMAs between its steps.  Iteration 0 multiplies the zeroed view of
+    // Iteration k computes the scores of tile k and the P.V product of tile
+    // k-1 (whose probabilities every wave published in iteration k-1), FP8
+    // interleaving the two, bf16 running the product after the score chain
+    // with tile k's softmax.  Iteration 0 multiplies the zeroed view of
     // "tile -1" by zeroed probabilities; iteration n computes throw-away
     // scores on stale data to finish tile n-1's product.  Ring: tile t in
     // slot t mod 4; tile k+2 is issued at iteration k into the slot of tile
@@ -596,6 +596,7 @@ void mla_verify_kernel(MlaArgs a) {
       // fragment v = 4 s + d lives in vf[v & 1]; P^T fragment (r, s) in pf[r].
       {
         constexpr int kKAhead = FP8 ? kKAheadFp8 : kKAheadBf16;
+        // kf: bf16 K fragments; vf, pf: the FP8 path's V^T and P^T fragments
         bf16x8 kf[kKAhead], vf[2], pf[4];
         u32x2 kw[kKAhead];   // FP8: raw K codes, a few steps ahead
         if constexpr (FP8) {
