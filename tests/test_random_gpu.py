@@ -3,7 +3,8 @@
 Each case draws its own shapes from a fixed seed: batch, head counts and
 group size, verify tokens, page size (every power-of-two class), lengths
 (zero, shorter than qlen, within one page, ragged multi-tile), real lengths,
-window, sinks, bf16 or FP8 cache and split count.  The hand-written tests
+window, sinks, bf16 or FP8 cache and split count, with up to 64 score
+columns per kv head on the verify path.  The hand-written tests
 pin each feature alone; these check that the features compose.  Every call
 goes through the C ABI; never-attended cache slots are NaN-poisoned.
 """
@@ -60,6 +61,41 @@ def test_gqa_random(pd, seed):
     S = c["S"]
     S = pd.gqa_split_cap(w.B, w.Hkv, max(int(w.seq_lens.max()), 1), w.window) if S == "cap" else int(S)
     real = None if w.real_seq_lens is None else torch.from_numpy(w.real_seq_lens).cuda()
+    scales = dict(k_scale=vals["k_scale"], v_scale=vals["v_scale"]) if c["fp8"] else {}
+    out, lse = pd.paged_verify_gqa(vals["q"], vals["kv"], torch.from_numpy(w.block_table).cuda(),
+                                   torch.from_numpy(w.seq_lens).cuda(), w.qlen, w.sm_scale,
+                                   sinks=vals["sinks"], window=w.window, real_seq_lens=real,
+                                   num_kv_splits=S, **scales)
+    torch.cuda.synchronize()
+    O, L = oracle_gqa(w, vals)
+    what = (f"seed={seed} B={w.B} Hq={w.Hq} Hkv={w.Hkv} qlen={w.qlen} P={w.P} "
+            f"window={w.window} fp8={c['fp8']} S={S} lens={list(w.seq_lens)}")
+    check_attention(out, lse, O, L, o_atol=O_ATOL_FP8 if c["fp8"] else 2e-2, what=what)
+
+
+def _gqa_wide_case(seed):
+    """Verify with 17 to 64 score columns (2 or 4 column groups)."""
+    rng = np.random.default_rng(9300 + seed)
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    qlen, G = [(2, 16), (3, 8), (4, 8), (8, 8), (5, 4), (16, 4), (4, 16), (9, 4)][seed % 8]
+    B = int(rng.integers(1, 6))
+    lens = _lengths(rng, B, 600)
+    real = np.maximum(lens - rng.integers(0, 4, size=B), 0)
+    return dict(fixed_lens=lens, qlen=qlen, fixed_real=real, heads=(G * Hkv, Hkv),
+                window=int(rng.choice([0, 0, 9, 100])), page_size=int(rng.choice(PAGES)),
+                fp8=bool(rng.random() < 0.4), S=rng.choice(["cap", 1, 2, 4]))
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_gqa_random_wide(pd, seed):
+    c = _gqa_wide_case(seed)
+    w = gqa_workload("gqa_verify", fixed_lens=c["fixed_lens"], qlen=c["qlen"],
+                     fixed_real=c["fixed_real"], heads=c["heads"], window=c["window"],
+                     page_size=c["page_size"], pool="tight", seed_offset=100 + seed)
+    vals = w.values("cuda", poison=True, fp8=c["fp8"])
+    S = c["S"]
+    S = pd.gqa_split_cap(w.B, w.Hkv, max(int(w.seq_lens.max()), 1), w.window) if S == "cap" else int(S)
+    real = torch.from_numpy(w.real_seq_lens).cuda()
     scales = dict(k_scale=vals["k_scale"], v_scale=vals["v_scale"]) if c["fp8"] else {}
     out, lse = pd.paged_verify_gqa(vals["q"], vals["kv"], torch.from_numpy(w.block_table).cuda(),
                                    torch.from_numpy(w.seq_lens).cuda(), w.qlen, w.sm_scale,
