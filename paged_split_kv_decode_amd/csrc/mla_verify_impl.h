@@ -25,8 +25,8 @@
 //   fill the request queue and stall the wave).  FP8 fragments are read
 //   from the FP8 tile itself (K with 8-byte reads, V^T with
 //   ds_read_b64_tr_b8) and converted in registers, exactly
-//   (v_cvt_scalef32_pk_bf16_fp8, scale 1); k_scale is folded into the
-//   softmax scale and the output.
+//   (v_cvt_scalef32_pk_bf16_fp8, scale 1); k_scale multiplies the raw
+//   scores and the output.
 // * Scores: each wave owns 32 rows; S^T[token, row] = K . Q^T with
 //   v_mfma_f32_32x32x16_bf16, its query fragment (32 x 576 bf16, 144 VGPRs)
 //   held for the whole piece, K fragments read from LDS a few steps ahead,
@@ -243,12 +243,16 @@ void mla_verify_kernel(MlaArgs a) {
     const int h_row = row_ok ? my_row % a.H : 0;
     const int hi_row = row_ok ? max(min(L - a.qlen + 1 + t_row, Lr), 0) : 0;
     const int hi_blk = __builtin_amdgcn_readfirstlane(block_hi(L, Lr, rb));
+    // the wave's smallest row limit: tiles below it need no causal mask
+    const int hi_wmin = __builtin_amdgcn_readfirstlane(-wave_max(-hi_row));
 
     float kscale = 1.f;
     if constexpr (FP8) {
       if (a.k_scale != nullptr) kscale = a.k_scale[0];
     }
-    const float c = a.scale_log2 * kscale;   // log2-domain scale of raw scores
+    // log2-domain scale of the scores: x = K . q (FP8: codes . q times
+    // k_scale, so both caches give the same x), logit = x * c
+    const float c = a.scale_log2;
 
     // ---- Q fragment: B operand of S^T = K Q^T (32 rows x 576 dims) --------
     // A row past the request's rows reads the request's first row instead:
@@ -677,9 +681,11 @@ void mla_verify_kernel(MlaArgs a) {
           __builtin_amdgcn_sched_barrier(0);
         }
         if (kLateFetch && k + 3 < n) pg_next = fetch(tb + k + 3);
+        // The softmax works on the raw scores: max(x) * c is max(x * c) for
+        // c > 0, and each probability takes one fma, exp2(x * c - m_ref).
         float x[16];
   #pragma unroll
-        for (int e = 0; e < 16; ++e) x[e] = sacc[e] * c;
+        for (int e = 0; e < 16; ++e) x[e] = FP8 ? sacc[e] * kscale : sacc[e];
         if constexpr (!FP8) {
           // bf16: tile k-1's 32 products with tile k's softmax
           // interleaved by hand, one product and a slice of the softmax per
@@ -694,6 +700,7 @@ void mla_verify_kernel(MlaArgs a) {
           u32x4 pw0 = {0, 0, 0, 0}, pw1 = {0, 0, 0, 0};
           // V^T fragment v = 4 s + d in vr[v % 2], P^T (r, s) in pr[r]
           bf16x8 vr[2], pr[4];
+          const bool mask_tile = tok0 + kTileTokens > hi_wmin;   // wave-uniform
           vr[0] = vread(0, 0);
           vr[1] = vread(0, 1);
   #pragma unroll
@@ -706,24 +713,26 @@ void mla_verify_kernel(MlaArgs a) {
             if (s == 0 && d == 3) pr[r] = pread(r, 1);
             if (j < 2) {
               // causal limit of this lane's row: token tok0 + 8 (e / 4) + 4 g2 + e % 4 < hi_row
+              if (mask_tile) {
   #pragma unroll
-              for (int e = 8 * j; e < 8 * j + 8; ++e) {
-                const int tok = tok0 + 8 * (e >> 2) + 4 * g2 + (e & 3);
-                x[e] = tok >= hi_row ? neg_inf() : x[e];
+                for (int e = 8 * j; e < 8 * j + 8; ++e) {
+                  const int tok = tok0 + 8 * (e >> 2) + 4 * g2 + (e & 3);
+                  x[e] = tok >= hi_row ? neg_inf() : x[e];
+                }
               }
             } else if (j == 2) {
               m_a = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
             } else if (j == 3) {
               const float m_b = fmaxf(fmaxf(fmaxf(x[8], x[9]), fmaxf(x[10], x[11])),
                                       fmaxf(fmaxf(x[12], x[13]), fmaxf(x[14], x[15])));
-              mt = max_xor32(fmaxf(m_a, m_b));
+              mt = max_xor32(fmaxf(m_a, m_b)) * c;
             } else if (j == 4) {
               // first non-empty tile of the row: its max becomes the reference
               m_ref_n = m_ref == neg_inf() ? mt : m_ref;
               ovf_n = mt - m_ref_n > kRefHeadroomLog2;   // false while -inf
               mref = m_ref_n == neg_inf() ? 0.f : m_ref_n;
             } else if (j >= 5 && j < 21) {
-              p[j - 5] = fast_exp2(x[j - 5] - mref);
+              p[j - 5] = fast_exp2(__builtin_fmaf(x[j - 5], c, -mref));
               lsum += p[j - 5];
             } else if (j == 21) {
               pw0 = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
@@ -748,7 +757,7 @@ void mla_verify_kernel(MlaArgs a) {
           if (!live) break;
 
           // causal limit of this lane's row: token tok0 + 8j + 4 g2 + i < hi_row
-          if (tok0 + kTileTokens > hi_row) {
+          if (tok0 + kTileTokens > hi_wmin && tok0 + kTileTokens > hi_row) {
   #pragma unroll
             for (int e = 0; e < 16; ++e) {
               const int tok = tok0 + 8 * (e >> 2) + 4 * g2 + (e & 3);
@@ -760,7 +769,7 @@ void mla_verify_kernel(MlaArgs a) {
           float mt = x[0];
   #pragma unroll
           for (int e = 1; e < 16; ++e) mt = fmaxf(mt, x[e]);
-          mt = max_xor32(mt);
+          mt = max_xor32(mt) * c;
           m_seen = fmaxf(m_seen, mt);
           // first non-empty tile of the row: take its max as the reference (the
           // accumulator and l are still exactly 0, so nothing needs rescaling)
@@ -771,7 +780,7 @@ void mla_verify_kernel(MlaArgs a) {
           float lsum = 0.f;   // summed as on the bf16 path, so the two round alike
   #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            p[e] = fast_exp2(x[e] - mref);
+            p[e] = fast_exp2(__builtin_fmaf(x[e], c, -mref));
             lsum += p[e];
           }
           l_run += lsum;
