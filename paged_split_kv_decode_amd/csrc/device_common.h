@@ -93,10 +93,12 @@ __device__ __forceinline__ float readlane(float v, int lane) {
 }
 
 // fp32 -> bf16 bits with round-to-nearest-even (v_cvt_pk_bf16_f32 on gfx950).
+// (converted as a pair: one v_cvt_pk_bf16_f32; two scalar casts became two
+// conversions, a shift and an or)
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo;
-  __bf16 b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {

@@ -646,22 +646,29 @@ void mla_verify_kernel(MlaArgs a) {
 #define PD_MFMA_S(PRE, C, POST)                                                         \
   asm volatile(PRE "v_mfma_f32_32x32x16_bf16 %0, %1, %2, " C POST                      \
                : "+v"(sacc) : "v"(kop), "v"(qf[kk]))
+            // (the first step only writes the accumulator: the previous
+            // tile's scores are dead by then, so their registers can hold
+            // the softmax's copy without a move)
+#define PD_MFMA_S0(PRE)                                                                 \
+  asm volatile(PRE "v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"                            \
+               : "=&v"(sacc) : "v"(kop), "v"(qf[kk]))
             if constexpr (FP8) {
               if (kk == 0)
-                PD_MFMA_S("s_nop 2\n\t", "0", "");
+                PD_MFMA_S0("s_nop 2\n\t");
               else if (kk + 1 < kKSteps)
                 PD_MFMA_S("s_nop 2\n\t", "%0", "");
               else
                 PD_MFMA_S("s_nop 2\n\t", "%0", "\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
             } else {
               if (kk == 0)
-                PD_MFMA_S("", "0", "");
+                PD_MFMA_S0("");
               else if (kk + 1 < kKSteps)
                 PD_MFMA_S("", "%0", "");
               else
                 PD_MFMA_S("", "%0", "\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
             }
 #undef PD_MFMA_S
+#undef PD_MFMA_S0
           }
           if (FP8 && kk < 32) {
             const int s = kk / 16, idx = kk % 16, d = idx >> 2, r = idx & 3, v = 4 * s + d;
@@ -721,10 +728,14 @@ void mla_verify_kernel(MlaArgs a) {
                 }
               }
             } else if (j == 2) {
-              m_a = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+              // (chains, which the compiler turns into three-input maxima)
+              m_a = x[0];
+  #pragma unroll
+              for (int e = 1; e < 8; ++e) m_a = fmaxf(m_a, x[e]);
             } else if (j == 3) {
-              const float m_b = fmaxf(fmaxf(fmaxf(x[8], x[9]), fmaxf(x[10], x[11])),
-                                      fmaxf(fmaxf(x[12], x[13]), fmaxf(x[14], x[15])));
+              float m_b = x[8];
+  #pragma unroll
+              for (int e = 9; e < 16; ++e) m_b = fmaxf(m_b, x[e]);
               mt = max_xor32(fmaxf(m_a, m_b)) * c;
             } else if (j == 4) {
               // first non-empty tile of the row: its max becomes the reference
