@@ -112,6 +112,42 @@ __device__ __forceinline__ int tile_off(int c, int r16) {
 // The fp8 ring (before dequantisation) keeps chunk-column-major pages: fp8
 // chunk c8 (16 bytes) of row r16 at slot 16 c8 + r16.
 
+// Load j of a wave's share of a tile (global_load_lds_dwordx4: 16 bytes per
+// lane): global address base (+ voff) + j kG, LDS address dst + j kL.  The
+// instruction's immediate offset (j kG) moves both addresses, so M0 gets
+// dst + j (kL - kG), in the same statement.  j is a constant once the
+// caller's loop is unrolled, so the switch folds to one statement and a load
+// costs no address arithmetic.  kLaneAddr: base is the lane's own 64-bit
+// address; otherwise base is wave-uniform and voff the lane's byte offset.
+// The s_nop covers the M0-write -> LDS-DMA hazard.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+template <int kG, int kL, bool kLaneAddr>
+__device__ __forceinline__ void dma_step(int j, const char* base, uint32_t voff, uint32_t dst) {
+  static_assert(kL >= kG, "M0 takes the LDS step less the global step");
+  if constexpr (!kLaneAddr) base = (const char*)scalar_ptr(base);
+  switch (j) {
+#define PD_DMA_CASE(J)                                                                           \
+  case J:                                                                                        \
+    if constexpr (kLaneAddr)                                                                     \
+      asm volatile("s_add_u32 m0, %0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:%3"  \
+                   :                                                                             \
+                   : "s"(dst), "v"(base), "i"((J) * (kL - kG)), "i"((J) * kG)                    \
+                   : "memory", "m0", "scc");                                                     \
+    else                                                                                         \
+      asm volatile("s_add_u32 m0, %0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 offset:%4"   \
+                   :                                                                             \
+                   : "s"(dst), "v"(voff), "s"(base), "i"((J) * (kL - kG)), "i"((J) * kG)         \
+                   : "memory", "m0", "scc");                                                     \
+    break;
+    PD_DMA_CASE(0) PD_DMA_CASE(1) PD_DMA_CASE(2) PD_DMA_CASE(3) PD_DMA_CASE(4)
+    PD_DMA_CASE(5) PD_DMA_CASE(6) PD_DMA_CASE(7) PD_DMA_CASE(8)
+#undef PD_DMA_CASE
+    default: break;
+  }
+}
+#pragma clang diagnostic pop
+
 
 // PC: the page class, 1, 2, 4 or 8 (the page size), 16 (every power-of-two
 // page of 16 tokens or more; log2 of the size in a.p_shift) or 0 (every
@@ -350,14 +386,16 @@ void mla_verify_kernel(MlaArgs a) {
     constexpr int kLStep = FP8 ? 1024 : 2048;  // LDS bytes per instruction
     const int g_first = FP8 ? 64 * i0 : 0;
     const int l_first = FP8 ? i0 * 1024 : (wave & 1) * 1024;
-    // A tile's loads for this wave, validated: load j reads base + gstep j
-    // (+ voff, PC = 16) into LDS address dst + j kLStep (gstep = 0 for a page
-    // that is not read).  PC < 16: base is the lane's own address.
+    // A tile's loads for this wave, validated: load j reads base + j kGStep
+    // (+ voff, PC = 16) into LDS address dst + j kLStep.  PC < 16: base is
+    // the lane's own address.  A page that is not read comes from the first
+    // bytes of q (one query row is 1152 bytes, past the last load's end at
+    // 8 * 128 + 16 bytes), whose values no product sees.
+    static_assert(kLoadsPerWave <= 9 && (kLoadsPerWave - 1) * kGStep + 16 <= kRowBytes, "load steps stay inside one q row");
     struct TileLoads {
       const char* base;
       uint32_t voff;
       uint32_t dst;
-      int gstep;
     };
     const uint32_t num_pages = (uint32_t)a.num_pages;
     auto prepare = [&](const TilePages& tp, int slot) {
@@ -376,7 +414,6 @@ void mla_verify_kernel(MlaArgs a) {
         const int slot0 = (my_page & 1) ? tp.slot0[1] : tp.slot0[0];
         tl.base = ok ? kv + (int64_t)my_pid * sp_bytes + slot0 * st_bytes + g_first : (const char*)a.q;
         tl.voff = ok ? lane_off : 0u;
-        tl.gstep = ok ? kGStep : 0;
       } else {
         // every entry this wave read is of an attended page if at or below
         // the block's last page; general pages: candidates past the page of
@@ -413,21 +450,12 @@ void mla_verify_kernel(MlaArgs a) {
         const bool ok = tp.first + cand <= last_page && (uint32_t)id < num_pages;
         const uint32_t chunk = FP8 ? 16u * (uint32_t)(lane >> 4) + (uint32_t)g_first
                                    : 16u * (uint32_t)((lane & 7) ^ (lane >> 3) ^ (wave & 1));
-        // bf16: a lane whose page is not read steps through the first bytes
-        // of q (at least 32 rows of 1152 bytes), so the step stays
-        // wave-uniform, one register less (measured faster for bf16 only)
         tl.base = ok ? kv + (int64_t)id * sp_bytes + slot * st_bytes + chunk : (const char*)a.q;
         tl.voff = 0u;
-        tl.gstep = (FP8 && !ok) ? 0 : kGStep;
       }
       return tl;
     };
-    auto load_one = [&](const TileLoads& tl, int j) {
-      if constexpr (kBigP)
-        global_to_lds_16(tl.base + tl.gstep * j, tl.voff, tl.dst + j * kLStep);
-      else
-        global_to_lds_16_v(tl.base + tl.gstep * j, tl.dst + j * kLStep);
-    };
+    auto load_one = [&](const TileLoads& tl, int j) { dma_step<kGStep, kLStep, !kBigP>(j, tl.base, tl.voff, tl.dst); };
     auto issue = [&](const TilePages& tp, int slot) {
       const TileLoads tl = prepare(tp, slot);
       if (wave < kIssueWaves) {
@@ -631,62 +659,74 @@ void mla_verify_kernel(MlaArgs a) {
           if (k + 2 < n) tl_next = prepare(pg_next, (k + 2) & (NS - 1));
           __builtin_amdgcn_sched_barrier(0);
         }
-  #pragma unroll
-        for (int kk = 0; kk < kKSteps; ++kk) {
-          {
-            bf16x8 kop;
-            if constexpr (FP8) {
-              const u32x2 w = kw[kk % kKAhead];
-              kop = cvt8x8(w[0], w[1]);
-            } else {
-              kop = kf[kk % kKAhead];
-            }
-            // (FP8: 3 wait states after the conversions; last step: 24 before
-            // the vector ALU reads the result)
+        // bf16: the chain in two copies, with and without the next tile's
+        // loads, so no step branches on whether this wave loads (FP8, whose
+        // chain also carries the products, spills registers that way and
+        // branches per load instead).
+        auto chain = [&](auto with_loads) {
+    #pragma unroll
+          for (int kk = 0; kk < kKSteps; ++kk) {
+            {
+              bf16x8 kop;
+              if constexpr (FP8) {
+                const u32x2 w = kw[kk % kKAhead];
+                kop = cvt8x8(w[0], w[1]);
+              } else {
+                kop = kf[kk % kKAhead];
+              }
+              // (FP8: 3 wait states after the conversions; last step: 24 before
+              // the vector ALU reads the result)
 #define PD_MFMA_S(PRE, C, POST)                                                         \
-  asm volatile(PRE "v_mfma_f32_32x32x16_bf16 %0, %1, %2, " C POST                      \
-               : "+v"(sacc) : "v"(kop), "v"(qf[kk]))
-            // (the first step only writes the accumulator: the previous
-            // tile's scores are dead by then, so their registers can hold
-            // the softmax's copy without a move)
+    asm volatile(PRE "v_mfma_f32_32x32x16_bf16 %0, %1, %2, " C POST                      \
+                 : "+v"(sacc) : "v"(kop), "v"(qf[kk]))
+              // (the first step only writes the accumulator: the previous
+              // tile's scores are dead by then, so their registers can hold
+              // the softmax's copy without a move)
 #define PD_MFMA_S0(PRE)                                                                 \
-  asm volatile(PRE "v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"                            \
-               : "=&v"(sacc) : "v"(kop), "v"(qf[kk]))
-            if constexpr (FP8) {
-              if (kk == 0)
-                PD_MFMA_S0("s_nop 2\n\t");
-              else if (kk + 1 < kKSteps)
-                PD_MFMA_S("s_nop 2\n\t", "%0", "");
-              else
-                PD_MFMA_S("s_nop 2\n\t", "%0", "\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
-            } else {
-              if (kk == 0)
-                PD_MFMA_S0("");
-              else if (kk + 1 < kKSteps)
-                PD_MFMA_S("", "%0", "");
-              else
-                PD_MFMA_S("", "%0", "\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
-            }
+    asm volatile(PRE "v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"                            \
+                 : "=&v"(sacc) : "v"(kop), "v"(qf[kk]))
+              if constexpr (FP8) {
+                if (kk == 0)
+                  PD_MFMA_S0("s_nop 2\n\t");
+                else if (kk + 1 < kKSteps)
+                  PD_MFMA_S("s_nop 2\n\t", "%0", "");
+                else
+                  PD_MFMA_S("s_nop 2\n\t", "%0", "\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
+              } else {
+                if (kk == 0)
+                  PD_MFMA_S0("");
+                else if (kk + 1 < kKSteps)
+                  PD_MFMA_S("", "%0", "");
+                else
+                  PD_MFMA_S("", "%0", "\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
+              }
 #undef PD_MFMA_S
 #undef PD_MFMA_S0
+            }
+            if (FP8 && kk < 32) {
+              const int s = kk / 16, idx = kk % 16, d = idx >> 2, r = idx & 3, v = 4 * s + d;
+              o[idx] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[v & 1], pf[r], o[idx], 0, 0, 0);
+              // V^T fragment v is done after its last row group: fetch v + 2
+              if (r == 3 && v + 2 < 8) vf[v & 1] = vread((v + 2) >> 2, (v + 2) & 3);
+              // P^T (r, 0) is done after block d = 3: fetch (r, 1)
+              if (s == 0 && d == 3) pf[r] = pread(r, 1);
+            }
+            if constexpr (FP8) {
+              if (kk + kKAhead < kKSteps) kw[kk % kKAhead] = kread8(kk + kKAhead);
+            } else {
+              if (kk + kKAhead < kKSteps) kf[kk % kKAhead] = kread(kk + kKAhead);
+            }
+            if constexpr (decltype(with_loads)::value) {
+              if (kk % kLoadSpacing == 0 && kk / kLoadSpacing < kLoadsPerWave && (!FP8 || load_next))
+                load_one(tl_next, kk / kLoadSpacing);
+            }
+            __builtin_amdgcn_sched_barrier(0);
           }
-          if (FP8 && kk < 32) {
-            const int s = kk / 16, idx = kk % 16, d = idx >> 2, r = idx & 3, v = 4 * s + d;
-            o[idx] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[v & 1], pf[r], o[idx], 0, 0, 0);
-            // V^T fragment v is done after its last row group: fetch v + 2
-            if (r == 3 && v + 2 < 8) vf[v & 1] = vread((v + 2) >> 2, (v + 2) & 3);
-            // P^T (r, 0) is done after block d = 3: fetch (r, 1)
-            if (s == 0 && d == 3) pf[r] = pread(r, 1);
-          }
-          if constexpr (FP8) {
-            if (kk + kKAhead < kKSteps) kw[kk % kKAhead] = kread8(kk + kKAhead);
-          } else {
-            if (kk + kKAhead < kKSteps) kf[kk % kKAhead] = kread(kk + kKAhead);
-          }
-          if (kk % kLoadSpacing == 0 && kk / kLoadSpacing < kLoadsPerWave && load_next)
-            load_one(tl_next, kk / kLoadSpacing);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+        };
+        if (FP8 || load_next)
+          chain(std::true_type{});
+        else
+          chain(std::false_type{});
         if (kLateFetch && k + 3 < n) pg_next = fetch(tb + k + 3);
         // The softmax works on the raw scores: max(x) * c is max(x * c) for
         // c > 0, and each probability takes one fma, exp2(x * c - m_ref).
