@@ -490,7 +490,8 @@ PD_API int paged_kv_append(const void* src0, int64_t src0_stride_tok, int64_t sr
  * q            [B*qlen, H, Lk] bf16, strides (q_stride_row, q_stride_h, 1).
  * kv           latent cache [num_pages, P, 1, Lk] (a [num_pages*P, 1, Lk]
  *              view is the same memory), element type kv_dtype, strides
- *              (kv_stride_page, kv_stride_tok, -, 1).
+ *              (kv_stride_page, kv_stride_tok, -, 1); each of the two strides
+ *              spans under 4 GiB (PD_ERR_UNSUPPORTED otherwise).
  * k_scale      device fp32 scalar dequantising an FP8 cache (value = code *
  *              k_scale, for K and V alike), or NULL for 1; ignored for bf16.
  * block_table  [B, max_blocks] int32; seq_lens, real_seq_lens [B] int32

@@ -579,6 +579,12 @@ int mla_common(const void* q, int64_t q_stride_row, int64_t q_stride_h, const vo
   if (!aligned16(q) || !aligned16(kv) || q_stride_row % 8 || q_stride_h % 8 ||
       kv_stride_page % kv_align || kv_stride_tok % kv_align)
     return PD_ERR_ALIGN;
+  {
+    // the kernel forms page and token offsets as 32 x 32-bit products
+    const int64_t elem = kv_dtype == PD_KV_BF16 ? 2 : 1;
+    if (kv_stride_page > (int64_t)UINT32_MAX / elem || kv_stride_tok > (int64_t)UINT32_MAX / elem)
+      return PD_ERR_UNSUPPORTED;
+  }
   if (!partials_only && (!aligned16(out) || o_stride_row % 8 || o_stride_h % 8))
     return PD_ERR_ALIGN;
   const int64_t rows = (int64_t)batch * qlen;

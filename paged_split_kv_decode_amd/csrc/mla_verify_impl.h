@@ -311,6 +311,7 @@ void mla_verify_kernel(MlaArgs a) {
     const int elem = FP8 ? 1 : 2;
     const int64_t sp_bytes = a.kv_sp * elem;
     const int64_t st_bytes = a.kv_st * elem;
+    const uint32_t sp32 = (uint32_t)sp_bytes, st32 = (uint32_t)st_bytes;
     const PD_CONST int32_t* bt_row = as_const(a.bt) + (int64_t)b * a.bt_sb;
     // an attended block-table entry of this wave's rows is out of range
     // (combined over the workgroup at the end of the piece)
@@ -320,43 +321,42 @@ void mla_verify_kernel(MlaArgs a) {
     // The entries are only checked when the tile is issued, so the scalar
     // loads stay in flight for a whole iteration.  Page class PC = 16: every
     // page of 16 tokens or more; a 16-row region of a tile then lies inside
-    // one page (entry j: region j, at token slot slot0[j]).  PC < 16: each
-    // issuing wave reads the entries of its own rows' pages only (kCand of
-    // them), and each lane picks its row's page.
+    // one page, and a wave reads the one entry of the region it loads.
+    // PC < 16: each issuing wave reads the entries of its own rows' pages
+    // only (kCand of them), and each lane picks its row's page.
     constexpr bool kGen = PC == 0;
     constexpr bool kBigP = PC >= 16;
     constexpr int kWaveRows = FP8 ? 16 : 8;                 // rows of a tile one issuing wave loads
     // candidate pages of an issuing wave's rows
-    constexpr int kCand = kBigP ? 2 : kGen ? (FP8 ? 6 : 4) : kWaveRows / (PC > 0 ? PC : 1);
+    constexpr int kCand = kBigP ? 1 : kGen ? (FP8 ? 6 : 4) : kWaveRows / (PC > 0 ? PC : 1);
     const int p_shift = kBigP ? a.p_shift : kGen ? 0 : __builtin_ctz(PC > 0 ? PC : 1);
     // hi_blk >= 1 whenever a tile is read
     const int last_page = kGen ? (hi_blk - 1) / a.P : (hi_blk - 1) >> p_shift;
     struct TilePages {
       int id[kCand];
-      bool att[kBigP ? 2 : 1];       // region attended (PC = 16)
-      int slot0[kBigP ? 2 : 1];      // token slot of the region's (PC = 16) or the wave's
-                                     // (general pages) first row
+      bool att;                      // the wave's region is attended (PC = 16)
+      int slot0;                     // token slot of the wave's region's (PC = 16) or the
+                                     // wave's (general pages) first row
       int first;                     // page index of entry 0 (PC < 16)
     };
     auto fetch = [&](int T) {
       TilePages tp;
       if constexpr (kBigP) {
-  #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int tok = 32 * T + 16 * j;
-          tp.att[j] = tok < hi_blk;
-          tp.slot0[j] = tok & ((1 << p_shift) - 1);
-          tp.id[j] = tp.att[j] ? bt_row[tok >> p_shift] : 0;
-        }
+        // the entry of region (wave / waves per page) % 2 only, the one this
+        // wave loads (the other waves check the other region's entry)
+        const int tok = 32 * T + 16 * ((wave / (kIssueWaves / 2)) & 1);
+        tp.att = tok < hi_blk;
+        tp.slot0 = tok & ((1 << p_shift) - 1);
+        tp.id[0] = tp.att ? bt_row[tok >> p_shift] : 0;
       } else {
         // this wave's rows are tile tokens kWaveRows * w .. + kWaveRows - 1
         const int tok = 32 * T + kWaveRows * (wave & (FP8 ? 1 : 3));
         if constexpr (kGen) {
           tp.first = tok / a.P;
-          tp.slot0[0] = tok - tp.first * a.P;
+          tp.slot0 = tok - tp.first * a.P;
         } else {
           tp.first = tok >> p_shift;
-          tp.slot0[0] = 0;
+          tp.slot0 = 0;
         }
   #pragma unroll
         for (int c = 0; c < kCand; ++c) tp.id[c] = bt_row[min(tp.first + c, last_page)];
@@ -402,24 +402,19 @@ void mla_verify_kernel(MlaArgs a) {
       TileLoads tl;
       tl.dst = lds_addr(lds + slot * kRingTile + my_page * (FP8 ? kPageRegion8 : kPageRegion) + l_first);
       if constexpr (kBigP) {
-        bool pok[2];
-  #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const bool inr = (uint32_t)tp.id[j] < num_pages;
-          bad |= tp.att[j] && !inr;
-          pok[j] = tp.att[j] && inr;
-        }
-        const bool ok = (my_page & 1) ? pok[1] : pok[0];
-        const int my_pid = (my_page & 1) ? tp.id[1] : tp.id[0];
-        const int slot0 = (my_page & 1) ? tp.slot0[1] : tp.slot0[0];
-        tl.base = ok ? kv + (int64_t)my_pid * sp_bytes + slot0 * st_bytes + g_first : (const char*)a.q;
+        const bool inr = (uint32_t)tp.id[0] < num_pages;
+        bad |= tp.att && !inr;
+        const bool ok = tp.att && inr;
+        // 32 x 32-bit products (the host keeps both strides below 4 GiB)
+        tl.base = ok ? kv + (uint64_t)(uint32_t)tp.id[0] * sp32 + (uint64_t)(uint32_t)tp.slot0 * st32 + g_first
+                     : (const char*)a.q;
         tl.voff = ok ? lane_off : 0u;
       } else {
         // every entry this wave read is of an attended page if at or below
         // the block's last page; general pages: candidates past the page of
         // the wave's last row are read (inside the attended pages) but are
         // not this wave's, so they are neither used nor checked here
-        const int n_cand = kGen ? (tp.slot0[0] + kWaveRows - 1) / a.P + 1 : kCand;
+        const int n_cand = kGen ? (tp.slot0 + kWaveRows - 1) / a.P + 1 : kCand;
         if (wave < kIssueWaves) {
   #pragma unroll
           for (int c = 0; c < kCand; ++c)
@@ -432,7 +427,7 @@ void mla_verify_kernel(MlaArgs a) {
         const int row = FP8 ? row8 : (lane >> 3);
         int cand, slot;
         if constexpr (kGen) {
-          const int rr = tp.slot0[0] + row;
+          const int rr = tp.slot0 + row;
           cand = rr / a.P;
           slot = rr - cand * a.P;
         } else {

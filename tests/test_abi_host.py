@@ -289,6 +289,11 @@ def test_mla_argument_checks_happen_before_any_hip_call():
     assert _mla(out=FAKE + 2) == PD_ERR_ALIGN
     assert _mla(dt=1, st=576 + 8) == PD_ERR_ALIGN              # fp8 rows need 16 B
     assert _mla(S=2) == PD_ERR_WORKSPACE
+    # page and token strides span under 4 GiB (32 x 32-bit offsets in the kernel)
+    assert _mla(sp=1 << 31) == PD_ERR_UNSUPPORTED                # 4 GiB of bf16
+    assert _mla(sp=(1 << 31) - 8, S=2) == PD_ERR_WORKSPACE     # passes the stride check, launches nothing
+    assert _mla(dt=1, sp=1 << 32) == PD_ERR_UNSUPPORTED          # 4 GiB of fp8 codes
+    assert _mla(st=1 << 31) == PD_ERR_UNSUPPORTED
 
 
 def test_merge_argument_checks():
