@@ -710,6 +710,17 @@ void mla_verify_kernel(MlaArgs a) {
               if (kk + kKAhead < kKSteps) kw[kk % kKAhead] = kread8(kk + kKAhead);
             } else {
               if (kk + kKAhead < kKSteps) kf[kk % kKAhead] = kread(kk + kKAhead);
+              // the product's first V^T and P^T fragments (tile k-1), read
+              // in the last score steps, past the chain's last K read, so
+              // they have landed when the products start
+              if (kk == kKSteps - 5) {
+                vf[0] = vread(0, 0);
+                vf[1] = vread(0, 1);
+              } else if (kk == kKSteps - 4 || kk == kKSteps - 3) {
+                const int r0 = 2 * (kk - (kKSteps - 4));
+                pf[r0] = pread(r0, 0);
+                pf[r0 + 1] = pread(r0 + 1, 0);
+              }
             }
             if constexpr (decltype(with_loads)::value) {
               if (kk % kLoadSpacing == 0 && kk / kLoadSpacing < kLoadsPerWave && (!FP8 || load_next))
@@ -741,12 +752,9 @@ void mla_verify_kernel(MlaArgs a) {
           float p[16];
           u32x4 pw0 = {0, 0, 0, 0}, pw1 = {0, 0, 0, 0};
           // V^T fragment v = 4 s + d in vr[v % 2], P^T (r, s) in pr[r]
-          bf16x8 vr[2], pr[4];
+          // (the first ones read in the score loop)
+          bf16x8 vr[2] = {vf[0], vf[1]}, pr[4] = {pf[0], pf[1], pf[2], pf[3]};
           const bool mask_tile = tok0 + kTileTokens > hi_wmin;   // wave-uniform
-          vr[0] = vread(0, 0);
-          vr[1] = vread(0, 1);
-  #pragma unroll
-          for (int r = 0; r < 4; ++r) pr[r] = pread(r, 0);
   #pragma unroll
           for (int j = 0; j < 32; ++j) {
             const int s = j / 16, idx = j % 16, d = idx >> 2, r = idx & 3, v = 4 * s + d;
