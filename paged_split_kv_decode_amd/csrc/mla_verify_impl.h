@@ -25,8 +25,8 @@
 //   fill the request queue and stall the wave).  FP8 fragments are read
 //   from the FP8 tile itself (K with 8-byte reads, V^T with
 //   ds_read_b64_tr_b8) and converted in registers, exactly
-//   (v_cvt_scalef32_pk_bf16_fp8, scale 1); k_scale multiplies the raw
-//   scores and the output.
+//   (v_cvt_scalef32_pk_bf16_fp8, scale 1); k_scale goes into the
+//   softmax scale and the output.
 // * Scores: each wave owns 32 rows; S^T[token, row] = K . Q^T with
 //   v_mfma_f32_32x32x16_bf16, its query fragment (32 x 576 bf16, 144 VGPRs)
 //   held for the whole piece, K fragments read from LDS a few steps ahead,
@@ -658,19 +658,24 @@ void mla_verify_kernel(MlaArgs a) {
         // loads, so no step branches on whether this wave loads (FP8, whose
         // chain also carries the products, spills registers that way and
         // branches per load instead).
+        // FP8: step kk's K fragment is converted one step ahead, right after
+        // step kk-1's score MFMA, into the other of two registers (never the
+        // one the MFMA in flight reads)
+        bf16x8 kc[2];
+        if constexpr (FP8) kc[0] = cvt8x8(kw[0][0], kw[0][1]);
         auto chain = [&](auto with_loads) {
     #pragma unroll
           for (int kk = 0; kk < kKSteps; ++kk) {
             {
               bf16x8 kop;
-              if constexpr (FP8) {
-                const u32x2 w = kw[kk % kKAhead];
-                kop = cvt8x8(w[0], w[1]);
-              } else {
+              if constexpr (FP8)
+                kop = kc[kk & 1];
+              else
                 kop = kf[kk % kKAhead];
-              }
-              // (FP8: 3 wait states after the conversions; last step: 24 before
-              // the vector ALU reads the result)
+              // (FP8: 3 wait states after the conversions: the previous step's
+              // product MFMA and K read and one s_nop, or an s_nop 2 where the
+              // previous step has neither; last step: 24 before the vector
+              // ALU reads the result)
 #define PD_MFMA_S(PRE, C, POST)                                                         \
     asm volatile(PRE "v_mfma_f32_32x32x16_bf16 %0, %1, %2, " C POST                      \
                  : "+v"(sacc) : "v"(kop), "v"(qf[kk]))
@@ -683,6 +688,8 @@ void mla_verify_kernel(MlaArgs a) {
               if constexpr (FP8) {
                 if (kk == 0)
                   PD_MFMA_S0("s_nop 2\n\t");
+                else if (kk <= 32)
+                  PD_MFMA_S("s_nop 0\n\t", "%0", "");
                 else if (kk + 1 < kKSteps)
                   PD_MFMA_S("s_nop 2\n\t", "%0", "");
                 else
@@ -697,6 +704,14 @@ void mla_verify_kernel(MlaArgs a) {
               }
 #undef PD_MFMA_S
 #undef PD_MFMA_S0
+            }
+            if constexpr (FP8) {
+              if (kk + 1 < kKSteps) {
+                const u32x2 w = kw[(kk + 1) % kKAhead];
+                kc[(kk + 1) & 1] = cvt8x8(w[0], w[1]);
+              }
+              // (the conversions stay ahead of the product MFMA and the K read)
+              __builtin_amdgcn_sched_barrier(0);
             }
             if (FP8 && kk < 32) {
               const int s = kk / 16, idx = kk % 16, d = idx >> 2, r = idx & 3, v = 4 * s + d;
@@ -734,11 +749,14 @@ void mla_verify_kernel(MlaArgs a) {
         else
           chain(std::false_type{});
         if (kLateFetch && k + 3 < n) pg_next = fetch(tb + k + 3);
-        // The softmax works on the raw scores: max(x) * c is max(x * c) for
-        // c > 0, and each probability takes one fma, exp2(x * c - m_ref).
+        // The softmax works on the raw scores x (FP8: code . q, with k_scale
+        // in the scale cx = c * k_scale): max(x) * cx is max(x * cx) for
+        // cx > 0 (min for cx < 0), and each probability takes one fma,
+        // exp2(x * cx - m_ref).  With a power-of-two k_scale both caches give
+        // the same products, so they round alike.
         float x[16];
   #pragma unroll
-        for (int e = 0; e < 16; ++e) x[e] = FP8 ? sacc[e] * kscale : sacc[e];
+        for (int e = 0; e < 16; ++e) x[e] = sacc[e];
         if constexpr (!FP8) {
           // bf16: tile k-1's 32 products with tile k's softmax
           // interleaved by hand, one product and a slice of the softmax per
@@ -786,9 +804,12 @@ void mla_verify_kernel(MlaArgs a) {
               ovf_n = mt - m_ref_n > kRefHeadroomLog2;   // false while -inf
               mref = m_ref_n == neg_inf() ? 0.f : m_ref_n;
             } else if (j >= 5 && j < 21) {
+              // each step adds the previous step's probability (the row sum
+              // in the FP8 path's order), so no add waits on the exp just issued
               p[j - 5] = fast_exp2(__builtin_fmaf(x[j - 5], c, -mref));
-              lsum += p[j - 5];
+              if (j > 5) lsum += p[j - 6];
             } else if (j == 21) {
+              lsum += p[15];
               pw0 = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                           pack_bf16x2(p[6], p[7])};
             } else if (j == 22) {
@@ -811,19 +832,30 @@ void mla_verify_kernel(MlaArgs a) {
           if (!live) break;
 
           // causal limit of this lane's row: token tok0 + 8j + 4 g2 + i < hi_row
+          const float cx = c * kscale;
+          const bool up = !(cx < 0.f);   // wave-uniform
+          // (a masked key's raw score is the one whose probability is 0)
+          const float x_masked = up ? neg_inf() : __builtin_inff();
           if (tok0 + kTileTokens > hi_wmin && tok0 + kTileTokens > hi_row) {
   #pragma unroll
             for (int e = 0; e < 16; ++e) {
               const int tok = tok0 + 8 * (e >> 2) + 4 * g2 + (e & 3);
-              if (tok >= hi_row) x[e] = neg_inf();
+              if (tok >= hi_row) x[e] = x_masked;
             }
           }
 
           // ---- online softmax against the fixed row reference ----
           float mt = x[0];
+          if (up) {
   #pragma unroll
-          for (int e = 1; e < 16; ++e) mt = fmaxf(mt, x[e]);
-          mt = max_xor32(mt) * c;
+            for (int e = 1; e < 16; ++e) mt = fmaxf(mt, x[e]);
+            mt = max_xor32(mt);
+          } else {
+  #pragma unroll
+            for (int e = 1; e < 16; ++e) mt = fminf(mt, x[e]);
+            mt = -max_xor32(-mt);
+          }
+          mt *= cx;
           m_seen = fmaxf(m_seen, mt);
           // first non-empty tile of the row: take its max as the reference (the
           // accumulator and l are still exactly 0, so nothing needs rescaling)
@@ -834,7 +866,7 @@ void mla_verify_kernel(MlaArgs a) {
           float lsum = 0.f;   // summed as on the bf16 path, so the two round alike
   #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            p[e] = fast_exp2(__builtin_fmaf(x[e], c, -mref));
+            p[e] = fast_exp2(__builtin_fmaf(x[e], cx, -mref));
             lsum += p[e];
           }
           l_run += lsum;
