@@ -247,10 +247,12 @@ PD_API int paged_decode_gqa(const void* q, int64_t q_stride_b, int64_t q_stride_
  * workspace    >= pd_workspace_bytes(B*qlen, Hq, S, D) bytes when S > 1.
  * Other arguments as for paged_decode_gqa.
  *
- * Supported: as paged_decode_gqa, with qlen * G <= 64 (the verify tokens of a
- * kv head's query heads share the score tiles, groups of 16 (token, head)
- * columns, so a cache tile is read once for all of them); otherwise
- * PD_ERR_UNSUPPORTED.  Also
+ * Supported: as paged_decode_gqa, any qlen >= 1.  Up to 64 (token, head)
+ * pairs, qlen * G <= 64, the verify tokens of a kv head's query heads share
+ * the score tiles (groups of 16 columns), so a cache tile is read once for
+ * all of them.  Longer verify rows run as ceil(qlen * G / 64) launches of
+ * consecutive tokens (slice sizes differ by at most one), each reading the
+ * cache again; the split merge, if any, follows the last.  Also
  * ((qlen-1)*q_stride_row + (G-1)*q_stride_h + D) * 2 < 2^31.  FP8 cache
  * strides must be multiples of 16.
  */

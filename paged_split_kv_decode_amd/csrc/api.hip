@@ -227,7 +227,11 @@ static int gqa_common(const void* q, int64_t q_stride_b, int64_t q_stride_h, con
   const bool fp8 = kv_dtype == PD_KV_FP8_E4M3FN;
   const int32_t G = num_q_heads / num_kv_heads;
   if (page_size < 1) return PD_ERR_INVALID;
-  if (head_dim != 128 || !page_ok(page_size) || (int64_t)qlen * G > 64)
+  // Score columns: at most 64 (verify token, head) pairs per launch.  Fixed
+  // verify rows past that run as slices of whole tokens, one launch each
+  // (the cache is then read once per slice); variable rows do not.
+  if (head_dim != 128 || !page_ok(page_size) || G > 64 ||
+      (cu_seqlens_q != nullptr && (int64_t)qlen * G > 64))
     return PD_ERR_UNSUPPORTED;
   if (batch == 0) return PD_OK;
   if (q == nullptr || kv == nullptr || block_table == nullptr || seq_lens == nullptr ||
@@ -302,6 +306,9 @@ static int gqa_common(const void* q, int64_t q_stride_b, int64_t q_stride_h, con
   a.seq_lens = seq_lens;
   a.real_lens = real_seq_lens;
   a.qlen = qlen;
+  a.q_req_rows = qlen;
+  a.t_off = 0;
+  a.len_sub = 0;
   a.cu_q = cu_seqlens_q;
   a.total_rows = (int32_t)rows;
   a.kv_fp8 = fp8 ? 1 : 0;
@@ -335,7 +342,24 @@ static int gqa_common(const void* q, int64_t q_stride_b, int64_t q_stride_h, con
     a.vn_sh = app->v_sh * eb;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (pd::launch_gqa_decode(a, s) != hipSuccess) return PD_ERR_HIP;
+  const int32_t per_launch = 64 / G;   // verify tokens of one launch
+  if (cu_seqlens_q != nullptr || qlen <= per_launch) {
+    if (pd::launch_gqa_decode(a, s) != hipSuccess) return PD_ERR_HIP;
+  } else {
+    // equal slices (sizes differ by at most one), in token order: with the
+    // fused append, a slice's new tokens are in the cache before the next
+    // slice attends them
+    const int32_t n_sl = (qlen + per_launch - 1) / per_launch;
+    int32_t t0 = 0;
+    for (int32_t i = 0; i < n_sl; ++i) {
+      const int32_t n = qlen / n_sl + (i < qlen % n_sl ? 1 : 0);
+      a.qlen = n;
+      a.t_off = t0;
+      a.len_sub = qlen - t0 - n;
+      if (pd::launch_gqa_decode(a, s) != hipSuccess) return PD_ERR_HIP;
+      t0 += n;
+    }
+  }
   if (num_kv_splits > 1 && !partials_only) {
     pd::MergeArgs m{};
     m.ws = workspace;

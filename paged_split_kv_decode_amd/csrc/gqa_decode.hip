@@ -62,7 +62,9 @@ hipError_t launch_gqa_decode(const GqaArgs& a, hipStream_t stream) {
   const int n = grid_size();
   if (n <= 0) return hipErrorInvalidDevice;
   // the verify instantiations also take decode with more than 16 heads per kv head
-  const bool verify = a.qlen > 1 || a.real_lens != nullptr || a.cu_q != nullptr || a.G > 16;
+  // (a slice of longer verify rows is verify whatever its length)
+  const bool verify = a.qlen > 1 || a.q_req_rows > 1 || a.real_lens != nullptr ||
+                      a.cu_q != nullptr || a.G > 16;
   if (a.P <= 0) return hipErrorInvalidValue;
   return a.kn != nullptr ? launch_classes<true>(a, verify, n, stream)
                          : launch_classes<false>(a, verify, n, stream);

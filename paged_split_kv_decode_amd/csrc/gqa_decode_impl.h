@@ -122,7 +122,7 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 struct Req {
   int lo, hi, nt;
   int n, row0;   // query rows of the request: n tokens from row row0
-  int L;         // seq_lens[b] as given (the fused append's tokens end there)
+  int L;         // seq_lens[b] as given, less len_sub (the fused append's tokens end there)
 };
 
 // Length bound standing for "no real length given".
@@ -131,9 +131,10 @@ constexpr int kNoReal = 1 << 30;
 // Key range of verify row t of a request with n query tokens, length L
 // (clamped to the block-table row) and real length Lr: [lo_t, hi_t) with
 // hi_t = max(min(L - n + 1 + t, Lr), 0) and, with a window,
-// lo_t = max(hi_t - window, 0).
+// lo_t = max(hi_t - window, 0).  A slice of longer verify rows (len_sub
+// tokens after it) takes L - len_sub for L after the clamp.
 __device__ __forceinline__ int row_hi(const GqaArgs& a, int L, int Lr, int t, int n) {
-  L = min(max(L, 0), a.max_blocks * a.P);
+  L = min(max(L, 0), a.max_blocks * a.P) - a.len_sub;
   return max(min(L - n + 1 + t, Lr), 0);
 }
 __device__ __forceinline__ int row_lo(const GqaArgs& a, int hi) {
@@ -146,21 +147,21 @@ __device__ __forceinline__ Req range_of(const GqaArgs& a, int L, int Lr, int n) 
   Req r;
   r.n = n;
   r.row0 = 0;
-  r.L = L;
+  r.L = L - a.len_sub;
   r.hi = n > 0 ? row_hi(a, L, Lr, n - 1, n) : 0;
   r.lo = row_lo(a, row_hi(a, L, Lr, 0, n));
   r.nt = r.hi > r.lo ? ((r.hi + 31) >> 5) - (r.lo >> 5) : 0;
   return r;
 }
 
-// Query rows of request b: rows row0 .. row0 + n - 1.  Uniform: b * qlen and
-// qlen.  Variable ("cumulative query lengths"): cu_q[b] .. cu_q[b + 1] - 1,
+// Query rows of request b: rows row0 .. row0 + n - 1.  Uniform: b *
+// q_req_rows + t_off and qlen.  Variable ("cumulative query lengths"): cu_q[b] .. cu_q[b + 1] - 1,
 // clamped to [0, total_rows) and to at most qlen rows (the column bound).
 struct QRows {
   int row0, n;
 };
 __device__ __forceinline__ QRows query_rows(const GqaArgs& a, int b) {
-  if (a.cu_q == nullptr) return QRows{b * a.qlen, a.qlen};
+  if (a.cu_q == nullptr) return QRows{b * a.q_req_rows + a.t_off, a.qlen};
   const int r0 = min(max((int)as_const(a.cu_q)[b], 0), a.total_rows);
   const int r1 = min(max((int)as_const(a.cu_q)[b + 1], r0), a.total_rows);
   return QRows{r0, min(r1 - r0, a.qlen)};

@@ -29,7 +29,13 @@ struct GqaArgs {
   const int32_t* seq_lens;
   const int32_t* real_lens;  // nullptr: equal to seq_lens
   int32_t qlen;              // verify tokens per request (the most, with cu_q); qlen * G <= 64
-  const int32_t* cu_q;       // nullptr: request b has rows b * qlen + t; else [B + 1]
+  // Uniform rows (cu_q == nullptr) may be one slice of longer verify rows:
+  // the launch's token t of request b is row b * q_req_rows + t_off + t, and
+  // len_sub (the request's verify tokens after the slice) comes off every
+  // row's causal limit and off the newest-token positions.  A whole call:
+  // q_req_rows = qlen, t_off = len_sub = 0.
+  int32_t q_req_rows, t_off, len_sub;
+  const int32_t* cu_q;       // nullptr: request b has rows b * q_req_rows + t_off + t; else [B + 1]
                              // cumulative query lengths (rows cu_q[b] .. cu_q[b + 1] - 1)
   int32_t total_rows;        // rows of q / out / lse (B * qlen, or cu_q[B])
   int32_t kv_fp8;            // 1: FP8 E4M3FN codes, K scaled by k_scale, V by v_scale

@@ -193,13 +193,53 @@ void check_gqa() {
   EXPECT(p.decode() == PD_ERR_UNSUPPORTED);
   p.P = 0;
   EXPECT(p.decode() == PD_ERR_INVALID);
-  // columns: qlen * G up to 64
+  // columns: qlen * G up to 64 in one launch
   Gqa v = g;
   v.qlen = 8;
   v.q_sr = 64 * 128;
-  EXPECT(v.verify() == PD_OK && r.gqa.qlen == 8 && r.gqa.total_rows == 16);
+  n = r.n_gqa;
+  EXPECT(v.verify() == PD_OK && r.gqa.qlen == 8 && r.gqa.total_rows == 16 && r.n_gqa == n + 1 &&
+         r.gqa.q_req_rows == 8 && r.gqa.t_off == 0 && r.gqa.len_sub == 0);
+  // longer rows: equal slices of whole tokens in token order, each with the
+  // tokens after it taken off the causal limit (G = 8: 8 tokens per launch)
   v.qlen = 9;
-  EXPECT(v.verify() == PD_ERR_UNSUPPORTED);
+  n = r.n_gqa;
+  EXPECT(v.verify() == PD_OK && r.n_gqa == n + 2);
+  {
+    const int* s0 = r.gqa_slice[n % 16];
+    const int* s1 = r.gqa_slice[(n + 1) % 16];
+    EXPECT(s0[0] == 5 && s0[1] == 0 && s0[2] == 4 && s0[3] == 9);
+    EXPECT(s1[0] == 4 && s1[1] == 5 && s1[2] == 0 && s1[3] == 9);
+  }
+  v.qlen = 20;
+  v.S = 4;
+  v.ws = kFakeF;
+  v.wsb = pd_workspace_bytes(2 * 20, 64, 4, 128);
+  n = r.n_gqa;
+  int nm3 = r.n_merge;
+  EXPECT(v.verify() == PD_OK && r.n_gqa == n + 3 && r.n_merge == nm3 + 1 && r.merge.rows == 40);
+  {
+    int t = 0;
+    for (int i = 0; i < 3; ++i) {
+      const int* si = r.gqa_slice[(n + i) % 16];
+      EXPECT(si[0] == (i < 2 ? 7 : 6) && si[1] == t && si[2] == 20 - t - si[0] && si[3] == 20);
+      t += si[0];
+    }
+    EXPECT(t == 20);
+  }
+  // G = 64: one token per launch
+  Gqa w = g;
+  w.Hq = 8 * 64;
+  w.qlen = 3;
+  w.q_sr = 8 * 64 * 128;
+  w.o_sr = 8 * 64 * 128;
+  n = r.n_gqa;
+  EXPECT(w.verify() == PD_OK && r.n_gqa == n + 3 && r.gqa.qlen == 1 && r.gqa.t_off == 2 &&
+         r.gqa.len_sub == 0);
+  // variable rows are never sliced
+  v = g;
+  v.qlen = 9;
+  EXPECT(v.varlen(kFakeI, 18) == PD_ERR_UNSUPPORTED);
   Gqa h = g;
   h.Hq = 8 * 64;
   EXPECT(h.decode() == PD_OK && r.gqa.G == 64);

@@ -12,8 +12,14 @@ Record g_rec;
 namespace pd {
 
 hipError_t launch_gqa_decode(const GqaArgs& a, hipStream_t) {
-  pd_stub::g_rec.gqa = a;
-  ++pd_stub::g_rec.n_gqa;
+  auto& r = pd_stub::g_rec;
+  r.gqa = a;
+  int* sl = r.gqa_slice[r.n_gqa % 16];
+  sl[0] = a.qlen;
+  sl[1] = a.t_off;
+  sl[2] = a.len_sub;
+  sl[3] = a.q_req_rows;
+  ++r.n_gqa;
   return hipSuccess;
 }
 

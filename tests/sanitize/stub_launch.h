@@ -11,6 +11,8 @@ struct Record {
   pd::MergeArgs merge{};
   pd::AppendArgs append{};
   int n_gqa = 0, n_mla = 0, n_merge = 0, n_append = 0;
+  // (qlen, t_off, len_sub, q_req_rows) of GQA launches n_gqa - 1 ... (mod 16)
+  int gqa_slice[16][4] = {};
 };
 
 extern Record g_rec;

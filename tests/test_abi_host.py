@@ -229,7 +229,10 @@ def test_gqa_verify_argument_checks_happen_before_any_hip_call():
     assert _gqav(qlen=0) == PD_ERR_INVALID
     assert _gqav(q=NULL) == PD_ERR_INVALID
     assert _gqav(scale=float("inf")) == PD_ERR_INVALID
-    assert _gqav(qlen=9) == PD_ERR_UNSUPPORTED                 # qlen * G = 72 > 64
+    # qlen * G = 72 > 64: accepted (two launches of 5 and 4 tokens); the
+    # missing workspace stops it before any HIP call
+    assert _gqav(qlen=9, S=4) == PD_ERR_WORKSPACE
+    assert _gqav(qlen=9, Hq=8 * 65, Hkv=8) == PD_ERR_UNSUPPORTED   # G = 65
     assert _gqa(Hq=8 * 65, Hkv=8) == PD_ERR_UNSUPPORTED       # G = 65
     assert _gqav(qlen=4, Hq=32, D=64) == PD_ERR_UNSUPPORTED
     assert _gqav(osr=64 * 128 + 4) == PD_ERR_ALIGN
@@ -337,7 +340,7 @@ def _gqavp(**kw):
 def test_gqa_verify_partials_argument_checks_happen_before_any_hip_call():
     assert _gqavp(B=0, q=NULL, kv=NULL, bt=NULL, sl=NULL, ws=NULL, wsb=0) == PD_OK
     assert _gqavp(qlen=0) == PD_ERR_INVALID
-    assert _gqavp(qlen=9) == PD_ERR_UNSUPPORTED                # qlen * G = 72 > 64
+    assert _gqavp(qlen=9) == PD_ERR_WORKSPACE                  # sliced; 18 rows need more
     assert _gqavp(dt=1, per=2) == PD_ERR_INVALID
     # fixed qlen: rows = B * qlen, total_rows ignored
     assert _gqavp(wsb=4 * 64 * 129 * 4 - 4) == PD_ERR_WORKSPACE
@@ -410,7 +413,7 @@ def test_fused_append_argument_checks_happen_before_any_hip_call():
     assert _gqaa(kn=FAKE + 8) == PD_ERR_ALIGN                 # rows in 16-byte chunks
     assert _gqaa(vnh=128 + 4) == PD_ERR_ALIGN
     assert _gqaa(dt=1, knr=8 * 128 + 8) == PD_ERR_ALIGN       # FP8: strides of 16 codes
-    assert _gqaa(qlen=9) == PD_ERR_UNSUPPORTED                 # qlen * G = 72 > 64, as verify
+    assert _gqaa(qlen=9, S=4) == PD_ERR_WORKSPACE              # qlen * G = 72: sliced, as verify
     assert _gqaa(knr=1 << 31) == PD_ERR_UNSUPPORTED
     assert _gqaa(S=4) == PD_ERR_WORKSPACE
     need = lib.pd_workspace_bytes(2 * 2, 64, 4, 128)

@@ -115,6 +115,9 @@ CASES = [
     ("verify2", dict(batch=6, len_range=(1, 700), qlen=2, real_drop=(0, 2))),
     ("verify4_cols32", dict(batch=5, len_range=(1, 600), qlen=4, real_drop=(0, 3))),
     ("verify8_cols64", dict(batch=4, len_range=(1, 500), qlen=8, window=100)),
+    # 12 tokens x 8 heads: two slices, the second attends the first's new
+    # tokens from the cache the first launch wrote
+    ("verify12_sliced", dict(batch=4, len_range=(1, 500), qlen=12, real_drop=(0, 2))),
 ]
 
 

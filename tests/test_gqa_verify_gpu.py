@@ -2,7 +2,8 @@
 
 Every call goes through the C ABI (ctypes binding).  Inputs are seeded
 ``synth`` workloads with every never-attended cache slot NaN-poisoned.  The
-tests cover qlen x G up to 64 columns (one to four score tiles of 16),
+tests cover qlen x G up to 64 columns (one to four score tiles of 16) and
+longer verify rows (run as slices of whole tokens),
 decode with up to 64 heads per kv head, windows, real lengths, both page sizes and split counts, rows with no key, bit-exact
 marker keys at each row's own causal limit and window start, bitwise
 agreement with paged_decode_gqa at qlen = 1, invariance to page placement,
@@ -62,6 +63,39 @@ def test_reduced_verify(pd, qlen, heads, S):
     check_attention(out, lse, O, L, what=f"qlen={qlen} heads={heads} S={S}")
 
 
+# qlen * G above 64: the library runs slices of whole tokens, one launch each
+SLICED = [(9, (64, 8)), (16, (64, 8)), (20, (32, 4)), (3, (64, 1)), (5, (128, 4)), (33, (16, 8))]
+
+
+@pytest.mark.parametrize("qlen,heads", SLICED, ids=[f"q{q}g{h[0] // h[1]}" for q, h in SLICED])
+@pytest.mark.parametrize("S", ["cap", 1, 3])
+@pytest.mark.parametrize("window", [0, 37])
+def test_sliced_verify(pd, qlen, heads, S, window):
+    w = gqa_workload("gqa_verify", batch=5, len_range=(1, 700), qlen=qlen, heads=heads,
+                     real_drop=(0, 3), window=window or None, seed_offset=qlen + window)
+    vals = w.values("cuda", poison=True)
+    if S == "cap":
+        S = pd.gqa_split_cap(w.B, w.Hkv, int(w.seq_lens.max()), w.window)
+    out, lse = _run(pd, w, vals, S)
+    O, L = oracle_gqa(w, vals)
+    check_attention(out, lse, O, L, what=f"sliced qlen={qlen} heads={heads} S={S} W={window}")
+
+
+def test_sliced_verify_fp8(pd):
+    from helpers import O_ATOL_FP8
+    w = gqa_workload("gqa_verify", batch=5, len_range=(1, 700), qlen=12, heads=(64, 8),
+                     real_drop=(0, 2), seed_offset=5)
+    vals = w.values("cuda", poison=True, fp8=True)
+    for S in (1, 4):
+        bt_d, sl, real = _dev(w)
+        out, lse = pd.paged_verify_gqa(vals["q"], vals["kv"], bt_d, sl, w.qlen, w.sm_scale,
+                                       sinks=vals["sinks"], real_seq_lens=real, num_kv_splits=S,
+                                       k_scale=vals["k_scale"], v_scale=vals["v_scale"])
+        torch.cuda.synchronize()
+        O, L = oracle_gqa(w, vals)
+        check_attention(out, lse, O, L, o_atol=O_ATOL_FP8, what=f"sliced fp8 S={S}")
+
+
 @pytest.mark.parametrize("qlen,heads", [(4, (32, 8)), (8, (64, 8))])
 @pytest.mark.parametrize("window", [1, 5, 100])
 @pytest.mark.parametrize("P", [16, 32, 12])
@@ -93,16 +127,17 @@ def test_rows_without_keys_are_exact(pd, S):
                 assert torch.all(torch.isneginf(lse[r])), (b, t)
 
 
+@pytest.mark.parametrize("qlen", [4, 12], ids=["q4", "q12"])
 @pytest.mark.parametrize("heads", [(16, 4), (64, 4)], ids=["cols16", "cols64"])
 @pytest.mark.parametrize("order", ["last", "first"])
 @pytest.mark.parametrize("P", [16, 32])
-def test_marker_at_each_rows_limit_is_bit_exact(pd, order, P, heads):
+def test_marker_at_each_rows_limit_is_bit_exact(pd, order, P, heads, qlen):
     """Key j scores 128 * m_j with m_j = j ("last") or 200 - j ("first"), so
     each row's result is exactly the V row of its largest attended key: its
     own last key hi_t - 1, or its first key lo_t (window start).  Keys past a
     row's limit are still attended by the later rows, so a causal-mask slip
     selects a different V row."""
-    D, qlen, W = 128, 4, 37
+    D, W = 128, 37   # qlen 12 at 16 heads per kv head: three slices of 4 tokens
     Hq, Hkv = heads
     lens = [70, 33, 95, 4]
     B = len(lens)
